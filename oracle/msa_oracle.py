@@ -1,0 +1,305 @@
+"""Plain, slow, float64 CPU oracle of the MSA online-routing + sparse-attention path.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  It
+shares no code with the HIP path; the only thing both sides share is the
+seeded input generator in ``synth``.
+
+Every function follows the plain definition of one step, in float64, with
+materialised intermediates (the full token x chunk score tensor, a full sort
+for top-k, an explicit concatenation for attention).  Sources, cited by page
+and section:
+
+* [P1] "MSA-arXiv26" paper note, section 核心方法 (method): 架构 (architecture),
+  Document-wise RoPE, Memory Parallel 推理 (inference).
+* [P2] "MSA: Memory Sparse Attention" project README, sections
+  Overall Design > Architecture and Overall Design > Inference Pipeline.
+* [P3] MSA project note, section 架构设计 > MSA Layer 工作流程 (layer workflow).
+
+Readings where the pages are silent (each also listed in the design notes):
+
+* R1  "token-wise max" runs over the query tokens and the document's pooled
+      chunks, giving one score per document; the head mean sits inside.
+* R2  pool first, then L2-normalise the pooled routing key.
+* R3  routing uses as many query heads as key heads (no GQA in routing).
+* R4  no RoPE on routing vectors.
+* R5  norms are clamped at eps = 1e-8 (a zero vector has cosine 0).
+* R6  a partial last chunk is the mean of the tokens it has.
+* R9  ranking is by (score descending, document id ascending).
+* R10 an empty document scores -inf; k larger than the number of documents
+      is an error.
+* R11 a pooled chunk sits at its chunk index inside its document (0, 1, ...).
+* R12 local token i sits at position q_pos_offset + i, q_pos_offset = k by
+      default ("offset by k").
+* R13 the T query tokens are the last T of the L_loc local tokens; causal
+      inside the local part; every retrieved entry is visible to every query
+      token.
+* R14 query head hq reads KV head floor(hq / (Hq / Hkv)).
+* R15 softmax scale 1/sqrt(d).
+* R16 rotate-half RoPE: pairs (m, m + d/2), angle p * base**(-2m/d).
+* R17 context order: retrieved documents in rank order, each in chunk order,
+      then the local tokens.
+* R18 stores (normalised routing keys, pooled K and V) are rounded once,
+      round-to-nearest-even, to the store dtype.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+EPS = 1e-8
+
+
+# ---------------------------------------------------------------------------
+# rounding to the store dtype (R18)
+# ---------------------------------------------------------------------------
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (8 significand bits),
+    ties to even; returned as float64.  Finite normal inputs only."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                          # x = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)   # rint: ties to even
+
+
+def round_to_f32(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def round_to_store(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "f32":
+        return round_to_f32(x)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# document index
+# ---------------------------------------------------------------------------
+
+def chunk_offsets(tok_off: np.ndarray, chunk: int) -> np.ndarray:
+    """Chunk CSR offsets: document i has ceil(len_i / chunk) pooled chunks."""
+    tok_off = np.asarray(tok_off, dtype=np.int64)
+    lens = np.diff(tok_off)
+    counts = (lens + chunk - 1) // chunk
+    out = np.zeros(len(lens) + 1, dtype=np.int64)
+    out[1:] = np.cumsum(counts)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Stage 1: chunk-mean pooling and routing-key normalisation
+# [P1 架构; P2 Overall Design > Architecture ("chunk-mean pooled"); P2 Inference
+#  Pipeline, "Global Memory Encoding"; P3 MSA Layer 工作流程 step 1]
+# ---------------------------------------------------------------------------
+
+def pool(x: np.ndarray, tok_off: np.ndarray, chunk: int) -> np.ndarray:
+    """Chunk means of per-token vectors.
+
+    x: [n_tok, H, d]; document i owns tokens tok_off[i] .. tok_off[i+1]-1.
+    Chunk j of document i averages tokens tok_off[i] + j*chunk up to (not
+    including) min(tok_off[i] + (j+1)*chunk, tok_off[i+1]) (R6).
+    Returns [n_chunks, H, d] float64, chunks in document order.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    tok_off = np.asarray(tok_off, dtype=np.int64)
+    rows = []
+    for i in range(len(tok_off) - 1):
+        lo, hi = int(tok_off[i]), int(tok_off[i + 1])
+        for s in range(lo, hi, chunk):
+            e = min(s + chunk, hi)
+            rows.append(x[s:e].sum(axis=0) / (e - s))
+    if not rows:
+        return np.zeros((0,) + x.shape[1:], dtype=np.float64)
+    return np.stack(rows)
+
+
+def l2_normalize(x: np.ndarray, eps: float = EPS) -> np.ndarray:
+    """x / max(||x||_2, eps) over the last axis (R5)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt((x * x).sum(axis=-1, keepdims=True))
+    return x / np.maximum(n, eps)
+
+
+def pool_encode(x: np.ndarray, tok_off: np.ndarray, chunk: int, normalize: bool,
+                dtype: str) -> np.ndarray:
+    """Pooled store entry: chunk mean, L2-normalised per (chunk, head) for
+    the routing keys (R2), rounded once to the store dtype (R18)."""
+    p = pool(x, tok_off, chunk)
+    if normalize:
+        p = l2_normalize(p)
+    return round_to_store(p, dtype)
+
+
+# ---------------------------------------------------------------------------
+# Stage 2: routing score, top-k, context assembly
+# [P1 架构 (cosine similarity, top-k documents); P2 Overall Design >
+#  Architecture ("cosine similarity (mean-pooled over heads, then token-wise
+#  max)"); P2 Inference Pipeline, "Online Routing & Context Assembly";
+#  P3 MSA Layer 工作流程 steps 2-4]
+# ---------------------------------------------------------------------------
+
+def chunk_cosines(q_r: np.ndarray, kr_store: np.ndarray, eps: float = EPS) -> np.ndarray:
+    """s[b, t, c] = (1/H) sum_h cos(q_r[b, t, h], kr[c, h]).
+
+    q_r: [B, T, H, d] raw routing queries; kr_store: [N, H, d], already
+    L2-normalised store entries (their cosine equals their dot product with
+    a unit query).  Head mean inside the token/chunk max (R1, R3)."""
+    q = l2_normalize(np.asarray(q_r, dtype=np.float64), eps)
+    k = np.asarray(kr_store, dtype=np.float64)
+    B, T, H, d = q.shape
+    N = k.shape[0]
+    # per-head dot products, then the mean over heads
+    s = np.zeros((B, T, N), dtype=np.float64)
+    for h in range(H):
+        s += q[:, :, h, :] @ k[:, h, :].T
+    return s / H
+
+
+def route_scores(q_r: np.ndarray, kr_store: np.ndarray, chunk_off: np.ndarray,
+                 eps: float = EPS) -> np.ndarray:
+    """One score per (query, document): the max over the query's tokens and
+    the document's chunks of the head-mean cosine (R1).  Empty documents
+    score -inf (R10).  Returns [B, D] float64."""
+    s = chunk_cosines(q_r, kr_store, eps)          # [B, T, N]
+    per_chunk = s.max(axis=1)                      # token-wise max -> [B, N]
+    chunk_off = np.asarray(chunk_off, dtype=np.int64)
+    D = len(chunk_off) - 1
+    out = np.full((s.shape[0], D), -np.inf, dtype=np.float64)
+    for i in range(D):
+        lo, hi = int(chunk_off[i]), int(chunk_off[i + 1])
+        if hi > lo:
+            out[:, i] = per_chunk[:, lo:hi].max(axis=1)
+    return out
+
+
+def topk(doc_score: np.ndarray, k: int):
+    """The k best documents per query, ordered by (score desc, id asc) (R9).
+    Returns (ids int32 [B, k], vals float64 [B, k])."""
+    doc_score = np.asarray(doc_score, dtype=np.float64)
+    B, D = doc_score.shape
+    if k < 1 or k > D:
+        raise ValueError("k must be in [1, n_docs]")
+    ids = np.empty((B, k), dtype=np.int32)
+    vals = np.empty((B, k), dtype=np.float64)
+    doc = np.arange(D)
+    for b in range(B):
+        order = np.lexsort((doc, -doc_score[b]))   # primary: -score, then id
+        ids[b] = order[:k]
+        vals[b] = doc_score[b, order[:k]]
+    return ids, vals
+
+
+def gather(ids_b: np.ndarray, chunk_off: np.ndarray, k_bar: np.ndarray, v_bar: np.ndarray):
+    """Context of one query: the selected documents' pooled K/V in rank order,
+    each document's chunks in order (R17), with each entry's position inside
+    its document (R11)."""
+    ks, vs, pos = [], [], []
+    for doc in ids_b:
+        lo, hi = int(chunk_off[doc]), int(chunk_off[doc + 1])
+        ks.append(np.asarray(k_bar[lo:hi], dtype=np.float64))
+        vs.append(np.asarray(v_bar[lo:hi], dtype=np.float64))
+        pos.append(np.arange(hi - lo, dtype=np.int64))
+    H, d = k_bar.shape[1:]
+    if ks:
+        return np.concatenate(ks), np.concatenate(vs), np.concatenate(pos)
+    return np.zeros((0, H, d)), np.zeros((0, H, d)), np.zeros(0, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Stage 3: sparse attention with document-wise and global RoPE
+# [P1 Document-wise RoPE; P2 Overall Design > Architecture, "Parallel
+#  (document-wise) RoPE" and "Global RoPE (active context)"; P2 Inference
+#  Pipeline, "Sparse Generation"; P3 MSA Layer 工作流程 steps 4-5]
+# ---------------------------------------------------------------------------
+
+def rope_angles(pos: np.ndarray, d: int, base: float) -> np.ndarray:
+    """angle[..., m] = pos * base**(-2m/d), m < d/2, in float64 (R16)."""
+    m = np.arange(d // 2, dtype=np.float64)
+    theta = base ** (-2.0 * m / d)
+    return np.asarray(pos, dtype=np.float64)[..., None] * theta
+
+
+def rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Rotate-half RoPE: the pair (x[m], x[m + d/2]) turns by angle[m].
+
+    x: [..., d]; pos broadcasts against x[..., 0]."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    a = rope_angles(pos, d, base)
+    c, s = np.cos(a), np.sin(a)
+    x1, x2 = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def attend_one(q: np.ndarray, k_ctx: np.ndarray, v_ctx: np.ndarray, ctx_pos: np.ndarray,
+               k_loc: np.ndarray, v_loc: np.ndarray, q_pos_offset: int, base: float,
+               sm_scale: float) -> np.ndarray:
+    """Attention of one query (T tokens) over [retrieved context ; local].
+
+    q: [T, Hq, d]; k_ctx/v_ctx: [n_ctx, Hkv, d] pooled, un-rotated;
+    ctx_pos: [n_ctx] positions inside their documents (R11);
+    k_loc/v_loc: [L_loc, Hkv, d] un-rotated.  Query token t is local token
+    L_loc - T + t (R13) at position q_pos_offset + L_loc - T + t (R12); it
+    sees every context entry and local tokens 0 .. L_loc - T + t.
+    Returns [T, Hq, d] float64."""
+    T, Hq, d = q.shape
+    L_loc, Hkv = k_loc.shape[:2]
+    G = Hq // Hkv
+    n_ctx = k_ctx.shape[0]
+    # explicit concatenation of the context (R17) and its positions
+    k_all = np.concatenate([np.asarray(k_ctx, np.float64), np.asarray(k_loc, np.float64)])
+    v_all = np.concatenate([np.asarray(v_ctx, np.float64), np.asarray(v_loc, np.float64)])
+    pos_all = np.concatenate([np.asarray(ctx_pos, np.int64),
+                              q_pos_offset + np.arange(L_loc, dtype=np.int64)])
+    k_rot = rope(k_all, pos_all[:, None], base)                  # [n, Hkv, d]
+    q_abs = L_loc - T + np.arange(T)                             # local index of each token
+    q_rot = rope(q, (q_pos_offset + q_abs)[:, None], base)       # [T, Hq, d]
+    out = np.zeros((T, Hq, d), dtype=np.float64)
+    for t in range(T):
+        visible = np.ones(n_ctx + L_loc, dtype=bool)
+        visible[n_ctx + q_abs[t] + 1:] = False                    # causal on the local part
+        for hq in range(Hq):
+            g = hq // G                                           # R14
+            logits = sm_scale * (k_rot[:, g, :] @ q_rot[t, hq])
+            logits = np.where(visible, logits, -np.inf)
+            mx = logits.max()
+            p = np.exp(logits - mx)
+            p /= p.sum()
+            out[t, hq] = p @ v_all[:, g, :]
+    return out
+
+
+def sparse_attention(q: np.ndarray, contexts, k_loc: np.ndarray, v_loc: np.ndarray,
+                     q_pos_offset: int, base: float, sm_scale: float | None = None) -> np.ndarray:
+    """Batched form of ``attend_one``.  contexts[b] = (k_ctx, v_ctx, ctx_pos)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, T, Hq, d = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)                                # R15
+    out = np.zeros(q.shape, dtype=np.float64)
+    for b in range(B):
+        kc, vc, pc = contexts[b]
+        out[b] = attend_one(q[b], kc, vc, pc, k_loc[b], v_loc[b], q_pos_offset, base, sm_scale)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# one routed layer, end to end (R7, R8: per layer, per query, one top-k)
+# ---------------------------------------------------------------------------
+
+def layer(q_r, kr_store, chunk_off, k_bar, v_bar, k, q, k_loc, v_loc,
+          q_pos_offset=None, base=1e6, sm_scale=None, ids_override=None):
+    """Route -> top-k -> assemble -> attend for one layer.
+
+    ``ids_override`` (B x k) replaces the oracle's own selection for the
+    attention step: inside the tie band several selections are correct and
+    the attention is then compared on the selection actually made."""
+    if q_pos_offset is None:
+        q_pos_offset = k
+    doc_score = route_scores(q_r, kr_store, chunk_off)
+    ids, vals = topk(doc_score, k)
+    use = ids if ids_override is None else np.asarray(ids_override)
+    ctx = [gather(use[b], chunk_off, k_bar, v_bar) for b in range(q.shape[0])]
+    out = sparse_attention(q, ctx, k_loc, v_loc, q_pos_offset, base, sm_scale)
+    return dict(doc_score=doc_score, ids=ids, vals=vals, contexts=ctx, out=out)
