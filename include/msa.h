@@ -1,0 +1,230 @@
+/*
+ * msa.h - C ABI of the MSA (Memory Sparse Attention) online-routing and
+ * sparse-attention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the three-stage inference pipeline of "MSA: Memory
+ * Sparse Attention" (project README, Overall Design > Inference Pipeline):
+ *   Stage 1, Global Memory Encoding  -> msa_pool_encode
+ *   Stage 2, Online Routing & Context Assembly
+ *                                     -> msa_route_score, msa_topk, msa_gather_kv
+ *   Stage 3, Sparse Generation        -> msa_sparse_attn
+ * The layer itself is described in the README's Overall Design > Architecture
+ * and in the "MSA-arXiv26" paper note, section 核心方法 > 架构 and
+ * Document-wise RoPE.
+ *
+ * Conventions shared by every call
+ *  - Return value: an msa_status.  Arguments are validated on the host before
+ *    any HIP call; an invalid call enqueues nothing.  msa_last_error() gives a
+ *    human-readable detail of the last failure on the calling thread.
+ *  - Ownership: the caller owns every buffer.  The library allocates no
+ *    device or host memory; scratch space comes from the caller through
+ *    `ws` / `ws_bytes`, sized by the matching *_workspace query.
+ *  - Pointers are device pointers unless the name ends in `_h` (host).
+ *    Device buffers must be 16-byte aligned.
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    null stream) and the call returns.  The one host synchronisation is
+ *    msa_gather_kv in MSA_SRC_HOST_MEMCPY mode (documented there).
+ *  - Layouts are row-major with the last index contiguous.  Offsets are
+ *    int64; document ids, chunk->document maps, positions and lengths are
+ *    int32.
+ *  - dtype: MSA_F32 or MSA_BF16 (bfloat16 stored as its 16-bit pattern).
+ *  - Device faults of an enqueued kernel surface as MSA_ERR_HIP from the
+ *    launch check or at the caller's next synchronisation.
+ *  - No mutable global state: calls on distinct streams may run from
+ *    different threads.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1, /* a pointer, size or relation between sizes is wrong */
+  MSA_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels implement     */
+  MSA_ERR_WORKSPACE = 3,   /* ws_bytes smaller than the *_workspace query       */
+  MSA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed        */
+} msa_status;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+
+typedef enum {
+  MSA_SRC_DEVICE = 0,      /* K/V store in device memory (HBM)                          */
+  MSA_SRC_HOST_MAPPED = 1, /* store in pinned host memory, read by the gather kernel     */
+  MSA_SRC_HOST_MEMCPY = 2  /* store in pinned host memory, copied with hipMemcpyAsync on
+                              a side stream                                             */
+} msa_src_mode;
+
+/* Version of this ABI (bumped on any signature change). */
+int msa_abi_version(void);
+
+/* Static description of a status code. */
+const char* msa_status_string(int status);
+
+/* Detail message of the last failing call on this thread ("" if none). */
+const char* msa_last_error(void);
+
+/*
+ * msa_chunk_offsets (host only) - the chunk CSR of a tokenised memory.
+ * Chunk-wise pooling compresses each document on its own (README, Overall
+ * Design > Architecture: document latent states are chunk-mean pooled), so
+ * document i of len_i = tok_off_h[i+1] - tok_off_h[i] tokens owns
+ * ceil(len_i / chunk) pooled chunks; the last one may be partial.
+ *   tok_off_h   [n_docs + 1] non-decreasing, tok_off_h[0] == 0 (host)
+ *   chunk_off_h [n_docs + 1] output (host)
+ * Errors: INVALID_ARG for NULL pointers, n_docs < 1, chunk < 1, a decreasing
+ * or non-zero-based tok_off_h.
+ */
+int msa_chunk_offsets(const int64_t* tok_off_h, int64_t n_docs, int chunk, int64_t* chunk_off_h);
+
+/*
+ * msa_chunk_doc_map - inverse of the chunk CSR: chunk_doc[c] = the document
+ * that owns pooled chunk c (README, Inference Pipeline: per-document top-k
+ * needs every chunk's document).  Built once per memory, read by
+ * msa_pool_encode and msa_route_score.
+ *   chunk_off [n_docs + 1] device, non-decreasing, chunk_off[n_docs] == n_chunks
+ *   chunk_doc [n_chunks]   device output
+ * Errors: INVALID_ARG for NULL pointers or n_docs < 1, n_chunks < 1.
+ */
+int msa_chunk_doc_map(const int64_t* chunk_off, int64_t n_docs, int64_t n_chunks, int32_t* chunk_doc,
+                      void* stream);
+
+/*
+ * msa_pool_encode - Stage 1 ("Global Memory Encoding", README Inference
+ * Pipeline; "chunk-wise mean pool", paper note 核心方法 > 架构).
+ * For pooled chunk c = chunk j of document i and head h:
+ *   out[c,h,:] = mean of x[t,h,:] over the tokens t of that chunk
+ *                (tokens tok_off[i] + j*chunk ... min(+chunk, tok_off[i+1]) - 1;
+ *                a partial last chunk averages the tokens it has),
+ *   and if l2_normalize: out[c,h,:] /= max(||out[c,h,:]||_2, 1e-8)
+ *   (the routing keys, compared by cosine similarity).
+ * Accumulation is float32; each output is rounded once (to nearest even)
+ * to dtype.  Keys and values are stored un-rotated: RoPE is applied at
+ * attention time.
+ *   x         [n_tok, H, d] dtype
+ *   tok_off   [n_docs + 1] int64, chunk_off [n_docs + 1] int64 (chunk CSR of
+ *             tok_off for this chunk size), chunk_doc [n_chunks] int32
+ *   out       [n_chunks, H, d] dtype
+ * Errors: INVALID_ARG (NULL, non-positive sizes, d odd), UNSUPPORTED
+ * (H*d > 4096 or H*d not a multiple of 8).
+ */
+int msa_pool_encode(int dtype, const void* x, const int64_t* tok_off, const int64_t* chunk_off,
+                    const int32_t* chunk_doc, int64_t n_docs, int64_t n_tok, int64_t n_chunks, int H,
+                    int d, int chunk, int l2_normalize, void* out, void* stream);
+
+/*
+ * msa_route_score - Stage 2 routing score (README, Overall Design >
+ * Architecture: cosine similarity, mean-pooled over heads, then token-wise
+ * max; paper note 核心方法 > 架构: cosine against every document's compressed
+ * routing key).  For query b and document i:
+ *   doc_score[b,i] = max over tokens t < T and chunks c of document i of
+ *                    (1/H) * sum_h < q_r[b,t,h,:] / max(||q_r[b,t,h,:]||, 1e-8), kr_hat[c,h,:] >
+ * kr_hat must already be L2-normalised (msa_pool_encode with l2_normalize),
+ * so the dot product is the cosine.  A document with no chunk scores -inf.
+ * Products are exact (bf16 x bf16 or f32 x f32) with float32 accumulation;
+ * the query norm is applied per (token, head) in float32.  The score matrix
+ * is never materialised; the store is streamed once.
+ *   q_r        [B, T, H, d] dtype (raw routing queries)
+ *   kr_hat     [n_chunks, H, d] dtype
+ *   chunk_doc  [n_chunks] int32 (msa_chunk_doc_map); entries outside
+ *              [0, n_docs) are ignored
+ *   doc_score  [B, n_docs] float32 output
+ *   ws         msa_route_score_workspace() bytes (may be 0 -> ws may be NULL)
+ * Errors: INVALID_ARG (NULL, non-positive sizes), WORKSPACE, UNSUPPORTED
+ * (d > 256 or d % 8 != 0).
+ */
+size_t msa_route_score_workspace(int dtype, int B, int T, int H, int d, int64_t n_docs, int64_t n_chunks);
+int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
+                    const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks, float* doc_score,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * msa_topk - Stage 2 selection (README, Overall Design > Architecture:
+ * "selects Top-k documents"; paper note 核心方法 > 架构: top-k documents by
+ * cosine similarity).  For each query b the k documents with the largest
+ * doc_score, ordered by (score descending, document id ascending); ties are
+ * broken by the lower id, so the result is unique.
+ *   doc_score [B, n_docs] float32 (no NaN)
+ *   ids       [B, k] int32 output, vals [B, k] float32 output (rank order)
+ *   ws        msa_topk_workspace() bytes
+ * Errors: INVALID_ARG (NULL, B < 1, k < 1, k > n_docs), UNSUPPORTED (k > 256),
+ * WORKSPACE.
+ */
+size_t msa_topk_workspace(int B, int64_t n_docs, int k);
+int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
+             size_t ws_bytes, void* stream);
+
+/*
+ * msa_gather_kv - Stage 2 context assembly (README, Inference Pipeline:
+ * "load only the selected K/V"; tiered storage with the content K/V in host
+ * DRAM fetched when selected: README Inference Pipeline and paper note
+ * Memory Parallel 推理).  For query b:
+ *   the context is the chunks of documents ids[b,0], ids[b,1], ... (rank
+ *   order), each document's chunks in order:
+ *     k_ctx[b,e,:,:] = k_bar[c,:,:], v_ctx[b,e,:,:] = v_bar[c,:,:],
+ *     ctx_pos[b,e]   = c - chunk_off[doc]   (position inside the document,
+ *                                            document-wise RoPE)
+ *   ctx_len[b] = sum of the selected documents' chunk counts.
+ * Entries e >= ctx_len[b] are left untouched.
+ *   ids        [B, k] int32 (device); ids outside [0, n_docs) are an error
+ *              only in the sense that they contribute no entries
+ *   chunk_off  [n_docs + 1] int64 device; chunk_off_h the same on the host
+ *              (required for MSA_SRC_HOST_MEMCPY, else may be NULL)
+ *   k_bar/v_bar [n_chunks, Hkv, d] dtype: device memory (MSA_SRC_DEVICE) or
+ *              pinned host memory from hipHostMalloc (the two host modes)
+ *   max_doc_chunks  an upper bound of any document's chunk count
+ *   k_ctx/v_ctx [B, max_ctx, Hkv, d] dtype, ctx_pos [B, max_ctx] int32,
+ *   ctx_len [B] int32 outputs
+ *   ids_h      pinned host staging of B*k int32 (MSA_SRC_HOST_MEMCPY only)
+ *   copy_stream  side stream of the host copies (MSA_SRC_HOST_MEMCPY only);
+ *              `stream` waits for it before returning work on `stream`.
+ * MSA_SRC_HOST_MEMCPY copies the ids to ids_h and synchronises `stream`
+ * once (the host must know the selection to issue the copies).
+ * Errors: INVALID_ARG (NULL, sizes, max_ctx < k * max_doc_chunks),
+ * UNSUPPORTED (src_mode), HIP.
+ */
+int msa_gather_kv(int dtype, const int32_t* ids, int B, int k, const int64_t* chunk_off,
+                  const int64_t* chunk_off_h, int64_t n_docs, int max_doc_chunks, const void* k_bar,
+                  const void* v_bar, int64_t n_chunks, int Hkv, int d, int src_mode, int max_ctx,
+                  void* k_ctx, void* v_ctx, int32_t* ctx_pos, int32_t* ctx_len, int32_t* ids_h,
+                  void* stream, void* copy_stream);
+
+/*
+ * msa_sparse_attn - Stage 3 sparse attention (README, Overall Design >
+ * Architecture: the selected compressed K/V concatenated with the query's
+ * local K/V for autoregressive decoding; "Parallel (document-wise) RoPE"
+ * and "Global RoPE (active context)"; paper note, Document-wise RoPE).
+ * For query b, token t < T and query head hq (KV head g = hq / (Hq/Hkv)):
+ *   keys: context entries e < ctx_len[b] at position ctx_pos[b,e] (each
+ *         document restarts at 0), all visible; local tokens i < L_loc at
+ *         position q_pos_offset + i, visible iff i <= L_loc - T + t (the T
+ *         query tokens are the last T local tokens; causal).
+ *   query position: q_pos_offset + L_loc - T + t ("offset by k": pass k).
+ *   RoPE: rotate-half, the pair (m, m + d/2) turns by pos * rope_base^(-2m/d)
+ *         (angles reduced in float64), applied to q and every key on the fly.
+ *   out[b,t,hq,:] = softmax_j(sm_scale * <R q, R k_j>) . v_j   (float32)
+ *   q     [B, T, Hq, d] dtype; k_ctx/v_ctx/ctx_pos/ctx_len from msa_gather_kv
+ *   k_loc/v_loc [B, L_loc, Hkv, d] dtype, un-rotated
+ *   ctx_pos values must lie in [0, max_ctx)
+ *   out   [B, T, Hq, d] float32
+ *   ws    msa_sparse_attn_workspace() bytes
+ * Errors: INVALID_ARG (NULL, sizes, Hq % Hkv != 0, L_loc < T, d odd,
+ * q_pos_offset < 0), UNSUPPORTED (d > 256), WORKSPACE.
+ */
+size_t msa_sparse_attn_workspace(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc,
+                                 int q_pos_offset);
+int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d, const void* k_ctx,
+                    const void* v_ctx, const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx,
+                    const void* k_loc, const void* v_loc, int L_loc, int q_pos_offset, float rope_base,
+                    float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -1,0 +1,29 @@
+"""MI355X-native MSA (Memory Sparse Attention) routing + sparse-attention path.
+
+Thin Python binding over the C-ABI library ``libmsa.so`` (``include/msa.h``):
+argument marshalling only; every step runs in the library's HIP kernels.
+PyTorch provides device memory and streams.  Importing fails loudly if the
+library has not been built (``python -m sparse_attention_long_msa_amd.build``).
+"""
+from ._binding import (  # noqa: F401
+    MSA_BF16,
+    MSA_F32,
+    MSA_SRC_DEVICE,
+    MSA_SRC_HOST_MAPPED,
+    MSA_SRC_HOST_MEMCPY,
+    MsaError,
+    lib,
+    lib_path,
+    msa_abi_version,
+    msa_chunk_doc_map,
+    msa_chunk_offsets,
+    msa_gather_kv,
+    msa_pool_encode,
+    msa_route_score,
+    msa_route_score_workspace,
+    msa_sparse_attn,
+    msa_sparse_attn_workspace,
+    msa_topk,
+    msa_topk_workspace,
+)
+from .pipeline import LayerRunner  # noqa: F401

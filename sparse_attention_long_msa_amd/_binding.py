@@ -1,0 +1,210 @@
+"""ctypes binding of libmsa.so.  Same names as the C ABI; each function only
+marshals torch tensors / numpy arrays into pointers and sizes, allocates
+outputs and workspaces with torch when the caller passes none, and raises
+MsaError on a non-OK status."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libmsa.so")
+
+MSA_F32, MSA_BF16 = 0, 1
+MSA_SRC_DEVICE, MSA_SRC_HOST_MAPPED, MSA_SRC_HOST_MEMCPY = 0, 1, 2
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_int64
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+_SIGS = {
+    "msa_abi_version": (_I, []),
+    "msa_status_string": (ctypes.c_char_p, [_I]),
+    "msa_last_error": (ctypes.c_char_p, []),
+    "msa_chunk_offsets": (_I, [_P, _L, _I, _P]),
+    "msa_chunk_doc_map": (_I, [_P, _L, _L, _P, _P]),
+    "msa_pool_encode": (_I, [_I, _P, _P, _P, _P, _L, _L, _L, _I, _I, _I, _I, _P, _P]),
+    "msa_route_score_workspace": (_S, [_I, _I, _I, _I, _I, _L, _L]),
+    "msa_route_score": (_I, [_I, _P, _I, _I, _I, _I, _P, _P, _L, _L, _P, _P, _S, _P]),
+    "msa_topk_workspace": (_S, [_I, _L, _I]),
+    "msa_topk": (_I, [_P, _I, _L, _I, _P, _P, _P, _S, _P]),
+    "msa_gather_kv": (_I, [_I, _P, _I, _I, _P, _P, _L, _I, _P, _P, _L, _I, _I, _I, _I,
+                           _P, _P, _P, _P, _P, _P, _P]),
+    "msa_sparse_attn_workspace": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "msa_sparse_attn": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _I, _I,
+                             _F, _F, _P, _P, _S, _P]),
+}
+
+
+class MsaError(RuntimeError):
+    def __init__(self, name, status, detail):
+        super().__init__(f"{name} failed: status {status} ({_status_string(status)}): {detail}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(lib_path):
+        raise ImportError(f"{lib_path} is not built: run `python -m sparse_attention_long_msa_amd.build`")
+    h = ctypes.CDLL(lib_path)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(h, name)
+        f.restype = res
+        f.argtypes = args
+    return h
+
+
+lib = _load()
+
+
+def _status_string(s):
+    return lib.msa_status_string(s).decode()
+
+
+def _check(name, rc):
+    if rc != 0:
+        raise MsaError(name, rc, lib.msa_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return s.cuda_stream if hasattr(s, "cuda_stream") else s
+
+
+def _dtype(t):
+    if t.dtype == torch.float32:
+        return MSA_F32
+    if t.dtype == torch.bfloat16:
+        return MSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ws(nbytes, device, ws):
+    if nbytes == 0:
+        return ws, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def msa_abi_version():
+    return lib.msa_abi_version()
+
+
+def msa_chunk_offsets(tok_off, chunk):
+    tok_off = np.ascontiguousarray(np.asarray(tok_off, dtype=np.int64))
+    out = np.empty_like(tok_off)
+    _check("msa_chunk_offsets", lib.msa_chunk_offsets(_ptr(tok_off), len(tok_off) - 1, chunk, _ptr(out)))
+    return out
+
+
+def msa_chunk_doc_map(chunk_off, n_chunks, chunk_doc=None, stream=None):
+    if chunk_doc is None:
+        chunk_doc = torch.empty(n_chunks, dtype=torch.int32, device=chunk_off.device)
+    _check("msa_chunk_doc_map", lib.msa_chunk_doc_map(_ptr(chunk_off), chunk_off.numel() - 1, n_chunks,
+                                                      _ptr(chunk_doc), _stream(stream)))
+    return chunk_doc
+
+
+def msa_pool_encode(x, tok_off, chunk_off, chunk_doc, chunk, l2_normalize, out=None, stream=None):
+    n_tok, H, d = x.shape
+    n_chunks = chunk_doc.numel()
+    if out is None:
+        out = torch.empty((n_chunks, H, d), dtype=x.dtype, device=x.device)
+    _check("msa_pool_encode", lib.msa_pool_encode(
+        _dtype(x), _ptr(x), _ptr(tok_off), _ptr(chunk_off), _ptr(chunk_doc), tok_off.numel() - 1, n_tok,
+        n_chunks, H, d, chunk, int(bool(l2_normalize)), _ptr(out), _stream(stream)))
+    return out
+
+
+def msa_route_score_workspace(dtype, B, T, H, d, n_docs, n_chunks):
+    return lib.msa_route_score_workspace(dtype, B, T, H, d, n_docs, n_chunks)
+
+
+def msa_route_score(q_r, kr_hat, chunk_doc, n_docs, doc_score=None, ws=None, stream=None):
+    B, T, H, d = q_r.shape
+    n_chunks = kr_hat.shape[0]
+    dt = _dtype(q_r)
+    if doc_score is None:
+        doc_score = torch.empty((B, n_docs), dtype=torch.float32, device=q_r.device)
+    ws, wsb = _ws(msa_route_score_workspace(dt, B, T, H, d, n_docs, n_chunks), q_r.device, ws)
+    _check("msa_route_score", lib.msa_route_score(
+        dt, _ptr(q_r), B, T, H, d, _ptr(kr_hat), _ptr(chunk_doc), n_docs, n_chunks, _ptr(doc_score),
+        _ptr(ws), wsb, _stream(stream)))
+    return doc_score
+
+
+def msa_topk_workspace(B, n_docs, k):
+    return lib.msa_topk_workspace(B, n_docs, k)
+
+
+def msa_topk(doc_score, k, ids=None, vals=None, ws=None, stream=None):
+    B, n_docs = doc_score.shape
+    if ids is None:
+        ids = torch.empty((B, k), dtype=torch.int32, device=doc_score.device)
+    if vals is None:
+        vals = torch.empty((B, k), dtype=torch.float32, device=doc_score.device)
+    ws, wsb = _ws(msa_topk_workspace(B, n_docs, k), doc_score.device, ws)
+    _check("msa_topk", lib.msa_topk(_ptr(doc_score), B, n_docs, k, _ptr(ids), _ptr(vals), _ptr(ws), wsb,
+                                    _stream(stream)))
+    return ids, vals
+
+
+def msa_gather_kv(ids, chunk_off, k_bar, v_bar, max_doc_chunks, max_ctx, src_mode=MSA_SRC_DEVICE,
+                  chunk_off_h=None, k_ctx=None, v_ctx=None, ctx_pos=None, ctx_len=None, ids_h=None,
+                  stream=None, copy_stream=None, device=None):
+    B, k = ids.shape
+    n_chunks, Hkv, d = k_bar.shape
+    dev = device if device is not None else ids.device
+    if k_ctx is None:
+        k_ctx = torch.empty((B, max_ctx, Hkv, d), dtype=k_bar.dtype, device=dev)
+    if v_ctx is None:
+        v_ctx = torch.empty((B, max_ctx, Hkv, d), dtype=v_bar.dtype, device=dev)
+    if ctx_pos is None:
+        ctx_pos = torch.empty((B, max_ctx), dtype=torch.int32, device=dev)
+    if ctx_len is None:
+        ctx_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if src_mode == MSA_SRC_HOST_MEMCPY and ids_h is None:
+        ids_h = torch.empty((B, k), dtype=torch.int32, pin_memory=True)
+    _check("msa_gather_kv", lib.msa_gather_kv(
+        _dtype(k_bar), _ptr(ids), B, k, _ptr(chunk_off), _ptr(chunk_off_h), chunk_off.numel() - 1,
+        max_doc_chunks, _ptr(k_bar), _ptr(v_bar), n_chunks, Hkv, d, src_mode, max_ctx, _ptr(k_ctx),
+        _ptr(v_ctx), _ptr(ctx_pos), _ptr(ctx_len), _ptr(ids_h), _stream(stream),
+        None if copy_stream is None else _stream(copy_stream)))
+    return k_ctx, v_ctx, ctx_pos, ctx_len
+
+
+def msa_sparse_attn_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset):
+    return lib.msa_sparse_attn_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset)
+
+
+def msa_sparse_attn(q, k_ctx, v_ctx, ctx_pos, ctx_len, k_loc, v_loc, q_pos_offset, rope_base=1e6,
+                    sm_scale=None, out=None, ws=None, stream=None):
+    B, T, Hq, d = q.shape
+    max_ctx, Hkv = k_ctx.shape[1], k_ctx.shape[2]
+    L_loc = k_loc.shape[1]
+    dt = _dtype(q)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
+    ws, wsb = _ws(msa_sparse_attn_workspace(dt, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset), q.device, ws)
+    _check("msa_sparse_attn", lib.msa_sparse_attn(
+        dt, _ptr(q), B, T, Hq, Hkv, d, _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_pos), _ptr(ctx_len), max_ctx,
+        _ptr(k_loc), _ptr(v_loc), L_loc, q_pos_offset, float(rope_base), float(sm_scale), _ptr(out),
+        _ptr(ws), wsb, _stream(stream)))
+    return out

@@ -1,0 +1,505 @@
+// Stage 3 sparse attention over [retrieved pooled K/V ; local K/V] with
+// document-wise RoPE applied on the fly.
+// (MSA README, Overall Design > Architecture: the selected compressed K/V
+//  are concatenated with the query's local K/V for autoregressive decoding;
+//  "Parallel (document-wise) RoPE": every document restarts at position 0;
+//  "Global RoPE (active context)": the query starts at index k.  Paper note,
+//  Document-wise RoPE.)
+//
+// Keys of query b: context entries e < ctx_len[b] (position ctx_pos[b,e],
+// visible to every token) then local tokens i < L_loc (position
+// q_pos_offset + i, causal: token t sees i <= L_loc - T + t).
+//
+// bf16 path (d = 128): flash-decoding.  One wave owns (query b, KV head g,
+// 16 query rows = (token, head-in-group) pairs, one key split).  Per step of
+// 32 keys: K rows are the A operand of v_mfma_f32_16x16x32_bf16 (loaded
+// from HBM, rotated in registers), the rotated query the B operand, giving
+// S^T[key][row]; the online softmax runs per column (one lane per row);
+// P^T goes straight from the accumulator into the B operand of the PV
+// product O^T = V^T P^T, whose A operand is the V tile transposed through
+// LDS.  Splits are merged by a combine kernel.  RoPE angles come from a
+// cos/sin table computed in float64 per call.
+#include <algorithm>
+
+#include "common.h"
+
+namespace msa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int AT_D = 128;
+constexpr int AT_WAVES = 4;
+constexpr int AT_THREADS = 64 * AT_WAVES;
+constexpr int AT_VT_STRIDE = 80;                  // bytes per d-row of the transposed V tile (32 keys + pad, 16-byte aligned)
+constexpr int AT_VT_BYTES = AT_D * AT_VT_STRIDE;  // per wave
+constexpr int AT_VEC_THREADS = 256;
+constexpr int AT_VEC_MAX_KEYS = 32768;
+
+// tab[p][m] = (cos, sin)(p * base^(-2m/d)), angle formed and reduced in float64
+__global__ void rope_table_kernel(float2* __restrict__ tab, int P, int half, double base, int d) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(P) * half) return;
+  const int p = int(i / half), m = int(i % half);
+  const double theta = pow(base, -2.0 * double(m) / double(d));
+  double sn, cs;
+  sincos(double(p) * theta, &sn, &cs);
+  tab[i] = make_float2(float(cs), float(sn));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ void unpack8(const uint4& u, float (&x)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(w[e] << 16);
+    x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&x)[8]) {
+  return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                    pack_bf16x2(x[6], x[7]));
+}
+
+// Rotate the lane's 16 (m, m + 64) pairs: lo[kk] holds dims 32kk + 8*g4 + e,
+// hi[kk] dims 64 + 32kk + 8*g4 + e (kk = 0, 1).  cs points at tab[pos][0].
+__device__ __forceinline__ void rope_rotate(uint4 (&v)[4], const float2* __restrict__ cs, int g4) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    float lo[8], hi[8];
+    unpack8(v[kk], lo);
+    unpack8(v[kk + 2], hi);
+    const float4* c4 = reinterpret_cast<const float4*>(cs + 32 * kk + 8 * g4);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float4 t = c4[e2];  // (cos, sin) of two consecutive m
+      const float c0 = t.x, s0 = t.y, c1 = t.z, s1 = t.w;
+      const float a0 = lo[2 * e2], b0 = hi[2 * e2], a1 = lo[2 * e2 + 1], b1 = hi[2 * e2 + 1];
+      lo[2 * e2] = a0 * c0 - b0 * s0;
+      hi[2 * e2] = b0 * c0 + a0 * s0;
+      lo[2 * e2 + 1] = a1 * c1 - b1 * s1;
+      hi[2 * e2 + 1] = b1 * c1 + a1 * s1;
+    }
+    v[kk] = pack8(lo);
+    v[kk + 2] = pack8(hi);
+  }
+}
+
+struct KeySrc {
+  int64_t row;   // row index into the [*, Hkv, d] tensor (already including b)
+  int pos;
+  bool local;
+  bool valid;
+};
+
+__device__ __forceinline__ KeySrc key_src(int j, int b, int ctxl, int n_keys, int max_ctx, int L_loc, int qpo,
+                                          const int32_t* __restrict__ ctx_pos, int P) {
+  KeySrc k;
+  if (j < ctxl) {
+    k.row = int64_t(b) * max_ctx + j;
+    int p = ctx_pos[int64_t(b) * max_ctx + j];
+    k.pos = p < 0 ? 0 : (p >= P ? P - 1 : p);
+    k.local = false;
+    k.valid = true;
+  } else if (j < n_keys) {
+    const int li = j - ctxl;
+    k.row = int64_t(b) * L_loc + li;
+    k.pos = qpo + li;
+    k.local = true;
+    k.valid = true;
+  } else {
+    k.row = int64_t(b) * L_loc;  // any finite row; its weight is zero
+    k.pos = 0;
+    k.local = true;
+    k.valid = false;
+  }
+  return k;
+}
+
+template <int G>
+__global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
+    const uint16_t* __restrict__ q, int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_ctx,
+    const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
+    int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
+    const float2* __restrict__ tab, int P, float scale_log2, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
+    int n_splits, int keys_per_split, int n_rt) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int lc = lane % 16, g4 = lane / 16;
+  unsigned char* vt = smem + size_t(wave) * AT_VT_BYTES;
+
+  int64_t gw = int64_t(blockIdx.x) * AT_WAVES + wave;
+  const int split = int(gw % n_splits);
+  gw /= n_splits;
+  const int rt = int(gw % n_rt);
+  gw /= n_rt;
+  const int g = int(gw % Hkv);
+  const int b = int(gw / Hkv);
+  if (b >= B) return;
+
+  // query row of this lane's column
+  const int r = rt * 16 + lc;
+  const int t = r / G, hh = r % G;
+  const bool row_ok = t < T;
+  const int hq = g * G + hh;
+  const int horizon = L_loc - T + t;  // last visible local index for this row
+  const int64_t kv_stride = int64_t(Hkv) * AT_D;
+
+  bf16x8 bq[4];
+  {
+    uint4 qv[4];
+    const int tt = row_ok ? t : 0;
+    const uint16_t* qp = q + ((int64_t(b) * T + tt) * Hq + hq) * AT_D + 8 * g4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qv[kk] = *reinterpret_cast<const uint4*>(qp + 32 * kk);
+    int pq = qpo + L_loc - T + tt;
+    pq = pq < 0 ? 0 : (pq >= P ? P - 1 : pq);
+    rope_rotate(qv, tab + int64_t(pq) * (AT_D / 2), g4);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) bq[kk] = __builtin_bit_cast(bf16x8, row_ok ? qv[kk] : make_uint4(0, 0, 0, 0));
+  }
+
+  const int ctxl = ctx_len[b];
+  const int n_keys = ctxl + L_loc;
+  const int j_begin = split * keys_per_split;
+  const int j_end = min(n_keys, j_begin + keys_per_split);
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int j0 = j_begin; j0 < j_end; j0 += 32) {
+    // ---- S^T = K_rot . Q_rot^T for two 16-key tiles
+    f32x4 s[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const KeySrc ks = key_src(j0 + 16 * tau + lc, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+      const uint16_t* kp = (ks.local ? k_loc : k_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 8 * g4;
+      uint4 kv[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kv[kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
+      rope_rotate(kv, tab + int64_t(ks.pos) * (AT_D / 2), g4);
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv[kk]), bq[kk], acc, 0, 0, 0);
+      s[tau] = acc;
+    }
+    // ---- mask and online softmax for column lc (base-2 domain)
+    float x[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kj = j0 + 16 * tau + 4 * g4 + i;
+        const bool vis = row_ok && kj < j_end && (kj < ctxl || kj - ctxl <= horizon);
+        x[tau][i] = vis ? s[tau][i] * scale_log2 : -INFINITY;
+        mt = fmaxf(mt, x[tau][i]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float psum = 0.f;
+    float p[2][4];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[tau][i] = exp2f(x[tau][i] - m_use);
+        psum += p[tau][i];
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    const bf16x8 pb = __builtin_bit_cast(
+        bf16x8, make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                           pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])));
+
+    // ---- V tile -> LDS, transposed: vt[d][slot], slot 8*g + 4*tau + i <-> key 16*tau + 4*g + i
+#pragma unroll
+    for (int rho = 0; rho < 2; ++rho) {
+      uint4 vv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const KeySrc ks = key_src(j0 + 16 * rho + 4 * g4 + i, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+        const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 8 * lc;
+        vv[i] = *reinterpret_cast<const uint4*>(vp);
+      }
+      const uint32_t w0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
+      const uint32_t w1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+      const uint32_t w2[4] = {vv[2].x, vv[2].y, vv[2].z, vv[2].w};
+      const uint32_t w3[4] = {vv[3].x, vv[3].y, vv[3].z, vv[3].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) ? 16 : 0;
+        const uint32_t a0 = (w0[e / 2] >> sh) & 0xFFFFu, a1 = (w1[e / 2] >> sh) & 0xFFFFu;
+        const uint32_t a2 = (w2[e / 2] >> sh) & 0xFFFFu, a3 = (w3[e / 2] >> sh) & 0xFFFFu;
+        uint2 pk = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+        *reinterpret_cast<uint2*>(vt + (8 * lc + e) * AT_VT_STRIDE + 2 * (8 * g4 + 4 * rho)) = pk;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // ---- O^T += V^T . P^T
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint4 a = *reinterpret_cast<const uint4*>(vt + (16 * dt + lc) * AT_VT_STRIDE + 16 * g4);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- partial result of this split: O^T[d = 16dt + 4*g4 + i][row lc]
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const int64_t rowid = ((int64_t(split) * B + b) * T + t) * Hq + hq;
+  float* op = ws_o + rowid * AT_D;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<float4*>(op + 16 * dt + 4 * g4) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  if (g4 == 0) ws_ml[rowid] = make_float2(m_run, l_run);
+}
+
+// out[b,t,hq,:] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s
+__global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, int n_splits,
+                                    int64_t rows, int d, float* __restrict__ out) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= rows * d) return;
+  const int64_t row = i / d;
+  const int e = int(i % d);
+  float m = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) m = fmaxf(m, ws_ml[s * rows + row].x);
+  const float mu = m == -INFINITY ? 0.f : m;
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < n_splits; ++s) {
+    const float2 ml = ws_ml[s * rows + row];
+    if (ml.y == 0.f) continue;
+    const float w = exp2f(ml.x - mu);
+    den += w * ml.y;
+    num += w * ws_o[(s * rows + row) * d + e];
+  }
+  out[i] = den > 0.f ? num / den : 0.f;
+}
+
+// Vector path (float32 or any even d): one workgroup per (b, t, hq); the
+// logits of every visible key are formed in float32, then the softmax and
+// the value sum.
+template <int DT>
+__global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
+    const typename Elem<DT>::T* __restrict__ q, int B, int T, int Hq, int Hkv, int d,
+    const typename Elem<DT>::T* __restrict__ k_ctx, const typename Elem<DT>::T* __restrict__ v_ctx,
+    const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len, int max_ctx,
+    const typename Elem<DT>::T* __restrict__ k_loc, const typename Elem<DT>::T* __restrict__ v_loc, int L_loc,
+    int qpo, const float2* __restrict__ tab, int P, float sm_scale, float* __restrict__ out) {
+  using E = Elem<DT>;
+  extern __shared__ float vsm[];
+  float* qr = vsm;               // [d]
+  float* red = vsm + d;          // [AT_VEC_THREADS]
+  float* logit = red + AT_VEC_THREADS;
+  const int hq = blockIdx.x % Hq;
+  const int t = (blockIdx.x / Hq) % T;
+  const int b = blockIdx.x / (Hq * T);
+  const int G = Hq / Hkv, g = hq / G, half = d / 2;
+  const int horizon = L_loc - T + t;
+  int pq = qpo + L_loc - T + t;
+  pq = pq < 0 ? 0 : (pq >= P ? P - 1 : pq);
+  const typename E::T* qp = q + ((int64_t(b) * T + t) * Hq + hq) * d;
+  for (int m = threadIdx.x; m < half; m += AT_VEC_THREADS) {
+    const float2 cs = tab[int64_t(pq) * half + m];
+    const float x1 = E::load(qp, m), x2 = E::load(qp, m + half);
+    qr[m] = x1 * cs.x - x2 * cs.y;
+    qr[m + half] = x2 * cs.x + x1 * cs.y;
+  }
+  __syncthreads();
+  const int ctxl = ctx_len[b];
+  const int n_keys = ctxl + L_loc;
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j < n_keys; j += AT_VEC_THREADS) {
+    const typename E::T* kp;
+    int pos;
+    bool vis = true;
+    if (j < ctxl) {
+      kp = k_ctx + ((int64_t(b) * max_ctx + j) * Hkv + g) * d;
+      pos = ctx_pos[int64_t(b) * max_ctx + j];
+      pos = pos < 0 ? 0 : (pos >= P ? P - 1 : pos);
+    } else {
+      const int li = j - ctxl;
+      kp = k_loc + ((int64_t(b) * L_loc + li) * Hkv + g) * d;
+      pos = qpo + li;
+      vis = li <= horizon;
+    }
+    float lg = -INFINITY;
+    if (vis) {
+      float dot = 0.f;
+      const float2* cs = tab + int64_t(pos) * half;
+      for (int m = 0; m < half; ++m) {
+        const float k1 = E::load(kp, m), k2 = E::load(kp, m + half);
+        const float2 c = cs[m];
+        dot += qr[m] * (k1 * c.x - k2 * c.y) + qr[m + half] * (k2 * c.x + k1 * c.y);
+      }
+      lg = dot * sm_scale;
+    }
+    logit[j] = lg;
+    mx = fmaxf(mx, lg);
+  }
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int st = AT_VEC_THREADS / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + st]);
+    __syncthreads();
+  }
+  const float gmax = red[0];
+  __syncthreads();
+  float sum = 0.f;
+  for (int j = threadIdx.x; j < n_keys; j += AT_VEC_THREADS) {
+    const float p = logit[j] == -INFINITY ? 0.f : expf(logit[j] - gmax);
+    logit[j] = p;
+    sum += p;
+  }
+  red[threadIdx.x] = sum;
+  __syncthreads();
+  for (int st = AT_VEC_THREADS / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  const float den = red[0];
+  float* op = out + ((int64_t(b) * T + t) * Hq + hq) * d;
+  for (int e = threadIdx.x; e < d; e += AT_VEC_THREADS) {
+    float acc = 0.f;
+    for (int j = 0; j < n_keys; ++j) {
+      const float p = logit[j];
+      if (p == 0.f) continue;
+      const typename E::T* vp = j < ctxl ? v_ctx + ((int64_t(b) * max_ctx + j) * Hkv + g) * d
+                                         : v_loc + ((int64_t(b) * L_loc + (j - ctxl)) * Hkv + g) * d;
+      acc += p * E::load(vp, e);
+    }
+    op[e] = acc / den;
+  }
+}
+
+struct AttnPlan {
+  bool mfma;
+  int P;            // rows of the RoPE table
+  int n_rt;         // 16-row tiles per (b, g)
+  int n_splits;
+  int keys_per_split;
+  size_t tab_bytes, o_bytes, ml_bytes;
+};
+
+static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc, int qpo) {
+  AttnPlan p{};
+  const int G = Hkv > 0 ? Hq / Hkv : 0;
+  p.mfma = dtype == MSA_BF16 && d == AT_D && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+  p.P = std::max(qpo + L_loc, max_ctx);
+  p.tab_bytes = align_up(size_t(p.P) * (d / 2) * sizeof(float2), 256);
+  if (!p.mfma) return p;
+  p.n_rt = (T * G + 15) / 16;
+  const int64_t n_keys_max = int64_t(max_ctx) + L_loc;
+  const int64_t units = int64_t(B) * Hkv * p.n_rt;
+  int64_t s = (4096 + units - 1) / units;
+  s = std::max<int64_t>(1, std::min<int64_t>(s, (n_keys_max + 63) / 64));
+  int64_t kps = (n_keys_max + s - 1) / s;
+  kps = (kps + 31) / 32 * 32;
+  p.keys_per_split = int(kps);
+  p.n_splits = int((n_keys_max + kps - 1) / kps);
+  const int64_t rows = int64_t(B) * T * Hq;
+  p.o_bytes = align_up(size_t(p.n_splits) * rows * d * sizeof(float), 256);
+  p.ml_bytes = align_up(size_t(p.n_splits) * rows * sizeof(float2), 256);
+  return p;
+}
+
+}  // namespace msa
+
+extern "C" size_t msa_sparse_attn_workspace(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc,
+                                            int q_pos_offset) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 2 || max_ctx < 0 || L_loc < 1 || q_pos_offset < 0) return 0;
+  const msa::AttnPlan p = msa::attn_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
+  return p.tab_bytes + p.o_bytes + p.ml_bytes;
+}
+
+extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d, const void* k_ctx,
+                               const void* v_ctx, const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx,
+                               const void* k_loc, const void* v_loc, int L_loc, int q_pos_offset, float rope_base,
+                               float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  using namespace msa;
+  MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, "msa_sparse_attn: bad dtype");
+  MSA_REQUIRE(q && k_ctx && v_ctx && ctx_pos && ctx_len && k_loc && v_loc && out && ws, MSA_ERR_INVALID_ARG,
+              "msa_sparse_attn: NULL pointer");
+  MSA_REQUIRE(B >= 1 && T >= 1 && Hq >= 1 && Hkv >= 1 && d >= 2 && max_ctx >= 1 && L_loc >= 1, MSA_ERR_INVALID_ARG,
+              "msa_sparse_attn: non-positive size");
+  MSA_REQUIRE(Hq % Hkv == 0, MSA_ERR_INVALID_ARG, "msa_sparse_attn: Hq % Hkv != 0");
+  MSA_REQUIRE(L_loc >= T, MSA_ERR_INVALID_ARG, "msa_sparse_attn: L_loc < T");
+  MSA_REQUIRE(d % 2 == 0, MSA_ERR_INVALID_ARG, "msa_sparse_attn: d must be even");
+  MSA_REQUIRE(q_pos_offset >= 0, MSA_ERR_INVALID_ARG, "msa_sparse_attn: q_pos_offset < 0");
+  MSA_REQUIRE(rope_base > 1.f, MSA_ERR_INVALID_ARG, "msa_sparse_attn: rope_base must exceed 1");
+  MSA_REQUIRE(d <= 256, MSA_ERR_UNSUPPORTED, "msa_sparse_attn: d > 256");
+  MSA_REQUIRE(int64_t(q_pos_offset) + L_loc < (int64_t(1) << 30), MSA_ERR_UNSUPPORTED, "msa_sparse_attn: positions too large");
+  const AttnPlan p = attn_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
+  MSA_REQUIRE(ws_bytes >= p.tab_bytes + p.o_bytes + p.ml_bytes, MSA_ERR_WORKSPACE, "msa_sparse_attn: workspace too small");
+  if (!p.mfma)
+    MSA_REQUIRE(int64_t(max_ctx) + L_loc <= AT_VEC_MAX_KEYS, MSA_ERR_UNSUPPORTED,
+                "msa_sparse_attn: more than 32768 keys on the vector path");
+  hipStream_t s = as_stream(stream);
+  float2* tab = static_cast<float2*>(ws);
+  {
+    const int64_t n = int64_t(p.P) * (d / 2);
+    hipLaunchKernelGGL(rope_table_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, tab, p.P, d / 2,
+                       double(rope_base), d);
+    MSA_LAUNCH_CHECK();
+  }
+  if (p.mfma) {
+    MSA_REQUIRE(uintptr_t(q) % 16 == 0 && uintptr_t(k_ctx) % 16 == 0 && uintptr_t(v_ctx) % 16 == 0 &&
+                    uintptr_t(k_loc) % 16 == 0 && uintptr_t(v_loc) % 16 == 0,
+                MSA_ERR_INVALID_ARG, "msa_sparse_attn: tensors must be 16-byte aligned");
+    float* ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.tab_bytes);
+    float2* ws_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.tab_bytes + p.o_bytes);
+    const int G = Hq / Hkv;
+    const int64_t waves = int64_t(B) * Hkv * p.n_rt * p.n_splits;
+    const dim3 grid(unsigned((waves + AT_WAVES - 1) / AT_WAVES)), block(AT_THREADS);
+    const size_t smem = size_t(AT_WAVES) * AT_VT_BYTES;
+    const float scale_log2 = sm_scale * 1.4426950408889634f;
+#define AT_LAUNCH(GV)                                                                                            \
+  hipLaunchKernelGGL((attn_mfma_kernel<GV>), grid, block, smem, s, static_cast<const uint16_t*>(q), B, T, Hq, Hkv, \
+                     static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos, ctx_len,  \
+                     max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc), L_loc,    \
+                     q_pos_offset, tab, p.P, scale_log2, ws_o, ws_ml, p.n_splits, p.keys_per_split, p.n_rt)
+    switch (G) {
+      case 1: AT_LAUNCH(1); break;
+      case 2: AT_LAUNCH(2); break;
+      case 4: AT_LAUNCH(4); break;
+      case 8: AT_LAUNCH(8); break;
+      default: AT_LAUNCH(16); break;
+    }
+#undef AT_LAUNCH
+    MSA_LAUNCH_CHECK();
+    const int64_t rows = int64_t(B) * T * Hq;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * d + 255) / 256)), dim3(256), 0, s, ws_o, ws_ml,
+                       p.n_splits, rows, d, out);
+    MSA_LAUNCH_CHECK();
+    return MSA_OK;
+  }
+  const size_t smem = (size_t(d) + AT_VEC_THREADS + size_t(max_ctx) + L_loc) * sizeof(float);
+  const dim3 grid(unsigned(int64_t(B) * T * Hq)), block(AT_VEC_THREADS);
+  if (dtype == MSA_BF16)
+    hipLaunchKernelGGL(attn_vec_kernel<MSA_BF16>, grid, block, smem, s, static_cast<const uint16_t*>(q), B, T, Hq, Hkv,
+                       d, static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos, ctx_len,
+                       max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc), L_loc,
+                       q_pos_offset, tab, p.P, sm_scale, out);
+  else
+    hipLaunchKernelGGL(attn_vec_kernel<MSA_F32>, grid, block, smem, s, static_cast<const float*>(q), B, T, Hq, Hkv, d,
+                       static_cast<const float*>(k_ctx), static_cast<const float*>(v_ctx), ctx_pos, ctx_len, max_ctx,
+                       static_cast<const float*>(k_loc), static_cast<const float*>(v_loc), L_loc, q_pos_offset, tab,
+                       p.P, sm_scale, out);
+  MSA_LAUNCH_CHECK();
+  return MSA_OK;
+}

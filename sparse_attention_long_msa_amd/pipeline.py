@@ -1,0 +1,81 @@
+"""Per-layer driver of the routing + sparse-attention path.
+
+One routed layer runs route score -> top-k -> context assembly -> sparse
+attention on one stream (README, Inference Pipeline: Online Routing & Context
+Assembly, then Sparse Generation; routing happens in every upper-half layer,
+each with its own routing-key store).  ``LayerRunner`` owns the per-layer
+outputs and workspaces so a loop over layers allocates nothing.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _binding as B
+
+
+class LayerRunner:
+    def __init__(self, *, batch, tokens, q_heads, kv_heads, head_dim, n_docs, n_chunks, k, max_doc_chunks,
+                 local_len, dtype, device, q_pos_offset=None, rope_base=1e6, sm_scale=None,
+                 src_mode=B.MSA_SRC_DEVICE, chunk_off_h=None):
+        self.B, self.T, self.Hq, self.Hkv, self.d = batch, tokens, q_heads, kv_heads, head_dim
+        self.n_docs, self.n_chunks, self.k = n_docs, n_chunks, k
+        self.max_doc_chunks = max_doc_chunks
+        self.max_ctx = k * max_doc_chunks
+        self.L_loc = local_len
+        self.q_pos_offset = k if q_pos_offset is None else q_pos_offset
+        self.rope_base = rope_base
+        self.sm_scale = 1.0 / math.sqrt(head_dim) if sm_scale is None else sm_scale
+        self.src_mode = src_mode
+        self.chunk_off_h = chunk_off_h
+        self.dtype = dtype
+        dt = B.MSA_BF16 if dtype == torch.bfloat16 else B.MSA_F32
+        dev = torch.device(device)
+        f32, i32 = torch.float32, torch.int32
+        self.doc_score = torch.empty((batch, n_docs), dtype=f32, device=dev)
+        self.ids = torch.empty((batch, k), dtype=i32, device=dev)
+        self.vals = torch.empty((batch, k), dtype=f32, device=dev)
+        self.k_ctx = torch.empty((batch, self.max_ctx, kv_heads, head_dim), dtype=dtype, device=dev)
+        self.v_ctx = torch.empty_like(self.k_ctx)
+        self.ctx_pos = torch.empty((batch, self.max_ctx), dtype=i32, device=dev)
+        self.ctx_len = torch.empty((batch,), dtype=i32, device=dev)
+        self.out = torch.empty((batch, tokens, q_heads, head_dim), dtype=f32, device=dev)
+
+        def ws(n):
+            return torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+
+        self.rs_ws = ws(B.msa_route_score_workspace(dt, batch, tokens, kv_heads, head_dim, n_docs, n_chunks))
+        self.tk_ws = ws(B.msa_topk_workspace(batch, n_docs, k))
+        self.at_ws = ws(B.msa_sparse_attn_workspace(dt, batch, tokens, q_heads, kv_heads, head_dim, self.max_ctx,
+                                                    local_len, self.q_pos_offset))
+        self.ids_h = None
+        self.copy_stream = None
+        if src_mode == B.MSA_SRC_HOST_MEMCPY:
+            self.ids_h = torch.empty((batch, k), dtype=i32, pin_memory=True)
+            self.copy_stream = torch.cuda.Stream(device=dev)
+
+    def route(self, q_r, kr_hat, chunk_doc, stream=None):
+        B.msa_route_score(q_r, kr_hat, chunk_doc, self.n_docs, doc_score=self.doc_score, ws=self.rs_ws,
+                          stream=stream)
+        return self.doc_score
+
+    def select(self, stream=None):
+        B.msa_topk(self.doc_score, self.k, ids=self.ids, vals=self.vals, ws=self.tk_ws, stream=stream)
+        return self.ids, self.vals
+
+    def assemble(self, chunk_off, k_bar, v_bar, stream=None):
+        B.msa_gather_kv(self.ids, chunk_off, k_bar, v_bar, self.max_doc_chunks, self.max_ctx, self.src_mode,
+                        chunk_off_h=self.chunk_off_h, k_ctx=self.k_ctx, v_ctx=self.v_ctx, ctx_pos=self.ctx_pos,
+                        ctx_len=self.ctx_len, ids_h=self.ids_h, stream=stream, copy_stream=self.copy_stream)
+
+    def attend(self, q, k_loc, v_loc, stream=None):
+        B.msa_sparse_attn(q, self.k_ctx, self.v_ctx, self.ctx_pos, self.ctx_len, k_loc, v_loc, self.q_pos_offset,
+                          self.rope_base, self.sm_scale, out=self.out, ws=self.at_ws, stream=stream)
+        return self.out
+
+    def run(self, q_r, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc, stream=None):
+        self.route(q_r, kr_hat, chunk_doc, stream)
+        self.select(stream)
+        self.assemble(chunk_off, k_bar, v_bar, stream)
+        return self.attend(q, k_loc, v_loc, stream)

@@ -1,0 +1,117 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every symbol include/msa.h declares, and rejects invalid calls with the
+documented status before touching the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_attention_long_msa_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    txt = open(os.path.join(ROOT, "include", "msa.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert len(syms) >= 13
+    h = ctypes.CDLL(M.lib_path)
+    for s in syms:
+        assert hasattr(h, s), s
+
+
+def test_abi_version_and_status_strings():
+    assert M.msa_abi_version() == 1
+    assert M.lib.msa_status_string(0).decode() == "ok"
+    assert "workspace" in M.lib.msa_status_string(3).decode()
+
+
+def test_chunk_offsets_host_matches_oracle():
+    r = np.random.default_rng(0)
+    lens = r.integers(0, 700, size=300)
+    lens[::17] = 0
+    tok_off = np.concatenate([[0], np.cumsum(lens)])
+    for chunk in (1, 7, 64):
+        np.testing.assert_array_equal(M.msa_chunk_offsets(tok_off, chunk), O.chunk_offsets(tok_off, chunk))
+
+
+@pytest.mark.parametrize("bad", [[1, 5], [0, 5, 3]])
+def test_chunk_offsets_rejects_bad_offsets(bad):
+    with pytest.raises(M.MsaError) as e:
+        M.msa_chunk_offsets(bad, 64)
+    assert e.value.status == 1
+
+
+P = ctypes.c_void_p(16)   # a non-null dummy; validation fails before any dereference
+
+
+def test_route_score_validation():
+    L = M.lib
+    assert L.msa_route_score(1, None, 1, 1, 8, 128, P, P, 4, 4, P, None, 0, None) == 1
+    assert L.msa_route_score(1, P, 0, 1, 8, 128, P, P, 4, 4, P, None, 0, None) == 1
+    assert L.msa_route_score(7, P, 1, 1, 8, 128, P, P, 4, 4, P, None, 0, None) == 1
+    assert L.msa_route_score(1, P, 1, 1, 8, 260, P, P, 4, 4, P, None, 0, None) == 2
+    # float32 needs a workspace for the column norms
+    need = L.msa_route_score_workspace(0, 1, 16, 8, 128, 4, 4)
+    assert need >= 16 * 8 * 4
+    assert L.msa_route_score(0, P, 1, 16, 8, 128, P, P, 4, 4, P, P, need - 1, None) == 3
+
+
+def test_topk_validation():
+    L = M.lib
+    assert L.msa_topk(P, 1, 10, 0, P, P, P, 1 << 20, None) == 1
+    assert L.msa_topk(P, 1, 10, 11, P, P, P, 1 << 20, None) == 1
+    assert L.msa_topk(P, 1, 1000, 300, P, P, P, 1 << 30, None) == 2
+    need = L.msa_topk_workspace(1, 100000, 16)
+    assert need > 0
+    assert L.msa_topk(P, 1, 100000, 16, P, P, P, need - 1, None) == 3
+    assert L.msa_topk_workspace(1, 4096, 16) == 0      # one slice: no workspace
+
+
+def test_gather_rejects_small_context_and_bad_mode():
+    L = M.lib
+    # max_ctx (31) < k * max_doc_chunks (32)
+    assert L.msa_gather_kv(1, P, 2, 4, P, None, 10, 8, P, P, 80, 8, 128, 0, 31, P, P, P, P, None, None, None) == 1
+    assert L.msa_gather_kv(1, P, 2, 4, P, None, 10, 8, P, P, 80, 8, 128, 9, 32, P, P, P, P, None, None, None) == 2
+    assert L.msa_gather_kv(1, P, 2, 11, P, None, 10, 8, P, P, 80, 8, 128, 0, 88, P, P, P, P, None, None, None) == 1
+    # host-memcpy mode needs the host offsets and the pinned id staging
+    assert L.msa_gather_kv(1, P, 2, 4, P, None, 10, 8, P, P, 80, 8, 128, 2, 32, P, P, P, P, None, None, None) == 1
+
+
+def test_sparse_attn_validation():
+    L = M.lib
+    base = dict(dtype=1, q=P, B=1, T=4, Hq=32, Hkv=8, d=128, kc=P, vc=P, cp=P, cl=P, max_ctx=16, kl=P, vl=P,
+                L=8, qpo=4, base=1e6, scale=0.088, out=P, ws=P, wsb=1 << 30, s=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.msa_sparse_attn(a["dtype"], a["q"], a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["kc"], a["vc"],
+                                 a["cp"], a["cl"], a["max_ctx"], a["kl"], a["vl"], a["L"], a["qpo"], a["base"],
+                                 a["scale"], a["out"], a["ws"], a["wsb"], a["s"])
+    assert call(Hq=30) == 1          # Hq % Hkv
+    assert call(L=3) == 1            # L_loc < T
+    assert call(d=127) == 1          # odd head dim
+    assert call(qpo=-1) == 1
+    assert call(d=512) == 2
+    assert call(q=None) == 1
+    assert call(wsb=16) == 3
+    assert L.msa_sparse_attn_workspace(1, 1, 4, 32, 8, 128, 16, 8, 4) > 0
+
+
+def test_pool_and_docmap_validation():
+    L = M.lib
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 128, 0, 1, P, None) == 1     # chunk 0
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 127, 64, 1, P, None) == 1    # odd d
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 64, 128, 64, 1, P, None) == 2   # H*d > 4096
+    assert L.msa_chunk_doc_map(None, 4, 8, P, None) == 1
+    assert L.msa_chunk_doc_map(P, 0, 8, P, None) == 1
+    assert M.lib.msa_last_error().decode() != ""

@@ -1,0 +1,180 @@
+"""Stage parity on the GPU: every msa_* call against the oracle's same step,
+fed the same seeded inputs, at sizes that span several tiles, ragged
+documents, empty documents and partial chunks."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.helpers import (ATOL_ATTN, RTOL_SCORE, check_ids, check_scores, dev, gen, host, ragged_lengths,
+                           to_dev, to_dev_i64)
+
+pytestmark = pytest.mark.gpu
+
+M = pytest.importorskip("sparse_attention_long_msa_amd")
+
+
+def _doc_index(lengths, chunk):
+    tok_off = synth.offsets(lengths)
+    chunk_off = O.chunk_offsets(tok_off, chunk)
+    n_chunks = int(chunk_off[-1])
+    co_d = to_dev_i64(chunk_off)
+    cd = M.msa_chunk_doc_map(co_d, n_chunks)
+    return tok_off, chunk_off, n_chunks, co_d, cd
+
+
+def test_synth_device_matches_host():
+    from synth import device as SD
+    for bf16, start, n, sp in ((True, 0, 100003, 0), (False, 12345678901, 4099, 0), (True, 7, 5000, -3)):
+        t = torch.empty(n, dtype=torch.bfloat16 if bf16 else torch.float32, device=dev())
+        SD.fill(t, 1234, 3, synth.T_KR, start=start, scale_pow2=sp)
+        want = synth.normal(1234, synth.stream_id(3, synth.T_KR), start, n, bf16=bf16, scale_pow2=sp)
+        got = t.float().cpu().numpy()
+        np.testing.assert_array_equal(got, want)
+
+
+def test_chunk_doc_map():
+    lens = ragged_lengths(1, 500, 0, 300, n_empty=40)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    want = np.repeat(np.arange(500), np.diff(chunk_off))
+    np.testing.assert_array_equal(cd.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("normalize", [False, True])
+@pytest.mark.parametrize("chunk", [64, 1, 5])
+def test_pool_encode(bf16, normalize, chunk):
+    H, d = 8, 128
+    lens = ragged_lengths(2, 37, 0, 400, n_empty=3)
+    lens[0] = 130                                    # two full chunks and a partial one
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, chunk)
+    x = gen(11, 0, synth.T_KR, (int(lens.sum()), H, d), bf16)
+    out = M.msa_pool_encode(to_dev(x, bf16), to_dev_i64(tok_off), co_d, cd, chunk, normalize)
+    ref = O.pool_encode(x, tok_off, chunk, normalize, "bf16" if bf16 else "f32")
+    got = host(out)
+    if bf16:
+        # float32 accumulation may move the once-rounded result by one bf16 ulp
+        ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+        assert np.all(np.abs(got - ref) <= ulp + 1e-30)
+        assert np.mean(got == ref) > 0.99
+    else:
+        np.testing.assert_allclose(got, ref, rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("B,T", [(1, 64), (1, 16), (1, 1), (2, 32), (32, 1), (1, 128), (3, 7), (1, 80)])
+def test_route_score(bf16, B, T):
+    H, d = 8, 128
+    lens = ragged_lengths(3 + T, 180, 1, 1500, n_empty=5)
+    while ((lens + 63) // 64).sum() % 32 == 0:
+        lens[-1] += 64
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    assert n_chunks % 32 != 0 and n_chunks > 32 * 40            # many tiles and a ragged tail
+    dt = "bf16" if bf16 else "f32"
+    raw = gen(21, 0, synth.T_KR, (n_chunks, H, d), bf16)
+    store = O.round_to_store(O.l2_normalize(raw.astype(np.float64)), dt)
+    q = gen(22, 0, synth.T_QR, (B, T, H, d), bf16)
+    # plant a needle: one chunk of document 17 is the first query token itself
+    nd = 17
+    store[chunk_off[nd]] = O.round_to_store(O.l2_normalize(q[0, 0].astype(np.float64)), dt)
+    ds = M.msa_route_score(to_dev(q, bf16), to_dev(store, bf16), cd, len(lens))
+    ref = O.route_scores(q, store, chunk_off)
+    got = host(ds)
+    err = check_scores(got, ref, RTOL_SCORE[dt], k=16)
+    print(f"route_score {dt} B={B} T={T}: normwise err {err:.3g}")
+    assert np.argmax(got[0]) == nd
+
+
+def test_route_score_rescale_invariance():
+    """Cosine is invariant to a positive rescale of the routing query."""
+    H, d = 8, 128
+    lens = ragged_lengths(5, 64, 64, 640)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    store = O.round_to_store(O.l2_normalize(gen(31, 0, synth.T_KR, (n_chunks, H, d), True)), "bf16")
+    q = gen(32, 0, synth.T_QR, (1, 64, H, d), True)
+    a = host(M.msa_route_score(to_dev(q, True), to_dev(store, True), cd, len(lens)))
+    b = host(M.msa_route_score(to_dev(q * 4.0, True), to_dev(store, True), cd, len(lens)))
+    np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("B,D,k", [(1, 64, 4), (1, 2048, 16), (1, 195312, 16), (32, 10518, 16), (2, 5000, 256),
+                                   (3, 4096, 1), (1, 4097, 32), (1, 9000, 9000 // 40)])
+def test_topk_exact(B, D, k):
+    r = np.random.default_rng(B * 7 + D)
+    s = np.round(r.normal(size=(B, D)), 3).astype(np.float32)       # many exact ties
+    s[:, r.integers(0, D, size=D // 10)] = -np.inf
+    ids, vals = M.msa_topk(torch.from_numpy(s).to(dev()), k)
+    want_ids, want_vals = O.topk(s.astype(np.float64), k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), want_ids)
+    np.testing.assert_array_equal(vals.cpu().numpy().astype(np.float64), want_vals)
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_gather(bf16, mode):
+    Hkv, d, B, k = 8, 128, 3, 5
+    lens = ragged_lengths(6, 50, 0, 500, n_empty=2)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    kb = gen(41, 0, synth.T_K, (n_chunks, Hkv, d), bf16)
+    vb = gen(42, 0, synth.T_V, (n_chunks, Hkv, d), bf16)
+    r = np.random.default_rng(9)
+    ids = np.stack([r.choice(50, size=k, replace=False) for _ in range(B)]).astype(np.int32)
+    mdc = int(np.diff(chunk_off).max())
+    max_ctx = k * mdc
+    if mode == 0:
+        kbar, vbar = to_dev(kb, bf16), to_dev(vb, bf16)
+    else:
+        kbar = to_dev(kb, bf16).cpu().pin_memory()
+        vbar = to_dev(vb, bf16).cpu().pin_memory()
+    kc, vc, cp, cl = M.msa_gather_kv(torch.from_numpy(ids).to(dev()), co_d, kbar, vbar, mdc, max_ctx, src_mode=mode,
+                                     chunk_off_h=chunk_off if mode == 2 else None, device=dev())
+    torch.cuda.synchronize()
+    for b in range(B):
+        rk, rv, rp = O.gather(ids[b], chunk_off, kb, vb)
+        n = len(rp)
+        assert int(cl[b]) == n
+        np.testing.assert_array_equal(host(kc[b, :n]), rk)
+        np.testing.assert_array_equal(host(vc[b, :n]), rv)
+        np.testing.assert_array_equal(cp[b, :n].cpu().numpy(), rp)
+
+
+def _attn_case(seed, B, T, Hq, Hkv, d, L_loc, ctx_lens, bf16, max_ctx):
+    q = gen(seed, 0, synth.T_Q, (B, T, Hq, d), bf16)
+    kl = gen(seed, 0, synth.T_KLOC, (B, L_loc, Hkv, d), bf16)
+    vl = gen(seed, 0, synth.T_VLOC, (B, L_loc, Hkv, d), bf16)
+    kc = gen(seed, 0, synth.T_K, (B, max_ctx, Hkv, d), bf16, scale_pow2=-3)
+    vc = gen(seed, 0, synth.T_V, (B, max_ctx, Hkv, d), bf16, scale_pow2=-3)
+    r = np.random.default_rng(seed)
+    cp = r.integers(0, min(128, max_ctx), size=(B, max_ctx)).astype(np.int32)
+    cl = np.asarray(ctx_lens, dtype=np.int32)
+    return q, kl, vl, kc, vc, cp, cl
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("B,T,L_loc,ctx", [(1, 16, 16, [32]), (1, 64, 4096, [128]), (32, 1, 8192, None),
+                                           (2, 3, 50, [0, 77]), (1, 128, 300, [1000]), (4, 1, 1, [5, 0, 31, 64])])
+def test_sparse_attention(bf16, B, T, L_loc, ctx):
+    Hq, Hkv, d, qpo = 32, 8, 128, 16
+    if ctx is None:
+        ctx = list(np.random.default_rng(0).integers(100, 2048, size=B))
+    max_ctx = max(max(ctx), 1)
+    q, kl, vl, kc, vc, cp, cl = _attn_case(50 + T, B, T, Hq, Hkv, d, L_loc, ctx, bf16, max_ctx)
+    if not bf16 and B * (max_ctx + L_loc) > 200000:
+        pytest.skip("float32 path is the small-case vector path")
+    out = M.msa_sparse_attn(to_dev(q, bf16), to_dev(kc, bf16), to_dev(vc, bf16),
+                            torch.from_numpy(cp).to(dev()), torch.from_numpy(cl).to(dev()), to_dev(kl, bf16),
+                            to_dev(vl, bf16), qpo)
+    got = host(out)
+    sm = 1.0 / math.sqrt(d)
+    worst = 0.0
+    rows = range(B) if B <= 4 else [0, 7, 31]
+    for b in rows:
+        n = int(cl[b])
+        ref = O.attend_one(q[b], kc[b, :n], vc[b, :n], cp[b, :n], kl[b], vl[b], qpo, 1e6, sm)
+        e = np.abs(got[b] - ref).max()
+        worst = max(worst, e)
+        assert e <= ATOL_ATTN["bf16" if bf16 else "f32"], f"b={b}: max-abs {e}"
+    print(f"attention bf16={bf16} B={B} T={T}: max-abs {worst:.3g}")
