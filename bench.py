@@ -1,0 +1,254 @@
+"""Benchmark of the MSA routing + sparse-attention hot path on one MI355X.
+
+One step = one query through all routed layers: per layer, routing score over
+that layer's whole pooled routing-key store -> top-k -> context assembly
+(content K/V fetched from the host tier or HBM) -> sparse attention.  The
+default workload is the 100M-token memory (195,312 documents x 512 tokens,
+chunk 64 -> 1,562,496 pooled chunks per layer, 18 layers, 8 heads x 128,
+bf16; the routing-key store is 57.6 GB in HBM), query of 64 tokens, 32 query
+heads, 4,096 local tokens, k = 16.  Inputs are seeded synthetic data
+generated on the device before the timed region.
+
+Prints one JSON line.  --gpus above 1 is not supported (one GPU per process,
+no collectives in this build).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="cfg4")
+    ap.add_argument("--kv-tier", choices=["host", "hbm"], default="host")
+    ap.add_argument("--gather", choices=["mapped", "memcpy"], default="mapped")
+    ap.add_argument("--layers", type=int, default=None, help="override the routed-layer count (profiling only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-chunks", type=int, default=262144)
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 "
+                                   "(no sharding and no collectives)"}))
+        sys.exit(2)
+    import torch
+
+    import synth
+    from synth import configs
+    from synth import device as SD
+    import sparse_attention_long_msa_amd as M
+
+    p = configs.PRESETS[args.config]()
+    layers = p.layers if args.layers is None else args.layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16 if p.bf16 else torch.float32
+    esz = 2 if p.bf16 else 4
+    H, d, N, D = p.H, p.d, p.n_chunks, p.n_docs
+    log(f"{p.name}: {D} docs, {N} chunks/layer, {layers} layers, store {N * H * d * esz * layers / 1e9:.1f} GB")
+
+    # ------------------------------------------------------------ document index
+    chunk_off = p.chunk_off
+    tok_off = p.tok_off
+    co_d = torch.from_numpy(chunk_off).to(dev)
+    cd = M.msa_chunk_doc_map(co_d, N)
+
+    # ------------------------------------------------------------ query-side inputs (per layer)
+    qr = [SD.fill(torch.empty((p.B, p.T, H, d), dtype=bf, device=dev), p.qseed, l, synth.T_QR) for l in range(layers)]
+    qq = [SD.fill(torch.empty((p.B, p.T, p.Hq, d), dtype=bf, device=dev), p.qseed, l, synth.T_Q) for l in range(layers)]
+    kl = [SD.fill(torch.empty((p.B, p.L_loc, H, d), dtype=bf, device=dev), p.qseed, l, synth.T_KLOC)
+          for l in range(layers)]
+    vl = [SD.fill(torch.empty((p.B, p.L_loc, H, d), dtype=bf, device=dev), p.qseed, l, synth.T_VLOC)
+          for l in range(layers)]
+
+    # ------------------------------------------------------------ routing-key store (HBM)
+    t0 = time.time()
+    store = torch.empty((layers, N, H, d), dtype=bf, device=dev)
+    raw = torch.empty((N, H, d), dtype=bf, device=dev)
+    needles = synth.needle_docs(p.seed, D, p.n_needles)
+    if not p.pooled_level:
+        raise SystemExit("bench.py synthesises token-level presets only through the tests; use cfg4")
+    for l in range(layers):
+        SD.fill(raw, p.seed, l, synth.T_KR)
+        qh = qr[l][0].float().cpu().numpy()
+        for nd in needles:
+            lo, hi = int(chunk_off[nd]), int(chunk_off[nd + 1])
+            rows = synth.needle_rows(qh, p.seed, l, hi - lo, bf16=p.bf16, start=lo)
+            raw[lo:hi] = torch.from_numpy(rows).to(dev, bf)
+        # pooled-level synthesis: chunk = 1 pooling is the identity; this normalises
+        M.msa_pool_encode(raw, co_d, co_d, cd, 1, True, out=store[l])
+    torch.cuda.synchronize()
+    log(f"routing-key store ready in {time.time() - t0:.1f} s")
+
+    # ------------------------------------------------------------ content K/V tier
+    t0 = time.time()
+    tier = args.kv_tier
+    kbar, vbar = [], []
+    if tier == "host":
+        try:
+            for l in range(layers):
+                for lst, tid in ((kbar, synth.T_K), (vbar, synth.T_V)):
+                    SD.fill(raw, p.seed, l, tid, scale_pow2=-3)
+                    h = torch.empty((N, H, d), dtype=bf, pin_memory=True)
+                    h.copy_(raw)
+                    lst.append(h)
+                log(f"host tier layer {l} ready ({time.time() - t0:.1f} s)")
+            torch.cuda.synchronize()
+        except (RuntimeError, torch.OutOfMemoryError) as e:  # pinned host memory exhausted
+            log(f"pinned host tier unavailable ({str(e).splitlines()[0]}); falling back to the HBM tier")
+            kbar.clear()
+            vbar.clear()
+            torch.cuda.synchronize()
+            tier = "hbm"
+    if tier == "hbm":
+        for l in range(layers):
+            kbar.append(SD.fill(torch.empty((N, H, d), dtype=bf, device=dev), p.seed, l, synth.T_K, scale_pow2=-3))
+            vbar.append(SD.fill(torch.empty((N, H, d), dtype=bf, device=dev), p.seed, l, synth.T_V, scale_pow2=-3))
+        torch.cuda.synchronize()
+    del raw
+    log(f"content K/V tier '{tier}' ready in {time.time() - t0:.1f} s")
+    src_mode = M.MSA_SRC_DEVICE if tier == "hbm" else (
+        M.MSA_SRC_HOST_MAPPED if args.gather == "mapped" else M.MSA_SRC_HOST_MEMCPY)
+
+    runner = M.LayerRunner(batch=p.B, tokens=p.T, q_heads=p.Hq, kv_heads=H, head_dim=d, n_docs=D, n_chunks=N,
+                           k=p.k, max_doc_chunks=p.max_doc_chunks, local_len=p.L_loc, dtype=bf, device=dev,
+                           q_pos_offset=p.qpo, rope_base=p.rope_base, src_mode=src_mode, chunk_off_h=chunk_off)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for l in range(layers):
+            if ev is not None:
+                ev[l][0].record(stream)
+            runner.route(qr[l], store[l], cd)
+            if ev is not None:
+                ev[l][1].record(stream)
+            runner.select()
+            if ev is not None:
+                ev[l][2].record(stream)
+            runner.assemble(co_d, kbar[l], vbar[l])
+            if ev is not None:
+                ev[l][3].record(stream)
+            runner.attend(qq[l], kl[l], vl[l])
+            if ev is not None:
+                ev[l][4].record(stream)
+
+    # needle check on one pass (a property of the planted data, not timed)
+    step()
+    torch.cuda.synchronize()
+    ids0 = runner.ids.cpu().numpy()[0]
+    recall = float(np.mean([n in set(ids0.tolist()) for n in needles]))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(layers)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    stage = np.zeros(4)
+    route_ms = []
+    for s in range(args.steps):
+        for l in range(layers):
+            e = evs[s][l]
+            dts = [e[i].elapsed_time(e[i + 1]) for i in range(4)]
+            stage += dts
+            route_ms.append(dts[0])
+    stage /= args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    store_bytes = N * H * d * esz                      # per layer
+    step_bytes = store_bytes * layers
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9   # GB/s over the whole step
+    routing_gbps = step_bytes / ((stage[0] + stage[1]) * 1e-3) / 1e9
+    # algorithmic bytes of one msa_route_score launch: the store, the chunk->doc map,
+    # the routing query and the score row (initial fill + result)
+    alg_bytes = store_bytes + N * 4 + p.B * p.T * H * d * esz + 2 * p.B * D * 4
+    route_avg_ms = float(np.mean(route_ms))
+    achieved = alg_bytes / (route_avg_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": "routing-key (K_r) scan GB/s over the whole route+attn step, 100M-token memory",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if p.bf16 else "f32",
+        "data": "synthetic (seeded counter-based generator; planted needles)",
+        "config": {"workload": f"{p.name}: 100M-token memory, {D} docs x 512 tok, chunk {p.chunk}, "
+                               f"{N} chunks/layer, {layers} routed layers, H={H}, d={d}; query T={p.T}, "
+                               f"Hq={p.Hq}, L_loc={p.L_loc}, k={p.k}",
+                   "global_batch": p.B, "seq_len": p.T, "parallelism": "single GPU",
+                   "kv_tier": tier, "gather": args.gather if tier == "host" else "hbm"},
+        "route_attn_us_per_query": round(ms_per_step * 1e3 / p.B, 1),
+        "routing_GBps": round(routing_gbps, 1),
+        "routing_frac_of_8TBps": round(routing_gbps / 8000, 4),
+        "stage_ms_per_step": {"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
+                              "gather": round(stage[2], 4), "attention": round(stage[3], 4)},
+        "needle_recall_layer0": recall,
+        "roofline": {"kernel": "msa_route_score (route_score_mfma_kernel + score fill)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(achieved / 8000.0, 4), "traffic": None,
+                     "avg_launch_ms": round(route_avg_ms, 4), "alg_bytes_per_launch": int(alg_bytes)},
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(p, args.cpu_sample_chunks)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(p, n_sample_chunks):
+    """The float64 oracle's routing (score + top-k) on a bounded sample of the
+    same workload: layer 0, the first documents of the memory."""
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    n_docs = n_sample_chunks // p.max_doc_chunks
+    co = p.chunk_off[: n_docs + 1]
+    n = int(co[-1])
+    raw = synth.normal(p.seed, synth.stream_id(0, synth.T_KR), 0, n * p.H * p.d, bf16=p.bf16)
+    raw = raw.reshape(n, p.H, p.d)
+    qr = synth.tensor(p.qseed, 0, synth.T_QR, (p.B, p.T, p.H, p.d), bf16=p.bf16)
+    store = O.pool_encode(raw, co, 1, True, "bf16" if p.bf16 else "f32")   # offline stage, untimed
+    del raw
+    t0 = time.perf_counter()
+    s = O.route_scores(qr, store, co)
+    O.topk(s, p.k)
+    dt = time.perf_counter() - t0
+    gb = n * p.H * p.d * (2 if p.bf16 else 4) / 1e9
+    return {"value": round(gb / dt, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"layer 0, first {n_docs} documents ({n} pooled chunks, {gb:.2f} GB of bf16 routing keys), "
+                      f"routing score + top-k for one {p.T}-token query, float64"}
+
+
+if __name__ == "__main__":
+    main()
