@@ -270,25 +270,257 @@ __global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
   if (g4 == 0) ws_ml[rowid] = make_float2(m_run, l_run);
 }
 
+// ---------------------------------------------------------------- prefill (many query rows)
+// One workgroup of 8 waves owns (query b, KV head g, row group, key split);
+// its waves hold up to 16 row tiles (RTW per wave).  Each 32-key step is
+// loaded once by the whole workgroup, rotated once, and staged in LDS as
+// K_rot[key][d] (the A operand of S^T = K Q^T) and V^T[d][slot] (the A
+// operand of O^T = V^T P^T); the next step's global loads are in flight
+// while the current step is computed (two LDS buffers).
+
+constexpr int PF_WAVES = 8;
+constexpr int PF_THREADS = 64 * PF_WAVES;
+constexpr int PF_KS = 272;                         // bytes per key row of K_rot in LDS (256 + pad)
+constexpr int PF_K_BYTES = 32 * PF_KS;
+constexpr int PF_BUF = PF_K_BYTES + AT_VT_BYTES;   // one step buffer
+
+struct PfRegs {
+  uint2 klo, khi;     // dims 4x..4x+3 and 64+4x..64+4x+3 of key t/16
+  float4 cs0, cs1;    // (cos, sin) of m = 4x..4x+3 at the key's position
+  uint32_t v[4];      // V[4*kq + i][2*dp .. 2*dp+1]
+};
+
+template <int G, int RTW>
+__global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
+    const uint16_t* __restrict__ q, int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_ctx,
+    const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
+    int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
+    const float2* __restrict__ tab, int P, float scale_log2, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
+    int n_splits, int keys_per_split, int n_rt, int n_rg) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int lc = lane % 16, g4 = lane / 16;
+
+  int64_t wg = blockIdx.x;
+  const int split = int(wg % n_splits);
+  wg /= n_splits;
+  const int rg = int(wg % n_rg);
+  wg /= n_rg;
+  const int g = int(wg % Hkv);
+  const int b = int(wg / Hkv);
+  if (b >= B) return;
+  const int64_t kv_stride = int64_t(Hkv) * AT_D;
+
+  // ---- this wave's row tiles: rotated query fragments and row metadata
+  bf16x8 bq[RTW][4];
+  int trow[RTW], hqrow[RTW], horizon[RTW];
+  bool rok[RTW];
+#pragma unroll
+  for (int i = 0; i < RTW; ++i) {
+    const int rt = rg * (PF_WAVES * RTW) + wave + PF_WAVES * i;
+    const int r = rt * 16 + lc;
+    const int t = r / G;
+    rok[i] = rt < n_rt && t < T;
+    trow[i] = rok[i] ? t : 0;
+    hqrow[i] = g * G + r % G;
+    horizon[i] = L_loc - T + t;
+    uint4 qv[4];
+    const uint16_t* qp = q + ((int64_t(b) * T + trow[i]) * Hq + hqrow[i]) * AT_D + 8 * g4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qv[kk] = *reinterpret_cast<const uint4*>(qp + 32 * kk);
+    int pq = qpo + L_loc - T + trow[i];
+    pq = pq < 0 ? 0 : (pq >= P ? P - 1 : pq);
+    rope_rotate(qv, tab + int64_t(pq) * (AT_D / 2), g4);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) bq[i][kk] = __builtin_bit_cast(bf16x8, rok[i] ? qv[kk] : make_uint4(0, 0, 0, 0));
+  }
+
+  const int ctxl = ctx_len[b];
+  const int n_keys = ctxl + L_loc;
+  const int j_begin = split * keys_per_split;
+  const int j_end = min(n_keys, j_begin + keys_per_split);
+
+  // cooperative mapping of one 32-key step
+  const int lk = tid / 16, lx = tid % 16;     // K: key, 4-dim block
+  const int vq = tid / 64, vdp = tid % 64;    // V: key quad, dim pair
+
+  auto load_step = [&](int j0, PfRegs& R) {
+    {
+      const KeySrc ks = key_src(j0 + lk, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+      const uint16_t* kp = (ks.local ? k_loc : k_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 4 * lx;
+      R.klo = *reinterpret_cast<const uint2*>(kp);
+      R.khi = *reinterpret_cast<const uint2*>(kp + 64);
+      const float4* cp = reinterpret_cast<const float4*>(tab + int64_t(ks.pos) * (AT_D / 2) + 4 * lx);
+      R.cs0 = cp[0];
+      R.cs1 = cp[1];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const KeySrc ks = key_src(j0 + 4 * vq + i, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+      const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 2 * vdp;
+      R.v[i] = *reinterpret_cast<const uint32_t*>(vp);
+    }
+  };
+  auto store_step = [&](const PfRegs& R, unsigned char* buf) {
+    // rotate the 4 (m, m+64) pairs of this thread and store K_rot[key][d]
+    const float c[4] = {R.cs0.x, R.cs0.z, R.cs1.x, R.cs1.z};
+    const float sn[4] = {R.cs0.y, R.cs0.w, R.cs1.y, R.cs1.w};
+    const uint32_t lo[2] = {R.klo.x, R.klo.y}, hi[2] = {R.khi.x, R.khi.y};
+    float a[4], bb[4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      a[2 * e] = __uint_as_float(lo[e] << 16);
+      a[2 * e + 1] = __uint_as_float(lo[e] & 0xFFFF0000u);
+      bb[2 * e] = __uint_as_float(hi[e] << 16);
+      bb[2 * e + 1] = __uint_as_float(hi[e] & 0xFFFF0000u);
+    }
+    float ra[4], rb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ra[e] = a[e] * c[e] - bb[e] * sn[e];
+      rb[e] = bb[e] * c[e] + a[e] * sn[e];
+    }
+    unsigned char* krow = buf + lk * PF_KS;
+    *reinterpret_cast<uint2*>(krow + 8 * lx) = make_uint2(pack_bf16x2(ra[0], ra[1]), pack_bf16x2(ra[2], ra[3]));
+    *reinterpret_cast<uint2*>(krow + 128 + 8 * lx) = make_uint2(pack_bf16x2(rb[0], rb[1]), pack_bf16x2(rb[2], rb[3]));
+    // V^T[d][slot]: keys 4vq..4vq+3 = 16*tau + 4*gg + (0..3) -> slots 8*gg + 4*tau + (0..3)
+    unsigned char* vt = buf + PF_K_BYTES;
+    const int tau = vq / 4, gg = vq % 4;
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd) {
+      const int sh = dd ? 16 : 0;
+      const uint32_t e0 = (R.v[0] >> sh) & 0xFFFFu, e1 = (R.v[1] >> sh) & 0xFFFFu;
+      const uint32_t e2 = (R.v[2] >> sh) & 0xFFFFu, e3 = (R.v[3] >> sh) & 0xFFFFu;
+      *reinterpret_cast<uint2*>(vt + (2 * vdp + dd) * AT_VT_STRIDE + 2 * (8 * gg + 4 * tau)) =
+          make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+    }
+  };
+
+  float m_run[RTW], l_run[RTW];
+  f32x4 o[RTW][8];
+#pragma unroll
+  for (int i = 0; i < RTW; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  PfRegs R;
+  if (j_begin < j_end) {
+    load_step(j_begin, R);
+    store_step(R, smem);
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int j0 = j_begin; j0 < j_end; j0 += 32) {
+    const bool has_next = j0 + 32 < j_end;
+    if (has_next) load_step(j0 + 32, R);
+    const unsigned char* kb = smem + cur * PF_BUF;
+    const unsigned char* vb = kb + PF_K_BYTES;
+    // S^T for both 16-key tiles, for every row tile of this wave
+    bf16x8 ka[2][4];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        ka[tau][kk] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(kb + (16 * tau + lc) * PF_KS + 64 * kk + 16 * g4));
+    bf16x8 pb[RTW];
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+      f32x4 sv[2];
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tau][kk], bq[i][kk], acc, 0, 0, 0);
+        sv[tau] = acc;
+      }
+      float x[2][4];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kj = j0 + 16 * tau + 4 * g4 + e;
+          const bool vis = rok[i] && kj < j_end && (kj < ctxl || kj - ctxl <= horizon[i]);
+          x[tau][e] = vis ? sv[tau][e] * scale_log2 : -INFINITY;
+          mt = fmaxf(mt, x[tau][e]);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m_run[i], mt);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m_run[i] - m_use);
+      float p[2][4], psum = 0.f;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[tau][e] = exp2f(x[tau][e] - m_use);
+          psum += p[tau][e];
+        }
+      l_run[i] = l_run[i] * alpha + psum;
+      m_run[i] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
+      pb[i] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                                                    pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])));
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vb + (16 * dt + lc) * AT_VT_STRIDE + 16 * g4));
+#pragma unroll
+      for (int i = 0; i < RTW; ++i) o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[i], o[i][dt], 0, 0, 0);
+    }
+    if (has_next) store_step(R, smem + (cur ^ 1) * PF_BUF);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+#pragma unroll
+  for (int i = 0; i < RTW; ++i) {
+    float l = l_run[i];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!rok[i]) continue;
+    const int64_t rowid = ((int64_t(split) * B + b) * T + trow[i]) * Hq + hqrow[i];
+    float* op = ws_o + rowid * AT_D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(op + 16 * dt + 4 * g4) = make_float4(o[i][dt][0], o[i][dt][1], o[i][dt][2], o[i][dt][3]);
+    if (g4 == 0) ws_ml[rowid] = make_float2(m_run[i], l);
+  }
+}
+
 // out[b,t,hq,:] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s
 __global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, int n_splits,
                                     int64_t rows, int d, float* __restrict__ out) {
+  // one thread per (row, 4 dims); d is a multiple of 4 on this path
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= rows * d) return;
-  const int64_t row = i / d;
-  const int e = int(i % d);
+  const int dq = d / 4;
+  if (i >= rows * dq) return;
+  const int64_t row = i / dq;
+  const int e = int(i % dq) * 4;
   float m = -INFINITY;
   for (int s = 0; s < n_splits; ++s) m = fmaxf(m, ws_ml[s * rows + row].x);
   const float mu = m == -INFINITY ? 0.f : m;
-  float num = 0.f, den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
   for (int s = 0; s < n_splits; ++s) {
     const float2 ml = ws_ml[s * rows + row];
     if (ml.y == 0.f) continue;
     const float w = exp2f(ml.x - mu);
     den += w * ml.y;
-    num += w * ws_o[(s * rows + row) * d + e];
+    const float4 v = *reinterpret_cast<const float4*>(ws_o + (s * rows + row) * d + e);
+    num.x += w * v.x;
+    num.y += w * v.y;
+    num.z += w * v.z;
+    num.w += w * v.w;
   }
-  out[i] = den > 0.f ? num / den : 0.f;
+  const float r = den > 0.f ? 1.f / den : 0.f;
+  *reinterpret_cast<float4*>(out + row * d + e) = make_float4(num.x * r, num.y * r, num.z * r, num.w * r);
 }
 
 // Vector path (float32 or any even d): one workgroup per (b, t, hq); the
@@ -389,6 +621,9 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
 
 struct AttnPlan {
   bool mfma;
+  bool prefill;     // workgroup-cooperative kernel (2+ row tiles)
+  int rtw;          // row tiles per wave (prefill)
+  int n_rg;         // row groups (prefill)
   int P;            // rows of the RoPE table
   int n_rt;         // 16-row tiles per (b, g)
   int n_splits;
@@ -401,12 +636,23 @@ static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int m
   const int G = Hkv > 0 ? Hq / Hkv : 0;
   p.mfma = dtype == MSA_BF16 && d == AT_D && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
   p.P = std::max(qpo + L_loc, max_ctx);
+  p.P = std::max(p.P, 32);
   p.tab_bytes = align_up(size_t(p.P) * (d / 2) * sizeof(float2), 256);
   if (!p.mfma) return p;
   p.n_rt = (T * G + 15) / 16;
   const int64_t n_keys_max = int64_t(max_ctx) + L_loc;
-  const int64_t units = int64_t(B) * Hkv * p.n_rt;
-  int64_t s = (4096 + units - 1) / units;
+  p.prefill = p.n_rt >= 2;
+  int64_t units, target;
+  if (p.prefill) {
+    p.rtw = p.n_rt > PF_WAVES ? 2 : 1;
+    p.n_rg = (p.n_rt + PF_WAVES * p.rtw - 1) / (PF_WAVES * p.rtw);
+    units = int64_t(B) * Hkv * p.n_rg;      // workgroups per split
+    target = 256;                            // about one workgroup per CU
+  } else {
+    units = int64_t(B) * Hkv * p.n_rt;      // waves per split
+    target = 4096;
+  }
+  int64_t s = (target + units - 1) / units;
   s = std::max<int64_t>(1, std::min<int64_t>(s, (n_keys_max + 63) / 64));
   int64_t kps = (n_keys_max + s - 1) / s;
   kps = (kps + 31) / 32 * 32;
@@ -464,6 +710,37 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
     float* ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.tab_bytes);
     float2* ws_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.tab_bytes + p.o_bytes);
     const int G = Hq / Hkv;
+    const float scale_log2_pf = sm_scale * 1.4426950408889634f;
+    if (p.prefill) {
+      const dim3 pgrid(unsigned(int64_t(B) * Hkv * p.n_rg * p.n_splits)), pblock(PF_THREADS);
+      const size_t psmem = 2 * size_t(PF_BUF);
+#define PF_LAUNCH(GV, RV)                                                                                           \
+  hipLaunchKernelGGL((attn_prefill_kernel<GV, RV>), pgrid, pblock, psmem, s, static_cast<const uint16_t*>(q), B, T,  \
+                     Hq, Hkv, static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos,     \
+                     ctx_len, max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc),     \
+                     L_loc, q_pos_offset, tab, p.P, scale_log2_pf, ws_o, ws_ml, p.n_splits, p.keys_per_split, p.n_rt, \
+                     p.n_rg)
+      const int key = G * 4 + p.rtw;
+      switch (key) {
+        case 1 * 4 + 1: PF_LAUNCH(1, 1); break;
+        case 1 * 4 + 2: PF_LAUNCH(1, 2); break;
+        case 2 * 4 + 1: PF_LAUNCH(2, 1); break;
+        case 2 * 4 + 2: PF_LAUNCH(2, 2); break;
+        case 4 * 4 + 1: PF_LAUNCH(4, 1); break;
+        case 4 * 4 + 2: PF_LAUNCH(4, 2); break;
+        case 8 * 4 + 1: PF_LAUNCH(8, 1); break;
+        case 8 * 4 + 2: PF_LAUNCH(8, 2); break;
+        case 16 * 4 + 1: PF_LAUNCH(16, 1); break;
+        default: PF_LAUNCH(16, 2); break;
+      }
+#undef PF_LAUNCH
+      MSA_LAUNCH_CHECK();
+      const int64_t rows = int64_t(B) * T * Hq;
+      hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * (d / 4) + 255) / 256)), dim3(256), 0, s, ws_o,
+                         ws_ml, p.n_splits, rows, d, out);
+      MSA_LAUNCH_CHECK();
+      return MSA_OK;
+    }
     const int64_t waves = int64_t(B) * Hkv * p.n_rt * p.n_splits;
     const dim3 grid(unsigned((waves + AT_WAVES - 1) / AT_WAVES)), block(AT_THREADS);
     const size_t smem = size_t(AT_WAVES) * AT_VT_BYTES;
@@ -483,8 +760,8 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
 #undef AT_LAUNCH
     MSA_LAUNCH_CHECK();
     const int64_t rows = int64_t(B) * T * Hq;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * d + 255) / 256)), dim3(256), 0, s, ws_o, ws_ml,
-                       p.n_splits, rows, d, out);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * (d / 4) + 255) / 256)), dim3(256), 0, s, ws_o,
+                       ws_ml, p.n_splits, rows, d, out);
     MSA_LAUNCH_CHECK();
     return MSA_OK;
   }

@@ -74,6 +74,148 @@ __global__ __launch_bounds__(TK_THREADS) void topk_pass_kernel(const float* __re
   }
 }
 
+// ---------------------------------------------------------------- wave-level selection (k <= 64)
+// A wave keeps the 64 smallest keys seen so far, sorted across its lanes.  A
+// batch of 64 new keys is skipped when none beats the current k-th key;
+// otherwise it is bitonic-sorted across the lanes and merged: the
+// elementwise min of the kept list and the reversed batch holds the 64
+// smallest of both as a bitonic sequence, which a bitonic merge sorts.
+
+constexpr int TW_PER_LANE = 32;                 // keys a lane loads per wave pass
+constexpr int TW_PER_WAVE = 64 * TW_PER_LANE;   // 2048
+constexpr int TW_WAVES = 4;
+constexpr int TW_PER_WG = TW_WAVES * TW_PER_WAVE;
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const int lo = __shfl_xor(int(uint32_t(v)), m), hi = __shfl_xor(int(uint32_t(v >> 32)), m);
+  return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+}
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
+  const int lo = __shfl(int(uint32_t(v)), src), hi = __shfl(int(uint32_t(v >> 32)), src);
+  return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(v)), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(v >> 32)), lane);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// ascending bitonic sort of one key per lane over the 64 lanes
+__device__ __forceinline__ uint64_t wave_sort64(uint64_t key, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint64_t other = shfl_xor64(key, stride);
+      const bool up = (lane & size) == 0 || size == 64;
+      const bool lower = (lane & stride) == 0;
+      key = (lower == up) ? (key < other ? key : other) : (key < other ? other : key);
+    }
+  }
+  return key;
+}
+
+// sorts a bitonic sequence held one key per lane (ascending)
+__device__ __forceinline__ uint64_t wave_merge64(uint64_t key, int lane) {
+#pragma unroll
+  for (int stride = 32; stride > 0; stride >>= 1) {
+    const uint64_t other = shfl_xor64(key, stride);
+    const bool lower = (lane & stride) == 0;
+    key = lower ? (key < other ? key : other) : (key < other ? other : key);
+  }
+  return key;
+}
+
+__device__ __forceinline__ uint64_t wave_insert(uint64_t best, uint64_t key, int lane, int k) {
+  const uint64_t thr = readlane64(best, k - 1);
+  if (__ballot(key < thr) == 0) return best;
+  key = wave_sort64(key, lane);
+  const uint64_t rev = shfl64(key, 63 - lane);
+  return wave_merge64(best < rev ? best : rev, lane);
+}
+
+// Each wave selects the k best of up to TW_PER_WAVE inputs (32 per lane).
+// Filter first: the k-th smallest of the 64 lane minima bounds the k-th
+// smallest key from above (those k lane minima are k distinct keys), so
+// only keys <= that bound can be selected.  The survivors (at most 32 k,
+// usually about k) are compacted into LDS and sorted / merged 64 at a time.
+// Not FINAL: the wave writes its k keys to keys_out[b][wave][k].  FINAL (one
+// workgroup per query): the waves' lists are merged through LDS and written
+// as ids/vals.
+template <bool FROM_SCORES, bool FINAL>
+__global__ __launch_bounds__(64 * TW_WAVES) void topk_wave_kernel(const float* __restrict__ scores,
+                                                                  const uint64_t* __restrict__ keys_in, int64_t n,
+                                                                  int k, uint64_t* __restrict__ keys_out,
+                                                                  int32_t* __restrict__ ids, float* __restrict__ vals) {
+  __shared__ uint64_t surv[TW_WAVES][TW_PER_WAVE];
+  const int b = blockIdx.y;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int64_t wave_id = int64_t(blockIdx.x) * TW_WAVES + wave;
+  const int64_t base = wave_id * TW_PER_WAVE;
+  constexpr uint64_t SENT = ~uint64_t(0);
+  uint64_t v[TW_PER_LANE];
+  uint64_t lmin = SENT;
+#pragma unroll
+  for (int i = 0; i < TW_PER_LANE; ++i) {
+    const int64_t g = base + int64_t(i) * 64 + lane;
+    uint64_t key = SENT;
+    if (g < n) {
+      if constexpr (FROM_SCORES)
+        key = score_key(scores[int64_t(b) * n + g], uint32_t(g));
+      else
+        key = keys_in[int64_t(b) * n + g];
+    }
+    v[i] = key;
+    lmin = key < lmin ? key : lmin;
+  }
+  const uint64_t bound = readlane64(wave_sort64(lmin, lane), k - 1);
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < TW_PER_LANE; ++i) cnt += (v[i] <= bound && v[i] != SENT) ? 1 : 0;
+  // exclusive prefix of the survivor counts across the wave
+  int incl = cnt;
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) {
+    const int o = __shfl_up(incl, sft);
+    if (lane >= sft) incl += o;
+  }
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  int pos = incl - cnt;
+  uint64_t* sw = surv[wave];
+#pragma unroll
+  for (int i = 0; i < TW_PER_LANE; ++i)
+    if (v[i] <= bound && v[i] != SENT) sw[pos++] = v[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  uint64_t best = wave_sort64(lane < total ? sw[lane] : SENT, lane);
+  for (int s0 = 64; s0 < total; s0 += 64) best = wave_insert(best, s0 + lane < total ? sw[s0 + lane] : SENT, lane, k);
+  if constexpr (!FINAL) {
+    if (lane < k) keys_out[(int64_t(b) * gridDim.x * TW_WAVES + wave_id) * k + lane] = best;
+  } else {
+    __syncthreads();
+    surv[wave][lane] = best;
+    __syncthreads();
+    if (wave == 0) {
+      uint64_t acc = best;
+#pragma unroll
+      for (int w = 1; w < TW_WAVES; ++w) acc = wave_insert(acc, surv[w][lane], lane, k);
+      if (lane < k) {
+        ids[int64_t(b) * k + lane] = int32_t(uint32_t(acc));
+        vals[int64_t(b) * k + lane] = order_key_float(~uint32_t(acc >> 32));
+      }
+    }
+  }
+}
+
+// Candidate counts of the wave passes: inputs > one workgroup's capacity are
+// reduced by non-final passes (every wave keeps k of its 2048 inputs; idle
+// waves of the last workgroup emit sentinel keys).
+static std::vector<int64_t> topk_wave_plan(int64_t n_docs, int k) {
+  std::vector<int64_t> ns{n_docs};
+  while (ns.back() > TW_PER_WG) ns.push_back((ns.back() + TW_PER_WG - 1) / TW_PER_WG * TW_WAVES * k);
+  return ns;
+}
+
 // Candidate counts of successive passes: n0 = n_docs, n_{i+1} = slices(n_i) * k.
 static std::vector<int64_t> topk_plan(int64_t n_docs, int k) {
   std::vector<int64_t> ns{n_docs};
@@ -85,7 +227,7 @@ static std::vector<int64_t> topk_plan(int64_t n_docs, int k) {
 
 extern "C" size_t msa_topk_workspace(int B, int64_t n_docs, int k) {
   if (B < 1 || n_docs < 1 || k < 1 || k > msa::TK_MAXK) return 0;
-  const auto ns = msa::topk_plan(n_docs, k);
+  const auto ns = k <= 64 ? msa::topk_wave_plan(n_docs, k) : msa::topk_plan(n_docs, k);
   int64_t mx = 0;
   for (size_t i = 1; i < ns.size(); ++i) mx = std::max(mx, ns[i]);
   return 2 * msa::align_up(size_t(B) * size_t(mx) * sizeof(uint64_t), 256);
@@ -103,9 +245,31 @@ extern "C" int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, in
   MSA_REQUIRE(ws_bytes >= need, MSA_ERR_WORKSPACE, "msa_topk: workspace too small");
   MSA_REQUIRE(need == 0 || ws, MSA_ERR_INVALID_ARG, "msa_topk: NULL workspace");
   hipStream_t s = as_stream(stream);
-  const auto ns = topk_plan(n_docs, k);
   uint64_t* buf[2] = {static_cast<uint64_t*>(ws),
                       reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + need / 2)};
+  if (k <= 64) {
+    const auto ns = topk_wave_plan(n_docs, k);
+    const dim3 block(64 * TW_WAVES);
+    for (size_t p = 0; p < ns.size(); ++p) {
+      const int64_t n = ns[p];
+      const bool first = p == 0, last = p + 1 == ns.size();
+      const dim3 grid{unsigned(last ? 1 : (n + TW_PER_WG - 1) / TW_PER_WG), unsigned(B)};
+      const uint64_t* kin = first ? nullptr : buf[(p - 1) % 2];
+      uint64_t* kout = last ? nullptr : buf[p % 2];
+      if (first && last)
+        hipLaunchKernelGGL((topk_wave_kernel<true, true>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+      else if (first)
+        hipLaunchKernelGGL((topk_wave_kernel<true, false>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+      else if (last)
+        hipLaunchKernelGGL((topk_wave_kernel<false, true>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+      else
+        hipLaunchKernelGGL((topk_wave_kernel<false, false>), grid, block, 0, s, doc_score, kin, n, k, kout, ids,
+                           vals);
+      MSA_LAUNCH_CHECK();
+    }
+    return MSA_OK;
+  }
+  const auto ns = topk_plan(n_docs, k);
   const dim3 block(TK_THREADS);
   for (size_t p = 0; p < ns.size(); ++p) {
     const int64_t n = ns[p];
