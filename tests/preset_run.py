@@ -1,0 +1,131 @@
+"""Builds one routed layer of a workload preset on the GPU (device-generated
+inputs, planted needles) and gives the oracle the same layer on the host, by
+document, so full-size presets can be checked on sampled documents."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle as O
+import synth
+from synth import device as SD
+import sparse_attention_long_msa_amd as M
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+class HostLayer:
+    """Host-side (oracle) view of layer l of preset p."""
+
+    def __init__(self, p, l):
+        self.p, self.l = p, l
+        self.dt = "bf16" if p.bf16 else "f32"
+        H, d = p.H, p.d
+        self.qr = synth.tensor(p.qseed, l, synth.T_QR, (p.B, p.T, H, d), bf16=p.bf16)
+        self.q = synth.tensor(p.qseed, l, synth.T_Q, (p.B, p.T, p.Hq, d), bf16=p.bf16)
+        self.needles = synth.needle_docs(p.seed, p.n_docs, p.n_needles)
+        # needle i belongs to query i (one per query) or to query 0
+        self.owner = {int(nd): (i if p.needle_per_query else 0) for i, nd in enumerate(self.needles)}
+
+    def raw_rows(self, tensor, doc):
+        """Raw rows (tokens, or pooled rows for pooled-level presets) of one document."""
+        p = self.p
+        off = p.chunk_off if p.pooled_level else p.tok_off
+        lo, hi = int(off[doc]), int(off[doc + 1])
+        scale = -3 if (p.pooled_level and tensor in (synth.T_K, synth.T_V)) else 0
+        x = synth.normal(p.seed, synth.stream_id(self.l, tensor), lo * p.H * p.d, (hi - lo) * p.H * p.d,
+                         bf16=p.bf16, scale_pow2=scale).reshape(hi - lo, p.H, p.d)
+        if tensor == synth.T_KR and int(doc) in self.owner:
+            b = self.owner[int(doc)]
+            x = synth.needle_rows(self.qr[b], p.seed, self.l, hi - lo, bf16=p.bf16, start=lo)
+        return x
+
+    def store(self, tensor, doc):
+        """Oracle store entries of one document (pooled; routing keys normalised)."""
+        p = self.p
+        x = self.raw_rows(tensor, doc)
+        chunk = 1 if p.pooled_level else p.chunk
+        return O.pool_encode(x, np.array([0, len(x)]), chunk, tensor == synth.T_KR, self.dt)
+
+    def doc_scores(self, docs):
+        """Oracle routing scores [B, len(docs)] of the given documents."""
+        out = np.empty((self.p.B, len(docs)))
+        for j, doc in enumerate(docs):
+            kr = self.store(synth.T_KR, doc)
+            out[:, j] = O.route_scores(self.qr, kr, np.array([0, len(kr)]))[:, 0]
+        return out
+
+    def local(self, b):
+        p = self.p
+        n = p.L_loc * p.H * p.d
+        kl = synth.normal(p.qseed, synth.stream_id(self.l, synth.T_KLOC), b * n, n, bf16=p.bf16)
+        vl = synth.normal(p.qseed, synth.stream_id(self.l, synth.T_VLOC), b * n, n, bf16=p.bf16)
+        return kl.reshape(p.L_loc, p.H, p.d), vl.reshape(p.L_loc, p.H, p.d)
+
+    def attention(self, b, ids_b):
+        """Oracle attention of query b over the documents ids_b (rank order)."""
+        p = self.p
+        ks, vs, ps = [], [], []
+        for doc in ids_b:
+            kb, vb = self.store(synth.T_K, doc), self.store(synth.T_V, doc)
+            ks.append(kb)
+            vs.append(vb)
+            ps.append(np.arange(len(kb)))
+        kl, vl = self.local(b)
+        return O.attend_one(self.q[b], np.concatenate(ks), np.concatenate(vs), np.concatenate(ps), kl, vl,
+                            p.qpo, p.rope_base, 1.0 / math.sqrt(p.d))
+
+
+class GpuLayer:
+    """Layer l of preset p built and run on the GPU through the C ABI."""
+
+    def __init__(self, p, l, host: HostLayer, src_mode=M.MSA_SRC_DEVICE):
+        self.p, self.l = p, l
+        d0 = dev()
+        bf = torch.bfloat16 if p.bf16 else torch.float32
+        H, d = p.H, p.d
+        co = p.chunk_off
+        self.co_d = torch.from_numpy(co).to(d0)
+        self.cd = M.msa_chunk_doc_map(self.co_d, p.n_chunks)
+        if p.pooled_level:
+            to_d, chunk, n_rows = self.co_d, 1, p.n_chunks
+            row_off = co
+        else:
+            to_d, chunk, n_rows = torch.from_numpy(p.tok_off).to(d0), p.chunk, int(p.lengths.sum())
+            row_off = p.tok_off
+        raw = torch.empty((n_rows, H, d), dtype=bf, device=d0)
+        self.store = {}
+        for tid in (synth.T_KR, synth.T_K, synth.T_V):
+            scale = -3 if (p.pooled_level and tid != synth.T_KR) else 0
+            SD.fill(raw, p.seed, l, tid, scale_pow2=scale)
+            if tid == synth.T_KR:
+                for nd, b in host.owner.items():
+                    lo, hi = int(row_off[nd]), int(row_off[nd + 1])
+                    rows = synth.needle_rows(host.qr[b], p.seed, l, hi - lo, bf16=p.bf16, start=lo)
+                    raw[lo:hi] = torch.from_numpy(rows).to(d0, bf)
+            self.store[tid] = M.msa_pool_encode(raw, to_d, self.co_d, self.cd, chunk, tid == synth.T_KR)
+        del raw
+        self.qr = torch.from_numpy(host.qr).to(d0, bf)
+        self.q = torch.from_numpy(host.q).to(d0, bf)
+        self.kl = SD.fill(torch.empty((p.B, p.L_loc, H, d), dtype=bf, device=d0), p.qseed, l, synth.T_KLOC)
+        self.vl = SD.fill(torch.empty((p.B, p.L_loc, H, d), dtype=bf, device=d0), p.qseed, l, synth.T_VLOC)
+        kb, vb = self.store[synth.T_K], self.store[synth.T_V]
+        if src_mode != M.MSA_SRC_DEVICE:
+            kb, vb = kb.cpu().pin_memory(), vb.cpu().pin_memory()
+        self.kb, self.vb = kb, vb
+        self.runner = M.LayerRunner(batch=p.B, tokens=p.T, q_heads=p.Hq, kv_heads=H, head_dim=d, n_docs=p.n_docs,
+                                    n_chunks=p.n_chunks, k=p.k, max_doc_chunks=p.max_doc_chunks,
+                                    local_len=p.L_loc, dtype=bf, device=d0, q_pos_offset=p.qpo,
+                                    rope_base=p.rope_base, src_mode=src_mode, chunk_off_h=co)
+
+    def run(self):
+        r = self.runner
+        r.run(self.qr, self.store[synth.T_KR], self.cd, self.co_d, self.kb, self.vb, self.q, self.kl, self.vl)
+        torch.cuda.synchronize()
+        return dict(doc_score=r.doc_score.cpu().double().numpy(), ids=r.ids.cpu().numpy(),
+                    vals=r.vals.cpu().double().numpy(), out=r.out.cpu().double().numpy(),
+                    ctx_len=r.ctx_len.cpu().numpy())
