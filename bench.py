@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the routed-layer count (profiling only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-chunks", type=int, default=262144)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (the reference for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -49,6 +51,9 @@ def main():
                                    "(no sharding and no collectives)"}))
         sys.exit(2)
     import torch
+
+    if args.copy_calibration:
+        return copy_calibration(torch)
 
     import synth
     from synth import configs
@@ -79,21 +84,33 @@ def main():
           for l in range(layers)]
 
     # ------------------------------------------------------------ routing-key store (HBM)
+    # The offline stage (pooling) runs here, before the timed region.  The
+    # 100M-token preset is synthesised at pooled level (chunk = 1 pooling,
+    # which only normalises); the others pool raw per-token tensors.
     t0 = time.time()
     store = torch.empty((layers, N, H, d), dtype=bf, device=dev)
-    raw = torch.empty((N, H, d), dtype=bf, device=dev)
+    if p.pooled_level:
+        rows_off, pool_chunk, n_rows, to_d = chunk_off, 1, N, co_d
+    else:
+        rows_off, pool_chunk, n_rows = tok_off, p.chunk, int(tok_off[-1])
+        to_d = torch.from_numpy(tok_off).to(dev)
+    raw = torch.empty((n_rows, H, d), dtype=bf, device=dev)
     needles = synth.needle_docs(p.seed, D, p.n_needles)
-    if not p.pooled_level:
-        raise SystemExit("bench.py synthesises token-level presets only through the tests; use cfg4")
+    encode_ms = []
     for l in range(layers):
         SD.fill(raw, p.seed, l, synth.T_KR)
-        qh = qr[l][0].float().cpu().numpy()
-        for nd in needles:
-            lo, hi = int(chunk_off[nd]), int(chunk_off[nd + 1])
+        for i, nd in enumerate(needles):
+            b = i if p.needle_per_query else 0
+            qh = qr[l][b].float().cpu().numpy()
+            lo, hi = int(rows_off[nd]), int(rows_off[nd + 1])
             rows = synth.needle_rows(qh, p.seed, l, hi - lo, bf16=p.bf16, start=lo)
             raw[lo:hi] = torch.from_numpy(rows).to(dev, bf)
-        # pooled-level synthesis: chunk = 1 pooling is the identity; this normalises
-        M.msa_pool_encode(raw, co_d, co_d, cd, 1, True, out=store[l])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        M.msa_pool_encode(raw, to_d, co_d, cd, pool_chunk, True, out=store[l])
+        e1.record()
+        torch.cuda.synchronize()
+        encode_ms.append(e0.elapsed_time(e1))
     torch.cuda.synchronize()
     log(f"routing-key store ready in {time.time() - t0:.1f} s")
 
@@ -101,13 +118,21 @@ def main():
     t0 = time.time()
     tier = args.kv_tier
     kbar, vbar = [], []
+    kv_scale = -3 if p.pooled_level else 0
+
+    def content(l, tid, out):
+        """pooled K or V of layer l into out (device)"""
+        SD.fill(raw, p.seed, l, tid, scale_pow2=kv_scale)
+        return M.msa_pool_encode(raw, to_d, co_d, cd, pool_chunk, False, out=out)
+
     if tier == "host":
         try:
+            tmp = torch.empty((N, H, d), dtype=bf, device=dev)
             for l in range(layers):
                 for lst, tid in ((kbar, synth.T_K), (vbar, synth.T_V)):
-                    SD.fill(raw, p.seed, l, tid, scale_pow2=-3)
+                    content(l, tid, tmp)
                     h = torch.empty((N, H, d), dtype=bf, pin_memory=True)
-                    h.copy_(raw)
+                    h.copy_(tmp)
                     lst.append(h)
                 log(f"host tier layer {l} ready ({time.time() - t0:.1f} s)")
             torch.cuda.synchronize()
@@ -119,8 +144,8 @@ def main():
             tier = "hbm"
     if tier == "hbm":
         for l in range(layers):
-            kbar.append(SD.fill(torch.empty((N, H, d), dtype=bf, device=dev), p.seed, l, synth.T_K, scale_pow2=-3))
-            vbar.append(SD.fill(torch.empty((N, H, d), dtype=bf, device=dev), p.seed, l, synth.T_V, scale_pow2=-3))
+            kbar.append(content(l, synth.T_K, torch.empty((N, H, d), dtype=bf, device=dev)))
+            vbar.append(content(l, synth.T_V, torch.empty((N, H, d), dtype=bf, device=dev)))
         torch.cuda.synchronize()
     del raw
     log(f"content K/V tier '{tier}' ready in {time.time() - t0:.1f} s")
@@ -152,8 +177,9 @@ def main():
     # needle check on one pass (a property of the planted data, not timed)
     step()
     torch.cuda.synchronize()
-    ids0 = runner.ids.cpu().numpy()[0]
-    recall = float(np.mean([n in set(ids0.tolist()) for n in needles]))
+    ids_all = runner.ids.cpu().numpy()
+    recall = float(np.mean([int(nd) in set(ids_all[i if p.needle_per_query else 0].tolist())
+                            for i, nd in enumerate(needles)]))
 
     for _ in range(args.warmup):
         step()
@@ -185,9 +211,18 @@ def main():
     alg_bytes = store_bytes + N * 4 + p.B * p.T * H * d * esz + 2 * p.B * D * 4
     route_avg_ms = float(np.mean(route_ms))
     achieved = alg_bytes / (route_avg_ms * 1e-3) / 1e9
+    # attention: K/V of the context and the local part, read once per KV head, plus Q and O
+    ctx_len = runner.ctx_len.cpu().numpy().astype(np.int64)
+    attn_bytes = int((ctx_len + p.L_loc).sum()) * H * d * 2 * esz + p.B * p.T * p.Hq * d * (esz + 4)
+    attn_gbps = attn_bytes * layers / (stage[3] * 1e-3) / 1e9
+    raw_bytes = n_rows * H * d * esz
+    encode_gbps = (raw_bytes + store_bytes) / (float(np.median(encode_ms)) * 1e-3) / 1e9
 
+    workload = (f"{p.name}: {int(p.lengths.sum())}-token memory, {D} docs, chunk {p.chunk}, {N} chunks/layer, "
+                f"{layers} routed layers, H={H}, d={d}; {p.B} quer{'y' if p.B == 1 else 'ies'} x T={p.T}, "
+                f"Hq={p.Hq}, L_loc={p.L_loc}, k={p.k}")
     res = {
-        "metric": "routing-key (K_r) scan GB/s over the whole route+attn step, 100M-token memory",
+        "metric": "routing-key (K_r) scan GB/s over the whole route+attn step",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -199,9 +234,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if p.bf16 else "f32",
         "data": "synthetic (seeded counter-based generator; planted needles)",
-        "config": {"workload": f"{p.name}: 100M-token memory, {D} docs x 512 tok, chunk {p.chunk}, "
-                               f"{N} chunks/layer, {layers} routed layers, H={H}, d={d}; query T={p.T}, "
-                               f"Hq={p.Hq}, L_loc={p.L_loc}, k={p.k}",
+        "config": {"workload": workload,
                    "global_batch": p.B, "seq_len": p.T, "parallelism": "single GPU",
                    "kv_tier": tier, "gather": args.gather if tier == "host" else "hbm"},
         "route_attn_us_per_query": round(ms_per_step * 1e3 / p.B, 1),
@@ -209,6 +242,10 @@ def main():
         "routing_frac_of_8TBps": round(routing_gbps / 8000, 4),
         "stage_ms_per_step": {"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
                               "gather": round(stage[2], 4), "attention": round(stage[3], 4)},
+        "attention_GBps": round(attn_gbps, 1),
+        "attention_frac_of_8TBps": round(attn_gbps / 8000, 4),
+        "attention_bytes_per_layer": attn_bytes,
+        "encode_GBps": round(encode_gbps, 1),
         "needle_recall_layer0": recall,
         "roofline": {"kernel": "msa_route_score (route_score_mfma_kernel + score fill)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
@@ -221,6 +258,20 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def copy_calibration(torch):
+    """A plain device copy of 1 GiB, three times: the reference that scales the
+    HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the other kernels."""
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty(n, dtype=torch.uint8, device="cuda")
+    x.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+
+
 def cpu_baseline(p, n_sample_chunks):
     """The float64 oracle's routing (score + top-k) on a bounded sample of the
     same workload: layer 0, the first documents of the memory."""
@@ -231,13 +282,18 @@ def cpu_baseline(p, n_sample_chunks):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    n_docs = n_sample_chunks // p.max_doc_chunks
+    n_docs = int(np.searchsorted(p.chunk_off, n_sample_chunks, side="right") - 1)
+    n_docs = max(1, min(n_docs, p.n_docs))
     co = p.chunk_off[: n_docs + 1]
     n = int(co[-1])
-    raw = synth.normal(p.seed, synth.stream_id(0, synth.T_KR), 0, n * p.H * p.d, bf16=p.bf16)
-    raw = raw.reshape(n, p.H, p.d)
     qr = synth.tensor(p.qseed, 0, synth.T_QR, (p.B, p.T, p.H, p.d), bf16=p.bf16)
-    store = O.pool_encode(raw, co, 1, True, "bf16" if p.bf16 else "f32")   # offline stage, untimed
+    if p.pooled_level:
+        rows, to, chunk = n, co, 1
+    else:
+        rows, to, chunk = int(p.tok_off[n_docs]), p.tok_off[: n_docs + 1], p.chunk
+    raw = synth.normal(p.seed, synth.stream_id(0, synth.T_KR), 0, rows * p.H * p.d, bf16=p.bf16)
+    raw = raw.reshape(rows, p.H, p.d)
+    store = O.pool_encode(raw, to, chunk, True, "bf16" if p.bf16 else "f32")   # offline stage, untimed
     del raw
     t0 = time.perf_counter()
     s = O.route_scores(qr, store, co)
@@ -246,8 +302,8 @@ def cpu_baseline(p, n_sample_chunks):
     gb = n * p.H * p.d * (2 if p.bf16 else 4) / 1e9
     return {"value": round(gb / dt, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"layer 0, first {n_docs} documents ({n} pooled chunks, {gb:.2f} GB of bf16 routing keys), "
-                      f"routing score + top-k for one {p.T}-token query, float64"}
+            "sample": f"layer 0, first {n_docs} documents ({n} pooled chunks, {gb:.2f} GB of routing keys), "
+                      f"routing score + top-k for {p.B} x {p.T}-token queries, float64"}
 
 
 if __name__ == "__main__":

@@ -120,39 +120,57 @@ __device__ __forceinline__ KeySrc key_src(int j, int b, int ctxl, int n_keys, in
   return k;
 }
 
+// ---------------------------------------------------------------- decode (one row tile)
+// One workgroup per (query b, key split, group of up to 8 KV heads); wave w
+// owns KV head g = 8 * hg + w and the (at most 16) query rows of that head.
+// The RoPE rows of the step's 32 keys are the same for every head, so the
+// workgroup stages them once in LDS; each wave streams its own head's K and
+// V.  The next step's K, V and RoPE rows are loaded while the current step
+// is computed.
+
+constexpr int DC_TAB_STRIDE = 528;                 // bytes per key row of (cos, sin) in LDS (512 + pad)
+constexpr int DC_TAB_BYTES = 32 * DC_TAB_STRIDE;
+
+struct DcRegs {
+  uint4 k[2][4];     // K rows (two 16-key tiles) of this wave's head
+  uint4 v[2][4];     // V rows for the transpose
+  uint4 t[2];        // this thread's share of the step's RoPE rows
+};
+
 template <int G>
-__global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
+__global__ __launch_bounds__(512) void attn_decode_kernel(
     const uint16_t* __restrict__ q, int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_ctx,
     const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
     const float2* __restrict__ tab, int P, float scale_log2, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
-    int n_splits, int keys_per_split, int n_rt) {
+    int n_splits, int keys_per_split, int n_hg) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int nw = blockDim.x / 64;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int lc = lane % 16, g4 = lane / 16;
-  unsigned char* vt = smem + size_t(wave) * AT_VT_BYTES;
+  unsigned char* tabs = smem;                                     // [2][32 keys][DC_TAB_STRIDE]
+  unsigned char* vt = smem + 2 * DC_TAB_BYTES + size_t(wave) * AT_VT_BYTES;
 
-  int64_t gw = int64_t(blockIdx.x) * AT_WAVES + wave;
-  const int split = int(gw % n_splits);
-  gw /= n_splits;
-  const int rt = int(gw % n_rt);
-  gw /= n_rt;
-  const int g = int(gw % Hkv);
-  const int b = int(gw / Hkv);
-  if (b >= B) return;
-
-  // query row of this lane's column
-  const int r = rt * 16 + lc;
-  const int t = r / G, hh = r % G;
-  const bool row_ok = t < T;
-  const int hq = g * G + hh;
-  const int horizon = L_loc - T + t;  // last visible local index for this row
+  int64_t wg = blockIdx.x;
+  const int split = int(wg % n_splits);
+  wg /= n_splits;
+  const int hg = int(wg % n_hg);
+  const int b = int(wg / n_hg);
+  const int g = hg * 8 + wave;
+  const bool head_ok = g < Hkv;
+  const int gg = head_ok ? g : 0;
   const int64_t kv_stride = int64_t(Hkv) * AT_D;
+
+  const int r = lc;                       // the only row tile
+  const int t = r / G, hh = r % G;
+  const bool row_ok = head_ok && t < T;
+  const int tt = row_ok ? t : 0;
+  const int hq = gg * G + hh;
+  const int horizon = L_loc - T + t;
 
   bf16x8 bq[4];
   {
     uint4 qv[4];
-    const int tt = row_ok ? t : 0;
     const uint16_t* qp = q + ((int64_t(b) * T + tt) * Hq + hq) * AT_D + 8 * g4;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qv[kk] = *reinterpret_cast<const uint4*>(qp + 32 * kk);
@@ -168,28 +186,118 @@ __global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
   const int j_begin = split * keys_per_split;
   const int j_end = min(n_keys, j_begin + keys_per_split);
 
+  // RoPE rows: the workgroup's threads split the 32 rows x 512 B of a step
+  const int nthr = nw * 64;
+  auto load_k = [&](int j0, DcRegs& R) {
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const KeySrc ks = key_src(j0 + 16 * tau + lc, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+      const uint16_t* kp = (ks.local ? k_loc : k_ctx) + ks.row * kv_stride + int64_t(gg) * AT_D + 8 * g4;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) R.k[tau][kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
+    }
+  };
+  auto load_vt = [&](int j0, DcRegs& R) {
+#pragma unroll
+    for (int rho = 0; rho < 2; ++rho)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const KeySrc ks = key_src(j0 + 16 * rho + 4 * g4 + i, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+        const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(gg) * AT_D + 8 * lc;
+        R.v[rho][i] = *reinterpret_cast<const uint4*>(vp);
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int piece = tid + u * nthr;         // 16-byte pieces: 32 rows x 32 pieces
+      if (piece < 32 * 32) {
+        const int key = piece / 32, off = piece % 32;
+        const KeySrc ks = key_src(j0 + key, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+        R.t[u] = reinterpret_cast<const uint4*>(tab + int64_t(ks.pos) * (AT_D / 2))[off];
+      }
+    }
+  };
+  auto store_tab = [&](const DcRegs& R, unsigned char* buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int piece = tid + u * nthr;
+      if (piece < 32 * 32)
+        *reinterpret_cast<uint4*>(buf + (piece / 32) * DC_TAB_STRIDE + (piece % 32) * 16) = R.t[u];
+    }
+  };
+
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // V tile -> this wave's LDS, transposed: vt[d][slot], slot 8*g + 4*tau + i <-> key 16*tau + 4*g + i
+  auto store_vt = [&](const DcRegs& R) {
+#pragma unroll
+    for (int rho = 0; rho < 2; ++rho) {
+      const uint4* vv = R.v[rho];
+      const uint32_t w0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
+      const uint32_t w1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+      const uint32_t w2[4] = {vv[2].x, vv[2].y, vv[2].z, vv[2].w};
+      const uint32_t w3[4] = {vv[3].x, vv[3].y, vv[3].z, vv[3].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) ? 16 : 0;
+        const uint32_t a0 = (w0[e / 2] >> sh) & 0xFFFFu, a1 = (w1[e / 2] >> sh) & 0xFFFFu;
+        const uint32_t a2 = (w2[e / 2] >> sh) & 0xFFFFu, a3 = (w3[e / 2] >> sh) & 0xFFFFu;
+        *reinterpret_cast<uint2*>(vt + (8 * lc + e) * AT_VT_STRIDE + 2 * (8 * g4 + 4 * rho)) =
+            make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+      }
+    }
+  };
+
+  // Pipeline: K of step s+1 is requested before the S^T of step s; V and the
+  // RoPE rows of step s+1 right after it.  V^T of step s+1 and its RoPE rows
+  // are written to LDS at the end of step s, so only K waits in registers.
+  DcRegs cur, nxt;
+  if (j_begin < j_end) {
+    load_k(j_begin, cur);
+    load_vt(j_begin, cur);
+    store_tab(cur, tabs);
+    store_vt(cur);
+  }
+  __syncthreads();
+  int tb = 0;
   for (int j0 = j_begin; j0 < j_end; j0 += 32) {
-    // ---- S^T = K_rot . Q_rot^T for two 16-key tiles
+    const bool has_next = j0 + 32 < j_end;
+    if (has_next) load_k(j0 + 32, nxt);
+    const unsigned char* tbuf = tabs + tb * DC_TAB_BYTES;
+    // ---- rotate K with the staged RoPE rows, S^T = K_rot . Q_rot^T
     f32x4 s[2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const KeySrc ks = key_src(j0 + 16 * tau + lc, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
-      const uint16_t* kp = (ks.local ? k_loc : k_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 8 * g4;
-      uint4 kv[4];
+      uint4 kv[4] = {cur.k[tau][0], cur.k[tau][1], cur.k[tau][2], cur.k[tau][3]};
+      const unsigned char* row = tbuf + (16 * tau + lc) * DC_TAB_STRIDE;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kv[kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
-      rope_rotate(kv, tab + int64_t(ks.pos) * (AT_D / 2), g4);
+      for (int kk = 0; kk < 2; ++kk) {
+        float lo[8], hi[8];
+        unpack8(kv[kk], lo);
+        unpack8(kv[kk + 2], hi);
+        const float4* c4 = reinterpret_cast<const float4*>(row + (32 * kk + 8 * g4) * 8);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float4 cs = c4[e2];
+          const float a0 = lo[2 * e2], b0 = hi[2 * e2], a1 = lo[2 * e2 + 1], b1 = hi[2 * e2 + 1];
+          lo[2 * e2] = a0 * cs.x - b0 * cs.y;
+          hi[2 * e2] = b0 * cs.x + a0 * cs.y;
+          lo[2 * e2 + 1] = a1 * cs.z - b1 * cs.w;
+          hi[2 * e2 + 1] = b1 * cs.z + a1 * cs.w;
+        }
+        kv[kk] = pack8(lo);
+        kv[kk + 2] = pack8(hi);
+      }
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv[kk]), bq[kk], acc, 0, 0, 0);
       s[tau] = acc;
     }
+    __builtin_amdgcn_sched_barrier(0);   // keep the next V / RoPE loads after this step's S^T
+    if (has_next) load_vt(j0 + 32, nxt);
     // ---- mask and online softmax for column lc (base-2 domain)
     float x[2][4];
     float mt = -INFINITY;
@@ -223,39 +331,24 @@ __global__ __launch_bounds__(AT_THREADS) void attn_mfma_kernel(
     const bf16x8 pb = __builtin_bit_cast(
         bf16x8, make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                            pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])));
-
-    // ---- V tile -> LDS, transposed: vt[d][slot], slot 8*g + 4*tau + i <-> key 16*tau + 4*g + i
-#pragma unroll
-    for (int rho = 0; rho < 2; ++rho) {
-      uint4 vv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const KeySrc ks = key_src(j0 + 16 * rho + 4 * g4 + i, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
-        const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 8 * lc;
-        vv[i] = *reinterpret_cast<const uint4*>(vp);
-      }
-      const uint32_t w0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
-      const uint32_t w1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
-      const uint32_t w2[4] = {vv[2].x, vv[2].y, vv[2].z, vv[2].w};
-      const uint32_t w3[4] = {vv[3].x, vv[3].y, vv[3].z, vv[3].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) ? 16 : 0;
-        const uint32_t a0 = (w0[e / 2] >> sh) & 0xFFFFu, a1 = (w1[e / 2] >> sh) & 0xFFFFu;
-        const uint32_t a2 = (w2[e / 2] >> sh) & 0xFFFFu, a3 = (w3[e / 2] >> sh) & 0xFFFFu;
-        uint2 pk = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-        *reinterpret_cast<uint2*>(vt + (8 * lc + e) * AT_VT_STRIDE + 2 * (8 * g4 + 4 * rho)) = pk;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     // ---- O^T += V^T . P^T
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const uint4 a = *reinterpret_cast<const uint4*>(vt + (16 * dt + lc) * AT_VT_STRIDE + 16 * g4);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[dt], 0, 0, 0);
     }
-    __builtin_amdgcn_wave_barrier();
+    if (has_next) {
+      // LDS operations of one wave complete in order, so this step's V^T reads
+      // above precede the next step's writes to the same buffer
+      store_vt(nxt);
+      store_tab(nxt, tabs + (tb ^ 1) * DC_TAB_BYTES);
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) cur.k[tau][kk] = nxt.k[tau][kk];
+    }
+    __syncthreads();
+    tb ^= 1;
   }
 
   // ---- partial result of this split: O^T[d = 16dt + 4*g4 + i][row lc]
@@ -406,17 +499,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     for (int dt = 0; dt < 8; ++dt) o[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  PfRegs R;
-  if (j_begin < j_end) {
-    load_step(j_begin, R);
-    store_step(R, smem);
-  }
-  __syncthreads();
-  int cur = 0;
-  for (int j0 = j_begin; j0 < j_end; j0 += 32) {
-    const bool has_next = j0 + 32 < j_end;
-    if (has_next) load_step(j0 + 32, R);
-    const unsigned char* kb = smem + cur * PF_BUF;
+  auto compute_step = [&](int j0, const unsigned char* kb) {
     const unsigned char* vb = kb + PF_K_BYTES;
     // S^T for both 16-key tiles, for every row tile of this wave
     bf16x8 ka[2][4];
@@ -474,7 +557,29 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
 #pragma unroll
       for (int i = 0; i < RTW; ++i) o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[i], o[i][dt], 0, 0, 0);
     }
-    if (has_next) store_step(R, smem + (cur ^ 1) * PF_BUF);
+  };
+
+  // Two steps of global loads in flight: while step s is computed from one
+  // LDS buffer, step s+1 waits in registers for the other buffer and step
+  // s+2 is being loaded.
+  PfRegs RA, RB;
+  if (j_begin < j_end) {
+    load_step(j_begin, RA);
+    store_step(RA, smem);
+    if (j_begin + 32 < j_end) load_step(j_begin + 32, RB);
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int j0 = j_begin; j0 < j_end; j0 += 64) {
+    if (j0 + 64 < j_end) load_step(j0 + 64, RA);
+    compute_step(j0, smem + cur * PF_BUF);
+    if (j0 + 32 < j_end) store_step(RB, smem + (cur ^ 1) * PF_BUF);
+    __syncthreads();
+    cur ^= 1;
+    if (j0 + 32 >= j_end) break;
+    if (j0 + 96 < j_end) load_step(j0 + 96, RB);
+    compute_step(j0 + 32, smem + cur * PF_BUF);
+    if (j0 + 64 < j_end) store_step(RA, smem + (cur ^ 1) * PF_BUF);
     __syncthreads();
     cur ^= 1;
   }
@@ -508,10 +613,10 @@ __global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float2
   const float mu = m == -INFINITY ? 0.f : m;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.f;
+#pragma unroll 4
   for (int s = 0; s < n_splits; ++s) {
     const float2 ml = ws_ml[s * rows + row];
-    if (ml.y == 0.f) continue;
-    const float w = exp2f(ml.x - mu);
+    const float w = exp2f(ml.x - mu);   // 0 for a split that saw no visible key
     den += w * ml.y;
     const float4 v = *reinterpret_cast<const float4*>(ws_o + (s * rows + row) * d + e);
     num.x += w * v.x;
@@ -624,6 +729,7 @@ struct AttnPlan {
   bool prefill;     // workgroup-cooperative kernel (2+ row tiles)
   int rtw;          // row tiles per wave (prefill)
   int n_rg;         // row groups (prefill)
+  int n_hg;         // KV-head groups of 8 (decode)
   int P;            // rows of the RoPE table
   int n_rt;         // 16-row tiles per (b, g)
   int n_splits;
@@ -649,8 +755,9 @@ static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int m
     units = int64_t(B) * Hkv * p.n_rg;      // workgroups per split
     target = 256;                            // about one workgroup per CU
   } else {
-    units = int64_t(B) * Hkv * p.n_rt;      // waves per split
-    target = 4096;
+    p.n_hg = (Hkv + 7) / 8;
+    units = int64_t(B) * p.n_hg;            // workgroups per split
+    target = 1024;
   }
   int64_t s = (target + units - 1) / units;
   s = std::max<int64_t>(1, std::min<int64_t>(s, (n_keys_max + 63) / 64));
@@ -741,23 +848,25 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
       MSA_LAUNCH_CHECK();
       return MSA_OK;
     }
-    const int64_t waves = int64_t(B) * Hkv * p.n_rt * p.n_splits;
-    const dim3 grid(unsigned((waves + AT_WAVES - 1) / AT_WAVES)), block(AT_THREADS);
-    const size_t smem = size_t(AT_WAVES) * AT_VT_BYTES;
+    const int nw = 8;   // waves beyond Hkv only help stage the RoPE rows
+    const dim3 grid(unsigned(int64_t(B) * p.n_hg * p.n_splits)), block(unsigned(64 * nw));
+    const size_t smem = 2 * size_t(DC_TAB_BYTES) + size_t(nw) * AT_VT_BYTES;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-#define AT_LAUNCH(GV)                                                                                            \
-  hipLaunchKernelGGL((attn_mfma_kernel<GV>), grid, block, smem, s, static_cast<const uint16_t*>(q), B, T, Hq, Hkv, \
-                     static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos, ctx_len,  \
-                     max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc), L_loc,    \
-                     q_pos_offset, tab, p.P, scale_log2, ws_o, ws_ml, p.n_splits, p.keys_per_split, p.n_rt)
+#define DC_LAUNCH(GV)                                                                                              \
+  MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_decode_kernel<GV>),                        \
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)));                     \
+  hipLaunchKernelGGL((attn_decode_kernel<GV>), grid, block, smem, s, static_cast<const uint16_t*>(q), B, T, Hq, Hkv, \
+                     static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos, ctx_len,     \
+                     max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc), L_loc,       \
+                     q_pos_offset, tab, p.P, scale_log2, ws_o, ws_ml, p.n_splits, p.keys_per_split, p.n_hg)
     switch (G) {
-      case 1: AT_LAUNCH(1); break;
-      case 2: AT_LAUNCH(2); break;
-      case 4: AT_LAUNCH(4); break;
-      case 8: AT_LAUNCH(8); break;
-      default: AT_LAUNCH(16); break;
+      case 1: DC_LAUNCH(1); break;
+      case 2: DC_LAUNCH(2); break;
+      case 4: DC_LAUNCH(4); break;
+      case 8: DC_LAUNCH(8); break;
+      default: DC_LAUNCH(16); break;
     }
-#undef AT_LAUNCH
+#undef DC_LAUNCH
     MSA_LAUNCH_CHECK();
     const int64_t rows = int64_t(B) * T * Hq;
     hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * (d / 4) + 255) / 256)), dim3(256), 0, s, ws_o,
