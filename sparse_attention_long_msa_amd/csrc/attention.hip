@@ -31,8 +31,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int AT_D = 128;
 constexpr int AT_WAVES = 4;
 constexpr int AT_THREADS = 64 * AT_WAVES;
-constexpr int AT_VT_STRIDE = 80;                  // bytes per d-row of the transposed V tile (32 keys + pad, 16-byte aligned)
-constexpr int AT_VT_BYTES = AT_D * AT_VT_STRIDE;  // per wave
 constexpr int AT_VEC_THREADS = 256;
 constexpr int AT_VEC_MAX_KEYS = 32768;
 
@@ -63,6 +61,30 @@ __device__ __forceinline__ void unpack8(const uint4& u, float (&x)[8]) {
 __device__ __forceinline__ uint4 pack8(const float (&x)[8]) {
   return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                     pack_bf16x2(x[6], x[7]));
+}
+
+// Row-major V tile in LDS: 32 keys x 128 d (bf16), row stride AT_VS bytes.
+constexpr int AT_VS = 288;                   // 256 + 32: the 16 rows of one transpose read hit 8 bank groups
+constexpr int AT_V_BYTES = 32 * AT_VS;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// A operand of O^T = V^T P^T for d-tile dt: lane (lc, g4) receives
+// V[16*tau + 4*g4 + r][16*dt + lc] in slot 4*tau + r.  ds_read_b64_tr_b16
+// hands lane i of each 16-lane group element i % 4 of the 8-byte chunks
+// addressed by lanes 4r + i/4 (r = 0..3); so lane j = 4r + q of group g4
+// addresses key 16*tau + 4*g4 + r, dims 16*dt + 4q .. +3.
+__device__ __forceinline__ bf16x8 pv_operand(const unsigned char* vlds, int dt, int lane) {
+  const int g4 = lane / 16, j = lane % 16;
+  const int r = j / 4, q = j % 4;
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  const unsigned char* p0 = vlds + (4 * g4 + r) * AT_VS + (16 * dt + 4 * q) * 2;
+  const unsigned char* p1 = p0 + 16 * AT_VS;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p0));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p1));
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
 }
 
 // Rotate the lane's 16 (m, m + 64) pairs: lo[kk] holds dims 32kk + 8*g4 + e,
@@ -133,7 +155,7 @@ constexpr int DC_TAB_BYTES = 32 * DC_TAB_STRIDE;
 
 struct DcRegs {
   uint4 k[2][4];     // K rows (two 16-key tiles) of this wave's head
-  uint4 v[2][4];     // V rows for the transpose
+  uint4 v[2][4];     // V rows: key 16*rho + 4*g4 + i, dims 8*lc .. +7
   uint4 t[2];        // this thread's share of the step's RoPE rows
 };
 
@@ -149,7 +171,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int lc = lane % 16, g4 = lane / 16;
   unsigned char* tabs = smem;                                     // [2][32 keys][DC_TAB_STRIDE]
-  unsigned char* vt = smem + 2 * DC_TAB_BYTES + size_t(wave) * AT_VT_BYTES;
+  unsigned char* vrm = smem + 2 * DC_TAB_BYTES + size_t(wave) * AT_V_BYTES;   // this wave's V rows
 
   int64_t wg = blockIdx.x;
   const int split = int(wg % n_splits);
@@ -185,10 +207,21 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
   const int n_keys = ctxl + L_loc;
   const int j_begin = split * keys_per_split;
   const int j_end = min(n_keys, j_begin + keys_per_split);
-
-  // RoPE rows: the workgroup's threads split the 32 rows x 512 B of a step
   const int nthr = nw * 64;
+  // a step whose 32 keys are all local tokens addresses them affinely
+  auto all_local = [&](int j0) { return j0 >= ctxl && j0 + 32 <= n_keys; };
+
   auto load_k = [&](int j0, DcRegs& R) {
+    if (all_local(j0)) {
+      const uint16_t* kb = k_loc + (int64_t(b) * L_loc + (j0 - ctxl)) * kv_stride + int64_t(gg) * AT_D + 8 * g4;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const uint16_t* kp = kb + int32_t(16 * tau + lc) * int32_t(kv_stride);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) R.k[tau][kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
+      }
+      return;
+    }
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const KeySrc ks = key_src(j0 + 16 * tau + lc, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
@@ -198,6 +231,21 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
     }
   };
   auto load_vt = [&](int j0, DcRegs& R) {
+    if (all_local(j0)) {
+      const uint16_t* vb = v_loc + (int64_t(b) * L_loc + (j0 - ctxl)) * kv_stride + int64_t(gg) * AT_D + 8 * lc;
+#pragma unroll
+      for (int rho = 0; rho < 2; ++rho)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          R.v[rho][i] = *reinterpret_cast<const uint4*>(vb + int32_t(16 * rho + 4 * g4 + i) * int32_t(kv_stride));
+      const float2* trow = tab + int64_t(qpo + j0 - ctxl) * (AT_D / 2);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int piece = tid + u * nthr;     // 16-byte pieces: 32 rows x 32 pieces
+        if (piece < 32 * 32) R.t[u] = reinterpret_cast<const uint4*>(trow + (piece / 32) * (AT_D / 2))[piece % 32];
+      }
+      return;
+    }
 #pragma unroll
     for (int rho = 0; rho < 2; ++rho)
 #pragma unroll
@@ -208,7 +256,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
       }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int piece = tid + u * nthr;         // 16-byte pieces: 32 rows x 32 pieces
+      const int piece = tid + u * nthr;
       if (piece < 32 * 32) {
         const int key = piece / 32, off = piece % 32;
         const KeySrc ks = key_src(j0 + key, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
@@ -224,41 +272,29 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
         *reinterpret_cast<uint4*>(buf + (piece / 32) * DC_TAB_STRIDE + (piece % 32) * 16) = R.t[u];
     }
   };
+  // V rows stay row-major in LDS; the PV operand is read with transpose loads
+  auto store_v = [&](const DcRegs& R) {
+#pragma unroll
+    for (int rho = 0; rho < 2; ++rho)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(vrm + (16 * rho + 4 * g4 + i) * AT_VS + 16 * lc) = R.v[rho][i];
+  };
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // V tile -> this wave's LDS, transposed: vt[d][slot], slot 8*g + 4*tau + i <-> key 16*tau + 4*g + i
-  auto store_vt = [&](const DcRegs& R) {
-#pragma unroll
-    for (int rho = 0; rho < 2; ++rho) {
-      const uint4* vv = R.v[rho];
-      const uint32_t w0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
-      const uint32_t w1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
-      const uint32_t w2[4] = {vv[2].x, vv[2].y, vv[2].z, vv[2].w};
-      const uint32_t w3[4] = {vv[3].x, vv[3].y, vv[3].z, vv[3].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) ? 16 : 0;
-        const uint32_t a0 = (w0[e / 2] >> sh) & 0xFFFFu, a1 = (w1[e / 2] >> sh) & 0xFFFFu;
-        const uint32_t a2 = (w2[e / 2] >> sh) & 0xFFFFu, a3 = (w3[e / 2] >> sh) & 0xFFFFu;
-        *reinterpret_cast<uint2*>(vt + (8 * lc + e) * AT_VT_STRIDE + 2 * (8 * g4 + 4 * rho)) =
-            make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-      }
-    }
-  };
-
   // Pipeline: K of step s+1 is requested before the S^T of step s; V and the
-  // RoPE rows of step s+1 right after it.  V^T of step s+1 and its RoPE rows
+  // RoPE rows of step s+1 right after it.  V of step s+1 and its RoPE rows
   // are written to LDS at the end of step s, so only K waits in registers.
   DcRegs cur, nxt;
   if (j_begin < j_end) {
     load_k(j_begin, cur);
     load_vt(j_begin, cur);
     store_tab(cur, tabs);
-    store_vt(cur);
+    store_v(cur);
   }
   __syncthreads();
   int tb = 0;
@@ -333,14 +369,12 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
                            pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])));
     // ---- O^T += V^T . P^T
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint4 a = *reinterpret_cast<const uint4*>(vt + (16 * dt + lc) * AT_VT_STRIDE + 16 * g4);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[dt], 0, 0, 0);
-    }
+    for (int dt = 0; dt < 8; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pv_operand(vrm, dt, lane), pb, o[dt], 0, 0, 0);
     if (has_next) {
-      // LDS operations of one wave complete in order, so this step's V^T reads
+      // LDS operations of one wave complete in order, so this step's V reads
       // above precede the next step's writes to the same buffer
-      store_vt(nxt);
+      store_v(nxt);
       store_tab(nxt, tabs + (tb ^ 1) * DC_TAB_BYTES);
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
@@ -375,12 +409,12 @@ constexpr int PF_WAVES = 8;
 constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_KS = 272;                         // bytes per key row of K_rot in LDS (256 + pad)
 constexpr int PF_K_BYTES = 32 * PF_KS;
-constexpr int PF_BUF = PF_K_BYTES + AT_VT_BYTES;   // one step buffer
+constexpr int PF_BUF = PF_K_BYTES + AT_V_BYTES;    // one step buffer
 
 struct PfRegs {
   uint2 klo, khi;     // dims 4x..4x+3 and 64+4x..64+4x+3 of key t/16
   float4 cs0, cs1;    // (cos, sin) of m = 4x..4x+3 at the key's position
-  uint32_t v[4];      // V[4*kq + i][2*dp .. 2*dp+1]
+  uint4 v;            // V[t/16][8*(t%16) .. +7]
 };
 
 template <int G, int RTW>
@@ -434,8 +468,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
   const int j_end = min(n_keys, j_begin + keys_per_split);
 
   // cooperative mapping of one 32-key step
-  const int lk = tid / 16, lx = tid % 16;     // K: key, 4-dim block
-  const int vq = tid / 64, vdp = tid % 64;    // V: key quad, dim pair
+  const int lk = tid / 16, lx = tid % 16;     // K: key, 4-dim block; V: key, 8-dim block
 
   auto load_step = [&](int j0, PfRegs& R) {
     {
@@ -447,11 +480,10 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
       R.cs0 = cp[0];
       R.cs1 = cp[1];
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const KeySrc ks = key_src(j0 + 4 * vq + i, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
-      const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 2 * vdp;
-      R.v[i] = *reinterpret_cast<const uint32_t*>(vp);
+    {
+      const KeySrc ks = key_src(j0 + lk, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+      const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 8 * lx;
+      R.v = *reinterpret_cast<const uint4*>(vp);
     }
   };
   auto store_step = [&](const PfRegs& R, unsigned char* buf) {
@@ -476,17 +508,8 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     unsigned char* krow = buf + lk * PF_KS;
     *reinterpret_cast<uint2*>(krow + 8 * lx) = make_uint2(pack_bf16x2(ra[0], ra[1]), pack_bf16x2(ra[2], ra[3]));
     *reinterpret_cast<uint2*>(krow + 128 + 8 * lx) = make_uint2(pack_bf16x2(rb[0], rb[1]), pack_bf16x2(rb[2], rb[3]));
-    // V^T[d][slot]: keys 4vq..4vq+3 = 16*tau + 4*gg + (0..3) -> slots 8*gg + 4*tau + (0..3)
-    unsigned char* vt = buf + PF_K_BYTES;
-    const int tau = vq / 4, gg = vq % 4;
-#pragma unroll
-    for (int dd = 0; dd < 2; ++dd) {
-      const int sh = dd ? 16 : 0;
-      const uint32_t e0 = (R.v[0] >> sh) & 0xFFFFu, e1 = (R.v[1] >> sh) & 0xFFFFu;
-      const uint32_t e2 = (R.v[2] >> sh) & 0xFFFFu, e3 = (R.v[3] >> sh) & 0xFFFFu;
-      *reinterpret_cast<uint2*>(vt + (2 * vdp + dd) * AT_VT_STRIDE + 2 * (8 * gg + 4 * tau)) =
-          make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-    }
+    // V stays row-major; the PV operand is read with transpose loads
+    *reinterpret_cast<uint4*>(buf + PF_K_BYTES + lk * AT_VS + 16 * lx) = R.v;
   };
 
   float m_run[RTW], l_run[RTW];
@@ -553,7 +576,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vb + (16 * dt + lc) * AT_VT_STRIDE + 16 * g4));
+      const bf16x8 a = pv_operand(vb, dt, lane);
 #pragma unroll
       for (int i = 0; i < RTW; ++i) o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[i], o[i][dt], 0, 0, 0);
     }
@@ -850,7 +873,7 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
     }
     const int nw = 8;   // waves beyond Hkv only help stage the RoPE rows
     const dim3 grid(unsigned(int64_t(B) * p.n_hg * p.n_splits)), block(unsigned(64 * nw));
-    const size_t smem = 2 * size_t(DC_TAB_BYTES) + size_t(nw) * AT_VT_BYTES;
+    const size_t smem = 2 * size_t(DC_TAB_BYTES) + size_t(nw) * AT_V_BYTES;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
 #define DC_LAUNCH(GV)                                                                                              \
   MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_decode_kernel<GV>),                        \
