@@ -88,7 +88,8 @@ def main():
     # 100M-token preset is synthesised at pooled level (chunk = 1 pooling,
     # which only normalises); the others pool raw per-token tensors.
     t0 = time.time()
-    store = torch.empty((layers, N, H, d), dtype=bf, device=dev)
+    kr_layout = M.MSA_LAYOUT_TILED if p.bf16 else M.MSA_LAYOUT_ROWS
+    store = torch.empty((layers, M.padded_chunks(N, kr_layout), H, d), dtype=bf, device=dev)
     if p.pooled_level:
         rows_off, pool_chunk, n_rows, to_d = chunk_off, 1, N, co_d
     else:
@@ -107,7 +108,7 @@ def main():
             raw[lo:hi] = torch.from_numpy(rows).to(dev, bf)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        M.msa_pool_encode(raw, to_d, co_d, cd, pool_chunk, True, out=store[l])
+        M.msa_pool_encode(raw, to_d, co_d, cd, pool_chunk, True, out=store[l], layout=kr_layout)
         e1.record()
         torch.cuda.synchronize()
         encode_ms.append(e0.elapsed_time(e1))
@@ -154,7 +155,8 @@ def main():
 
     runner = M.LayerRunner(batch=p.B, tokens=p.T, q_heads=p.Hq, kv_heads=H, head_dim=d, n_docs=D, n_chunks=N,
                            k=p.k, max_doc_chunks=p.max_doc_chunks, local_len=p.L_loc, dtype=bf, device=dev,
-                           q_pos_offset=p.qpo, rope_base=p.rope_base, src_mode=src_mode, chunk_off_h=chunk_off)
+                           q_pos_offset=p.qpo, rope_base=p.rope_base, src_mode=src_mode, chunk_off_h=chunk_off,
+                           kr_layout=kr_layout)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):

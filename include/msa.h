@@ -54,6 +54,16 @@ typedef enum {
 typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
 
 typedef enum {
+  MSA_LAYOUT_ROWS = 0,  /* [n_chunks, H, d], row-major                                   */
+  MSA_LAYOUT_TILED = 1  /* groups of 16 chunks stored as [H][d/32][4][16][8]: chunk c, head h,
+                           element e sits at (c/16)*16*H*d + h*16*d + (e/32)*512 + ((e%32)/8)*128
+                           + (c%16)*8 + e%8.  Needs d % 32 == 0; the buffer holds
+                           ceil(n_chunks/16)*16 chunks and the padding chunks are zero.  It is
+                           the MFMA operand order of msa_route_score: every 16-byte-per-lane
+                           load of a wave reads 1 KB contiguous.                             */
+} msa_layout;
+
+typedef enum {
   MSA_SRC_DEVICE = 0,      /* K/V store in device memory (HBM)                          */
   MSA_SRC_HOST_MAPPED = 1, /* store in pinned host memory, read by the gather kernel     */
   MSA_SRC_HOST_MEMCPY = 2  /* store in pinned host memory, copied with hipMemcpyAsync on
@@ -95,6 +105,15 @@ int msa_chunk_doc_map(const int64_t* chunk_off, int64_t n_docs, int64_t n_chunks
                       void* stream);
 
 /*
+ * msa_tile_routing_keys - reorder a row-major pooled routing-key store
+ * [n_chunks, H, d] into MSA_LAYOUT_TILED (see msa_layout), zeroing the
+ * padding chunks of the last group.  A pure permutation (bit-exact).
+ *   src [n_chunks, H, d] dtype; dst ceil(n_chunks/16)*16 chunks, dtype
+ * Errors: INVALID_ARG (NULL, sizes, d % 32 != 0, src == dst).
+ */
+int msa_tile_routing_keys(int dtype, const void* src, int64_t n_chunks, int H, int d, void* dst, void* stream);
+
+/*
  * msa_pool_encode - Stage 1 ("Global Memory Encoding", README Inference
  * Pipeline; "chunk-wise mean pool", paper note 核心方法 > 架构).
  * For pooled chunk c = chunk j of document i and head h:
@@ -109,13 +128,14 @@ int msa_chunk_doc_map(const int64_t* chunk_off, int64_t n_docs, int64_t n_chunks
  *   x         [n_tok, H, d] dtype
  *   tok_off   [n_docs + 1] int64, chunk_off [n_docs + 1] int64 (chunk CSR of
  *             tok_off for this chunk size), chunk_doc [n_chunks] int32
- *   out       [n_chunks, H, d] dtype
- * Errors: INVALID_ARG (NULL, non-positive sizes, d odd), UNSUPPORTED
- * (H*d > 4096 or H*d not a multiple of 8).
+ *   out       [n_chunks, H, d] dtype in out_layout (msa_layout; MSA_LAYOUT_TILED
+ *             needs d % 32 == 0 and room for ceil(n_chunks/16)*16 chunks)
+ * Errors: INVALID_ARG (NULL, non-positive sizes, d odd, bad layout),
+ * UNSUPPORTED (H*d > 4096 or H*d not a multiple of 8).
  */
 int msa_pool_encode(int dtype, const void* x, const int64_t* tok_off, const int64_t* chunk_off,
                     const int32_t* chunk_doc, int64_t n_docs, int64_t n_tok, int64_t n_chunks, int H,
-                    int d, int chunk, int l2_normalize, void* out, void* stream);
+                    int d, int chunk, int l2_normalize, int out_layout, void* out, void* stream);
 
 /*
  * msa_route_score - Stage 2 routing score (README, Overall Design >
@@ -130,16 +150,18 @@ int msa_pool_encode(int dtype, const void* x, const int64_t* tok_off, const int6
  * the query norm is applied per (token, head) in float32.  The score matrix
  * is never materialised; the store is streamed once.
  *   q_r        [B, T, H, d] dtype (raw routing queries)
- *   kr_hat     [n_chunks, H, d] dtype
+ *   kr_hat     [n_chunks, H, d] dtype in kr_layout (msa_layout).  The MFMA
+ *              path (bf16, H = 8, d = 128) streams MSA_LAYOUT_TILED at full
+ *              HBM rate; MSA_LAYOUT_ROWS is accepted by every path.
  *   chunk_doc  [n_chunks] int32 (msa_chunk_doc_map); entries outside
  *              [0, n_docs) are ignored
  *   doc_score  [B, n_docs] float32 output
  *   ws         msa_route_score_workspace() bytes (may be 0 -> ws may be NULL)
- * Errors: INVALID_ARG (NULL, non-positive sizes), WORKSPACE, UNSUPPORTED
- * (d > 256 or d % 8 != 0).
+ * Errors: INVALID_ARG (NULL, non-positive sizes, bad layout), WORKSPACE,
+ * UNSUPPORTED (d > 256 or d % 8 != 0; MSA_LAYOUT_TILED outside the MFMA path).
  */
 size_t msa_route_score_workspace(int dtype, int B, int T, int H, int d, int64_t n_docs, int64_t n_chunks);
-int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
+int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat, int kr_layout,
                     const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks, float* doc_score,
                     void* ws, size_t ws_bytes, void* stream);
 

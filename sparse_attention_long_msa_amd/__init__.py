@@ -3,11 +3,13 @@
 Thin Python binding over the C-ABI library ``libmsa.so`` (``include/msa.h``):
 argument marshalling only; every step runs in the library's HIP kernels.
 PyTorch provides device memory and streams.  Importing fails loudly if the
-library has not been built (``python -m sparse_attention_long_msa_amd.build``).
+library has not been built (``python sparse_attention_long_msa_amd/build.py``).
 """
 from ._binding import (  # noqa: F401
     MSA_BF16,
     MSA_F32,
+    MSA_LAYOUT_ROWS,
+    MSA_LAYOUT_TILED,
     MSA_SRC_DEVICE,
     MSA_SRC_HOST_MAPPED,
     MSA_SRC_HOST_MEMCPY,
@@ -24,6 +26,8 @@ from ._binding import (  # noqa: F401
     msa_sparse_attn,
     msa_sparse_attn_workspace,
     msa_topk,
+    msa_tile_routing_keys,
     msa_topk_workspace,
+    padded_chunks,
 )
 from .pipeline import LayerRunner  # noqa: F401

@@ -16,6 +16,7 @@ lib_path = os.path.join(_HERE, "libmsa.so")
 
 MSA_F32, MSA_BF16 = 0, 1
 MSA_SRC_DEVICE, MSA_SRC_HOST_MAPPED, MSA_SRC_HOST_MEMCPY = 0, 1, 2
+MSA_LAYOUT_ROWS, MSA_LAYOUT_TILED = 0, 1
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -29,9 +30,10 @@ _SIGS = {
     "msa_last_error": (ctypes.c_char_p, []),
     "msa_chunk_offsets": (_I, [_P, _L, _I, _P]),
     "msa_chunk_doc_map": (_I, [_P, _L, _L, _P, _P]),
-    "msa_pool_encode": (_I, [_I, _P, _P, _P, _P, _L, _L, _L, _I, _I, _I, _I, _P, _P]),
+    "msa_tile_routing_keys": (_I, [_I, _P, _L, _I, _I, _P, _P]),
+    "msa_pool_encode": (_I, [_I, _P, _P, _P, _P, _L, _L, _L, _I, _I, _I, _I, _I, _P, _P]),
     "msa_route_score_workspace": (_S, [_I, _I, _I, _I, _I, _L, _L]),
-    "msa_route_score": (_I, [_I, _P, _I, _I, _I, _I, _P, _P, _L, _L, _P, _P, _S, _P]),
+    "msa_route_score": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P, _P, _S, _P]),
     "msa_topk_workspace": (_S, [_I, _L, _I]),
     "msa_topk": (_I, [_P, _I, _L, _I, _P, _P, _P, _S, _P]),
     "msa_gather_kv": (_I, [_I, _P, _I, _I, _P, _P, _L, _I, _P, _P, _L, _I, _I, _I, _I,
@@ -50,10 +52,13 @@ class MsaError(RuntimeError):
 
 def _load():
     if not os.path.exists(lib_path):
-        raise ImportError(f"{lib_path} is not built: run `python -m sparse_attention_long_msa_amd.build`")
+        raise ImportError(f"{lib_path} is not built: run `python sparse_attention_long_msa_amd/build.py`")
     h = ctypes.CDLL(lib_path)
     for name, (res, args) in _SIGS.items():
-        f = getattr(h, name)
+        try:
+            f = getattr(h, name)
+        except AttributeError as e:
+            raise ImportError(f"{lib_path} lacks {name}: rebuild with `python sparse_attention_long_msa_amd/build.py`") from e
         f.restype = res
         f.argtypes = args
     return h
@@ -120,14 +125,29 @@ def msa_chunk_doc_map(chunk_off, n_chunks, chunk_doc=None, stream=None):
     return chunk_doc
 
 
-def msa_pool_encode(x, tok_off, chunk_off, chunk_doc, chunk, l2_normalize, out=None, stream=None):
+def padded_chunks(n_chunks, layout):
+    """Rows a store of n_chunks chunks occupies in the given layout."""
+    return (n_chunks + 15) // 16 * 16 if layout == MSA_LAYOUT_TILED else n_chunks
+
+
+def msa_tile_routing_keys(src, out=None, stream=None):
+    n_chunks, H, d = src.shape
+    if out is None:
+        out = torch.empty((padded_chunks(n_chunks, MSA_LAYOUT_TILED), H, d), dtype=src.dtype, device=src.device)
+    _check("msa_tile_routing_keys", lib.msa_tile_routing_keys(_dtype(src), _ptr(src), n_chunks, H, d, _ptr(out),
+                                                              _stream(stream)))
+    return out
+
+
+def msa_pool_encode(x, tok_off, chunk_off, chunk_doc, chunk, l2_normalize, out=None, layout=MSA_LAYOUT_ROWS,
+                    stream=None):
     n_tok, H, d = x.shape
     n_chunks = chunk_doc.numel()
     if out is None:
-        out = torch.empty((n_chunks, H, d), dtype=x.dtype, device=x.device)
+        out = torch.empty((padded_chunks(n_chunks, layout), H, d), dtype=x.dtype, device=x.device)
     _check("msa_pool_encode", lib.msa_pool_encode(
         _dtype(x), _ptr(x), _ptr(tok_off), _ptr(chunk_off), _ptr(chunk_doc), tok_off.numel() - 1, n_tok,
-        n_chunks, H, d, chunk, int(bool(l2_normalize)), _ptr(out), _stream(stream)))
+        n_chunks, H, d, chunk, int(bool(l2_normalize)), layout, _ptr(out), _stream(stream)))
     return out
 
 
@@ -135,15 +155,17 @@ def msa_route_score_workspace(dtype, B, T, H, d, n_docs, n_chunks):
     return lib.msa_route_score_workspace(dtype, B, T, H, d, n_docs, n_chunks)
 
 
-def msa_route_score(q_r, kr_hat, chunk_doc, n_docs, doc_score=None, ws=None, stream=None):
+def msa_route_score(q_r, kr_hat, chunk_doc, n_docs, doc_score=None, ws=None, layout=MSA_LAYOUT_ROWS, stream=None):
     B, T, H, d = q_r.shape
-    n_chunks = kr_hat.shape[0]
+    n_chunks = chunk_doc.numel()
+    if kr_hat.shape[0] < padded_chunks(n_chunks, layout):
+        raise ValueError("kr_hat holds fewer chunks than chunk_doc names")
     dt = _dtype(q_r)
     if doc_score is None:
         doc_score = torch.empty((B, n_docs), dtype=torch.float32, device=q_r.device)
     ws, wsb = _ws(msa_route_score_workspace(dt, B, T, H, d, n_docs, n_chunks), q_r.device, ws)
     _check("msa_route_score", lib.msa_route_score(
-        dt, _ptr(q_r), B, T, H, d, _ptr(kr_hat), _ptr(chunk_doc), n_docs, n_chunks, _ptr(doc_score),
+        dt, _ptr(q_r), B, T, H, d, _ptr(kr_hat), layout, _ptr(chunk_doc), n_docs, n_chunks, _ptr(doc_score),
         _ptr(ws), wsb, _stream(stream)))
     return doc_score
 

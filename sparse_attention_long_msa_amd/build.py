@@ -1,6 +1,6 @@
 """Build the HIP libraries for gfx950, in-tree.
 
-    python -m sparse_attention_long_msa_amd.build
+    python sparse_attention_long_msa_amd/build.py
 
 compiles ``csrc/*.hip`` into ``libmsa.so`` (the C-ABI library declared in
 ``include/msa.h``) and ``synth/synth_device.hip`` into ``synth/libmsa_synth.so``

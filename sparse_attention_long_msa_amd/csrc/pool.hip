@@ -8,17 +8,25 @@
 // (H*d elements each), so threads stream them with 16-byte loads; row
 // groups of the workgroup take interleaved tokens and are combined in a
 // fixed order, so the result is deterministic.
+#include <algorithm>
+
 #include "common.h"
 
 namespace msa {
 
 constexpr int kPoolThreads = 256;
 
+// Element offset of (chunk c, head h, element e) in MSA_LAYOUT_TILED.
+__device__ __forceinline__ int64_t tiled_offset(int64_t c, int h, int e, int H, int d) {
+  return (c / 16) * (16 * int64_t(H) * d) + int64_t(h) * (16 * d) + (e / 32) * 512 + ((e % 32) / 8) * 128 +
+         (c % 16) * 8 + (e % 8);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
     const typename Elem<DT>::T* __restrict__ x, const int64_t* __restrict__ tok_off,
     const int64_t* __restrict__ chunk_off, const int32_t* __restrict__ chunk_doc, int64_t n_chunks,
-    int H, int d, int chunk, int normalize, typename Elem<DT>::T* __restrict__ out) {
+    int H, int d, int chunk, int normalize, int tiled, typename Elem<DT>::T* __restrict__ out) {
   constexpr int VE = 16 / Elem<DT>::bytes;  // elements per 16-byte vector
   extern __shared__ float smem[];
   const int E = H * d;
@@ -83,20 +91,70 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
     __syncthreads();
     for (int e = tid; e < E; e += kPoolThreads) {
       const float r = normalize ? mean[e] / scale[e / d] : mean[e];
+      const int64_t o = tiled ? tiled_offset(c, e / d, e % d, H, d) : c * E + e;
       if constexpr (DT == MSA_BF16)
-        out[c * E + e] = f32_to_bf16(r);
+        out[o] = f32_to_bf16(r);
       else
-        out[c * E + e] = r;
+        out[o] = r;
     }
     __syncthreads();
   }
 }
 
+// MSA_LAYOUT_ROWS -> MSA_LAYOUT_TILED; one thread per 8 consecutive elements
+// of one (chunk, head); chunks past n_chunks in the last group are zeroed.
+template <typename T>
+__global__ void tile_kernel(const T* __restrict__ src, int64_t n_chunks, int H, int d, T* __restrict__ dst) {
+  const int vpr = d / 8;                                   // 8-element vectors per (chunk, head)
+  const int64_t n_pad = (n_chunks + 15) / 16 * 16;
+  const int64_t total = n_pad * H * vpr;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += int64_t(gridDim.x) * blockDim.x) {
+    const int v = int(i % vpr);
+    const int h = int((i / vpr) % H);
+    const int64_t c = i / (int64_t(vpr) * H);
+    T* o = dst + tiled_offset(c, h, 8 * v, H, d);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = c < n_chunks ? src[(c * H + h) * d + 8 * v + e] : T(0);
+  }
+}
+
+template <typename T>
+__global__ void zero_padding_kernel(int64_t n_chunks, int H, int d, T* __restrict__ dst) {
+  const int64_t n_pad = (n_chunks + 15) / 16 * 16;
+  const int64_t per = int64_t(H) * d;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < (n_pad - n_chunks) * per;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t c = n_chunks + i / per;
+    const int h = int((i % per) / d), e = int(i % d);
+    dst[tiled_offset(c, h, e, H, d)] = T(0);
+  }
+}
+
 }  // namespace msa
+
+extern "C" int msa_tile_routing_keys(int dtype, const void* src, int64_t n_chunks, int H, int d, void* dst,
+                                     void* stream) {
+  using namespace msa;
+  MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, "msa_tile_routing_keys: bad dtype");
+  MSA_REQUIRE(src && dst && src != dst, MSA_ERR_INVALID_ARG, "msa_tile_routing_keys: NULL or aliased pointers");
+  MSA_REQUIRE(n_chunks >= 1 && H >= 1 && d >= 32 && d % 32 == 0, MSA_ERR_INVALID_ARG,
+              "msa_tile_routing_keys: sizes (d must be a multiple of 32)");
+  const int64_t total = (n_chunks + 15) / 16 * 16 * H * (d / 8);
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
+  if (dtype == MSA_BF16)
+    hipLaunchKernelGGL(tile_kernel<uint16_t>, dim3(unsigned(blocks)), dim3(256), 0, as_stream(stream),
+                       static_cast<const uint16_t*>(src), n_chunks, H, d, static_cast<uint16_t*>(dst));
+  else
+    hipLaunchKernelGGL(tile_kernel<float>, dim3(unsigned(blocks)), dim3(256), 0, as_stream(stream),
+                       static_cast<const float*>(src), n_chunks, H, d, static_cast<float*>(dst));
+  MSA_LAUNCH_CHECK();
+  return MSA_OK;
+}
 
 extern "C" int msa_pool_encode(int dtype, const void* x, const int64_t* tok_off, const int64_t* chunk_off,
                                const int32_t* chunk_doc, int64_t n_docs, int64_t n_tok, int64_t n_chunks,
-                               int H, int d, int chunk, int l2_normalize, void* out, void* stream) {
+                               int H, int d, int chunk, int l2_normalize, int out_layout, void* out,
+                               void* stream) {
   using namespace msa;
   MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, "msa_pool_encode: bad dtype");
   MSA_REQUIRE(x && tok_off && chunk_off && chunk_doc && out, MSA_ERR_INVALID_ARG,
@@ -104,6 +162,8 @@ extern "C" int msa_pool_encode(int dtype, const void* x, const int64_t* tok_off,
   MSA_REQUIRE(n_docs >= 1 && n_tok >= 1 && n_chunks >= 1 && H >= 1 && d >= 2 && chunk >= 1,
               MSA_ERR_INVALID_ARG, "msa_pool_encode: non-positive size");
   MSA_REQUIRE(d % 2 == 0, MSA_ERR_INVALID_ARG, "msa_pool_encode: d must be even");
+  MSA_REQUIRE(out_layout == MSA_LAYOUT_ROWS || (out_layout == MSA_LAYOUT_TILED && d % 32 == 0), MSA_ERR_INVALID_ARG,
+              "msa_pool_encode: bad out_layout (tiled needs d % 32 == 0)");
   const int E = H * d;
   const int VE = 16 / dtype_bytes(dtype);
   MSA_REQUIRE(E <= 4096 && E % 8 == 0, MSA_ERR_UNSUPPORTED, "msa_pool_encode: H*d must be <= 4096 and a multiple of 8");
@@ -118,11 +178,20 @@ extern "C" int msa_pool_encode(int dtype, const void* x, const int64_t* tok_off,
   if (dtype == MSA_BF16)
     hipLaunchKernelGGL(pool_kernel<MSA_BF16>, dim3(unsigned(grid)), dim3(kPoolThreads), smem, as_stream(stream),
                        static_cast<const uint16_t*>(x), tok_off, chunk_off, chunk_doc, n_chunks, H, d, chunk,
-                       l2_normalize, static_cast<uint16_t*>(out));
+                       l2_normalize, out_layout, static_cast<uint16_t*>(out));
   else
     hipLaunchKernelGGL(pool_kernel<MSA_F32>, dim3(unsigned(grid)), dim3(kPoolThreads), smem, as_stream(stream),
                        static_cast<const float*>(x), tok_off, chunk_off, chunk_doc, n_chunks, H, d, chunk,
-                       l2_normalize, static_cast<float*>(out));
+                       l2_normalize, out_layout, static_cast<float*>(out));
   MSA_LAUNCH_CHECK();
+  if (out_layout == MSA_LAYOUT_TILED && n_chunks % 16 != 0) {
+    if (dtype == MSA_BF16)
+      hipLaunchKernelGGL(zero_padding_kernel<uint16_t>, dim3(64), dim3(256), 0, as_stream(stream), n_chunks, H, d,
+                         static_cast<uint16_t*>(out));
+    else
+      hipLaunchKernelGGL(zero_padding_kernel<float>, dim3(64), dim3(256), 0, as_stream(stream), n_chunks, H, d,
+                         static_cast<float*>(out));
+    MSA_LAUNCH_CHECK();
+  }
   return MSA_OK;
 }

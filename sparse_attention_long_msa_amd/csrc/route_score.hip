@@ -66,7 +66,7 @@ __device__ __forceinline__ void seg_max_emit(float v, int doc, int lane, float* 
 // NT: 16-column tiles per column group (<= 4); UNIFORM_B: every 16-column
 // tile belongs to one query (T % 16 == 0), so the token max is taken in
 // registers before the document max.
-template <int NT, bool UNIFORM_B>
+template <int NT, bool UNIFORM_B, bool TILED>
 __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     const uint16_t* __restrict__ q_r, int T, int J, const uint16_t* __restrict__ kr,
     const int32_t* __restrict__ chunk_doc, int64_t n_docs, int64_t n_chunks, float* __restrict__ doc_score,
@@ -146,14 +146,24 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
 
   // A operand of head h for the tile: lane (lc, g4) reads chunk row lc, elements
   // 32*kk + 8*g4 .. +8 of the head (four lanes cover 64 contiguous bytes)
+  const int64_t n_cgroups = (n_chunks + 15) / 16;   // 16-chunk groups of the tiled layout
   auto load_head = [&](int64_t tl, int h, uint4 (&dst)[RS_MT][RS_KK]) {
 #pragma unroll
     for (int m = 0; m < RS_MT; ++m) {
-      int64_t c = tl * RS_TILE + 16 * m + lc;
-      if (c >= n_chunks) c = n_chunks - 1;
-      const uint4* p = reinterpret_cast<const uint4*>(kr + c * rowE + int64_t(h) * RS_D + 8 * g4);
+      if constexpr (TILED) {
+        // 16-chunk group: one wave instruction reads 1 KB contiguous (lane-ordered)
+        int64_t grp = tl * RS_MT + m;
+        if (grp >= n_cgroups) grp = n_cgroups - 1;
+        const uint16_t* p = kr + grp * (16 * rowE) + int64_t(h) * (16 * RS_D) + 8 * lane;
 #pragma unroll
-      for (int kk = 0; kk < RS_KK; ++kk) dst[m][kk] = p[kk * 4];
+        for (int kk = 0; kk < RS_KK; ++kk) dst[m][kk] = load_stream(p + kk * 512);   // read once
+      } else {
+        int64_t c = tl * RS_TILE + 16 * m + lc;
+        if (c >= n_chunks) c = n_chunks - 1;
+        const uint4* p = reinterpret_cast<const uint4*>(kr + c * rowE + int64_t(h) * RS_D + 8 * g4);
+#pragma unroll
+        for (int kk = 0; kk < RS_KK; ++kk) dst[m][kk] = p[kk * 4];
+      }
     }
   };
 
@@ -323,8 +333,8 @@ extern "C" size_t msa_route_score_workspace(int dtype, int B, int T, int H, int 
 }
 
 extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
-                               const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks, float* doc_score,
-                               void* ws, size_t ws_bytes, void* stream) {
+                               int kr_layout, const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks,
+                               float* doc_score, void* ws, size_t ws_bytes, void* stream) {
   using namespace msa;
   MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, "msa_route_score: bad dtype");
   MSA_REQUIRE(q_r && kr_hat && chunk_doc && doc_score, MSA_ERR_INVALID_ARG, "msa_route_score: NULL pointer");
@@ -332,6 +342,10 @@ extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, 
               "msa_route_score: non-positive size");
   MSA_REQUIRE(int64_t(B) * T < (int64_t(1) << 24), MSA_ERR_UNSUPPORTED, "msa_route_score: B*T too large");
   MSA_REQUIRE(d <= 256 && d % 8 == 0, MSA_ERR_UNSUPPORTED, "msa_route_score: d must be a multiple of 8, <= 256");
+  MSA_REQUIRE(kr_layout == MSA_LAYOUT_ROWS || kr_layout == MSA_LAYOUT_TILED, MSA_ERR_INVALID_ARG,
+              "msa_route_score: bad kr_layout");
+  MSA_REQUIRE(kr_layout == MSA_LAYOUT_ROWS || use_mfma(dtype, H, d), MSA_ERR_UNSUPPORTED,
+              "msa_route_score: the tiled layout needs the MFMA path (bf16, H = 8, d = 128)");
   const size_t need = msa_route_score_workspace(dtype, B, T, H, d, n_docs, n_chunks);
   MSA_REQUIRE(ws_bytes >= need, MSA_ERR_WORKSPACE, "msa_route_score: workspace too small");
   MSA_REQUIRE(need == 0 || ws, MSA_ERR_INVALID_ARG, "msa_route_score: NULL workspace");
@@ -359,12 +373,19 @@ extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, 
     const int64_t tiles_per_range = (tiles_total + n_ranges - 1) / n_ranges;
     const size_t smem = size_t(NT) * RS_H * RS_KK * 1024 + size_t(RS_WAVES) * RS_SCRATCH + size_t(RS_H) * NT * 16 * 4;
     const dim3 grid(unsigned(n_ranges * n_groups)), block(RS_THREADS);
-#define RS_LAUNCH(NTV, UNI)                                                                              \
-  MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&route_score_mfma_kernel<NTV, UNI>),   \
+#define RS_LAUNCH2(NTV, UNI, TIL)                                                                        \
+  MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&route_score_mfma_kernel<NTV, UNI, TIL>), \
                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)));           \
-  hipLaunchKernelGGL((route_score_mfma_kernel<NTV, UNI>), grid, block, smem, s,                        \
+  hipLaunchKernelGGL((route_score_mfma_kernel<NTV, UNI, TIL>), grid, block, smem, s,                   \
                      static_cast<const uint16_t*>(q_r), T, J, static_cast<const uint16_t*>(kr_hat),     \
                      chunk_doc, n_docs, n_chunks, doc_score, n_groups, int(n_ranges), tiles_per_range)
+#define RS_LAUNCH(NTV, UNI)           \
+  if (tiled) {                        \
+    RS_LAUNCH2(NTV, UNI, true);       \
+  } else {                            \
+    RS_LAUNCH2(NTV, UNI, false);      \
+  }
+    const bool tiled = kr_layout == MSA_LAYOUT_TILED;
     switch (NT * 2 + (uniform ? 1 : 0)) {
       case 2: RS_LAUNCH(1, false); break;
       case 3: RS_LAUNCH(1, true); break;
@@ -376,6 +397,7 @@ extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, 
       default: RS_LAUNCH(4, true); break;
     }
 #undef RS_LAUNCH
+#undef RS_LAUNCH2
     MSA_LAUNCH_CHECK();
     return MSA_OK;
   }

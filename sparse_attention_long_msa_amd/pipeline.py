@@ -18,7 +18,7 @@ from . import _binding as B
 class LayerRunner:
     def __init__(self, *, batch, tokens, q_heads, kv_heads, head_dim, n_docs, n_chunks, k, max_doc_chunks,
                  local_len, dtype, device, q_pos_offset=None, rope_base=1e6, sm_scale=None,
-                 src_mode=B.MSA_SRC_DEVICE, chunk_off_h=None):
+                 src_mode=B.MSA_SRC_DEVICE, chunk_off_h=None, kr_layout=B.MSA_LAYOUT_ROWS):
         self.B, self.T, self.Hq, self.Hkv, self.d = batch, tokens, q_heads, kv_heads, head_dim
         self.n_docs, self.n_chunks, self.k = n_docs, n_chunks, k
         self.max_doc_chunks = max_doc_chunks
@@ -28,6 +28,7 @@ class LayerRunner:
         self.rope_base = rope_base
         self.sm_scale = 1.0 / math.sqrt(head_dim) if sm_scale is None else sm_scale
         self.src_mode = src_mode
+        self.kr_layout = kr_layout
         self.chunk_off_h = chunk_off_h
         self.dtype = dtype
         dt = B.MSA_BF16 if dtype == torch.bfloat16 else B.MSA_F32
@@ -57,7 +58,7 @@ class LayerRunner:
 
     def route(self, q_r, kr_hat, chunk_doc, stream=None):
         B.msa_route_score(q_r, kr_hat, chunk_doc, self.n_docs, doc_score=self.doc_score, ws=self.rs_ws,
-                          stream=stream)
+                          layout=self.kr_layout, stream=stream)
         return self.doc_score
 
     def select(self, stream=None):

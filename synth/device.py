@@ -16,7 +16,7 @@ def _lib():
     global _h
     if _h is None:
         if not os.path.exists(_LIB):
-            raise ImportError(f"{_LIB} is not built: run `python -m sparse_attention_long_msa_amd.build`")
+            raise ImportError(f"{_LIB} is not built: run `python sparse_attention_long_msa_amd/build.py`")
         _h = ctypes.CDLL(_LIB)
         _h.msa_synth_fill.restype = ctypes.c_int
         _h.msa_synth_fill.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,

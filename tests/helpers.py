@@ -29,6 +29,23 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy() if t.is_floating_point() else t.cpu().numpy()
 
 
+def tile_np(x: np.ndarray) -> np.ndarray:
+    """Row-major [N, H, d] -> the MSA_LAYOUT_TILED element order, padded with
+    zero chunks to a multiple of 16; returned as [N_pad, H, d]-shaped storage."""
+    N, H, d = x.shape
+    n_pad = (N + 15) // 16 * 16
+    xp = np.zeros((n_pad, H, d), dtype=x.dtype)
+    xp[:N] = x
+    t = xp.reshape(n_pad // 16, 16, H, d // 32, 4, 8).transpose(0, 2, 3, 4, 1, 5)
+    return np.ascontiguousarray(t).reshape(n_pad, H, d)
+
+
+def untile_np(t: np.ndarray, N: int) -> np.ndarray:
+    n_pad, H, d = t.shape
+    x = t.reshape(n_pad // 16, H, d // 32, 4, 16, 8).transpose(0, 4, 1, 2, 3, 5)
+    return np.ascontiguousarray(x).reshape(n_pad, H, d)[:N]
+
+
 def ragged_lengths(seed: int, n_docs: int, lo: int, hi: int, n_empty: int = 0) -> np.ndarray:
     r = np.random.default_rng(seed)
     lens = r.integers(lo, hi + 1, size=n_docs).astype(np.int64)

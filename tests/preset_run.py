@@ -107,7 +107,9 @@ class GpuLayer:
                     lo, hi = int(row_off[nd]), int(row_off[nd + 1])
                     rows = synth.needle_rows(host.qr[b], p.seed, l, hi - lo, bf16=p.bf16, start=lo)
                     raw[lo:hi] = torch.from_numpy(rows).to(d0, bf)
-            self.store[tid] = M.msa_pool_encode(raw, to_d, self.co_d, self.cd, chunk, tid == synth.T_KR)
+            lay = M.MSA_LAYOUT_TILED if (tid == synth.T_KR and p.bf16) else M.MSA_LAYOUT_ROWS
+            self.store[tid] = M.msa_pool_encode(raw, to_d, self.co_d, self.cd, chunk, tid == synth.T_KR,
+                                                layout=lay)
         del raw
         self.qr = torch.from_numpy(host.qr).to(d0, bf)
         self.q = torch.from_numpy(host.q).to(d0, bf)
@@ -120,7 +122,8 @@ class GpuLayer:
         self.runner = M.LayerRunner(batch=p.B, tokens=p.T, q_heads=p.Hq, kv_heads=H, head_dim=d, n_docs=p.n_docs,
                                     n_chunks=p.n_chunks, k=p.k, max_doc_chunks=p.max_doc_chunks,
                                     local_len=p.L_loc, dtype=bf, device=d0, q_pos_offset=p.qpo,
-                                    rope_base=p.rope_base, src_mode=src_mode, chunk_off_h=co)
+                                    rope_base=p.rope_base, src_mode=src_mode, chunk_off_h=co,
+                                    kr_layout=M.MSA_LAYOUT_TILED if p.bf16 else M.MSA_LAYOUT_ROWS)
 
     def run(self):
         r = self.runner

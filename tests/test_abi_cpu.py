@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.msa_abi_version() == 1
+    assert M.msa_abi_version() == 2
     assert M.lib.msa_status_string(0).decode() == "ok"
     assert "workspace" in M.lib.msa_status_string(3).decode()
 
@@ -56,14 +56,16 @@ P = ctypes.c_void_p(16)   # a non-null dummy; validation fails before any derefe
 
 def test_route_score_validation():
     L = M.lib
-    assert L.msa_route_score(1, None, 1, 1, 8, 128, P, P, 4, 4, P, None, 0, None) == 1
-    assert L.msa_route_score(1, P, 0, 1, 8, 128, P, P, 4, 4, P, None, 0, None) == 1
-    assert L.msa_route_score(7, P, 1, 1, 8, 128, P, P, 4, 4, P, None, 0, None) == 1
-    assert L.msa_route_score(1, P, 1, 1, 8, 260, P, P, 4, 4, P, None, 0, None) == 2
+    assert L.msa_route_score(1, None, 1, 1, 8, 128, P, 0, P, 4, 4, P, None, 0, None) == 1
+    assert L.msa_route_score(1, P, 0, 1, 8, 128, P, 0, P, 4, 4, P, None, 0, None) == 1
+    assert L.msa_route_score(7, P, 1, 1, 8, 128, P, 0, P, 4, 4, P, None, 0, None) == 1
+    assert L.msa_route_score(1, P, 1, 1, 8, 260, P, 0, P, 4, 4, P, None, 0, None) == 2
+    assert L.msa_route_score(1, P, 1, 1, 8, 128, P, 5, P, 4, 4, P, None, 0, None) == 1     # bad layout
+    assert L.msa_route_score(1, P, 1, 1, 4, 128, P, 1, P, 4, 4, P, P, 1 << 20, None) == 2  # tiled off the MFMA path
     # float32 needs a workspace for the column norms
     need = L.msa_route_score_workspace(0, 1, 16, 8, 128, 4, 4)
     assert need >= 16 * 8 * 4
-    assert L.msa_route_score(0, P, 1, 16, 8, 128, P, P, 4, 4, P, P, need - 1, None) == 3
+    assert L.msa_route_score(0, P, 1, 16, 8, 128, P, 0, P, 4, 4, P, P, need - 1, None) == 3
 
 
 def test_topk_validation():
@@ -109,9 +111,12 @@ def test_sparse_attn_validation():
 
 def test_pool_and_docmap_validation():
     L = M.lib
-    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 128, 0, 1, P, None) == 1     # chunk 0
-    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 127, 64, 1, P, None) == 1    # odd d
-    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 64, 128, 64, 1, P, None) == 2   # H*d > 4096
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 128, 0, 1, 0, P, None) == 1     # chunk 0
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 127, 64, 1, 0, P, None) == 1    # odd d
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 64, 128, 64, 1, 0, P, None) == 2   # H*d > 4096
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 48, 64, 1, 1, P, None) == 1     # tiled needs d % 32
+    assert L.msa_tile_routing_keys(1, P, 10, 8, 48, ctypes.c_void_p(32), None) == 1
+    assert L.msa_tile_routing_keys(1, P, 10, 8, 128, P, None) == 1                     # aliased
     assert L.msa_chunk_doc_map(None, 4, 8, P, None) == 1
     assert L.msa_chunk_doc_map(P, 0, 8, P, None) == 1
     assert M.lib.msa_last_error().decode() != ""

@@ -10,7 +10,7 @@ import torch
 import oracle as O
 import synth
 from tests.helpers import (ATOL_ATTN, RTOL_SCORE, check_ids, check_scores, dev, gen, host, ragged_lengths,
-                           to_dev, to_dev_i64)
+                           tile_np, to_dev, to_dev_i64, untile_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,18 +43,31 @@ def test_chunk_doc_map():
     np.testing.assert_array_equal(cd.cpu().numpy(), want)
 
 
+def test_tile_routing_keys_is_the_documented_permutation():
+    for N, H, d in ((37, 8, 128), (64, 2, 32), (1, 8, 128)):
+        x = gen(5, 0, synth.T_KR, (N, H, d), True)
+        t = M.msa_tile_routing_keys(to_dev(x, True))
+        np.testing.assert_array_equal(host(t), tile_np(x))
+        np.testing.assert_array_equal(untile_np(host(t), N), x)
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("normalize", [False, True])
 @pytest.mark.parametrize("chunk", [64, 1, 5])
-def test_pool_encode(bf16, normalize, chunk):
+@pytest.mark.parametrize("layout", [0, 1])
+def test_pool_encode(bf16, normalize, chunk, layout):
     H, d = 8, 128
     lens = ragged_lengths(2, 37, 0, 400, n_empty=3)
     lens[0] = 130                                    # two full chunks and a partial one
     tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, chunk)
     x = gen(11, 0, synth.T_KR, (int(lens.sum()), H, d), bf16)
-    out = M.msa_pool_encode(to_dev(x, bf16), to_dev_i64(tok_off), co_d, cd, chunk, normalize)
+    out = M.msa_pool_encode(to_dev(x, bf16), to_dev_i64(tok_off), co_d, cd, chunk, normalize, layout=layout)
     ref = O.pool_encode(x, tok_off, chunk, normalize, "bf16" if bf16 else "f32")
     got = host(out)
+    if layout == 1:
+        assert got.shape[0] == (n_chunks + 15) // 16 * 16
+        assert np.all(untile_np(got, got.shape[0])[n_chunks:] == 0)      # zero padding chunks
+        got = untile_np(got, n_chunks)
     if bf16:
         # float32 accumulation may move the once-rounded result by one bf16 ulp
         ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
@@ -64,9 +77,9 @@ def test_pool_encode(bf16, normalize, chunk):
         np.testing.assert_allclose(got, ref, rtol=2e-6, atol=1e-7)
 
 
-@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("bf16,layout", [(True, 1), (True, 0), (False, 0)])
 @pytest.mark.parametrize("B,T", [(1, 64), (1, 16), (1, 1), (2, 32), (32, 1), (1, 128), (3, 7), (1, 80)])
-def test_route_score(bf16, B, T):
+def test_route_score(bf16, layout, B, T):
     H, d = 8, 128
     lens = ragged_lengths(3 + T, 180, 1, 1500, n_empty=5)
     while ((lens + 63) // 64).sum() % 32 == 0:
@@ -80,11 +93,12 @@ def test_route_score(bf16, B, T):
     # plant a needle: one chunk of document 17 is the first query token itself
     nd = 17
     store[chunk_off[nd]] = O.round_to_store(O.l2_normalize(q[0, 0].astype(np.float64)), dt)
-    ds = M.msa_route_score(to_dev(q, bf16), to_dev(store, bf16), cd, len(lens))
+    st = tile_np(store) if layout == 1 else store
+    ds = M.msa_route_score(to_dev(q, bf16), to_dev(st, bf16), cd, len(lens), layout=layout)
     ref = O.route_scores(q, store, chunk_off)
     got = host(ds)
     err = check_scores(got, ref, RTOL_SCORE[dt], k=16)
-    print(f"route_score {dt} B={B} T={T}: normwise err {err:.3g}")
+    print(f"route_score {dt} layout={layout} B={B} T={T}: normwise err {err:.3g}")
     assert np.argmax(got[0]) == nd
 
 
@@ -95,8 +109,9 @@ def test_route_score_rescale_invariance():
     tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
     store = O.round_to_store(O.l2_normalize(gen(31, 0, synth.T_KR, (n_chunks, H, d), True)), "bf16")
     q = gen(32, 0, synth.T_QR, (1, 64, H, d), True)
-    a = host(M.msa_route_score(to_dev(q, True), to_dev(store, True), cd, len(lens)))
-    b = host(M.msa_route_score(to_dev(q * 4.0, True), to_dev(store, True), cd, len(lens)))
+    st = to_dev(tile_np(store), True)
+    a = host(M.msa_route_score(to_dev(q, True), st, cd, len(lens), layout=1))
+    b = host(M.msa_route_score(to_dev(q * 4.0, True), st, cd, len(lens), layout=1))
     np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-7)
 
 
