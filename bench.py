@@ -251,13 +251,38 @@ def main():
         "needle_recall_layer0": recall,
         "roofline": {"kernel": "msa_route_score (route_score_mfma_kernel + score fill)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-                     "frac": round(achieved / 8000.0, 4), "traffic": None,
+                     "frac": round(achieved / 8000.0, 4), "traffic": counted_traffic(p.name),
                      "avg_launch_ms": round(route_avg_ms, 4), "alg_bytes_per_launch": int(alg_bytes)},
     }
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_sample_chunks)
     print(json.dumps(res), flush=True)
+
+
+def counted_traffic(preset_name):
+    """HBM bytes per routing-score launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE scaled by a plain copy), or None when the
+    kernel sources changed since the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "route_score_100M.txt")
+    if preset_name != "cfg4" or not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("route_score.hip", "common.h"):
+        h.update(open(os.path.join(here, "sparse_attention_long_msa_amd", "csrc", f), "rb").read())
+    if fields.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def copy_calibration(torch):
