@@ -229,6 +229,9 @@ int msa_gather_kv(int dtype, const int32_t* ids, int B, int k, const int64_t* ch
  *   query position: q_pos_offset + L_loc - T + t ("offset by k": pass k).
  *   RoPE: rotate-half, the pair (m, m + d/2) turns by pos * rope_base^(-2m/d)
  *         (angles reduced in float64), applied to q and every key on the fly.
+ *         The (cos, sin) rows come from rope_table (msa_rope_table with the same
+ *         rope_base and d, at least msa_rope_table_rows() rows) or, when
+ *         rope_table is NULL, are computed into the workspace on every call.
  *   out[b,t,hq,:] = softmax_j(sm_scale * <R q, R k_j>) . v_j   (float32)
  *   q     [B, T, Hq, d] dtype; k_ctx/v_ctx/ctx_pos/ctx_len from msa_gather_kv
  *   k_loc/v_loc [B, L_loc, Hkv, d] dtype, un-rotated
@@ -243,7 +246,22 @@ size_t msa_sparse_attn_workspace(int dtype, int B, int T, int Hq, int Hkv, int d
 int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d, const void* k_ctx,
                     const void* v_ctx, const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx,
                     const void* k_loc, const void* v_loc, int L_loc, int q_pos_offset, float rope_base,
-                    float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+                    const float* rope_table, int rope_table_rows, float sm_scale, float* out, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
+ * msa_rope_table - the (cos, sin) rows msa_sparse_attn rotates with, built
+ * once and reused by every layer and call with the same base and d.  Row p,
+ * pair m holds (cos, sin)(p * rope_base^(-2m/d)) with the angle formed and
+ * reduced in float64 and rounded to float32 (document-wise RoPE: positions
+ * are document-local chunk indices and the query's offset positions).
+ *   table [rows, d/2, 2] float32 device output
+ * msa_rope_table_rows gives the rows msa_sparse_attn needs:
+ * max(q_pos_offset + L_loc, max_ctx, 32).
+ * Errors: INVALID_ARG (NULL, rows < 1, d odd, rope_base <= 1).
+ */
+int msa_rope_table_rows(int max_ctx, int L_loc, int q_pos_offset);
+int msa_rope_table(int rows, int d, float rope_base, float* table, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,8 @@ from ._binding import (  # noqa: F401
     msa_gather_kv,
     msa_pool_encode,
     msa_route_score,
+    msa_rope_table,
+    msa_rope_table_rows,
     msa_route_score_workspace,
     msa_sparse_attn,
     msa_sparse_attn_workspace,

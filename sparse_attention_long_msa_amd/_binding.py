@@ -40,7 +40,9 @@ _SIGS = {
                            _P, _P, _P, _P, _P, _P, _P]),
     "msa_sparse_attn_workspace": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "msa_sparse_attn": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _I, _I,
-                             _F, _F, _P, _P, _S, _P]),
+                             _F, _P, _I, _F, _P, _P, _S, _P]),
+    "msa_rope_table_rows": (_I, [_I, _I, _I]),
+    "msa_rope_table": (_I, [_I, _I, _F, _P, _P]),
 }
 
 
@@ -214,8 +216,19 @@ def msa_sparse_attn_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_off
     return lib.msa_sparse_attn_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset)
 
 
+def msa_rope_table_rows(max_ctx, L_loc, q_pos_offset):
+    return lib.msa_rope_table_rows(max_ctx, L_loc, q_pos_offset)
+
+
+def msa_rope_table(rows, d, rope_base=1e6, table=None, device=None, stream=None):
+    if table is None:
+        table = torch.empty((rows, d // 2, 2), dtype=torch.float32, device=device)
+    _check("msa_rope_table", lib.msa_rope_table(rows, d, float(rope_base), _ptr(table), _stream(stream)))
+    return table
+
+
 def msa_sparse_attn(q, k_ctx, v_ctx, ctx_pos, ctx_len, k_loc, v_loc, q_pos_offset, rope_base=1e6,
-                    sm_scale=None, out=None, ws=None, stream=None):
+                    sm_scale=None, out=None, ws=None, rope_table=None, stream=None):
     B, T, Hq, d = q.shape
     max_ctx, Hkv = k_ctx.shape[1], k_ctx.shape[2]
     L_loc = k_loc.shape[1]
@@ -227,6 +240,7 @@ def msa_sparse_attn(q, k_ctx, v_ctx, ctx_pos, ctx_len, k_loc, v_loc, q_pos_offse
     ws, wsb = _ws(msa_sparse_attn_workspace(dt, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset), q.device, ws)
     _check("msa_sparse_attn", lib.msa_sparse_attn(
         dt, _ptr(q), B, T, Hq, Hkv, d, _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_pos), _ptr(ctx_len), max_ctx,
-        _ptr(k_loc), _ptr(v_loc), L_loc, q_pos_offset, float(rope_base), float(sm_scale), _ptr(out),
-        _ptr(ws), wsb, _stream(stream)))
+        _ptr(k_loc), _ptr(v_loc), L_loc, q_pos_offset, float(rope_base), _ptr(rope_table),
+        0 if rope_table is None else rope_table.shape[0], float(sm_scale), _ptr(out), _ptr(ws), wsb,
+        _stream(stream)))
     return out

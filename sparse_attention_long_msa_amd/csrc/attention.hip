@@ -165,7 +165,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
     const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
     const float2* __restrict__ tab, int P, float scale_log2, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
-    int n_splits, int keys_per_split, int n_hg) {
+    int n_splits, int n_hg) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int nw = blockDim.x / 64;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -205,8 +205,10 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
 
   const int ctxl = ctx_len[b];
   const int n_keys = ctxl + L_loc;
-  const int j_begin = split * keys_per_split;
-  const int j_end = min(n_keys, j_begin + keys_per_split);
+  // this query's keys split evenly over the n_splits workgroups (32-key steps)
+  const int kps = ((n_keys + n_splits - 1) / n_splits + 31) / 32 * 32;
+  const int j_begin = split * kps;
+  const int j_end = min(n_keys, j_begin + kps);
   const int nthr = nw * 64;
   // a step whose 32 keys are all local tokens addresses them affinely
   auto all_local = [&](int j0) { return j0 >= ctxl && j0 + 32 <= n_keys; };
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
     const float2* __restrict__ tab, int P, float scale_log2, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
-    int n_splits, int keys_per_split, int n_rt, int n_rg) {
+    int n_splits, int n_rt, int n_rg) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int lc = lane % 16, g4 = lane / 16;
@@ -464,8 +466,10 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
 
   const int ctxl = ctx_len[b];
   const int n_keys = ctxl + L_loc;
-  const int j_begin = split * keys_per_split;
-  const int j_end = min(n_keys, j_begin + keys_per_split);
+  // this query's keys split evenly over the n_splits workgroups (32-key steps)
+  const int kps = ((n_keys + n_splits - 1) / n_splits + 31) / 32 * 32;
+  const int j_begin = split * kps;
+  const int j_end = min(n_keys, j_begin + kps);
 
   // cooperative mapping of one 32-key step
   const int lk = tid / 16, lx = tid % 16;     // K: key, 4-dim block; V: key, 8-dim block
@@ -756,16 +760,16 @@ struct AttnPlan {
   int P;            // rows of the RoPE table
   int n_rt;         // 16-row tiles per (b, g)
   int n_splits;
-  int keys_per_split;
   size_t tab_bytes, o_bytes, ml_bytes;
 };
+
+static int rope_rows(int max_ctx, int L_loc, int qpo) { return std::max(std::max(qpo + L_loc, max_ctx), 32); }
 
 static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc, int qpo) {
   AttnPlan p{};
   const int G = Hkv > 0 ? Hq / Hkv : 0;
   p.mfma = dtype == MSA_BF16 && d == AT_D && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
-  p.P = std::max(qpo + L_loc, max_ctx);
-  p.P = std::max(p.P, 32);
+  p.P = rope_rows(max_ctx, L_loc, qpo);
   p.tab_bytes = align_up(size_t(p.P) * (d / 2) * sizeof(float2), 256);
   if (!p.mfma) return p;
   p.n_rt = (T * G + 15) / 16;
@@ -780,14 +784,12 @@ static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int m
   } else {
     p.n_hg = (Hkv + 7) / 8;
     units = int64_t(B) * p.n_hg;            // workgroups per split
-    target = 1024;
+    target = 512;                            // two rounds of one 8-wave workgroup per CU
   }
+  // the kernels split each query's actual keys evenly over n_splits
   int64_t s = (target + units - 1) / units;
   s = std::max<int64_t>(1, std::min<int64_t>(s, (n_keys_max + 63) / 64));
-  int64_t kps = (n_keys_max + s - 1) / s;
-  kps = (kps + 31) / 32 * 32;
-  p.keys_per_split = int(kps);
-  p.n_splits = int((n_keys_max + kps - 1) / kps);
+  p.n_splits = int(s);
   const int64_t rows = int64_t(B) * T * Hq;
   p.o_bytes = align_up(size_t(p.n_splits) * rows * d * sizeof(float), 256);
   p.ml_bytes = align_up(size_t(p.n_splits) * rows * sizeof(float2), 256);
@@ -795,6 +797,23 @@ static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int m
 }
 
 }  // namespace msa
+
+extern "C" int msa_rope_table_rows(int max_ctx, int L_loc, int q_pos_offset) {
+  if (max_ctx < 0 || L_loc < 1 || q_pos_offset < 0) return 0;
+  return msa::rope_rows(max_ctx, L_loc, q_pos_offset);
+}
+
+extern "C" int msa_rope_table(int rows, int d, float rope_base, float* table, void* stream) {
+  using namespace msa;
+  MSA_REQUIRE(table, MSA_ERR_INVALID_ARG, "msa_rope_table: NULL table");
+  MSA_REQUIRE(rows >= 1 && d >= 2 && d % 2 == 0, MSA_ERR_INVALID_ARG, "msa_rope_table: bad rows or d");
+  MSA_REQUIRE(rope_base > 1.f, MSA_ERR_INVALID_ARG, "msa_rope_table: rope_base must exceed 1");
+  const int64_t n = int64_t(rows) * (d / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, as_stream(stream),
+                     reinterpret_cast<float2*>(table), rows, d / 2, double(rope_base), d);
+  MSA_LAUNCH_CHECK();
+  return MSA_OK;
+}
 
 extern "C" size_t msa_sparse_attn_workspace(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc,
                                             int q_pos_offset) {
@@ -806,7 +825,8 @@ extern "C" size_t msa_sparse_attn_workspace(int dtype, int B, int T, int Hq, int
 extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d, const void* k_ctx,
                                const void* v_ctx, const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx,
                                const void* k_loc, const void* v_loc, int L_loc, int q_pos_offset, float rope_base,
-                               float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+                               const float* rope_table, int rope_table_rows, float sm_scale, float* out, void* ws,
+                               size_t ws_bytes, void* stream) {
   using namespace msa;
   MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, "msa_sparse_attn: bad dtype");
   MSA_REQUIRE(q && k_ctx && v_ctx && ctx_pos && ctx_len && k_loc && v_loc && out && ws, MSA_ERR_INVALID_ARG,
@@ -825,13 +845,17 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
   if (!p.mfma)
     MSA_REQUIRE(int64_t(max_ctx) + L_loc <= AT_VEC_MAX_KEYS, MSA_ERR_UNSUPPORTED,
                 "msa_sparse_attn: more than 32768 keys on the vector path");
+  MSA_REQUIRE(!rope_table || rope_table_rows >= p.P, MSA_ERR_INVALID_ARG,
+              "msa_sparse_attn: rope_table has fewer rows than msa_rope_table_rows()");
   hipStream_t s = as_stream(stream);
-  float2* tab = static_cast<float2*>(ws);
-  {
+  const float2* tab = reinterpret_cast<const float2*>(rope_table);
+  if (!tab) {
+    float2* wtab = static_cast<float2*>(ws);
     const int64_t n = int64_t(p.P) * (d / 2);
-    hipLaunchKernelGGL(rope_table_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, tab, p.P, d / 2,
+    hipLaunchKernelGGL(rope_table_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, wtab, p.P, d / 2,
                        double(rope_base), d);
     MSA_LAUNCH_CHECK();
+    tab = wtab;
   }
   if (p.mfma) {
     MSA_REQUIRE(uintptr_t(q) % 16 == 0 && uintptr_t(k_ctx) % 16 == 0 && uintptr_t(v_ctx) % 16 == 0 &&
@@ -848,7 +872,7 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
   hipLaunchKernelGGL((attn_prefill_kernel<GV, RV>), pgrid, pblock, psmem, s, static_cast<const uint16_t*>(q), B, T,  \
                      Hq, Hkv, static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos,     \
                      ctx_len, max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc),     \
-                     L_loc, q_pos_offset, tab, p.P, scale_log2_pf, ws_o, ws_ml, p.n_splits, p.keys_per_split, p.n_rt, \
+                     L_loc, q_pos_offset, tab, p.P, scale_log2_pf, ws_o, ws_ml, p.n_splits, p.n_rt,                  \
                      p.n_rg)
       const int key = G * 4 + p.rtw;
       switch (key) {
@@ -881,7 +905,7 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
   hipLaunchKernelGGL((attn_decode_kernel<GV>), grid, block, smem, s, static_cast<const uint16_t*>(q), B, T, Hq, Hkv, \
                      static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos, ctx_len,     \
                      max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc), L_loc,       \
-                     q_pos_offset, tab, p.P, scale_log2, ws_o, ws_ml, p.n_splits, p.keys_per_split, p.n_hg)
+                     q_pos_offset, tab, p.P, scale_log2, ws_o, ws_ml, p.n_splits, p.n_hg)
     switch (G) {
       case 1: DC_LAUNCH(1); break;
       case 2: DC_LAUNCH(2); break;

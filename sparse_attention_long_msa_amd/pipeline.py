@@ -50,6 +50,9 @@ class LayerRunner:
         self.tk_ws = ws(B.msa_topk_workspace(batch, n_docs, k))
         self.at_ws = ws(B.msa_sparse_attn_workspace(dt, batch, tokens, q_heads, kv_heads, head_dim, self.max_ctx,
                                                     local_len, self.q_pos_offset))
+        # the RoPE (cos, sin) rows are the same for every layer: built once
+        self.rope_table = B.msa_rope_table(B.msa_rope_table_rows(self.max_ctx, local_len, self.q_pos_offset),
+                                           head_dim, rope_base, device=dev)
         self.ids_h = None
         self.copy_stream = None
         if src_mode == B.MSA_SRC_HOST_MEMCPY:
@@ -72,7 +75,8 @@ class LayerRunner:
 
     def attend(self, q, k_loc, v_loc, stream=None):
         B.msa_sparse_attn(q, self.k_ctx, self.v_ctx, self.ctx_pos, self.ctx_len, k_loc, v_loc, self.q_pos_offset,
-                          self.rope_base, self.sm_scale, out=self.out, ws=self.at_ws, stream=stream)
+                          self.rope_base, self.sm_scale, out=self.out, ws=self.at_ws, rope_table=self.rope_table,
+                          stream=stream)
         return self.out
 
     def run(self, q_r, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc, stream=None):

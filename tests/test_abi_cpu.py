@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.msa_abi_version() == 2
+    assert M.msa_abi_version() == 3
     assert M.lib.msa_status_string(0).decode() == "ok"
     assert "workspace" in M.lib.msa_status_string(3).decode()
 
@@ -98,7 +98,7 @@ def test_sparse_attn_validation():
         a = dict(base, **kw)
         return L.msa_sparse_attn(a["dtype"], a["q"], a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["kc"], a["vc"],
                                  a["cp"], a["cl"], a["max_ctx"], a["kl"], a["vl"], a["L"], a["qpo"], a["base"],
-                                 a["scale"], a["out"], a["ws"], a["wsb"], a["s"])
+                                 a.get("tab"), a.get("rows", 0), a["scale"], a["out"], a["ws"], a["wsb"], a["s"])
     assert call(Hq=30) == 1          # Hq % Hkv
     assert call(L=3) == 1            # L_loc < T
     assert call(d=127) == 1          # odd head dim
@@ -106,7 +106,12 @@ def test_sparse_attn_validation():
     assert call(d=512) == 2
     assert call(q=None) == 1
     assert call(wsb=16) == 3
+    assert call(tab=P, rows=5) == 1  # caller table shorter than msa_rope_table_rows()
     assert L.msa_sparse_attn_workspace(1, 1, 4, 32, 8, 128, 16, 8, 4) > 0
+    assert L.msa_rope_table_rows(2048, 8192, 16) == 8208
+    assert L.msa_rope_table_rows(64, 1, 4) == 64
+    assert L.msa_rope_table(0, 128, 1e6, P, None) == 1
+    assert L.msa_rope_table(10, 128, 1.0, P, None) == 1
 
 
 def test_pool_and_docmap_validation():

@@ -193,3 +193,21 @@ def test_sparse_attention(bf16, B, T, L_loc, ctx):
         worst = max(worst, e)
         assert e <= ATOL_ATTN["bf16" if bf16 else "f32"], f"b={b}: max-abs {e}"
     print(f"attention bf16={bf16} B={B} T={T}: max-abs {worst:.3g}")
+
+
+def test_rope_table_values_and_reuse():
+    rows, d, base = M.msa_rope_table_rows(2048, 8192, 16), 128, 1e6
+    tab = M.msa_rope_table(rows, d, base, device=dev()).cpu().numpy().astype(np.float64)
+    ang = O.rope_angles(np.arange(rows), d, base)               # float64 angles
+    np.testing.assert_allclose(tab[..., 0], np.cos(ang), atol=1e-7, rtol=0)
+    np.testing.assert_allclose(tab[..., 1], np.sin(ang), atol=1e-7, rtol=0)
+    # a caller-built table gives the same bits as the per-call one
+    B, T, Hq, Hkv, L_loc, qpo = 2, 1, 32, 8, 300, 16
+    ctx = [77, 128]
+    q, kl, vl, kc, vc, cp, cl = _attn_case(91, B, T, Hq, Hkv, d, L_loc, ctx, True, max(ctx))
+    args = (to_dev(q, True), to_dev(kc, True), to_dev(vc, True), torch.from_numpy(cp).to(dev()),
+            torch.from_numpy(cl).to(dev()), to_dev(kl, True), to_dev(vl, True), qpo)
+    t2 = M.msa_rope_table(M.msa_rope_table_rows(max(ctx), L_loc, qpo), d, base, device=dev())
+    a = M.msa_sparse_attn(*args)
+    b = M.msa_sparse_attn(*args, rope_table=t2)
+    assert torch.equal(a, b)
