@@ -64,7 +64,23 @@ __global__ __launch_bounds__(GK_THREADS) void gather_kernel(const int32_t* __res
     const uint4* vs = v_bar + lo * row_vec;
     uint4* kd = k_ctx + (int64_t(b) * max_ctx + dest) * row_vec;
     uint4* vd = v_ctx + (int64_t(b) * max_ctx + dest) * row_vec;
-    for (int64_t i = threadIdx.x; i < total; i += GK_THREADS) {
+    // four independent 16-byte loads of K and of V in flight per thread
+    constexpr int U = 4;
+    int64_t i = threadIdx.x;
+    for (; i + (U - 1) * GK_THREADS < total; i += U * GK_THREADS) {
+      uint4 a[U], c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        a[u] = ks[i + u * GK_THREADS];
+        c[u] = vs[i + u * GK_THREADS];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kd[i + u * GK_THREADS] = a[u];
+        vd[i + u * GK_THREADS] = c[u];
+      }
+    }
+    for (; i < total; i += GK_THREADS) {
       kd[i] = ks[i];
       vd[i] = vs[i];
     }

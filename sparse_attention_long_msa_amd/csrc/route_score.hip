@@ -91,6 +91,43 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
   if (range >= n_ranges) return;
   const int col0 = group * 64;
 
+  const int g4 = lane / 16;       // lane group: k-slice of the operands, row block of the result
+  const int lc = lane % 16;       // column (query token) of this lane inside a 16-column tile
+  const int64_t tiles_total = (n_chunks + RS_TILE - 1) / RS_TILE;
+  const int64_t t_begin = int64_t(range) * tiles_per_range;
+  int64_t t_end = t_begin + tiles_per_range;
+  if (t_end > tiles_total) t_end = tiles_total;
+  const int64_t rowE = int64_t(H) * RS_D;  // elements per chunk
+  int64_t tile = t_begin + wave;
+
+  // A operand of head h for the tile: lane (lc, g4) holds chunk row lc, elements
+  // 32*kk + 8*g4 .. +8 of the head.  Row-major stores give four lanes 64
+  // contiguous bytes per load; the tiled layout gives the wave 1 KB.
+  const int64_t n_cgroups = (n_chunks + 15) / 16;   // 16-chunk groups of the tiled layout
+  auto load_head = [&](int64_t tl, int h, uint4 (&dst)[RS_MT][RS_KK]) {
+#pragma unroll
+    for (int m = 0; m < RS_MT; ++m) {
+      if constexpr (TILED) {
+        // 16-chunk group: one wave instruction reads 1 KB contiguous (lane-ordered)
+        int64_t grp = tl * RS_MT + m;
+        if (grp >= n_cgroups) grp = n_cgroups - 1;
+        const uint16_t* p = kr + grp * (16 * rowE) + int64_t(h) * (16 * RS_D) + 8 * lane;
+#pragma unroll
+        for (int kk = 0; kk < RS_KK; ++kk) dst[m][kk] = load_stream(p + kk * 512);   // read once
+      } else {
+        int64_t c = tl * RS_TILE + 16 * m + lc;
+        if (c >= n_chunks) c = n_chunks - 1;
+        const uint4* p = reinterpret_cast<const uint4*>(kr + c * rowE + int64_t(h) * RS_D + 8 * g4);
+#pragma unroll
+        for (int kk = 0; kk < RS_KK; ++kk) dst[m][kk] = p[kk * 4];
+      }
+    }
+  };
+
+  // the first head of the first tile is in flight while the queries are staged
+  uint4 bufA[RS_MT][RS_KK], bufB[RS_MT][RS_KK];
+  if (tile < t_end) load_head(tile, 0, bufA);
+
   // ---- stage the raw routing queries of this column group in fragment order
   const int nfrag_pieces = NT * H * RS_KK * 64;
   for (int p = threadIdx.x; p < nfrag_pieces; p += RS_THREADS) {
@@ -104,8 +141,6 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
   __syncthreads();
 
   // ---- column scale w[h][n][lc] = 1 / (H * max(||q[col,h]||, eps)), kept in LDS
-  const int g4 = lane / 16;       // lane group: k-slice of the operands, row block of the result
-  const int lc = lane % 16;       // column (query token) of this lane inside a 16-column tile
   float* wl = reinterpret_cast<float*>(smem + size_t(NT) * H * RS_KK * 1024 + size_t(RS_WAVES) * RS_SCRATCH);
   if (wave == 0) {
     for (int n = 0; n < NT; ++n)
@@ -136,37 +171,6 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     colb[n] = col < J ? col / T : -1;
   }
 
-  const int64_t tiles_total = (n_chunks + RS_TILE - 1) / RS_TILE;
-  const int64_t t_begin = int64_t(range) * tiles_per_range;
-  int64_t t_end = t_begin + tiles_per_range;
-  if (t_end > tiles_total) t_end = tiles_total;
-  const int64_t rowE = int64_t(H) * RS_D;  // elements per chunk
-  int64_t tile = t_begin + wave;
-  if (tile >= t_end) return;
-
-  // A operand of head h for the tile: lane (lc, g4) reads chunk row lc, elements
-  // 32*kk + 8*g4 .. +8 of the head (four lanes cover 64 contiguous bytes)
-  const int64_t n_cgroups = (n_chunks + 15) / 16;   // 16-chunk groups of the tiled layout
-  auto load_head = [&](int64_t tl, int h, uint4 (&dst)[RS_MT][RS_KK]) {
-#pragma unroll
-    for (int m = 0; m < RS_MT; ++m) {
-      if constexpr (TILED) {
-        // 16-chunk group: one wave instruction reads 1 KB contiguous (lane-ordered)
-        int64_t grp = tl * RS_MT + m;
-        if (grp >= n_cgroups) grp = n_cgroups - 1;
-        const uint16_t* p = kr + grp * (16 * rowE) + int64_t(h) * (16 * RS_D) + 8 * lane;
-#pragma unroll
-        for (int kk = 0; kk < RS_KK; ++kk) dst[m][kk] = load_stream(p + kk * 512);   // read once
-      } else {
-        int64_t c = tl * RS_TILE + 16 * m + lc;
-        if (c >= n_chunks) c = n_chunks - 1;
-        const uint4* p = reinterpret_cast<const uint4*>(kr + c * rowE + int64_t(h) * RS_D + 8 * g4);
-#pragma unroll
-        for (int kk = 0; kk < RS_KK; ++kk) dst[m][kk] = p[kk * 4];
-      }
-    }
-  };
-
   f32x4 tot[RS_MT][NT];
   auto head_step = [&](const uint4 (&a)[RS_MT][RS_KK], int h) {
     f32x4 acc[RS_MT][NT];
@@ -190,8 +194,7 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     }
   };
 
-  uint4 bufA[RS_MT][RS_KK], bufB[RS_MT][RS_KK];
-  load_head(tile, 0, bufA);
+  if (tile >= t_end) return;
   for (;;) {
     const int mydoc = (lane < 32 && tile * RS_TILE + lane < n_chunks) ? chunk_doc[tile * RS_TILE + lane] : -1;
 #pragma unroll

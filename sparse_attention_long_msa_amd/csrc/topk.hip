@@ -100,30 +100,56 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
   return (uint64_t(hi) << 32) | lo;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_mov64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp(int(uint32_t(v)), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(int(uint32_t(v >> 32)), CTRL, 0xF, 0xF, false);
+  return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+}
+
+// value of lane (lane ^ stride): DPP inside a 16-lane row, cross-lane
+// permutes for 16 and 32
+template <int STRIDE>
+__device__ __forceinline__ uint64_t xor_partner64(uint64_t v, int lane) {
+  if constexpr (STRIDE == 1) return dpp_mov64<0xB1>(v);          // quad_perm [1,0,3,2]
+  else if constexpr (STRIDE == 2) return dpp_mov64<0x4E>(v);     // quad_perm [2,3,0,1]
+  else if constexpr (STRIDE == 4) {
+    // row_ror:n hands lane i the value of lane (i - n) mod 16 within its row
+    const uint64_t a = dpp_mov64<0x124>(v), b = dpp_mov64<0x12C>(v);   // from i - 4 / i + 4
+    return (lane & 4) ? a : b;
+  } else if constexpr (STRIDE == 8) return dpp_mov64<0x128>(v);  // row_ror 8
+  else return shfl_xor64(v, STRIDE);
+}
+
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t key, int lane) {
+  const uint64_t other = xor_partner64<STRIDE>(key, lane);
+  const bool up = (lane & SIZE) == 0 || SIZE == 64;
+  const bool lower = (lane & STRIDE) == 0;
+  return (lower == up) ? (key < other ? key : other) : (key < other ? other : key);
+}
+
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint64_t bitonic_stage(uint64_t key, int lane) {
+  key = bitonic_step<SIZE, STRIDE>(key, lane);
+  if constexpr (STRIDE > 1) key = bitonic_stage<SIZE, STRIDE / 2>(key, lane);
+  return key;
+}
+
 // ascending bitonic sort of one key per lane over the 64 lanes
 __device__ __forceinline__ uint64_t wave_sort64(uint64_t key, int lane) {
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint64_t other = shfl_xor64(key, stride);
-      const bool up = (lane & size) == 0 || size == 64;
-      const bool lower = (lane & stride) == 0;
-      key = (lower == up) ? (key < other ? key : other) : (key < other ? other : key);
-    }
-  }
+  key = bitonic_stage<2, 1>(key, lane);
+  key = bitonic_stage<4, 2>(key, lane);
+  key = bitonic_stage<8, 4>(key, lane);
+  key = bitonic_stage<16, 8>(key, lane);
+  key = bitonic_stage<32, 16>(key, lane);
+  key = bitonic_stage<64, 32>(key, lane);
   return key;
 }
 
 // sorts a bitonic sequence held one key per lane (ascending)
 __device__ __forceinline__ uint64_t wave_merge64(uint64_t key, int lane) {
-#pragma unroll
-  for (int stride = 32; stride > 0; stride >>= 1) {
-    const uint64_t other = shfl_xor64(key, stride);
-    const bool lower = (lane & stride) == 0;
-    key = lower ? (key < other ? key : other) : (key < other ? other : key);
-  }
-  return key;
+  return bitonic_stage<64, 32>(key, lane);
 }
 
 __device__ __forceinline__ uint64_t wave_insert(uint64_t best, uint64_t key, int lane, int k) {
