@@ -31,7 +31,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="cfg4")
     ap.add_argument("--kv-tier", choices=["host", "hbm"], default="host")
-    ap.add_argument("--gather", choices=["mapped", "memcpy"], default="mapped")
+    ap.add_argument("--gather", choices=["mapped", "memcpy"], default="mapped",
+                    help="host tier: how the selected K/V cross the host link")
+    ap.add_argument("--hbm-assembly", choices=["index", "copy"], default="index",
+                    help="HBM tier: attention reads the selected rows in place (index) or from a gathered copy")
     ap.add_argument("--layers", type=int, default=None, help="override the routed-layer count (profiling only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-chunks", type=int, default=262144)
@@ -156,7 +159,7 @@ def main():
     runner = M.LayerRunner(batch=p.B, tokens=p.T, q_heads=p.Hq, kv_heads=H, head_dim=d, n_docs=D, n_chunks=N,
                            k=p.k, max_doc_chunks=p.max_doc_chunks, local_len=p.L_loc, dtype=bf, device=dev,
                            q_pos_offset=p.qpo, rope_base=p.rope_base, src_mode=src_mode, chunk_off_h=chunk_off,
-                           kr_layout=kr_layout)
+                           kr_layout=kr_layout, indexed=(tier == "hbm" and args.hbm_assembly == "index"))
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -238,7 +241,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; planted needles)",
         "config": {"workload": workload,
                    "global_batch": p.B, "seq_len": p.T, "parallelism": "single GPU",
-                   "kv_tier": tier, "gather": args.gather if tier == "host" else "hbm"},
+                   "kv_tier": tier, "gather": args.gather if tier == "host" else f"hbm-{args.hbm_assembly}"},
         "route_attn_us_per_query": round(ms_per_step * 1e3 / p.B, 1),
         "routing_GBps": round(routing_gbps, 1),
         "routing_frac_of_8TBps": round(routing_gbps / 8000, 4),

@@ -7,7 +7,8 @@
  *   Stage 1, Global Memory Encoding  -> msa_pool_encode
  *   Stage 2, Online Routing & Context Assembly
  *                                     -> msa_route_score, msa_topk, msa_gather_kv
- *   Stage 3, Sparse Generation        -> msa_sparse_attn
+ *                                        (or msa_context_index for a store in HBM)
+ *   Stage 3, Sparse Generation        -> msa_sparse_attn (msa_sparse_attn_indexed)
  * The layer itself is described in the README's Overall Design > Architecture
  * and in the "MSA-arXiv26" paper note, section 核心方法 > 架构 and
  * Document-wise RoPE.
@@ -217,6 +218,26 @@ int msa_gather_kv(int dtype, const int32_t* ids, int B, int k, const int64_t* ch
                   void* stream, void* copy_stream);
 
 /*
+ * msa_context_index - Stage 2 context assembly for a store that stays in
+ * device memory (README, Inference Pipeline: only the selected documents'
+ * K/V take part; the concatenation with the local context is then an index,
+ * not a copy).  Same context definition as msa_gather_kv, but instead of the
+ * rows themselves it writes where they live:
+ *   ctx_row[b,e] = c (row of the pooled K/V store), ctx_pos[b,e] = c - chunk_off[doc]
+ *   ctx_len[b]   = sum of the selected documents' chunk counts
+ * Entries e >= ctx_len[b] are left untouched.
+ *   ids        [B, k] int32 device; ids outside [0, n_docs) contribute nothing
+ *   chunk_off  [n_docs + 1] int64 device
+ *   n_chunks   rows of the store (< 2^31, rows are int32)
+ *   ctx_row, ctx_pos [B, max_ctx] int32, ctx_len [B] int32 device outputs
+ * Errors: INVALID_ARG (NULL, sizes, max_ctx < k * max_doc_chunks),
+ * UNSUPPORTED (n_chunks >= 2^31, B or k > 65535), HIP.
+ */
+int msa_context_index(const int32_t* ids, int B, int k, const int64_t* chunk_off, int64_t n_docs,
+                      int max_doc_chunks, int64_t n_chunks, int max_ctx, int32_t* ctx_row, int32_t* ctx_pos,
+                      int32_t* ctx_len, void* stream);
+
+/*
  * msa_sparse_attn - Stage 3 sparse attention (README, Overall Design >
  * Architecture: the selected compressed K/V concatenated with the query's
  * local K/V for autoregressive decoding; "Parallel (document-wise) RoPE"
@@ -248,6 +269,23 @@ int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, int Hkv, int
                     const void* k_loc, const void* v_loc, int L_loc, int q_pos_offset, float rope_base,
                     const float* rope_table, int rope_table_rows, float sm_scale, float* out, void* ws,
                     size_t ws_bytes, void* stream);
+
+/*
+ * msa_sparse_attn_indexed - msa_sparse_attn over a context given by
+ * msa_context_index: context entry e of query b is row ctx_row[b,e] of the
+ * pooled store k_bar/v_bar [n_chunks, Hkv, d] (device memory, dtype), read in
+ * place.  Every other argument, the result and the workspace
+ * (msa_sparse_attn_workspace) are those of msa_sparse_attn; the two give
+ * bit-identical outputs for the same context.  Rows outside [0, n_chunks) are
+ * clamped into the store (they are a caller error, never an out-of-bounds read).
+ * Errors: those of msa_sparse_attn; INVALID_ARG also for ctx_row NULL or
+ * n_chunks outside [1, 2^31).
+ */
+int msa_sparse_attn_indexed(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d, const void* k_bar,
+                            const void* v_bar, int64_t n_chunks, const int32_t* ctx_row, const int32_t* ctx_pos,
+                            const int32_t* ctx_len, int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
+                            int q_pos_offset, float rope_base, const float* rope_table, int rope_table_rows,
+                            float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * msa_rope_table - the (cos, sin) rows msa_sparse_attn rotates with, built

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     msa_abi_version,
     msa_chunk_doc_map,
     msa_chunk_offsets,
+    msa_context_index,
     msa_gather_kv,
     msa_pool_encode,
     msa_route_score,
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     msa_rope_table_rows,
     msa_route_score_workspace,
     msa_sparse_attn,
+    msa_sparse_attn_indexed,
     msa_sparse_attn_workspace,
     msa_topk,
     msa_tile_routing_keys,

@@ -38,9 +38,12 @@ _SIGS = {
     "msa_topk": (_I, [_P, _I, _L, _I, _P, _P, _P, _S, _P]),
     "msa_gather_kv": (_I, [_I, _P, _I, _I, _P, _P, _L, _I, _P, _P, _L, _I, _I, _I, _I,
                            _P, _P, _P, _P, _P, _P, _P]),
+    "msa_context_index": (_I, [_P, _I, _I, _P, _L, _I, _L, _I, _P, _P, _P, _P]),
     "msa_sparse_attn_workspace": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "msa_sparse_attn": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _I, _I,
                              _F, _P, _I, _F, _P, _P, _S, _P]),
+    "msa_sparse_attn_indexed": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _L, _P, _P, _P, _I, _P, _P, _I, _I,
+                                     _F, _P, _I, _F, _P, _P, _S, _P]),
     "msa_rope_table_rows": (_I, [_I, _I, _I]),
     "msa_rope_table": (_I, [_I, _I, _F, _P, _P]),
 }
@@ -212,6 +215,22 @@ def msa_gather_kv(ids, chunk_off, k_bar, v_bar, max_doc_chunks, max_ctx, src_mod
     return k_ctx, v_ctx, ctx_pos, ctx_len
 
 
+def msa_context_index(ids, chunk_off, n_chunks, max_doc_chunks, max_ctx, ctx_row=None, ctx_pos=None, ctx_len=None,
+                      stream=None):
+    B, k = ids.shape
+    dev = ids.device
+    if ctx_row is None:
+        ctx_row = torch.empty((B, max_ctx), dtype=torch.int32, device=dev)
+    if ctx_pos is None:
+        ctx_pos = torch.empty((B, max_ctx), dtype=torch.int32, device=dev)
+    if ctx_len is None:
+        ctx_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check("msa_context_index", lib.msa_context_index(
+        _ptr(ids), B, k, _ptr(chunk_off), chunk_off.numel() - 1, max_doc_chunks, n_chunks, max_ctx, _ptr(ctx_row),
+        _ptr(ctx_pos), _ptr(ctx_len), _stream(stream)))
+    return ctx_row, ctx_pos, ctx_len
+
+
 def msa_sparse_attn_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset):
     return lib.msa_sparse_attn_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset)
 
@@ -241,6 +260,26 @@ def msa_sparse_attn(q, k_ctx, v_ctx, ctx_pos, ctx_len, k_loc, v_loc, q_pos_offse
     _check("msa_sparse_attn", lib.msa_sparse_attn(
         dt, _ptr(q), B, T, Hq, Hkv, d, _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_pos), _ptr(ctx_len), max_ctx,
         _ptr(k_loc), _ptr(v_loc), L_loc, q_pos_offset, float(rope_base), _ptr(rope_table),
+        0 if rope_table is None else rope_table.shape[0], float(sm_scale), _ptr(out), _ptr(ws), wsb,
+        _stream(stream)))
+    return out
+
+
+def msa_sparse_attn_indexed(q, k_bar, v_bar, ctx_row, ctx_pos, ctx_len, k_loc, v_loc, q_pos_offset, rope_base=1e6,
+                            sm_scale=None, out=None, ws=None, rope_table=None, stream=None):
+    B, T, Hq, d = q.shape
+    n_chunks, Hkv = k_bar.shape[0], k_bar.shape[1]
+    max_ctx = ctx_row.shape[1]
+    L_loc = k_loc.shape[1]
+    dt = _dtype(q)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
+    ws, wsb = _ws(msa_sparse_attn_workspace(dt, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset), q.device, ws)
+    _check("msa_sparse_attn_indexed", lib.msa_sparse_attn_indexed(
+        dt, _ptr(q), B, T, Hq, Hkv, d, _ptr(k_bar), _ptr(v_bar), n_chunks, _ptr(ctx_row), _ptr(ctx_pos),
+        _ptr(ctx_len), max_ctx, _ptr(k_loc), _ptr(v_loc), L_loc, q_pos_offset, float(rope_base), _ptr(rope_table),
         0 if rope_table is None else rope_table.shape[0], float(sm_scale), _ptr(out), _ptr(ws), wsb,
         _stream(stream)))
     return out

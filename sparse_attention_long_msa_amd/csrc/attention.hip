@@ -118,13 +118,54 @@ struct KeySrc {
   bool valid;
 };
 
+// Context entry e of query b: row b * max_ctx + e of a gathered context, or,
+// when ctx_row is given, row ctx_row[b, e] of the pooled store itself (the
+// concatenation is then only an index; rows are clamped into the store).
+__device__ __forceinline__ int64_t ctx_src_row(int64_t e, const int32_t* __restrict__ ctx_row, int64_t ctx_rows) {
+  if (!ctx_row) return e;
+  const int64_t r = ctx_row[e];
+  return r < 0 ? 0 : (r >= ctx_rows ? ctx_rows - 1 : r);
+}
+
+// A workgroup's context entries [lo, lo + n) as (store row, clamped
+// position), staged in LDS once so that no step waits on an index load.
+constexpr int AT_CIDX = 2048;
+constexpr int AT_CIDX_BYTES = AT_CIDX * 8;
+struct CtxCache {
+  const int2* e;
+  int lo, n;
+};
+
+__device__ __forceinline__ CtxCache stage_ctx(int2* lds, int b, int j_begin, int j_end, int ctxl, int max_ctx,
+                                              const int32_t* __restrict__ ctx_pos, int P,
+                                              const int32_t* __restrict__ ctx_row, int64_t ctx_rows, int tid,
+                                              int nthr) {
+  CtxCache c;
+  c.e = lds;
+  c.lo = j_begin;
+  c.n = max(0, min(min(j_end, ctxl) - j_begin, AT_CIDX));
+  for (int i = tid; i < c.n; i += nthr) {
+    const int64_t e = int64_t(b) * max_ctx + j_begin + i;
+    int p = ctx_pos[e];
+    p = p < 0 ? 0 : (p >= P ? P - 1 : p);
+    lds[i] = make_int2(ctx_row ? int(ctx_src_row(e, ctx_row, ctx_rows)) : 0, p);
+  }
+  return c;
+}
+
 __device__ __forceinline__ KeySrc key_src(int j, int b, int ctxl, int n_keys, int max_ctx, int L_loc, int qpo,
-                                          const int32_t* __restrict__ ctx_pos, int P) {
+                                          const int32_t* __restrict__ ctx_pos, int P,
+                                          const int32_t* __restrict__ ctx_row, int64_t ctx_rows,
+                                          const CtxCache& cc) {
   KeySrc k;
   if (j < ctxl) {
-    k.row = int64_t(b) * max_ctx + j;
-    int p = ctx_pos[int64_t(b) * max_ctx + j];
-    k.pos = p < 0 ? 0 : (p >= P ? P - 1 : p);
+    // every context key of the workgroup's range is cached (the host sizes the
+    // splits for it); keys past the range end are masked, any row will do
+    const int i = j - cc.lo;
+    const bool in = i >= 0 && i < cc.n;
+    const int2 v = in ? cc.e[i] : make_int2(0, 0);
+    k.row = ctx_row ? int64_t(v.x) : int64_t(b) * max_ctx + (in ? j : 0);
+    k.pos = v.y;
     k.local = false;
     k.valid = true;
   } else if (j < n_keys) {
@@ -159,14 +200,15 @@ struct DcRegs {
   uint4 t[2];        // this thread's share of the step's RoPE rows
 };
 
-template <int G>
+template <int G, bool IDX>
 __global__ __launch_bounds__(512) void attn_decode_kernel(
     const uint16_t* __restrict__ q, int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_ctx,
     const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
-    const float2* __restrict__ tab, int P, float scale_log2, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
-    int n_splits, int n_hg) {
+    const int32_t* __restrict__ ctx_row_in, int64_t ctx_rows, const float2* __restrict__ tab, int P, float scale_log2,
+    float* __restrict__ ws_o, float2* __restrict__ ws_ml, int n_splits, int n_hg) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int32_t* __restrict__ ctx_row = IDX ? ctx_row_in : nullptr;
   const int nw = blockDim.x / 64;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int lc = lane % 16, g4 = lane / 16;
@@ -203,7 +245,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
     for (int kk = 0; kk < 4; ++kk) bq[kk] = __builtin_bit_cast(bf16x8, row_ok ? qv[kk] : make_uint4(0, 0, 0, 0));
   }
 
-  const int ctxl = ctx_len[b];
+  const int ctxl = min(max(ctx_len[b], 0), max_ctx);
   const int n_keys = ctxl + L_loc;
   // this query's keys split evenly over the n_splits workgroups (32-key steps)
   const int kps = ((n_keys + n_splits - 1) / n_splits + 31) / 32 * 32;
@@ -213,6 +255,9 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
   // a step whose 32 keys are all local tokens addresses them affinely
   auto all_local = [&](int j0) { return j0 >= ctxl && j0 + 32 <= n_keys; };
 
+  const CtxCache cc = stage_ctx(reinterpret_cast<int2*>(smem + 2 * DC_TAB_BYTES + size_t(nw) * AT_V_BYTES), b, j_begin,
+                                j_end, ctxl, max_ctx, ctx_pos, P, ctx_row, ctx_rows, tid, nthr);
+  __syncthreads();
   auto load_k = [&](int j0, DcRegs& R) {
     if (all_local(j0)) {
       const uint16_t* kb = k_loc + (int64_t(b) * L_loc + (j0 - ctxl)) * kv_stride + int64_t(gg) * AT_D + 8 * g4;
@@ -226,7 +271,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
     }
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const KeySrc ks = key_src(j0 + 16 * tau + lc, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+      const KeySrc ks = key_src(j0 + 16 * tau + lc, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
       const uint16_t* kp = (ks.local ? k_loc : k_ctx) + ks.row * kv_stride + int64_t(gg) * AT_D + 8 * g4;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) R.k[tau][kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
@@ -252,7 +297,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
     for (int rho = 0; rho < 2; ++rho)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const KeySrc ks = key_src(j0 + 16 * rho + 4 * g4 + i, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+        const KeySrc ks = key_src(j0 + 16 * rho + 4 * g4 + i, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
         const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(gg) * AT_D + 8 * lc;
         R.v[rho][i] = *reinterpret_cast<const uint4*>(vp);
       }
@@ -261,7 +306,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
       const int piece = tid + u * nthr;
       if (piece < 32 * 32) {
         const int key = piece / 32, off = piece % 32;
-        const KeySrc ks = key_src(j0 + key, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+        const KeySrc ks = key_src(j0 + key, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
         R.t[u] = reinterpret_cast<const uint4*>(tab + int64_t(ks.pos) * (AT_D / 2))[off];
       }
     }
@@ -419,14 +464,15 @@ struct PfRegs {
   uint4 v;            // V[t/16][8*(t%16) .. +7]
 };
 
-template <int G, int RTW>
+template <int G, int RTW, bool IDX>
 __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_ctx,
     const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
-    const float2* __restrict__ tab, int P, float scale_log2, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
-    int n_splits, int n_rt, int n_rg) {
+    const int32_t* __restrict__ ctx_row_in, int64_t ctx_rows, const float2* __restrict__ tab, int P, float scale_log2,
+    float* __restrict__ ws_o, float2* __restrict__ ws_ml, int n_splits, int n_rt, int n_rg) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int32_t* __restrict__ ctx_row = IDX ? ctx_row_in : nullptr;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int lc = lane % 16, g4 = lane / 16;
 
@@ -464,7 +510,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     for (int kk = 0; kk < 4; ++kk) bq[i][kk] = __builtin_bit_cast(bf16x8, rok[i] ? qv[kk] : make_uint4(0, 0, 0, 0));
   }
 
-  const int ctxl = ctx_len[b];
+  const int ctxl = min(max(ctx_len[b], 0), max_ctx);
   const int n_keys = ctxl + L_loc;
   // this query's keys split evenly over the n_splits workgroups (32-key steps)
   const int kps = ((n_keys + n_splits - 1) / n_splits + 31) / 32 * 32;
@@ -473,10 +519,13 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
 
   // cooperative mapping of one 32-key step
   const int lk = tid / 16, lx = tid % 16;     // K: key, 4-dim block; V: key, 8-dim block
+  const CtxCache cc = stage_ctx(reinterpret_cast<int2*>(smem + 2 * size_t(PF_BUF)), b, j_begin, j_end, ctxl, max_ctx,
+                                ctx_pos, P, ctx_row, ctx_rows, tid, PF_THREADS);
+  __syncthreads();
 
   auto load_step = [&](int j0, PfRegs& R) {
     {
-      const KeySrc ks = key_src(j0 + lk, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+      const KeySrc ks = key_src(j0 + lk, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
       const uint16_t* kp = (ks.local ? k_loc : k_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 4 * lx;
       R.klo = *reinterpret_cast<const uint2*>(kp);
       R.khi = *reinterpret_cast<const uint2*>(kp + 64);
@@ -485,7 +534,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
       R.cs1 = cp[1];
     }
     {
-      const KeySrc ks = key_src(j0 + lk, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P);
+      const KeySrc ks = key_src(j0 + lk, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
       const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 8 * lx;
       R.v = *reinterpret_cast<const uint4*>(vp);
     }
@@ -664,7 +713,8 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
     const typename Elem<DT>::T* __restrict__ k_ctx, const typename Elem<DT>::T* __restrict__ v_ctx,
     const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len, int max_ctx,
     const typename Elem<DT>::T* __restrict__ k_loc, const typename Elem<DT>::T* __restrict__ v_loc, int L_loc,
-    int qpo, const float2* __restrict__ tab, int P, float sm_scale, float* __restrict__ out) {
+    int qpo, const int32_t* __restrict__ ctx_row, int64_t ctx_rows, const float2* __restrict__ tab, int P,
+    float sm_scale, float* __restrict__ out) {
   using E = Elem<DT>;
   extern __shared__ float vsm[];
   float* qr = vsm;               // [d]
@@ -685,7 +735,7 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
     qr[m + half] = x2 * cs.x + x1 * cs.y;
   }
   __syncthreads();
-  const int ctxl = ctx_len[b];
+  const int ctxl = min(max(ctx_len[b], 0), max_ctx);
   const int n_keys = ctxl + L_loc;
   float mx = -INFINITY;
   for (int j = threadIdx.x; j < n_keys; j += AT_VEC_THREADS) {
@@ -693,7 +743,7 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
     int pos;
     bool vis = true;
     if (j < ctxl) {
-      kp = k_ctx + ((int64_t(b) * max_ctx + j) * Hkv + g) * d;
+      kp = k_ctx + (ctx_src_row(int64_t(b) * max_ctx + j, ctx_row, ctx_rows) * Hkv + g) * d;
       pos = ctx_pos[int64_t(b) * max_ctx + j];
       pos = pos < 0 ? 0 : (pos >= P ? P - 1 : pos);
     } else {
@@ -743,7 +793,7 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
     for (int j = 0; j < n_keys; ++j) {
       const float p = logit[j];
       if (p == 0.f) continue;
-      const typename E::T* vp = j < ctxl ? v_ctx + ((int64_t(b) * max_ctx + j) * Hkv + g) * d
+      const typename E::T* vp = j < ctxl ? v_ctx + (ctx_src_row(int64_t(b) * max_ctx + j, ctx_row, ctx_rows) * Hkv + g) * d
                                          : v_loc + ((int64_t(b) * L_loc + (j - ctxl)) * Hkv + g) * d;
       acc += p * E::load(vp, e);
     }
@@ -786,9 +836,11 @@ static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int m
     units = int64_t(B) * p.n_hg;            // workgroups per split
     target = 512;                            // two rounds of one 8-wave workgroup per CU
   }
-  // the kernels split each query's actual keys evenly over n_splits
+  // the kernels split each query's actual keys evenly over n_splits; a split's
+  // context entries must fit the workgroup's LDS index cache
   int64_t s = (target + units - 1) / units;
   s = std::max<int64_t>(1, std::min<int64_t>(s, (n_keys_max + 63) / 64));
+  if (max_ctx > AT_CIDX) s = std::max<int64_t>(s, (n_keys_max + AT_CIDX - 33) / (AT_CIDX - 32));
   p.n_splits = int(s);
   const int64_t rows = int64_t(B) * T * Hq;
   p.o_bytes = align_up(size_t(p.n_splits) * rows * d * sizeof(float), 256);
@@ -822,31 +874,34 @@ extern "C" size_t msa_sparse_attn_workspace(int dtype, int B, int T, int Hq, int
   return p.tab_bytes + p.o_bytes + p.ml_bytes;
 }
 
-extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d, const void* k_ctx,
-                               const void* v_ctx, const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx,
-                               const void* k_loc, const void* v_loc, int L_loc, int q_pos_offset, float rope_base,
-                               const float* rope_table, int rope_table_rows, float sm_scale, float* out, void* ws,
-                               size_t ws_bytes, void* stream) {
-  using namespace msa;
-  MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, "msa_sparse_attn: bad dtype");
+namespace msa {
+
+// Shared body of msa_sparse_attn (gathered context, ctx_row == NULL) and
+// msa_sparse_attn_indexed (context rows read in place from the pooled store).
+static int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
+                       const void* k_ctx, const void* v_ctx, const int32_t* ctx_row, int64_t ctx_rows,
+                       const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx, const void* k_loc,
+                       const void* v_loc, int L_loc, int q_pos_offset, float rope_base, const float* rope_table,
+                       int rope_table_rows, float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
   MSA_REQUIRE(q && k_ctx && v_ctx && ctx_pos && ctx_len && k_loc && v_loc && out && ws, MSA_ERR_INVALID_ARG,
-              "msa_sparse_attn: NULL pointer");
+              fn + ": NULL pointer");
   MSA_REQUIRE(B >= 1 && T >= 1 && Hq >= 1 && Hkv >= 1 && d >= 2 && max_ctx >= 1 && L_loc >= 1, MSA_ERR_INVALID_ARG,
-              "msa_sparse_attn: non-positive size");
-  MSA_REQUIRE(Hq % Hkv == 0, MSA_ERR_INVALID_ARG, "msa_sparse_attn: Hq % Hkv != 0");
-  MSA_REQUIRE(L_loc >= T, MSA_ERR_INVALID_ARG, "msa_sparse_attn: L_loc < T");
-  MSA_REQUIRE(d % 2 == 0, MSA_ERR_INVALID_ARG, "msa_sparse_attn: d must be even");
-  MSA_REQUIRE(q_pos_offset >= 0, MSA_ERR_INVALID_ARG, "msa_sparse_attn: q_pos_offset < 0");
-  MSA_REQUIRE(rope_base > 1.f, MSA_ERR_INVALID_ARG, "msa_sparse_attn: rope_base must exceed 1");
-  MSA_REQUIRE(d <= 256, MSA_ERR_UNSUPPORTED, "msa_sparse_attn: d > 256");
-  MSA_REQUIRE(int64_t(q_pos_offset) + L_loc < (int64_t(1) << 30), MSA_ERR_UNSUPPORTED, "msa_sparse_attn: positions too large");
+              fn + ": non-positive size");
+  MSA_REQUIRE(Hq % Hkv == 0, MSA_ERR_INVALID_ARG, fn + ": Hq % Hkv != 0");
+  MSA_REQUIRE(L_loc >= T, MSA_ERR_INVALID_ARG, fn + ": L_loc < T");
+  MSA_REQUIRE(d % 2 == 0, MSA_ERR_INVALID_ARG, fn + ": d must be even");
+  MSA_REQUIRE(q_pos_offset >= 0, MSA_ERR_INVALID_ARG, fn + ": q_pos_offset < 0");
+  MSA_REQUIRE(rope_base > 1.f, MSA_ERR_INVALID_ARG, fn + ": rope_base must exceed 1");
+  MSA_REQUIRE(d <= 256, MSA_ERR_UNSUPPORTED, fn + ": d > 256");
+  MSA_REQUIRE(int64_t(q_pos_offset) + L_loc < (int64_t(1) << 30), MSA_ERR_UNSUPPORTED, fn + ": positions too large");
   const AttnPlan p = attn_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
-  MSA_REQUIRE(ws_bytes >= p.tab_bytes + p.o_bytes + p.ml_bytes, MSA_ERR_WORKSPACE, "msa_sparse_attn: workspace too small");
+  MSA_REQUIRE(ws_bytes >= p.tab_bytes + p.o_bytes + p.ml_bytes, MSA_ERR_WORKSPACE, fn + ": workspace too small");
   if (!p.mfma)
     MSA_REQUIRE(int64_t(max_ctx) + L_loc <= AT_VEC_MAX_KEYS, MSA_ERR_UNSUPPORTED,
-                "msa_sparse_attn: more than 32768 keys on the vector path");
+                fn + ": more than 32768 keys on the vector path");
   MSA_REQUIRE(!rope_table || rope_table_rows >= p.P, MSA_ERR_INVALID_ARG,
-              "msa_sparse_attn: rope_table has fewer rows than msa_rope_table_rows()");
+              fn + ": rope_table has fewer rows than msa_rope_table_rows()");
   hipStream_t s = as_stream(stream);
   const float2* tab = reinterpret_cast<const float2*>(rope_table);
   if (!tab) {
@@ -860,20 +915,26 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
   if (p.mfma) {
     MSA_REQUIRE(uintptr_t(q) % 16 == 0 && uintptr_t(k_ctx) % 16 == 0 && uintptr_t(v_ctx) % 16 == 0 &&
                     uintptr_t(k_loc) % 16 == 0 && uintptr_t(v_loc) % 16 == 0,
-                MSA_ERR_INVALID_ARG, "msa_sparse_attn: tensors must be 16-byte aligned");
+                MSA_ERR_INVALID_ARG, fn + ": tensors must be 16-byte aligned");
     float* ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.tab_bytes);
     float2* ws_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.tab_bytes + p.o_bytes);
     const int G = Hq / Hkv;
     const float scale_log2_pf = sm_scale * 1.4426950408889634f;
     if (p.prefill) {
       const dim3 pgrid(unsigned(int64_t(B) * Hkv * p.n_rg * p.n_splits)), pblock(PF_THREADS);
-      const size_t psmem = 2 * size_t(PF_BUF);
-#define PF_LAUNCH(GV, RV)                                                                                           \
-  hipLaunchKernelGGL((attn_prefill_kernel<GV, RV>), pgrid, pblock, psmem, s, static_cast<const uint16_t*>(q), B, T,  \
+      const size_t psmem = 2 * size_t(PF_BUF) + AT_CIDX_BYTES;
+#define PF_LAUNCH2(GV, RV, IV)                                                                                      \
+  hipLaunchKernelGGL((attn_prefill_kernel<GV, RV, IV>), pgrid, pblock, psmem, s, static_cast<const uint16_t*>(q), B, T,  \
                      Hq, Hkv, static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos,     \
                      ctx_len, max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc),     \
-                     L_loc, q_pos_offset, tab, p.P, scale_log2_pf, ws_o, ws_ml, p.n_splits, p.n_rt,                  \
-                     p.n_rg)
+                     L_loc, q_pos_offset, ctx_row, ctx_rows, tab, p.P, scale_log2_pf, ws_o, ws_ml, p.n_splits,       \
+                     p.n_rt, p.n_rg)
+#define PF_LAUNCH(GV, RV)       \
+  if (ctx_row) {                \
+    PF_LAUNCH2(GV, RV, true);   \
+  } else {                      \
+    PF_LAUNCH2(GV, RV, false);  \
+  }
       const int key = G * 4 + p.rtw;
       switch (key) {
         case 1 * 4 + 1: PF_LAUNCH(1, 1); break;
@@ -888,6 +949,7 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
         default: PF_LAUNCH(16, 2); break;
       }
 #undef PF_LAUNCH
+#undef PF_LAUNCH2
       MSA_LAUNCH_CHECK();
       const int64_t rows = int64_t(B) * T * Hq;
       hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * (d / 4) + 255) / 256)), dim3(256), 0, s, ws_o,
@@ -897,15 +959,21 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
     }
     const int nw = 8;   // waves beyond Hkv only help stage the RoPE rows
     const dim3 grid(unsigned(int64_t(B) * p.n_hg * p.n_splits)), block(unsigned(64 * nw));
-    const size_t smem = 2 * size_t(DC_TAB_BYTES) + size_t(nw) * AT_V_BYTES;
+    const size_t smem = 2 * size_t(DC_TAB_BYTES) + size_t(nw) * AT_V_BYTES + AT_CIDX_BYTES;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-#define DC_LAUNCH(GV)                                                                                              \
-  MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_decode_kernel<GV>),                        \
+#define DC_LAUNCH2(GV, IV)                                                                                         \
+  MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_decode_kernel<GV, IV>),                    \
                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)));                     \
-  hipLaunchKernelGGL((attn_decode_kernel<GV>), grid, block, smem, s, static_cast<const uint16_t*>(q), B, T, Hq, Hkv, \
+  hipLaunchKernelGGL((attn_decode_kernel<GV, IV>), grid, block, smem, s, static_cast<const uint16_t*>(q), B, T, Hq, Hkv, \
                      static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos, ctx_len,     \
                      max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc), L_loc,       \
-                     q_pos_offset, tab, p.P, scale_log2, ws_o, ws_ml, p.n_splits, p.n_hg)
+                     q_pos_offset, ctx_row, ctx_rows, tab, p.P, scale_log2, ws_o, ws_ml, p.n_splits, p.n_hg)
+#define DC_LAUNCH(GV)        \
+  if (ctx_row) {             \
+    DC_LAUNCH2(GV, true);    \
+  } else {                   \
+    DC_LAUNCH2(GV, false);   \
+  }
     switch (G) {
       case 1: DC_LAUNCH(1); break;
       case 2: DC_LAUNCH(2); break;
@@ -914,6 +982,7 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
       default: DC_LAUNCH(16); break;
     }
 #undef DC_LAUNCH
+#undef DC_LAUNCH2
     MSA_LAUNCH_CHECK();
     const int64_t rows = int64_t(B) * T * Hq;
     hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * (d / 4) + 255) / 256)), dim3(256), 0, s, ws_o,
@@ -927,12 +996,39 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
     hipLaunchKernelGGL(attn_vec_kernel<MSA_BF16>, grid, block, smem, s, static_cast<const uint16_t*>(q), B, T, Hq, Hkv,
                        d, static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos, ctx_len,
                        max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc), L_loc,
-                       q_pos_offset, tab, p.P, sm_scale, out);
+                       q_pos_offset, ctx_row, ctx_rows, tab, p.P, sm_scale, out);
   else
     hipLaunchKernelGGL(attn_vec_kernel<MSA_F32>, grid, block, smem, s, static_cast<const float*>(q), B, T, Hq, Hkv, d,
                        static_cast<const float*>(k_ctx), static_cast<const float*>(v_ctx), ctx_pos, ctx_len, max_ctx,
-                       static_cast<const float*>(k_loc), static_cast<const float*>(v_loc), L_loc, q_pos_offset, tab,
-                       p.P, sm_scale, out);
+                       static_cast<const float*>(k_loc), static_cast<const float*>(v_loc), L_loc, q_pos_offset,
+                       ctx_row, ctx_rows, tab, p.P, sm_scale, out);
   MSA_LAUNCH_CHECK();
   return MSA_OK;
+}
+
+}  // namespace msa
+
+extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d, const void* k_ctx,
+                               const void* v_ctx, const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx,
+                               const void* k_loc, const void* v_loc, int L_loc, int q_pos_offset, float rope_base,
+                               const float* rope_table, int rope_table_rows, float sm_scale, float* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return msa::sparse_attn("msa_sparse_attn", dtype, q, B, T, Hq, Hkv, d, k_ctx, v_ctx, nullptr, 0, ctx_pos, ctx_len,
+                          max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows, sm_scale,
+                          out, ws, ws_bytes, stream);
+}
+
+extern "C" int msa_sparse_attn_indexed(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
+                                       const void* k_bar, const void* v_bar, int64_t n_chunks, const int32_t* ctx_row,
+                                       const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx, const void* k_loc,
+                                       const void* v_loc, int L_loc, int q_pos_offset, float rope_base,
+                                       const float* rope_table, int rope_table_rows, float sm_scale, float* out,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  using namespace msa;
+  MSA_REQUIRE(ctx_row, MSA_ERR_INVALID_ARG, "msa_sparse_attn_indexed: NULL pointer");
+  MSA_REQUIRE(n_chunks >= 1 && n_chunks <= INT32_MAX, MSA_ERR_INVALID_ARG,
+              "msa_sparse_attn_indexed: n_chunks must lie in [1, 2^31)");
+  return sparse_attn("msa_sparse_attn_indexed", dtype, q, B, T, Hq, Hkv, d, k_bar, v_bar, ctx_row, n_chunks, ctx_pos,
+                     ctx_len, max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows,
+                     sm_scale, out, ws, ws_bytes, stream);
 }

@@ -9,7 +9,9 @@
 // One workgroup per (query, rank).  The source may be device memory or
 // mapped pinned host memory (the kernel then reads over the host link);
 // MSA_SRC_HOST_MEMCPY instead issues hipMemcpyAsync per document on a side
-// stream after one host synchronisation on the ids.
+// stream after one host synchronisation on the ids.  msa_context_index writes
+// only each entry's store row, for attention that reads a device-resident
+// store in place.
 #include <vector>
 
 #include "common.h"
@@ -37,14 +39,19 @@ __device__ int64_t rank_offset(const int32_t* __restrict__ ids_b, int r, const i
   return v;
 }
 
-template <bool COPY>
+// MODE: GK_POS writes positions and lengths only, GK_COPY also copies the
+// rows, GK_ROWS writes each entry's store row instead of copying it.
+enum { GK_POS = 0, GK_COPY = 1, GK_ROWS = 2 };
+
+template <int MODE>
 __global__ __launch_bounds__(GK_THREADS) void gather_kernel(const int32_t* __restrict__ ids, int k,
                                                             const int64_t* __restrict__ chunk_off, int64_t n_docs,
                                                             const uint4* __restrict__ k_bar,
                                                             const uint4* __restrict__ v_bar, int64_t row_vec,
                                                             int max_ctx, uint4* __restrict__ k_ctx,
                                                             uint4* __restrict__ v_ctx, int32_t* __restrict__ ctx_pos,
-                                                            int32_t* __restrict__ ctx_len) {
+                                                            int32_t* __restrict__ ctx_len,
+                                                            int32_t* __restrict__ ctx_row) {
   __shared__ int64_t red[GK_THREADS];
   const int r = blockIdx.x, b = blockIdx.y;
   const int32_t* ids_b = ids + int64_t(b) * k;
@@ -57,8 +64,11 @@ __global__ __launch_bounds__(GK_THREADS) void gather_kernel(const int32_t* __res
   }
   if (dest + n > max_ctx) n = dest < max_ctx ? max_ctx - dest : 0;  // never write past the context
   if (r == k - 1 && threadIdx.x == 0) ctx_len[b] = int32_t(dest + n);
-  for (int64_t i = threadIdx.x; i < n; i += GK_THREADS) ctx_pos[int64_t(b) * max_ctx + dest + i] = int32_t(i);
-  if constexpr (COPY) {
+  for (int64_t i = threadIdx.x; i < n; i += GK_THREADS) {
+    ctx_pos[int64_t(b) * max_ctx + dest + i] = int32_t(i);
+    if constexpr (MODE == GK_ROWS) ctx_row[int64_t(b) * max_ctx + dest + i] = int32_t(lo + i);
+  }
+  if constexpr (MODE == GK_COPY) {
     const int64_t total = n * row_vec;
     const uint4* ks = k_bar + lo * row_vec;
     const uint4* vs = v_bar + lo * row_vec;
@@ -122,9 +132,9 @@ extern "C" int msa_gather_kv(int dtype, const int32_t* ids, int B, int k, const 
   hipStream_t s = as_stream(stream);
   const dim3 grid{unsigned(k), unsigned(B)}, block{GK_THREADS};
   if (src_mode != MSA_SRC_HOST_MEMCPY) {
-    hipLaunchKernelGGL(gather_kernel<true>, grid, block, 0, s, ids, k, chunk_off, n_docs,
+    hipLaunchKernelGGL(gather_kernel<GK_COPY>, grid, block, 0, s, ids, k, chunk_off, n_docs,
                        static_cast<const uint4*>(k_bar), static_cast<const uint4*>(v_bar), row_vec, max_ctx,
-                       static_cast<uint4*>(k_ctx), static_cast<uint4*>(v_ctx), ctx_pos, ctx_len);
+                       static_cast<uint4*>(k_ctx), static_cast<uint4*>(v_ctx), ctx_pos, ctx_len, nullptr);
     MSA_LAUNCH_CHECK();
     return MSA_OK;
   }
@@ -134,9 +144,9 @@ extern "C" int msa_gather_kv(int dtype, const int32_t* ids, int B, int k, const 
   MSA_HIP_CHECK(hipMemcpyAsync(ids_h, ids, size_t(B) * k * sizeof(int32_t), hipMemcpyDeviceToHost, s));
   MSA_HIP_CHECK(hipStreamSynchronize(s));
   // positions and lengths on the compute stream
-  hipLaunchKernelGGL(gather_kernel<false>, grid, block, 0, s, ids, k, chunk_off, n_docs,
+  hipLaunchKernelGGL(gather_kernel<GK_POS>, grid, block, 0, s, ids, k, chunk_off, n_docs,
                      static_cast<const uint4*>(k_bar), static_cast<const uint4*>(v_bar), row_vec, max_ctx,
-                     static_cast<uint4*>(k_ctx), static_cast<uint4*>(v_ctx), ctx_pos, ctx_len);
+                     static_cast<uint4*>(k_ctx), static_cast<uint4*>(v_ctx), ctx_pos, ctx_len, nullptr);
   MSA_LAUNCH_CHECK();
   const char* kb = static_cast<const char*>(k_bar);
   const char* vb = static_cast<const char*>(v_bar);
@@ -164,5 +174,25 @@ extern "C" int msa_gather_kv(int dtype, const int32_t* ids, int B, int k, const 
     MSA_HIP_CHECK(hipEventRecord(ce.ev, cs));
     MSA_HIP_CHECK(hipStreamWaitEvent(s, ce.ev, 0));
   }
+  return MSA_OK;
+}
+
+extern "C" int msa_context_index(const int32_t* ids, int B, int k, const int64_t* chunk_off, int64_t n_docs,
+                                 int max_doc_chunks, int64_t n_chunks, int max_ctx, int32_t* ctx_row,
+                                 int32_t* ctx_pos, int32_t* ctx_len, void* stream) {
+  using namespace msa;
+  MSA_REQUIRE(ids && chunk_off && ctx_row && ctx_pos && ctx_len, MSA_ERR_INVALID_ARG,
+              "msa_context_index: NULL pointer");
+  MSA_REQUIRE(B >= 1 && k >= 1 && n_docs >= 1 && n_chunks >= 1 && max_doc_chunks >= 1, MSA_ERR_INVALID_ARG,
+              "msa_context_index: non-positive size");
+  MSA_REQUIRE(k <= n_docs, MSA_ERR_INVALID_ARG, "msa_context_index: k > n_docs");
+  MSA_REQUIRE(n_chunks <= INT32_MAX, MSA_ERR_UNSUPPORTED, "msa_context_index: n_chunks must be below 2^31");
+  MSA_REQUIRE(int64_t(max_ctx) >= int64_t(k) * max_doc_chunks, MSA_ERR_INVALID_ARG,
+              "msa_context_index: max_ctx < k * max_doc_chunks");
+  MSA_REQUIRE(B <= 65535 && k <= 65535, MSA_ERR_UNSUPPORTED, "msa_context_index: B or k too large");
+  const dim3 grid{unsigned(k), unsigned(B)}, block{GK_THREADS};
+  hipLaunchKernelGGL(gather_kernel<GK_ROWS>, grid, block, 0, as_stream(stream), ids, k, chunk_off, n_docs, nullptr,
+                     nullptr, int64_t(0), max_ctx, nullptr, nullptr, ctx_pos, ctx_len, ctx_row);
+  MSA_LAUNCH_CHECK();
   return MSA_OK;
 }

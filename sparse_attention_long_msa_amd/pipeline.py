@@ -5,6 +5,10 @@ attention on one stream (README, Inference Pipeline: Online Routing & Context
 Assembly, then Sparse Generation; routing happens in every upper-half layer,
 each with its own routing-key store).  ``LayerRunner`` owns the per-layer
 outputs and workspaces so a loop over layers allocates nothing.
+
+With ``indexed=True`` (a device-resident K/V store) the context is not copied:
+assembly writes each context entry's store row and attention reads the rows in
+place; the result is bit-identical to the gathered path.
 """
 from __future__ import annotations
 
@@ -18,7 +22,9 @@ from . import _binding as B
 class LayerRunner:
     def __init__(self, *, batch, tokens, q_heads, kv_heads, head_dim, n_docs, n_chunks, k, max_doc_chunks,
                  local_len, dtype, device, q_pos_offset=None, rope_base=1e6, sm_scale=None,
-                 src_mode=B.MSA_SRC_DEVICE, chunk_off_h=None, kr_layout=B.MSA_LAYOUT_ROWS):
+                 src_mode=B.MSA_SRC_DEVICE, chunk_off_h=None, kr_layout=B.MSA_LAYOUT_ROWS, indexed=False):
+        if indexed and src_mode != B.MSA_SRC_DEVICE:
+            raise ValueError("indexed assembly reads the K/V store in place: it must be in device memory")
         self.B, self.T, self.Hq, self.Hkv, self.d = batch, tokens, q_heads, kv_heads, head_dim
         self.n_docs, self.n_chunks, self.k = n_docs, n_chunks, k
         self.max_doc_chunks = max_doc_chunks
@@ -37,8 +43,14 @@ class LayerRunner:
         self.doc_score = torch.empty((batch, n_docs), dtype=f32, device=dev)
         self.ids = torch.empty((batch, k), dtype=i32, device=dev)
         self.vals = torch.empty((batch, k), dtype=f32, device=dev)
-        self.k_ctx = torch.empty((batch, self.max_ctx, kv_heads, head_dim), dtype=dtype, device=dev)
-        self.v_ctx = torch.empty_like(self.k_ctx)
+        self.indexed = indexed
+        if indexed:
+            self.ctx_row = torch.empty((batch, self.max_ctx), dtype=i32, device=dev)
+            self.k_ctx = self.v_ctx = None
+        else:
+            self.k_ctx = torch.empty((batch, self.max_ctx, kv_heads, head_dim), dtype=dtype, device=dev)
+            self.v_ctx = torch.empty_like(self.k_ctx)
+        self._store = None
         self.ctx_pos = torch.empty((batch, self.max_ctx), dtype=i32, device=dev)
         self.ctx_len = torch.empty((batch,), dtype=i32, device=dev)
         self.out = torch.empty((batch, tokens, q_heads, head_dim), dtype=f32, device=dev)
@@ -69,11 +81,22 @@ class LayerRunner:
         return self.ids, self.vals
 
     def assemble(self, chunk_off, k_bar, v_bar, stream=None):
+        if self.indexed:
+            B.msa_context_index(self.ids, chunk_off, k_bar.shape[0], self.max_doc_chunks, self.max_ctx,
+                                ctx_row=self.ctx_row, ctx_pos=self.ctx_pos, ctx_len=self.ctx_len, stream=stream)
+            self._store = (k_bar, v_bar)
+            return
         B.msa_gather_kv(self.ids, chunk_off, k_bar, v_bar, self.max_doc_chunks, self.max_ctx, self.src_mode,
                         chunk_off_h=self.chunk_off_h, k_ctx=self.k_ctx, v_ctx=self.v_ctx, ctx_pos=self.ctx_pos,
                         ctx_len=self.ctx_len, ids_h=self.ids_h, stream=stream, copy_stream=self.copy_stream)
 
     def attend(self, q, k_loc, v_loc, stream=None):
+        if self.indexed:
+            k_bar, v_bar = self._store
+            B.msa_sparse_attn_indexed(q, k_bar, v_bar, self.ctx_row, self.ctx_pos, self.ctx_len, k_loc, v_loc,
+                                      self.q_pos_offset, self.rope_base, self.sm_scale, out=self.out, ws=self.at_ws,
+                                      rope_table=self.rope_table, stream=stream)
+            return self.out
         B.msa_sparse_attn(q, self.k_ctx, self.v_ctx, self.ctx_pos, self.ctx_len, k_loc, v_loc, self.q_pos_offset,
                           self.rope_base, self.sm_scale, out=self.out, ws=self.at_ws, rope_table=self.rope_table,
                           stream=stream)

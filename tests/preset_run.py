@@ -83,7 +83,7 @@ class HostLayer:
 class GpuLayer:
     """Layer l of preset p built and run on the GPU through the C ABI."""
 
-    def __init__(self, p, l, host: HostLayer, src_mode=M.MSA_SRC_DEVICE):
+    def __init__(self, p, l, host: HostLayer, src_mode=M.MSA_SRC_DEVICE, indexed=False):
         self.p, self.l = p, l
         d0 = dev()
         bf = torch.bfloat16 if p.bf16 else torch.float32
@@ -123,7 +123,8 @@ class GpuLayer:
                                     n_chunks=p.n_chunks, k=p.k, max_doc_chunks=p.max_doc_chunks,
                                     local_len=p.L_loc, dtype=bf, device=d0, q_pos_offset=p.qpo,
                                     rope_base=p.rope_base, src_mode=src_mode, chunk_off_h=co,
-                                    kr_layout=M.MSA_LAYOUT_TILED if p.bf16 else M.MSA_LAYOUT_ROWS)
+                                    kr_layout=M.MSA_LAYOUT_TILED if p.bf16 else M.MSA_LAYOUT_ROWS,
+                                    indexed=indexed)
 
     def run(self):
         r = self.runner

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.msa_abi_version() == 3
+    assert M.msa_abi_version() == 4
     assert M.lib.msa_status_string(0).decode() == "ok"
     assert "workspace" in M.lib.msa_status_string(3).decode()
 
@@ -87,6 +87,31 @@ def test_gather_rejects_small_context_and_bad_mode():
     assert L.msa_gather_kv(1, P, 2, 11, P, None, 10, 8, P, P, 80, 8, 128, 0, 88, P, P, P, P, None, None, None) == 1
     # host-memcpy mode needs the host offsets and the pinned id staging
     assert L.msa_gather_kv(1, P, 2, 4, P, None, 10, 8, P, P, 80, 8, 128, 2, 32, P, P, P, P, None, None, None) == 1
+
+
+def test_context_index_validation():
+    L = M.lib
+    #            ids B  k  chunk_off n_docs maxdc n_chunks max_ctx row pos len stream
+    assert L.msa_context_index(P, 2, 4, P, 10, 8, 80, 31, P, P, P, None) == 1      # max_ctx < k * max_doc_chunks
+    assert L.msa_context_index(P, 2, 11, P, 10, 8, 80, 88, P, P, P, None) == 1     # k > n_docs
+    assert L.msa_context_index(P, 2, 4, P, 10, 8, 80, 32, None, P, P, None) == 1   # NULL ctx_row
+    assert L.msa_context_index(P, 2, 4, P, 10, 8, 1 << 31, 32, P, P, P, None) == 2  # int32 rows
+    assert L.msa_context_index(P, 0, 4, P, 10, 8, 80, 32, P, P, P, None) == 1
+
+
+def test_sparse_attn_indexed_validation():
+    L = M.lib
+
+    def call(n_chunks=80, row=P, Hq=32, q=P, wsb=1 << 30):
+        return L.msa_sparse_attn_indexed(1, q, 1, 4, Hq, 8, 128, P, P, n_chunks, row, P, P, 16, P, P, 8, 4, 1e6,
+                                         None, 0, 0.088, P, P, wsb, None)
+    assert call(row=None) == 1
+    assert call(n_chunks=0) == 1
+    assert call(n_chunks=1 << 31) == 1
+    assert call(Hq=30) == 1
+    assert call(q=None) == 1
+    assert call(wsb=16) == 3
+    assert "msa_sparse_attn_indexed" in L.msa_last_error().decode()
 
 
 def test_sparse_attn_validation():

@@ -156,6 +156,65 @@ def test_gather(bf16, mode):
         np.testing.assert_array_equal(cp[b, :n].cpu().numpy(), rp)
 
 
+@pytest.mark.parametrize("B,k", [(3, 5), (1, 50), (4, 1)])
+def test_context_index(B, k):
+    lens = ragged_lengths(7, 50, 0, 500, n_empty=3)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    r = np.random.default_rng(10 + k)
+    ids = np.stack([r.choice(50, size=k, replace=False) for _ in range(B)]).astype(np.int32)
+    mdc = int(np.diff(chunk_off).max())
+    max_ctx = k * mdc
+    row, pos, ln = M.msa_context_index(torch.from_numpy(ids).to(dev()), co_d, n_chunks, mdc, max_ctx)
+    torch.cuda.synchronize()
+    # the oracle's concatenation of a store whose row c holds the value c gives the rows
+    rowval = np.arange(n_chunks, dtype=np.float64)[:, None, None]
+    for b in range(B):
+        rk, _, rp = O.gather(ids[b], chunk_off, rowval, rowval)
+        n = len(rp)
+        assert int(ln[b]) == n
+        np.testing.assert_array_equal(row[b, :n].cpu().numpy(), rk[:, 0, 0].astype(np.int32))
+        np.testing.assert_array_equal(pos[b, :n].cpu().numpy(), rp)
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("B,T,L_loc,ctx", [(1, 16, 16, [32]), (32, 1, 2048, None), (2, 64, 300, [0, 700]),
+                                           (4, 1, 1, [5, 0, 31, 64]), (1, 128, 200, [1000]),
+                                           (2, 1, 64, [4100, 2500]), (1, 64, 64, [5000])])
+def test_sparse_attention_indexed(bf16, B, T, L_loc, ctx):
+    """Attention reading the context rows in place equals the gathered path
+    bit for bit and the oracle within tolerance."""
+    Hq, Hkv, d, qpo, n_rows = 32, 8, 128, 16, 3000
+    if ctx is None:
+        ctx = list(np.random.default_rng(1).integers(100, 1500, size=B))
+    max_ctx = max(max(ctx), 1)
+    if not bf16 and B * (max_ctx + L_loc) > 200000:
+        pytest.skip("float32 path is the small-case vector path")
+    seed = 70 + T
+    q = gen(seed, 0, synth.T_Q, (B, T, Hq, d), bf16)
+    kl = gen(seed, 0, synth.T_KLOC, (B, L_loc, Hkv, d), bf16)
+    vl = gen(seed, 0, synth.T_VLOC, (B, L_loc, Hkv, d), bf16)
+    kst = gen(seed, 0, synth.T_K, (n_rows, Hkv, d), bf16, scale_pow2=-3)
+    vst = gen(seed, 0, synth.T_V, (n_rows, Hkv, d), bf16, scale_pow2=-3)
+    r = np.random.default_rng(seed)
+    rows = r.integers(0, n_rows, size=(B, max_ctx)).astype(np.int32)
+    cp = r.integers(0, min(128, max_ctx), size=(B, max_ctx)).astype(np.int32)   # positions < max_ctx
+    cl = np.asarray(ctx, dtype=np.int32)
+    d_rows, d_cp, d_cl = (torch.from_numpy(a).to(dev()) for a in (rows, cp, cl))
+    kst_d, vst_d = to_dev(kst, bf16), to_dev(vst, bf16)
+    qd, kld, vld = to_dev(q, bf16), to_dev(kl, bf16), to_dev(vl, bf16)
+    got = M.msa_sparse_attn_indexed(qd, kst_d, vst_d, d_rows, d_cp, d_cl, kld, vld, qpo)
+    gathered = M.msa_sparse_attn(qd, kst_d[d_rows.long()].contiguous(), vst_d[d_rows.long()].contiguous(), d_cp,
+                                 d_cl, kld, vld, qpo)
+    assert torch.equal(got, gathered)
+    sm = 1.0 / math.sqrt(d)
+    g = host(got)
+    for b in (range(B) if B <= 4 else [0, 17, 31]):
+        n = int(cl[b])
+        ref = O.attend_one(q[b], kst[rows[b, :n]], vst[rows[b, :n]], cp[b, :n], kl[b], vl[b], qpo, 1e6, sm)
+        e = np.abs(g[b] - ref).max()
+        assert e <= ATOL_ATTN["bf16" if bf16 else "f32"], f"b={b}: max-abs {e}"
+
+
 def _attn_case(seed, B, T, Hq, Hkv, d, L_loc, ctx_lens, bf16, max_ctx):
     q = gen(seed, 0, synth.T_Q, (B, T, Hq, d), bf16)
     kl = gen(seed, 0, synth.T_KLOC, (B, L_loc, Hkv, d), bf16)
