@@ -45,8 +45,11 @@ __global__ void rope_table_kernel(float2* __restrict__ tab, int P, int half, dou
   tab[i] = make_float2(float(cs), float(sn));
 }
 
+// two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ void unpack8(const uint4& u, float (&x)[8]) {
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
       for (int rho = 0; rho < 2; ++rho)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          R.v[rho][i] = *reinterpret_cast<const uint4*>(vb + int32_t(16 * rho + 4 * g4 + i) * int32_t(kv_stride));
+          R.v[rho][i] = load_stream(vb + int32_t(16 * rho + 4 * g4 + i) * int32_t(kv_stride));
       const float2* trow = tab + int64_t(qpo + j0 - ctxl) * (AT_D / 2);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
       for (int i = 0; i < 4; ++i) {
         const KeySrc ks = key_src(j0 + 16 * rho + 4 * g4 + i, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
         const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(gg) * AT_D + 8 * lc;
-        R.v[rho][i] = *reinterpret_cast<const uint4*>(vp);
+        R.v[rho][i] = load_stream(vp);
       }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -409,8 +412,10 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
       }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    if (__ballot(alpha != 1.f)) {   // skip the rescale when no row's running max moved
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
     const bf16x8 pb = __builtin_bit_cast(
         bf16x8, make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                            pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])));
@@ -536,7 +541,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     {
       const KeySrc ks = key_src(j0 + lk, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
       const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 8 * lx;
-      R.v = *reinterpret_cast<const uint4*>(vp);
+      R.v = load_stream(vp);
     }
   };
   auto store_step = [&](const PfRegs& R, unsigned char* buf) {
@@ -622,8 +627,10 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
         }
       l_run[i] = l_run[i] * alpha + psum;
       m_run[i] = m_new;
+      if (__ballot(alpha != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
+        for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
+      }
       pb[i] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                                                     pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])));
     }
