@@ -132,7 +132,7 @@ __device__ __forceinline__ int64_t ctx_src_row(int64_t e, const int32_t* __restr
 
 // A workgroup's context entries [lo, lo + n) as (store row, clamped
 // position), staged in LDS once so that no step waits on an index load.
-constexpr int AT_CIDX = 2048;
+constexpr int AT_CIDX = 1024;
 constexpr int AT_CIDX_BYTES = AT_CIDX * 8;
 struct CtxCache {
   const int2* e;
@@ -160,51 +160,62 @@ __device__ __forceinline__ KeySrc key_src(int j, int b, int ctxl, int n_keys, in
                                           const int32_t* __restrict__ ctx_pos, int P,
                                           const int32_t* __restrict__ ctx_row, int64_t ctx_rows,
                                           const CtxCache& cc) {
+  // Branch-free (selects only), so the loads that follow stay straight-line
+  // code.  Every context key of the workgroup's range is cached (the host
+  // sizes the splits for it); the cache read is clamped into the cache and
+  // its value is used only for such keys.  Keys past the range end or past
+  // n_keys are masked by the caller: any in-bounds row will do.
+  (void)ctx_pos;
+  (void)P;
+  (void)ctx_rows;
+  const int i = j - cc.lo;
+  const bool in = i >= 0 && i < cc.n;
+  const int2 e = cc.e[min(max(i, 0), AT_CIDX - 1)];
+  const bool is_ctx = j < ctxl;
+  const int li = min(max(j - ctxl, 0), L_loc - 1);
+  const int64_t crow = ctx_row ? int64_t(in ? e.x : 0) : int64_t(b) * max_ctx + (in ? j : 0);
   KeySrc k;
-  if (j < ctxl) {
-    // every context key of the workgroup's range is cached (the host sizes the
-    // splits for it); keys past the range end are masked, any row will do
-    const int i = j - cc.lo;
-    const bool in = i >= 0 && i < cc.n;
-    const int2 v = in ? cc.e[i] : make_int2(0, 0);
-    k.row = ctx_row ? int64_t(v.x) : int64_t(b) * max_ctx + (in ? j : 0);
-    k.pos = v.y;
-    k.local = false;
-    k.valid = true;
-  } else if (j < n_keys) {
-    const int li = j - ctxl;
-    k.row = int64_t(b) * L_loc + li;
-    k.pos = qpo + li;
-    k.local = true;
-    k.valid = true;
-  } else {
-    k.row = int64_t(b) * L_loc;  // any finite row; its weight is zero
-    k.pos = 0;
-    k.local = true;
-    k.valid = false;
-  }
+  k.row = is_ctx ? crow : int64_t(b) * L_loc + li;
+  k.pos = is_ctx ? (in ? e.y : 0) : qpo + li;
+  k.local = !is_ctx;
+  k.valid = j < n_keys;
   return k;
 }
 
 // ---------------------------------------------------------------- decode (one row tile)
-// One workgroup per (query b, key split, group of up to 8 KV heads); wave w
-// owns KV head g = 8 * hg + w and the (at most 16) query rows of that head.
+// One workgroup per (query b, key split, group of up to 4 KV heads); wave w
+// owns KV head g = 4 * hg + w and the (at most 16) query rows of that head.
 // The RoPE rows of the step's 32 keys are the same for every head, so the
 // workgroup stages them once in LDS; each wave streams its own head's K and
 // V.  The next step's K, V and RoPE rows are loaded while the current step
-// is computed.
+// is computed.  Four waves per workgroup (two workgroups per CU) keep the
+// per-step barrier that publishes the shared rows to a small group.
 
 constexpr int DC_TAB_STRIDE = 528;                 // bytes per key row of (cos, sin) in LDS (512 + pad)
 constexpr int DC_TAB_BYTES = 32 * DC_TAB_STRIDE;
 
+constexpr int DC_WAVES = 4;                        // KV heads (waves) per workgroup; two workgroups per CU
+constexpr int DC_THREADS = 64 * DC_WAVES;
+constexpr int DC_TAB_PT = 32 * 32 / DC_THREADS;    // RoPE-row pieces staged per thread
+static_assert(DC_TAB_PT * DC_THREADS == 32 * 32, "the threads cover the step's RoPE rows");
+
 struct DcRegs {
   uint4 k[2][4];     // K rows (two 16-key tiles) of this wave's head
+};
+struct VRegs {
   uint4 v[2][4];     // V rows: key 16*rho + 4*g4 + i, dims 8*lc .. +7
-  uint4 t[2];        // this thread's share of the step's RoPE rows
+};
+struct TabRegs {
+  uint4 t[DC_TAB_PT];   // this thread's pieces of the step's RoPE rows
 };
 
+// This wave's LDS operations are complete, then the workgroup barrier; unlike
+// __syncthreads() it does not wait for outstanding vector-memory loads.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+
 template <int G, bool IDX>
-__global__ __launch_bounds__(512) void attn_decode_kernel(
+__global__ __launch_bounds__(DC_THREADS, 2) void attn_decode_kernel(
     const uint16_t* __restrict__ q, int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_ctx,
     const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
@@ -223,7 +234,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
   wg /= n_splits;
   const int hg = int(wg % n_hg);
   const int b = int(wg / n_hg);
-  const int g = hg * 8 + wave;
+  const int g = hg * DC_WAVES + wave;
   const bool head_ok = g < Hkv;
   const int gg = head_ok ? g : 0;
   const int64_t kv_stride = int64_t(Hkv) * AT_D;
@@ -261,74 +272,81 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
   const CtxCache cc = stage_ctx(reinterpret_cast<int2*>(smem + 2 * DC_TAB_BYTES + size_t(nw) * AT_V_BYTES), b, j_begin,
                                 j_end, ctxl, max_ctx, ctx_pos, P, ctx_row, ctx_rows, tid, nthr);
   __syncthreads();
+  // Addresses are formed under the (uniform) all-local test, the loads come
+  // after it: every path issues the same loads, so the compiler's waits on
+  // the load counter stay partial.
   auto load_k = [&](int j0, DcRegs& R) {
+    const uint16_t* kp[2];
     if (all_local(j0)) {
       const uint16_t* kb = k_loc + (int64_t(b) * L_loc + (j0 - ctxl)) * kv_stride + int64_t(gg) * AT_D + 8 * g4;
 #pragma unroll
+      for (int tau = 0; tau < 2; ++tau) kp[tau] = kb + int32_t(16 * tau + lc) * int32_t(kv_stride);
+    } else {
+#pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        const uint16_t* kp = kb + int32_t(16 * tau + lc) * int32_t(kv_stride);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) R.k[tau][kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
+        const KeySrc ks = key_src(j0 + 16 * tau + lc, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
+        kp[tau] = (ks.local ? k_loc : k_ctx) + ks.row * kv_stride + int64_t(gg) * AT_D + 8 * g4;
       }
-      return;
     }
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const KeySrc ks = key_src(j0 + 16 * tau + lc, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
-      const uint16_t* kp = (ks.local ? k_loc : k_ctx) + ks.row * kv_stride + int64_t(gg) * AT_D + 8 * g4;
+    for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) R.k[tau][kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
-    }
+      for (int kk = 0; kk < 4; ++kk) R.k[tau][kk] = load_global(kp[tau] + 32 * kk);
   };
-  auto load_vt = [&](int j0, DcRegs& R) {
+  auto load_v = [&](int j0) {
+    const uint16_t* vp[2][4];
     if (all_local(j0)) {
       const uint16_t* vb = v_loc + (int64_t(b) * L_loc + (j0 - ctxl)) * kv_stride + int64_t(gg) * AT_D + 8 * lc;
 #pragma unroll
       for (int rho = 0; rho < 2; ++rho)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          R.v[rho][i] = load_stream(vb + int32_t(16 * rho + 4 * g4 + i) * int32_t(kv_stride));
-      const float2* trow = tab + int64_t(qpo + j0 - ctxl) * (AT_D / 2);
+        for (int i = 0; i < 4; ++i) vp[rho][i] = vb + int32_t(16 * rho + 4 * g4 + i) * int32_t(kv_stride);
+    } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int piece = tid + u * nthr;     // 16-byte pieces: 32 rows x 32 pieces
-        if (piece < 32 * 32) R.t[u] = reinterpret_cast<const uint4*>(trow + (piece / 32) * (AT_D / 2))[piece % 32];
-      }
-      return;
+      for (int rho = 0; rho < 2; ++rho)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const KeySrc ks = key_src(j0 + 16 * rho + 4 * g4 + i, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P,
+                                    ctx_row, ctx_rows, cc);
+          vp[rho][i] = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(gg) * AT_D + 8 * lc;
+        }
     }
+    VRegs v;
 #pragma unroll
     for (int rho = 0; rho < 2; ++rho)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const KeySrc ks = key_src(j0 + 16 * rho + 4 * g4 + i, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
-        const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(gg) * AT_D + 8 * lc;
-        R.v[rho][i] = load_stream(vp);
-      }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int piece = tid + u * nthr;
-      if (piece < 32 * 32) {
-        const int key = piece / 32, off = piece % 32;
-        const KeySrc ks = key_src(j0 + key, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
-        R.t[u] = reinterpret_cast<const uint4*>(tab + int64_t(ks.pos) * (AT_D / 2))[off];
-      }
-    }
+      for (int i = 0; i < 4; ++i) v.v[rho][i] = load_stream(vp[rho][i]);
+    return v;
   };
-  auto store_tab = [&](const DcRegs& R, unsigned char* buf) {
+  // The step's 32 RoPE rows (32 x 32 pieces of 16 bytes), DC_TAB_PT pieces per
+  // thread, through registers into a padded LDS buffer
+  auto load_tab = [&](int j0) {
+    TabRegs t;
+    const bool loc = all_local(j0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int piece = tid + u * nthr;
-      if (piece < 32 * 32)
-        *reinterpret_cast<uint4*>(buf + (piece / 32) * DC_TAB_STRIDE + (piece % 32) * 16) = R.t[u];
+    for (int u = 0; u < DC_TAB_PT; ++u) {
+      const int piece = tid + u * DC_THREADS;
+      const int key = piece / 32;
+      const int pos = loc ? qpo + j0 - ctxl + key
+                          : key_src(j0 + key, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc).pos;
+      t.t[u] = reinterpret_cast<const uint4*>(tab + int64_t(pos) * (AT_D / 2))[piece % 32];
+    }
+    return t;
+  };
+  auto store_tab = [&](const TabRegs& t, unsigned char* buf) {
+#pragma unroll
+    for (int u = 0; u < DC_TAB_PT; ++u) {
+      const int piece = tid + u * DC_THREADS;
+      *reinterpret_cast<uint4*>(buf + (piece / 32) * DC_TAB_STRIDE + (piece % 32) * 16) = t.t[u];
     }
   };
   // V rows stay row-major in LDS; the PV operand is read with transpose loads
-  auto store_v = [&](const DcRegs& R) {
+  auto store_v = [&](const VRegs& v) {
 #pragma unroll
     for (int rho = 0; rho < 2; ++rho)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(vrm + (16 * rho + 4 * g4 + i) * AT_VS + 16 * lc) = R.v[rho][i];
+        *reinterpret_cast<uint4*>(vrm + (16 * rho + 4 * g4 + i) * AT_VS + 16 * lc) = v.v[rho][i];
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -336,27 +354,29 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Pipeline: K of step s+1 is requested before the S^T of step s; V and the
-  // RoPE rows of step s+1 right after it.  V of step s+1 and its RoPE rows
-  // are written to LDS at the end of step s, so only K waits in registers.
-  DcRegs cur, nxt;
+  // Pipeline (per wave; the vector-memory counter completes loads in issue
+  // order): at the top of step s, K(s) is in flight to registers and V(s),
+  // RoPE(s) are in LDS.  Step s first requests RoPE(s+1) and V(s+1) into
+  // registers, then computes S^T(s), then requests K(s+1) into the registers
+  // K(s) just freed, then finishes step s and writes RoPE(s+1) (other LDS
+  // buffer) and V(s+1) to LDS.  The closing barrier waits only for LDS
+  // traffic, so K(s+1) stays in flight across it and the memory pipe never
+  // drains.
+  DcRegs R;
   if (j_begin < j_end) {
-    load_k(j_begin, cur);
-    load_vt(j_begin, cur);
-    store_tab(cur, tabs);
-    store_v(cur);
+    const TabRegs t0 = load_tab(j_begin);
+    const VRegs v0 = load_v(j_begin);
+    load_k(j_begin, R);
+    store_tab(t0, tabs);
+    store_v(v0);
   }
-  __syncthreads();
-  int tb = 0;
-  for (int j0 = j_begin; j0 < j_end; j0 += 32) {
-    const bool has_next = j0 + 32 < j_end;
-    if (has_next) load_k(j0 + 32, nxt);
-    const unsigned char* tbuf = tabs + tb * DC_TAB_BYTES;
+  lds_barrier();
+  // S^T of the step at j0 from K(s) in registers and RoPE(s) in tbuf
+  auto score = [&](const unsigned char* tbuf, f32x4 (&s)[2]) {
     // ---- rotate K with the staged RoPE rows, S^T = K_rot . Q_rot^T
-    f32x4 s[2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      uint4 kv[4] = {cur.k[tau][0], cur.k[tau][1], cur.k[tau][2], cur.k[tau][3]};
+      uint4 kv[4] = {R.k[tau][0], R.k[tau][1], R.k[tau][2], R.k[tau][3]};
       const unsigned char* row = tbuf + (16 * tau + lc) * DC_TAB_STRIDE;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -382,8 +402,9 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv[kk]), bq[kk], acc, 0, 0, 0);
       s[tau] = acc;
     }
-    __builtin_amdgcn_sched_barrier(0);   // keep the next V / RoPE loads after this step's S^T
-    if (has_next) load_vt(j0 + 32, nxt);
+  };
+  // mask, online softmax and O^T += V^T . P^T of the step at j0
+  auto finish = [&](int j0, const f32x4 (&s)[2]) {
     // ---- mask and online softmax for column lc (base-2 domain)
     float x[2][4];
     float mt = -INFINITY;
@@ -423,18 +444,32 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pv_operand(vrm, dt, lane), pb, o[dt], 0, 0, 0);
-    if (has_next) {
-      // LDS operations of one wave complete in order, so this step's V reads
-      // above precede the next step's writes to the same buffer
-      store_v(nxt);
-      store_tab(nxt, tabs + (tb ^ 1) * DC_TAB_BYTES);
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) cur.k[tau][kk] = nxt.k[tau][kk];
-    }
-    __syncthreads();
+  };
+
+  int tb = 0;
+  int j0 = j_begin;
+  // steps with a successor prefetch it unconditionally (straight-line code
+  // keeps the compiler's load-counter waits partial); the last step is peeled
+  for (; j0 + 32 < j_end; j0 += 32) {
+    const TabRegs tn = load_tab(j0 + 32);
+    const VRegs vn = load_v(j0 + 32);
+    f32x4 s[2];
+    score(tabs + tb * DC_TAB_BYTES, s);
+    __builtin_amdgcn_sched_barrier(0);   // K(s) is consumed: its registers take K(s+1)
+    load_k(j0 + 32, R);
+    finish(j0, s);
+    // LDS operations of one wave complete in order, so this step's V reads
+    // precede the next step's writes to the same buffer; the other RoPE
+    // buffer was last read in step s-1, before its closing barrier
+    store_tab(tn, tabs + (tb ^ 1) * DC_TAB_BYTES);
+    store_v(vn);
+    lds_barrier();
     tb ^= 1;
+  }
+  if (j0 < j_end) {
+    f32x4 s[2];
+    score(tabs + tb * DC_TAB_BYTES, s);
+    finish(j0, s);
   }
 
   // ---- partial result of this split: O^T[d = 16dt + 4*g4 + i][row lc]
@@ -839,9 +874,9 @@ static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int m
     units = int64_t(B) * Hkv * p.n_rg;      // workgroups per split
     target = 256;                            // about one workgroup per CU
   } else {
-    p.n_hg = (Hkv + 7) / 8;
+    p.n_hg = (Hkv + DC_WAVES - 1) / DC_WAVES;
     units = int64_t(B) * p.n_hg;            // workgroups per split
-    target = 512;                            // two rounds of one 8-wave workgroup per CU
+    target = 1024;                           // two rounds of two 4-wave workgroups per CU
   }
   // the kernels split each query's actual keys evenly over n_splits; a split's
   // context entries must fit the workgroup's LDS index cache
@@ -964,8 +999,8 @@ static int sparse_attn(const std::string& fn, int dtype, const void* q, int B, i
       MSA_LAUNCH_CHECK();
       return MSA_OK;
     }
-    const int nw = 8;   // waves beyond Hkv only help stage the RoPE rows
-    const dim3 grid(unsigned(int64_t(B) * p.n_hg * p.n_splits)), block(unsigned(64 * nw));
+    const int nw = DC_WAVES;   // waves beyond Hkv only help stage the RoPE rows
+    const dim3 grid{unsigned(int64_t(B) * p.n_hg * p.n_splits)}, block{unsigned(DC_THREADS)};
     const size_t smem = 2 * size_t(DC_TAB_BYTES) + size_t(nw) * AT_V_BYTES + AT_CIDX_BYTES;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
 #define DC_LAUNCH2(GV, IV)                                                                                         \

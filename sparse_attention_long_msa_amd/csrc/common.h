@@ -73,6 +73,15 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16-byte load from global memory, stated as such: a pointer chosen among
+// several at run time would otherwise be read with a flat load, which also
+// counts against the LDS counter.
+__device__ __forceinline__ uint4 load_global(const void* p) {
+  typedef const __attribute__((address_space(1))) u32x4* gptr;
+  const u32x4 v = *(gptr)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int DT> struct Elem;
 template <> struct Elem<MSA_F32> {
   using T = float;
