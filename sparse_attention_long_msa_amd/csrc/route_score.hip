@@ -25,7 +25,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int RS_WAVES = 8;
 constexpr int RS_THREADS = 64 * RS_WAVES;
 constexpr int RS_MT = 2;                 // 16-chunk row tiles per wave tile
-constexpr int RS_TILE = 16 * RS_MT;      // chunks per wave tile
 constexpr int RS_D = 128;                // head dim of the MFMA path
 constexpr int RS_H = 8;                  // heads of the MFMA path
 constexpr int RS_KK = RS_D / 32;         // k-steps of 32 per head
@@ -93,7 +92,9 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
 
   const int g4 = lane / 16;       // lane group: k-slice of the operands, row block of the result
   const int lc = lane % 16;       // column (query token) of this lane inside a 16-column tile
-  const int64_t tiles_total = (n_chunks + RS_TILE - 1) / RS_TILE;
+  constexpr int MT = RS_MT;
+  constexpr int TILE = 16 * MT;   // chunks per wave tile
+  const int64_t tiles_total = (n_chunks + TILE - 1) / TILE;
   const int64_t t_begin = int64_t(range) * tiles_per_range;
   int64_t t_end = t_begin + tiles_per_range;
   if (t_end > tiles_total) t_end = tiles_total;
@@ -104,18 +105,18 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
   // 32*kk + 8*g4 .. +8 of the head.  Row-major stores give four lanes 64
   // contiguous bytes per load; the tiled layout gives the wave 1 KB.
   const int64_t n_cgroups = (n_chunks + 15) / 16;   // 16-chunk groups of the tiled layout
-  auto load_head = [&](int64_t tl, int h, uint4 (&dst)[RS_MT][RS_KK]) {
+  auto load_head = [&](int64_t tl, int h, uint4 (&dst)[MT][RS_KK]) {
 #pragma unroll
-    for (int m = 0; m < RS_MT; ++m) {
+    for (int m = 0; m < MT; ++m) {
       if constexpr (TILED) {
         // 16-chunk group: one wave instruction reads 1 KB contiguous (lane-ordered)
-        int64_t grp = tl * RS_MT + m;
+        int64_t grp = tl * MT + m;
         if (grp >= n_cgroups) grp = n_cgroups - 1;
         const uint16_t* p = kr + grp * (16 * rowE) + int64_t(h) * (16 * RS_D) + 8 * lane;
 #pragma unroll
         for (int kk = 0; kk < RS_KK; ++kk) dst[m][kk] = load_stream(p + kk * 512);   // read once
       } else {
-        int64_t c = tl * RS_TILE + 16 * m + lc;
+        int64_t c = tl * TILE + 16 * m + lc;
         if (c >= n_chunks) c = n_chunks - 1;
         const uint4* p = reinterpret_cast<const uint4*>(kr + c * rowE + int64_t(h) * RS_D + 8 * g4);
 #pragma unroll
@@ -124,9 +125,15 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     }
   };
 
-  // the first head of the first tile is in flight while the queries are staged
-  uint4 bufA[RS_MT][RS_KK], bufB[RS_MT][RS_KK];
-  if (tile < t_end) load_head(tile, 0, bufA);
+  // a ring of D head loads is in flight per wave; the first tile's first D
+  // heads load while the queries are staged
+  constexpr int D = 2;
+  static_assert(H % D == 0, "the head ring divides the heads");
+  uint4 buf[D][MT][RS_KK];
+  if (tile < t_end) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_head(tile, d, buf[d]);
+  }
 
   // ---- stage the raw routing queries of this column group in fragment order
   const int nfrag_pieces = NT * H * RS_KK * 64;
@@ -142,24 +149,25 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
 
   // ---- column scale w[h][n][lc] = 1 / (H * max(||q[col,h]||, eps)), kept in LDS
   float* wl = reinterpret_cast<float*>(smem + size_t(NT) * H * RS_KK * 1024 + size_t(RS_WAVES) * RS_SCRATCH);
-  if (wave == 0) {
-    for (int n = 0; n < NT; ++n)
-      for (int h = 0; h < H; ++h) {
-        float ss = 0.f;
+  static_assert(RS_WAVES == H, "one wave per head computes the column norms");
+  {
+    const int h = wave;
+    for (int n = 0; n < NT; ++n) {
+      float ss = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < RS_KK; ++kk) {
-          const uint4 u = qfrag[((n * H + h) * RS_KK + kk) * 64 + lane];
-          const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+      for (int kk = 0; kk < RS_KK; ++kk) {
+        const uint4 u = qfrag[((n * H + h) * RS_KK + kk) * 64 + lane];
+        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a = __uint_as_float(uu[e] << 16), b = __uint_as_float(uu[e] & 0xFFFF0000u);
-            ss += a * a + b * b;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float a = __uint_as_float(uu[e] << 16), b = __uint_as_float(uu[e] & 0xFFFF0000u);
+          ss += a * a + b * b;
         }
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        if (g4 == 0) wl[(h * NT + n) * 16 + lc] = 1.f / (float(H) * fmaxf(sqrtf(ss), 1e-8f));
       }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      if (g4 == 0) wl[(h * NT + n) * 16 + lc] = 1.f / (float(H) * fmaxf(sqrtf(ss), 1e-8f));
+    }
   }
   __syncthreads();
 
@@ -171,16 +179,16 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     colb[n] = col < J ? col / T : -1;
   }
 
-  f32x4 tot[RS_MT][NT];
-  auto head_step = [&](const uint4 (&a)[RS_MT][RS_KK], int h) {
-    f32x4 acc[RS_MT][NT];
+  f32x4 tot[MT][NT];
+  auto head_step = [&](const uint4 (&a)[MT][RS_KK], int h) {
+    f32x4 acc[MT][NT];
 #pragma unroll
     for (int kk = 0; kk < RS_KK; ++kk) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const bf16x8 bq = as_bf16x8(qfrag[((n * H + h) * RS_KK + kk) * 64 + lane]);
 #pragma unroll
-        for (int m = 0; m < RS_MT; ++m) {
+        for (int m = 0; m < MT; ++m) {
           const f32x4 cin = kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[m][n];
           acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[m][kk]), bq, cin, 0, 0, 0);
         }
@@ -190,27 +198,31 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     for (int n = 0; n < NT; ++n) {
       const float wv = wl[(h * NT + n) * 16 + lc];
 #pragma unroll
-      for (int m = 0; m < RS_MT; ++m) tot[m][n] += wv * acc[m][n];
+      for (int m = 0; m < MT; ++m) tot[m][n] += wv * acc[m][n];
     }
   };
 
   if (tile >= t_end) return;
   for (;;) {
-    const int mydoc = (lane < 32 && tile * RS_TILE + lane < n_chunks) ? chunk_doc[tile * RS_TILE + lane] : -1;
+    const int mydoc = (lane < TILE && tile * TILE + lane < n_chunks) ? chunk_doc[tile * TILE + lane] : -1;
 #pragma unroll
-    for (int m = 0; m < RS_MT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int n = 0; n < NT; ++n) tot[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t next_tile = tile + RS_WAVES;
+    // past the wave's last tile the ring refills from tile 0 (read by every
+    // wave, so cached; never used): the loop stays straight-line code and the
+    // compiler's waits on the load counter stay partial
+    const int64_t pref_tile = next_tile < t_end ? next_tile : 0;
 #pragma unroll 1
-    for (int h = 0; h < H; h += 2) {
-      load_head(tile, h + 1, bufB);
-      head_step(bufA, h);
-      if (h + 2 < H)
-        load_head(tile, h + 2, bufA);
-      else if (next_tile < t_end)
-        load_head(next_tile, 0, bufA);
-      head_step(bufB, h + 1);
+    for (int h0 = 0; h0 < H; h0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int h = h0 + d, hn = h + D;
+        head_step(buf[d], h);
+        load_head(hn < H ? tile : pref_tile, hn < H ? hn : hn - H, buf[d]);
+        __builtin_amdgcn_sched_barrier(0);   // refill issued right after its head, not sunk below the ring
+      }
     }
     // ---- epilogue: lane (lc, g4) holds score[chunk 16m + 4*g4 + r][column 16n + lc]
     if constexpr (UNIFORM_B) {
@@ -223,9 +235,9 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
 #pragma unroll
         for (int n1 = 0; n1 < n0; ++n1) first = first && (colb[n1] != b);
         if (!first) continue;
-        float v[RS_MT][4];
+        float v[MT][4];
 #pragma unroll
-        for (int m = 0; m < RS_MT; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float x = -INFINITY;
@@ -236,13 +248,13 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
           }
         if (lc == 0) {
 #pragma unroll
-          for (int m = 0; m < RS_MT; ++m)
+          for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int r = 0; r < 4; ++r) scratch[16 * m + 4 * g4 + r] = v[m][r];
         }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        const float cv = lane < 32 ? scratch[lane] : -INFINITY;
+        const float cv = lane < TILE ? scratch[lane] : -INFINITY;
         seg_max_emit(cv, mydoc, lane, doc_score + int64_t(b) * n_docs, n_docs);
         __builtin_amdgcn_wave_barrier();
       }
@@ -253,7 +265,7 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
 #pragma unroll
-        for (int m = 0; m < RS_MT; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
           for (int r = 0; r < 4; ++r) scratch[lc * 33 + 16 * m + 4 * g4 + r] = tot[m][n][r];
         __builtin_amdgcn_wave_barrier();
@@ -263,8 +275,8 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
           float* row = doc_score + int64_t(b) * n_docs;
           float run = -INFINITY;
           int run_doc = -1;
-          for (int i = 0; i < 8; ++i) {
-            const int rr = 8 * g4 + i;
+          for (int i = 0; i < TILE / 4; ++i) {
+            const int rr = (TILE / 4) * g4 + i;
             const int dd = sdoc[rr];
             const float x = scratch[lc * 33 + rr];
             if (dd != run_doc) {
@@ -366,11 +378,11 @@ extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, 
     const int n_groups = (J + 63) / 64;
     const int NT = std::min(4, (J + 15) / 16);
     const bool uniform = (T % 16) == 0;
-    const int64_t tiles_total = (n_chunks + RS_TILE - 1) / RS_TILE;
     int dev = 0;
     MSA_HIP_CHECK(hipGetDevice(&dev));
     int n_cu = 0;
     MSA_HIP_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+    const int64_t tiles_total = (n_chunks + 16 * RS_MT - 1) / (16 * RS_MT);
     int64_t n_ranges = std::min<int64_t>(n_cu, (tiles_total + RS_WAVES - 1) / RS_WAVES);
     if (n_groups > 1) n_ranges = (n_ranges + 7) / 8 * 8;
     const int64_t tiles_per_range = (tiles_total + n_ranges - 1) / n_ranges;
