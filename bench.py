@@ -37,7 +37,9 @@ def parse():
                     help="HBM tier: attention reads the selected rows in place (index) or from a gathered copy")
     ap.add_argument("--layers", type=int, default=None, help="override the routed-layer count (profiling only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-chunks", type=int, default=262144)
+    ap.add_argument("--cpu-sample-chunks", type=int, default=None,
+                    help="routing-key chunks of the oracle's sample (default: 1048576 at pooled level, "
+                         "262144 for token-level memories, whose sample the oracle also pools)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (the reference for the HBM byte counters)")
     return ap.parse_args()
@@ -259,7 +261,7 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(p, args.cpu_sample_chunks)
+        res["cpu_baseline"] = cpu_baseline(p, layers, args.cpu_sample_chunks)
     print(json.dumps(res), flush=True)
 
 
@@ -302,38 +304,76 @@ def copy_calibration(torch):
     print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
-def cpu_baseline(p, n_sample_chunks):
-    """The float64 oracle's routing (score + top-k) on a bounded sample of the
-    same workload: layer 0, the first documents of the memory."""
+def cpu_baseline(p, layers, n_sample_chunks=None):
+    """The float64 oracle's routing (score + top-k) timed on a bounded sample
+    of the same workload: every routed layer's query scored against the
+    routing keys of layer 0's first documents.  The sample's keys come from
+    the seeded generator (its device copy, bit-identical to the host one) and
+    are pooled and normalised by the oracle before the timed region."""
+    import torch
+
     import oracle as O
     import synth
+    from synth import device as SD
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    if n_sample_chunks is None:
+        n_sample_chunks = 1 << 20 if p.pooled_level else 1 << 18
     n_docs = int(np.searchsorted(p.chunk_off, n_sample_chunks, side="right") - 1)
     n_docs = max(1, min(n_docs, p.n_docs))
     co = p.chunk_off[: n_docs + 1]
     n = int(co[-1])
-    qr = synth.tensor(p.qseed, 0, synth.T_QR, (p.B, p.T, p.H, p.d), bf16=p.bf16)
+    dt_name = "bf16" if p.bf16 else "f32"
+    t_prep = time.perf_counter()
+    blk = 1 << 17
+    buf = torch.empty((blk, p.H, p.d), dtype=torch.bfloat16 if p.bf16 else torch.float32, device="cuda")
+
+    def gen_rows(r0, r1):
+        """rows r0 .. r1-1 of layer 0's raw routing keys (float64, host)"""
+        out = np.empty((r1 - r0, p.H, p.d), dtype=np.float64)
+        for a in range(r0, r1, blk):
+            b = min(r1, a + blk)
+            SD.fill(buf[: b - a], p.seed, 0, synth.T_KR, start=a * p.H * p.d)
+            out[a - r0:b - r0] = buf[: b - a].float().cpu().numpy()
+        return out
+
     if p.pooled_level:
-        rows, to, chunk = n, co, 1
+        # chunk = 1: pooling is the identity, the store is the normalised, rounded
+        # keys (the oracle's pool_encode, checked here on a slice, without its
+        # per-chunk loop)
+        raw = gen_rows(0, n)
+        store = O.round_to_store(O.l2_normalize(raw), dt_name)
+        assert np.array_equal(store[:256], O.pool_encode(raw[:256], np.arange(257), 1, True, dt_name))
+        del raw
     else:
-        rows, to, chunk = int(p.tok_off[n_docs]), p.tok_off[: n_docs + 1], p.chunk
-    raw = synth.normal(p.seed, synth.stream_id(0, synth.T_KR), 0, rows * p.H * p.d, bf16=p.bf16)
-    raw = raw.reshape(rows, p.H, p.d)
-    store = O.pool_encode(raw, to, chunk, True, "bf16" if p.bf16 else "f32")   # offline stage, untimed
-    del raw
+        # the oracle pools the tokens of a few documents at a time
+        parts, d0 = [], 0
+        while d0 < n_docs:
+            d1 = int(np.searchsorted(p.tok_off, p.tok_off[d0] + (1 << 20), side="right") - 1)
+            d1 = min(n_docs, max(d0 + 1, d1))
+            t0_, t1_ = int(p.tok_off[d0]), int(p.tok_off[d1])
+            parts.append(O.pool_encode(gen_rows(t0_, t1_), p.tok_off[d0:d1 + 1] - t0_, p.chunk, True, dt_name))
+            d0 = d1
+        store = np.concatenate(parts)
+        assert store.shape[0] == n
+    del buf
+    queries = [synth.tensor(p.qseed, l, synth.T_QR, (p.B, p.T, p.H, p.d), bf16=p.bf16) for l in range(layers)]
+    t_prep = time.perf_counter() - t_prep
     t0 = time.perf_counter()
-    s = O.route_scores(qr, store, co)
-    O.topk(s, p.k)
+    for qr in queries:
+        s = O.route_scores(qr, store, co)
+        O.topk(s, p.k)
     dt = time.perf_counter() - t0
-    gb = n * p.H * p.d * (2 if p.bf16 else 4) / 1e9
+    gb = layers * n * p.H * p.d * (2 if p.bf16 else 4) / 1e9
+    log(f"cpu baseline: sample prepared in {t_prep:.1f} s, oracle routing {dt:.1f} s")
     return {"value": round(gb / dt, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"layer 0, first {n_docs} documents ({n} pooled chunks, {gb:.2f} GB of routing keys), "
-                      f"routing score + top-k for {p.B} x {p.T}-token queries, float64"}
+            "sample": f"layer 0, first {n_docs} documents ({n} pooled chunks, "
+                      f"{n * p.H * p.d * (2 if p.bf16 else 4) / 1e9:.2f} GB of routing keys) scored against each of the "
+                      f"{layers} routed layers' {p.B} x {p.T}-token queries: routing score + top-k, float64"}
 
 
 if __name__ == "__main__":
