@@ -9,6 +9,13 @@ bf16; the routing-key store is 57.6 GB in HBM), query of 64 tokens, 32 query
 heads, 4,096 local tokens, k = 16.  Inputs are seeded synthetic data
 generated on the device before the timed region.
 
+Timing: the K timed steps are measured by the wall clock between two device
+synchronisations; inside them only one pair of HIP events per step brackets a
+routing-score launch (the roofline's launch duration).  The per-stage
+breakdown comes from up to 3 further steps with events between all stages
+(each event record idles the device for a few microseconds, so these steps
+are not part of the timed region).
+
 Prints one JSON line.  --gpus above 1 is not supported (one GPU per process,
 no collectives in this build).
 """
@@ -164,11 +171,18 @@ def main():
                            kr_layout=kr_layout, indexed=(tier == "hbm" and args.hbm_assembly == "index"))
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev=None, route_ev=None, route_layer=-1):
+        """One pass of the whole path over all routed layers.  ev: per-stage
+        events of every layer (stage breakdown); route_ev: events around the
+        routing-score call of layer route_layer only (the timed steps)."""
         for l in range(layers):
             if ev is not None:
                 ev[l][0].record(stream)
+            if l == route_layer:
+                route_ev[0].record(stream)
             runner.route(qr[l], store[l], cd)
+            if l == route_layer:
+                route_ev[1].record(stream)
             if ev is not None:
                 ev[l][1].record(stream)
             runner.select()
@@ -191,23 +205,30 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(layers)]
-           for _ in range(args.steps)]
+    # timed steps: one pair of events per step, around one layer's routing-score
+    # call (a different layer each step), so that the step is not slowed by
+    # instrumentation; the whole-step time is the wall clock
+    route_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
-        step(evs[s])
+        step(route_ev=route_evs[s], route_layer=s % layers)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    route_ms = [e[0].elapsed_time(e[1]) for e in route_evs]
+    # stage breakdown: extra, untimed steps with events between all stages
+    n_stage = min(args.steps, 3)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(layers)]
+           for _ in range(n_stage)]
+    for s in range(n_stage):
+        step(evs[s])
+    torch.cuda.synchronize()
     stage = np.zeros(4)
-    route_ms = []
-    for s in range(args.steps):
+    for s in range(n_stage):
         for l in range(layers):
             e = evs[s][l]
-            dts = [e[i].elapsed_time(e[i + 1]) for i in range(4)]
-            stage += dts
-            route_ms.append(dts[0])
-    stage /= args.steps
+            stage += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
+    stage /= n_stage
     ms_per_step = wall * 1e3 / args.steps
     store_bytes = N * H * d * esz                      # per layer
     step_bytes = store_bytes * layers

@@ -869,7 +869,7 @@ static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int m
   p.prefill = p.n_rt >= 2;
   int64_t units, target;
   if (p.prefill) {
-    p.rtw = p.n_rt > PF_WAVES ? 2 : 1;
+    p.rtw = 1;   // one row tile per wave: more workgroups, fewer key splits
     p.n_rg = (p.n_rt + PF_WAVES * p.rtw - 1) / (PF_WAVES * p.rtw);
     units = int64_t(B) * Hkv * p.n_rg;      // workgroups per split
     target = 256;                            // about one workgroup per CU
