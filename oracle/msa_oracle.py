@@ -41,6 +41,10 @@ Readings where the pages are silent (each also listed in the design notes):
       then the local tokens.
 * R18 stores (normalised routing keys, pooled K and V) are rounded once,
       round-to-nearest-even, to the store dtype.
+* R23-R26 (Memory Interleave, see ``interleave``): the router stands in for
+      the model's document-id generation, fetched documents are appended in
+      round order, the query offset is the number of documents fetched, and
+      the number of rounds is fixed.
 """
 from __future__ import annotations
 
@@ -303,3 +307,65 @@ def layer(q_r, kr_store, chunk_off, k_bar, v_bar, k, q, k_loc, v_loc,
     ctx = [gather(use[b], chunk_off, k_bar, v_bar) for b in range(q.shape[0])]
     out = sparse_attention(q, ctx, k_loc, v_loc, q_pos_offset, base, sm_scale)
     return dict(doc_score=doc_score, ids=ids, vals=vals, contexts=ctx, out=out)
+
+
+# ---------------------------------------------------------------------------
+# Memory Interleave: rounds of routing with a growing context
+# [P1 核心方法 > Memory Interleave (generate doc id -> fetch -> add to the
+#  query -> retrieve again); P2 Key Contributions ("generative retrieval ->
+#  context expansion -> generation") and Fig. 3 ("optional multi-round
+#  interleave"); P3 核心创新 > Memory Interleave]
+#
+# R23 the model that emits document ids is not part of this path: round r's
+#     documents are the top k of round r's routing query among the documents
+#     not fetched in earlier rounds.
+# R24 fetched documents are appended to the context in round order (rank order
+#     inside a round), each restarting its positions at 0; each round's
+#     routing query is an input (in a model it follows from the grown context).
+# R25 the query's global offset is the number of documents fetched (rounds x k).
+# R26 the number of rounds is fixed (the model's stop decision is not modelled).
+# ---------------------------------------------------------------------------
+
+def topk_excluding(doc_score: np.ndarray, k: int, excluded) -> tuple:
+    """``topk`` over the documents of each query that are not in excluded[b].
+    When fewer than k documents remain, the trailing ids are -1 and their
+    values NaN."""
+    doc_score = np.asarray(doc_score, dtype=np.float64)
+    B, D = doc_score.shape
+    if k < 1 or k > D:
+        raise ValueError("k must be in [1, n_docs]")
+    ids = np.full((B, k), -1, dtype=np.int32)
+    vals = np.full((B, k), np.nan, dtype=np.float64)
+    for b in range(B):
+        keep = np.ones(D, dtype=bool)
+        ex = np.asarray(list(excluded[b]), dtype=np.int64)
+        keep[ex[(ex >= 0) & (ex < D)]] = False
+        doc = np.nonzero(keep)[0]
+        order = doc[np.lexsort((doc, -doc_score[b, doc]))]
+        n = min(k, len(order))
+        ids[b, :n] = order[:n]
+        vals[b, :n] = doc_score[b, order[:n]]
+    return ids, vals
+
+
+def interleave(q_r_rounds, kr_store, chunk_off, k_bar, v_bar, k, q, k_loc, v_loc, base=1e6, sm_scale=None,
+               ids_override=None):
+    """Rounds of route -> top-k among documents not yet fetched -> append,
+    then attention over every fetched document and the local tokens (R23-R26).
+
+    ``ids_override[r]`` (B x k) replaces round r's own selection for the
+    exclusions of later rounds and for the context (inside the tie band
+    several selections are correct)."""
+    B = q.shape[0]
+    fetched = [[] for _ in range(B)]
+    rounds = []
+    for r, qr in enumerate(q_r_rounds):
+        doc_score = route_scores(qr, kr_store, chunk_off)
+        ids, vals = topk_excluding(doc_score, k, fetched)
+        rounds.append(dict(doc_score=doc_score, ids=ids, vals=vals))
+        use = ids if ids_override is None else np.asarray(ids_override[r])
+        for b in range(B):
+            fetched[b].extend(int(x) for x in use[b] if x >= 0)
+    ctx = [gather(np.asarray(fetched[b], dtype=np.int64), chunk_off, k_bar, v_bar) for b in range(B)]
+    out = sparse_attention(q, ctx, k_loc, v_loc, len(q_r_rounds) * k, base, sm_scale)
+    return dict(rounds=rounds, fetched=fetched, contexts=ctx, out=out)

@@ -384,3 +384,85 @@ def test_planted_needle_is_rank_one_tiny():
     ids, vals = O.topk(s, p.k)
     assert ids[0, 0] == nd[0]
     assert vals[0, 0] > vals[0, 1] + 0.1
+
+
+# ---------------------------------------------------------------- Memory Interleave (R23-R26)
+
+def _interleave_case(seed, n_docs=40, B=2, T=3, H=4, d=16, rounds=3, k=4):
+    r = rng(seed)
+    lens = r.integers(1, 6, size=n_docs)
+    chunk_off = np.concatenate([[0], np.cumsum(lens)])
+    N = int(chunk_off[-1])
+    store = O.l2_normalize(r.standard_normal((N, H, d)))
+    kb, vb = r.standard_normal((N, H, d)), r.standard_normal((N, H, d))
+    qr = [r.standard_normal((B, T, H, d)) for _ in range(rounds)]
+    q = r.standard_normal((B, T, 2 * H, d))
+    kl, vl = r.standard_normal((B, 5, H, d)), r.standard_normal((B, 5, H, d))
+    return qr, store, chunk_off, kb, vb, q, kl, vl
+
+
+def test_interleave_same_query_each_round_equals_one_longer_ranking():
+    """With one routing query reused in every round, the rounds' selections
+    laid end to end are the top (rounds x k) of that query's ranking
+    (heapq selection by (-score, id))."""
+    qr, store, co, kb, vb, q, kl, vl = _interleave_case(1)
+    rounds, k = 4, 5
+    res = O.interleave([qr[0]] * rounds, store, co, kb, vb, k, q, kl, vl)
+    s = O.route_scores(qr[0], store, co)
+    for b in range(q.shape[0]):
+        want = [i for _, i in heapq.nsmallest(rounds * k, [(-s[b, i], i) for i in range(s.shape[1])])]
+        got = np.concatenate([rd["ids"][b] for rd in res["rounds"]]).tolist()
+        assert got == want
+        assert res["fetched"][b] == want
+
+
+def test_interleave_rounds_match_iterative_argmax():
+    """Each round picks, k times, the best document not yet fetched (a plain
+    iterative argmax with the id tie-break); no document is fetched twice."""
+    qr, store, co, kb, vb, q, kl, vl = _interleave_case(2)
+    k = 4
+    res = O.interleave(qr, store, co, kb, vb, k, q, kl, vl)
+    for b in range(q.shape[0]):
+        taken = set()
+        for r, rd in enumerate(res["rounds"]):
+            s = O.route_scores(qr[r], store, co)[b]
+            for j in range(k):
+                best = None
+                for i in range(len(s)):
+                    if i in taken:
+                        continue
+                    if best is None or s[i] > s[best]:
+                        best = i
+                assert rd["ids"][b, j] == best and rd["vals"][b, j] == s[best]
+                taken.add(best)
+        assert len(res["fetched"][b]) == len(set(res["fetched"][b])) == k * len(qr)
+
+
+def test_interleave_pads_when_documents_run_out():
+    s = np.array([[0.3, 0.9, -0.2, 0.5, 0.1]])
+    ids, vals = O.topk_excluding(s, 3, [[1, 3, 0]])
+    assert ids.tolist() == [[4, 2, -1]]
+    assert vals[0, :2].tolist() == [0.1, -0.2] and np.isnan(vals[0, 2])
+    # ties keep the id order; excluded ids outside [0, D) are ignored
+    ids, _ = O.topk_excluding(np.array([[0.5, 0.5, 0.5, 0.7]]), 2, [[3, 99, -1]])
+    assert ids.tolist() == [[0, 1]]
+
+
+def test_interleave_context_is_round_then_rank_order_with_local_positions():
+    """Document-wise positions restart at 0 for every fetched document, in
+    the order the documents were fetched (worked by hand on a tiny index)."""
+    co = np.array([0, 2, 5, 6, 9])                 # 4 documents of 2, 3, 1, 3 chunks
+    N = 9
+    kb = np.arange(N, dtype=np.float64).reshape(N, 1, 1).repeat(2, axis=2)
+    out = O.gather(np.array([3, 0, 1]), co, kb, kb)
+    assert out[0][:, 0, 0].tolist() == [6, 7, 8, 0, 1, 2, 3, 4]
+    assert out[2].tolist() == [0, 1, 2, 0, 1, 0, 1, 2]
+
+
+def test_interleave_one_round_is_the_single_layer():
+    qr, store, co, kb, vb, q, kl, vl = _interleave_case(3)
+    k = 6
+    one = O.interleave(qr[:1], store, co, kb, vb, k, q, kl, vl)
+    ref = O.layer(qr[0], store, co, kb, vb, k, q, kl, vl)
+    assert np.array_equal(one["rounds"][0]["ids"], ref["ids"])
+    assert np.abs(one["out"] - ref["out"]).max() < 1e-13
