@@ -172,8 +172,11 @@ int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, cons
  * cosine similarity).  For each query b the k documents with the largest
  * doc_score, ordered by (score descending, document id ascending); ties are
  * broken by the lower id, so the result is unique.
- *   doc_score [B, n_docs] float32 (no NaN)
- *   ids       [B, k] int32 output, vals [B, k] float32 output (rank order)
+ *   doc_score [B, n_docs] float32; a NaN score marks an excluded document
+ *              (msa_exclude_docs), which is never selected
+ *   ids       [B, k] int32 output, vals [B, k] float32 output (rank order);
+ *              when fewer than k documents are left, the trailing ids are -1
+ *              (their vals NaN)
  *   ws        msa_topk_workspace() bytes
  * Errors: INVALID_ARG (NULL, B < 1, k < 1, k > n_docs), UNSUPPORTED (k > 256),
  * WORKSPACE.
@@ -181,6 +184,19 @@ int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, cons
 size_t msa_topk_workspace(int B, int64_t n_docs, int k);
 int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
              size_t ws_bytes, void* stream);
+
+/*
+ * msa_exclude_docs - Memory Interleave (paper note 核心方法 > Memory
+ * Interleave; README, Key Contributions and Fig. 3: rounds of retrieval, each
+ * adding documents to the context).  Marks the documents fetched in earlier
+ * rounds so that the next msa_topk skips them:
+ *   doc_score[b, ids[s, b, j]] = NaN   for s < n_sets, j < k
+ *   doc_score [B, n_docs] float32, updated in place (after msa_route_score)
+ *   ids       [n_sets, B, k] int32 device (earlier rounds' msa_topk ids);
+ *             ids outside [0, n_docs) (-1 included) are ignored
+ * Errors: INVALID_ARG (NULL, sizes).  n_sets = 0 does nothing.
+ */
+int msa_exclude_docs(float* doc_score, int B, int64_t n_docs, const int32_t* ids, int n_sets, int k, void* stream);
 
 /*
  * msa_gather_kv - Stage 2 context assembly (README, Inference Pipeline:
@@ -236,6 +252,23 @@ int msa_gather_kv(int dtype, const int32_t* ids, int B, int k, const int64_t* ch
 int msa_context_index(const int32_t* ids, int B, int k, const int64_t* chunk_off, int64_t n_docs,
                       int max_doc_chunks, int64_t n_chunks, int max_ctx, int32_t* ctx_row, int32_t* ctx_pos,
                       int32_t* ctx_len, void* stream);
+
+/*
+ * msa_context_append - msa_context_index for one more round of Memory
+ * Interleave: the documents ids[b, :] (rank order) are appended after the
+ * ctx_len_in[b] entries already in the context, which are kept.
+ *   ctx_row, ctx_pos [B, max_ctx] int32 device, updated from entry
+ *             ctx_len_in[b] on (same definitions as msa_context_index)
+ *   ctx_len_in [B] int32 device input; ctx_len_out [B] int32 device output
+ *             (a different array) = ctx_len_in + the appended chunk counts,
+ *             never beyond max_ctx (entries that do not fit are dropped)
+ *   ids       [B, k] int32; -1 (an exhausted msa_topk) contributes nothing
+ * Errors: INVALID_ARG (NULL, aliased lengths, sizes, max_ctx < k *
+ * max_doc_chunks), UNSUPPORTED (n_chunks >= 2^31, B or k > 65535), HIP.
+ */
+int msa_context_append(const int32_t* ids, int B, int k, const int64_t* chunk_off, int64_t n_docs,
+                       int max_doc_chunks, int64_t n_chunks, int max_ctx, int32_t* ctx_row, int32_t* ctx_pos,
+                       const int32_t* ctx_len_in, int32_t* ctx_len_out, void* stream);
 
 /*
  * msa_sparse_attn - Stage 3 sparse attention (README, Overall Design >

@@ -19,7 +19,9 @@ from ._binding import (  # noqa: F401
     msa_abi_version,
     msa_chunk_doc_map,
     msa_chunk_offsets,
+    msa_context_append,
     msa_context_index,
+    msa_exclude_docs,
     msa_gather_kv,
     msa_pool_encode,
     msa_route_score,

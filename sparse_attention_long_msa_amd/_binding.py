@@ -39,6 +39,8 @@ _SIGS = {
     "msa_gather_kv": (_I, [_I, _P, _I, _I, _P, _P, _L, _I, _P, _P, _L, _I, _I, _I, _I,
                            _P, _P, _P, _P, _P, _P, _P]),
     "msa_context_index": (_I, [_P, _I, _I, _P, _L, _I, _L, _I, _P, _P, _P, _P]),
+    "msa_exclude_docs": (_I, [_P, _I, _L, _P, _I, _I, _P]),
+    "msa_context_append": (_I, [_P, _I, _I, _P, _L, _I, _L, _I, _P, _P, _P, _P, _P]),
     "msa_sparse_attn_workspace": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "msa_sparse_attn": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _I, _I,
                              _F, _P, _I, _F, _P, _P, _S, _P]),
@@ -229,6 +231,24 @@ def msa_context_index(ids, chunk_off, n_chunks, max_doc_chunks, max_ctx, ctx_row
         _ptr(ids), B, k, _ptr(chunk_off), chunk_off.numel() - 1, max_doc_chunks, n_chunks, max_ctx, _ptr(ctx_row),
         _ptr(ctx_pos), _ptr(ctx_len), _stream(stream)))
     return ctx_row, ctx_pos, ctx_len
+
+
+def msa_exclude_docs(doc_score, ids_sets, stream=None):
+    """ids_sets: [n_sets, B, k] int32 (earlier rounds' selections)."""
+    B, n_docs = doc_score.shape
+    n_sets, _, k = ids_sets.shape
+    _check("msa_exclude_docs", lib.msa_exclude_docs(_ptr(doc_score), B, n_docs, _ptr(ids_sets) if n_sets else None,
+                                                    n_sets, k, _stream(stream)))
+    return doc_score
+
+
+def msa_context_append(ids, chunk_off, n_chunks, max_doc_chunks, ctx_row, ctx_pos, ctx_len_in, ctx_len_out,
+                       stream=None):
+    B, k = ids.shape
+    _check("msa_context_append", lib.msa_context_append(
+        _ptr(ids), B, k, _ptr(chunk_off), chunk_off.numel() - 1, max_doc_chunks, n_chunks, ctx_row.shape[1],
+        _ptr(ctx_row), _ptr(ctx_pos), _ptr(ctx_len_in), _ptr(ctx_len_out), _stream(stream)))
+    return ctx_row, ctx_pos, ctx_len_out
 
 
 def msa_sparse_attn_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset):

@@ -51,11 +51,15 @@ __global__ __launch_bounds__(GK_THREADS) void gather_kernel(const int32_t* __res
                                                             int max_ctx, uint4* __restrict__ k_ctx,
                                                             uint4* __restrict__ v_ctx, int32_t* __restrict__ ctx_pos,
                                                             int32_t* __restrict__ ctx_len,
-                                                            int32_t* __restrict__ ctx_row) {
+                                                            int32_t* __restrict__ ctx_row,
+                                                            const int32_t* __restrict__ ctx_len_in) {
   __shared__ int64_t red[GK_THREADS];
   const int r = blockIdx.x, b = blockIdx.y;
   const int32_t* ids_b = ids + int64_t(b) * k;
-  const int64_t dest = rank_offset(ids_b, r, chunk_off, n_docs, red);
+  // entries already in the context (appending): they are kept
+  int64_t base = ctx_len_in ? int64_t(ctx_len_in[b]) : 0;
+  base = base < 0 ? 0 : (base > max_ctx ? max_ctx : base);
+  const int64_t dest = base + rank_offset(ids_b, r, chunk_off, n_docs, red);
   const int32_t doc = ids_b[r];
   int64_t lo = 0, n = 0;
   if (doc >= 0 && doc < n_docs) {
@@ -134,7 +138,7 @@ extern "C" int msa_gather_kv(int dtype, const int32_t* ids, int B, int k, const 
   if (src_mode != MSA_SRC_HOST_MEMCPY) {
     hipLaunchKernelGGL(gather_kernel<GK_COPY>, grid, block, 0, s, ids, k, chunk_off, n_docs,
                        static_cast<const uint4*>(k_bar), static_cast<const uint4*>(v_bar), row_vec, max_ctx,
-                       static_cast<uint4*>(k_ctx), static_cast<uint4*>(v_ctx), ctx_pos, ctx_len, nullptr);
+                       static_cast<uint4*>(k_ctx), static_cast<uint4*>(v_ctx), ctx_pos, ctx_len, nullptr, nullptr);
     MSA_LAUNCH_CHECK();
     return MSA_OK;
   }
@@ -146,7 +150,7 @@ extern "C" int msa_gather_kv(int dtype, const int32_t* ids, int B, int k, const 
   // positions and lengths on the compute stream
   hipLaunchKernelGGL(gather_kernel<GK_POS>, grid, block, 0, s, ids, k, chunk_off, n_docs,
                      static_cast<const uint4*>(k_bar), static_cast<const uint4*>(v_bar), row_vec, max_ctx,
-                     static_cast<uint4*>(k_ctx), static_cast<uint4*>(v_ctx), ctx_pos, ctx_len, nullptr);
+                     static_cast<uint4*>(k_ctx), static_cast<uint4*>(v_ctx), ctx_pos, ctx_len, nullptr, nullptr);
   MSA_LAUNCH_CHECK();
   const char* kb = static_cast<const char*>(k_bar);
   const char* vb = static_cast<const char*>(v_bar);
@@ -192,7 +196,28 @@ extern "C" int msa_context_index(const int32_t* ids, int B, int k, const int64_t
   MSA_REQUIRE(B <= 65535 && k <= 65535, MSA_ERR_UNSUPPORTED, "msa_context_index: B or k too large");
   const dim3 grid{unsigned(k), unsigned(B)}, block{GK_THREADS};
   hipLaunchKernelGGL(gather_kernel<GK_ROWS>, grid, block, 0, as_stream(stream), ids, k, chunk_off, n_docs, nullptr,
-                     nullptr, int64_t(0), max_ctx, nullptr, nullptr, ctx_pos, ctx_len, ctx_row);
+                     nullptr, int64_t(0), max_ctx, nullptr, nullptr, ctx_pos, ctx_len, ctx_row, nullptr);
+  MSA_LAUNCH_CHECK();
+  return MSA_OK;
+}
+
+extern "C" int msa_context_append(const int32_t* ids, int B, int k, const int64_t* chunk_off, int64_t n_docs,
+                                  int max_doc_chunks, int64_t n_chunks, int max_ctx, int32_t* ctx_row,
+                                  int32_t* ctx_pos, const int32_t* ctx_len_in, int32_t* ctx_len_out, void* stream) {
+  using namespace msa;
+  MSA_REQUIRE(ids && chunk_off && ctx_row && ctx_pos && ctx_len_in && ctx_len_out, MSA_ERR_INVALID_ARG,
+              "msa_context_append: NULL pointer");
+  MSA_REQUIRE(ctx_len_in != ctx_len_out, MSA_ERR_INVALID_ARG,
+              "msa_context_append: ctx_len_in and ctx_len_out must be different arrays");
+  MSA_REQUIRE(B >= 1 && k >= 1 && n_docs >= 1 && n_chunks >= 1 && max_doc_chunks >= 1, MSA_ERR_INVALID_ARG,
+              "msa_context_append: non-positive size");
+  MSA_REQUIRE(n_chunks <= INT32_MAX, MSA_ERR_UNSUPPORTED, "msa_context_append: n_chunks must be below 2^31");
+  MSA_REQUIRE(int64_t(max_ctx) >= int64_t(k) * max_doc_chunks, MSA_ERR_INVALID_ARG,
+              "msa_context_append: max_ctx < k * max_doc_chunks");
+  MSA_REQUIRE(B <= 65535 && k <= 65535, MSA_ERR_UNSUPPORTED, "msa_context_append: B or k too large");
+  const dim3 grid{unsigned(k), unsigned(B)}, block{GK_THREADS};
+  hipLaunchKernelGGL(gather_kernel<GK_ROWS>, grid, block, 0, as_stream(stream), ids, k, chunk_off, n_docs, nullptr,
+                     nullptr, int64_t(0), max_ctx, nullptr, nullptr, ctx_pos, ctx_len_out, ctx_row, ctx_len_in);
   MSA_LAUNCH_CHECK();
   return MSA_OK;
 }

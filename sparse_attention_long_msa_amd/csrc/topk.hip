@@ -2,8 +2,10 @@
 // (MSA README, Overall Design > Architecture: "selects Top-k documents";
 //  paper note 核心方法 > 架构: top-k documents by cosine similarity.)
 //
-// Every (score, id) pair becomes one 64-bit key whose ascending order is the
-// ranking: the high word is the bit-complement of the order-preserving image
+// A NaN score marks a document excluded from the selection (msa_exclude_docs):
+// it gets the absent key, and when fewer than k documents remain the trailing
+// ids are -1.  Every (score, id) pair becomes one 64-bit key whose ascending
+// order is the ranking: the high word is the bit-complement of the order-preserving image
 // of the float score, the low word the document id.  Keys are unique, so
 // the selection is exact and deterministic.  Each pass sorts slices of 4096
 // keys in LDS with a bitonic network and keeps the k smallest of each slice;
@@ -37,10 +39,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_pass_kernel(const float* __re
     const int64_t g = base + i;
     uint64_t key = ~uint64_t(0);
     if (g < n) {
-      if constexpr (FROM_SCORES)
-        key = score_key(scores[int64_t(b) * n + g], uint32_t(g));
-      else
+      if constexpr (FROM_SCORES) {
+        const float sc = scores[int64_t(b) * n + g];
+        if (sc == sc) key = score_key(sc, uint32_t(g));   // NaN: an excluded document
+      } else {
         key = keys_in[int64_t(b) * n + g];
+      }
     }
     sk[i] = key;
   }
@@ -103,10 +107,12 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topk_wave_kernel(const float* _
     const int64_t g = base + int64_t(i) * 64 + lane;
     uint64_t key = SENT;
     if (g < n) {
-      if constexpr (FROM_SCORES)
-        key = score_key(scores[int64_t(b) * n + g], uint32_t(g));
-      else
+      if constexpr (FROM_SCORES) {
+        const float sc = scores[int64_t(b) * n + g];
+        if (sc == sc) key = score_key(sc, uint32_t(g));   // NaN: an excluded document
+      } else {
         key = keys_in[int64_t(b) * n + g];
+      }
     }
     v[i] = key;
     lmin = key < lmin ? key : lmin;
@@ -231,5 +237,32 @@ extern "C" int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, in
       hipLaunchKernelGGL((topk_pass_kernel<false, false>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
     MSA_LAUNCH_CHECK();
   }
+  return MSA_OK;
+}
+
+namespace msa {
+
+// doc_score[b, ids[s][b][j]] = NaN for every set s and j < k (ids [n_sets][B][k])
+__global__ void exclude_kernel(float* __restrict__ doc_score, int B, int64_t n_docs, const int32_t* __restrict__ ids,
+                               int k, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t doc = ids[i];
+  const int64_t b = (i / k) % B;
+  if (doc >= 0 && doc < n_docs) doc_score[b * n_docs + doc] = __uint_as_float(0x7FC00000u);
+}
+
+}  // namespace msa
+
+extern "C" int msa_exclude_docs(float* doc_score, int B, int64_t n_docs, const int32_t* ids, int n_sets, int k,
+                                void* stream) {
+  using namespace msa;
+  MSA_REQUIRE(doc_score && (ids || n_sets == 0), MSA_ERR_INVALID_ARG, "msa_exclude_docs: NULL pointer");
+  MSA_REQUIRE(B >= 1 && n_docs >= 1 && n_sets >= 0 && k >= 1, MSA_ERR_INVALID_ARG, "msa_exclude_docs: bad size");
+  const int64_t n = int64_t(n_sets) * B * k;
+  if (n == 0) return MSA_OK;
+  hipLaunchKernelGGL(exclude_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, as_stream(stream), doc_score, B,
+                     n_docs, ids, k, n);
+  MSA_LAUNCH_CHECK();
   return MSA_OK;
 }

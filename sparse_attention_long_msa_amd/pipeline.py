@@ -22,15 +22,20 @@ from . import _binding as B
 class LayerRunner:
     def __init__(self, *, batch, tokens, q_heads, kv_heads, head_dim, n_docs, n_chunks, k, max_doc_chunks,
                  local_len, dtype, device, q_pos_offset=None, rope_base=1e6, sm_scale=None,
-                 src_mode=B.MSA_SRC_DEVICE, chunk_off_h=None, kr_layout=B.MSA_LAYOUT_ROWS, indexed=False):
+                 src_mode=B.MSA_SRC_DEVICE, chunk_off_h=None, kr_layout=B.MSA_LAYOUT_ROWS, indexed=False,
+                 rounds=1):
         if indexed and src_mode != B.MSA_SRC_DEVICE:
             raise ValueError("indexed assembly reads the K/V store in place: it must be in device memory")
+        if rounds > 1 and not indexed:
+            raise ValueError("Memory Interleave rounds grow an indexed context (K/V store in device memory)")
+        self.rounds = rounds
         self.B, self.T, self.Hq, self.Hkv, self.d = batch, tokens, q_heads, kv_heads, head_dim
         self.n_docs, self.n_chunks, self.k = n_docs, n_chunks, k
         self.max_doc_chunks = max_doc_chunks
-        self.max_ctx = k * max_doc_chunks
+        self.max_ctx = rounds * k * max_doc_chunks
         self.L_loc = local_len
-        self.q_pos_offset = k if q_pos_offset is None else q_pos_offset
+        # "offset by k": the number of documents in the context (rounds x k)
+        self.q_pos_offset = rounds * k if q_pos_offset is None else q_pos_offset
         self.rope_base = rope_base
         self.sm_scale = 1.0 / math.sqrt(head_dim) if sm_scale is None else sm_scale
         self.src_mode = src_mode
@@ -53,6 +58,8 @@ class LayerRunner:
         self._store = None
         self.ctx_pos = torch.empty((batch, self.max_ctx), dtype=i32, device=dev)
         self.ctx_len = torch.empty((batch,), dtype=i32, device=dev)
+        self._lens = [self.ctx_len, torch.empty_like(self.ctx_len)]   # round r writes _lens[r % 2]
+        self.ids_rounds = torch.empty((rounds, batch, k), dtype=i32, device=dev) if rounds > 1 else None
         self.out = torch.empty((batch, tokens, q_heads, head_dim), dtype=f32, device=dev)
 
         def ws(n):
@@ -101,6 +108,28 @@ class LayerRunner:
                           self.rope_base, self.sm_scale, out=self.out, ws=self.at_ws, rope_table=self.rope_table,
                           stream=stream)
         return self.out
+
+    def interleave(self, q_r_rounds, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc, stream=None):
+        """Memory Interleave: per round, route with that round's routing query,
+        skip the documents fetched in earlier rounds, select k and append them
+        to the context; then attend over every fetched document and the local
+        tokens.  Round r's ids are ids_rounds[r]."""
+        R = len(q_r_rounds)
+        if R > self.rounds:
+            raise ValueError(f"built for {self.rounds} rounds")
+        for r, q_r in enumerate(q_r_rounds):
+            self.route(q_r, kr_hat, chunk_doc, stream)
+            B.msa_exclude_docs(self.doc_score, self.ids_rounds[:r], stream)
+            B.msa_topk(self.doc_score, self.k, ids=self.ids_rounds[r], vals=self.vals, ws=self.tk_ws, stream=stream)
+            if r == 0:
+                B.msa_context_index(self.ids_rounds[0], chunk_off, k_bar.shape[0], self.max_doc_chunks, self.max_ctx,
+                                    ctx_row=self.ctx_row, ctx_pos=self.ctx_pos, ctx_len=self._lens[0], stream=stream)
+            else:
+                B.msa_context_append(self.ids_rounds[r], chunk_off, k_bar.shape[0], self.max_doc_chunks, self.ctx_row,
+                                     self.ctx_pos, self._lens[(r - 1) % 2], self._lens[r % 2], stream=stream)
+        self.ctx_len = self._lens[(R - 1) % 2]
+        self._store = (k_bar, v_bar)
+        return self.attend(q, k_loc, v_loc, stream)
 
     def run(self, q_r, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc, stream=None):
         self.route(q_r, kr_hat, chunk_doc, stream)

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.msa_abi_version() == 4
+    assert M.msa_abi_version() == 5
     assert M.lib.msa_status_string(0).decode() == "ok"
     assert "workspace" in M.lib.msa_status_string(3).decode()
 
@@ -87,6 +87,18 @@ def test_gather_rejects_small_context_and_bad_mode():
     assert L.msa_gather_kv(1, P, 2, 11, P, None, 10, 8, P, P, 80, 8, 128, 0, 88, P, P, P, P, None, None, None) == 1
     # host-memcpy mode needs the host offsets and the pinned id staging
     assert L.msa_gather_kv(1, P, 2, 4, P, None, 10, 8, P, P, 80, 8, 128, 2, 32, P, P, P, P, None, None, None) == 1
+
+
+def test_interleave_validation():
+    L = M.lib
+    assert L.msa_exclude_docs(None, 1, 10, P, 1, 4, None) == 1
+    assert L.msa_exclude_docs(P, 1, 10, None, 1, 4, None) == 1
+    assert L.msa_exclude_docs(P, 0, 10, P, 1, 4, None) == 1
+    assert L.msa_exclude_docs(P, 1, 10, None, 0, 4, None) == 0      # nothing to exclude: no launch
+    #                          ids B  k  co n_docs maxdc n_chunks max_ctx row pos len_in len_out
+    assert L.msa_context_append(P, 2, 4, P, 10, 8, 80, 32, P, P, P, P, None) == 1            # aliased lengths
+    assert L.msa_context_append(P, 2, 4, P, 10, 8, 80, 31, P, P, P, ctypes.c_void_p(32), None) == 1
+    assert L.msa_context_append(P, 2, 4, P, 10, 8, 80, 32, P, P, None, P, None) == 1
 
 
 def test_context_index_validation():

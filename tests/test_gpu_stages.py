@@ -215,6 +215,97 @@ def test_sparse_attention_indexed(bf16, B, T, L_loc, ctx):
         assert e <= ATOL_ATTN["bf16" if bf16 else "f32"], f"b={b}: max-abs {e}"
 
 
+@pytest.mark.parametrize("B,D,k,n_sets", [(3, 5000, 16, 2), (2, 300, 64, 4), (1, 40, 16, 2), (2, 2000, 100, 3),
+                                          (4, 20000, 32, 1)])
+def test_exclude_then_topk(B, D, k, n_sets):
+    """Documents fetched in earlier rounds are skipped; ties keep the id order;
+    when the documents run out the trailing ids are -1 (oracle topk_excluding)."""
+    r = np.random.default_rng(D + k)
+    s = np.round(r.standard_normal((B, D)), 2).astype(np.float32)   # many ties
+    s[:, ::97] = -np.inf                                             # empty documents
+    sets = np.stack([np.stack([r.choice(D, size=k, replace=False) for _ in range(B)]) for _ in range(n_sets)])
+    sets = sets.astype(np.int32)
+    sets[0, 0, 0] = -1                      # an exhausted round
+    sets[-1, -1, -1] = D + 7                # out of range: ignored
+    ds = torch.from_numpy(s).to(dev())
+    M.msa_exclude_docs(ds, torch.from_numpy(sets).to(dev()))
+    ids, vals = M.msa_topk(ds, k)
+    torch.cuda.synchronize()
+    want_ids, want_vals = O.topk_excluding(s.astype(np.float64), k, [sets[:, b].reshape(-1).tolist() for b in range(B)])
+    np.testing.assert_array_equal(ids.cpu().numpy(), want_ids)
+    got_v = vals.cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(np.isnan(got_v), np.isnan(want_vals))
+    np.testing.assert_array_equal(got_v[~np.isnan(got_v)], want_vals[~np.isnan(want_vals)])
+
+
+def test_context_append_rounds():
+    lens = ragged_lengths(17, 60, 0, 500, n_empty=4)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    B, k, R = 3, 5, 4
+    mdc = int(np.diff(chunk_off).max())
+    max_ctx = R * k * mdc
+    r = np.random.default_rng(3)
+    picks = np.stack([r.permutation(60)[:R * k] for _ in range(B)]).astype(np.int32).reshape(B, R, k)
+    picks[1, 2, 3:] = -1                    # a round that ran out of documents
+    row = torch.full((B, max_ctx), -7, dtype=torch.int32, device=dev())
+    pos = torch.full((B, max_ctx), -7, dtype=torch.int32, device=dev())
+    lens_d = [torch.empty(B, dtype=torch.int32, device=dev()) for _ in range(2)]
+    for rd in range(R):
+        ids = torch.from_numpy(np.ascontiguousarray(picks[:, rd])).to(dev())
+        if rd == 0:
+            M.msa_context_index(ids, co_d, n_chunks, mdc, max_ctx, ctx_row=row, ctx_pos=pos, ctx_len=lens_d[0])
+        else:
+            M.msa_context_append(ids, co_d, n_chunks, mdc, row, pos, lens_d[(rd - 1) % 2], lens_d[rd % 2])
+    torch.cuda.synchronize()
+    ln = lens_d[(R - 1) % 2].cpu().numpy()
+    rowval = np.arange(n_chunks, dtype=np.float64)[:, None, None]
+    for b in range(B):
+        fetched = [int(x) for x in picks[b].reshape(-1) if x >= 0]
+        rk, _, rp = O.gather(np.asarray(fetched), chunk_off, rowval, rowval)
+        n = len(rp)
+        assert ln[b] == n
+        np.testing.assert_array_equal(row[b, :n].cpu().numpy(), rk[:, 0, 0].astype(np.int32))
+        np.testing.assert_array_equal(pos[b, :n].cpu().numpy(), rp)
+        assert (row[b, n:].cpu().numpy() == -7).all()      # nothing written past the context
+
+
+def test_interleave_end_to_end():
+    """Three rounds of route -> skip fetched -> top-k -> append, then attention
+    over the grown context, against the oracle's rounds on the GPU's picks."""
+    H, d, Hq, B, T, L_loc, k, R = 8, 128, 32, 2, 4, 300, 8, 3
+    lens = ragged_lengths(23, 900, 0, 1200, n_empty=20)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    D = len(lens)
+    mdc = int(np.diff(chunk_off).max())
+    store = O.round_to_bf16(O.l2_normalize(gen(61, 0, synth.T_KR, (n_chunks, H, d), True).astype(np.float64)))
+    kb = gen(61, 0, synth.T_K, (n_chunks, H, d), True, scale_pow2=-3)
+    vb = gen(61, 0, synth.T_V, (n_chunks, H, d), True, scale_pow2=-3)
+    qr = [gen(62, rd, synth.T_QR, (B, T, H, d), True) for rd in range(R)]
+    q = gen(62, 0, synth.T_Q, (B, T, Hq, d), True)
+    kl = gen(62, 0, synth.T_KLOC, (B, L_loc, H, d), True)
+    vl = gen(62, 0, synth.T_VLOC, (B, L_loc, H, d), True)
+    run = M.LayerRunner(batch=B, tokens=T, q_heads=Hq, kv_heads=H, head_dim=d, n_docs=D, n_chunks=n_chunks, k=k,
+                        max_doc_chunks=mdc, local_len=L_loc, dtype=torch.bfloat16, device=dev(),
+                        kr_layout=M.MSA_LAYOUT_TILED, indexed=True, rounds=R)
+    out = run.interleave([to_dev(x, True) for x in qr], to_dev(tile_np(store), True), cd, co_d, to_dev(kb, True),
+                         to_dev(vb, True), to_dev(q, True), to_dev(kl, True), to_dev(vl, True))
+    torch.cuda.synchronize()
+    gpu_ids = run.ids_rounds.cpu().numpy()
+    ref = O.interleave(qr, store, chunk_off, kb, vb, k, q, kl, vl, ids_override=gpu_ids)
+    fetched = [set() for _ in range(B)]
+    for rd in range(R):
+        s_ref = ref["rounds"][rd]["doc_score"].copy()
+        for b in range(B):
+            s_ref[b, list(fetched[b])] = -np.inf          # documents fetched earlier cannot be chosen
+            fetched[b].update(int(x) for x in gpu_ids[rd, b])
+        check_ids(gpu_ids[rd], s_ref, k)
+    for b in range(B):
+        assert len(fetched[b]) == R * k                   # no document fetched twice
+    e = np.abs(host(out) - ref["out"]).max()
+    assert e <= ATOL_ATTN["bf16"], e
+    assert int(run.ctx_len.cpu()[0]) == sum(int(np.diff(chunk_off)[x]) for x in gpu_ids[:, 0].reshape(-1))
+
+
 def _attn_case(seed, B, T, Hq, Hkv, d, L_loc, ctx_lens, bf16, max_ctx):
     q = gen(seed, 0, synth.T_Q, (B, T, Hq, d), bf16)
     kl = gen(seed, 0, synth.T_KLOC, (B, L_loc, Hkv, d), bf16)
