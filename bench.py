@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--hbm-assembly", choices=["index", "copy"], default="index",
                     help="HBM tier: attention reads the selected rows in place (index) or from a gathered copy")
     ap.add_argument("--layers", type=int, default=None, help="override the routed-layer count (profiling only)")
+    ap.add_argument("--rounds", type=int, default=1,
+                    help="Memory Interleave rounds per layer (> 1: route, skip the fetched documents, select and "
+                         "append, rounds times, then attend; content K/V in HBM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-chunks", type=int, default=None,
                     help="routing-key chunks of the oracle's sample (default: 1048576 at pooled level, "
@@ -130,6 +133,9 @@ def main():
     # ------------------------------------------------------------ content K/V tier
     t0 = time.time()
     tier = args.kv_tier
+    if args.rounds > 1 and tier != "hbm":
+        log("Memory Interleave rounds read the content K/V in place: using the HBM tier")
+        tier = "hbm"
     kbar, vbar = [], []
     kv_scale = -3 if p.pooled_level else 0
 
@@ -167,15 +173,31 @@ def main():
 
     runner = M.LayerRunner(batch=p.B, tokens=p.T, q_heads=p.Hq, kv_heads=H, head_dim=d, n_docs=D, n_chunks=N,
                            k=p.k, max_doc_chunks=p.max_doc_chunks, local_len=p.L_loc, dtype=bf, device=dev,
-                           q_pos_offset=p.qpo, rope_base=p.rope_base, src_mode=src_mode, chunk_off_h=chunk_off,
-                           kr_layout=kr_layout, indexed=(tier == "hbm" and args.hbm_assembly == "index"))
+                           q_pos_offset=p.qpo if args.rounds == 1 else None, rope_base=p.rope_base,
+                           src_mode=src_mode, chunk_off_h=chunk_off, kr_layout=kr_layout,
+                           indexed=(tier == "hbm" and (args.hbm_assembly == "index" or args.rounds > 1)),
+                           rounds=args.rounds)
     stream = torch.cuda.current_stream()
+    # routing queries of the later rounds: seeded like round 0's, seed + round
+    qr_rounds = [[qr[l]] + [SD.fill(torch.empty_like(qr[l]), p.qseed + r, l, synth.T_QR) for r in range(1, args.rounds)]
+                 for l in range(layers)]
 
     def step(ev=None, route_ev=None, route_layer=-1):
         """One pass of the whole path over all routed layers.  ev: per-stage
         events of every layer (stage breakdown); route_ev: events around the
         routing-score call of layer route_layer only (the timed steps)."""
         for l in range(layers):
+            if args.rounds > 1:
+                if ev is not None:
+                    ev[l][0].record(stream)
+                runner.fetch_rounds(qr_rounds[l], store[l], cd, co_d, kbar[l], vbar[l],
+                                    route_events=route_ev if l == route_layer else None)
+                if ev is not None:
+                    ev[l][3].record(stream)
+                runner.attend(qq[l], kl[l], vl[l])
+                if ev is not None:
+                    ev[l][4].record(stream)
+                continue
             if ev is not None:
                 ev[l][0].record(stream)
             if l == route_layer:
@@ -198,7 +220,7 @@ def main():
     # needle check on one pass (a property of the planted data, not timed)
     step()
     torch.cuda.synchronize()
-    ids_all = runner.ids.cpu().numpy()
+    ids_all = (runner.ids if args.rounds == 1 else runner.ids_rounds[0]).cpu().numpy()
     recall = float(np.mean([int(nd) in set(ids_all[i if p.needle_per_query else 0].tolist())
                             for i, nd in enumerate(needles)]))
 
@@ -227,11 +249,14 @@ def main():
     for s in range(n_stage):
         for l in range(layers):
             e = evs[s][l]
-            stage += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
+            if args.rounds > 1:   # rounds (route, skip, select, append) | attention
+                stage += [e[0].elapsed_time(e[3]), 0.0, 0.0, e[3].elapsed_time(e[4])]
+            else:
+                stage += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
     stage /= n_stage
     ms_per_step = wall * 1e3 / args.steps
     store_bytes = N * H * d * esz                      # per layer
-    step_bytes = store_bytes * layers
+    step_bytes = store_bytes * layers * args.rounds   # every round scans the layer's store
     value = step_bytes / (ms_per_step * 1e-3) / 1e9   # GB/s over the whole step
     routing_gbps = step_bytes / ((stage[0] + stage[1]) * 1e-3) / 1e9
     # algorithmic bytes of one msa_route_score launch: the store, the chunk->doc map,
@@ -264,12 +289,14 @@ def main():
         "data": "synthetic (seeded counter-based generator; planted needles)",
         "config": {"workload": workload,
                    "global_batch": p.B, "seq_len": p.T, "parallelism": "single GPU",
-                   "kv_tier": tier, "gather": args.gather if tier == "host" else f"hbm-{args.hbm_assembly}"},
+                   "kv_tier": tier, "gather": args.gather if tier == "host" else
+                   f"hbm-{args.hbm_assembly if args.rounds == 1 else 'index'}", "rounds": args.rounds},
         "route_attn_us_per_query": round(ms_per_step * 1e3 / p.B, 1),
         "routing_GBps": round(routing_gbps, 1),
         "routing_frac_of_8TBps": round(routing_gbps / 8000, 4),
-        "stage_ms_per_step": {"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
-                              "gather": round(stage[2], 4), "attention": round(stage[3], 4)},
+        "stage_ms_per_step": ({"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
+                               "gather": round(stage[2], 4), "attention": round(stage[3], 4)} if args.rounds == 1 else
+                              {"rounds_route_topk_append": round(stage[0], 4), "attention": round(stage[3], 4)}),
         "attention_GBps": round(attn_gbps, 1),
         "attention_frac_of_8TBps": round(attn_gbps / 8000, 4),
         "attention_bytes_per_layer": attn_bytes,

@@ -109,16 +109,21 @@ class LayerRunner:
                           stream=stream)
         return self.out
 
-    def interleave(self, q_r_rounds, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc, stream=None):
-        """Memory Interleave: per round, route with that round's routing query,
-        skip the documents fetched in earlier rounds, select k and append them
-        to the context; then attend over every fetched document and the local
-        tokens.  Round r's ids are ids_rounds[r]."""
+    def fetch_rounds(self, q_r_rounds, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, stream=None, route_events=None):
+        """The rounds of Memory Interleave: per round, route with that round's
+        routing query, skip the documents fetched in earlier rounds, select k
+        and append them to the context.  Round r's ids are ids_rounds[r].
+        route_events: optional (start, end) events recorded around round 0's
+        routing-score call."""
         R = len(q_r_rounds)
         if R > self.rounds:
             raise ValueError(f"built for {self.rounds} rounds")
         for r, q_r in enumerate(q_r_rounds):
+            if r == 0 and route_events is not None:
+                route_events[0].record(stream)
             self.route(q_r, kr_hat, chunk_doc, stream)
+            if r == 0 and route_events is not None:
+                route_events[1].record(stream)
             B.msa_exclude_docs(self.doc_score, self.ids_rounds[:r], stream)
             B.msa_topk(self.doc_score, self.k, ids=self.ids_rounds[r], vals=self.vals, ws=self.tk_ws, stream=stream)
             if r == 0:
@@ -129,6 +134,11 @@ class LayerRunner:
                                      self.ctx_pos, self._lens[(r - 1) % 2], self._lens[r % 2], stream=stream)
         self.ctx_len = self._lens[(R - 1) % 2]
         self._store = (k_bar, v_bar)
+
+    def interleave(self, q_r_rounds, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc, stream=None):
+        """Memory Interleave: fetch_rounds, then attention over every fetched
+        document and the local tokens (query offset rounds x k)."""
+        self.fetch_rounds(q_r_rounds, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, stream)
         return self.attend(q, k_loc, v_loc, stream)
 
     def run(self, q_r, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc, stream=None):
