@@ -92,7 +92,9 @@ __device__ __forceinline__ bf16x8 pv_operand(const unsigned char* vlds, int dt, 
 
 // Rotate the lane's 16 (m, m + 64) pairs: lo[kk] holds dims 32kk + 8*g4 + e,
 // hi[kk] dims 64 + 32kk + 8*g4 + e (kk = 0, 1).  cs points at tab[pos][0].
-__device__ __forceinline__ void rope_rotate(uint4 (&v)[4], const float2* __restrict__ cs, int g4) {
+// The rotated values are multiplied by scale before their one rounding.
+__device__ __forceinline__ void rope_rotate(uint4 (&v)[4], const float2* __restrict__ cs, int g4,
+                                            float scale = 1.f) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     float lo[8], hi[8];
@@ -104,10 +106,10 @@ __device__ __forceinline__ void rope_rotate(uint4 (&v)[4], const float2* __restr
       const float4 t = c4[e2];  // (cos, sin) of two consecutive m
       const float c0 = t.x, s0 = t.y, c1 = t.z, s1 = t.w;
       const float a0 = lo[2 * e2], b0 = hi[2 * e2], a1 = lo[2 * e2 + 1], b1 = hi[2 * e2 + 1];
-      lo[2 * e2] = a0 * c0 - b0 * s0;
-      hi[2 * e2] = b0 * c0 + a0 * s0;
-      lo[2 * e2 + 1] = a1 * c1 - b1 * s1;
-      hi[2 * e2 + 1] = b1 * c1 + a1 * s1;
+      lo[2 * e2] = (a0 * c0 - b0 * s0) * scale;
+      hi[2 * e2] = (b0 * c0 + a0 * s0) * scale;
+      lo[2 * e2 + 1] = (a1 * c1 - b1 * s1) * scale;
+      hi[2 * e2 + 1] = (b1 * c1 + a1 * s1) * scale;
     }
     v[kk] = pack8(lo);
     v[kk + 2] = pack8(hi);
@@ -497,6 +499,9 @@ constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_KS = 272;                         // bytes per key row of K_rot in LDS (256 + pad)
 constexpr int PF_K_BYTES = 32 * PF_KS;
 constexpr int PF_BUF = PF_K_BYTES + AT_V_BYTES;    // one step buffer
+constexpr int PF_DEPTH = 4;                        // steps whose loads are in flight (even)
+constexpr float PF_LAZY = 8.f;                     // running-max slack (base-2 logits)
+static_assert(PF_DEPTH % 2 == 0, "step s uses LDS buffer s % 2");
 
 struct PfRegs {
   uint2 klo, khi;     // dims 4x..4x+3 and 64+4x..64+4x+3 of key t/16
@@ -545,9 +550,17 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     for (int kk = 0; kk < 4; ++kk) qv[kk] = *reinterpret_cast<const uint4*>(qp + 32 * kk);
     int pq = qpo + L_loc - T + trow[i];
     pq = pq < 0 ? 0 : (pq >= P ? P - 1 : pq);
-    rope_rotate(qv, tab + int64_t(pq) * (AT_D / 2), g4);
+    rope_rotate(qv, tab + int64_t(pq) * (AT_D / 2), g4, scale_log2);   // logits come out in the base-2 domain
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) bq[i][kk] = __builtin_bit_cast(bf16x8, rok[i] ? qv[kk] : make_uint4(0, 0, 0, 0));
+  }
+  // the smallest causal horizon among this wave's rows: a step whose keys all
+  // lie within it (and within the split) needs no mask
+  int hmin = INT32_MAX;
+#pragma unroll
+  for (int i = 0; i < RTW; ++i) {
+    const int rt = rg * (PF_WAVES * RTW) + wave + PF_WAVES * i;
+    if (rt < n_rt) hmin = min(hmin, L_loc - T + (rt * 16) / G);
   }
 
   const int ctxl = min(max(ctx_len[b], 0), max_ctx);
@@ -563,21 +576,38 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
                                 ctx_pos, P, ctx_row, ctx_rows, tid, PF_THREADS);
   __syncthreads();
 
-  auto load_step = [&](int j0, PfRegs& R) {
-    {
+  // a step whose 32 keys are all local tokens addresses them affinely
+  auto all_local = [&](int j0) { return j0 >= ctxl && j0 + 32 <= n_keys; };
+  // Addresses are formed under the (uniform) all-local test and the loads
+  // come after it, so every path issues the same five loads and the
+  // compiler's waits on the load counter stay partial.
+  // element offsets of this thread's K/V row and RoPE row for a local key,
+  // less the part that depends on the (uniform) step start j0
+  const int64_t loc_kv = (int64_t(b) * L_loc - ctxl + lk) * kv_stride + int64_t(g) * AT_D;
+  const int64_t loc_tab = int64_t(qpo - ctxl + lk) * (AT_D / 2) + 4 * lx;
+  auto load_step = [&](int j0) {
+    const uint16_t* kp;
+    const uint16_t* vp;
+    const float2* tp;
+    if (all_local(j0)) {
+      const int64_t off = loc_kv + int64_t(j0) * kv_stride;
+      kp = k_loc + off + 4 * lx;
+      vp = v_loc + off + 8 * lx;
+      tp = tab + loc_tab + int64_t(j0) * (AT_D / 2);
+    } else {
       const KeySrc ks = key_src(j0 + lk, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
-      const uint16_t* kp = (ks.local ? k_loc : k_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 4 * lx;
-      R.klo = *reinterpret_cast<const uint2*>(kp);
-      R.khi = *reinterpret_cast<const uint2*>(kp + 64);
-      const float4* cp = reinterpret_cast<const float4*>(tab + int64_t(ks.pos) * (AT_D / 2) + 4 * lx);
-      R.cs0 = cp[0];
-      R.cs1 = cp[1];
+      const int64_t off = ks.row * kv_stride + int64_t(g) * AT_D;
+      kp = (ks.local ? k_loc : k_ctx) + off + 4 * lx;
+      vp = (ks.local ? v_loc : v_ctx) + off + 8 * lx;
+      tp = tab + int64_t(ks.pos) * (AT_D / 2) + 4 * lx;
     }
-    {
-      const KeySrc ks = key_src(j0 + lk, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows, cc);
-      const uint16_t* vp = (ks.local ? v_loc : v_ctx) + ks.row * kv_stride + int64_t(g) * AT_D + 8 * lx;
-      R.v = load_stream(vp);
-    }
+    PfRegs R;
+    R.klo = load_global8(kp);
+    R.khi = load_global8(kp + 64);
+    R.cs0 = __builtin_bit_cast(float4, load_global(tp));
+    R.cs1 = __builtin_bit_cast(float4, load_global(tp + 2));
+    R.v = load_global(vp);
+    return R;
   };
   auto store_step = [&](const PfRegs& R, unsigned char* buf) {
     // rotate the 4 (m, m+64) pairs of this thread and store K_rot[key][d]
@@ -615,8 +645,13 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     for (int dt = 0; dt < 8; ++dt) o[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // Online softmax in the base-2 domain with a lazy running max: a row's
+  // reference m moves only when a logit exceeds it by more than PF_LAZY, so
+  // the accumulators are rescaled rarely; p = 2^(x - m) then stays below
+  // 2^PF_LAZY, and the result, normalised by the same sums, is unchanged.
   auto compute_step = [&](int j0, const unsigned char* kb) {
     const unsigned char* vb = kb + PF_K_BYTES;
+    const bool full = j0 + 32 <= j_end && j0 + 31 - ctxl <= hmin;   // uniform
     // S^T for both 16-key tiles, for every row tile of this wave
     bf16x8 ka[2][4];
 #pragma unroll
@@ -628,44 +663,47 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     bf16x8 pb[RTW];
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
-      f32x4 sv[2];
+      float x[2][4];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tau][kk], bq[i][kk], acc, 0, 0, 0);
-        sv[tau] = acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[tau][e] = acc[e];
       }
-      float x[2][4];
-      float mt = -INFINITY;
+      if (!full) {
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
+        for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kj = j0 + 16 * tau + 4 * g4 + e;
-          const bool vis = rok[i] && kj < j_end && (kj < ctxl || kj - ctxl <= horizon[i]);
-          x[tau][e] = vis ? sv[tau][e] * scale_log2 : -INFINITY;
-          mt = fmaxf(mt, x[tau][e]);
-        }
+          for (int e = 0; e < 4; ++e) {
+            const int kj = j0 + 16 * tau + 4 * g4 + e;
+            const bool vis = rok[i] && kj < j_end && (kj < ctxl || kj - ctxl <= horizon[i]);
+            x[tau][e] = vis ? x[tau][e] : -INFINITY;
+          }
+      }
+      float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run[i], mt);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run[i] - m_use);
+      const bool grow = mt > m_run[i] + PF_LAZY;   // false while nothing is visible
+      if (__ballot(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[i] - mt) : 1.f;
+        m_run[i] = grow ? mt : m_run[i];
+        l_run[i] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
+      }
+      const float m_use = m_run[i] == -INFINITY ? 0.f : m_run[i];
       float p[2][4], psum = 0.f;
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[tau][e] = exp2f(x[tau][e] - m_use);
+          p[tau][e] = __builtin_amdgcn_exp2f(x[tau][e] - m_use);
           psum += p[tau][e];
         }
-      l_run[i] = l_run[i] * alpha + psum;
-      m_run[i] = m_new;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
-      }
+      l_run[i] += psum;
       pb[i] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                                                     pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])));
     }
@@ -677,29 +715,31 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     }
   };
 
-  // Two steps of global loads in flight: while step s is computed from one
-  // LDS buffer, step s+1 waits in registers for the other buffer and step
-  // s+2 is being loaded.
-  PfRegs RA, RB;
-  if (j_begin < j_end) {
-    load_step(j_begin, RA);
-    store_step(RA, smem);
-    if (j_begin + 32 < j_end) load_step(j_begin + 32, RB);
+  // Pipeline: the loads of the next PF_DEPTH steps are in flight in
+  // registers.  Step s writes its registers (rotating K) to LDS buffer s % 2,
+  // requests step s + PF_DEPTH into the registers it just freed, meets the
+  // workgroup at an LDS-only barrier (loads stay in flight across it) and
+  // computes from the buffer.  A buffer is rewritten two steps after it was
+  // read, and each wave's read precedes its next barrier, so one barrier per
+  // step suffices.  Requests past the last step repeat the last step's
+  // addresses (in bounds, never used), which keeps the loop free of branches
+  // around loads; steps of the last group past the end skip the compute.
+  const int n_steps = j_begin < j_end ? (j_end - j_begin + 31) / 32 : 0;
+  auto step_j = [&](int st) { return j_begin + 32 * min(st, n_steps - 1); };
+  PfRegs R[PF_DEPTH];
+  if (n_steps > 0) {
+#pragma unroll
+    for (int u = 0; u < PF_DEPTH; ++u) R[u] = load_step(step_j(u));
   }
-  __syncthreads();
-  int cur = 0;
-  for (int j0 = j_begin; j0 < j_end; j0 += 64) {
-    if (j0 + 64 < j_end) load_step(j0 + 64, RA);
-    compute_step(j0, smem + cur * PF_BUF);
-    if (j0 + 32 < j_end) store_step(RB, smem + (cur ^ 1) * PF_BUF);
-    __syncthreads();
-    cur ^= 1;
-    if (j0 + 32 >= j_end) break;
-    if (j0 + 96 < j_end) load_step(j0 + 96, RB);
-    compute_step(j0 + 32, smem + cur * PF_BUF);
-    if (j0 + 64 < j_end) store_step(RA, smem + (cur ^ 1) * PF_BUF);
-    __syncthreads();
-    cur ^= 1;
+  for (int s0 = 0; s0 < n_steps; s0 += PF_DEPTH) {
+#pragma unroll
+    for (int u = 0; u < PF_DEPTH; ++u) {
+      unsigned char* buf = smem + (u % 2) * PF_BUF;
+      store_step(R[u], buf);
+      R[u] = load_step(step_j(s0 + u + PF_DEPTH));
+      lds_barrier();
+      if (s0 + u < n_steps) compute_step(j_begin + 32 * (s0 + u), buf);
+    }
   }
 
 #pragma unroll
@@ -717,7 +757,8 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
   }
 }
 
-// out[b,t,hq,:] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s
+// out[b,t,hq,:] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, one pass with
+// a running maximum; eight splits' loads are issued together.
 __global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, int n_splits,
                                     int64_t rows, int d, float* __restrict__ out) {
   // one thread per (row, 4 dims); d is a multiple of 4 on this path
@@ -726,21 +767,39 @@ __global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float2
   if (i >= rows * dq) return;
   const int64_t row = i / dq;
   const int e = int(i % dq) * 4;
-  float m = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) m = fmaxf(m, ws_ml[s * rows + row].x);
-  const float mu = m == -INFINITY ? 0.f : m;
+  float m = -INFINITY, den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < n_splits; ++s) {
-    const float2 ml = ws_ml[s * rows + row];
-    const float w = exp2f(ml.x - mu);   // 0 for a split that saw no visible key
-    den += w * ml.y;
-    const float4 v = *reinterpret_cast<const float4*>(ws_o + (s * rows + row) * d + e);
-    num.x += w * v.x;
-    num.y += w * v.y;
-    num.z += w * v.z;
-    num.w += w * v.w;
+  constexpr int U = 8;
+  for (int s0 = 0; s0 < n_splits; s0 += U) {
+    float2 ml[U];
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = min(s0 + u, n_splits - 1);
+      ml[u] = ws_ml[sp * rows + row];
+      v[u] = *reinterpret_cast<const float4*>(ws_o + (sp * rows + row) * d + e);
+      if (s0 + u >= n_splits) ml[u].x = -INFINITY;   // past the last split: weight 0
+    }
+    float mg = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mg = fmaxf(mg, ml[u].x);
+    if (mg == -INFINITY) continue;   // no split so far saw a visible key
+    const float a = __builtin_amdgcn_exp2f(m - mg);   // 0 while m is -inf
+    den *= a;
+    num.x *= a;
+    num.y *= a;
+    num.z *= a;
+    num.w *= a;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = __builtin_amdgcn_exp2f(ml[u].x - mg);   // 0 for a split that saw no visible key
+      den += w * ml[u].y;
+      num.x += w * v[u].x;
+      num.y += w * v[u].y;
+      num.z += w * v[u].z;
+      num.w += w * v[u].w;
+    }
+    m = mg;
   }
   const float r = den > 0.f ? 1.f / den : 0.f;
   *reinterpret_cast<float4*>(out + row * d + e) = make_float4(num.x * r, num.y * r, num.z * r, num.w * r);

@@ -82,6 +82,14 @@ __device__ __forceinline__ uint4 load_global(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 8-byte load from global memory (see load_global).
+__device__ __forceinline__ uint2 load_global8(const void* p) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  typedef const __attribute__((address_space(1))) u32x2* gptr;
+  const u32x2 v = *(gptr)(p);
+  return make_uint2(v.x, v.y);
+}
+
 template <int DT> struct Elem;
 template <> struct Elem<MSA_F32> {
   using T = float;
