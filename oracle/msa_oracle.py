@@ -45,6 +45,10 @@ Readings where the pages are silent (each also listed in the design notes):
       the model's document-id generation, fetched documents are appended in
       round order, the query offset is the number of documents fetched, and
       the number of rounds is fixed.
+* R27-R31 (training-time path, see ``route_loss`` onwards): the routing loss
+      is a supervised contrastive loss over the documents with a temperature,
+      the max passes its derivative to one maximiser, the selection is held
+      fixed, and the store rounding is the identity in the backward.
 """
 from __future__ import annotations
 
@@ -369,3 +373,221 @@ def interleave(q_r_rounds, kr_store, chunk_off, k_bar, v_bar, k, q, k_loc, v_loc
     ctx = [gather(np.asarray(fetched[b], dtype=np.int64), chunk_off, k_bar, v_bar) for b in range(B)]
     out = sparse_attention(q, ctx, k_loc, v_loc, len(q_r_rounds) * k, base, sm_scale)
     return dict(rounds=rounds, fetched=fetched, contexts=ctx, out=out)
+
+
+# ---------------------------------------------------------------------------
+# Training-time path: the auxiliary routing loss and the backward of the path
+# [P1 训练 (continued pre-training with a generation loss plus an auxiliary
+#  supervised contrastive routing loss); P2 Abstract and Key Contributions
+#  (the layer is trainable end to end); P2 Implementation Notes (auxiliary
+#  routing loss)]
+#
+# R27 routing-loss form (the pages name it only): per query b and routed
+#     layer, the supervised contrastive loss of the query against all
+#     documents with the positive set P_b,
+#       L_b = -(1/|P_b|) sum_{p in P_b} log( exp(s_bp / tau) / sum_i exp(s_bi / tau) ),
+#     s the routing scores of the layer, tau a temperature (an input); empty
+#     documents (score -inf) carry no weight.
+# R28 the derivative of the token/chunk max goes to one maximiser: the
+#     smallest chunk index, then the smallest token, among those attaining it.
+# R29 x / max(||x||, eps) has derivative (I - xh xh^T) / ||x|| when
+#     ||x|| > eps, else I / eps.
+# R30 the selection (ids, context order and positions) is held fixed; the
+#     attention's gradients reach the query, the local K/V and the selected
+#     pooled rows, summed over every query and context entry that reads a row,
+#     and from the pooled rows the tokens of their chunk (the mean's adjoint).
+# R31 the store rounding (R18) is taken as the identity in the backward; the
+#     routing keys' gradient is taken at the normalised pooled entry and
+#     carried through the normalisation (R29) and the pooling to the tokens.
+# ---------------------------------------------------------------------------
+
+def route_loss(doc_score: np.ndarray, pos_ids: np.ndarray, tau: float):
+    """Routing loss per query (R27) and its gradient with respect to the scores.
+
+    doc_score: [B, D]; pos_ids: [B, P] document ids, -1 = padding (at least one
+    valid id per query).  Returns (loss [B], grad [B, D]) with
+    grad[b, i] = (softmax(s_b / tau)[i] - [i in P_b] / |P_b|) / tau."""
+    s = np.asarray(doc_score, dtype=np.float64)
+    B, D = s.shape
+    loss = np.zeros(B, dtype=np.float64)
+    grad = np.zeros((B, D), dtype=np.float64)
+    for b in range(B):
+        pos = sorted({int(p) for p in np.asarray(pos_ids[b]).ravel() if 0 <= p < D})
+        if not pos:
+            raise ValueError("every query needs a positive document")
+        z = s[b] / tau
+        mx = z[np.isfinite(z)].max()
+        lse = mx + np.log(np.exp(z - mx).sum())
+        loss[b] = -np.mean([z[p] - lse for p in pos])
+        target = np.zeros(D)
+        target[pos] = 1.0 / len(pos)
+        grad[b] = (np.exp(z - lse) - target) / tau
+    return loss, grad
+
+
+def route_argmax(q_r: np.ndarray, kr_store: np.ndarray, chunk_off: np.ndarray, eps: float = EPS):
+    """Routing scores with the maximiser of each (query, document) (R28).
+
+    Returns (doc_score [B, D], arg_chunk [B, D], arg_tok [B, D]); the
+    maximiser is the global chunk index and the query token; -1 for an empty
+    document."""
+    s = chunk_cosines(q_r, kr_store, eps)          # [B, T, N]
+    B, T, N = s.shape
+    chunk_off = np.asarray(chunk_off, dtype=np.int64)
+    D = len(chunk_off) - 1
+    score = np.full((B, D), -np.inf)
+    ac = np.full((B, D), -1, dtype=np.int64)
+    at = np.full((B, D), -1, dtype=np.int64)
+    for b in range(B):
+        for i in range(D):
+            lo, hi = int(chunk_off[i]), int(chunk_off[i + 1])
+            if hi == lo:
+                continue
+            block = s[b, :, lo:hi].T                # [chunks, T], chunk-major
+            flat = int(np.argmax(block))            # first maximiser: chunk, then token
+            c, t = divmod(flat, T)
+            score[b, i], ac[b, i], at[b, i] = block[c, t], lo + c, t
+    return score, ac, at
+
+
+def normalize_backward(x: np.ndarray, dy: np.ndarray, eps: float = EPS) -> np.ndarray:
+    """Gradient with respect to x of y = x / max(||x||, eps) over the last axis (R29)."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    n = np.sqrt((x * x).sum(axis=-1, keepdims=True))
+    big = n > eps
+    xh = x / np.where(big, n, 1.0)
+    proj = dy - xh * (xh * dy).sum(axis=-1, keepdims=True)
+    return np.where(big, proj / np.where(big, n, 1.0), dy / eps)
+
+
+def route_score_backward(q_r: np.ndarray, kr_store: np.ndarray, arg_chunk: np.ndarray, arg_tok: np.ndarray,
+                         grad: np.ndarray, eps: float = EPS):
+    """Gradients of sum_{b,i} grad[b, i] * s[b, i] with respect to the raw
+    routing queries and the (normalised) store entries (R28, R29, R31).
+
+    s[b, i] = (1/H) sum_h qhat[b, t*, h] . kr[c*, h] at the maximiser
+    (c*, t*) = (arg_chunk, arg_tok).  Returns (dq_r [B, T, H, d],
+    dkr [N, H, d])."""
+    q = np.asarray(q_r, dtype=np.float64)
+    kr = np.asarray(kr_store, dtype=np.float64)
+    B, T, H, d = q.shape
+    qh = l2_normalize(q, eps)
+    dqh = np.zeros_like(q)
+    dkr = np.zeros_like(kr)
+    for b in range(B):
+        for i in range(arg_chunk.shape[1]):
+            c, t = int(arg_chunk[b, i]), int(arg_tok[b, i])
+            if c < 0 or grad[b, i] == 0.0:
+                continue
+            w = grad[b, i] / H
+            dqh[b, t] += w * kr[c]
+            dkr[c] += w * qh[b, t]
+    return normalize_backward(q, dqh, eps), dkr
+
+
+def pool_backward(dy: np.ndarray, tok_off: np.ndarray, chunk: int, x: np.ndarray | None = None,
+                  eps: float = EPS) -> np.ndarray:
+    """Adjoint of ``pool``: token tau of chunk c receives dy[c] / n_c.  With x
+    (the token vectors) the pooled entry was L2-normalised (R2): dy is then
+    the gradient at the normalised entry and is first carried through the
+    normalisation of the chunk mean (R29, R31).  Returns [n_tok, H, d]."""
+    dy = np.asarray(dy, dtype=np.float64)
+    tok_off = np.asarray(tok_off, dtype=np.int64)
+    if x is not None:
+        dy = normalize_backward(pool(x, tok_off, chunk), dy, eps)
+    n_tok = int(tok_off[-1])
+    out = np.zeros((n_tok,) + dy.shape[1:], dtype=np.float64)
+    c = 0
+    for i in range(len(tok_off) - 1):
+        lo, hi = int(tok_off[i]), int(tok_off[i + 1])
+        for s0 in range(lo, hi, chunk):
+            e = min(s0 + chunk, hi)
+            out[s0:e] = dy[c] / (e - s0)
+            c += 1
+    return out
+
+
+def attend_one_backward(q: np.ndarray, k_ctx: np.ndarray, v_ctx: np.ndarray, ctx_pos: np.ndarray,
+                        k_loc: np.ndarray, v_loc: np.ndarray, q_pos_offset: int, base: float,
+                        sm_scale: float, dout: np.ndarray):
+    """Gradients of sum(attend_one(...) * dout) with respect to q, the context
+    entries and the local K/V (R30), each at the un-rotated input.
+
+    Softmax rows p, dp = dout . v, ds = p * (dp - sum(p * dp)); the rotated
+    query and keys receive sm_scale * ds times the other operand; a rotation's
+    adjoint is the rotation by the opposite angle.  Returns (dq [T, Hq, d],
+    dk_ctx, dv_ctx [n_ctx, Hkv, d], dk_loc, dv_loc [L_loc, Hkv, d])."""
+    T, Hq, d = q.shape
+    L_loc, Hkv = k_loc.shape[:2]
+    G = Hq // Hkv
+    n_ctx = k_ctx.shape[0]
+    k_all = np.concatenate([np.asarray(k_ctx, np.float64), np.asarray(k_loc, np.float64)])
+    v_all = np.concatenate([np.asarray(v_ctx, np.float64), np.asarray(v_loc, np.float64)])
+    pos_all = np.concatenate([np.asarray(ctx_pos, np.int64),
+                              q_pos_offset + np.arange(L_loc, dtype=np.int64)])
+    k_rot = rope(k_all, pos_all[:, None], base)
+    q_abs = L_loc - T + np.arange(T)
+    q_pos = (q_pos_offset + q_abs)[:, None]
+    q_rot = rope(q, q_pos, base)
+    dout = np.asarray(dout, dtype=np.float64)
+    dq_rot = np.zeros_like(q_rot)
+    dk_rot = np.zeros_like(k_rot)
+    dv_all = np.zeros_like(v_all)
+    for t in range(T):
+        visible = np.ones(n_ctx + L_loc, dtype=bool)
+        visible[n_ctx + q_abs[t] + 1:] = False
+        for hq in range(Hq):
+            g = hq // G
+            logits = sm_scale * (k_rot[:, g, :] @ q_rot[t, hq])
+            logits = np.where(visible, logits, -np.inf)
+            p = np.exp(logits - logits.max())
+            p /= p.sum()
+            dp = v_all[:, g, :] @ dout[t, hq]
+            ds = p * (dp - (p * dp).sum())
+            dq_rot[t, hq] = sm_scale * (ds @ k_rot[:, g, :])
+            dk_rot[:, g, :] += sm_scale * np.outer(ds, q_rot[t, hq])
+            dv_all[:, g, :] += np.outer(p, dout[t, hq])
+    dq = rope(dq_rot, -q_pos, base)
+    dk_all = rope(dk_rot, -pos_all[:, None], base)
+    return dq, dk_all[:n_ctx], dv_all[:n_ctx], dk_all[n_ctx:], dv_all[n_ctx:]
+
+
+def sparse_attention_backward(q: np.ndarray, contexts, k_loc: np.ndarray, v_loc: np.ndarray, q_pos_offset: int,
+                              base: float, dout: np.ndarray, sm_scale: float | None = None):
+    """Batched ``attend_one_backward``.  Returns (dq, ctx_grads, dk_loc, dv_loc)
+    with ctx_grads[b] = (dk_ctx, dv_ctx) per context entry of query b."""
+    q = np.asarray(q, dtype=np.float64)
+    B, T, Hq, d = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    dq = np.zeros(q.shape)
+    dk_loc = np.zeros(np.shape(k_loc))
+    dv_loc = np.zeros(np.shape(v_loc))
+    ctx_grads = []
+    for b in range(B):
+        kc, vc, pc = contexts[b]
+        dq[b], dkc, dvc, dk_loc[b], dv_loc[b] = attend_one_backward(
+            q[b], kc, vc, pc, k_loc[b], v_loc[b], q_pos_offset, base, sm_scale, dout[b])
+        ctx_grads.append((dkc, dvc))
+    return dq, ctx_grads, dk_loc, dv_loc
+
+
+def gather_backward(ids: np.ndarray, chunk_off: np.ndarray, ctx_grads, n_chunks: int):
+    """Adjoint of ``gather`` over all queries: each context entry's gradient is
+    added to the pooled row it was read from (R30).  Returns (dk_bar, dv_bar)
+    [n_chunks, Hkv, d]."""
+    dkb = dvb = None
+    for b, (dk, dv) in enumerate(ctx_grads):
+        if dkb is None:
+            dkb = np.zeros((n_chunks,) + dk.shape[1:])
+            dvb = np.zeros((n_chunks,) + dv.shape[1:])
+        e = 0
+        for doc in ids[b]:
+            if doc < 0:
+                continue
+            lo, hi = int(chunk_off[doc]), int(chunk_off[doc + 1])
+            dkb[lo:hi] += dk[e:e + hi - lo]
+            dvb[lo:hi] += dv[e:e + hi - lo]
+            e += hi - lo
+    return dkb, dvb
