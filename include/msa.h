@@ -334,6 +334,81 @@ int msa_sparse_attn_indexed(int dtype, const void* q, int B, int T, int Hq, int 
 int msa_rope_table_rows(int max_ctx, int L_loc, int q_pos_offset);
 int msa_rope_table(int rows, int d, float rope_base, float* table, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Training-time path (paper note 核心方法 > 训练: continued pre-training with
+ * a generation loss and an auxiliary supervised contrastive routing loss;
+ * README Abstract and Key Contributions: the layer is trained end to end;
+ * README Implementation Notes: auxiliary routing loss).  The selection
+ * (top-k ids, context order and positions) is held fixed; gradients are
+ * float32; a store's bf16 rounding is taken as the identity.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * msa_route_argmax - msa_route_score together with the maximiser of each
+ * score, for the routing backward.  doc_score[b,i] as in msa_route_score;
+ * (arg_chunk[b,i], arg_tok[b,i]) = the global chunk index and query token
+ * attaining it, the smallest chunk and then the smallest token among equal
+ * values; -1 for a document with no chunk.
+ *   q_r [B, T, H, d] dtype, kr_hat [n_chunks, H, d] dtype (MSA_LAYOUT_ROWS),
+ *   chunk_doc [n_chunks] int32, doc_score [B, n_docs] float32,
+ *   arg_chunk / arg_tok [B, n_docs] int32 outputs,
+ *   ws msa_route_argmax_workspace() bytes.
+ * bf16 with d % 32 == 0 runs on MFMA (exact products, float32 sums).
+ * Errors: INVALID_ARG (NULL, sizes), WORKSPACE, UNSUPPORTED (d > 256,
+ * B*T >= 2^24, n_chunks * T >= 2^32 - 1).
+ */
+size_t msa_route_argmax_workspace(int dtype, int B, int T, int H, int d, int64_t n_docs, int64_t n_chunks);
+int msa_route_argmax(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
+                     const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks, float* doc_score,
+                     int32_t* arg_chunk, int32_t* arg_tok, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * msa_route_loss - the auxiliary routing loss (reading: the supervised
+ * contrastive form over all documents).  For query b with positive set P_b
+ * (the distinct ids of pos_ids[b,:] inside [0, n_docs); -1 pads):
+ *   loss[b]    = -(1/|P_b|) sum_{p in P_b} log( exp(s_bp/tau) / sum_i exp(s_bi/tau) )
+ *   grad[b,i]  = d loss[b] / d s_bi = (softmax_i(s_b/tau) - [i in P_b]/|P_b|) / tau
+ * Documents scoring -inf (no chunk) or NaN carry no weight (grad 0).  A query
+ * without a valid positive gets loss NaN.
+ *   doc_score [B, n_docs] float32, pos_ids [B, n_pos] int32,
+ *   loss [B] float32, grad [B, n_docs] float32 outputs
+ * Errors: INVALID_ARG (NULL, sizes, tau <= 0), UNSUPPORTED (B > 65535,
+ * n_pos > 256).
+ */
+int msa_route_loss(const float* doc_score, int B, int64_t n_docs, const int32_t* pos_ids, int n_pos, float tau,
+                   float* loss, float* grad, void* stream);
+
+/*
+ * msa_route_score_backward - gradients of sum_{b,i} grad[b,i] * doc_score[b,i]:
+ * the score's derivative reaches its maximiser (c*, t*) = (arg_chunk, arg_tok)
+ * only, through s = (1/H) sum_h <q_r[b,t*,h]/||q_r[b,t*,h]||, kr_hat[c*,h]>.
+ *   dq_r    [B, T, H, d] float32, overwritten: w.r.t. the raw routing query
+ *           (through its normalisation; below norm 1e-8 the map is q / 1e-8)
+ *   dkr_hat [n_chunks, H, d] float32, ACCUMULATED (+=): w.r.t. the normalised
+ *           store entries (msa_pool_backward with x carries it to the tokens)
+ *   arg_chunk / arg_tok from msa_route_argmax; entries out of range or with
+ *   grad 0 contribute nothing.  Float atomics: the summation order varies.
+ * Errors: INVALID_ARG (NULL, sizes), UNSUPPORTED (n_chunks >= 2^31).
+ */
+int msa_route_score_backward(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
+                             int64_t n_chunks, const int32_t* arg_chunk, const int32_t* arg_tok,
+                             const float* grad, int64_t n_docs, float* dq_r, float* dkr_hat, void* stream);
+
+/*
+ * msa_pool_backward - adjoint of msa_pool_encode's chunk mean: token t of
+ * pooled chunk c receives dy[c] / n_c (n_c the chunk's token count).  With x
+ * (the token vectors given to msa_pool_encode with l2_normalize) dy is the
+ * gradient at the normalised entry and is first carried back through the
+ * normalisation of the chunk mean (recomputed in float32).
+ *   dy [n_chunks, H, d] float32; x [n_tok, H, d] dtype or NULL;
+ *   dx [n_tok, H, d] float32 output (every token of a chunk is written)
+ *   tok_off, chunk_off, chunk_doc as for msa_pool_encode
+ * Errors: INVALID_ARG (NULL, sizes), UNSUPPORTED (d > 256).
+ */
+int msa_pool_backward(int dtype, const float* dy, const int64_t* tok_off, const int64_t* chunk_off,
+                      const int32_t* chunk_doc, int64_t n_docs, int64_t n_tok, int64_t n_chunks, int H, int d,
+                      int chunk, const void* x, float* dx, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,12 @@ from ._binding import (  # noqa: F401
     msa_context_index,
     msa_exclude_docs,
     msa_gather_kv,
+    msa_pool_backward,
     msa_pool_encode,
+    msa_route_argmax,
+    msa_route_argmax_workspace,
+    msa_route_loss,
+    msa_route_score_backward,
     msa_route_score,
     msa_rope_table,
     msa_rope_table_rows,

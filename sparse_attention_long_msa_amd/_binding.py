@@ -48,6 +48,11 @@ _SIGS = {
                                      _F, _P, _I, _F, _P, _P, _S, _P]),
     "msa_rope_table_rows": (_I, [_I, _I, _I]),
     "msa_rope_table": (_I, [_I, _I, _F, _P, _P]),
+    "msa_route_argmax_workspace": (_S, [_I, _I, _I, _I, _I, _L, _L]),
+    "msa_route_argmax": (_I, [_I, _P, _I, _I, _I, _I, _P, _P, _L, _L, _P, _P, _P, _P, _S, _P]),
+    "msa_route_loss": (_I, [_P, _I, _L, _P, _I, _F, _P, _P, _P]),
+    "msa_route_score_backward": (_I, [_I, _P, _I, _I, _I, _I, _P, _L, _P, _P, _P, _L, _P, _P, _P]),
+    "msa_pool_backward": (_I, [_I, _P, _P, _P, _P, _L, _L, _L, _I, _I, _I, _P, _P, _P]),
 }
 
 
@@ -303,3 +308,68 @@ def msa_sparse_attn_indexed(q, k_bar, v_bar, ctx_row, ctx_pos, ctx_len, k_loc, v
         0 if rope_table is None else rope_table.shape[0], float(sm_scale), _ptr(out), _ptr(ws), wsb,
         _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------- training-time path
+
+def msa_route_argmax_workspace(dtype, B, T, H, d, n_docs, n_chunks):
+    return lib.msa_route_argmax_workspace(dtype, B, T, H, d, n_docs, n_chunks)
+
+
+def msa_route_argmax(q_r, kr_hat, chunk_doc, n_docs, doc_score=None, arg_chunk=None, arg_tok=None, ws=None,
+                     stream=None):
+    B, T, H, d = q_r.shape
+    n_chunks = chunk_doc.numel()
+    if kr_hat.shape[0] < n_chunks:
+        raise ValueError("kr_hat holds fewer chunks than chunk_doc names")
+    dev = q_r.device
+    dt = _dtype(q_r)
+    if doc_score is None:
+        doc_score = torch.empty((B, n_docs), dtype=torch.float32, device=dev)
+    if arg_chunk is None:
+        arg_chunk = torch.empty((B, n_docs), dtype=torch.int32, device=dev)
+    if arg_tok is None:
+        arg_tok = torch.empty((B, n_docs), dtype=torch.int32, device=dev)
+    ws, wsb = _ws(msa_route_argmax_workspace(dt, B, T, H, d, n_docs, n_chunks), dev, ws)
+    _check("msa_route_argmax", lib.msa_route_argmax(
+        dt, _ptr(q_r), B, T, H, d, _ptr(kr_hat), _ptr(chunk_doc), n_docs, n_chunks, _ptr(doc_score),
+        _ptr(arg_chunk), _ptr(arg_tok), _ptr(ws), wsb, _stream(stream)))
+    return doc_score, arg_chunk, arg_tok
+
+
+def msa_route_loss(doc_score, pos_ids, tau, loss=None, grad=None, stream=None):
+    B, n_docs = doc_score.shape
+    n_pos = pos_ids.shape[1]
+    if loss is None:
+        loss = torch.empty((B,), dtype=torch.float32, device=doc_score.device)
+    if grad is None:
+        grad = torch.empty_like(doc_score)
+    _check("msa_route_loss", lib.msa_route_loss(_ptr(doc_score), B, n_docs, _ptr(pos_ids), n_pos, float(tau),
+                                                _ptr(loss), _ptr(grad), _stream(stream)))
+    return loss, grad
+
+
+def msa_route_score_backward(q_r, kr_hat, arg_chunk, arg_tok, grad, dkr_hat, dq_r=None, stream=None):
+    """dkr_hat [n_chunks, H, d] float32 is accumulated into (zero it first)."""
+    B, T, H, d = q_r.shape
+    n_chunks = dkr_hat.shape[0]
+    n_docs = grad.shape[1]
+    if dq_r is None:
+        dq_r = torch.empty((B, T, H, d), dtype=torch.float32, device=q_r.device)
+    _check("msa_route_score_backward", lib.msa_route_score_backward(
+        _dtype(q_r), _ptr(q_r), B, T, H, d, _ptr(kr_hat), n_chunks, _ptr(arg_chunk), _ptr(arg_tok), _ptr(grad),
+        n_docs, _ptr(dq_r), _ptr(dkr_hat), _stream(stream)))
+    return dq_r, dkr_hat
+
+
+def msa_pool_backward(dy, tok_off, chunk_off, chunk_doc, n_tok, chunk, x=None, dtype=None, dx=None, stream=None):
+    """dx [n_tok, H, d] float32.  x (the token vectors, when the pooled entry
+    was L2-normalised) sets the dtype; otherwise ``dtype`` (default bf16)."""
+    n_chunks, H, d = dy.shape
+    if dx is None:
+        dx = torch.empty((n_tok, H, d), dtype=torch.float32, device=dy.device)
+    dt = _dtype(x) if x is not None else (MSA_BF16 if dtype is None else dtype)
+    _check("msa_pool_backward", lib.msa_pool_backward(
+        dt, _ptr(dy), _ptr(tok_off), _ptr(chunk_off), _ptr(chunk_doc), tok_off.numel() - 1, n_tok, n_chunks, H, d,
+        chunk, _ptr(x), _ptr(dx), _stream(stream)))
+    return dx

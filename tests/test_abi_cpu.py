@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.msa_abi_version() == 5
+    assert M.msa_abi_version() == 6
     assert M.lib.msa_status_string(0).decode() == "ok"
     assert "workspace" in M.lib.msa_status_string(3).decode()
 
@@ -99,6 +99,28 @@ def test_interleave_validation():
     assert L.msa_context_append(P, 2, 4, P, 10, 8, 80, 32, P, P, P, P, None) == 1            # aliased lengths
     assert L.msa_context_append(P, 2, 4, P, 10, 8, 80, 31, P, P, P, ctypes.c_void_p(32), None) == 1
     assert L.msa_context_append(P, 2, 4, P, 10, 8, 80, 32, P, P, None, P, None) == 1
+
+
+def test_training_path_validation():
+    L = M.lib
+    F = ctypes.c_float
+    #                      dt q  B  T  H  d   kr chunk_doc n_docs n_chunks score ac at ws wsb stream
+    assert L.msa_route_argmax(1, None, 1, 4, 8, 128, P, P, 10, 80, P, P, P, P, 1 << 30, None) == 1
+    assert L.msa_route_argmax(1, P, 1, 4, 8, 128, P, P, 10, 80, P, P, P, P, 0, None) == 3          # workspace
+    assert L.msa_route_argmax(1, P, 1, 4, 8, 512, P, P, 10, 80, P, P, P, P, 1 << 30, None) == 2    # d > 256
+    assert L.msa_route_argmax(1, P, 1, 1 << 12, 8, 128, P, P, 10, 1 << 21, P, P, P, P, 1 << 40, None) == 2
+    #                    score B n_docs pos n_pos tau loss grad stream
+    assert L.msa_route_loss(P, 1, 10, P, 2, F(0.0), P, P, None) == 1      # tau <= 0
+    assert L.msa_route_loss(P, 1, 10, None, 2, F(0.1), P, P, None) == 1
+    assert L.msa_route_loss(P, 1, 10, P, 300, F(0.1), P, P, None) == 2    # n_pos > 256
+    #                             dt q  B  T  H  d   kr n_chunks ac at grad n_docs dq dkr stream
+    assert L.msa_route_score_backward(1, P, 1, 4, 8, 128, P, 80, P, P, P, 0, P, P, None) == 1
+    assert L.msa_route_score_backward(1, P, 1, 4, 8, 128, P, 1 << 31, P, P, P, 10, P, P, None) == 2
+    assert L.msa_route_score_backward(1, P, 1, 4, 8, 128, P, 80, P, P, P, 10, P, None, None) == 1
+    #                      dt dy tok chunk_off chunk_doc n_docs n_tok n_chunks H d chunk x dx stream
+    assert L.msa_pool_backward(1, P, P, P, P, 4, 100, 8, 8, 512, 64, None, P, None) == 2
+    assert L.msa_pool_backward(1, P, P, P, P, 4, 100, 8, 8, 128, 0, None, P, None) == 1
+    assert L.msa_pool_backward(1, None, P, P, P, 4, 100, 8, 8, 128, 64, None, P, None) == 1
 
 
 def test_context_index_validation():
