@@ -409,6 +409,36 @@ int msa_pool_backward(int dtype, const float* dy, const int64_t* tok_off, const 
                       const int32_t* chunk_doc, int64_t n_docs, int64_t n_tok, int64_t n_chunks, int H, int d,
                       int chunk, const void* x, float* dx, void* stream);
 
+/*
+ * msa_sparse_attn_backward - gradients of msa_sparse_attn_indexed (same
+ * arguments, same definition of the keys, positions and mask) given dout, the
+ * gradient of its output:
+ *   dq     [B, T, Hq, d] float32, overwritten
+ *   dk_loc, dv_loc [B, L_loc, Hkv, d] float32, overwritten
+ *   dk_bar, dv_bar [n_chunks, Hkv, d] float32, ACCUMULATED (+=): each context
+ *          entry adds its gradient to the store row it reads (ctx_row), so a
+ *          row read by several queries receives their sum (float atomics).
+ * The forward is recomputed inside (its log-sum-exp per query row kept);
+ * then with P the softmax, D = <dout, out>, dP = dout . v and
+ * dS = P * (dP - D): dv = sum P dout, dk = R(-pos) sm_scale sum dS R q,
+ * dq = R(-pos_q) sm_scale sum dS R k (R the RoPE rotation; its adjoint turns
+ * by the opposite angle).  The bf16 d = 128 path runs on MFMA with bf16
+ * operands (dout rounded to bf16) and float32 accumulation; other shapes use
+ * a float32 vector path (at most 16384 - d - 256 keys and 8192 query rows
+ * per KV head).
+ *   ws  msa_sparse_attn_backward_workspace() bytes
+ * Errors: those of msa_sparse_attn_indexed; INVALID_ARG for NULL gradients;
+ * WORKSPACE; UNSUPPORTED beyond the vector path's sizes.
+ */
+size_t msa_sparse_attn_backward_workspace(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc,
+                                          int q_pos_offset);
+int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d, const void* k_bar,
+                             const void* v_bar, int64_t n_chunks, const int32_t* ctx_row, const int32_t* ctx_pos,
+                             const int32_t* ctx_len, int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
+                             int q_pos_offset, float rope_base, const float* rope_table, int rope_table_rows,
+                             float sm_scale, const float* dout, float* dq, float* dk_loc, float* dv_loc,
+                             float* dk_bar, float* dv_bar, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

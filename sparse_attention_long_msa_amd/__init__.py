@@ -34,6 +34,8 @@ from ._binding import (  # noqa: F401
     msa_rope_table_rows,
     msa_route_score_workspace,
     msa_sparse_attn,
+    msa_sparse_attn_backward,
+    msa_sparse_attn_backward_workspace,
     msa_sparse_attn_indexed,
     msa_sparse_attn_workspace,
     msa_topk,

@@ -53,6 +53,9 @@ _SIGS = {
     "msa_route_loss": (_I, [_P, _I, _L, _P, _I, _F, _P, _P, _P]),
     "msa_route_score_backward": (_I, [_I, _P, _I, _I, _I, _I, _P, _L, _P, _P, _P, _L, _P, _P, _P]),
     "msa_pool_backward": (_I, [_I, _P, _P, _P, _P, _L, _L, _L, _I, _I, _I, _P, _P, _P]),
+    "msa_sparse_attn_backward_workspace": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "msa_sparse_attn_backward": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _L, _P, _P, _P, _I, _P, _P, _I, _I,
+                                      _F, _P, _I, _F, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
 }
 
 
@@ -373,3 +376,36 @@ def msa_pool_backward(dy, tok_off, chunk_off, chunk_doc, n_tok, chunk, x=None, d
         dt, _ptr(dy), _ptr(tok_off), _ptr(chunk_off), _ptr(chunk_doc), tok_off.numel() - 1, n_tok, n_chunks, H, d,
         chunk, _ptr(x), _ptr(dx), _stream(stream)))
     return dx
+
+
+def msa_sparse_attn_backward_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset):
+    return lib.msa_sparse_attn_backward_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset)
+
+
+def msa_sparse_attn_backward(q, k_bar, v_bar, ctx_row, ctx_pos, ctx_len, k_loc, v_loc, q_pos_offset, dout,
+                             dk_bar, dv_bar, rope_base=1e6, sm_scale=None, rope_table=None, dq=None, dk_loc=None,
+                             dv_loc=None, ws=None, stream=None):
+    """Gradients of msa_sparse_attn_indexed.  dk_bar / dv_bar [n_chunks, Hkv, d]
+    float32 are accumulated into (zero them first); dq, dk_loc, dv_loc are
+    written.  Returns (dq, dk_loc, dv_loc, dk_bar, dv_bar)."""
+    B, T, Hq, d = q.shape
+    n_chunks, Hkv = k_bar.shape[0], k_bar.shape[1]
+    max_ctx = ctx_row.shape[1]
+    L_loc = k_loc.shape[1]
+    dt = _dtype(q)
+    dev_ = q.device
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if dq is None:
+        dq = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev_)
+    if dk_loc is None:
+        dk_loc = torch.empty((B, L_loc, Hkv, d), dtype=torch.float32, device=dev_)
+    if dv_loc is None:
+        dv_loc = torch.empty((B, L_loc, Hkv, d), dtype=torch.float32, device=dev_)
+    ws, wsb = _ws(msa_sparse_attn_backward_workspace(dt, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset), dev_, ws)
+    _check("msa_sparse_attn_backward", lib.msa_sparse_attn_backward(
+        dt, _ptr(q), B, T, Hq, Hkv, d, _ptr(k_bar), _ptr(v_bar), n_chunks, _ptr(ctx_row), _ptr(ctx_pos),
+        _ptr(ctx_len), max_ctx, _ptr(k_loc), _ptr(v_loc), L_loc, q_pos_offset, float(rope_base), _ptr(rope_table),
+        0 if rope_table is None else rope_table.shape[0], float(sm_scale), _ptr(dout), _ptr(dq), _ptr(dk_loc),
+        _ptr(dv_loc), _ptr(dk_bar), _ptr(dv_bar), _ptr(ws), wsb, _stream(stream)))
+    return dq, dk_loc, dv_loc, dk_bar, dv_bar

@@ -21,18 +21,9 @@
 // cos/sin table computed in float64 per call.
 #include <algorithm>
 
-#include "common.h"
+#include "attn_common.h"
 
 namespace msa {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int AT_D = 128;
-constexpr int AT_WAVES = 4;
-constexpr int AT_THREADS = 64 * AT_WAVES;
-constexpr int AT_VEC_THREADS = 256;
-constexpr int AT_VEC_MAX_KEYS = 32768;
 
 // tab[p][m] = (cos, sin)(p * base^(-2m/d)), angle formed and reduced in float64
 __global__ void rope_table_kernel(float2* __restrict__ tab, int P, int half, double base, int d) {
@@ -43,145 +34,6 @@ __global__ void rope_table_kernel(float2* __restrict__ tab, int P, int half, dou
   double sn, cs;
   sincos(double(p) * theta, &sn, &cs);
   tab[i] = make_float2(float(cs), float(sn));
-}
-
-// two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ void unpack8(const uint4& u, float (&x)[8]) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = __uint_as_float(w[e] << 16);
-    x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-  }
-}
-
-__device__ __forceinline__ uint4 pack8(const float (&x)[8]) {
-  return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                    pack_bf16x2(x[6], x[7]));
-}
-
-// Row-major V tile in LDS: 32 keys x 128 d (bf16), row stride AT_VS bytes.
-constexpr int AT_VS = 288;                   // 256 + 32: the 16 rows of one transpose read hit 8 bank groups
-constexpr int AT_V_BYTES = 32 * AT_VS;
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-
-// A operand of O^T = V^T P^T for d-tile dt: lane (lc, g4) receives
-// V[16*tau + 4*g4 + r][16*dt + lc] in slot 4*tau + r.  ds_read_b64_tr_b16
-// hands lane i of each 16-lane group element i % 4 of the 8-byte chunks
-// addressed by lanes 4r + i/4 (r = 0..3); so lane j = 4r + q of group g4
-// addresses key 16*tau + 4*g4 + r, dims 16*dt + 4q .. +3.
-__device__ __forceinline__ bf16x8 pv_operand(const unsigned char* vlds, int dt, int lane) {
-  const int g4 = lane / 16, j = lane % 16;
-  const int r = j / 4, q = j % 4;
-  typedef __attribute__((address_space(3))) v4s* lds_v4s;
-  const unsigned char* p0 = vlds + (4 * g4 + r) * AT_VS + (16 * dt + 4 * q) * 2;
-  const unsigned char* p1 = p0 + 16 * AT_VS;
-  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p0));
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p1));
-  typedef short v8s __attribute__((ext_vector_type(8)));
-  const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, both);
-}
-
-// Rotate the lane's 16 (m, m + 64) pairs: lo[kk] holds dims 32kk + 8*g4 + e,
-// hi[kk] dims 64 + 32kk + 8*g4 + e (kk = 0, 1).  cs points at tab[pos][0].
-// The rotated values are multiplied by scale before their one rounding.
-__device__ __forceinline__ void rope_rotate(uint4 (&v)[4], const float2* __restrict__ cs, int g4,
-                                            float scale = 1.f) {
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    float lo[8], hi[8];
-    unpack8(v[kk], lo);
-    unpack8(v[kk + 2], hi);
-    const float4* c4 = reinterpret_cast<const float4*>(cs + 32 * kk + 8 * g4);
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const float4 t = c4[e2];  // (cos, sin) of two consecutive m
-      const float c0 = t.x, s0 = t.y, c1 = t.z, s1 = t.w;
-      const float a0 = lo[2 * e2], b0 = hi[2 * e2], a1 = lo[2 * e2 + 1], b1 = hi[2 * e2 + 1];
-      lo[2 * e2] = (a0 * c0 - b0 * s0) * scale;
-      hi[2 * e2] = (b0 * c0 + a0 * s0) * scale;
-      lo[2 * e2 + 1] = (a1 * c1 - b1 * s1) * scale;
-      hi[2 * e2 + 1] = (b1 * c1 + a1 * s1) * scale;
-    }
-    v[kk] = pack8(lo);
-    v[kk + 2] = pack8(hi);
-  }
-}
-
-struct KeySrc {
-  int64_t row;   // row index into the [*, Hkv, d] tensor (already including b)
-  int pos;
-  bool local;
-  bool valid;
-};
-
-// Context entry e of query b: row b * max_ctx + e of a gathered context, or,
-// when ctx_row is given, row ctx_row[b, e] of the pooled store itself (the
-// concatenation is then only an index; rows are clamped into the store).
-__device__ __forceinline__ int64_t ctx_src_row(int64_t e, const int32_t* __restrict__ ctx_row, int64_t ctx_rows) {
-  if (!ctx_row) return e;
-  const int64_t r = ctx_row[e];
-  return r < 0 ? 0 : (r >= ctx_rows ? ctx_rows - 1 : r);
-}
-
-// A workgroup's context entries [lo, lo + n) as (store row, clamped
-// position), staged in LDS once so that no step waits on an index load.
-constexpr int AT_CIDX = 1024;
-constexpr int AT_CIDX_BYTES = AT_CIDX * 8;
-struct CtxCache {
-  const int2* e;
-  int lo, n;
-};
-
-__device__ __forceinline__ CtxCache stage_ctx(int2* lds, int b, int j_begin, int j_end, int ctxl, int max_ctx,
-                                              const int32_t* __restrict__ ctx_pos, int P,
-                                              const int32_t* __restrict__ ctx_row, int64_t ctx_rows, int tid,
-                                              int nthr) {
-  CtxCache c;
-  c.e = lds;
-  c.lo = j_begin;
-  c.n = max(0, min(min(j_end, ctxl) - j_begin, AT_CIDX));
-  for (int i = tid; i < c.n; i += nthr) {
-    const int64_t e = int64_t(b) * max_ctx + j_begin + i;
-    int p = ctx_pos[e];
-    p = p < 0 ? 0 : (p >= P ? P - 1 : p);
-    lds[i] = make_int2(ctx_row ? int(ctx_src_row(e, ctx_row, ctx_rows)) : 0, p);
-  }
-  return c;
-}
-
-__device__ __forceinline__ KeySrc key_src(int j, int b, int ctxl, int n_keys, int max_ctx, int L_loc, int qpo,
-                                          const int32_t* __restrict__ ctx_pos, int P,
-                                          const int32_t* __restrict__ ctx_row, int64_t ctx_rows,
-                                          const CtxCache& cc) {
-  // Branch-free (selects only), so the loads that follow stay straight-line
-  // code.  Every context key of the workgroup's range is cached (the host
-  // sizes the splits for it); the cache read is clamped into the cache and
-  // its value is used only for such keys.  Keys past the range end or past
-  // n_keys are masked by the caller: any in-bounds row will do.
-  (void)ctx_pos;
-  (void)P;
-  (void)ctx_rows;
-  const int i = j - cc.lo;
-  const bool in = i >= 0 && i < cc.n;
-  const int2 e = cc.e[min(max(i, 0), AT_CIDX - 1)];
-  const bool is_ctx = j < ctxl;
-  const int li = min(max(j - ctxl, 0), L_loc - 1);
-  const int64_t crow = ctx_row ? int64_t(in ? e.x : 0) : int64_t(b) * max_ctx + (in ? j : 0);
-  KeySrc k;
-  k.row = is_ctx ? crow : int64_t(b) * L_loc + li;
-  k.pos = is_ctx ? (in ? e.y : 0) : qpo + li;
-  k.local = !is_ctx;
-  k.valid = j < n_keys;
-  return k;
 }
 
 // ---------------------------------------------------------------- decode (one row tile)
@@ -211,8 +63,6 @@ struct TabRegs {
   uint4 t[DC_TAB_PT];   // this thread's pieces of the step's RoPE rows
 };
 
-// This wave's LDS operations are complete, then the workgroup barrier; unlike
-// __syncthreads() it does not wait for outstanding vector-memory loads.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 
@@ -760,7 +610,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
 // out[b,t,hq,:] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, one pass with
 // a running maximum; eight splits' loads are issued together.
 __global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, int n_splits,
-                                    int64_t rows, int d, float* __restrict__ out) {
+                                    int64_t rows, int d, float* __restrict__ out, float* __restrict__ lse) {
   // one thread per (row, 4 dims); d is a multiple of 4 on this path
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int dq = d / 4;
@@ -803,6 +653,7 @@ __global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float2
   }
   const float r = den > 0.f ? 1.f / den : 0.f;
   *reinterpret_cast<float4*>(out + row * d + e) = make_float4(num.x * r, num.y * r, num.z * r, num.w * r);
+  if (lse && e == 0) lse[row] = den > 0.f ? m + __log2f(den) : -INFINITY;
 }
 
 // Vector path (float32 or any even d): one workgroup per (b, t, hq); the
@@ -815,7 +666,7 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
     const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len, int max_ctx,
     const typename Elem<DT>::T* __restrict__ k_loc, const typename Elem<DT>::T* __restrict__ v_loc, int L_loc,
     int qpo, const int32_t* __restrict__ ctx_row, int64_t ctx_rows, const float2* __restrict__ tab, int P,
-    float sm_scale, float* __restrict__ out) {
+    float sm_scale, float* __restrict__ out, float* __restrict__ lse) {
   using E = Elem<DT>;
   extern __shared__ float vsm[];
   float* qr = vsm;               // [d]
@@ -889,6 +740,8 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
   }
   const float den = red[0];
   float* op = out + ((int64_t(b) * T + t) * Hq + hq) * d;
+  if (lse && threadIdx.x == 0)
+    lse[(int64_t(b) * T + t) * Hq + hq] = den > 0.f ? (gmax + logf(den)) * 1.4426950408889634f : -INFINITY;
   for (int e = threadIdx.x; e < d; e += AT_VEC_THREADS) {
     float acc = 0.f;
     for (int j = 0; j < n_keys; ++j) {
@@ -914,7 +767,6 @@ struct AttnPlan {
   size_t tab_bytes, o_bytes, ml_bytes;
 };
 
-static int rope_rows(int max_ctx, int L_loc, int qpo) { return std::max(std::max(qpo + L_loc, max_ctx), 32); }
 
 static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc, int qpo) {
   AttnPlan p{};
@@ -979,11 +831,11 @@ namespace msa {
 
 // Shared body of msa_sparse_attn (gathered context, ctx_row == NULL) and
 // msa_sparse_attn_indexed (context rows read in place from the pooled store).
-static int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
-                       const void* k_ctx, const void* v_ctx, const int32_t* ctx_row, int64_t ctx_rows,
-                       const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx, const void* k_loc,
-                       const void* v_loc, int L_loc, int q_pos_offset, float rope_base, const float* rope_table,
-                       int rope_table_rows, float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
+                const void* k_ctx, const void* v_ctx, const int32_t* ctx_row, int64_t ctx_rows, const int32_t* ctx_pos,
+                const int32_t* ctx_len, int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
+                int q_pos_offset, float rope_base, const float* rope_table, int rope_table_rows, float sm_scale,
+                float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
   MSA_REQUIRE(q && k_ctx && v_ctx && ctx_pos && ctx_len && k_loc && v_loc && out && ws, MSA_ERR_INVALID_ARG,
               fn + ": NULL pointer");
@@ -1054,7 +906,7 @@ static int sparse_attn(const std::string& fn, int dtype, const void* q, int B, i
       MSA_LAUNCH_CHECK();
       const int64_t rows = int64_t(B) * T * Hq;
       hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * (d / 4) + 255) / 256)), dim3(256), 0, s, ws_o,
-                         ws_ml, p.n_splits, rows, d, out);
+                         ws_ml, p.n_splits, rows, d, out, lse);
       MSA_LAUNCH_CHECK();
       return MSA_OK;
     }
@@ -1087,7 +939,7 @@ static int sparse_attn(const std::string& fn, int dtype, const void* q, int B, i
     MSA_LAUNCH_CHECK();
     const int64_t rows = int64_t(B) * T * Hq;
     hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * (d / 4) + 255) / 256)), dim3(256), 0, s, ws_o,
-                       ws_ml, p.n_splits, rows, d, out);
+                       ws_ml, p.n_splits, rows, d, out, lse);
     MSA_LAUNCH_CHECK();
     return MSA_OK;
   }
@@ -1097,12 +949,12 @@ static int sparse_attn(const std::string& fn, int dtype, const void* q, int B, i
     hipLaunchKernelGGL(attn_vec_kernel<MSA_BF16>, grid, block, smem, s, static_cast<const uint16_t*>(q), B, T, Hq, Hkv,
                        d, static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos, ctx_len,
                        max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc), L_loc,
-                       q_pos_offset, ctx_row, ctx_rows, tab, p.P, sm_scale, out);
+                       q_pos_offset, ctx_row, ctx_rows, tab, p.P, sm_scale, out, lse);
   else
     hipLaunchKernelGGL(attn_vec_kernel<MSA_F32>, grid, block, smem, s, static_cast<const float*>(q), B, T, Hq, Hkv, d,
                        static_cast<const float*>(k_ctx), static_cast<const float*>(v_ctx), ctx_pos, ctx_len, max_ctx,
                        static_cast<const float*>(k_loc), static_cast<const float*>(v_loc), L_loc, q_pos_offset,
-                       ctx_row, ctx_rows, tab, p.P, sm_scale, out);
+                       ctx_row, ctx_rows, tab, p.P, sm_scale, out, lse);
   MSA_LAUNCH_CHECK();
   return MSA_OK;
 }
@@ -1116,7 +968,7 @@ extern "C" int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, i
                                size_t ws_bytes, void* stream) {
   return msa::sparse_attn("msa_sparse_attn", dtype, q, B, T, Hq, Hkv, d, k_ctx, v_ctx, nullptr, 0, ctx_pos, ctx_len,
                           max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows, sm_scale,
-                          out, ws, ws_bytes, stream);
+                          out, nullptr, ws, ws_bytes, stream);
 }
 
 extern "C" int msa_sparse_attn_indexed(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
@@ -1131,5 +983,5 @@ extern "C" int msa_sparse_attn_indexed(int dtype, const void* q, int B, int T, i
               "msa_sparse_attn_indexed: n_chunks must lie in [1, 2^31)");
   return sparse_attn("msa_sparse_attn_indexed", dtype, q, B, T, Hq, Hkv, d, k_bar, v_bar, ctx_row, n_chunks, ctx_pos,
                      ctx_len, max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows,
-                     sm_scale, out, ws, ws_bytes, stream);
+                     sm_scale, out, nullptr, ws, ws_bytes, stream);
 }

@@ -1,0 +1,683 @@
+// Backward of the Stage 3 sparse attention (training-time path).
+// (Paper note 核心方法 > 训练 and README Abstract: the MSA layer is trained end
+//  to end; the selection is held fixed and the gradients reach the query, the
+//  local K/V and the selected pooled rows, summed over every query and
+//  context entry that reads a row.)
+//
+// The forward is recomputed (its kernels, with the per-row base-2
+// log-sum-exp), then per query row D = <dO, O>.  With P = softmax of the
+// scaled logits, dP = dO V^T and dS = P * (dP - D):
+//   dV = P^T dO,  dK_rot = scale dS^T Q_rot,  dQ_rot = scale dS K_rot,
+// and a rotation's adjoint is the rotation by the opposite angle.
+//
+// bf16, d = 128 (MFMA): the rotated query scaled by scale * log2(e) and dO
+// are staged once as bf16 rows.  dK/dV: one wave per 16-key tile holds its
+// rotated K and V as MFMA operands and walks every query row tile of its
+// head (rows staged in LDS per tile): S and dP come from
+// v_mfma_f32_16x16x32_bf16, and P, dS leave the accumulator in exactly the
+// B-operand order of v_mfma_f32_16x16x16bf16_1k, whose A operand (dO^T or
+// Q^T) is read with LDS transpose loads.  dQ: one wave per 16-row tile over a
+// key split, like the forward prefill; partial sums per split are added and
+// turned back by the query's rotation in a last pass.
+#include "attn_common.h"
+
+namespace msa {
+
+constexpr int BW_WAVES = 4;
+constexpr int BW_THREADS = 64 * BW_WAVES;
+constexpr float BW_LOG2E = 1.4426950408889634f;
+
+// A operand of a 16x16x16 product from a row-major bf16 tile (16 rows, row
+// stride AT_VS): lane (lc, g4) receives tile[4*g4 + r][16*dt + lc], r = 0..3
+// (the first of pv_operand's two transpose reads).
+__device__ __forceinline__ v4s tr_operand4(const unsigned char* tile, int dt, int lane) {
+  const int g4 = lane / 16, j = lane % 16;
+  const int r = j / 4, q = j % 4;
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(tile + (4 * g4 + r) * AT_VS + (16 * dt + 4 * q) * 2));
+}
+
+__device__ __forceinline__ v4s pack4(float a, float b, float c, float d) {
+  return __builtin_bit_cast(v4s, make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d)));
+}
+
+// Source row and position of key j of query b (context entries first, then
+// the local tokens); rows are clamped into their tensor.
+struct BwKey {
+  int64_t row;
+  int pos;
+  bool local, valid;
+};
+__device__ __forceinline__ BwKey bw_key(int j, int b, int ctxl, int n_keys, int max_ctx, int L_loc, int qpo,
+                                        const int32_t* __restrict__ ctx_pos, int P, const int32_t* __restrict__ ctx_row,
+                                        int64_t ctx_rows) {
+  BwKey k;
+  k.valid = j >= 0 && j < n_keys;
+  k.local = j >= ctxl;
+  if (!k.local) {
+    const int64_t e = int64_t(b) * max_ctx + j;
+    k.row = ctx_src_row(e, ctx_row, ctx_rows);
+    const int p = ctx_pos[e];
+    k.pos = p < 0 ? 0 : (p >= P ? P - 1 : p);
+  } else {
+    const int li = min(max(j - ctxl, 0), L_loc - 1);
+    k.row = int64_t(b) * L_loc + li;
+    k.pos = qpo + li;
+  }
+  return k;
+}
+
+// ---------------------------------------------------------------- row preparation
+// One wave per query row (b, t, hq): D = <dO, O>; for the MFMA path also the
+// bf16 rows of dO and of the rotated query times scale * log2(e) (rotated in
+// float32, rounded once, as the forward does).
+template <int DT, bool MF>
+__global__ __launch_bounds__(BW_THREADS) void bwd_prep_kernel(
+    const typename Elem<DT>::T* __restrict__ q, int T, int Hq, int d, int L_loc, int qpo, const float2* __restrict__ tab,
+    int P, float qscale, const float* __restrict__ out, const float* __restrict__ dout, int64_t rows,
+    float* __restrict__ Dv, uint16_t* __restrict__ qs16, uint16_t* __restrict__ do16) {
+  const int64_t r = int64_t(blockIdx.x) * BW_WAVES + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  if (r >= rows) return;
+  float acc = 0.f;
+  for (int e = lane; e < d; e += 64) acc += out[r * d + e] * dout[r * d + e];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (lane == 0) Dv[r] = acc;
+  if (!MF) return;
+  const int t = int((r / Hq) % T);
+  int pq = qpo + L_loc - T + t;
+  pq = pq < 0 ? 0 : (pq >= P ? P - 1 : pq);
+  const int half = d / 2;
+  for (int m = lane; m < half; m += 64) {
+    const float a = Elem<DT>::load(q + r * d, m), bb = Elem<DT>::load(q + r * d, m + half);
+    const float2 cs = tab[int64_t(pq) * half + m];
+    qs16[r * d + m] = f32_to_bf16((a * cs.x - bb * cs.y) * qscale);
+    qs16[r * d + m + half] = f32_to_bf16((bb * cs.x + a * cs.y) * qscale);
+  }
+  for (int e = lane; e < d; e += 64) do16[r * d + e] = f32_to_bf16(dout[r * d + e]);
+}
+
+// ---------------------------------------------------------------- dK, dV (MFMA)
+template <int G>
+__global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(
+    int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_bar, const uint16_t* __restrict__ v_bar,
+    int64_t ctx_rows, const int32_t* __restrict__ ctx_row, const int32_t* __restrict__ ctx_pos,
+    const int32_t* __restrict__ ctx_len, int max_ctx, const uint16_t* __restrict__ k_loc,
+    const uint16_t* __restrict__ v_loc, int L_loc, int qpo, const float2* __restrict__ tab, int P,
+    const uint16_t* __restrict__ qs16, const uint16_t* __restrict__ do16, const float* __restrict__ lse,
+    const float* __restrict__ Dv, int n_kb, float* __restrict__ dk_loc, float* __restrict__ dv_loc,
+    float* __restrict__ dk_bar, float* __restrict__ dv_bar) {
+  __shared__ __attribute__((aligned(16))) unsigned char qt[16 * AT_VS];
+  __shared__ __attribute__((aligned(16))) unsigned char dt_[16 * AT_VS];
+  __shared__ float slse[16], sD[16];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int lc = lane % 16, g4 = lane / 16;
+  int64_t wg = blockIdx.x;
+  const int kb = int(wg % n_kb);
+  wg /= n_kb;
+  const int g = int(wg % Hkv);
+  const int b = int(wg / Hkv);
+  const int ctxl = min(max(ctx_len[b], 0), max_ctx);
+  const int n_keys = ctxl + L_loc;
+  const int j0 = (kb * BW_WAVES + wave) * 16;       // this wave's 16 keys
+  const int R = T * G;                               // query rows of this KV head
+  const int n_rt = (R + 15) / 16;
+
+  // the lane's key (column lc of every product) as rotated K and as V
+  const BwKey kl = bw_key(j0 + lc, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows);
+  uint4 kr[4], vr[4];
+  {
+    const uint16_t* kp = (kl.local ? k_loc : k_bar) + (kl.row * Hkv + g) * AT_D + 8 * g4;
+    const uint16_t* vp = (kl.local ? v_loc : v_bar) + (kl.row * Hkv + g) * AT_D + 8 * g4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      kr[kk] = kl.valid ? load_global(kp + 32 * kk) : make_uint4(0, 0, 0, 0);
+      vr[kk] = kl.valid ? load_global(vp + 32 * kk) : make_uint4(0, 0, 0, 0);
+    }
+    rope_rotate(kr, tab + int64_t(kl.pos) * (AT_D / 2), g4);
+  }
+  const bool wave_live = j0 < n_keys;
+  f32x4 dkT[8], dvT[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    dkT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dvT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int srow = tid / 16, scol = tid % 16;       // staging: one 16-byte piece per thread and tile
+  for (int rt = 0; rt < n_rt; ++rt) {
+    {
+      const int r = rt * 16 + srow;
+      uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
+      if (r < R) {
+        const int64_t grow = (int64_t(b) * T + r / G) * Hq + g * G + r % G;
+        a = load_global(qs16 + grow * AT_D + 8 * scol);
+        c = load_global(do16 + grow * AT_D + 8 * scol);
+      }
+      *reinterpret_cast<uint4*>(qt + srow * AT_VS + 16 * scol) = a;
+      *reinterpret_cast<uint4*>(dt_ + srow * AT_VS + 16 * scol) = c;
+      if (tid < 16) {
+        const int r2 = rt * 16 + tid;
+        const int64_t grow = (int64_t(b) * T + r2 / G) * Hq + g * G + r2 % G;
+        slse[tid] = r2 < R ? lse[grow] : INFINITY;
+        sD[tid] = r2 < R ? Dv[grow] : 0.f;
+      }
+    }
+    __syncthreads();
+    // rows of this tile see key j iff j < ctxl or j - ctxl <= L_loc - T + t
+    const int t_max = min(rt * 16 + 15, R - 1) / G;
+    if (wave_live && !(j0 >= ctxl && j0 - ctxl > L_loc - T + t_max)) {
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 qa = *reinterpret_cast<const uint4*>(qt + lc * AT_VS + 64 * kk + 16 * g4);
+        const uint4 da = *reinterpret_cast<const uint4*>(dt_ + lc * AT_VS + 64 * kk + 16 * g4);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa), __builtin_bit_cast(bf16x8, kr[kk]), s,
+                                                    0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, da), __builtin_bit_cast(bf16x8, vr[kk]),
+                                                     dp, 0, 0, 0);
+      }
+      // lane (lc, g4) holds S and dP at row 4*g4 + i, key lc
+      float p[4], ds[4];
+      const int j = j0 + lc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * g4 + i, r = rt * 16 + rr;
+        const bool vis = kl.valid && r < R && (j < ctxl || j - ctxl <= L_loc - T + r / G);
+        p[i] = vis ? __builtin_amdgcn_exp2f(s[i] - slse[rr]) : 0.f;
+        ds[i] = p[i] * (dp[i] - sD[rr]);
+      }
+      const v4s pb = pack4(p[0], p[1], p[2], p[3]);
+      const v4s sb = pack4(ds[0], ds[1], ds[2], ds[3]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        dvT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tr_operand4(dt_, dt, lane), pb, dvT[dt], 0, 0, 0);
+        dkT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tr_operand4(qt, dt, lane), sb, dkT[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  if (!kl.valid) return;
+  // lane holds dK_rot^T, dV^T at dims e = 16*dt + 4*g4 + i of key lc; the
+  // query rows carried scale * log2(e), so dK_rot = sum(dS q_s) / log2(e)
+  const float2* cs = tab + int64_t(kl.pos) * (AT_D / 2);
+  float dk[8][4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float2 c = cs[16 * dt + 4 * g4 + i];
+      const float a = dkT[dt][i] * (1.f / BW_LOG2E), bb = dkT[dt + 4][i] * (1.f / BW_LOG2E);
+      dk[dt][i] = a * c.x + bb * c.y;          // the inverse rotation
+      dk[dt + 4][i] = bb * c.x - a * c.y;
+    }
+  }
+  if (kl.local) {
+    float* kd = dk_loc + (kl.row * Hkv + g) * AT_D;
+    float* vd = dv_loc + (kl.row * Hkv + g) * AT_D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      *reinterpret_cast<float4*>(kd + 16 * dt + 4 * g4) = make_float4(dk[dt][0], dk[dt][1], dk[dt][2], dk[dt][3]);
+      *reinterpret_cast<float4*>(vd + 16 * dt + 4 * g4) = make_float4(dvT[dt][0], dvT[dt][1], dvT[dt][2], dvT[dt][3]);
+    }
+  } else {   // a pooled row may be read by several queries
+    float* kd = dk_bar + (kl.row * Hkv + g) * AT_D;
+    float* vd = dv_bar + (kl.row * Hkv + g) * AT_D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        unsafeAtomicAdd(kd + 16 * dt + 4 * g4 + i, dk[dt][i]);
+        unsafeAtomicAdd(vd + 16 * dt + 4 * g4 + i, dvT[dt][i]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dQ (MFMA)
+// One wave per 16-row tile of a KV head, four tiles per workgroup, over one
+// key split; each 32-key step stages the rotated K and V rows in LDS.
+constexpr int BQ_KV_BYTES = 32 * AT_VS;
+
+template <int G>
+__global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(
+    int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_bar, const uint16_t* __restrict__ v_bar,
+    int64_t ctx_rows, const int32_t* __restrict__ ctx_row, const int32_t* __restrict__ ctx_pos,
+    const int32_t* __restrict__ ctx_len, int max_ctx, const uint16_t* __restrict__ k_loc,
+    const uint16_t* __restrict__ v_loc, int L_loc, int qpo, const float2* __restrict__ tab, int P,
+    const uint16_t* __restrict__ qs16, const uint16_t* __restrict__ do16, const float* __restrict__ lse,
+    const float* __restrict__ Dv, int n_rg, int n_splits, float* __restrict__ ws_dq) {
+  __shared__ __attribute__((aligned(16))) unsigned char kt[BQ_KV_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[BQ_KV_BYTES];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int lc = lane % 16, g4 = lane / 16;
+  int64_t wg = blockIdx.x;
+  const int split = int(wg % n_splits);
+  wg /= n_splits;
+  const int rg = int(wg % n_rg);
+  wg /= n_rg;
+  const int g = int(wg % Hkv);
+  const int b = int(wg / Hkv);
+  const int ctxl = min(max(ctx_len[b], 0), max_ctx);
+  const int n_keys = ctxl + L_loc;
+  const int R = T * G;
+  const int r = (rg * BW_WAVES + wave) * 16 + lc;   // this lane's query row (column lc)
+  const bool rok = r < R;
+  const int t = rok ? r / G : 0;
+  const int64_t grow = (int64_t(b) * T + t) * Hq + g * G + (rok ? r % G : 0);
+  const int horizon = L_loc - T + t;
+  uint4 qb[4], db[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    qb[kk] = rok ? load_global(qs16 + grow * AT_D + 32 * kk + 8 * g4) : make_uint4(0, 0, 0, 0);
+    db[kk] = rok ? load_global(do16 + grow * AT_D + 32 * kk + 8 * g4) : make_uint4(0, 0, 0, 0);
+  }
+  const float l2 = rok ? lse[grow] : INFINITY;
+  const float Dr = rok ? Dv[grow] : 0.f;
+  f32x4 dqT[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) dqT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kps = ((n_keys + n_splits - 1) / n_splits + 31) / 32 * 32;
+  const int j_begin = split * kps;
+  const int j_end = min(n_keys, j_begin + kps);
+  // staging: 16 keys per pass of the workgroup, thread (key lk, 4-dim block lx)
+  const int lk = tid / 16, lx = tid % 16;
+  for (int j0 = j_begin; j0 < j_end; j0 += 32) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int key = 16 * half + lk;
+      const BwKey ks = bw_key(j0 + key, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows);
+      const uint16_t* kp = (ks.local ? k_loc : k_bar) + (ks.row * Hkv + g) * AT_D;
+      const uint16_t* vp = (ks.local ? v_loc : v_bar) + (ks.row * Hkv + g) * AT_D;
+      const uint2 klo = load_global8(kp + 4 * lx), khi = load_global8(kp + 64 + 4 * lx);
+      const uint4 v = load_global(vp + 8 * lx);
+      const float4 c0 = reinterpret_cast<const float4*>(tab + int64_t(ks.pos) * (AT_D / 2) + 4 * lx)[0];
+      const float4 c1 = reinterpret_cast<const float4*>(tab + int64_t(ks.pos) * (AT_D / 2) + 4 * lx)[1];
+      const float c[4] = {c0.x, c0.z, c1.x, c1.z}, sn[4] = {c0.y, c0.w, c1.y, c1.w};
+      const float a[4] = {__uint_as_float(klo.x << 16), __uint_as_float(klo.x & 0xFFFF0000u),
+                          __uint_as_float(klo.y << 16), __uint_as_float(klo.y & 0xFFFF0000u)};
+      const float bb[4] = {__uint_as_float(khi.x << 16), __uint_as_float(khi.x & 0xFFFF0000u),
+                           __uint_as_float(khi.y << 16), __uint_as_float(khi.y & 0xFFFF0000u)};
+      float ra[4], rb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ra[e] = a[e] * c[e] - bb[e] * sn[e];
+        rb[e] = bb[e] * c[e] + a[e] * sn[e];
+      }
+      unsigned char* krow = kt + key * AT_VS;
+      *reinterpret_cast<uint2*>(krow + 8 * lx) = make_uint2(pack_bf16x2(ra[0], ra[1]), pack_bf16x2(ra[2], ra[3]));
+      *reinterpret_cast<uint2*>(krow + 128 + 8 * lx) = make_uint2(pack_bf16x2(rb[0], rb[1]), pack_bf16x2(rb[2], rb[3]));
+      *reinterpret_cast<uint4*>(vt + key * AT_VS + 16 * lx) = v;
+    }
+    __syncthreads();
+    float dsv[2][4];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(kt + (16 * tau + lc) * AT_VS + 64 * kk + 16 * g4);
+        const uint4 va = *reinterpret_cast<const uint4*>(vt + (16 * tau + lc) * AT_VS + 64 * kk + 16 * g4);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qb[kk]), s,
+                                                    0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, db[kk]),
+                                                     dp, 0, 0, 0);
+      }
+      // lane (lc, g4): key 16*tau + 4*g4 + i, row lc
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 16 * tau + 4 * g4 + i;
+        const bool vis = rok && j < j_end && (j < ctxl || j - ctxl <= horizon);
+        const float p = vis ? __builtin_amdgcn_exp2f(s[i] - l2) : 0.f;
+        dsv[tau][i] = p * (dp[i] - Dr);
+      }
+    }
+    const bf16x8 sb = __builtin_bit_cast(
+        bf16x8, make_uint4(pack_bf16x2(dsv[0][0], dsv[0][1]), pack_bf16x2(dsv[0][2], dsv[0][3]),
+                           pack_bf16x2(dsv[1][0], dsv[1][1]), pack_bf16x2(dsv[1][2], dsv[1][3])));
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      dqT[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pv_operand(kt, dt, lane), sb, dqT[dt], 0, 0, 0);
+    __syncthreads();
+  }
+  if (!rok) return;
+  float* op = ws_dq + (int64_t(split) * B * T * Hq + grow) * AT_D;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<float4*>(op + 16 * dt + 4 * g4) = make_float4(dqT[dt][0], dqT[dt][1], dqT[dt][2], dqT[dt][3]);
+}
+
+// dq = R(-pos_q) (scale * sum over splits of the partial dQ_rot), one thread per (row, pair m)
+__global__ void attn_bwd_dq_sum_kernel(const float* __restrict__ ws_dq, int n_splits, int64_t rows, int T, int Hq,
+                                       int d, int L_loc, int qpo, const float2* __restrict__ tab, int P, float scale,
+                                       float* __restrict__ dq) {
+  const int half = d / 2;
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= rows * half) return;
+  const int64_t r = i / half;
+  const int m = int(i % half);
+  float a = 0.f, bb = 0.f;
+  for (int s = 0; s < n_splits; ++s) {
+    a += ws_dq[(s * rows + r) * d + m];
+    bb += ws_dq[(s * rows + r) * d + m + half];
+  }
+  a *= scale;
+  bb *= scale;
+  const int t = int((r / Hq) % T);
+  int pq = qpo + L_loc - T + t;
+  pq = pq < 0 ? 0 : (pq >= P ? P - 1 : pq);
+  const float2 c = tab[int64_t(pq) * half + m];
+  dq[r * d + m] = a * c.x + bb * c.y;
+  dq[r * d + m + half] = bb * c.x - a * c.y;
+}
+
+// ---------------------------------------------------------------- vector path
+// float32 or any even d: dQ one workgroup per query row, dK/dV one
+// workgroup per (query, KV head, key); float32 arithmetic throughout.
+template <int DT>
+__device__ __forceinline__ float rot_dot(const typename Elem<DT>::T* kp, const float2* cs, const float* qr, int half,
+                                         int lo, int step) {
+  float dot = 0.f;
+  for (int m = lo; m < half; m += step) {
+    const float k1 = Elem<DT>::load(kp, m), k2 = Elem<DT>::load(kp, m + half);
+    const float2 c = cs[m];
+    dot += qr[m] * (k1 * c.x - k2 * c.y) + qr[m + half] * (k2 * c.x + k1 * c.y);
+  }
+  return dot;
+}
+
+template <int DT>
+__global__ __launch_bounds__(AT_VEC_THREADS) void attn_bwd_vec_dq_kernel(
+    const typename Elem<DT>::T* __restrict__ q, int B, int T, int Hq, int Hkv, int d,
+    const typename Elem<DT>::T* __restrict__ k_bar, const typename Elem<DT>::T* __restrict__ v_bar, int64_t ctx_rows,
+    const int32_t* __restrict__ ctx_row, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
+    int max_ctx, const typename Elem<DT>::T* __restrict__ k_loc, const typename Elem<DT>::T* __restrict__ v_loc,
+    int L_loc, int qpo, const float2* __restrict__ tab, int P, float sm_scale, const float* __restrict__ lse,
+    const float* __restrict__ Dv, const float* __restrict__ dout, float* __restrict__ dq) {
+  using E = Elem<DT>;
+  extern __shared__ float bsm[];
+  float* qr = bsm;                  // [d] rotated query
+  float* red = bsm + d;             // [AT_VEC_THREADS]
+  float* dsv = red + AT_VEC_THREADS;   // [n_keys]
+  const int64_t row = blockIdx.x;
+  const int hq = int(row % Hq), t = int((row / Hq) % T), b = int(row / (int64_t(Hq) * T));
+  const int G = Hq / Hkv, g = hq / G, half = d / 2;
+  const int horizon = L_loc - T + t;
+  int pq = qpo + L_loc - T + t;
+  pq = pq < 0 ? 0 : (pq >= P ? P - 1 : pq);
+  for (int m = threadIdx.x; m < half; m += AT_VEC_THREADS) {
+    const float a = E::load(q + row * d, m), bb = E::load(q + row * d, m + half);
+    const float2 c = tab[int64_t(pq) * half + m];
+    qr[m] = a * c.x - bb * c.y;
+    qr[m + half] = bb * c.x + a * c.y;
+  }
+  __syncthreads();
+  const int ctxl = min(max(ctx_len[b], 0), max_ctx);
+  const int n_keys = ctxl + L_loc;
+  const float l_nat = lse[row] * (1.f / BW_LOG2E), D = Dv[row];
+  for (int j = threadIdx.x; j < n_keys; j += AT_VEC_THREADS) {
+    const BwKey ks = bw_key(j, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows);
+    float ds = 0.f;
+    if (!ks.local || int(ks.row - int64_t(b) * L_loc) <= horizon) {
+      const typename E::T* kp = (ks.local ? k_loc : k_bar) + (ks.row * Hkv + g) * d;
+      const typename E::T* vp = (ks.local ? v_loc : v_bar) + (ks.row * Hkv + g) * d;
+      const float p = expf(rot_dot<DT>(kp, tab + int64_t(ks.pos) * half, qr, half, 0, 1) * sm_scale - l_nat);
+      float dp = 0.f;
+      for (int e = 0; e < d; ++e) dp += dout[row * d + e] * E::load(vp, e);
+      ds = p * (dp - D);
+    }
+    dsv[j] = ds;
+  }
+  __syncthreads();
+  for (int m = threadIdx.x; m < half; m += AT_VEC_THREADS) {
+    float a = 0.f, bb = 0.f;
+    for (int j = 0; j < n_keys; ++j) {
+      const float ds = dsv[j];
+      if (ds == 0.f) continue;
+      const BwKey ks = bw_key(j, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows);
+      const typename E::T* kp = (ks.local ? k_loc : k_bar) + (ks.row * Hkv + g) * d;
+      const float2 c = tab[int64_t(ks.pos) * half + m];
+      const float k1 = E::load(kp, m), k2 = E::load(kp, m + half);
+      a += ds * (k1 * c.x - k2 * c.y);
+      bb += ds * (k2 * c.x + k1 * c.y);
+    }
+    a *= sm_scale;
+    bb *= sm_scale;
+    const float2 c = tab[int64_t(pq) * half + m];
+    dq[row * d + m] = a * c.x + bb * c.y;
+    dq[row * d + m + half] = bb * c.x - a * c.y;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(AT_VEC_THREADS) void attn_bwd_vec_dkdv_kernel(
+    const typename Elem<DT>::T* __restrict__ q, int B, int T, int Hq, int Hkv, int d,
+    const typename Elem<DT>::T* __restrict__ k_bar, const typename Elem<DT>::T* __restrict__ v_bar, int64_t ctx_rows,
+    const int32_t* __restrict__ ctx_row, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
+    int max_ctx, const typename Elem<DT>::T* __restrict__ k_loc, const typename Elem<DT>::T* __restrict__ v_loc,
+    int L_loc, int qpo, const float2* __restrict__ tab, int P, float sm_scale, const float* __restrict__ lse,
+    const float* __restrict__ Dv, const float* __restrict__ dout, int n_keys_max, float* __restrict__ dk_loc,
+    float* __restrict__ dv_loc, float* __restrict__ dk_bar, float* __restrict__ dv_bar) {
+  using E = Elem<DT>;
+  extern __shared__ float bsm[];
+  float* kr = bsm;                  // [d] rotated key
+  float* pr = bsm + d;              // [T * G] p of each row
+  float* dr = pr + T * (Hq / Hkv);  // [T * G] ds of each row
+  const int64_t wg = blockIdx.x;
+  const int j = int(wg % n_keys_max);
+  const int g = int((wg / n_keys_max) % Hkv);
+  const int b = int(wg / (int64_t(n_keys_max) * Hkv));
+  const int G = Hq / Hkv, half = d / 2, R = T * G;
+  const int ctxl = min(max(ctx_len[b], 0), max_ctx);
+  const int n_keys = ctxl + L_loc;
+  if (j >= n_keys) return;
+  const BwKey ks = bw_key(j, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows);
+  const typename E::T* kp = (ks.local ? k_loc : k_bar) + (ks.row * Hkv + g) * d;
+  const typename E::T* vp = (ks.local ? v_loc : v_bar) + (ks.row * Hkv + g) * d;
+  const float2* kcs = tab + int64_t(ks.pos) * half;
+  for (int m = threadIdx.x; m < half; m += AT_VEC_THREADS) {
+    const float k1 = E::load(kp, m), k2 = E::load(kp, m + half);
+    kr[m] = k1 * kcs[m].x - k2 * kcs[m].y;
+    kr[m + half] = k2 * kcs[m].x + k1 * kcs[m].y;
+  }
+  __syncthreads();
+  const int li = j - ctxl;
+  for (int r = threadIdx.x; r < R; r += AT_VEC_THREADS) {
+    const int t = r / G, hq = g * G + r % G;
+    const int64_t row = (int64_t(b) * T + t) * Hq + hq;
+    float p = 0.f, ds = 0.f;
+    if (j < ctxl || li <= L_loc - T + t) {
+      int pq = qpo + L_loc - T + t;
+      pq = pq < 0 ? 0 : (pq >= P ? P - 1 : pq);
+      const float2* qcs = tab + int64_t(pq) * half;
+      float dot = 0.f;
+      for (int m = 0; m < half; ++m) {
+        const float a = E::load(q + row * d, m), bb = E::load(q + row * d, m + half);
+        dot += (a * qcs[m].x - bb * qcs[m].y) * kr[m] + (bb * qcs[m].x + a * qcs[m].y) * kr[m + half];
+      }
+      p = expf(dot * sm_scale - lse[row] * (1.f / BW_LOG2E));
+      float dp = 0.f;
+      for (int e = 0; e < d; ++e) dp += dout[row * d + e] * E::load(vp, e);
+      ds = p * (dp - Dv[row]);
+    }
+    pr[r] = p;
+    dr[r] = ds;
+  }
+  __syncthreads();
+  for (int m = threadIdx.x; m < half; m += AT_VEC_THREADS) {
+    float a = 0.f, bb = 0.f, va = 0.f, vb = 0.f;
+    for (int r = 0; r < R; ++r) {
+      const int t = r / G, hq = g * G + r % G;
+      const int64_t row = (int64_t(b) * T + t) * Hq + hq;
+      va += pr[r] * dout[row * d + m];
+      vb += pr[r] * dout[row * d + m + half];
+      const float ds = dr[r];
+      if (ds == 0.f) continue;
+      int pq = qpo + L_loc - T + t;
+      pq = pq < 0 ? 0 : (pq >= P ? P - 1 : pq);
+      const float2 c = tab[int64_t(pq) * half + m];
+      const float x = E::load(q + row * d, m), y = E::load(q + row * d, m + half);
+      a += ds * (x * c.x - y * c.y);
+      bb += ds * (y * c.x + x * c.y);
+    }
+    a *= sm_scale;
+    bb *= sm_scale;
+    const float2 c = kcs[m];
+    const float ka = a * c.x + bb * c.y, kb = bb * c.x - a * c.y;
+    if (ks.local) {
+      const int64_t o = (ks.row * Hkv + g) * d;
+      dk_loc[o + m] = ka;
+      dk_loc[o + m + half] = kb;
+      dv_loc[o + m] = va;
+      dv_loc[o + m + half] = vb;
+    } else {
+      const int64_t o = (ks.row * Hkv + g) * d;
+      unsafeAtomicAdd(dk_bar + o + m, ka);
+      unsafeAtomicAdd(dk_bar + o + m + half, kb);
+      unsafeAtomicAdd(dv_bar + o + m, va);
+      unsafeAtomicAdd(dv_bar + o + m + half, vb);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- plan
+struct BwdPlan {
+  bool mfma;
+  size_t fwd_bytes, out_bytes, row_bytes, bf_bytes, dq_bytes;
+  int n_rg, n_splits, n_kb;
+};
+
+static BwdPlan bwd_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc, int qpo) {
+  BwdPlan p{};
+  const int G = Hq / Hkv;
+  p.mfma = dtype == MSA_BF16 && d == AT_D && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+  p.fwd_bytes = align_up(msa_sparse_attn_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, qpo), 256);
+  const int64_t rows = int64_t(B) * T * Hq;
+  p.out_bytes = align_up(size_t(rows) * d * 4, 256);
+  p.row_bytes = align_up(size_t(rows) * 4, 256);                // lse, D
+  p.bf_bytes = p.mfma ? align_up(size_t(rows) * d * 2, 256) : 0;  // qs16, do16
+  if (p.mfma) {
+    const int n_rt = (T * G + 15) / 16;
+    p.n_rg = (n_rt + BW_WAVES - 1) / BW_WAVES;
+    const int64_t units = int64_t(B) * Hkv * p.n_rg;
+    const int64_t n_keys_max = int64_t(max_ctx) + L_loc;
+    int64_t s = (256 + units - 1) / units;
+    s = std::max<int64_t>(1, std::min<int64_t>(s, (n_keys_max + 127) / 128));
+    p.n_splits = int(s);
+    p.dq_bytes = align_up(size_t(p.n_splits) * rows * d * 4, 256);
+    p.n_kb = int((n_keys_max + 16 * BW_WAVES - 1) / (16 * BW_WAVES));
+  }
+  return p;
+}
+
+}  // namespace msa
+
+extern "C" size_t msa_sparse_attn_backward_workspace(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx,
+                                                     int L_loc, int q_pos_offset) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 2 || max_ctx < 0 || L_loc < 1 || q_pos_offset < 0 || Hq % Hkv)
+    return 0;
+  const msa::BwdPlan p = msa::bwd_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
+  return p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes + p.dq_bytes;
+}
+
+extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
+                                        const void* k_bar, const void* v_bar, int64_t n_chunks, const int32_t* ctx_row,
+                                        const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx,
+                                        const void* k_loc, const void* v_loc, int L_loc, int q_pos_offset,
+                                        float rope_base, const float* rope_table, int rope_table_rows, float sm_scale,
+                                        const float* dout, float* dq, float* dk_loc, float* dv_loc, float* dk_bar,
+                                        float* dv_bar, void* ws, size_t ws_bytes, void* stream) {
+  using namespace msa;
+  const std::string fn = "msa_sparse_attn_backward";
+  MSA_REQUIRE(ctx_row && dout && dq && dk_loc && dv_loc && dk_bar && dv_bar, MSA_ERR_INVALID_ARG,
+              fn + ": NULL pointer");
+  MSA_REQUIRE(n_chunks >= 1 && n_chunks <= INT32_MAX, MSA_ERR_INVALID_ARG, fn + ": n_chunks must lie in [1, 2^31)");
+  MSA_REQUIRE(B >= 1 && T >= 1 && Hq >= 1 && Hkv >= 1 && d >= 2 && max_ctx >= 1 && L_loc >= 1 && Hq % Hkv == 0,
+              MSA_ERR_INVALID_ARG, fn + ": bad sizes");
+  const BwdPlan p = bwd_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
+  const size_t need = p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes + p.dq_bytes;
+  MSA_REQUIRE(ws && ws_bytes >= need, MSA_ERR_WORKSPACE, fn + ": workspace too small");
+  if (!p.mfma)
+    MSA_REQUIRE(size_t(d) + AT_VEC_THREADS + size_t(max_ctx) + L_loc <= 16384, MSA_ERR_UNSUPPORTED,
+                fn + ": too many keys for the vector path");
+  char* w = static_cast<char*>(ws);
+  float* out = reinterpret_cast<float*>(w + p.fwd_bytes);
+  float* lse = reinterpret_cast<float*>(w + p.fwd_bytes + p.out_bytes);
+  float* Dv = reinterpret_cast<float*>(w + p.fwd_bytes + p.out_bytes + p.row_bytes);
+  uint16_t* qs16 = reinterpret_cast<uint16_t*>(w + p.fwd_bytes + p.out_bytes + 2 * p.row_bytes);
+  uint16_t* do16 = reinterpret_cast<uint16_t*>(w + p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + p.bf_bytes);
+  float* ws_dq = reinterpret_cast<float*>(w + p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes);
+  // the forward (validates every shared argument) with the per-row log-sum-exp
+  const int rc = sparse_attn(fn, dtype, q, B, T, Hq, Hkv, d, k_bar, v_bar, ctx_row, n_chunks, ctx_pos, ctx_len,
+                             max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows,
+                             sm_scale, out, lse, ws, p.fwd_bytes, stream);
+  if (rc != MSA_OK) return rc;
+  hipStream_t s = as_stream(stream);
+  // the forward built the RoPE rows at the start of its workspace when none were given
+  const float2* tab = reinterpret_cast<const float2*>(rope_table ? rope_table : static_cast<const float*>(ws));
+  const int P = rope_rows(max_ctx, L_loc, q_pos_offset);
+  const int64_t rows = int64_t(B) * T * Hq;
+  const int G = Hq / Hkv;
+  const unsigned prep_grid = unsigned((rows + BW_WAVES - 1) / BW_WAVES);
+  if (p.mfma) {
+    hipLaunchKernelGGL((bwd_prep_kernel<MSA_BF16, true>), dim3(prep_grid), dim3(BW_THREADS), 0, s,
+                       static_cast<const uint16_t*>(q), T, Hq, d, L_loc, q_pos_offset, tab, P, sm_scale * BW_LOG2E,
+                       out, dout, rows, Dv, qs16, do16);
+    MSA_LAUNCH_CHECK();
+    const uint16_t* kb = static_cast<const uint16_t*>(k_bar);
+    const uint16_t* vb = static_cast<const uint16_t*>(v_bar);
+    const uint16_t* kl = static_cast<const uint16_t*>(k_loc);
+    const uint16_t* vl = static_cast<const uint16_t*>(v_loc);
+    const dim3 kgrid(unsigned(int64_t(B) * Hkv * p.n_kb)), qgrid(unsigned(int64_t(B) * Hkv * p.n_rg * p.n_splits));
+#define BW_LAUNCH(GV)                                                                                              \
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<GV>), kgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, kb, vb, n_chunks,   \
+                     ctx_row, ctx_pos, ctx_len, max_ctx, kl, vl, L_loc, q_pos_offset, tab, P, qs16, do16, lse, Dv, \
+                     p.n_kb, dk_loc, dv_loc, dk_bar, dv_bar);                                                      \
+  MSA_LAUNCH_CHECK();                                                                                              \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<GV>), qgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, kb, vb, n_chunks,     \
+                     ctx_row, ctx_pos, ctx_len, max_ctx, kl, vl, L_loc, q_pos_offset, tab, P, qs16, do16, lse, Dv, \
+                     p.n_rg, p.n_splits, ws_dq)
+    switch (G) {
+      case 1: BW_LAUNCH(1); break;
+      case 2: BW_LAUNCH(2); break;
+      case 4: BW_LAUNCH(4); break;
+      case 8: BW_LAUNCH(8); break;
+      default: BW_LAUNCH(16); break;
+    }
+#undef BW_LAUNCH
+    MSA_LAUNCH_CHECK();
+    const int64_t n = rows * (d / 2);
+    hipLaunchKernelGGL(attn_bwd_dq_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, ws_dq, p.n_splits,
+                       rows, T, Hq, d, L_loc, q_pos_offset, tab, P, sm_scale, dq);
+    MSA_LAUNCH_CHECK();
+    return MSA_OK;
+  }
+  const int n_keys_max = max_ctx + L_loc;
+  const size_t qsm = (size_t(d) + AT_VEC_THREADS + size_t(n_keys_max)) * sizeof(float);
+  const size_t ksm = (size_t(d) + 2 * size_t(T) * G) * sizeof(float);
+  MSA_REQUIRE(ksm <= 65536, MSA_ERR_UNSUPPORTED, fn + ": too many query rows for the vector path");
+#define BV_LAUNCH(DTV, TY)                                                                                          \
+  hipLaunchKernelGGL((bwd_prep_kernel<DTV, false>), dim3(prep_grid), dim3(BW_THREADS), 0, s,                        \
+                     static_cast<const TY*>(q), T, Hq, d, L_loc, q_pos_offset, tab, P, 0.f, out, dout, rows, Dv,    \
+                     nullptr, nullptr);                                                                             \
+  MSA_LAUNCH_CHECK();                                                                                               \
+  hipLaunchKernelGGL((attn_bwd_vec_dq_kernel<DTV>), dim3(unsigned(rows)), dim3(AT_VEC_THREADS), qsm, s,             \
+                     static_cast<const TY*>(q), B, T, Hq, Hkv, d, static_cast<const TY*>(k_bar),                    \
+                     static_cast<const TY*>(v_bar), n_chunks, ctx_row, ctx_pos, ctx_len, max_ctx,                   \
+                     static_cast<const TY*>(k_loc), static_cast<const TY*>(v_loc), L_loc, q_pos_offset, tab, P,     \
+                     sm_scale, lse, Dv, dout, dq);                                                                  \
+  MSA_LAUNCH_CHECK();                                                                                               \
+  hipLaunchKernelGGL((attn_bwd_vec_dkdv_kernel<DTV>), dim3(unsigned(int64_t(B) * Hkv * n_keys_max)),                \
+                     dim3(AT_VEC_THREADS), ksm, s, static_cast<const TY*>(q), B, T, Hq, Hkv, d,                     \
+                     static_cast<const TY*>(k_bar), static_cast<const TY*>(v_bar), n_chunks, ctx_row, ctx_pos,      \
+                     ctx_len, max_ctx, static_cast<const TY*>(k_loc), static_cast<const TY*>(v_loc), L_loc,         \
+                     q_pos_offset, tab, P, sm_scale, lse, Dv, dout, n_keys_max, dk_loc, dv_loc, dk_bar, dv_bar)
+  if (dtype == MSA_BF16) {
+    BV_LAUNCH(MSA_BF16, uint16_t);
+  } else {
+    BV_LAUNCH(MSA_F32, float);
+  }
+#undef BV_LAUNCH
+  MSA_LAUNCH_CHECK();
+  return MSA_OK;
+}

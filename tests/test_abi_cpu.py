@@ -123,6 +123,20 @@ def test_training_path_validation():
     assert L.msa_pool_backward(1, None, P, P, P, 4, 100, 8, 8, 128, 64, None, P, None) == 1
 
 
+def test_sparse_attn_backward_validation():
+    L = M.lib
+    F = ctypes.c_float
+
+    def call(dk_bar=P, n_chunks=80, wsb=1 << 30, Hkv=8):
+        return L.msa_sparse_attn_backward(1, P, 1, 16, 32, Hkv, 128, P, P, n_chunks, P, P, P, 32, P, P, 64, 4,
+                                          F(1e6), None, 0, F(0.088), P, P, P, P, dk_bar, P, P, wsb, None)
+    assert call(dk_bar=None) == 1
+    assert call(n_chunks=0) == 1
+    assert call(Hkv=7) == 1                         # Hq % Hkv != 0
+    assert call(wsb=16) == 3
+    assert M.msa_sparse_attn_backward_workspace(1, 1, 16, 32, 8, 128, 32, 64, 4) > 0
+
+
 def test_context_index_validation():
     L = M.lib
     #            ids B  k  chunk_off n_docs maxdc n_chunks max_ctx row pos len stream

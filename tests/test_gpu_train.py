@@ -181,3 +181,56 @@ def test_routing_training_chain():
     rdx = O.pool_backward(rdk, tok_off, chunk, x=x)
     for got, ref in ((host(dq), rdq), (host(dx), rdx)):
         assert np.abs(got - ref).max() <= 1e-3 * np.abs(ref).max()
+
+
+# ---------------------------------------------------------------- attention backward
+
+def _bwd_case(seed, B, T, Hq, Hkv, d, L_loc, n_docs, k, bf16, shared_ids=False):
+    r = np.random.default_rng(seed)
+    lens = r.integers(1, 9, size=n_docs) * 64 - r.integers(0, 40, size=n_docs)   # 1..8 chunks, partial last
+    chunk_off = O.chunk_offsets(synth.offsets(lens), 64)
+    n_chunks = int(chunk_off[-1])
+    kb = gen(seed, 0, synth.T_K, (n_chunks, Hkv, d), bf16, scale_pow2=-3)
+    vb = gen(seed, 0, synth.T_V, (n_chunks, Hkv, d), bf16, scale_pow2=-3)
+    q = gen(seed, 0, synth.T_Q, (B, T, Hq, d), bf16)
+    kl = gen(seed, 0, synth.T_KLOC, (B, L_loc, Hkv, d), bf16)
+    vl = gen(seed, 0, synth.T_VLOC, (B, L_loc, Hkv, d), bf16)
+    ids = np.stack([r.choice(n_docs, size=k, replace=False) for _ in range(B)]).astype(np.int32)
+    if shared_ids:
+        ids[1:] = ids[0]                       # every query reads the same rows: the row sums meet
+    dout = r.normal(size=(B, T, Hq, d)).astype(np.float32)
+    return chunk_off, n_chunks, kb, vb, q, kl, vl, ids, dout
+
+
+@pytest.mark.parametrize("bf16,B,T,Hq,Hkv,d,L_loc,k,shared", [
+    (True, 1, 16, 32, 8, 128, 64, 4, False),
+    (True, 2, 5, 32, 8, 128, 40, 3, True),       # 20 rows per head: a ragged row tile; shared rows
+    (True, 1, 64, 32, 8, 128, 300, 8, False),
+    (True, 3, 1, 16, 8, 128, 100, 5, True),      # decode-shaped rows, G = 2
+    (False, 2, 3, 8, 2, 32, 20, 3, True),        # the float32 vector path
+    (True, 1, 4, 6, 2, 64, 30, 2, False),        # bf16 vector path (d = 64, G = 3)
+])
+def test_sparse_attn_backward(bf16, B, T, Hq, Hkv, d, L_loc, k, shared):
+    qpo = k
+    chunk_off, n_chunks, kb, vb, q, kl, vl, ids, dout = _bwd_case(70 + T + B, B, T, Hq, Hkv, d, L_loc, 40, k, bf16,
+                                                                  shared)
+    max_doc = int(np.diff(chunk_off).max())
+    max_ctx = k * max_doc
+    co_d = to_dev_i64(chunk_off)
+    row, pos, ln = M.msa_context_index(torch.from_numpy(ids).to(dev()), co_d, n_chunks, max_doc, max_ctx)
+    dkb = torch.zeros((n_chunks, Hkv, d), dtype=torch.float32, device=dev())
+    dvb = torch.zeros_like(dkb)
+    dq, dkl, dvl, dkb, dvb = M.msa_sparse_attn_backward(
+        to_dev(q, bf16), to_dev(kb, bf16), to_dev(vb, bf16), row, pos, ln, to_dev(kl, bf16), to_dev(vl, bf16), qpo,
+        torch.from_numpy(dout).to(dev()), dkb, dvb)
+    ctx = [O.gather(ids[b], chunk_off, kb, vb) for b in range(B)]
+    rdq, cg, rdkl, rdvl = O.sparse_attention_backward(q, ctx, kl, vl, qpo, 1e6, dout.astype(np.float64))
+    rdkb, rdvb = O.gather_backward(ids, chunk_off, cg, n_chunks)
+    # bf16 operands (P, dS, dout, the rotated q and k) carry 2^-9 relative rounding each
+    tol = 1.5e-2 if bf16 else 1e-4
+    for name, got, ref in (("dq", dq, rdq), ("dk_loc", dkl, rdkl), ("dv_loc", dvl, rdvl), ("dk_bar", dkb, rdkb),
+                           ("dv_bar", dvb, rdvb)):
+        g = host(got)
+        err = np.abs(g - ref).max() / np.abs(ref).max()
+        print(f"{name}: normwise error {err:.3g}")
+        assert err <= tol, f"{name}: normwise error {err:.3g} > {tol}"
