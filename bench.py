@@ -52,6 +52,9 @@ def parse():
                          "262144 for token-level memories, whose sample the oracle also pools)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (the reference for the HBM byte counters)")
+    ap.add_argument("--train", action="store_true",
+                    help="time the training-time path instead (routing loss and attention backward per routed "
+                         "layer; --config defaults to train64k)")
     return ap.parse_args()
 
 
@@ -69,6 +72,8 @@ def main():
 
     if args.copy_calibration:
         return copy_calibration(torch)
+    if args.train:
+        return train_main(args, torch)
 
     import synth
     from synth import configs
@@ -336,6 +341,158 @@ def counted_traffic(preset_name):
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def train_main(args, torch):
+    """Training-time path, one step = every routed layer of one sample:
+    routing scores with their maximisers -> routing loss -> routing-score
+    backward -> top-k -> context index -> attention backward (forward
+    recomputed) -> pooling backward of the routing keys, K and V to the
+    tokens.  Inputs are seeded synthetic tensors; the output gradient of the
+    attention is a seeded synthetic tensor."""
+    import synth
+    from synth import configs
+    from synth import device as SD
+    import sparse_attention_long_msa_amd as M
+
+    name = "train64k" if args.config == "cfg4" else args.config
+    p = configs.TRAIN_PRESETS[name]()
+    layers = p.layers if args.layers is None else args.layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16
+    H, d, N, D, B, T, Hq, L, k = p.H, p.d, p.n_chunks, p.n_docs, p.B, p.T, p.Hq, p.L_loc, p.k
+    tau = 0.1
+    tok_off, chunk_off = p.tok_off, p.chunk_off
+    n_tok = int(tok_off[-1])
+    to_d = torch.from_numpy(tok_off).to(dev)
+    co_d = torch.from_numpy(chunk_off).to(dev)
+    cd = M.msa_chunk_doc_map(co_d, N)
+    t0 = time.time()
+    # token-level routing keys (kept: the pooling backward renormalises them), pooled stores
+    xr = [SD.fill(torch.empty((n_tok, H, d), dtype=bf, device=dev), p.seed, l, synth.T_KR) for l in range(layers)]
+    kr = [M.msa_pool_encode(xr[l], to_d, co_d, cd, p.chunk, True) for l in range(layers)]
+    raw = torch.empty((n_tok, H, d), dtype=bf, device=dev)
+    kbar, vbar = [], []
+    for l in range(layers):
+        kbar.append(M.msa_pool_encode(SD.fill(raw, p.seed, l, synth.T_K), to_d, co_d, cd, p.chunk, False))
+        vbar.append(M.msa_pool_encode(SD.fill(raw, p.seed, l, synth.T_V), to_d, co_d, cd, p.chunk, False))
+    del raw
+    qr = [SD.fill(torch.empty((B, T, H, d), dtype=bf, device=dev), p.qseed, l, synth.T_QR) for l in range(layers)]
+    qq = [SD.fill(torch.empty((B, T, Hq, d), dtype=bf, device=dev), p.qseed, l, synth.T_Q) for l in range(layers)]
+    kl = [SD.fill(torch.empty((B, L, H, d), dtype=bf, device=dev), p.qseed, l, synth.T_KLOC) for l in range(layers)]
+    vl = [SD.fill(torch.empty((B, L, H, d), dtype=bf, device=dev), p.qseed, l, synth.T_VLOC) for l in range(layers)]
+    dout = [SD.fill(torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev), p.qseed, l, synth.T_DOUT)
+            for l in range(layers)]
+    pos = torch.from_numpy(np.stack([synth.needle_docs(p.seed, D, p.n_needles, salt=b) for b in range(B)])
+                           .astype(np.int32)).to(dev)
+    max_doc = p.max_doc_chunks
+    max_ctx = k * max_doc
+    tab = M.msa_rope_table(M.msa_rope_table_rows(max_ctx, L, p.qpo), d, p.rope_base, device=dev)
+    # outputs and scratch, reused by every layer
+    f32 = dict(dtype=torch.float32, device=dev)
+    score, ac, at = (torch.empty((B, D), **f32), torch.empty((B, D), dtype=torch.int32, device=dev),
+                     torch.empty((B, D), dtype=torch.int32, device=dev))
+    ax_ws = torch.empty(M.msa_route_argmax_workspace(M.MSA_BF16, B, T, H, d, D, N), dtype=torch.uint8, device=dev)
+    loss = torch.empty((layers, B), **f32)
+    grad = torch.empty((B, D), **f32)
+    dqr = torch.empty((B, T, H, d), **f32)
+    dkr, dkb, dvb = (torch.empty((N, H, d), **f32) for _ in range(3))
+    ids, vals = torch.empty((B, k), dtype=torch.int32, device=dev), torch.empty((B, k), **f32)
+    tk_ws = torch.empty(max(M.msa_topk_workspace(B, D, k), 1), dtype=torch.uint8, device=dev)
+    row, cpos, clen = (torch.empty((B, max_ctx), dtype=torch.int32, device=dev),
+                       torch.empty((B, max_ctx), dtype=torch.int32, device=dev),
+                       torch.empty((B,), dtype=torch.int32, device=dev))
+    bw_ws = torch.empty(M.msa_sparse_attn_backward_workspace(M.MSA_BF16, B, T, Hq, H, d, max_ctx, L, p.qpo),
+                        dtype=torch.uint8, device=dev)
+    dq, dkl, dvl = (torch.empty((B, T, Hq, d), **f32), torch.empty((B, L, H, d), **f32),
+                    torch.empty((B, L, H, d), **f32))
+    dxr, dxk, dxv = (torch.empty((n_tok, H, d), **f32) for _ in range(3))
+    torch.cuda.synchronize()
+    log(f"{p.name}: {D} docs, {N} chunks/layer, {layers} layers, T={T}; inputs ready in {time.time() - t0:.1f} s")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for l in range(layers):
+            if ev is not None:
+                ev[l][0].record(stream)
+            M.msa_route_argmax(qr[l], kr[l], cd, D, doc_score=score, arg_chunk=ac, arg_tok=at, ws=ax_ws)
+            M.msa_route_loss(score, pos, tau, loss=loss[l], grad=grad)
+            dkr.zero_()
+            M.msa_route_score_backward(qr[l], kr[l], ac, at, grad, dkr, dq_r=dqr)
+            M.msa_topk(score, k, ids=ids, vals=vals, ws=tk_ws)
+            M.msa_context_index(ids, co_d, N, max_doc, max_ctx, ctx_row=row, ctx_pos=cpos, ctx_len=clen)
+            if ev is not None:
+                ev[l][1].record(stream)
+            dkb.zero_()
+            dvb.zero_()
+            M.msa_sparse_attn_backward(qq[l], kbar[l], vbar[l], row, cpos, clen, kl[l], vl[l], p.qpo, dout[l], dkb,
+                                       dvb, rope_base=p.rope_base, rope_table=tab, dq=dq, dk_loc=dkl, dv_loc=dvl,
+                                       ws=bw_ws)
+            if ev is not None:
+                ev[l][2].record(stream)
+            M.msa_pool_backward(dkr, to_d, co_d, cd, n_tok, p.chunk, x=xr[l], dx=dxr)
+            M.msa_pool_backward(dkb, to_d, co_d, cd, n_tok, p.chunk, dtype=M.MSA_BF16, dx=dxk)
+            M.msa_pool_backward(dvb, to_d, co_d, cd, n_tok, p.chunk, dtype=M.MSA_BF16, dx=dxv)
+            if ev is not None:
+                ev[l][3].record(stream)
+
+    step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    n_stage = min(args.steps, 3)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(layers)] for _ in range(n_stage)]
+    for s_ in range(n_stage):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    stage = np.zeros(3)
+    for s_ in range(n_stage):
+        for l in range(layers):
+            e = evs[s_][l]
+            stage += [e[i].elapsed_time(e[i + 1]) for i in range(3)]
+    stage /= n_stage
+    ms = wall * 1e3 / args.steps
+    # attention backward, per layer: visible (row, key) pairs x (4 d forward + 10 d backward) flops
+    ctx_len = int(clen.sum().item())
+    horizon = L - T + np.arange(T)
+    pairs = Hq * (B * T * (ctx_len // B) + B * int(np.minimum(horizon + 1, L).sum()))
+    attn_flops = pairs * 14 * d
+    attn_ms = stage[1] / layers
+    achieved = attn_flops / (attn_ms * 1e-3) / 1e12
+    res = {
+        "metric": "training-path query tokens/s (routing loss + attention backward, all routed layers)",
+        "value": round(B * T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator)",
+        "config": {"workload": f"{p.name}: {n_tok}-token memory, {D} docs, chunk {p.chunk}, {N} chunks/layer, "
+                               f"{layers} routed layers, H={H}, d={d}; {B} x T={T} trained tokens, Hq={Hq}, "
+                               f"L_loc={L}, k={k}, {p.n_needles} positives, tau={tau}",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "stage_ms_per_step": {"routing_fwd_loss_bwd_topk_index": round(stage[0], 4),
+                              "attention_fwd_recompute_and_bwd": round(stage[1], 4),
+                              "pool_backward_kr_k_v": round(stage[2], 4)},
+        "mean_routing_loss": round(float(loss.mean().item()), 5),
+        "roofline": {"kernel": "msa_sparse_attn_backward (forward recompute + dK/dV + dQ)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(achieved / 2500.0, 4), "traffic": None,
+                     "avg_call_ms": round(attn_ms, 4), "alg_flops_per_call": int(attn_flops)},
+    }
+    print(json.dumps(res), flush=True)
 
 
 def copy_calibration(torch):

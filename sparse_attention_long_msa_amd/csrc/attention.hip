@@ -63,7 +63,6 @@ struct TabRegs {
   uint4 t[DC_TAB_PT];   // this thread's pieces of the step's RoPE rows
 };
 
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 
 template <int G, bool IDX>

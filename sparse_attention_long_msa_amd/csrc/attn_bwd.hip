@@ -26,6 +26,8 @@ namespace msa {
 constexpr int BW_WAVES = 4;
 constexpr int BW_THREADS = 64 * BW_WAVES;
 constexpr float BW_LOG2E = 1.4426950408889634f;
+constexpr int BW_DEPTH = 4;   // tiles (dK/dV) or key steps (dQ) whose loads are in flight (even)
+static_assert(BW_DEPTH % 2 == 0, "tile i uses LDS buffer i % 2");
 
 // A operand of a 16x16x16 product from a row-major bf16 tile (16 rows, row
 // stride AT_VS): lane (lc, g4) receives tile[4*g4 + r][16*dt + lc], r = 0..3
@@ -99,6 +101,15 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_prep_kernel(
 }
 
 // ---------------------------------------------------------------- dK, dV (MFMA)
+// Workgroup = (query b, KV head g, block of 64 keys, range of row tiles); the
+// row tiles of the range are staged through two LDS buffers, the next one
+// loading while the current one is computed (LDS-only barriers).  Each row
+// range writes its partial sums; a reduce pass adds them.
+struct BwRows {
+  uint4 q, o;      // this thread's 16-byte piece of the tile's q_s and dO rows
+  float l, D;      // threads 0..15: the rows' log-sum-exp and D
+};
+
 template <int G>
 __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(
     int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_bar, const uint16_t* __restrict__ v_bar,
@@ -106,23 +117,28 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(
     const int32_t* __restrict__ ctx_len, int max_ctx, const uint16_t* __restrict__ k_loc,
     const uint16_t* __restrict__ v_loc, int L_loc, int qpo, const float2* __restrict__ tab, int P,
     const uint16_t* __restrict__ qs16, const uint16_t* __restrict__ do16, const float* __restrict__ lse,
-    const float* __restrict__ Dv, int n_kb, float* __restrict__ dk_loc, float* __restrict__ dv_loc,
-    float* __restrict__ dk_bar, float* __restrict__ dv_bar) {
-  __shared__ __attribute__((aligned(16))) unsigned char qt[16 * AT_VS];
-  __shared__ __attribute__((aligned(16))) unsigned char dt_[16 * AT_VS];
-  __shared__ float slse[16], sD[16];
+    const float* __restrict__ Dv, int n_kb, int n_rs, float* __restrict__ part_k, float* __restrict__ part_v) {
+  __shared__ __attribute__((aligned(16))) unsigned char qt[2][16 * AT_VS];
+  __shared__ __attribute__((aligned(16))) unsigned char ot[2][16 * AT_VS];
+  __shared__ float slse[2][16], sD[2][16];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int lc = lane % 16, g4 = lane / 16;
   int64_t wg = blockIdx.x;
+  const int rs = int(wg % n_rs);
+  wg /= n_rs;
   const int kb = int(wg % n_kb);
   wg /= n_kb;
   const int g = int(wg % Hkv);
   const int b = int(wg / Hkv);
   const int ctxl = min(max(ctx_len[b], 0), max_ctx);
   const int n_keys = ctxl + L_loc;
+  if (kb * BW_WAVES * 16 >= n_keys) return;          // no key of this block exists for query b
   const int j0 = (kb * BW_WAVES + wave) * 16;       // this wave's 16 keys
   const int R = T * G;                               // query rows of this KV head
   const int n_rt = (R + 15) / 16;
+  const int per = (n_rt + n_rs - 1) / n_rs;
+  const int rt_begin = rs * per, rt_end = min(n_rt, rt_begin + per);
+  if (rt_begin >= rt_end) return;
 
   // the lane's key (column lc of every product) as rotated K and as V
   const BwKey kl = bw_key(j0 + lc, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows);
@@ -145,98 +161,165 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(
     dvT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const int srow = tid / 16, scol = tid % 16;       // staging: one 16-byte piece per thread and tile
-  for (int rt = 0; rt < n_rt; ++rt) {
-    {
-      const int r = rt * 16 + srow;
-      uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
-      if (r < R) {
-        const int64_t grow = (int64_t(b) * T + r / G) * Hq + g * G + r % G;
-        a = load_global(qs16 + grow * AT_D + 8 * scol);
-        c = load_global(do16 + grow * AT_D + 8 * scol);
-      }
-      *reinterpret_cast<uint4*>(qt + srow * AT_VS + 16 * scol) = a;
-      *reinterpret_cast<uint4*>(dt_ + srow * AT_VS + 16 * scol) = c;
-      if (tid < 16) {
-        const int r2 = rt * 16 + tid;
-        const int64_t grow = (int64_t(b) * T + r2 / G) * Hq + g * G + r2 % G;
-        slse[tid] = r2 < R ? lse[grow] : INFINITY;
-        sD[tid] = r2 < R ? Dv[grow] : 0.f;
-      }
+  auto grow_of = [&](int r) { return (int64_t(b) * T + r / G) * Hq + g * G + r % G; };
+  // loads of row tile rt, always issued (rows past R read row R - 1 and are zeroed)
+  auto load_rows = [&](int rt) {
+    BwRows x;
+    const int r = rt * 16 + srow, rc = min(r, R - 1);
+    const int64_t gr = grow_of(rc);
+    x.q = load_global(qs16 + gr * AT_D + 8 * scol);
+    x.o = load_global(do16 + gr * AT_D + 8 * scol);
+    if (r >= R) x.q = x.o = make_uint4(0, 0, 0, 0);
+    const int r2 = rt * 16 + (tid % 16), r2c = min(r2, R - 1);
+    const float lv = lse[grow_of(r2c)], dv = Dv[grow_of(r2c)];
+    x.l = r2 < R ? lv : INFINITY;
+    x.D = r2 < R ? dv : 0.f;
+    return x;
+  };
+  auto store_rows = [&](const BwRows& x, int buf) {
+    *reinterpret_cast<uint4*>(qt[buf] + srow * AT_VS + 16 * scol) = x.q;
+    *reinterpret_cast<uint4*>(ot[buf] + srow * AT_VS + 16 * scol) = x.o;
+    if (tid < 16) {
+      slse[buf][tid] = x.l;
+      sD[buf][tid] = x.D;
     }
-    __syncthreads();
+  };
+  auto compute = [&](int rt, int buf) {
     // rows of this tile see key j iff j < ctxl or j - ctxl <= L_loc - T + t
     const int t_max = min(rt * 16 + 15, R - 1) / G;
-    if (wave_live && !(j0 >= ctxl && j0 - ctxl > L_loc - T + t_max)) {
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!wave_live || (j0 >= ctxl && j0 - ctxl > L_loc - T + t_max)) return;
+    const unsigned char* qb = qt[buf];
+    const unsigned char* ob = ot[buf];
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint4 qa = *reinterpret_cast<const uint4*>(qt + lc * AT_VS + 64 * kk + 16 * g4);
-        const uint4 da = *reinterpret_cast<const uint4*>(dt_ + lc * AT_VS + 64 * kk + 16 * g4);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa), __builtin_bit_cast(bf16x8, kr[kk]), s,
-                                                    0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, da), __builtin_bit_cast(bf16x8, vr[kk]),
-                                                     dp, 0, 0, 0);
-      }
-      // lane (lc, g4) holds S and dP at row 4*g4 + i, key lc
-      float p[4], ds[4];
-      const int j = j0 + lc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 4 * g4 + i, r = rt * 16 + rr;
-        const bool vis = kl.valid && r < R && (j < ctxl || j - ctxl <= L_loc - T + r / G);
-        p[i] = vis ? __builtin_amdgcn_exp2f(s[i] - slse[rr]) : 0.f;
-        ds[i] = p[i] * (dp[i] - sD[rr]);
-      }
-      const v4s pb = pack4(p[0], p[1], p[2], p[3]);
-      const v4s sb = pack4(ds[0], ds[1], ds[2], ds[3]);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        dvT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tr_operand4(dt_, dt, lane), pb, dvT[dt], 0, 0, 0);
-        dkT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tr_operand4(qt, dt, lane), sb, dkT[dt], 0, 0, 0);
-      }
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint4 qa = *reinterpret_cast<const uint4*>(qb + lc * AT_VS + 64 * kk + 16 * g4);
+      const uint4 da = *reinterpret_cast<const uint4*>(ob + lc * AT_VS + 64 * kk + 16 * g4);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa), __builtin_bit_cast(bf16x8, kr[kk]),
+                                                   sc, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, da), __builtin_bit_cast(bf16x8, vr[kk]),
+                                                   dp, 0, 0, 0);
     }
-    __syncthreads();
-  }
-  if (!kl.valid) return;
-  // lane holds dK_rot^T, dV^T at dims e = 16*dt + 4*g4 + i of key lc; the
-  // query rows carried scale * log2(e), so dK_rot = sum(dS q_s) / log2(e)
-  const float2* cs = tab + int64_t(kl.pos) * (AT_D / 2);
-  float dk[8][4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+    // lane (lc, g4) holds S and dP at row 4*g4 + i, key lc
+    float p[4], ds[4];
+    const int j = j0 + lc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float2 c = cs[16 * dt + 4 * g4 + i];
-      const float a = dkT[dt][i] * (1.f / BW_LOG2E), bb = dkT[dt + 4][i] * (1.f / BW_LOG2E);
-      dk[dt][i] = a * c.x + bb * c.y;          // the inverse rotation
-      dk[dt + 4][i] = bb * c.x - a * c.y;
+      const int rr = 4 * g4 + i, r = rt * 16 + rr;
+      const bool vis = kl.valid && r < R && (j < ctxl || j - ctxl <= L_loc - T + r / G);
+      p[i] = vis ? __builtin_amdgcn_exp2f(sc[i] - slse[buf][rr]) : 0.f;
+      ds[i] = p[i] * (dp[i] - sD[buf][rr]);
     }
-  }
-  if (kl.local) {
-    float* kd = dk_loc + (kl.row * Hkv + g) * AT_D;
-    float* vd = dv_loc + (kl.row * Hkv + g) * AT_D;
+    const v4s pb = pack4(p[0], p[1], p[2], p[3]);
+    const v4s sb = pack4(ds[0], ds[1], ds[2], ds[3]);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      *reinterpret_cast<float4*>(kd + 16 * dt + 4 * g4) = make_float4(dk[dt][0], dk[dt][1], dk[dt][2], dk[dt][3]);
-      *reinterpret_cast<float4*>(vd + 16 * dt + 4 * g4) = make_float4(dvT[dt][0], dvT[dt][1], dvT[dt][2], dvT[dt][3]);
+      dvT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tr_operand4(ob, dt, lane), pb, dvT[dt], 0, 0, 0);
+      dkT[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tr_operand4(qb, dt, lane), sb, dkT[dt], 0, 0, 0);
     }
-  } else {   // a pooled row may be read by several queries
-    float* kd = dk_bar + (kl.row * Hkv + g) * AT_D;
-    float* vd = dv_bar + (kl.row * Hkv + g) * AT_D;
+  };
+  // BW_DEPTH row tiles are in flight in registers.  Buffer i % 2 is
+  // rewritten two tiles after it was read and each wave's reads of it
+  // precede its next barrier, so one barrier per tile suffices.  Requests
+  // past the range repeat its last tile (in bounds, never computed).
+  const int n_t = rt_end - rt_begin;
+  auto rt_at = [&](int i) { return rt_begin + min(i, n_t - 1); };
+  BwRows ring[BW_DEPTH];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+  for (int u = 0; u < BW_DEPTH; ++u) ring[u] = load_rows(rt_at(u));
+  for (int i0 = 0; i0 < n_t; i0 += BW_DEPTH) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        unsafeAtomicAdd(kd + 16 * dt + 4 * g4 + i, dk[dt][i]);
-        unsafeAtomicAdd(vd + 16 * dt + 4 * g4 + i, dvT[dt][i]);
-      }
+    for (int u = 0; u < BW_DEPTH; ++u) {
+      store_rows(ring[u], u & 1);
+      ring[u] = load_rows(rt_at(i0 + u + BW_DEPTH));
+      lds_barrier();
+      if (i0 + u < n_t) compute(rt_begin + i0 + u, u & 1);
+    }
+  }
+  if (!kl.valid) return;
+  // partial sums of this row range: lane holds dK_rot^T, dV^T at dims
+  // e = 16*dt + 4*g4 + i of key lc; the query rows carried scale * log2(e),
+  // so dK_rot = sum(dS q_s) / log2(e)
+  const int64_t slot = ((int64_t(rs) * B + b) * (int64_t(n_kb) * BW_WAVES * 16) + j0 + lc) * Hkv + g;
+  float* kd = part_k + slot * AT_D;
+  float* vd = part_v + slot * AT_D;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    *reinterpret_cast<float4*>(kd + 16 * dt + 4 * g4) =
+        make_float4(dkT[dt][0], dkT[dt][1], dkT[dt][2], dkT[dt][3]) * (1.f / BW_LOG2E);
+    *reinterpret_cast<float4*>(vd + 16 * dt + 4 * g4) = make_float4(dvT[dt][0], dvT[dt][1], dvT[dt][2], dvT[dt][3]);
+  }
+}
+
+// Sum of the row ranges' partials per (query, key, KV head, pair block),
+// the inverse rotation of dK, then a plain store for a local key and an
+// atomic add for a pooled row (several queries may read it).
+__global__ void attn_bwd_dkdv_reduce_kernel(const float* __restrict__ part_k, const float* __restrict__ part_v,
+                                            int n_rs, int B, int KM, int Hkv, int L_loc, int qpo,
+                                            const int32_t* __restrict__ ctx_row, int64_t ctx_rows,
+                                            const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
+                                            int max_ctx, const float2* __restrict__ tab, int P,
+                                            float* __restrict__ dk_loc, float* __restrict__ dv_loc,
+                                            float* __restrict__ dk_bar, float* __restrict__ dv_bar) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;   // (b, j, g, quad of pairs)
+  const int64_t n = int64_t(B) * KM * Hkv * 16;
+  if (i >= n) return;
+  const int qd = int(i % 16);
+  const int g = int((i / 16) % Hkv);
+  const int j = int((i / (16 * Hkv)) % KM);
+  const int b = int(i / (16 * int64_t(Hkv) * KM));
+  const int ctxl = min(max(ctx_len[b], 0), max_ctx);
+  const int n_keys = ctxl + L_loc;
+  if (j >= n_keys) return;
+  const BwKey kl = bw_key(j, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows);
+  float4 ka = make_float4(0.f, 0.f, 0.f, 0.f), kb = ka, va = ka, vb = ka;
+  for (int r = 0; r < n_rs; ++r) {
+    const int64_t o = (((int64_t(r) * B + b) * KM + j) * Hkv + g) * AT_D + 4 * qd;
+    ka += *reinterpret_cast<const float4*>(part_k + o);
+    kb += *reinterpret_cast<const float4*>(part_k + o + AT_D / 2);
+    va += *reinterpret_cast<const float4*>(part_v + o);
+    vb += *reinterpret_cast<const float4*>(part_v + o + AT_D / 2);
+  }
+  const float4 c0 = reinterpret_cast<const float4*>(tab + int64_t(kl.pos) * (AT_D / 2) + 4 * qd)[0];
+  const float4 c1 = reinterpret_cast<const float4*>(tab + int64_t(kl.pos) * (AT_D / 2) + 4 * qd)[1];
+  const float c[4] = {c0.x, c0.z, c1.x, c1.z}, sn[4] = {c0.y, c0.w, c1.y, c1.w};
+  const float a[4] = {ka.x, ka.y, ka.z, ka.w}, bb[4] = {kb.x, kb.y, kb.z, kb.w};
+  float lo[4], hi[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {          // the inverse rotation of the pair (m, m + 64)
+    lo[e] = a[e] * c[e] + bb[e] * sn[e];
+    hi[e] = bb[e] * c[e] - a[e] * sn[e];
+  }
+  const int64_t o = (kl.row * Hkv + g) * AT_D + 4 * qd;
+  if (kl.local) {
+    *reinterpret_cast<float4*>(dk_loc + o) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<float4*>(dk_loc + o + AT_D / 2) = make_float4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<float4*>(dv_loc + o) = va;
+    *reinterpret_cast<float4*>(dv_loc + o + AT_D / 2) = vb;
+  } else {
+    const float v4[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      unsafeAtomicAdd(dk_bar + o + e, lo[e]);
+      unsafeAtomicAdd(dk_bar + o + AT_D / 2 + e, hi[e]);
+      unsafeAtomicAdd(dv_bar + o + e, v4[e]);
+      unsafeAtomicAdd(dv_bar + o + AT_D / 2 + e, v4[4 + e]);
+    }
   }
 }
 
 // ---------------------------------------------------------------- dQ (MFMA)
 // One wave per 16-row tile of a KV head, four tiles per workgroup, over one
-// key split; each 32-key step stages the rotated K and V rows in LDS.
+// key split.  Each 32-key step's rotated K and V rows go through two LDS
+// buffers; the next step loads (branch-free addressing through the split's
+// context entries cached in LDS) while the current one is computed.
 constexpr int BQ_KV_BYTES = 32 * AT_VS;
+
+struct BqRegs {
+  uint2 klo[2], khi[2];   // dims 4x..4x+3 and 64+4x..64+4x+3 of keys lk and 16 + lk
+  float4 c0[2], c1[2];    // their (cos, sin) rows for m = 4x..4x+3
+  uint4 v[2];             // V dims 8x..8x+7
+};
 
 template <int G>
 __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(
@@ -246,8 +329,9 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ v_loc, int L_loc, int qpo, const float2* __restrict__ tab, int P,
     const uint16_t* __restrict__ qs16, const uint16_t* __restrict__ do16, const float* __restrict__ lse,
     const float* __restrict__ Dv, int n_rg, int n_splits, float* __restrict__ ws_dq) {
-  __shared__ __attribute__((aligned(16))) unsigned char kt[BQ_KV_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char vt[BQ_KV_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char kt[2][BQ_KV_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[2][BQ_KV_BYTES];
+  __shared__ int2 cidx[AT_CIDX];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int lc = lane % 16, g4 = lane / 16;
   int64_t wg = blockIdx.x;
@@ -280,55 +364,70 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(
   const int kps = ((n_keys + n_splits - 1) / n_splits + 31) / 32 * 32;
   const int j_begin = split * kps;
   const int j_end = min(n_keys, j_begin + kps);
+  const CtxCache cc = stage_ctx(cidx, b, j_begin, j_end, ctxl, max_ctx, ctx_pos, P, ctx_row, ctx_rows, tid,
+                                BW_THREADS);
+  __syncthreads();
   // staging: 16 keys per pass of the workgroup, thread (key lk, 4-dim block lx)
   const int lk = tid / 16, lx = tid % 16;
-  for (int j0 = j_begin; j0 < j_end; j0 += 32) {
+  auto load_step = [&](int jj) {
+    BqRegs x;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int key = 16 * half + lk;
-      const BwKey ks = bw_key(j0 + key, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows);
+    for (int h = 0; h < 2; ++h) {
+      const KeySrc ks = key_src(jj + 16 * h + lk, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row,
+                                ctx_rows, cc);
       const uint16_t* kp = (ks.local ? k_loc : k_bar) + (ks.row * Hkv + g) * AT_D;
       const uint16_t* vp = (ks.local ? v_loc : v_bar) + (ks.row * Hkv + g) * AT_D;
-      const uint2 klo = load_global8(kp + 4 * lx), khi = load_global8(kp + 64 + 4 * lx);
-      const uint4 v = load_global(vp + 8 * lx);
-      const float4 c0 = reinterpret_cast<const float4*>(tab + int64_t(ks.pos) * (AT_D / 2) + 4 * lx)[0];
-      const float4 c1 = reinterpret_cast<const float4*>(tab + int64_t(ks.pos) * (AT_D / 2) + 4 * lx)[1];
-      const float c[4] = {c0.x, c0.z, c1.x, c1.z}, sn[4] = {c0.y, c0.w, c1.y, c1.w};
-      const float a[4] = {__uint_as_float(klo.x << 16), __uint_as_float(klo.x & 0xFFFF0000u),
-                          __uint_as_float(klo.y << 16), __uint_as_float(klo.y & 0xFFFF0000u)};
-      const float bb[4] = {__uint_as_float(khi.x << 16), __uint_as_float(khi.x & 0xFFFF0000u),
-                           __uint_as_float(khi.y << 16), __uint_as_float(khi.y & 0xFFFF0000u)};
+      const float2* tp = tab + int64_t(ks.pos) * (AT_D / 2) + 4 * lx;
+      x.klo[h] = load_global8(kp + 4 * lx);
+      x.khi[h] = load_global8(kp + 64 + 4 * lx);
+      x.c0[h] = __builtin_bit_cast(float4, load_global(tp));
+      x.c1[h] = __builtin_bit_cast(float4, load_global(tp + 2));
+      x.v[h] = load_global(vp + 8 * lx);
+    }
+    return x;
+  };
+  auto store_step = [&](const BqRegs& x, int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = 16 * h + lk;
+      const float c[4] = {x.c0[h].x, x.c0[h].z, x.c1[h].x, x.c1[h].z};
+      const float sn[4] = {x.c0[h].y, x.c0[h].w, x.c1[h].y, x.c1[h].w};
+      const float a[4] = {__uint_as_float(x.klo[h].x << 16), __uint_as_float(x.klo[h].x & 0xFFFF0000u),
+                          __uint_as_float(x.klo[h].y << 16), __uint_as_float(x.klo[h].y & 0xFFFF0000u)};
+      const float bb[4] = {__uint_as_float(x.khi[h].x << 16), __uint_as_float(x.khi[h].x & 0xFFFF0000u),
+                           __uint_as_float(x.khi[h].y << 16), __uint_as_float(x.khi[h].y & 0xFFFF0000u)};
       float ra[4], rb[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         ra[e] = a[e] * c[e] - bb[e] * sn[e];
         rb[e] = bb[e] * c[e] + a[e] * sn[e];
       }
-      unsigned char* krow = kt + key * AT_VS;
+      unsigned char* krow = kt[buf] + key * AT_VS;
       *reinterpret_cast<uint2*>(krow + 8 * lx) = make_uint2(pack_bf16x2(ra[0], ra[1]), pack_bf16x2(ra[2], ra[3]));
       *reinterpret_cast<uint2*>(krow + 128 + 8 * lx) = make_uint2(pack_bf16x2(rb[0], rb[1]), pack_bf16x2(rb[2], rb[3]));
-      *reinterpret_cast<uint4*>(vt + key * AT_VS + 16 * lx) = v;
+      *reinterpret_cast<uint4*>(vt[buf] + key * AT_VS + 16 * lx) = x.v[h];
     }
-    __syncthreads();
+  };
+  auto compute_step = [&](int jj, int buf) {
     float dsv[2][4];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(kt + (16 * tau + lc) * AT_VS + 64 * kk + 16 * g4);
-        const uint4 va = *reinterpret_cast<const uint4*>(vt + (16 * tau + lc) * AT_VS + 64 * kk + 16 * g4);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qb[kk]), s,
-                                                    0, 0, 0);
+        const uint4 ka = *reinterpret_cast<const uint4*>(kt[buf] + (16 * tau + lc) * AT_VS + 64 * kk + 16 * g4);
+        const uint4 va = *reinterpret_cast<const uint4*>(vt[buf] + (16 * tau + lc) * AT_VS + 64 * kk + 16 * g4);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qb[kk]),
+                                                     sc, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, db[kk]),
                                                      dp, 0, 0, 0);
       }
       // lane (lc, g4): key 16*tau + 4*g4 + i, row lc
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = j0 + 16 * tau + 4 * g4 + i;
+        const int j = jj + 16 * tau + 4 * g4 + i;
         const bool vis = rok && j < j_end && (j < ctxl || j - ctxl <= horizon);
-        const float p = vis ? __builtin_amdgcn_exp2f(s[i] - l2) : 0.f;
+        const float p = vis ? __builtin_amdgcn_exp2f(sc[i] - l2) : 0.f;
         dsv[tau][i] = p * (dp[i] - Dr);
       }
     }
@@ -337,8 +436,26 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(
                            pack_bf16x2(dsv[1][0], dsv[1][1]), pack_bf16x2(dsv[1][2], dsv[1][3])));
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-      dqT[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pv_operand(kt, dt, lane), sb, dqT[dt], 0, 0, 0);
-    __syncthreads();
+      dqT[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pv_operand(kt[buf], dt, lane), sb, dqT[dt], 0, 0, 0);
+  };
+  const int n_steps = j_begin < j_end ? (j_end - j_begin + 31) / 32 : 0;
+  if (n_steps > 0) {
+    // BW_DEPTH steps are in flight; a buffer is rewritten two steps after it
+    // was read; requests past the last step repeat its addresses (in bounds,
+    // never used)
+    auto j_at = [&](int i) { return j_begin + 32 * min(i, n_steps - 1); };
+    BqRegs ring[BW_DEPTH];
+#pragma unroll
+    for (int u = 0; u < BW_DEPTH; ++u) ring[u] = load_step(j_at(u));
+    for (int i0 = 0; i0 < n_steps; i0 += BW_DEPTH) {
+#pragma unroll
+      for (int u = 0; u < BW_DEPTH; ++u) {
+        store_step(ring[u], u & 1);
+        ring[u] = load_step(j_at(i0 + u + BW_DEPTH));
+        lds_barrier();
+        if (i0 + u < n_steps) compute_step(j_at(i0 + u), u & 1);
+      }
+    }
   }
   if (!rok) return;
   float* op = ws_dq + (int64_t(split) * B * T * Hq + grow) * AT_D;
@@ -543,8 +660,8 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_bwd_vec_dkdv_kernel(
 // ---------------------------------------------------------------- plan
 struct BwdPlan {
   bool mfma;
-  size_t fwd_bytes, out_bytes, row_bytes, bf_bytes, dq_bytes;
-  int n_rg, n_splits, n_kb;
+  size_t fwd_bytes, out_bytes, row_bytes, bf_bytes, dq_bytes, part_bytes;
+  int n_rg, n_splits, n_kb, n_rs;
 };
 
 static BwdPlan bwd_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc, int qpo) {
@@ -563,9 +680,15 @@ static BwdPlan bwd_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int max
     const int64_t n_keys_max = int64_t(max_ctx) + L_loc;
     int64_t s = (256 + units - 1) / units;
     s = std::max<int64_t>(1, std::min<int64_t>(s, (n_keys_max + 127) / 128));
+    // a split's context entries must fit the LDS index cache
+    if (max_ctx > AT_CIDX) s = std::max<int64_t>(s, (n_keys_max + AT_CIDX - 33) / (AT_CIDX - 32));
     p.n_splits = int(s);
     p.dq_bytes = align_up(size_t(p.n_splits) * rows * d * 4, 256);
     p.n_kb = int((n_keys_max + 16 * BW_WAVES - 1) / (16 * BW_WAVES));
+    const int64_t kunits = int64_t(B) * Hkv * p.n_kb;
+    // about two workgroups per CU in one round
+    p.n_rs = int(std::max<int64_t>(1, std::min<int64_t>(512 / kunits, n_rt)));
+    p.part_bytes = align_up(size_t(p.n_rs) * B * size_t(p.n_kb) * BW_WAVES * 16 * Hkv * d * 4, 256);
   }
   return p;
 }
@@ -577,7 +700,7 @@ extern "C" size_t msa_sparse_attn_backward_workspace(int dtype, int B, int T, in
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 2 || max_ctx < 0 || L_loc < 1 || q_pos_offset < 0 || Hq % Hkv)
     return 0;
   const msa::BwdPlan p = msa::bwd_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
-  return p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes + p.dq_bytes;
+  return p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes + p.dq_bytes + 2 * p.part_bytes;
 }
 
 extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
@@ -595,7 +718,7 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
   MSA_REQUIRE(B >= 1 && T >= 1 && Hq >= 1 && Hkv >= 1 && d >= 2 && max_ctx >= 1 && L_loc >= 1 && Hq % Hkv == 0,
               MSA_ERR_INVALID_ARG, fn + ": bad sizes");
   const BwdPlan p = bwd_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
-  const size_t need = p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes + p.dq_bytes;
+  const size_t need = p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes + p.dq_bytes + 2 * p.part_bytes;
   MSA_REQUIRE(ws && ws_bytes >= need, MSA_ERR_WORKSPACE, fn + ": workspace too small");
   if (!p.mfma)
     MSA_REQUIRE(size_t(d) + AT_VEC_THREADS + size_t(max_ctx) + L_loc <= 16384, MSA_ERR_UNSUPPORTED,
@@ -607,6 +730,8 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
   uint16_t* qs16 = reinterpret_cast<uint16_t*>(w + p.fwd_bytes + p.out_bytes + 2 * p.row_bytes);
   uint16_t* do16 = reinterpret_cast<uint16_t*>(w + p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + p.bf_bytes);
   float* ws_dq = reinterpret_cast<float*>(w + p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes);
+  float* part_k = reinterpret_cast<float*>(reinterpret_cast<char*>(ws_dq) + p.dq_bytes);
+  float* part_v = reinterpret_cast<float*>(reinterpret_cast<char*>(part_k) + p.part_bytes);
   // the forward (validates every shared argument) with the per-row log-sum-exp
   const int rc = sparse_attn(fn, dtype, q, B, T, Hq, Hkv, d, k_bar, v_bar, ctx_row, n_chunks, ctx_pos, ctx_len,
                              max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows,
@@ -628,11 +753,13 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
     const uint16_t* vb = static_cast<const uint16_t*>(v_bar);
     const uint16_t* kl = static_cast<const uint16_t*>(k_loc);
     const uint16_t* vl = static_cast<const uint16_t*>(v_loc);
-    const dim3 kgrid(unsigned(int64_t(B) * Hkv * p.n_kb)), qgrid(unsigned(int64_t(B) * Hkv * p.n_rg * p.n_splits));
+    const dim3 kgrid(unsigned(int64_t(B) * Hkv * p.n_kb * p.n_rs)),
+        qgrid(unsigned(int64_t(B) * Hkv * p.n_rg * p.n_splits));
+
 #define BW_LAUNCH(GV)                                                                                              \
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<GV>), kgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, kb, vb, n_chunks,   \
                      ctx_row, ctx_pos, ctx_len, max_ctx, kl, vl, L_loc, q_pos_offset, tab, P, qs16, do16, lse, Dv, \
-                     p.n_kb, dk_loc, dv_loc, dk_bar, dv_bar);                                                      \
+                     p.n_kb, p.n_rs, part_k, part_v);                                                              \
   MSA_LAUNCH_CHECK();                                                                                              \
   hipLaunchKernelGGL((attn_bwd_dq_kernel<GV>), qgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, kb, vb, n_chunks,     \
                      ctx_row, ctx_pos, ctx_len, max_ctx, kl, vl, L_loc, q_pos_offset, tab, P, qs16, do16, lse, Dv, \
@@ -646,6 +773,17 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
     }
 #undef BW_LAUNCH
     MSA_LAUNCH_CHECK();
+    {
+      // row ranges that hold at least one row tile (the others wrote nothing)
+      const int n_rt = (T * G + 15) / 16, per = (n_rt + p.n_rs - 1) / p.n_rs;
+      const int n_rs_used = (n_rt + per - 1) / per;
+      const int KM = p.n_kb * BW_WAVES * 16;
+      const int64_t nr = int64_t(B) * KM * Hkv * 16;
+      hipLaunchKernelGGL(attn_bwd_dkdv_reduce_kernel, dim3(unsigned((nr + 255) / 256)), dim3(256), 0, s, part_k,
+                         part_v, n_rs_used, B, KM, Hkv, L_loc, q_pos_offset, ctx_row, n_chunks, ctx_pos, ctx_len, max_ctx,
+                         tab, P, dk_loc, dv_loc, dk_bar, dv_bar);
+      MSA_LAUNCH_CHECK();
+    }
     const int64_t n = rows * (d / 2);
     hipLaunchKernelGGL(attn_bwd_dq_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, ws_dq, p.n_splits,
                        rows, T, Hq, d, L_loc, q_pos_offset, tab, P, sm_scale, dq);

@@ -161,6 +161,7 @@ __device__ __forceinline__ KeySrc key_src(int j, int b, int ctxl, int n_keys, in
 
 // This wave's LDS operations are complete, then the workgroup barrier; unlike
 // __syncthreads() it does not wait for outstanding vector-memory loads.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // RoPE table rows the attention kernels need: max(qpo + L_loc, max_ctx, 32)
 inline int rope_rows(int max_ctx, int L_loc, int qpo) { return std::max(std::max(qpo + L_loc, max_ctx), 32); }

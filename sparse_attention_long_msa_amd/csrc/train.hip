@@ -68,7 +68,8 @@ __device__ __forceinline__ uint64_t cand_key(float s, uint32_t idx) {
 }
 
 // ---------------------------------------------------------------- scores with maximiser
-// bf16 path: one wave per 16-chunk tile.  Per head, the tile's rows are the
+// bf16 path: one wave per (16-chunk tile, group of 64 query columns), so that
+// long queries and small memories still fill the chip.  Per head, the tile's rows are the
 // A operand of v_mfma_f32_16x16x32_bf16 (16 bytes per lane, loaded once per
 // head) and the raw bf16 queries the B operand; each head's fp32 result is
 // scaled by 1 / (H ||q||) and summed, so products are exact.  The token max
@@ -80,9 +81,11 @@ constexpr int AX_NT = 4;   // 16-column tiles per pass
 __global__ __launch_bounds__(TR_THREADS) void route_argmax_mfma_kernel(
     const uint16_t* __restrict__ q, int T, int J, int H, int d, const uint16_t* __restrict__ kr,
     const int32_t* __restrict__ chunk_doc, int64_t n_docs, int64_t n_chunks, const float* __restrict__ winv,
-    uint64_t* __restrict__ keys) {
+    int n_cg, uint64_t* __restrict__ keys) {
   const int lane = threadIdx.x % 64, lc = lane % 16, g4 = lane / 16;
-  const int64_t tile = int64_t(blockIdx.x) * TR_WAVES + threadIdx.x / 64;
+  const int64_t wid = int64_t(blockIdx.x) * TR_WAVES + threadIdx.x / 64;
+  const int64_t tile = wid / n_cg;
+  const int cg = int(wid % n_cg);
   const int64_t c0 = tile * 16;
   if (c0 >= n_chunks) return;
   const int64_t crow = c0 + lc;                       // A-operand row of this lane
@@ -94,7 +97,8 @@ __global__ __launch_bounds__(TR_THREADS) void route_argmax_mfma_kernel(
     const int64_t c = c0 + 4 * g4 + i;
     rdoc[i] = c < n_chunks ? chunk_doc[c] : -1;
   }
-  for (int col0 = 0; col0 < J; col0 += 16 * AX_NT) {
+  {
+    const int col0 = cg * 16 * AX_NT;
     f32x4 tot[AX_NT];
 #pragma unroll
     for (int n = 0; n < AX_NT; ++n) tot[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -415,6 +419,58 @@ __global__ __launch_bounds__(TR_THREADS) void pool_bwd_kernel(
   }
 }
 
+// Row path: one workgroup per pooled chunk, H*d/4 threads, thread q owning
+// elements 4q..4q+3 of a token row (head q / (d/4)); every token of the
+// chunk is written as whole contiguous rows.  Per-head sums reduce across
+// the d/4 lanes of the head.
+template <int DT>
+__global__ void pool_bwd_rows_kernel(const float* __restrict__ dy, int64_t n_chunks, int H, int d,
+                                     const int64_t* __restrict__ tok_off, const int64_t* __restrict__ chunk_off,
+                                     const int32_t* __restrict__ chunk_doc, int64_t n_docs, int chunk,
+                                     const typename Elem<DT>::T* __restrict__ x, float* __restrict__ dx) {
+  const int64_t c = blockIdx.x;
+  const int qd = threadIdx.x, HD = H * d, lanes = d / 4;
+  const int doc = chunk_doc[c];
+  if (doc < 0 || doc >= n_docs) return;
+  const int64_t t0 = tok_off[doc] + (c - chunk_off[doc]) * int64_t(chunk);
+  const int64_t n = min(int64_t(chunk), tok_off[doc + 1] - t0);
+  if (n <= 0) return;
+  float4 dm = *reinterpret_cast<const float4*>(dy + c * HD + 4 * qd);
+  if (x) {
+    float4 mean = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t tau = t0; tau < t0 + n; ++tau) {
+      const typename Elem<DT>::T* xp = x + tau * HD + 4 * qd;
+      mean.x += Elem<DT>::load(xp, 0);
+      mean.y += Elem<DT>::load(xp, 1);
+      mean.z += Elem<DT>::load(xp, 2);
+      mean.w += Elem<DT>::load(xp, 3);
+    }
+    const float inv_n = 1.f / float(n);
+    mean = mean * inv_n;
+    float ss = mean.x * mean.x + mean.y * mean.y + mean.z * mean.z + mean.w * mean.w;
+    float dot = mean.x * dm.x + mean.y * dm.y + mean.z * dm.z + mean.w * dm.w;
+    for (int m = 1; m < lanes; m <<= 1) {   // the lanes of one head are an aligned power-of-two group
+      ss += __shfl_xor(ss, m);
+      dot += __shfl_xor(dot, m);
+    }
+    const float nrm = sqrtf(ss);
+    if (nrm > TR_EPS) {
+      const float inv = 1.f / nrm, cc = dot * inv * inv;
+      dm = (dm - mean * cc) * inv;
+    } else {
+      dm = dm * (1.f / TR_EPS);
+    }
+  }
+  dm = dm * (1.f / float(n));
+  for (int64_t tau = t0; tau < t0 + n; ++tau) *reinterpret_cast<float4*>(dx + tau * HD + 4 * qd) = dm;
+}
+
+static bool pool_bwd_rows(int H, int d) {
+  const int lanes = d / 4;
+  return d % 4 == 0 && lanes >= 1 && lanes <= 64 && (lanes & (lanes - 1)) == 0 && H * d / 4 <= 1024 &&
+         (H * d / 4) % 64 == 0;
+}
+
 static bool argmax_mfma(int dtype, int d) { return dtype == MSA_BF16 && d % 32 == 0; }
 
 static unsigned grid_for(int64_t n, int64_t per_block) {
@@ -466,9 +522,10 @@ extern "C" int msa_route_argmax(int dtype, const void* q_r, int B, int T, int H,
   MSA_LAUNCH_CHECK();
   if (argmax_mfma(dtype, d)) {
     const int64_t tiles = (n_chunks + 15) / 16;
-    hipLaunchKernelGGL(route_argmax_mfma_kernel, dim3(grid_for(tiles, TR_WAVES)), dim3(TR_THREADS), 0, s,
+    const int n_cg = (J + 16 * AX_NT - 1) / (16 * AX_NT);
+    hipLaunchKernelGGL(route_argmax_mfma_kernel, dim3(grid_for(tiles * n_cg, TR_WAVES)), dim3(TR_THREADS), 0, s,
                        static_cast<const uint16_t*>(q_r), T, J, H, d, static_cast<const uint16_t*>(kr_hat),
-                       chunk_doc, n_docs, n_chunks, winv, keys);
+                       chunk_doc, n_docs, n_chunks, winv, n_cg, keys);
   } else if (dtype == MSA_BF16) {
     hipLaunchKernelGGL(route_argmax_vec_kernel<MSA_BF16>, dim3(grid_for(n_chunks * J, 256)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q_r), T, J, H, d, static_cast<const uint16_t*>(kr_hat),
@@ -544,6 +601,17 @@ extern "C" int msa_pool_backward(int dtype, const float* dy, const int64_t* tok_
               "msa_pool_backward: non-positive size");
   MSA_REQUIRE(d <= 64 * PB_MAXE, MSA_ERR_UNSUPPORTED, "msa_pool_backward: d > 256");
   hipStream_t s = as_stream(stream);
+  if (pool_bwd_rows(H, d) && uintptr_t(dy) % 16 == 0 && uintptr_t(dx) % 16 == 0 && n_chunks < (int64_t(1) << 31)) {
+    const dim3 grid{unsigned(n_chunks)}, block{unsigned(H * d / 4)};
+    if (dtype == MSA_BF16)
+      hipLaunchKernelGGL(pool_bwd_rows_kernel<MSA_BF16>, grid, block, 0, s, dy, n_chunks, H, d, tok_off, chunk_off,
+                         chunk_doc, n_docs, chunk, static_cast<const uint16_t*>(x), dx);
+    else
+      hipLaunchKernelGGL(pool_bwd_rows_kernel<MSA_F32>, grid, block, 0, s, dy, n_chunks, H, d, tok_off, chunk_off,
+                         chunk_doc, n_docs, chunk, static_cast<const float*>(x), dx);
+    MSA_LAUNCH_CHECK();
+    return MSA_OK;
+  }
   const int64_t waves = n_chunks * H;
   if (dtype == MSA_BF16)
     hipLaunchKernelGGL(pool_bwd_kernel<MSA_BF16>, dim3(grid_for(waves, TR_WAVES)), dim3(TR_THREADS), 0, s, dy,

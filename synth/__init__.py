@@ -38,7 +38,7 @@ NORMAL_SCALE = np.float32(2.6428997921303014e-05)
 NORMAL_CENTRE = 131070
 
 # tensor ids inside a (seed, layer) pair; stream = layer * 16 + tensor id
-T_KR, T_K, T_V, T_QR, T_Q, T_KLOC, T_VLOC, T_NEEDLE = range(8)
+T_KR, T_K, T_V, T_QR, T_Q, T_KLOC, T_VLOC, T_NEEDLE, T_DOUT = range(9)
 
 
 def stream_id(layer: int, tensor: int) -> int:

@@ -115,7 +115,19 @@ def cfg5() -> Preset:
                   32, 1, 8192, 16, 32, needle_per_query=True, query_seed=1005)
 
 
+def train64k() -> Preset:
+    """Training-time workload (the pages' 64K-context fine-tuning stage):
+    128 documents x 512 tokens = 65,536 memory tokens, chunk 64 -> 1,024
+    pooled chunks per layer, bf16, 18 routed layers; 1,024 trained query
+    tokens that are their own causal local window, 32 query heads, k = 16.
+    Readings: the query length, the window and the 4 positive documents per
+    query (the routing loss's positive set) are not given by the pages."""
+    return Preset("train64k", 1006, True, 18, uniform_lengths(128, 512), 64, 8, 128, 32,
+                  1, 1024, 1024, 16, 4)
+
+
 PRESETS = {"cfg1": cfg1, "cfg2": cfg2, "cfg3": cfg3, "cfg4": cfg4, "cfg5": cfg5}
+TRAIN_PRESETS = {"train64k": train64k}
 
 
 def store_bytes(n_tokens: int, chunk: int, layers: int, heads: int, d: int,

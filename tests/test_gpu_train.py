@@ -140,8 +140,8 @@ def test_route_score_backward(bf16):
 @pytest.mark.parametrize("bf16", [True, False])
 @pytest.mark.parametrize("chunk", [64, 5, 1])
 @pytest.mark.parametrize("normalized", [False, True])
-def test_pool_backward(bf16, chunk, normalized):
-    H, d = 4, 64
+@pytest.mark.parametrize("H,d", [(4, 64), (8, 128), (3, 40)])     # whole-row kernel, and the per-head one (3 x 40)
+def test_pool_backward(bf16, chunk, normalized, H, d):
     lens = ragged_lengths(41, 60, 0, 300, n_empty=4)
     lens[0] = 130
     tok_off, chunk_off, n_chunks, co_d, cd = _index(lens, chunk)
