@@ -52,6 +52,9 @@ def parse():
                          "262144 for token-level memories, whose sample the oracle also pools)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (the reference for the HBM byte counters)")
+    ap.add_argument("--encode", action="store_true",
+                    help="time Stage 1 from hidden states instead (msa_encode over a 1M-token memory, one layer per "
+                         "call, hidden 2560)")
     ap.add_argument("--train", action="store_true",
                     help="time the training-time path instead (routing loss and attention backward per routed "
                          "layer; --config defaults to train64k)")
@@ -74,6 +77,8 @@ def main():
         return copy_calibration(torch)
     if args.train:
         return train_main(args, torch)
+    if args.encode:
+        return encode_main(args, torch)
 
     import synth
     from synth import configs
@@ -491,6 +496,79 @@ def train_main(args, torch):
                      "achieved": round(achieved, 2), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(achieved / 2500.0, 4), "traffic": None,
                      "avg_call_ms": round(attn_ms, 4), "alg_flops_per_call": int(attn_flops)},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def encode_main(args, torch):
+    """Stage 1 at corpus scale: one call = one routed layer's pooled stores
+    (K, V, normalised K_r) of the 1M-token memory (2,048 documents x 512
+    tokens, chunk 64) from the tokens' hidden states (hidden 2,560, the
+    backbone's width) and synthetic projection weights."""
+    import synth
+    from synth import configs
+    from synth import device as SD
+    import sparse_attention_long_msa_amd as M
+
+    p = configs.PRESETS["cfg2"]()
+    hidden, H, d = 2560, p.H, p.d
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16
+    tok_off, chunk_off = p.tok_off, p.chunk_off
+    n_tok, N = int(tok_off[-1]), p.n_chunks
+    to_d = torch.from_numpy(tok_off).to(dev)
+    co_d = torch.from_numpy(chunk_off).to(dev)
+    cd = M.msa_chunk_doc_map(co_d, N)
+    x = SD.fill(torch.empty((n_tok, hidden), dtype=bf, device=dev), p.seed, 0, synth.T_K)
+    w = SD.fill(torch.empty((3 * H * d, hidden), dtype=bf, device=dev), p.seed, 0, synth.T_V, scale_pow2=-6)
+    kb = torch.empty((N, H, d), dtype=bf, device=dev)
+    vb = torch.empty_like(kb)
+    kr = torch.empty((M.padded_chunks(N, M.MSA_LAYOUT_TILED), H, d), dtype=bf, device=dev)
+    ws = torch.empty(M.lib.msa_encode_workspace(M.MSA_BF16, N, hidden, H, d), dtype=torch.uint8, device=dev)
+
+    def call():
+        M.msa_encode(x, w, to_d, co_d, cd, p.chunk, H, d, kr_layout=M.MSA_LAYOUT_TILED, k_bar=kb, v_bar=vb,
+                     kr_hat=kr, ws=ws)
+
+    for _ in range(max(args.warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        call()
+        e[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    x_bytes = n_tok * hidden * 2
+    alg = x_bytes + 2 * N * hidden * 4 + 3 * H * d * hidden * 2 + 3 * N * H * d * 2
+    gemm_flops = 2 * N * hidden * 3 * H * d
+    res = {
+        "metric": "Stage-1 encode: hidden-state GB/s (pool + projection to K, V, K_r)",
+        "value": round(x_bytes / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; synthetic projection weights)",
+        "config": {"workload": f"encode: {n_tok}-token memory (cfg2 documents), chunk {p.chunk}, {N} chunks, "
+                               f"hidden {hidden}, H={H}, d={d}, one routed layer per call",
+                   "global_batch": 1, "seq_len": n_tok, "parallelism": "single GPU"},
+        "tokens_per_s": round(n_tok / (ms * 1e-3), 1),
+        "projected_100M_tokens_18_layers_s": round(18 * 100e6 / (n_tok / (ms * 1e-3)), 1),
+        "gemm_flops_per_call": gemm_flops,
+        "roofline": {"kernel": "msa_encode (pool_hidden_kernel + encode_gemm_kernel)", "bound": "hbm",
+                     "achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(alg / (ms * 1e-3) / 1e9 / 8000.0, 4), "traffic": None,
+                     "avg_call_ms": round(ms, 4), "alg_bytes_per_call": int(alg)},
     }
     print(json.dumps(res), flush=True)
 

@@ -139,6 +139,36 @@ int msa_pool_encode(int dtype, const void* x, const int64_t* tok_off, const int6
                     int d, int chunk, int l2_normalize, int out_layout, void* out, void* stream);
 
 /*
+ * msa_encode - Stage 1 at corpus scale ("Global Memory Encoding", README
+ * Inference Pipeline; paper note 核心方法 > 架构: each document's K, V and
+ * routing key K_r - the latter from an extra projector - chunk-wise mean
+ * pooled).  From the hidden states x of the memory's tokens and the
+ * projection weights, for pooled chunk c, head h:
+ *   k_bar[c,h,:]  = mean over the chunk's tokens t of (x[t,:] . W_k[h*d + e, :])_e
+ *   v_bar[c,h,:]  = the same with W_v
+ *   kr_hat[c,h,:] = the same with W_r, then / max(||.||_2, 1e-8)
+ * i.e. msa_pool_encode of the projected tokens (reading: the projections are
+ * linear, nothing is applied per token before the pool; K is stored
+ * un-rotated).  Since the mean commutes with the projection, the library
+ * pools the hidden states first (float32) and projects the pooled rows; bf16
+ * with d = 128 runs on MFMA with exact products.  Each output is rounded once
+ * to dtype.
+ *   x     [n_tok, hidden] dtype;  w_t [3*H*d, hidden] dtype: one row per output
+ *         feature, rows 0..H*d-1 for K, then V, then K_r (feature h*d + e)
+ *   tok_off, chunk_off, chunk_doc as for msa_pool_encode
+ *   k_bar, v_bar [n_chunks, H, d] dtype (rows); kr_hat in kr_layout (MSA_LAYOUT_TILED
+ *         needs d % 32 == 0 and room for ceil(n_chunks/16)*16 chunks, padding zeroed)
+ *   ws    msa_encode_workspace() bytes
+ * Errors: INVALID_ARG (NULL, sizes, layout, alignment), UNSUPPORTED (hidden not
+ * a whole number of 16-byte vectors), WORKSPACE.
+ */
+size_t msa_encode_workspace(int dtype, int64_t n_chunks, int hidden, int H, int d);
+int msa_encode(int dtype, const void* x, const void* w_t, int hidden, int H, int d, const int64_t* tok_off,
+               const int64_t* chunk_off, const int32_t* chunk_doc, int64_t n_docs, int64_t n_tok, int64_t n_chunks,
+               int chunk, int kr_layout, void* k_bar, void* v_bar, void* kr_hat, void* ws, size_t ws_bytes,
+               void* stream);
+
+/*
  * msa_route_score - Stage 2 routing score (README, Overall Design >
  * Architecture: cosine similarity, mean-pooled over heads, then token-wise
  * max; paper note 核心方法 > 架构: cosine against every document's compressed

@@ -45,6 +45,7 @@ Readings where the pages are silent (each also listed in the design notes):
       the model's document-id generation, fetched documents are appended in
       round order, the query offset is the number of documents fetched, and
       the number of rounds is fixed.
+* R32 (``encode``): K, V and K_r are linear projections of the hidden state.
 * R27-R31 (training-time path, see ``route_loss`` onwards): the routing loss
       is a supervised contrastive loss over the documents with a temperature,
       the max passes its derivative to one maximiser, the selection is held
@@ -591,3 +592,31 @@ def gather_backward(ids: np.ndarray, chunk_off: np.ndarray, ctx_grads, n_chunks:
             dvb[lo:hi] += dv[e:e + hi - lo]
             e += hi - lo
     return dkb, dvb
+
+
+# ---------------------------------------------------------------------------
+# Stage 1 from hidden states: projection, then the chunk-wise pool
+# [P2 Inference Pipeline, "Global Memory Encoding" (a forward over the corpus
+#  caches the chunk-pooled K, V, K_r); P1 架构 (each document's K/V/K_r, the
+#  routing key from an extra projector, chunk-wise mean pooled)]
+#
+# R32 K, V and K_r are linear projections of the token's hidden state (no
+#     per-token normalisation before the pool); K is stored un-rotated (R11).
+# ---------------------------------------------------------------------------
+
+def encode(x: np.ndarray, w_t: np.ndarray, tok_off: np.ndarray, chunk: int, H: int, d: int, dtype: str):
+    """Pooled stores of a memory from its tokens' hidden states (R32).
+
+    x: [n_tok, hidden]; w_t: [3*H*d, hidden], one row per output feature:
+    rows h*d + e of K, then of V, then of K_r.  Every token is projected,
+    then ``pool_encode`` pools (and, for K_r, normalises) and rounds.
+    Returns (k_bar, v_bar, kr_hat), each [n_chunks, H, d]."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_t, dtype=np.float64)
+    Hd = H * d
+    proj = x @ w.T
+    k = proj[:, :Hd].reshape(-1, H, d)
+    v = proj[:, Hd:2 * Hd].reshape(-1, H, d)
+    r = proj[:, 2 * Hd:].reshape(-1, H, d)
+    return (pool_encode(k, tok_off, chunk, False, dtype), pool_encode(v, tok_off, chunk, False, dtype),
+            pool_encode(r, tok_off, chunk, True, dtype))

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     msa_chunk_offsets,
     msa_context_append,
     msa_context_index,
+    msa_encode,
     msa_exclude_docs,
     msa_gather_kv,
     msa_pool_backward,

@@ -53,6 +53,8 @@ _SIGS = {
     "msa_route_loss": (_I, [_P, _I, _L, _P, _I, _F, _P, _P, _P]),
     "msa_route_score_backward": (_I, [_I, _P, _I, _I, _I, _I, _P, _L, _P, _P, _P, _L, _P, _P, _P]),
     "msa_pool_backward": (_I, [_I, _P, _P, _P, _P, _L, _L, _L, _I, _I, _I, _P, _P, _P]),
+    "msa_encode_workspace": (_S, [_I, _L, _I, _I, _I]),
+    "msa_encode": (_I, [_I, _P, _P, _I, _I, _I, _P, _P, _P, _L, _L, _L, _I, _I, _P, _P, _P, _P, _S, _P]),
     "msa_sparse_attn_backward_workspace": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "msa_sparse_attn_backward": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _L, _P, _P, _P, _I, _P, _P, _I, _I,
                                       _F, _P, _I, _F, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
@@ -409,3 +411,24 @@ def msa_sparse_attn_backward(q, k_bar, v_bar, ctx_row, ctx_pos, ctx_len, k_loc, 
         0 if rope_table is None else rope_table.shape[0], float(sm_scale), _ptr(dout), _ptr(dq), _ptr(dk_loc),
         _ptr(dv_loc), _ptr(dk_bar), _ptr(dv_bar), _ptr(ws), wsb, _stream(stream)))
     return dq, dk_loc, dv_loc, dk_bar, dv_bar
+
+
+def msa_encode(x, w_t, tok_off, chunk_off, chunk_doc, chunk, H, d, kr_layout=MSA_LAYOUT_ROWS, k_bar=None,
+               v_bar=None, kr_hat=None, ws=None, stream=None):
+    """Stage 1 from hidden states: x [n_tok, hidden], w_t [3*H*d, hidden]
+    (rows: K features, then V, then K_r).  Returns (k_bar, v_bar, kr_hat)."""
+    n_tok, hidden = x.shape
+    n_chunks = chunk_doc.numel()
+    dt = _dtype(x)
+    dev_ = x.device
+    if k_bar is None:
+        k_bar = torch.empty((n_chunks, H, d), dtype=x.dtype, device=dev_)
+    if v_bar is None:
+        v_bar = torch.empty((n_chunks, H, d), dtype=x.dtype, device=dev_)
+    if kr_hat is None:
+        kr_hat = torch.empty((padded_chunks(n_chunks, kr_layout), H, d), dtype=x.dtype, device=dev_)
+    ws, wsb = _ws(lib.msa_encode_workspace(dt, n_chunks, hidden, H, d), dev_, ws)
+    _check("msa_encode", lib.msa_encode(
+        dt, _ptr(x), _ptr(w_t), hidden, H, d, _ptr(tok_off), _ptr(chunk_off), _ptr(chunk_doc), tok_off.numel() - 1,
+        n_tok, n_chunks, chunk, kr_layout, _ptr(k_bar), _ptr(v_bar), _ptr(kr_hat), _ptr(ws), wsb, _stream(stream)))
+    return k_bar, v_bar, kr_hat

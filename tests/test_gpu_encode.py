@@ -1,0 +1,74 @@
+"""Parity of msa_encode (Stage 1 from hidden states) against the oracle's
+per-token projection and pool, on ragged documents with empty documents and
+partial chunks, both store layouts, the MFMA path and the vector path."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.helpers import gen, host, ragged_lengths, to_dev, to_dev_i64, untile_np
+
+pytestmark = pytest.mark.gpu
+
+M = pytest.importorskip("sparse_attention_long_msa_amd")
+
+
+def _case(seed, n_docs, hidden, H, d, chunk, bf16):
+    lens = ragged_lengths(seed, n_docs, 0, 300, n_empty=3)
+    lens[0] = 2 * chunk + 5
+    tok_off = synth.offsets(lens)
+    chunk_off = O.chunk_offsets(tok_off, chunk)
+    n_chunks = int(chunk_off[-1])
+    co_d = to_dev_i64(chunk_off)
+    cd = M.msa_chunk_doc_map(co_d, n_chunks)
+    x = gen(seed, 0, synth.T_K, (int(lens.sum()), hidden), bf16)
+    w = gen(seed, 0, synth.T_V, (3 * H * d, hidden), bf16, scale_pow2=-4)
+    return tok_off, chunk_off, n_chunks, co_d, cd, x, w
+
+
+def _check(got, ref, mag, min_exact):
+    """At most one bf16 ulp of the oracle plus the projection's error: the
+    pooled row is split into two bf16 parts (2^-17 relative), so 2^-16 of the
+    magnitude sum |pooled x| . |w| of the element (outputs of cancelling sums
+    are small next to that sum)."""
+    ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+    err = np.abs(got - ref)
+    bound = ulp + 2.0 ** -16 * mag
+    assert np.all(err <= bound), (err / bound).max()
+    assert np.mean(got == ref) >= min_exact, np.mean(got == ref)
+
+
+def _magnitudes(x, w, tok_off, chunk, H, d):
+    xa = O.pool(np.abs(x)[:, None, :], tok_off, chunk)[:, 0, :]
+    mag = (xa @ np.abs(w).T).reshape(-1, 3, H, d)
+    raw = (O.pool(x[:, None, :], tok_off, chunk)[:, 0, :] @ w[2 * H * d:].T).reshape(-1, H, d)
+    norm = np.maximum(np.sqrt((raw * raw).sum(-1, keepdims=True)), 1e-8)
+    return mag[:, 0], mag[:, 1], mag[:, 2] / norm
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("chunk", [64, 7])
+def test_encode_mfma(layout, chunk):
+    H, d, hidden = 2, 128, 320
+    tok_off, chunk_off, n_chunks, co_d, cd, x, w = _case(31, 40, hidden, H, d, chunk, True)
+    kb, vb, kr = M.msa_encode(to_dev(x, True), to_dev(w, True), to_dev_i64(tok_off), co_d, cd, chunk, H, d,
+                              kr_layout=layout)
+    rk, rv, rr = O.encode(x, w, tok_off, chunk, H, d, "bf16")
+    got_r = host(kr)
+    if layout == 1:
+        assert np.all(untile_np(got_r, got_r.shape[0])[n_chunks:] == 0)
+        got_r = untile_np(got_r, n_chunks)
+    mk, mv, mr = _magnitudes(x, w, tok_off, chunk, H, d)
+    _check(host(kb), rk, mk, 0.95)
+    _check(host(vb), rv, mv, 0.95)
+    _check(got_r, rr, mr, 0.95)
+
+
+def test_encode_vector_path_float32():
+    H, d, hidden = 2, 32, 48
+    tok_off, chunk_off, n_chunks, co_d, cd, x, w = _case(32, 25, hidden, H, d, 5, False)
+    kb, vb, kr = M.msa_encode(to_dev(x, False), to_dev(w, False), to_dev_i64(tok_off), co_d, cd, 5, H, d)
+    rk, rv, rr = O.encode(x, w, tok_off, 5, H, d, "f32")
+    for got, ref in ((kb, rk), (vb, rv), (kr, rr)):
+        np.testing.assert_allclose(host(got), ref, rtol=2e-5, atol=2e-6 * np.abs(ref).max())

@@ -466,3 +466,49 @@ def test_interleave_one_round_is_the_single_layer():
     ref = O.layer(qr[0], store, co, kb, vb, k, q, kl, vl)
     assert np.array_equal(one["rounds"][0]["ids"], ref["ids"])
     assert np.abs(one["out"] - ref["out"]).max() < 1e-13
+
+
+# ---------------------------------------------------------------- Stage 1 from hidden states (R32)
+
+def test_encode_with_identity_projections_is_pool_encode():
+    r = rng(21)
+    H, d = 2, 3
+    tok_off = np.array([0, 5, 5, 12])
+    x = r.normal(size=(12, H * d))
+    eye = np.eye(H * d)
+    kb, vb, kr = O.encode(x, np.concatenate([eye, 2 * eye, eye]), tok_off, 4, H, d, "f32")
+    xs = x.reshape(12, H, d)
+    np.testing.assert_array_equal(kb, O.pool_encode(xs, tok_off, 4, False, "f32"))
+    np.testing.assert_array_equal(vb, O.pool_encode(2 * xs, tok_off, 4, False, "f32"))
+    np.testing.assert_array_equal(kr, O.pool_encode(xs, tok_off, 4, True, "f32"))
+
+
+def test_encode_hand_worked():
+    """One document of three tokens, chunk 2, hidden 2, one head of d = 2:
+    W_k = [[1, 0], [1, 1]] (rows = features), W_v = 2 W_k, W_r = [[0, 1], [3, 0]]."""
+    x = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]])
+    wk = np.array([[1.0, 0.0], [1.0, 1.0]])
+    wt = np.concatenate([wk, 2 * wk, [[0.0, 1.0], [3.0, 0.0]]])
+    kb, vb, kr = O.encode(x, wt, np.array([0, 3]), 2, 1, 2, "f32")
+    # K per token: (1, 3), (3, 7), (5, 11); chunk means (2, 5) and (5, 11)
+    np.testing.assert_array_equal(kb[:, 0], [[2.0, 5.0], [5.0, 11.0]])
+    np.testing.assert_array_equal(vb[:, 0], [[4.0, 10.0], [10.0, 22.0]])
+    # K_r per token: (2, 3), (4, 9), (6, 15); means (3, 6) -> /sqrt(45), (6, 15) -> /sqrt(261)
+    np.testing.assert_allclose(kr[:, 0], [[3 / 45 ** 0.5, 6 / 45 ** 0.5], [6 / 261 ** 0.5, 15 / 261 ** 0.5]],
+                               rtol=1e-7)
+
+
+def test_encode_pool_commutes_with_the_projection():
+    """The mean of projected tokens is the projection of the mean token: the
+    identity the library's pool-then-project order rests on."""
+    r = rng(22)
+    H, d, hidden = 2, 4, 6
+    tok_off = np.array([0, 7, 7, 20])
+    x = r.normal(size=(20, hidden))
+    w = r.normal(size=(3 * H * d, hidden))
+    kb, vb, _ = O.encode(x, w, tok_off, 3, H, d, "f32")
+    xb = O.pool(x[:, None, :], tok_off, 3)[:, 0, :]
+    proj = xb @ w.T
+    np.testing.assert_allclose(kb, O.round_to_f32(proj[:, :H * d].reshape(-1, H, d)), rtol=2e-7, atol=1e-12)
+    np.testing.assert_allclose(vb, O.round_to_f32(proj[:, H * d:2 * H * d].reshape(-1, H, d)), rtol=2e-7,
+                               atol=1e-12)
