@@ -72,3 +72,33 @@ def test_encode_vector_path_float32():
     rk, rv, rr = O.encode(x, w, tok_off, 5, H, d, "f32")
     for got, ref in ((kb, rk), (vb, rv), (kr, rr)):
         np.testing.assert_allclose(host(got), ref, rtol=2e-5, atol=2e-6 * np.abs(ref).max())
+
+
+def test_encode_bench_workload_sampled_documents():
+    """The benchmark's launch: the 1M-token memory (2,048 documents x 512
+    tokens), hidden 2,560, tiled routing keys.  Documents are independent, so
+    the oracle encodes a sample of them on their own tokens."""
+    from synth import configs
+    from synth import device as SD
+    p = configs.PRESETS["cfg2"]()
+    hidden, H, d = 2560, p.H, p.d
+    tok_off, chunk_off = p.tok_off, p.chunk_off
+    N = p.n_chunks
+    co_d = to_dev_i64(chunk_off)
+    cd = M.msa_chunk_doc_map(co_d, N)
+    x = SD.fill(torch.empty((int(tok_off[-1]), hidden), dtype=torch.bfloat16, device="cuda"), p.seed, 0, synth.T_K)
+    w = SD.fill(torch.empty((3 * H * d, hidden), dtype=torch.bfloat16, device="cuda"), p.seed, 0, synth.T_V,
+                scale_pow2=-6)
+    kb, vb, kr = M.msa_encode(x, w, to_dev_i64(tok_off), co_d, cd, p.chunk, H, d, kr_layout=M.MSA_LAYOUT_TILED)
+    kr_rows = untile_np(host(kr), N)
+    wh = host(w)
+    for doc in (0, 777, 2047):
+        lo, hi = int(tok_off[doc]), int(tok_off[doc + 1])
+        xd = host(x[lo:hi])
+        sub = np.array([0, hi - lo])
+        rk, rv, rr = O.encode(xd, wh, sub, p.chunk, H, d, "bf16")
+        c0, c1 = int(chunk_off[doc]), int(chunk_off[doc + 1])
+        mk, mv, mr = _magnitudes(xd, wh, sub, p.chunk, H, d)
+        _check(host(kb[c0:c1]), rk, mk, 0.95)
+        _check(host(vb[c0:c1]), rv, mv, 0.95)
+        _check(kr_rows[c0:c1], rr, mr, 0.95)

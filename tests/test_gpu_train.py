@@ -234,3 +234,72 @@ def test_sparse_attn_backward(bf16, B, T, Hq, Hkv, d, L_loc, k, shared):
         err = np.abs(g - ref).max() / np.abs(ref).max()
         print(f"{name}: normwise error {err:.3g}")
         assert err <= tol, f"{name}: normwise error {err:.3g} > {tol}"
+
+
+
+def test_training_chain_at_the_bench_workload():
+    """One routed layer of the training benchmark's launch (train64k: 1,024
+    chunks, 1,024 trained tokens, 32 query heads, 1,024-token window, k = 16),
+    inputs from the same seeded device generator, every output against the
+    oracle on the GPU's own selection and maximisers."""
+    from synth import configs
+    from synth import device as SD
+    p = configs.TRAIN_PRESETS["train64k"]()
+    H, d, N, D, T, Hq, L, k = p.H, p.d, p.n_chunks, p.n_docs, p.T, p.Hq, p.L_loc, p.k
+    bf = torch.bfloat16
+    tok_off, chunk_off = p.tok_off, p.chunk_off
+    n_tok = int(tok_off[-1])
+    to_d, co_d = to_dev_i64(tok_off), to_dev_i64(chunk_off)
+    cd = M.msa_chunk_doc_map(co_d, N)
+    fill = lambda shape, seed, t, dt=bf, sp=0: SD.fill(torch.empty(shape, dtype=dt, device=dev()), seed, 0, t,
+                                                       scale_pow2=sp)
+    xr = fill((n_tok, H, d), p.seed, synth.T_KR)
+    kr = M.msa_pool_encode(xr, to_d, co_d, cd, p.chunk, True)
+    kbar = M.msa_pool_encode(fill((n_tok, H, d), p.seed, synth.T_K), to_d, co_d, cd, p.chunk, False)
+    vbar = M.msa_pool_encode(fill((n_tok, H, d), p.seed, synth.T_V), to_d, co_d, cd, p.chunk, False)
+    qr = fill((1, T, H, d), p.qseed, synth.T_QR)
+    q = fill((1, T, Hq, d), p.qseed, synth.T_Q)
+    kl = fill((1, L, H, d), p.qseed, synth.T_KLOC)
+    vl = fill((1, L, H, d), p.qseed, synth.T_VLOC)
+    dout = fill((1, T, Hq, d), p.qseed, synth.T_DOUT, torch.float32)
+    pos = np.array([synth.needle_docs(p.seed, D, p.n_needles)], dtype=np.int32)
+    score, ac, at = M.msa_route_argmax(qr, kr, cd, D)
+    loss, grad = M.msa_route_loss(score, torch.from_numpy(pos).to(dev()), 0.1)
+    dkr = torch.zeros((N, H, d), dtype=torch.float32, device=dev())
+    dqr, dkr = M.msa_route_score_backward(qr, kr, ac, at, grad, dkr)
+    ids, _ = M.msa_topk(score, k)
+    row, cpos, clen = M.msa_context_index(ids, co_d, N, p.max_doc_chunks, k * p.max_doc_chunks)
+    dkb = torch.zeros((N, H, d), dtype=torch.float32, device=dev())
+    dvb = torch.zeros_like(dkb)
+    dq, dkl, dvl, dkb, dvb = M.msa_sparse_attn_backward(q, kbar, vbar, row, cpos, clen, kl, vl, p.qpo, dout, dkb,
+                                                        dvb)
+    dxr = M.msa_pool_backward(dkr, to_d, co_d, cd, n_tok, p.chunk, x=xr)
+    # routing side
+    krh, qrh = host(kr), host(qr)
+    rs = O.route_scores(qrh, krh, chunk_off)
+    check_scores(host(score), rs, RTOL_SCORE["bf16"], k)
+    check_argmax(qrh, krh, chunk_off, host(ac), host(at))
+    rl, rg = O.route_loss(host(score), pos, 0.1)     # the loss on the GPU's own scores
+    np.testing.assert_allclose(host(loss), rl, rtol=1e-4)
+    rdq, rdk = O.route_score_backward(qrh, krh, host(ac), host(at), rg)
+    rdx = O.pool_backward(rdk, tok_off, p.chunk, x=host(xr))
+    for name, got, ref, tol in (("dq_r", dqr, rdq, 1e-4), ("dx_r", dxr, rdx, 1e-4)):
+        err = np.abs(host(got) - ref).max() / np.abs(ref).max()
+        assert err <= tol, f"{name}: normwise error {err:.3g}"
+    # attention side, on the GPU's selection; KV heads are independent, so the
+    # oracle runs one of them (its 4 query heads) at full length
+    g, G = 3, Hq // H
+    hs = slice(g * G, (g + 1) * G)
+    ids_h = host(ids)
+    kbh, vbh = host(kbar)[:, g:g + 1], host(vbar)[:, g:g + 1]
+    ctx = [O.gather(ids_h[0], chunk_off, kbh, vbh)]
+    rdq2, cg, rdkl, rdvl = O.sparse_attention_backward(host(q)[:, :, hs], ctx, host(kl)[:, :, g:g + 1],
+                                                       host(vl)[:, :, g:g + 1], p.qpo, p.rope_base,
+                                                       host(dout)[:, :, hs], sm_scale=1.0 / np.sqrt(d))
+    rdkb, rdvb = O.gather_backward(ids_h, chunk_off, cg, N)
+    for name, got, ref in (("dq", host(dq)[:, :, hs], rdq2), ("dk_loc", host(dkl)[:, :, g:g + 1], rdkl),
+                           ("dv_loc", host(dvl)[:, :, g:g + 1], rdvl), ("dk_bar", host(dkb)[:, g:g + 1], rdkb),
+                           ("dv_bar", host(dvb)[:, g:g + 1], rdvb)):
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        print(f"{name}: normwise error {err:.3g}")
+        assert err <= 1.5e-2, f"{name}: normwise error {err:.3g}"
