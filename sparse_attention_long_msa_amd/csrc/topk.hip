@@ -76,12 +76,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_pass_kernel(const float* __re
   }
 }
 
-constexpr int TW_PER_LANE = 32;                 // keys a lane loads per wave pass
-constexpr int TW_PER_WAVE = 64 * TW_PER_LANE;   // 2048
 constexpr int TW_WAVES = 4;
-constexpr int TW_PER_WG = TW_WAVES * TW_PER_WAVE;
+constexpr int TW_PL_FIRST = 8;    // keys a lane loads in the reducing passes (more waves in flight)
+constexpr int TW_PL_FINAL = 32;   // keys a lane loads in the final pass (one workgroup per query)
+constexpr int tw_per_wg(int pl) { return TW_WAVES * 64 * pl; }
 
-// Each wave selects the k best of up to TW_PER_WAVE inputs (32 per lane).
+// Each wave selects the k best of up to TW_PER_WAVE inputs (TW_PER_LANE per lane).
 // Filter first: the k-th smallest of the 64 lane minima bounds the k-th
 // smallest key from above (those k lane minima are k distinct keys), so
 // only keys <= that bound can be selected.  The survivors (at most 32 k,
@@ -89,11 +89,12 @@ constexpr int TW_PER_WG = TW_WAVES * TW_PER_WAVE;
 // Not FINAL: the wave writes its k keys to keys_out[b][wave][k].  FINAL (one
 // workgroup per query): the waves' lists are merged through LDS and written
 // as ids/vals.
-template <bool FROM_SCORES, bool FINAL>
+template <bool FROM_SCORES, bool FINAL, int TW_PER_LANE>
 __global__ __launch_bounds__(64 * TW_WAVES) void topk_wave_kernel(const float* __restrict__ scores,
                                                                   const uint64_t* __restrict__ keys_in, int64_t n,
                                                                   int k, uint64_t* __restrict__ keys_out,
                                                                   int32_t* __restrict__ ids, float* __restrict__ vals) {
+  constexpr int TW_PER_WAVE = 64 * TW_PER_LANE;
   __shared__ uint64_t surv[TW_WAVES][TW_PER_WAVE];
   const int b = blockIdx.y;
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
@@ -161,7 +162,8 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topk_wave_kernel(const float* _
 // waves of the last workgroup emit sentinel keys).
 static std::vector<int64_t> topk_wave_plan(int64_t n_docs, int k) {
   std::vector<int64_t> ns{n_docs};
-  while (ns.back() > TW_PER_WG) ns.push_back((ns.back() + TW_PER_WG - 1) / TW_PER_WG * TW_WAVES * k);
+  while (ns.back() > tw_per_wg(TW_PL_FINAL))
+    ns.push_back((ns.back() + tw_per_wg(TW_PL_FIRST) - 1) / tw_per_wg(TW_PL_FIRST) * TW_WAVES * k);
   return ns;
 }
 
@@ -202,17 +204,17 @@ extern "C" int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, in
     for (size_t p = 0; p < ns.size(); ++p) {
       const int64_t n = ns[p];
       const bool first = p == 0, last = p + 1 == ns.size();
-      const dim3 grid{unsigned(last ? 1 : (n + TW_PER_WG - 1) / TW_PER_WG), unsigned(B)};
+      const dim3 grid{unsigned(last ? 1 : (n + tw_per_wg(TW_PL_FIRST) - 1) / tw_per_wg(TW_PL_FIRST)), unsigned(B)};
       const uint64_t* kin = first ? nullptr : buf[(p - 1) % 2];
       uint64_t* kout = last ? nullptr : buf[p % 2];
       if (first && last)
-        hipLaunchKernelGGL((topk_wave_kernel<true, true>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+        hipLaunchKernelGGL((topk_wave_kernel<true, true, TW_PL_FINAL>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
       else if (first)
-        hipLaunchKernelGGL((topk_wave_kernel<true, false>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+        hipLaunchKernelGGL((topk_wave_kernel<true, false, TW_PL_FIRST>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
       else if (last)
-        hipLaunchKernelGGL((topk_wave_kernel<false, true>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+        hipLaunchKernelGGL((topk_wave_kernel<false, true, TW_PL_FINAL>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
       else
-        hipLaunchKernelGGL((topk_wave_kernel<false, false>), grid, block, 0, s, doc_score, kin, n, k, kout, ids,
+        hipLaunchKernelGGL((topk_wave_kernel<false, false, TW_PL_FIRST>), grid, block, 0, s, doc_score, kin, n, k, kout, ids,
                            vals);
       MSA_LAUNCH_CHECK();
     }
