@@ -120,7 +120,7 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(
     const float* __restrict__ Dv, int n_kb, int n_rs, float* __restrict__ part_k, float* __restrict__ part_v) {
   __shared__ __attribute__((aligned(16))) unsigned char qt[2][16 * AT_VS];
   __shared__ __attribute__((aligned(16))) unsigned char ot[2][16 * AT_VS];
-  __shared__ float slse[2][16], sD[2][16];
+  __shared__ __attribute__((aligned(16))) float slse[2][16], sD[2][16];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int lc = lane % 16, g4 = lane / 16;
   int64_t wg = blockIdx.x;
@@ -200,15 +200,21 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(
       dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, da), __builtin_bit_cast(bf16x8, vr[kk]),
                                                    dp, 0, 0, 0);
     }
-    // lane (lc, g4) holds S and dP at row 4*g4 + i, key lc
+    // lane (lc, g4) holds S and dP at row 4*g4 + i, key lc.  Rows past R
+    // carry lse = +inf (P = 0); keys past n_keys are never written.  Only
+    // the causal edge needs a mask (a uniform test finds the tiles without).
     float p[4], ds[4];
     const int j = j0 + lc;
+    const float4 l4 = *reinterpret_cast<const float4*>(&slse[buf][4 * g4]);
+    const float4 d4 = *reinterpret_cast<const float4*>(&sD[buf][4 * g4]);
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+    const bool full = j0 + 15 < ctxl || j0 + 15 - ctxl <= L_loc - T + (rt * 16) / G;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = 4 * g4 + i, r = rt * 16 + rr;
-      const bool vis = kl.valid && r < R && (j < ctxl || j - ctxl <= L_loc - T + r / G);
-      p[i] = vis ? __builtin_amdgcn_exp2f(sc[i] - slse[buf][rr]) : 0.f;
-      ds[i] = p[i] * (dp[i] - sD[buf][rr]);
+      const int r = rt * 16 + 4 * g4 + i;
+      const bool vis = full || j < ctxl || j - ctxl <= L_loc - T + r / G;
+      p[i] = vis ? __builtin_amdgcn_exp2f(sc[i] - lv[i]) : 0.f;
+      ds[i] = p[i] * (dp[i] - dv[i]);
     }
     const v4s pb = pack4(p[0], p[1], p[2], p[3]);
     const v4s sb = pack4(ds[0], ds[1], ds[2], ds[3]);
