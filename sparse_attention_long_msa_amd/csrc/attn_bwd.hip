@@ -11,14 +11,16 @@
 // and a rotation's adjoint is the rotation by the opposite angle.
 //
 // bf16, d = 128 (MFMA): the rotated query scaled by scale * log2(e) and dO
-// are staged once as bf16 rows.  dK/dV: one wave per 16-key tile holds its
-// rotated K and V as MFMA operands and walks every query row tile of its
-// head (rows staged in LDS per tile): S and dP come from
+// are staged once as bf16 rows, and every key once as its rotated K and V
+// (so that both kernels address keys affinely).  dK/dV: one wave per 16-key
+// tile holds its rotated K and V as MFMA operands and walks a range of the
+// head's query row tiles (rows staged in LDS per tile): S and dP come from
 // v_mfma_f32_16x16x32_bf16, and P, dS leave the accumulator in exactly the
 // B-operand order of v_mfma_f32_16x16x16bf16_1k, whose A operand (dO^T or
-// Q^T) is read with LDS transpose loads.  dQ: one wave per 16-row tile over a
-// key split, like the forward prefill; partial sums per split are added and
-// turned back by the query's rotation in a last pass.
+// Q^T) is read with LDS transpose loads; a reduce pass adds the ranges.  dQ:
+// one wave per 16-row tile over a key split, like the forward prefill;
+// partial sums per split are added and turned back by the query's rotation
+// in a last pass.
 #include "attn_common.h"
 
 namespace msa {
@@ -69,6 +71,53 @@ __device__ __forceinline__ BwKey bw_key(int j, int b, int ctxl, int n_keys, int 
   return k;
 }
 
+// ---------------------------------------------------------------- key preparation
+// Every key of every query once: krot[b, j, g, :] = R(pos_j) k_j (bf16, the
+// rounding the forward applies) and vg[b, j, g, :] = v_j, zero past the
+// query's keys, so that the backward kernels address keys affinely.  One
+// thread per (query, key, KV head, block of 8 rotation pairs).
+__global__ void bwd_keys_kernel(int B, int KM, int Hkv, const uint16_t* __restrict__ k_bar,
+                                const uint16_t* __restrict__ v_bar, int64_t ctx_rows,
+                                const int32_t* __restrict__ ctx_row, const int32_t* __restrict__ ctx_pos,
+                                const int32_t* __restrict__ ctx_len, int max_ctx, const uint16_t* __restrict__ k_loc,
+                                const uint16_t* __restrict__ v_loc, int L_loc, int qpo, const float2* __restrict__ tab,
+                                int P, uint16_t* __restrict__ krot, uint16_t* __restrict__ vg) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(B) * KM * Hkv * 8) return;
+  const int blk = int(i % 8);
+  const int g = int((i / 8) % Hkv);
+  const int j = int((i / (8 * Hkv)) % KM);
+  const int b = int(i / (8 * int64_t(Hkv) * KM));
+  const int ctxl = min(max(ctx_len[b], 0), max_ctx);
+  const BwKey kl = bw_key(j, b, ctxl, ctxl + L_loc, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows);
+  const int64_t o = ((int64_t(b) * KM + j) * Hkv + g) * AT_D + 8 * blk;
+  uint4 lo = make_uint4(0, 0, 0, 0), hi = lo, va = lo, vb = lo;
+  if (kl.valid) {
+    const int64_t src = (kl.row * Hkv + g) * AT_D + 8 * blk;
+    const uint16_t* kp = (kl.local ? k_loc : k_bar) + src;
+    const uint16_t* vp = (kl.local ? v_loc : v_bar) + src;
+    float a[8], bb[8];
+    unpack8(load_global(kp), a);
+    unpack8(load_global(kp + AT_D / 2), bb);
+    const float2* cs = tab + int64_t(kl.pos) * (AT_D / 2) + 8 * blk;
+    float ra[8], rb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float2 c = cs[e];
+      ra[e] = a[e] * c.x - bb[e] * c.y;
+      rb[e] = bb[e] * c.x + a[e] * c.y;
+    }
+    lo = pack8(ra);
+    hi = pack8(rb);
+    va = load_global(vp);
+    vb = load_global(vp + AT_D / 2);
+  }
+  *reinterpret_cast<uint4*>(krot + o) = lo;
+  *reinterpret_cast<uint4*>(krot + o + AT_D / 2) = hi;
+  *reinterpret_cast<uint4*>(vg + o) = va;
+  *reinterpret_cast<uint4*>(vg + o + AT_D / 2) = vb;
+}
+
 // ---------------------------------------------------------------- row preparation
 // One wave per query row (b, t, hq): D = <dO, O>; for the MFMA path also the
 // bf16 rows of dO and of the rotated query times scale * log2(e) (rotated in
@@ -112,12 +161,10 @@ struct BwRows {
 
 template <int G>
 __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(
-    int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_bar, const uint16_t* __restrict__ v_bar,
-    int64_t ctx_rows, const int32_t* __restrict__ ctx_row, const int32_t* __restrict__ ctx_pos,
-    const int32_t* __restrict__ ctx_len, int max_ctx, const uint16_t* __restrict__ k_loc,
-    const uint16_t* __restrict__ v_loc, int L_loc, int qpo, const float2* __restrict__ tab, int P,
-    const uint16_t* __restrict__ qs16, const uint16_t* __restrict__ do16, const float* __restrict__ lse,
-    const float* __restrict__ Dv, int n_kb, int n_rs, float* __restrict__ part_k, float* __restrict__ part_v) {
+    int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ krot, const uint16_t* __restrict__ vg, int KM,
+    const int32_t* __restrict__ ctx_len, int max_ctx, int L_loc, const uint16_t* __restrict__ qs16,
+    const uint16_t* __restrict__ do16, const float* __restrict__ lse, const float* __restrict__ Dv, int n_kb,
+    int n_rs, float* __restrict__ part_k, float* __restrict__ part_v) {
   __shared__ __attribute__((aligned(16))) unsigned char qt[2][16 * AT_VS];
   __shared__ __attribute__((aligned(16))) unsigned char ot[2][16 * AT_VS];
   __shared__ __attribute__((aligned(16))) float slse[2][16], sD[2][16];
@@ -141,17 +188,15 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(
   if (rt_begin >= rt_end) return;
 
   // the lane's key (column lc of every product) as rotated K and as V
-  const BwKey kl = bw_key(j0 + lc, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows);
+  const bool key_ok = j0 + lc < n_keys;
   uint4 kr[4], vr[4];
   {
-    const uint16_t* kp = (kl.local ? k_loc : k_bar) + (kl.row * Hkv + g) * AT_D + 8 * g4;
-    const uint16_t* vp = (kl.local ? v_loc : v_bar) + (kl.row * Hkv + g) * AT_D + 8 * g4;
+    const int64_t o = ((int64_t(b) * KM + min(j0 + lc, KM - 1)) * Hkv + g) * AT_D + 8 * g4;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      kr[kk] = kl.valid ? load_global(kp + 32 * kk) : make_uint4(0, 0, 0, 0);
-      vr[kk] = kl.valid ? load_global(vp + 32 * kk) : make_uint4(0, 0, 0, 0);
+      kr[kk] = load_global(krot + o + 32 * kk);
+      vr[kk] = load_global(vg + o + 32 * kk);
     }
-    rope_rotate(kr, tab + int64_t(kl.pos) * (AT_D / 2), g4);
   }
   const bool wave_live = j0 < n_keys;
   f32x4 dkT[8], dvT[8];
@@ -242,7 +287,7 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(
       if (i0 + u < n_t) compute(rt_begin + i0 + u, u & 1);
     }
   }
-  if (!kl.valid) return;
+  if (!key_ok) return;
   // partial sums of this row range: lane holds dK_rot^T, dV^T at dims
   // e = 16*dt + 4*g4 + i of key lc; the query rows carried scale * log2(e),
   // so dK_rot = sum(dS q_s) / log2(e)
@@ -316,28 +361,22 @@ __global__ void attn_bwd_dkdv_reduce_kernel(const float* __restrict__ part_k, co
 
 // ---------------------------------------------------------------- dQ (MFMA)
 // One wave per 16-row tile of a KV head, four tiles per workgroup, over one
-// key split.  Each 32-key step's rotated K and V rows go through two LDS
-// buffers; the next step loads (branch-free addressing through the split's
-// context entries cached in LDS) while the current one is computed.
+// key split.  Each 32-key step's rotated K and V rows (prepared once per
+// key) go through two LDS buffers; BW_DEPTH steps of loads are in flight.
 constexpr int BQ_KV_BYTES = 32 * AT_VS;
 
 struct BqRegs {
-  uint2 klo[2], khi[2];   // dims 4x..4x+3 and 64+4x..64+4x+3 of keys lk and 16 + lk
-  float4 c0[2], c1[2];    // their (cos, sin) rows for m = 4x..4x+3
-  uint4 v[2];             // V dims 8x..8x+7
+  uint4 k[2], v[2];       // dims 8x..8x+7 of keys lk and 16 + lk
 };
 
 template <int G>
 __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(
-    int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_bar, const uint16_t* __restrict__ v_bar,
-    int64_t ctx_rows, const int32_t* __restrict__ ctx_row, const int32_t* __restrict__ ctx_pos,
-    const int32_t* __restrict__ ctx_len, int max_ctx, const uint16_t* __restrict__ k_loc,
-    const uint16_t* __restrict__ v_loc, int L_loc, int qpo, const float2* __restrict__ tab, int P,
-    const uint16_t* __restrict__ qs16, const uint16_t* __restrict__ do16, const float* __restrict__ lse,
-    const float* __restrict__ Dv, int n_rg, int n_splits, float* __restrict__ ws_dq) {
+    int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ krot, const uint16_t* __restrict__ vg, int KM,
+    const int32_t* __restrict__ ctx_len, int max_ctx, int L_loc, const uint16_t* __restrict__ qs16,
+    const uint16_t* __restrict__ do16, const float* __restrict__ lse, const float* __restrict__ Dv, int n_rg,
+    int n_splits, float* __restrict__ ws_dq) {
   __shared__ __attribute__((aligned(16))) unsigned char kt[2][BQ_KV_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char vt[2][BQ_KV_BYTES];
-  __shared__ int2 cidx[AT_CIDX];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int lc = lane % 16, g4 = lane / 16;
   int64_t wg = blockIdx.x;
@@ -370,25 +409,17 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(
   const int kps = ((n_keys + n_splits - 1) / n_splits + 31) / 32 * 32;
   const int j_begin = split * kps;
   const int j_end = min(n_keys, j_begin + kps);
-  const CtxCache cc = stage_ctx(cidx, b, j_begin, j_end, ctxl, max_ctx, ctx_pos, P, ctx_row, ctx_rows, tid,
-                                BW_THREADS);
-  __syncthreads();
-  // staging: 16 keys per pass of the workgroup, thread (key lk, 4-dim block lx)
+  // staging: 16 keys per pass of the workgroup, thread (key lk, 8-dim block lx)
   const int lk = tid / 16, lx = tid % 16;
+  const uint16_t* kbase = krot + (int64_t(b) * KM * Hkv + g) * AT_D + 8 * lx;
+  const uint16_t* vbase = vg + (int64_t(b) * KM * Hkv + g) * AT_D + 8 * lx;
   auto load_step = [&](int jj) {
     BqRegs x;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const KeySrc ks = key_src(jj + 16 * h + lk, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row,
-                                ctx_rows, cc);
-      const uint16_t* kp = (ks.local ? k_loc : k_bar) + (ks.row * Hkv + g) * AT_D;
-      const uint16_t* vp = (ks.local ? v_loc : v_bar) + (ks.row * Hkv + g) * AT_D;
-      const float2* tp = tab + int64_t(ks.pos) * (AT_D / 2) + 4 * lx;
-      x.klo[h] = load_global8(kp + 4 * lx);
-      x.khi[h] = load_global8(kp + 64 + 4 * lx);
-      x.c0[h] = __builtin_bit_cast(float4, load_global(tp));
-      x.c1[h] = __builtin_bit_cast(float4, load_global(tp + 2));
-      x.v[h] = load_global(vp + 8 * lx);
+      const int64_t o = int64_t(min(jj + 16 * h + lk, KM - 1)) * Hkv * AT_D;
+      x.k[h] = load_global(kbase + o);
+      x.v[h] = load_global(vbase + o);
     }
     return x;
   };
@@ -396,21 +427,7 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int key = 16 * h + lk;
-      const float c[4] = {x.c0[h].x, x.c0[h].z, x.c1[h].x, x.c1[h].z};
-      const float sn[4] = {x.c0[h].y, x.c0[h].w, x.c1[h].y, x.c1[h].w};
-      const float a[4] = {__uint_as_float(x.klo[h].x << 16), __uint_as_float(x.klo[h].x & 0xFFFF0000u),
-                          __uint_as_float(x.klo[h].y << 16), __uint_as_float(x.klo[h].y & 0xFFFF0000u)};
-      const float bb[4] = {__uint_as_float(x.khi[h].x << 16), __uint_as_float(x.khi[h].x & 0xFFFF0000u),
-                           __uint_as_float(x.khi[h].y << 16), __uint_as_float(x.khi[h].y & 0xFFFF0000u)};
-      float ra[4], rb[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ra[e] = a[e] * c[e] - bb[e] * sn[e];
-        rb[e] = bb[e] * c[e] + a[e] * sn[e];
-      }
-      unsigned char* krow = kt[buf] + key * AT_VS;
-      *reinterpret_cast<uint2*>(krow + 8 * lx) = make_uint2(pack_bf16x2(ra[0], ra[1]), pack_bf16x2(ra[2], ra[3]));
-      *reinterpret_cast<uint2*>(krow + 128 + 8 * lx) = make_uint2(pack_bf16x2(rb[0], rb[1]), pack_bf16x2(rb[2], rb[3]));
+      *reinterpret_cast<uint4*>(kt[buf] + key * AT_VS + 16 * lx) = x.k[h];
       *reinterpret_cast<uint4*>(vt[buf] + key * AT_VS + 16 * lx) = x.v[h];
     }
   };
@@ -666,7 +683,7 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_bwd_vec_dkdv_kernel(
 // ---------------------------------------------------------------- plan
 struct BwdPlan {
   bool mfma;
-  size_t fwd_bytes, out_bytes, row_bytes, bf_bytes, dq_bytes, part_bytes;
+  size_t fwd_bytes, out_bytes, row_bytes, bf_bytes, dq_bytes, part_bytes, key_bytes;
   int n_rg, n_splits, n_kb, n_rs;
 };
 
@@ -686,9 +703,8 @@ static BwdPlan bwd_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int max
     const int64_t n_keys_max = int64_t(max_ctx) + L_loc;
     int64_t s = (256 + units - 1) / units;
     s = std::max<int64_t>(1, std::min<int64_t>(s, (n_keys_max + 127) / 128));
-    // a split's context entries must fit the LDS index cache
-    if (max_ctx > AT_CIDX) s = std::max<int64_t>(s, (n_keys_max + AT_CIDX - 33) / (AT_CIDX - 32));
     p.n_splits = int(s);
+    p.key_bytes = align_up(size_t(B) * size_t(n_keys_max) * Hkv * d * 2, 256);   // krot, vg
     p.dq_bytes = align_up(size_t(p.n_splits) * rows * d * 4, 256);
     p.n_kb = int((n_keys_max + 16 * BW_WAVES - 1) / (16 * BW_WAVES));
     const int64_t kunits = int64_t(B) * Hkv * p.n_kb;
@@ -706,7 +722,8 @@ extern "C" size_t msa_sparse_attn_backward_workspace(int dtype, int B, int T, in
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 2 || max_ctx < 0 || L_loc < 1 || q_pos_offset < 0 || Hq % Hkv)
     return 0;
   const msa::BwdPlan p = msa::bwd_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
-  return p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes + p.dq_bytes + 2 * p.part_bytes;
+  return p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes + p.dq_bytes + 2 * p.part_bytes +
+         2 * p.key_bytes;
 }
 
 extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
@@ -724,7 +741,8 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
   MSA_REQUIRE(B >= 1 && T >= 1 && Hq >= 1 && Hkv >= 1 && d >= 2 && max_ctx >= 1 && L_loc >= 1 && Hq % Hkv == 0,
               MSA_ERR_INVALID_ARG, fn + ": bad sizes");
   const BwdPlan p = bwd_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
-  const size_t need = p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes + p.dq_bytes + 2 * p.part_bytes;
+  const size_t need =
+      p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes + p.dq_bytes + 2 * p.part_bytes + 2 * p.key_bytes;
   MSA_REQUIRE(ws && ws_bytes >= need, MSA_ERR_WORKSPACE, fn + ": workspace too small");
   if (!p.mfma)
     MSA_REQUIRE(size_t(d) + AT_VEC_THREADS + size_t(max_ctx) + L_loc <= 16384, MSA_ERR_UNSUPPORTED,
@@ -738,6 +756,8 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
   float* ws_dq = reinterpret_cast<float*>(w + p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes);
   float* part_k = reinterpret_cast<float*>(reinterpret_cast<char*>(ws_dq) + p.dq_bytes);
   float* part_v = reinterpret_cast<float*>(reinterpret_cast<char*>(part_k) + p.part_bytes);
+  uint16_t* krot = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(part_v) + p.part_bytes);
+  uint16_t* vgat = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(krot) + p.key_bytes);
   // the forward (validates every shared argument) with the per-row log-sum-exp
   const int rc = sparse_attn(fn, dtype, q, B, T, Hq, Hkv, d, k_bar, v_bar, ctx_row, n_chunks, ctx_pos, ctx_len,
                              max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows,
@@ -762,14 +782,19 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
     const dim3 kgrid(unsigned(int64_t(B) * Hkv * p.n_kb * p.n_rs)),
         qgrid(unsigned(int64_t(B) * Hkv * p.n_rg * p.n_splits));
 
+    const int KMK = max_ctx + L_loc;   // keys per query in the prepared key buffers
+    {
+      const int64_t n = int64_t(B) * KMK * Hkv * 8;
+      hipLaunchKernelGGL(bwd_keys_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, B, KMK, Hkv, kb, vb,
+                         n_chunks, ctx_row, ctx_pos, ctx_len, max_ctx, kl, vl, L_loc, q_pos_offset, tab, P, krot, vgat);
+      MSA_LAUNCH_CHECK();
+    }
 #define BW_LAUNCH(GV)                                                                                              \
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<GV>), kgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, kb, vb, n_chunks,   \
-                     ctx_row, ctx_pos, ctx_len, max_ctx, kl, vl, L_loc, q_pos_offset, tab, P, qs16, do16, lse, Dv, \
-                     p.n_kb, p.n_rs, part_k, part_v);                                                              \
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<GV>), kgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, krot, vgat, KMK,   \
+                     ctx_len, max_ctx, L_loc, qs16, do16, lse, Dv, p.n_kb, p.n_rs, part_k, part_v);                 \
   MSA_LAUNCH_CHECK();                                                                                              \
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<GV>), qgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, kb, vb, n_chunks,     \
-                     ctx_row, ctx_pos, ctx_len, max_ctx, kl, vl, L_loc, q_pos_offset, tab, P, qs16, do16, lse, Dv, \
-                     p.n_rg, p.n_splits, ws_dq)
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<GV>), qgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, krot, vgat, KMK,     \
+                     ctx_len, max_ctx, L_loc, qs16, do16, lse, Dv, p.n_rg, p.n_splits, ws_dq)
     switch (G) {
       case 1: BW_LAUNCH(1); break;
       case 2: BW_LAUNCH(2); break;
