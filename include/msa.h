@@ -185,7 +185,9 @@ int msa_encode(int dtype, const void* x, const void* w_t, int hidden, int H, int
  *              path (bf16, H = 8, d = 128) streams MSA_LAYOUT_TILED at full
  *              HBM rate; MSA_LAYOUT_ROWS is accepted by every path.
  *   chunk_doc  [n_chunks] int32 (msa_chunk_doc_map); entries outside
- *              [0, n_docs) are ignored
+ *              [0, n_docs) are ignored; the valid entries must be
+ *              non-decreasing (each document's chunks contiguous, as the
+ *              chunk CSR lays them out)
  *   doc_score  [B, n_docs] float32 output
  *   ws         msa_route_score_workspace() bytes (may be 0 -> ws may be NULL)
  * Errors: INVALID_ARG (NULL, non-positive sizes, bad layout), WORKSPACE,

@@ -13,8 +13,11 @@
 // LDS in fragment order.  Each head is a separate K = 128 contraction whose
 // fp32 result is scaled by 1 / (H * ||q[t,h]||) and summed, so the query is
 // never rounded after normalisation.  The epilogue takes the token max in
-// registers (DPP row reductions), a segmented max over the tile's chunks by
-// document, and one exact ordered atomic max per (query, document, run).
+// registers (DPP row reductions) and a segmented max over the tile's chunks
+// by document.  Run maxima collect in an LDS table over the documents of the
+// workgroup's chunk range; documents inside the range are then stored once,
+// and only the range's two boundary documents take an exact ordered global
+// atomic max.
 #include "common.h"
 
 namespace msa {
@@ -48,9 +51,9 @@ __device__ __forceinline__ float dpp_row_max16(float v) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // Segmented max over lanes 0..31 (one chunk each) by document id, then one
-// atomic max per run head.  doc < 0 marks a lane with no chunk.
-__device__ __forceinline__ void seg_max_emit(float v, int doc, int lane, float* __restrict__ row,
-                                             int64_t n_docs) {
+// emit(doc, max) per run head.  doc < 0 marks a lane with no chunk.
+template <class Emit>
+__device__ __forceinline__ void seg_max_emit(float v, int doc, int lane, Emit&& emit) {
 #pragma unroll
   for (int s = 1; s < 32; s <<= 1) {
     const float w = __shfl_down(v, s, 32);
@@ -59,7 +62,15 @@ __device__ __forceinline__ void seg_max_emit(float v, int doc, int lane, float* 
   }
   const int prev = __shfl_up(doc, 1, 32);
   const bool head = (lane < 32) && (lane == 0 || prev != doc);
-  if (head && doc >= 0 && doc < n_docs) atomic_max_float(row + doc, v);
+  if (head && doc >= 0) emit(doc, v);
+}
+
+// max of an LDS float through the order-preserving integer image (as atomic_max_float)
+__device__ __forceinline__ void lds_max_float(float* addr, float v) {
+  if (__float_as_int(v) >= 0)
+    atomicMax(reinterpret_cast<int*>(addr), __float_as_int(v));
+  else
+    atomicMin(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
 }
 
 // NT: 16-column tiles per column group (<= 4); UNIFORM_B: every 16-column
@@ -69,7 +80,7 @@ template <int NT, bool UNIFORM_B, bool TILED>
 __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     const uint16_t* __restrict__ q_r, int T, int J, const uint16_t* __restrict__ kr,
     const int32_t* __restrict__ chunk_doc, int64_t n_docs, int64_t n_chunks, float* __restrict__ doc_score,
-    int n_groups, int n_ranges, int64_t tiles_per_range) {
+    int n_groups, int n_ranges, int64_t tiles_per_range, int tab_cap) {
   constexpr int H = RS_H;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint4* qfrag = reinterpret_cast<uint4*>(smem);  // [NT][H][KK][64 lanes] x 16 B
@@ -98,8 +109,35 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
   const int64_t t_begin = int64_t(range) * tiles_per_range;
   int64_t t_end = t_begin + tiles_per_range;
   if (t_end > tiles_total) t_end = tiles_total;
+  if (t_begin >= t_end) return;             // a range past the last tile (whole workgroup)
   const int64_t rowE = int64_t(H) * RS_D;  // elements per chunk
   int64_t tile = t_begin + wave;
+
+  // Document table: the chunks of the range are contiguous and chunk_doc is
+  // non-decreasing, so the range covers documents doc_lo..doc_hi and every
+  // document strictly between them lies wholly inside it.  Run maxima go to an
+  // LDS table [document][query]; at the end a document wholly inside the range
+  // (for a query wholly inside this column group) is stored plainly, only the
+  // two boundary documents need global atomics.  Ranges whose table would not
+  // fit fall back to one global atomic per run.
+  float* tab = reinterpret_cast<float*>(smem + size_t(NT) * H * RS_KK * 1024 + size_t(RS_WAVES) * RS_SCRATCH +
+                                        size_t(H) * NT * 16 * 4);
+  const int64_t c_last = (t_end * TILE < n_chunks ? t_end * TILE : n_chunks) - 1;
+  const int doc_lo = chunk_doc[t_begin * TILE], doc_hi = chunk_doc[c_last];
+  const int col_end = col0 + 64 < J ? col0 + 64 : J;
+  const int q_lo = col0 / T, q_hi = (col_end - 1) / T;
+  const int nq = q_hi - q_lo + 1;
+  const bool use_tab = doc_lo >= 0 && doc_hi < n_docs && doc_lo <= doc_hi &&
+                       (int64_t(doc_hi) - doc_lo + 1) * nq <= tab_cap;
+  const int n_tab = use_tab ? (doc_hi - doc_lo + 1) * nq : 0;
+  for (int i = threadIdx.x; i < n_tab; i += RS_THREADS) tab[i] = -INFINITY;
+  // query b, document doc (in [0, n_docs)), run maximum v
+  auto emit = [&](int b, int doc, float v) {
+    if (use_tab && doc >= doc_lo && doc <= doc_hi)
+      lds_max_float(tab + (doc - doc_lo) * nq + (b - q_lo), v);
+    else
+      atomic_max_float(doc_score + int64_t(b) * n_docs + doc, v);
+  };
 
   // A operand of head h for the tile: lane (lc, g4) holds chunk row lc, elements
   // 32*kk + 8*g4 .. +8 of the head.  Row-major stores give four lanes 64
@@ -202,98 +240,115 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     }
   };
 
-  if (tile >= t_end) return;
-  for (;;) {
-    const int mydoc = (lane < TILE && tile * TILE + lane < n_chunks) ? chunk_doc[tile * TILE + lane] : -1;
+  // waves without a tile skip the loop but still reach the table's barrier
+  if (tile < t_end) {
+    for (;;) {
+      const int mydoc = (lane < TILE && tile * TILE + lane < n_chunks) ? chunk_doc[tile * TILE + lane] : -1;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) tot[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int64_t next_tile = tile + RS_WAVES;
-    // past the wave's last tile the ring refills from tile 0 (read by every
-    // wave, so cached; never used): the loop stays straight-line code and the
-    // compiler's waits on the load counter stay partial
-    const int64_t pref_tile = next_tile < t_end ? next_tile : 0;
+        for (int n = 0; n < NT; ++n) tot[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int64_t next_tile = tile + RS_WAVES;
+      // past the wave's last tile the ring refills from tile 0 (read by every
+      // wave, so cached; never used): the loop stays straight-line code and the
+      // compiler's waits on the load counter stay partial
+      const int64_t pref_tile = next_tile < t_end ? next_tile : 0;
 #pragma unroll 1
-    for (int h0 = 0; h0 < H; h0 += D) {
+      for (int h0 = 0; h0 < H; h0 += D) {
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        const int h = h0 + d, hn = h + D;
-        head_step(buf[d], h);
-        load_head(hn < H ? tile : pref_tile, hn < H ? hn : hn - H, buf[d]);
-        __builtin_amdgcn_sched_barrier(0);   // refill issued right after its head, not sunk below the ring
+        for (int d = 0; d < D; ++d) {
+          const int h = h0 + d, hn = h + D;
+          head_step(buf[d], h);
+          load_head(hn < H ? tile : pref_tile, hn < H ? hn : hn - H, buf[d]);
+          __builtin_amdgcn_sched_barrier(0);   // refill issued right after its head, not sunk below the ring
+        }
       }
-    }
-    // ---- epilogue: lane (lc, g4) holds score[chunk 16m + 4*g4 + r][column 16n + lc]
-    if constexpr (UNIFORM_B) {
-      // token max inside each query's columns, then the document max
+      // ---- epilogue: lane (lc, g4) holds score[chunk 16m + 4*g4 + r][column 16n + lc]
+      if constexpr (UNIFORM_B) {
+        // token max inside each query's columns, then the document max
 #pragma unroll
-      for (int n0 = 0; n0 < NT; ++n0) {
-        const int b = colb[n0];
-        if (b < 0) continue;
-        bool first = true;
+        for (int n0 = 0; n0 < NT; ++n0) {
+          const int b = colb[n0];
+          if (b < 0) continue;
+          bool first = true;
 #pragma unroll
-        for (int n1 = 0; n1 < n0; ++n1) first = first && (colb[n1] != b);
-        if (!first) continue;
-        float v[MT][4];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x = -INFINITY;
-#pragma unroll
-            for (int n = 0; n < NT; ++n)
-              if (colb[n] == b) x = fmaxf(x, tot[m][n][r]);
-            v[m][r] = dpp_row_max16(x);
-          }
-        if (lc == 0) {
+          for (int n1 = 0; n1 < n0; ++n1) first = first && (colb[n1] != b);
+          if (!first) continue;
+          float v[MT][4];
 #pragma unroll
           for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) scratch[16 * m + 4 * g4 + r] = v[m][r];
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        const float cv = lane < TILE ? scratch[lane] : -INFINITY;
-        seg_max_emit(cv, mydoc, lane, doc_score + int64_t(b) * n_docs, n_docs);
-        __builtin_amdgcn_wave_barrier();
-      }
-    } else {
-      // every column is handled on its own: stage [16 columns][32 chunks] in LDS
-      int* sdoc = reinterpret_cast<int*>(scratch + 16 * 33);
-      if (lane < 32) sdoc[lane] = mydoc;
+            for (int r = 0; r < 4; ++r) {
+              float x = -INFINITY;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) scratch[lc * 33 + 16 * m + 4 * g4 + r] = tot[m][n][r];
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        const int b = colb[n];
-        if (b >= 0) {
-          float* row = doc_score + int64_t(b) * n_docs;
-          float run = -INFINITY;
-          int run_doc = -1;
-          for (int i = 0; i < TILE / 4; ++i) {
-            const int rr = (TILE / 4) * g4 + i;
-            const int dd = sdoc[rr];
-            const float x = scratch[lc * 33 + rr];
-            if (dd != run_doc) {
-              if (run_doc >= 0 && run_doc < n_docs) atomic_max_float(row + run_doc, run);
-              run_doc = dd;
-              run = x;
-            } else {
-              run = fmaxf(run, x);
+              for (int n = 0; n < NT; ++n)
+                if (colb[n] == b) x = fmaxf(x, tot[m][n][r]);
+              v[m][r] = dpp_row_max16(x);
             }
+          if (lc == 0) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) scratch[16 * m + 4 * g4 + r] = v[m][r];
           }
-          if (run_doc >= 0 && run_doc < n_docs) atomic_max_float(row + run_doc, run);
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          const float cv = lane < TILE ? scratch[lane] : -INFINITY;
+          seg_max_emit(cv, mydoc, lane, [&](int doc, float v) {
+            if (doc < n_docs) emit(b, doc, v);
+          });
+          __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_wave_barrier();
+      } else {
+        // every column is handled on its own: stage [16 columns][32 chunks] in LDS
+        int* sdoc = reinterpret_cast<int*>(scratch + 16 * 33);
+        if (lane < 32) sdoc[lane] = mydoc;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) scratch[lc * 33 + 16 * m + 4 * g4 + r] = tot[m][n][r];
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          const int b = colb[n];
+          if (b >= 0) {
+            float run = -INFINITY;
+            int run_doc = -1;
+            for (int i = 0; i < TILE / 4; ++i) {
+              const int rr = (TILE / 4) * g4 + i;
+              const int dd = sdoc[rr];
+              const float x = scratch[lc * 33 + rr];
+              if (dd != run_doc) {
+                if (run_doc >= 0 && run_doc < n_docs) emit(b, run_doc, run);
+                run_doc = dd;
+                run = x;
+              } else {
+                run = fmaxf(run, x);
+              }
+            }
+            if (run_doc >= 0 && run_doc < n_docs) emit(b, run_doc, run);
+          }
+          __builtin_amdgcn_wave_barrier();
+        }
       }
+      tile = next_tile;
+      if (tile >= t_end) break;
     }
-    tile = next_tile;
-    if (tile >= t_end) break;
+  }
+  if (use_tab) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_tab; i += RS_THREADS) {
+      const float v = tab[i];
+      if (v == -INFINITY) continue;   // the fill already holds it
+      const int doc = doc_lo + i / nq, b = q_lo + i % nq;
+      float* dst = doc_score + int64_t(b) * n_docs + doc;
+      const bool own_q = b * T >= col0 && (b + 1) * T <= col_end;
+      if (doc != doc_lo && doc != doc_hi && own_q)
+        *dst = v;
+      else
+        atomic_max_float(dst, v);
+    }
   }
 }
 
@@ -386,14 +441,20 @@ extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, 
     int64_t n_ranges = std::min<int64_t>(n_cu, (tiles_total + RS_WAVES - 1) / RS_WAVES);
     if (n_groups > 1) n_ranges = (n_ranges + 7) / 8 * 8;
     const int64_t tiles_per_range = (tiles_total + n_ranges - 1) / n_ranges;
-    const size_t smem = size_t(NT) * RS_H * RS_KK * 1024 + size_t(RS_WAVES) * RS_SCRATCH + size_t(RS_H) * NT * 16 * 4;
+    const size_t smem_base =
+        size_t(NT) * RS_H * RS_KK * 1024 + size_t(RS_WAVES) * RS_SCRATCH + size_t(RS_H) * NT * 16 * 4;
+    int lds_max = 0;
+    MSA_HIP_CHECK(hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
+    // the document table takes what LDS is left, up to 32 KB
+    const int tab_cap = int(std::min<int64_t>(8192, std::max<int64_t>(0, (int64_t(lds_max) - int64_t(smem_base)) / 4)));
+    const size_t smem = smem_base + size_t(tab_cap) * 4;
     const dim3 grid(unsigned(n_ranges * n_groups)), block(RS_THREADS);
 #define RS_LAUNCH2(NTV, UNI, TIL)                                                                        \
   MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&route_score_mfma_kernel<NTV, UNI, TIL>), \
                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)));           \
   hipLaunchKernelGGL((route_score_mfma_kernel<NTV, UNI, TIL>), grid, block, smem, s,                   \
                      static_cast<const uint16_t*>(q_r), T, J, static_cast<const uint16_t*>(kr_hat),     \
-                     chunk_doc, n_docs, n_chunks, doc_score, n_groups, int(n_ranges), tiles_per_range)
+                     chunk_doc, n_docs, n_chunks, doc_score, n_groups, int(n_ranges), tiles_per_range, tab_cap)
 #define RS_LAUNCH(NTV, UNI)           \
   if (tiled) {                        \
     RS_LAUNCH2(NTV, UNI, true);       \
