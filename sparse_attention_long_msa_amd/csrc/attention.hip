@@ -348,7 +348,7 @@ constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_KS = 272;                         // bytes per key row of K_rot in LDS (256 + pad)
 constexpr int PF_K_BYTES = 32 * PF_KS;
 constexpr int PF_BUF = PF_K_BYTES + AT_V_BYTES;    // one step buffer
-constexpr int PF_DEPTH = 4;                        // steps whose loads are in flight (even)
+constexpr int PF_DEPTH = 2;                        // steps whose loads are in flight (even)
 constexpr float PF_LAZY = 8.f;                     // running-max slack (base-2 logits)
 static_assert(PF_DEPTH % 2 == 0, "step s uses LDS buffer s % 2");
 

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_pass_kernel(const float* __re
 constexpr int TW_WAVES = 4;
 constexpr int TW_PL_FIRST = 8;    // keys a lane loads in the reducing passes (more waves in flight)
 constexpr int TW_PL_FINAL = 32;   // keys a lane loads in the final pass (one workgroup per query)
+// a final pass over at most tw_per_wg(TW_PL_FIRST) candidates loads TW_PL_FIRST keys per lane
 constexpr int tw_per_wg(int pl) { return TW_WAVES * 64 * pl; }
 
 // Each wave selects the k best of up to TW_PER_WAVE inputs (TW_PER_LANE per lane).
@@ -86,9 +87,9 @@ constexpr int tw_per_wg(int pl) { return TW_WAVES * 64 * pl; }
 // smallest key from above (those k lane minima are k distinct keys), so
 // only keys <= that bound can be selected.  The survivors (at most 32 k,
 // usually about k) are compacted into LDS and sorted / merged 64 at a time.
-// Not FINAL: the wave writes its k keys to keys_out[b][wave][k].  FINAL (one
-// workgroup per query): the waves' lists are merged through LDS and written
-// as ids/vals.
+// The waves' lists are then merged through LDS into the workgroup's k best:
+// not FINAL, they go to keys_out[b][workgroup][k]; FINAL (one workgroup per
+// query), they are written as ids/vals.
 template <bool FROM_SCORES, bool FINAL, int TW_PER_LANE>
 __global__ __launch_bounds__(64 * TW_WAVES) void topk_wave_kernel(const float* __restrict__ scores,
                                                                   const uint64_t* __restrict__ keys_in, int64_t n,
@@ -139,31 +140,31 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topk_wave_kernel(const float* _
   __builtin_amdgcn_wave_barrier();
   uint64_t best = wave_sort64(lane < total ? sw[lane] : SENT, lane);
   for (int s0 = 64; s0 < total; s0 += 64) best = wave_insert(best, s0 + lane < total ? sw[s0 + lane] : SENT, lane, k);
-  if constexpr (!FINAL) {
-    if (lane < k) keys_out[(int64_t(b) * gridDim.x * TW_WAVES + wave_id) * k + lane] = best;
-  } else {
-    __syncthreads();
-    surv[wave][lane] = best;
-    __syncthreads();
-    if (wave == 0) {
-      uint64_t acc = best;
+  __syncthreads();
+  surv[wave][lane] = best;
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t acc = best;
 #pragma unroll
-      for (int w = 1; w < TW_WAVES; ++w) acc = wave_insert(acc, surv[w][lane], lane, k);
-      if (lane < k) {
+    for (int w = 1; w < TW_WAVES; ++w) acc = wave_insert(acc, surv[w][lane], lane, k);
+    if (lane < k) {
+      if constexpr (FINAL) {
         ids[int64_t(b) * k + lane] = int32_t(uint32_t(acc));
         vals[int64_t(b) * k + lane] = order_key_float(~uint32_t(acc >> 32));
+      } else {
+        keys_out[(int64_t(b) * gridDim.x + blockIdx.x) * k + lane] = acc;
       }
     }
   }
 }
 
 // Candidate counts of the wave passes: inputs > one workgroup's capacity are
-// reduced by non-final passes (every wave keeps k of its 2048 inputs; idle
-// waves of the last workgroup emit sentinel keys).
+// reduced by non-final passes (every workgroup keeps k of its 2048 inputs;
+// idle waves of the last workgroup contribute sentinel keys).
 static std::vector<int64_t> topk_wave_plan(int64_t n_docs, int k) {
   std::vector<int64_t> ns{n_docs};
   while (ns.back() > tw_per_wg(TW_PL_FINAL))
-    ns.push_back((ns.back() + tw_per_wg(TW_PL_FIRST) - 1) / tw_per_wg(TW_PL_FIRST) * TW_WAVES * k);
+    ns.push_back((ns.back() + tw_per_wg(TW_PL_FIRST) - 1) / tw_per_wg(TW_PL_FIRST) * k);
   return ns;
 }
 
@@ -207,10 +208,15 @@ extern "C" int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, in
       const dim3 grid{unsigned(last ? 1 : (n + tw_per_wg(TW_PL_FIRST) - 1) / tw_per_wg(TW_PL_FIRST)), unsigned(B)};
       const uint64_t* kin = first ? nullptr : buf[(p - 1) % 2];
       uint64_t* kout = last ? nullptr : buf[p % 2];
-      if (first && last)
+      const bool small = n <= tw_per_wg(TW_PL_FIRST);
+      if (first && last && small)
+        hipLaunchKernelGGL((topk_wave_kernel<true, true, TW_PL_FIRST>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+      else if (first && last)
         hipLaunchKernelGGL((topk_wave_kernel<true, true, TW_PL_FINAL>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
       else if (first)
         hipLaunchKernelGGL((topk_wave_kernel<true, false, TW_PL_FIRST>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+      else if (last && small)
+        hipLaunchKernelGGL((topk_wave_kernel<false, true, TW_PL_FIRST>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
       else if (last)
         hipLaunchKernelGGL((topk_wave_kernel<false, true, TW_PL_FINAL>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
       else

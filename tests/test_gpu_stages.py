@@ -102,6 +102,28 @@ def test_route_score(bf16, layout, B, T):
     assert np.argmax(got[0]) == nd
 
 
+def test_route_score_document_table_paths():
+    """64 single-token queries over a memory mixing one-chunk documents (a
+    workgroup's range holds more (document, query) pairs than its LDS table:
+    one global atomic per run), long documents (the table path: interior
+    documents stored once, boundary documents atomically), a document that
+    spans several workgroup ranges, and empty documents."""
+    H, d, B, T = 8, 128, 64, 1
+    rng = np.random.default_rng(5)
+    lens = np.concatenate([np.full(3000, 64), rng.integers(1500, 2600, 40), [100_000], [0, 0],
+                           rng.integers(1, 200, 2000), [0]]).astype(np.int64)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    raw = gen(41, 0, synth.T_KR, (n_chunks, H, d), True)
+    store = O.round_to_store(O.l2_normalize(raw.astype(np.float64)), "bf16")
+    q = gen(42, 0, synth.T_QR, (B, T, H, d), True)
+    ref = O.route_scores(q, store, chunk_off)
+    for layout in (1, 0):
+        st = tile_np(store) if layout == 1 else store
+        got = host(M.msa_route_score(to_dev(q, True), to_dev(st, True), cd, len(lens), layout=layout))
+        err = check_scores(got, ref, RTOL_SCORE["bf16"], k=16)
+        print(f"route_score table paths layout={layout}: normwise err {err:.3g}")
+
+
 def test_route_score_rescale_invariance():
     """Cosine is invariant to a positive rescale of the routing query."""
     H, d = 8, 128
