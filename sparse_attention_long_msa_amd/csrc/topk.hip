@@ -76,30 +76,38 @@ __global__ __launch_bounds__(TK_THREADS) void topk_pass_kernel(const float* __re
   }
 }
 
+// Reducing passes: 4 waves of 8 keys per lane (many workgroups in flight).
+// Final pass (one workgroup per query): the same shape when the candidates
+// fit it, else 16 waves of 16 keys per lane (up to 16,384 candidates).
 constexpr int TW_WAVES = 4;
-constexpr int TW_PL_FIRST = 8;    // keys a lane loads in the reducing passes (more waves in flight)
-constexpr int TW_PL_FINAL = 32;   // keys a lane loads in the final pass (one workgroup per query)
-// a final pass over at most tw_per_wg(TW_PL_FIRST) candidates loads TW_PL_FIRST keys per lane
-constexpr int tw_per_wg(int pl) { return TW_WAVES * 64 * pl; }
+constexpr int TW_PL_FIRST = 8;
+constexpr int TW_WAVES_WIDE = 16;
+constexpr int TW_PL_WIDE = 16;
+constexpr int tw_per_wg(int waves, int pl) { return waves * 64 * pl; }
+// survivor slots per wave: at most k lanes hold keys <= the bound, and the
+// merge stage needs 64
+constexpr int tw_slots(int k, int pl) { return k * pl > 64 ? k * pl : 64; }
 
-// Each wave selects the k best of up to TW_PER_WAVE inputs (TW_PER_LANE per lane).
+// Each wave selects the k best of up to 64 * TW_PER_LANE inputs.
 // Filter first: the k-th smallest of the 64 lane minima bounds the k-th
 // smallest key from above (those k lane minima are k distinct keys), so
-// only keys <= that bound can be selected.  The survivors (at most 32 k,
-// usually about k) are compacted into LDS and sorted / merged 64 at a time.
-// The waves' lists are then merged through LDS into the workgroup's k best:
+// only keys <= that bound can be selected.  The survivors (at most
+// k * TW_PER_LANE, usually about k) are compacted into LDS and sorted /
+// merged 64 at a time.
+// The waves' sorted lists are then merged through LDS into the workgroup's k best:
 // not FINAL, they go to keys_out[b][workgroup][k]; FINAL (one workgroup per
 // query), they are written as ids/vals.
-template <bool FROM_SCORES, bool FINAL, int TW_PER_LANE>
-__global__ __launch_bounds__(64 * TW_WAVES) void topk_wave_kernel(const float* __restrict__ scores,
-                                                                  const uint64_t* __restrict__ keys_in, int64_t n,
-                                                                  int k, uint64_t* __restrict__ keys_out,
-                                                                  int32_t* __restrict__ ids, float* __restrict__ vals) {
+template <bool FROM_SCORES, bool FINAL, int TW_PER_LANE, int W>
+__global__ __launch_bounds__(64 * W) void topk_wave_kernel(const float* __restrict__ scores,
+                                                           const uint64_t* __restrict__ keys_in, int64_t n, int k,
+                                                           uint64_t* __restrict__ keys_out, int32_t* __restrict__ ids,
+                                                           float* __restrict__ vals) {
   constexpr int TW_PER_WAVE = 64 * TW_PER_LANE;
-  __shared__ uint64_t surv[TW_WAVES][TW_PER_WAVE];
+  extern __shared__ uint64_t surv_lds[];   // [W][tw_slots(k, TW_PER_LANE)]
+  const int slots = tw_slots(k, TW_PER_LANE);
   const int b = blockIdx.y;
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int64_t wave_id = int64_t(blockIdx.x) * TW_WAVES + wave;
+  const int64_t wave_id = int64_t(blockIdx.x) * W + wave;
   const int64_t base = wave_id * TW_PER_WAVE;
   constexpr uint64_t SENT = ~uint64_t(0);
   uint64_t v[TW_PER_LANE];
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topk_wave_kernel(const float* _
   }
   const int total = __builtin_amdgcn_readlane(incl, 63);
   int pos = incl - cnt;
-  uint64_t* sw = surv[wave];
+  uint64_t* sw = surv_lds + wave * slots;
 #pragma unroll
   for (int i = 0; i < TW_PER_LANE; ++i)
     if (v[i] <= bound && v[i] != SENT) sw[pos++] = v[i];
@@ -140,13 +148,22 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topk_wave_kernel(const float* _
   __builtin_amdgcn_wave_barrier();
   uint64_t best = wave_sort64(lane < total ? sw[lane] : SENT, lane);
   for (int s0 = 64; s0 < total; s0 += 64) best = wave_insert(best, s0 + lane < total ? sw[s0 + lane] : SENT, lane, k);
+  // pairwise tree merge of the waves' sorted lists: wave w < half takes in
+  // the list of wave w + half, log2(W) rounds
+  static_assert((W & (W - 1)) == 0, "a power-of-two number of waves");
   __syncthreads();
-  surv[wave][lane] = best;
+  sw[lane] = best;
   __syncthreads();
-  if (wave == 0) {
-    uint64_t acc = best;
 #pragma unroll
-    for (int w = 1; w < TW_WAVES; ++w) acc = wave_insert(acc, surv[w][lane], lane, k);
+  for (int half = W / 2; half >= 1; half /= 2) {
+    if (wave < half) {
+      best = wave_merge_sorted(best, surv_lds[(wave + half) * slots + lane], lane, k);
+      sw[lane] = best;
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+    const uint64_t acc = best;
     if (lane < k) {
       if constexpr (FINAL) {
         ids[int64_t(b) * k + lane] = int32_t(uint32_t(acc));
@@ -162,9 +179,9 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topk_wave_kernel(const float* _
 // reduced by non-final passes (every workgroup keeps k of its 2048 inputs;
 // idle waves of the last workgroup contribute sentinel keys).
 static std::vector<int64_t> topk_wave_plan(int64_t n_docs, int k) {
+  constexpr int64_t first = tw_per_wg(TW_WAVES, TW_PL_FIRST), wide = tw_per_wg(TW_WAVES_WIDE, TW_PL_WIDE);
   std::vector<int64_t> ns{n_docs};
-  while (ns.back() > tw_per_wg(TW_PL_FINAL))
-    ns.push_back((ns.back() + tw_per_wg(TW_PL_FIRST) - 1) / tw_per_wg(TW_PL_FIRST) * k);
+  while (ns.back() > wide) ns.push_back((ns.back() + first - 1) / first * k);
   return ns;
 }
 
@@ -201,27 +218,35 @@ extern "C" int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, in
                       reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + need / 2)};
   if (k <= 64) {
     const auto ns = topk_wave_plan(n_docs, k);
-    const dim3 block(64 * TW_WAVES);
     for (size_t p = 0; p < ns.size(); ++p) {
       const int64_t n = ns[p];
       const bool first = p == 0, last = p + 1 == ns.size();
-      const dim3 grid{unsigned(last ? 1 : (n + tw_per_wg(TW_PL_FIRST) - 1) / tw_per_wg(TW_PL_FIRST)), unsigned(B)};
+      const bool wide = last && n > tw_per_wg(TW_WAVES, TW_PL_FIRST);
+      const int waves = wide ? TW_WAVES_WIDE : TW_WAVES;
+      const size_t lds = size_t(waves) * tw_slots(k, wide ? TW_PL_WIDE : TW_PL_FIRST) * sizeof(uint64_t);
+      const dim3 block(64 * waves);
+      const dim3 grid{unsigned(last ? 1 : (n + tw_per_wg(TW_WAVES, TW_PL_FIRST) - 1) / tw_per_wg(TW_WAVES, TW_PL_FIRST)),
+                      unsigned(B)};
       const uint64_t* kin = first ? nullptr : buf[(p - 1) % 2];
       uint64_t* kout = last ? nullptr : buf[p % 2];
-      const bool small = n <= tw_per_wg(TW_PL_FIRST);
-      if (first && last && small)
-        hipLaunchKernelGGL((topk_wave_kernel<true, true, TW_PL_FIRST>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
-      else if (first && last)
-        hipLaunchKernelGGL((topk_wave_kernel<true, true, TW_PL_FINAL>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
-      else if (first)
-        hipLaunchKernelGGL((topk_wave_kernel<true, false, TW_PL_FIRST>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
-      else if (last && small)
-        hipLaunchKernelGGL((topk_wave_kernel<false, true, TW_PL_FIRST>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
-      else if (last)
-        hipLaunchKernelGGL((topk_wave_kernel<false, true, TW_PL_FINAL>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
-      else
-        hipLaunchKernelGGL((topk_wave_kernel<false, false, TW_PL_FIRST>), grid, block, 0, s, doc_score, kin, n, k, kout, ids,
-                           vals);
+#define TW_LAUNCH(FS, FIN, PL, W)                                                                                   \
+  MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_wave_kernel<FS, FIN, PL, W>),               \
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));                         \
+  hipLaunchKernelGGL((topk_wave_kernel<FS, FIN, PL, W>), grid, block, lds, s, doc_score, kin, n, k, kout, ids, vals)
+      if (first && last && wide) {
+        TW_LAUNCH(true, true, TW_PL_WIDE, TW_WAVES_WIDE);
+      } else if (first && last) {
+        TW_LAUNCH(true, true, TW_PL_FIRST, TW_WAVES);
+      } else if (first) {
+        TW_LAUNCH(true, false, TW_PL_FIRST, TW_WAVES);
+      } else if (last && wide) {
+        TW_LAUNCH(false, true, TW_PL_WIDE, TW_WAVES_WIDE);
+      } else if (last) {
+        TW_LAUNCH(false, true, TW_PL_FIRST, TW_WAVES);
+      } else {
+        TW_LAUNCH(false, false, TW_PL_FIRST, TW_WAVES);
+      }
+#undef TW_LAUNCH
       MSA_LAUNCH_CHECK();
     }
     return MSA_OK;

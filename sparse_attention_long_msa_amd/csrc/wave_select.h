@@ -86,6 +86,16 @@ __device__ __forceinline__ uint64_t wave_merge64(uint64_t key, int lane) {
   return bitonic_stage<64, 32>(key, lane);
 }
 
+// the 64 smallest of two ascending lists held one key per lane, ascending:
+// the elementwise min of one list and the other reversed is bitonic and holds
+// them, and a bitonic merge sorts it (skipped when other's head does not beat
+// best's k-th key)
+__device__ __forceinline__ uint64_t wave_merge_sorted(uint64_t best, uint64_t other, int lane, int k) {
+  if (!(readlane64(other, 0) < readlane64(best, k - 1))) return best;
+  const uint64_t rev = shfl64(other, 63 - lane);
+  return wave_merge64(best < rev ? best : rev, lane);
+}
+
 __device__ __forceinline__ uint64_t wave_insert(uint64_t best, uint64_t key, int lane, int k) {
   const uint64_t thr = readlane64(best, k - 1);
   if (__ballot(key < thr) == 0) return best;

@@ -138,7 +138,10 @@ def test_route_score_rescale_invariance():
 
 
 @pytest.mark.parametrize("B,D,k", [(1, 64, 4), (1, 2048, 16), (1, 195312, 16), (32, 10518, 16), (2, 5000, 256),
-                                   (3, 4096, 1), (1, 4097, 32), (1, 9000, 9000 // 40)])
+                                   (3, 4096, 1), (1, 4097, 32), (1, 9000, 9000 // 40),
+                                   # the 16-wave final pass at its capacity (k = 64: the largest LDS),
+                                   # one past it, a second reducing pass, a reducing pass into it
+                                   (2, 16384, 64), (1, 16385, 64), (2, 1_000_000, 64), (1, 300_000, 48)])
 def test_topk_exact(B, D, k):
     r = np.random.default_rng(B * 7 + D)
     s = np.round(r.normal(size=(B, D)), 3).astype(np.float32)       # many exact ties
