@@ -854,6 +854,7 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
                 fn + ": more than 32768 keys on the vector path");
   MSA_REQUIRE(!rope_table || rope_table_rows >= p.P, MSA_ERR_INVALID_ARG,
               fn + ": rope_table has fewer rows than msa_rope_table_rows()");
+  MSA_REQUIRE(uintptr_t(rope_table) % 16 == 0, MSA_ERR_INVALID_ARG, fn + ": rope_table must be 16-byte aligned");
   hipStream_t s = as_stream(stream);
   const float2* tab = reinterpret_cast<const float2*>(rope_table);
   if (!tab) {

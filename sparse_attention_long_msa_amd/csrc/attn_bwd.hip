@@ -119,14 +119,11 @@ __global__ void bwd_keys_kernel(int B, int KM, int Hkv, const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------- row preparation
-// One wave per query row (b, t, hq): D = <dO, O>; for the MFMA path also the
-// bf16 rows of dO and of the rotated query times scale * log2(e) (rotated in
-// float32, rounded once, as the forward does).
-template <int DT, bool MF>
-__global__ __launch_bounds__(BW_THREADS) void bwd_prep_kernel(
-    const typename Elem<DT>::T* __restrict__ q, int T, int Hq, int d, int L_loc, int qpo, const float2* __restrict__ tab,
-    int P, float qscale, const float* __restrict__ out, const float* __restrict__ dout, int64_t rows,
-    float* __restrict__ Dv, uint16_t* __restrict__ qs16, uint16_t* __restrict__ do16) {
+// Vector path: one wave per query row (b, t, hq) computes D = <dO, O>.
+template <int DT>
+__global__ __launch_bounds__(BW_THREADS) void bwd_prep_kernel(const float* __restrict__ out,
+                                                              const float* __restrict__ dout, int d, int64_t rows,
+                                                              float* __restrict__ Dv) {
   const int64_t r = int64_t(blockIdx.x) * BW_WAVES + threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
   if (r >= rows) return;
@@ -135,18 +132,54 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_prep_kernel(
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
   if (lane == 0) Dv[r] = acc;
-  if (!MF) return;
+}
+
+// MFMA path (bf16, d = 128): D = <dO, O>, and the bf16 rows of dO and of the
+// rotated query times scale * log2(e) (rotated in float32, rounded once, as
+// the forward does).  Sixteen lanes per row; lane i holds dims 4i..4i+3 and
+// 64+4i..64+4i+3 (the RoPE pairs).
+__global__ __launch_bounds__(BW_THREADS) void bwd_prep128_kernel(
+    const uint16_t* __restrict__ q, int T, int Hq, int L_loc, int qpo, const float2* __restrict__ tab, int P,
+    float qscale, const float* __restrict__ out, const float* __restrict__ dout, int64_t rows, float* __restrict__ Dv,
+    uint16_t* __restrict__ qs16, uint16_t* __restrict__ do16) {
+  const int64_t r = (int64_t(blockIdx.x) * BW_THREADS + threadIdx.x) / 16;
+  const int i = threadIdx.x % 16;
+  if (r >= rows) return;   // the row's sixteen lanes leave together
+  const int64_t base = r * AT_D;
+  const float4 o0 = *reinterpret_cast<const float4*>(out + base + 4 * i);
+  const float4 o1 = *reinterpret_cast<const float4*>(out + base + 64 + 4 * i);
+  const float4 g0 = *reinterpret_cast<const float4*>(dout + base + 4 * i);
+  const float4 g1 = *reinterpret_cast<const float4*>(dout + base + 64 + 4 * i);
+  float acc = o0.x * g0.x + o0.y * g0.y + o0.z * g0.z + o0.w * g0.w + o1.x * g1.x + o1.y * g1.y + o1.z * g1.z +
+              o1.w * g1.w;
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (i == 0) Dv[r] = acc;
   const int t = int((r / Hq) % T);
   int pq = qpo + L_loc - T + t;
   pq = pq < 0 ? 0 : (pq >= P ? P - 1 : pq);
-  const int half = d / 2;
-  for (int m = lane; m < half; m += 64) {
-    const float a = Elem<DT>::load(q + r * d, m), bb = Elem<DT>::load(q + r * d, m + half);
-    const float2 cs = tab[int64_t(pq) * half + m];
-    qs16[r * d + m] = f32_to_bf16((a * cs.x - bb * cs.y) * qscale);
-    qs16[r * d + m + half] = f32_to_bf16((bb * cs.x + a * cs.y) * qscale);
+  const uint2 qa = *reinterpret_cast<const uint2*>(q + base + 4 * i);
+  const uint2 qb = *reinterpret_cast<const uint2*>(q + base + 64 + 4 * i);
+  const float4 cs0 = *reinterpret_cast<const float4*>(tab + int64_t(pq) * (AT_D / 2) + 4 * i);
+  const float4 cs1 = *reinterpret_cast<const float4*>(tab + int64_t(pq) * (AT_D / 2) + 4 * i + 2);
+  const float a[4] = {bf16_to_f32(uint16_t(qa.x)), bf16_to_f32(uint16_t(qa.x >> 16)), bf16_to_f32(uint16_t(qa.y)),
+                      bf16_to_f32(uint16_t(qa.y >> 16))};
+  const float bb[4] = {bf16_to_f32(uint16_t(qb.x)), bf16_to_f32(uint16_t(qb.x >> 16)), bf16_to_f32(uint16_t(qb.y)),
+                       bf16_to_f32(uint16_t(qb.y >> 16))};
+  const float c[4] = {cs0.x, cs0.z, cs1.x, cs1.z}, sn[4] = {cs0.y, cs0.w, cs1.y, cs1.w};
+  uint16_t ra[4], rb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ra[e] = f32_to_bf16((a[e] * c[e] - bb[e] * sn[e]) * qscale);
+    rb[e] = f32_to_bf16((bb[e] * c[e] + a[e] * sn[e]) * qscale);
   }
-  for (int e = lane; e < d; e += 64) do16[r * d + e] = f32_to_bf16(dout[r * d + e]);
+  auto pack2 = [](uint16_t lo, uint16_t hi) { return uint32_t(lo) | (uint32_t(hi) << 16); };
+  *reinterpret_cast<uint2*>(qs16 + base + 4 * i) = make_uint2(pack2(ra[0], ra[1]), pack2(ra[2], ra[3]));
+  *reinterpret_cast<uint2*>(qs16 + base + 64 + 4 * i) = make_uint2(pack2(rb[0], rb[1]), pack2(rb[2], rb[3]));
+  *reinterpret_cast<uint2*>(do16 + base + 4 * i) =
+      make_uint2(pack2(f32_to_bf16(g0.x), f32_to_bf16(g0.y)), pack2(f32_to_bf16(g0.z), f32_to_bf16(g0.w)));
+  *reinterpret_cast<uint2*>(do16 + base + 64 + 4 * i) =
+      make_uint2(pack2(f32_to_bf16(g1.x), f32_to_bf16(g1.y)), pack2(f32_to_bf16(g1.z), f32_to_bf16(g1.w)));
 }
 
 // ---------------------------------------------------------------- dK, dV (MFMA)
@@ -744,6 +777,7 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
   const size_t need =
       p.fwd_bytes + p.out_bytes + 2 * p.row_bytes + 2 * p.bf_bytes + p.dq_bytes + 2 * p.part_bytes + 2 * p.key_bytes;
   MSA_REQUIRE(ws && ws_bytes >= need, MSA_ERR_WORKSPACE, fn + ": workspace too small");
+  MSA_REQUIRE(uintptr_t(dout) % 16 == 0, MSA_ERR_INVALID_ARG, fn + ": dout must be 16-byte aligned");
   if (!p.mfma)
     MSA_REQUIRE(size_t(d) + AT_VEC_THREADS + size_t(max_ctx) + L_loc <= 16384, MSA_ERR_UNSUPPORTED,
                 fn + ": too many keys for the vector path");
@@ -771,9 +805,9 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
   const int G = Hq / Hkv;
   const unsigned prep_grid = unsigned((rows + BW_WAVES - 1) / BW_WAVES);
   if (p.mfma) {
-    hipLaunchKernelGGL((bwd_prep_kernel<MSA_BF16, true>), dim3(prep_grid), dim3(BW_THREADS), 0, s,
-                       static_cast<const uint16_t*>(q), T, Hq, d, L_loc, q_pos_offset, tab, P, sm_scale * BW_LOG2E,
-                       out, dout, rows, Dv, qs16, do16);
+    hipLaunchKernelGGL(bwd_prep128_kernel, dim3(unsigned((rows * 16 + BW_THREADS - 1) / BW_THREADS)),
+                       dim3(BW_THREADS), 0, s, static_cast<const uint16_t*>(q), T, Hq, L_loc, q_pos_offset, tab, P,
+                       sm_scale * BW_LOG2E, out, dout, rows, Dv, qs16, do16);
     MSA_LAUNCH_CHECK();
     const uint16_t* kb = static_cast<const uint16_t*>(k_bar);
     const uint16_t* vb = static_cast<const uint16_t*>(v_bar);
@@ -826,9 +860,7 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
   const size_t ksm = (size_t(d) + 2 * size_t(T) * G) * sizeof(float);
   MSA_REQUIRE(ksm <= 65536, MSA_ERR_UNSUPPORTED, fn + ": too many query rows for the vector path");
 #define BV_LAUNCH(DTV, TY)                                                                                          \
-  hipLaunchKernelGGL((bwd_prep_kernel<DTV, false>), dim3(prep_grid), dim3(BW_THREADS), 0, s,                        \
-                     static_cast<const TY*>(q), T, Hq, d, L_loc, q_pos_offset, tab, P, 0.f, out, dout, rows, Dv,    \
-                     nullptr, nullptr);                                                                             \
+  hipLaunchKernelGGL((bwd_prep_kernel<DTV>), dim3(prep_grid), dim3(BW_THREADS), 0, s, out, dout, d, rows, Dv);     \
   MSA_LAUNCH_CHECK();                                                                                               \
   hipLaunchKernelGGL((attn_bwd_vec_dq_kernel<DTV>), dim3(unsigned(rows)), dim3(AT_VEC_THREADS), qsm, s,             \
                      static_cast<const TY*>(q), B, T, Hq, Hkv, d, static_cast<const TY*>(k_bar),                    \

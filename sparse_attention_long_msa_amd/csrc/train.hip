@@ -438,12 +438,22 @@ __global__ void pool_bwd_rows_kernel(const float* __restrict__ dy, int64_t n_chu
   float4 dm = *reinterpret_cast<const float4*>(dy + c * HD + 4 * qd);
   if (x) {
     float4 mean = make_float4(0.f, 0.f, 0.f, 0.f);
+    // the token loads are independent: unrolled, eight are in flight
+#pragma unroll 8
     for (int64_t tau = t0; tau < t0 + n; ++tau) {
       const typename Elem<DT>::T* xp = x + tau * HD + 4 * qd;
-      mean.x += Elem<DT>::load(xp, 0);
-      mean.y += Elem<DT>::load(xp, 1);
-      mean.z += Elem<DT>::load(xp, 2);
-      mean.w += Elem<DT>::load(xp, 3);
+      if constexpr (DT == MSA_BF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(xp);   // four bf16 in one 8-byte load
+        mean.x += __uint_as_float(u.x << 16);
+        mean.y += __uint_as_float(u.x & 0xFFFF0000u);
+        mean.z += __uint_as_float(u.y << 16);
+        mean.w += __uint_as_float(u.y & 0xFFFF0000u);
+      } else {
+        mean.x += Elem<DT>::load(xp, 0);
+        mean.y += Elem<DT>::load(xp, 1);
+        mean.z += Elem<DT>::load(xp, 2);
+        mean.w += Elem<DT>::load(xp, 3);
+      }
     }
     const float inv_n = 1.f / float(n);
     mean = mean * inv_n;
@@ -601,7 +611,8 @@ extern "C" int msa_pool_backward(int dtype, const float* dy, const int64_t* tok_
               "msa_pool_backward: non-positive size");
   MSA_REQUIRE(d <= 64 * PB_MAXE, MSA_ERR_UNSUPPORTED, "msa_pool_backward: d > 256");
   hipStream_t s = as_stream(stream);
-  if (pool_bwd_rows(H, d) && uintptr_t(dy) % 16 == 0 && uintptr_t(dx) % 16 == 0 && n_chunks < (int64_t(1) << 31)) {
+  if (pool_bwd_rows(H, d) && uintptr_t(dy) % 16 == 0 && uintptr_t(dx) % 16 == 0 && uintptr_t(x) % 8 == 0 &&
+      n_chunks < (int64_t(1) << 31)) {
     const dim3 grid{unsigned(n_chunks)}, block{unsigned(H * d / 4)};
     if (dtype == MSA_BF16)
       hipLaunchKernelGGL(pool_bwd_rows_kernel<MSA_BF16>, grid, block, 0, s, dy, n_chunks, H, d, tok_off, chunk_off,
