@@ -364,7 +364,8 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
     const int32_t* __restrict__ ctx_row_in, int64_t ctx_rows, const float2* __restrict__ tab, int P, float scale_log2,
-    float* __restrict__ ws_o, float2* __restrict__ ws_ml, int n_splits, int n_rt, int n_rg) {
+    float* __restrict__ ws_o, float2* __restrict__ ws_ml, int n_splits, int n_rt, int n_rg, float* __restrict__ out,
+    float* __restrict__ lse) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int32_t* __restrict__ ctx_row = IDX ? ctx_row_in : nullptr;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -597,6 +598,19 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (!rok[i]) continue;
+    if (n_splits == 1) {
+      // one split: the combine's result directly, with its arithmetic
+      // (out = O / l, lse = m + log2 l; a row that saw no visible key gets 0, -inf)
+      const int64_t row = (int64_t(b) * T + trow[i]) * Hq + hqrow[i];
+      const float r = l > 0.f ? 1.f / l : 0.f;
+      float* op = out + row * AT_D;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<float4*>(op + 16 * dt + 4 * g4) =
+            make_float4(o[i][dt][0] * r, o[i][dt][1] * r, o[i][dt][2] * r, o[i][dt][3] * r);
+      if (lse && g4 == 0) lse[row] = l > 0.f ? m_run[i] + __log2f(l) : -INFINITY;
+      continue;
+    }
     const int64_t rowid = ((int64_t(split) * B + b) * T + trow[i]) * Hq + hqrow[i];
     float* op = ws_o + rowid * AT_D;
 #pragma unroll
@@ -881,7 +895,7 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
                      Hq, Hkv, static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos,     \
                      ctx_len, max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc),     \
                      L_loc, q_pos_offset, ctx_row, ctx_rows, tab, p.P, scale_log2_pf, ws_o, ws_ml, p.n_splits,       \
-                     p.n_rt, p.n_rg)
+                     p.n_rt, p.n_rg, out, lse)
 #define PF_LAUNCH(GV, RV)       \
   if (ctx_row) {                \
     PF_LAUNCH2(GV, RV, true);   \
@@ -904,6 +918,7 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
 #undef PF_LAUNCH
 #undef PF_LAUNCH2
       MSA_LAUNCH_CHECK();
+      if (p.n_splits == 1) return MSA_OK;   // the prefill wrote out (and lse) itself
       const int64_t rows = int64_t(B) * T * Hq;
       hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * (d / 4) + 255) / 256)), dim3(256), 0, s, ws_o,
                          ws_ml, p.n_splits, rows, d, out, lse);

@@ -33,20 +33,18 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
 }
 
-__global__ void zero_u64_kernel(uint64_t* __restrict__ p, int64_t n) {
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
-    p[i] = 0;
-}
-
 __global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
     p[i] = 0.f;
 }
 
-// winv[j, h] = 1 / (H * max(||q[j, h]||, eps)), one wave per (j, h)
+// winv[j, h] = 1 / (H * max(||q[j, h]||, eps)), one wave per (j, h); the
+// same launch clears the n_zero argmax keys (grid-stride)
 template <int DT>
 __global__ void qscale_kernel(const typename Elem<DT>::T* __restrict__ q, int64_t JH, int H, int d,
-                              float* __restrict__ winv) {
+                              float* __restrict__ winv, uint64_t* __restrict__ zero, int64_t n_zero) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_zero; i += int64_t(gridDim.x) * blockDim.x)
+    zero[i] = 0;
   const int64_t w = int64_t(blockIdx.x) * TR_WAVES + threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
   if (w >= JH) return;
@@ -78,6 +76,9 @@ __device__ __forceinline__ uint64_t cand_key(float s, uint32_t idx) {
 // the atomic maximum.
 constexpr int AX_NT = 4;   // 16-column tiles per pass
 
+// KKS > 0 (d = 32 KKS, H even): all operands of a head are requested
+// together, the next head's while this one is computed; KKS = 0: any d.
+template <int KKS>
 __global__ __launch_bounds__(TR_THREADS) void route_argmax_mfma_kernel(
     const uint16_t* __restrict__ q, int T, int J, int H, int d, const uint16_t* __restrict__ kr,
     const int32_t* __restrict__ chunk_doc, int64_t n_docs, int64_t n_chunks, const float* __restrict__ winv,
@@ -102,27 +103,139 @@ __global__ __launch_bounds__(TR_THREADS) void route_argmax_mfma_kernel(
     f32x4 tot[AX_NT];
 #pragma unroll
     for (int n = 0; n < AX_NT; ++n) tot[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int h = 0; h < H; ++h) {
-      f32x4 acc[AX_NT];
+    if constexpr (KKS > 0) {
+      struct HeadOps {
+        uint4 a[KKS];
+        uint4 b[KKS][AX_NT];
+      };
+      auto load_ops = [&](int h, HeadOps& o) {
 #pragma unroll
-      for (int n = 0; n < AX_NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int kk = 0; kk < kks; ++kk) {
-        const uint4 a = crow_ok ? *reinterpret_cast<const uint4*>(kr + (crow * H + h) * d + 32 * kk + 8 * g4)
-                                : make_uint4(0, 0, 0, 0);
+        for (int kk = 0; kk < KKS; ++kk) {
+          o.a[kk] = crow_ok ? *reinterpret_cast<const uint4*>(kr + (crow * H + h) * d + 32 * kk + 8 * g4)
+                            : make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int n = 0; n < AX_NT; ++n) {
+            const int col = col0 + 16 * n + lc;
+            o.b[kk][n] = col < J ? *reinterpret_cast<const uint4*>(q + (int64_t(col) * H + h) * d + 32 * kk + 8 * g4)
+                                 : make_uint4(0, 0, 0, 0);
+          }
+        }
+      };
+      auto compute = [&](int h, const HeadOps& o) {
+        f32x4 acc[AX_NT];
+#pragma unroll
+        for (int n = 0; n < AX_NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KKS; ++kk)
+#pragma unroll
+          for (int n = 0; n < AX_NT; ++n)
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_tr(o.a[kk]), as_bf16x8_tr(o.b[kk][n]), acc[n],
+                                                              0, 0, 0);
 #pragma unroll
         for (int n = 0; n < AX_NT; ++n) {
           const int col = col0 + 16 * n + lc;
-          const uint4 bq = col < J ? *reinterpret_cast<const uint4*>(q + (int64_t(col) * H + h) * d + 32 * kk + 8 * g4)
-                                   : make_uint4(0, 0, 0, 0);
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_tr(a), as_bf16x8_tr(bq), acc[n], 0, 0, 0);
+          const float wv = col < J ? winv[int64_t(col) * H + h] : 0.f;
+          tot[n] += wv * acc[n];
+        }
+      };
+      // heads in pairs; the request after the last pair repeats the last head
+      // (in bounds, never used), so no branch sits around the loads
+      HeadOps o0, o1;
+      load_ops(0, o0);
+      for (int h = 0; h < H; h += 2) {
+        load_ops(h + 1, o1);
+        compute(h, o0);
+        load_ops(min(h + 2, H - 1), o0);
+        compute(h + 1, o1);
+      }
+    } else {
+      for (int h = 0; h < H; ++h) {
+        f32x4 acc[AX_NT];
+#pragma unroll
+        for (int n = 0; n < AX_NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < kks; ++kk) {
+          const uint4 a = crow_ok ? *reinterpret_cast<const uint4*>(kr + (crow * H + h) * d + 32 * kk + 8 * g4)
+                                  : make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int n = 0; n < AX_NT; ++n) {
+            const int col = col0 + 16 * n + lc;
+            const uint4 bq = col < J ? *reinterpret_cast<const uint4*>(q + (int64_t(col) * H + h) * d + 32 * kk + 8 * g4)
+                                     : make_uint4(0, 0, 0, 0);
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_tr(a), as_bf16x8_tr(bq), acc[n], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int n = 0; n < AX_NT; ++n) {
+          const int col = col0 + 16 * n + lc;
+          const float wv = col < J ? winv[int64_t(col) * H + h] : 0.f;
+          tot[n] += wv * acc[n];
         }
       }
+    }
+    // merge rows of one document in a lane's four rows, then one atomic maximum per run
+    auto emit = [&](const uint64_t (&key)[4], int b) {
+      uint64_t run = key[0];
+      int run_doc = rdoc[0];
 #pragma unroll
-      for (int n = 0; n < AX_NT; ++n) {
-        const int col = col0 + 16 * n + lc;
-        const float wv = col < J ? winv[int64_t(col) * H + h] : 0.f;
-        tot[n] += wv * acc[n];
+      for (int i = 1; i < 4; ++i) {
+        if (rdoc[i] == run_doc) {
+          run = key[i] > run ? key[i] : run;
+        } else {
+          if (run_doc >= 0 && run_doc < n_docs)
+            atomicMax(reinterpret_cast<unsigned long long*>(keys + int64_t(b) * n_docs + run_doc),
+                      (unsigned long long)run);
+          run = key[i];
+          run_doc = rdoc[i];
+        }
       }
+      if (run_doc >= 0 && run_doc < n_docs)
+        atomicMax(reinterpret_cast<unsigned long long*>(keys + int64_t(b) * n_docs + run_doc), (unsigned long long)run);
+    };
+    // all of the wave's columns are tokens of one query: the token maximum
+    // over the whole group in registers, then one set of atomics
+    const int col_last = col0 + 16 * AX_NT - 1;
+    if (col_last < J && col0 / T == col_last / T) {
+      uint64_t key[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t c = c0 + 4 * g4 + i;
+        uint64_t kmax = 0;
+#pragma unroll
+        for (int n = 0; n < AX_NT; ++n) {
+          const int t = (col0 + 16 * n + lc) % T;
+          const uint64_t kn = rdoc[i] >= 0 ? cand_key(tot[n][i], uint32_t(c * T + t)) : 0;
+          kmax = kn > kmax ? kn : kmax;
+        }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+          const uint64_t o = shfl_xor_u64(kmax, m);
+          kmax = o > kmax ? o : kmax;
+        }
+        key[i] = kmax;
+      }
+      // the workgroup's four waves share the chunk tile (n_cg % TR_WAVES == 0)
+      // and their 256 columns one query: merge the waves through LDS first
+      const int wcol0 = (cg - cg % TR_WAVES) * 16 * AX_NT, wcol_last = wcol0 + TR_WAVES * 16 * AX_NT - 1;
+      if (n_cg % TR_WAVES == 0 && wcol_last < J && wcol0 / T == wcol_last / T) {
+        __shared__ uint64_t wk[TR_WAVES][16];
+        const int wave = threadIdx.x / 64;
+        if (lc == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wk[wave][4 * g4 + i] = key[i];
+        }
+        __syncthreads();
+        if (wave == 0 && lc == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int w = 1; w < TR_WAVES; ++w) key[i] = wk[w][4 * g4 + i] > key[i] ? wk[w][4 * g4 + i] : key[i];
+          }
+          emit(key, col0 / T);
+        }
+        return;
+      }
+      if (lc == 0) emit(key, col0 / T);
+      return;
     }
 #pragma unroll
     for (int n = 0; n < AX_NT; ++n) {
@@ -150,21 +263,7 @@ __global__ __launch_bounds__(TR_THREADS) void route_argmax_mfma_kernel(
         }
       }
       if (!col_ok || (one_query && lc != 0)) continue;
-      // merge rows of one document, then one atomic maximum per run
-      uint64_t run = key[0];
-      int run_doc = rdoc[0];
-#pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        if (rdoc[i] == run_doc) {
-          run = key[i] > run ? key[i] : run;
-        } else {
-          if (run_doc >= 0 && run_doc < n_docs) atomicMax(reinterpret_cast<unsigned long long*>(keys + int64_t(b) * n_docs + run_doc), (unsigned long long)run);
-          run = key[i];
-          run_doc = rdoc[i];
-        }
-      }
-      if (run_doc >= 0 && run_doc < n_docs)
-        atomicMax(reinterpret_cast<unsigned long long*>(keys + int64_t(b) * n_docs + run_doc), (unsigned long long)run);
+      emit(key, b);
     }
   }
 }
@@ -520,22 +619,25 @@ extern "C" int msa_route_argmax(int dtype, const void* q_r, int B, int T, int H,
   const int64_t nkey = int64_t(B) * n_docs;
   uint64_t* keys = static_cast<uint64_t*>(ws);
   float* winv = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(size_t(nkey) * 8, 256));
-  hipLaunchKernelGGL(zero_u64_kernel, dim3(grid_for(nkey, 256 * 4)), dim3(256), 0, s, keys, nkey);
-  MSA_LAUNCH_CHECK();
   const int64_t JH = int64_t(J) * H;
   if (dtype == MSA_BF16)
     hipLaunchKernelGGL(qscale_kernel<MSA_BF16>, dim3(grid_for(JH, TR_WAVES)), dim3(TR_THREADS), 0, s,
-                       static_cast<const uint16_t*>(q_r), JH, H, d, winv);
+                       static_cast<const uint16_t*>(q_r), JH, H, d, winv, keys, nkey);
   else
     hipLaunchKernelGGL(qscale_kernel<MSA_F32>, dim3(grid_for(JH, TR_WAVES)), dim3(TR_THREADS), 0, s,
-                       static_cast<const float*>(q_r), JH, H, d, winv);
+                       static_cast<const float*>(q_r), JH, H, d, winv, keys, nkey);
   MSA_LAUNCH_CHECK();
   if (argmax_mfma(dtype, d)) {
     const int64_t tiles = (n_chunks + 15) / 16;
     const int n_cg = (J + 16 * AX_NT - 1) / (16 * AX_NT);
-    hipLaunchKernelGGL(route_argmax_mfma_kernel, dim3(grid_for(tiles * n_cg, TR_WAVES)), dim3(TR_THREADS), 0, s,
-                       static_cast<const uint16_t*>(q_r), T, J, H, d, static_cast<const uint16_t*>(kr_hat),
-                       chunk_doc, n_docs, n_chunks, winv, n_cg, keys);
+    if (d == 128 && H % 2 == 0)
+      hipLaunchKernelGGL(route_argmax_mfma_kernel<4>, dim3(grid_for(tiles * n_cg, TR_WAVES)), dim3(TR_THREADS), 0, s,
+                         static_cast<const uint16_t*>(q_r), T, J, H, d, static_cast<const uint16_t*>(kr_hat),
+                         chunk_doc, n_docs, n_chunks, winv, n_cg, keys);
+    else
+      hipLaunchKernelGGL(route_argmax_mfma_kernel<0>, dim3(grid_for(tiles * n_cg, TR_WAVES)), dim3(TR_THREADS), 0, s,
+                         static_cast<const uint16_t*>(q_r), T, J, H, d, static_cast<const uint16_t*>(kr_hat),
+                         chunk_doc, n_docs, n_chunks, winv, n_cg, keys);
   } else if (dtype == MSA_BF16) {
     hipLaunchKernelGGL(route_argmax_vec_kernel<MSA_BF16>, dim3(grid_for(n_chunks * J, 256)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q_r), T, J, H, d, static_cast<const uint16_t*>(kr_hat),
