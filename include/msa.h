@@ -420,7 +420,8 @@ int msa_route_loss(const float* doc_score, int B, int64_t n_docs, const int32_t*
  *           store entries (msa_pool_backward with x carries it to the tokens)
  *   arg_chunk / arg_tok from msa_route_argmax; entries out of range or with
  *   grad 0 contribute nothing.  Float atomics: the summation order varies.
- * Errors: INVALID_ARG (NULL, sizes), UNSUPPORTED (n_chunks >= 2^31).
+ * Errors: INVALID_ARG (NULL, sizes), UNSUPPORTED (n_chunks >= 2^31,
+ * B * n_docs * H > 2^32).
  */
 int msa_route_score_backward(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
                              int64_t n_chunks, const int32_t* arg_chunk, const int32_t* arg_tok,

@@ -381,7 +381,7 @@ __global__ __launch_bounds__(TR_THREADS) void route_loss_kernel(const float* __r
 }
 
 // ---------------------------------------------------------------- routing-score backward
-// One wave per (query, document): the score's derivative reaches the
+// One wave per (query, document, head): the score's derivative reaches the
 // maximiser only, dqhat[b, t*] += g/H * kr[c*] and dkr[c*] += g/H * qhat[b, t*]
 // (float atomics: several documents share a token, several queries a chunk).
 template <int DT>
@@ -390,7 +390,9 @@ __global__ __launch_bounds__(TR_THREADS) void route_bwd_scatter_kernel(
     int64_t n_chunks, const int32_t* __restrict__ arg_chunk, const int32_t* __restrict__ arg_tok,
     const float* __restrict__ grad, int64_t n_items, int64_t n_docs, float* __restrict__ dqh,
     float* __restrict__ dkr) {
-  const int64_t it = int64_t(blockIdx.x) * TR_WAVES + threadIdx.x / 64;
+  const int64_t wv = int64_t(blockIdx.x) * TR_WAVES + threadIdx.x / 64;
+  const int64_t it = wv / H;
+  const int h = int(wv % H);
   const int lane = threadIdx.x % 64;
   if (it >= n_items) return;
   const int64_t b = it / n_docs;
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(TR_THREADS) void route_bwd_scatter_kernel(
   const float g = grad[it];
   if (c < 0 || c >= n_chunks || t < 0 || t >= T || g == 0.f) return;
   const float w = g / float(H);
-  for (int h = 0; h < H; ++h) {
+  {
     const typename Elem<DT>::T* qp = q + ((b * T + t) * H + h) * d;
     const typename Elem<DT>::T* kp = kr + (int64_t(c) * H + h) * d;
     float ss = 0.f;
@@ -678,6 +680,8 @@ extern "C" int msa_route_score_backward(int dtype, const void* q_r, int B, int T
   MSA_REQUIRE(B >= 1 && T >= 1 && H >= 1 && d >= 1 && n_docs >= 1 && n_chunks >= 1, MSA_ERR_INVALID_ARG,
               "msa_route_score_backward: non-positive size");
   MSA_REQUIRE(n_chunks < (int64_t(1) << 31), MSA_ERR_UNSUPPORTED, "msa_route_score_backward: n_chunks >= 2^31");
+  MSA_REQUIRE(int64_t(B) * n_docs * H <= (int64_t(TR_WAVES) << 30), MSA_ERR_UNSUPPORTED,
+              "msa_route_score_backward: B * n_docs * H > 2^32");   // one wave per (query, document, head)
   hipStream_t s = as_stream(stream);
   const int64_t nq = int64_t(B) * T * H * d;
   hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(nq, 256 * 4)), dim3(256), 0, s, dq_r, nq);
@@ -685,14 +689,14 @@ extern "C" int msa_route_score_backward(int dtype, const void* q_r, int B, int T
   const int64_t items = int64_t(B) * n_docs;
   const int64_t rows = int64_t(B) * T * H;
   if (dtype == MSA_BF16) {
-    hipLaunchKernelGGL(route_bwd_scatter_kernel<MSA_BF16>, dim3(grid_for(items, TR_WAVES)), dim3(TR_THREADS), 0, s,
+    hipLaunchKernelGGL(route_bwd_scatter_kernel<MSA_BF16>, dim3(grid_for(items * H, TR_WAVES)), dim3(TR_THREADS), 0, s,
                        static_cast<const uint16_t*>(q_r), T, H, d, static_cast<const uint16_t*>(kr_hat), n_chunks,
                        arg_chunk, arg_tok, grad, items, n_docs, dq_r, dkr_hat);
     MSA_LAUNCH_CHECK();
     hipLaunchKernelGGL(normalize_bwd_kernel<MSA_BF16>, dim3(grid_for(rows, TR_WAVES)), dim3(TR_THREADS), 0, s,
                        static_cast<const uint16_t*>(q_r), rows, d, dq_r);
   } else {
-    hipLaunchKernelGGL(route_bwd_scatter_kernel<MSA_F32>, dim3(grid_for(items, TR_WAVES)), dim3(TR_THREADS), 0, s,
+    hipLaunchKernelGGL(route_bwd_scatter_kernel<MSA_F32>, dim3(grid_for(items * H, TR_WAVES)), dim3(TR_THREADS), 0, s,
                        static_cast<const float*>(q_r), T, H, d, static_cast<const float*>(kr_hat), n_chunks,
                        arg_chunk, arg_tok, grad, items, n_docs, dq_r, dkr_hat);
     MSA_LAUNCH_CHECK();
