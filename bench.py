@@ -402,7 +402,9 @@ def train_main(args, torch):
     loss = torch.empty((layers, B), **f32)
     grad = torch.empty((B, D), **f32)
     dqr = torch.empty((B, T, H, d), **f32)
-    dkr, dkb, dvb = (torch.empty((N, H, d), **f32) for _ in range(3))
+    # the three accumulated store gradients share one buffer: one clearing launch per layer
+    acc = torch.empty((3, N, H, d), **f32)
+    dkr, dkb, dvb = acc[0], acc[1], acc[2]
     ids, vals = torch.empty((B, k), dtype=torch.int32, device=dev), torch.empty((B, k), **f32)
     tk_ws = torch.empty(max(M.msa_topk_workspace(B, D, k), 1), dtype=torch.uint8, device=dev)
     row, cpos, clen = (torch.empty((B, max_ctx), dtype=torch.int32, device=dev),
@@ -423,14 +425,12 @@ def train_main(args, torch):
                 ev[l][0].record(stream)
             M.msa_route_argmax(qr[l], kr[l], cd, D, doc_score=score, arg_chunk=ac, arg_tok=at, ws=ax_ws)
             M.msa_route_loss(score, pos, tau, loss=loss[l], grad=grad)
-            dkr.zero_()
+            acc.zero_()
             M.msa_route_score_backward(qr[l], kr[l], ac, at, grad, dkr, dq_r=dqr)
             M.msa_topk(score, k, ids=ids, vals=vals, ws=tk_ws)
             M.msa_context_index(ids, co_d, N, max_doc, max_ctx, ctx_row=row, ctx_pos=cpos, ctx_len=clen)
             if ev is not None:
                 ev[l][1].record(stream)
-            dkb.zero_()
-            dvb.zero_()
             M.msa_sparse_attn_backward(qq[l], kbar[l], vbar[l], row, cpos, clen, kl[l], vl[l], p.qpo, dout[l], dkb,
                                        dvb, rope_base=p.rope_base, rope_table=tab, dq=dq, dk_loc=dkl, dv_loc=dvl,
                                        ws=bw_ws)
