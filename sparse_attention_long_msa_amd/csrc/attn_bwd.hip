@@ -192,32 +192,50 @@ struct BwRows {
   float l, D;      // threads 0..15: the rows' log-sum-exp and D
 };
 
+// Row ranges of the dK/dV pass.  Key block kb holds key slots [64 kb, 64 kb + 64);
+// slots below max_ctx may be context entries, seen by every row; a block of
+// local keys only (local index >= 64 kb - max_ctx) is seen by the rows whose
+// causal horizon L_loc - T + t reaches it.  Those rows, from the first row
+// tile that can see the block, are cut into ranges of rt_per row tiles.
+__host__ __device__ inline int bw_rt_min(int kb, int max_ctx, int L_loc, int T, int G) {
+  const int t_min = kb * BW_WAVES * 16 - max_ctx - (L_loc - T);
+  return kb * BW_WAVES * 16 < max_ctx || t_min <= 0 ? 0 : (t_min * G) / 16;
+}
+__host__ __device__ inline int bw_n_ranges(int kb, int max_ctx, int L_loc, int T, int G, int n_rt, int rt_per) {
+  const int rt_min = bw_rt_min(kb, max_ctx, L_loc, T, G);
+  return rt_min >= n_rt ? 0 : (n_rt - rt_min + rt_per - 1) / rt_per;
+}
+
 template <int G>
 __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(
     int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ krot, const uint16_t* __restrict__ vg, int KM,
     const int32_t* __restrict__ ctx_len, int max_ctx, int L_loc, const uint16_t* __restrict__ qs16,
     const uint16_t* __restrict__ do16, const float* __restrict__ lse, const float* __restrict__ Dv, int n_kb,
-    int n_rs, float* __restrict__ part_k, float* __restrict__ part_v) {
+    int rt_per, int n_items, float* __restrict__ part_k, float* __restrict__ part_v) {
   __shared__ __attribute__((aligned(16))) unsigned char qt[2][16 * AT_VS];
   __shared__ __attribute__((aligned(16))) unsigned char ot[2][16 * AT_VS];
   __shared__ __attribute__((aligned(16))) float slse[2][16], sD[2][16];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int lc = lane % 16, g4 = lane / 16;
   int64_t wg = blockIdx.x;
-  const int rs = int(wg % n_rs);
-  wg /= n_rs;
-  const int kb = int(wg % n_kb);
-  wg /= n_kb;
+  const int item = int(wg % n_items);                // (key block, row range) of this (b, g)
+  wg /= n_items;
   const int g = int(wg % Hkv);
   const int b = int(wg / Hkv);
+  const int R = T * G;                               // query rows of this KV head
+  const int n_rt = (R + 15) / 16;
+  int kb = 0, rs = item;
+  for (; kb < n_kb; ++kb) {                          // uniform scalar search
+    const int nr = bw_n_ranges(kb, max_ctx, L_loc, T, G, n_rt, rt_per);
+    if (rs < nr) break;
+    rs -= nr;
+  }
+  if (kb >= n_kb) return;
   const int ctxl = min(max(ctx_len[b], 0), max_ctx);
   const int n_keys = ctxl + L_loc;
   if (kb * BW_WAVES * 16 >= n_keys) return;          // no key of this block exists for query b
   const int j0 = (kb * BW_WAVES + wave) * 16;       // this wave's 16 keys
-  const int R = T * G;                               // query rows of this KV head
-  const int n_rt = (R + 15) / 16;
-  const int per = (n_rt + n_rs - 1) / n_rs;
-  const int rt_begin = rs * per, rt_end = min(n_rt, rt_begin + per);
+  const int rt_begin = bw_rt_min(kb, max_ctx, L_loc, T, G) + rs * rt_per, rt_end = min(n_rt, rt_begin + rt_per);
   if (rt_begin >= rt_end) return;
 
   // the lane's key (column lc of every product) as rotated K and as V
@@ -339,7 +357,7 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(
 // the inverse rotation of dK, then a plain store for a local key and an
 // atomic add for a pooled row (several queries may read it).
 __global__ void attn_bwd_dkdv_reduce_kernel(const float* __restrict__ part_k, const float* __restrict__ part_v,
-                                            int n_rs, int B, int KM, int Hkv, int L_loc, int qpo,
+                                            int T, int G, int rt_per, int B, int KM, int Hkv, int L_loc, int qpo,
                                             const int32_t* __restrict__ ctx_row, int64_t ctx_rows,
                                             const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
                                             int max_ctx, const float2* __restrict__ tab, int P,
@@ -357,7 +375,8 @@ __global__ void attn_bwd_dkdv_reduce_kernel(const float* __restrict__ part_k, co
   if (j >= n_keys) return;
   const BwKey kl = bw_key(j, b, ctxl, n_keys, max_ctx, L_loc, qpo, ctx_pos, P, ctx_row, ctx_rows);
   float4 ka = make_float4(0.f, 0.f, 0.f, 0.f), kb = ka, va = ka, vb = ka;
-  for (int r = 0; r < n_rs; ++r) {
+  const int n_ranges = bw_n_ranges(j / (BW_WAVES * 16), max_ctx, L_loc, T, G, (T * G + 15) / 16, rt_per);
+  for (int r = 0; r < n_ranges; ++r) {
     const int64_t o = (((int64_t(r) * B + b) * KM + j) * Hkv + g) * AT_D + 4 * qd;
     ka += *reinterpret_cast<const float4*>(part_k + o);
     kb += *reinterpret_cast<const float4*>(part_k + o + AT_D / 2);
@@ -717,7 +736,7 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_bwd_vec_dkdv_kernel(
 struct BwdPlan {
   bool mfma;
   size_t fwd_bytes, out_bytes, row_bytes, bf_bytes, dq_bytes, part_bytes, key_bytes;
-  int n_rg, n_splits, n_kb, n_rs;
+  int n_rg, n_splits, n_kb, rt_per, n_items;
 };
 
 static BwdPlan bwd_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc, int qpo) {
@@ -740,10 +759,17 @@ static BwdPlan bwd_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int max
     p.key_bytes = align_up(size_t(B) * size_t(n_keys_max) * Hkv * d * 2, 256);   // krot, vg
     p.dq_bytes = align_up(size_t(p.n_splits) * rows * d * 4, 256);
     p.n_kb = int((n_keys_max + 16 * BW_WAVES - 1) / (16 * BW_WAVES));
-    const int64_t kunits = int64_t(B) * Hkv * p.n_kb;
-    // about two workgroups per CU in one round
-    p.n_rs = int(std::max<int64_t>(1, std::min<int64_t>(512 / kunits, n_rt)));
-    p.part_bytes = align_up(size_t(p.n_rs) * B * size_t(p.n_kb) * BW_WAVES * 16 * Hkv * d * 4, 256);
+    // dK/dV: the visible row tiles of every key block in ranges of rt_per
+    // tiles, sized for about 1,024 workgroups (four per CU), at most 8 ranges
+    // per block (the partial sums a key carries)
+    int64_t vis = 0;
+    for (int kb = 0; kb < p.n_kb; ++kb) vis += n_rt - bw_rt_min(kb, max_ctx, L_loc, T, G);
+    vis *= int64_t(B) * Hkv;
+    p.rt_per = int(std::max<int64_t>({(vis + 1023) / 1024, (n_rt + 7) / 8, 1}));
+    p.n_items = 0;
+    for (int kb = 0; kb < p.n_kb; ++kb) p.n_items += bw_n_ranges(kb, max_ctx, L_loc, T, G, n_rt, p.rt_per);
+    const int max_nr = (n_rt + p.rt_per - 1) / p.rt_per;
+    p.part_bytes = align_up(size_t(max_nr) * B * size_t(p.n_kb) * BW_WAVES * 16 * Hkv * d * 4, 256);
   }
   return p;
 }
@@ -813,7 +839,7 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
     const uint16_t* vb = static_cast<const uint16_t*>(v_bar);
     const uint16_t* kl = static_cast<const uint16_t*>(k_loc);
     const uint16_t* vl = static_cast<const uint16_t*>(v_loc);
-    const dim3 kgrid(unsigned(int64_t(B) * Hkv * p.n_kb * p.n_rs)),
+    const dim3 kgrid(unsigned(int64_t(B) * Hkv * p.n_items)),
         qgrid(unsigned(int64_t(B) * Hkv * p.n_rg * p.n_splits));
 
     const int KMK = max_ctx + L_loc;   // keys per query in the prepared key buffers
@@ -825,7 +851,7 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
     }
 #define BW_LAUNCH(GV)                                                                                              \
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<GV>), kgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, krot, vgat, KMK,   \
-                     ctx_len, max_ctx, L_loc, qs16, do16, lse, Dv, p.n_kb, p.n_rs, part_k, part_v);                 \
+                     ctx_len, max_ctx, L_loc, qs16, do16, lse, Dv, p.n_kb, p.rt_per, p.n_items, part_k, part_v);    \
   MSA_LAUNCH_CHECK();                                                                                              \
   hipLaunchKernelGGL((attn_bwd_dq_kernel<GV>), qgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, krot, vgat, KMK,     \
                      ctx_len, max_ctx, L_loc, qs16, do16, lse, Dv, p.n_rg, p.n_splits, ws_dq)
@@ -839,14 +865,12 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
 #undef BW_LAUNCH
     MSA_LAUNCH_CHECK();
     {
-      // row ranges that hold at least one row tile (the others wrote nothing)
-      const int n_rt = (T * G + 15) / 16, per = (n_rt + p.n_rs - 1) / p.n_rs;
-      const int n_rs_used = (n_rt + per - 1) / per;
+      // every key sums the partials of its block's row ranges
       const int KM = p.n_kb * BW_WAVES * 16;
       const int64_t nr = int64_t(B) * KM * Hkv * 16;
       hipLaunchKernelGGL(attn_bwd_dkdv_reduce_kernel, dim3(unsigned((nr + 255) / 256)), dim3(256), 0, s, part_k,
-                         part_v, n_rs_used, B, KM, Hkv, L_loc, q_pos_offset, ctx_row, n_chunks, ctx_pos, ctx_len, max_ctx,
-                         tab, P, dk_loc, dv_loc, dk_bar, dv_bar);
+                         part_v, T, G, p.rt_per, B, KM, Hkv, L_loc, q_pos_offset, ctx_row, n_chunks, ctx_pos, ctx_len,
+                         max_ctx, tab, P, dk_loc, dv_loc, dk_bar, dv_bar);
       MSA_LAUNCH_CHECK();
     }
     const int64_t n = rows * (d / 2);
