@@ -27,7 +27,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int RS_WAVES = 8;
 constexpr int RS_THREADS = 64 * RS_WAVES;
-constexpr int RS_MT = 2;                 // 16-chunk row tiles per wave tile
+constexpr int RS_MT = 1;                 // 16-chunk row tiles per wave tile
 constexpr int RS_D = 128;                // head dim of the MFMA path
 constexpr int RS_H = 8;                  // heads of the MFMA path
 constexpr int RS_KK = RS_D / 32;         // k-steps of 32 per head
@@ -76,7 +76,8 @@ __device__ __forceinline__ void lds_max_float(float* addr, float v) {
 // NT: 16-column tiles per column group (<= 4); UNIFORM_B: every 16-column
 // tile belongs to one query (T % 16 == 0), so the token max is taken in
 // registers before the document max.
-template <int NT, bool UNIFORM_B, bool TILED>
+// D: head loads in flight per wave (the ring)
+template <int NT, bool UNIFORM_B, bool TILED, int D>
 __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     const uint16_t* __restrict__ q_r, int T, int J, const uint16_t* __restrict__ kr,
     const int32_t* __restrict__ chunk_doc, int64_t n_docs, int64_t n_chunks, float* __restrict__ doc_score,
@@ -165,7 +166,6 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
 
   // a ring of D head loads is in flight per wave; the first tile's first D
   // heads load while the queries are staged
-  constexpr int D = 2;
   static_assert(H % D == 0, "the head ring divides the heads");
   uint4 buf[D][MT][RS_KK];
   if (tile < t_end) {
@@ -449,17 +449,23 @@ extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, 
     const int tab_cap = int(std::min<int64_t>(8192, std::max<int64_t>(0, (int64_t(lds_max) - int64_t(smem_base)) / 4)));
     const size_t smem = smem_base + size_t(tab_cap) * 4;
     const dim3 grid(unsigned(n_ranges * n_groups)), block(RS_THREADS);
-#define RS_LAUNCH2(NTV, UNI, TIL)                                                                        \
-  MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&route_score_mfma_kernel<NTV, UNI, TIL>), \
+#define RS_LAUNCH3(NTV, UNI, TIL, DV)                                                                    \
+  MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&route_score_mfma_kernel<NTV, UNI, TIL, DV>), \
                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)));           \
-  hipLaunchKernelGGL((route_score_mfma_kernel<NTV, UNI, TIL>), grid, block, smem, s,                   \
+  hipLaunchKernelGGL((route_score_mfma_kernel<NTV, UNI, TIL, DV>), grid, block, smem, s,               \
                      static_cast<const uint16_t*>(q_r), T, J, static_cast<const uint16_t*>(kr_hat),     \
                      chunk_doc, n_docs, n_chunks, doc_score, n_groups, int(n_ranges), tiles_per_range, tab_cap)
-#define RS_LAUNCH(NTV, UNI)           \
-  if (tiled) {                        \
-    RS_LAUNCH2(NTV, UNI, true);       \
-  } else {                            \
-    RS_LAUNCH2(NTV, UNI, false);      \
+// Tiled stores stream one 16-chunk group per wave, a head at a time: one head
+// in flight per wave reads each group strictly in order and measured best
+// with one column group; column groups sharing a range (their second read
+// hits L2) measured best with two.  Row-major stores keep two.
+#define RS_LAUNCH(NTV, UNI)                    \
+  if (tiled && n_groups == 1) {                \
+    RS_LAUNCH3(NTV, UNI, true, 1);             \
+  } else if (tiled) {                          \
+    RS_LAUNCH3(NTV, UNI, true, 2);             \
+  } else {                                     \
+    RS_LAUNCH3(NTV, UNI, false, 2);            \
   }
     const bool tiled = kr_layout == MSA_LAYOUT_TILED;
     switch (NT * 2 + (uniform ? 1 : 0)) {
@@ -473,7 +479,7 @@ extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, 
       default: RS_LAUNCH(4, true); break;
     }
 #undef RS_LAUNCH
-#undef RS_LAUNCH2
+#undef RS_LAUNCH3
     MSA_LAUNCH_CHECK();
     return MSA_OK;
   }
