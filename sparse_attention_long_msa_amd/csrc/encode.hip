@@ -29,12 +29,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int EN_THREADS = 256;
 constexpr float EN_EPS = 1e-8f;
 
-// xbar[c, :] = mean of the hidden rows of chunk c (float32)
-template <int DT>
+// xbar[c, :] = mean of the hidden rows of chunk c (float32).  SPLIT (bf16
+// input, MFMA path): the mean is written instead as its two bf16 parts,
+// hi = bf16(m) to xbar_hi and lo = bf16(m - hi) to xbar_lo (n_chunks x hidden
+// each, the same bytes as the float32 row), once for every projection.
+template <int DT, bool SPLIT>
 __global__ __launch_bounds__(1024) void pool_hidden_kernel(
     const typename Elem<DT>::T* __restrict__ x, int hidden, const int64_t* __restrict__ tok_off,
     const int64_t* __restrict__ chunk_off, const int32_t* __restrict__ chunk_doc, int64_t n_docs, int64_t n_chunks,
     int chunk, float* __restrict__ xbar) {
+  static_assert(!SPLIT || DT == MSA_BF16, "the split rows serve the bf16 MFMA path");
   constexpr int VE = 16 / Elem<DT>::bytes;   // elements per 16-byte vector
   const int nv = hidden / VE;
   for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
@@ -64,10 +68,27 @@ __global__ __launch_bounds__(1024) void pool_hidden_kernel(
           acc[3] += __uint_as_float(w.w);
         }
       }
-      float* o = xbar + c * hidden + int64_t(v) * VE;
+      if constexpr (SPLIT) {
+        uint16_t* xh = reinterpret_cast<uint16_t*>(xbar);
+        uint16_t* xl = xh + n_chunks * hidden;
+        uint32_t hi[VE / 2], lo[VE / 2];
 #pragma unroll
-      for (int e = 0; e < VE; e += 4)
-        *reinterpret_cast<float4*>(o + e) = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+        for (int e = 0; e < VE / 2; ++e) {
+          const float m0 = acc[2 * e] * inv, m1 = acc[2 * e + 1] * inv;
+          const uint16_t h0 = f32_to_bf16(m0), h1 = f32_to_bf16(m1);
+          hi[e] = uint32_t(h0) | (uint32_t(h1) << 16);
+          lo[e] = uint32_t(f32_to_bf16(m0 - bf16_to_f32(h0))) | (uint32_t(f32_to_bf16(m1 - bf16_to_f32(h1))) << 16);
+        }
+        const int64_t o = c * hidden + int64_t(v) * VE;
+        *reinterpret_cast<uint4*>(xh + o) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4*>(xl + o) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      } else {
+        float* o = xbar + c * hidden + int64_t(v) * VE;
+#pragma unroll
+        for (int e = 0; e < VE; e += 4)
+          *reinterpret_cast<float4*>(o + e) =
+              make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+      }
     }
   }
 }
@@ -85,30 +106,44 @@ __device__ __forceinline__ int64_t store_index(int64_t c, int h, int e, int H, i
 
 // Workgroup = 128 pooled rows x one head (128 columns) of one of K, V, K_r;
 // wave w computes rows 32w..32w+31 (two 16-row tiles, so that each weight
-// fragment feeds two products).  A operand: the pooled rows as two bf16
-// parts (hi + lo), read by each wave; B operand: the 32-wide k-slice of the
-// head's 128 weight rows (w_t [3*H*128, hidden], one row per output feature)
-// staged once per workgroup in LDS, the next slice loading while the
-// current one is used.
+// fragment feeds two products).  A operand: the pooled rows' two bf16 parts
+// (hi + lo, written by the pooling kernel), read by each wave; B operand:
+// the 32-wide k-slice of the head's 128 weight rows (w_t [3*H*128, hidden],
+// one row per output feature) staged once per workgroup in LDS, the next
+// slice loading while the current one is used.
+// Workgroups map to (row tile, column block) XCD-aware when the column
+// blocks split evenly over the 8 XCDs (workgroup i runs on XCD i % 8): each
+// XCD owns a few column blocks, whose weights stay in its L2, and takes the
+// row tiles in order, so the workgroups sharing a row tile run together and
+// the tile is read once per XCD.
 constexpr int EN_D = 128;
 constexpr int EN_ROWS = 128;   // pooled rows per workgroup
 constexpr int EN_BS = 5;       // LDS stride of a weight row, in 16-byte pieces (4 + 1 pad)
 
 __global__ __launch_bounds__(EN_THREADS) void encode_gemm_kernel(
-    const float* __restrict__ xbar, int hidden, const uint16_t* __restrict__ w_t, int H, int64_t n_chunks,
-    int kr_tiled, uint16_t* __restrict__ k_bar, uint16_t* __restrict__ v_bar, uint16_t* __restrict__ kr_hat) {
+    const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl, int hidden, const uint16_t* __restrict__ w_t,
+    int H, int64_t n_chunks, int kr_tiled, uint16_t* __restrict__ k_bar, uint16_t* __restrict__ v_bar,
+    uint16_t* __restrict__ kr_hat) {
   __shared__ uint4 bs[2][EN_D * EN_BS];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, lc = lane % 16, g4 = lane / 16;
   const int64_t n_rt = (n_chunks + EN_ROWS - 1) / EN_ROWS;
-  const int64_t rt = blockIdx.x % n_rt;
-  const int cb = int(blockIdx.x / n_rt);          // column block: tensor * H + head
-  const int tensor = cb / H, h = cb % H;
-  const float* ap[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int64_t row = min(rt * EN_ROWS + 32 * wave + 16 * m + lc, n_chunks - 1);   // A-operand row of this lane
-    ap[m] = xbar + row * hidden + 8 * g4;
+  const int n_cb = 3 * H;                          // column blocks: tensor * H + head
+  int64_t rt;
+  int cb;
+  if (n_cb % 8 == 0) {
+    const int cpx = n_cb / 8;                      // column blocks per XCD
+    const int64_t slot = blockIdx.x / 8;
+    cb = int(blockIdx.x % 8) * cpx + int(slot % cpx);
+    rt = slot / cpx;
+  } else {
+    rt = blockIdx.x % n_rt;
+    cb = int(blockIdx.x / n_rt);
   }
+  const int tensor = cb / H, h = cb % H;
+  int64_t arow[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)   // A-operand row of this lane
+    arow[m] = min(rt * EN_ROWS + 32 * wave + 16 * m + lc, n_chunks - 1) * hidden + 8 * g4;
   // staging: thread tid copies pieces (row tid / 2, k-quarters 2 * (tid % 2) + {0, 1}) of the slice
   const int srow = tid / 2, sq = 2 * (tid % 2);
   const uint16_t* sp = w_t + (int64_t(cb) * EN_D + srow) * hidden + 8 * sq;
@@ -130,19 +165,8 @@ __global__ __launch_bounds__(EN_THREADS) void encode_gemm_kernel(
     bf16x8 ahi[2], alo[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const float4 a0 = *reinterpret_cast<const float4*>(ap[m] + k0);
-      const float4 a1 = *reinterpret_cast<const float4*>(ap[m] + k0 + 4);
-      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t h0 = f32_to_bf16(av[2 * e]), h1 = f32_to_bf16(av[2 * e + 1]);
-        const uint16_t l0 = f32_to_bf16(av[2 * e] - bf16_to_f32(h0)), l1 = f32_to_bf16(av[2 * e + 1] - bf16_to_f32(h1));
-        hi[e] = uint32_t(h0) | (uint32_t(h1) << 16);
-        lo[e] = uint32_t(l0) | (uint32_t(l1) << 16);
-      }
-      ahi[m] = __builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
-      alo[m] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+      ahi[m] = __builtin_bit_cast(bf16x8, load_global(xh + arow[m] + k0));
+      alo[m] = __builtin_bit_cast(bf16x8, load_global(xl + arow[m] + k0));
     }
     // a buffer is rewritten two slices after it was read; each wave's reads precede its next barrier
     lds_barrier_enc();
@@ -273,20 +297,25 @@ extern "C" int msa_encode(int dtype, const void* x, const void* w_t, int hidden,
   const unsigned pgrid = unsigned(std::min<int64_t>(n_chunks, 1 << 20));
   const int nv = hidden / (16 / dtype_bytes(dtype));
   const unsigned pblock = unsigned(std::min(1024, (nv + 63) / 64 * 64));   // one thread per 16-byte vector of a row
-  if (dtype == MSA_BF16)
-    hipLaunchKernelGGL(pool_hidden_kernel<MSA_BF16>, dim3(pgrid), dim3(pblock), 0, s,
+  if (encode_mfma(dtype, hidden, d))
+    hipLaunchKernelGGL((pool_hidden_kernel<MSA_BF16, true>), dim3(pgrid), dim3(pblock), 0, s,
+                       static_cast<const uint16_t*>(x), hidden, tok_off, chunk_off, chunk_doc, n_docs, n_chunks, chunk,
+                       xbar);
+  else if (dtype == MSA_BF16)
+    hipLaunchKernelGGL((pool_hidden_kernel<MSA_BF16, false>), dim3(pgrid), dim3(pblock), 0, s,
                        static_cast<const uint16_t*>(x), hidden, tok_off, chunk_off, chunk_doc, n_docs, n_chunks, chunk,
                        xbar);
   else
-    hipLaunchKernelGGL(pool_hidden_kernel<MSA_F32>, dim3(pgrid), dim3(pblock), 0, s, static_cast<const float*>(x),
-                       hidden, tok_off, chunk_off, chunk_doc, n_docs, n_chunks, chunk, xbar);
+    hipLaunchKernelGGL((pool_hidden_kernel<MSA_F32, false>), dim3(pgrid), dim3(pblock), 0, s,
+                       static_cast<const float*>(x), hidden, tok_off, chunk_off, chunk_doc, n_docs, n_chunks, chunk, xbar);
   MSA_LAUNCH_CHECK();
   const int tiled = kr_layout == MSA_LAYOUT_TILED;
   if (encode_mfma(dtype, hidden, d)) {
     const int64_t n_rt = (n_chunks + EN_ROWS - 1) / EN_ROWS;
-    hipLaunchKernelGGL(encode_gemm_kernel, dim3(unsigned(n_rt * 3 * H)), dim3(EN_THREADS), 0, s, xbar, hidden,
-                       static_cast<const uint16_t*>(w_t), H, n_chunks, tiled, static_cast<uint16_t*>(k_bar),
-                       static_cast<uint16_t*>(v_bar), static_cast<uint16_t*>(kr_hat));
+    const uint16_t* xh = reinterpret_cast<const uint16_t*>(xbar);
+    hipLaunchKernelGGL(encode_gemm_kernel, dim3(unsigned(n_rt * 3 * H)), dim3(EN_THREADS), 0, s, xh,
+                       xh + n_chunks * hidden, hidden, static_cast<const uint16_t*>(w_t), H, n_chunks, tiled,
+                       static_cast<uint16_t*>(k_bar), static_cast<uint16_t*>(v_bar), static_cast<uint16_t*>(kr_hat));
     MSA_LAUNCH_CHECK();
   } else {
     float* kr_tmp = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(size_t(n_chunks) * hidden * 4, 256));
