@@ -217,12 +217,19 @@ def main():
                 route_ev[1].record(stream)
             if ev is not None:
                 ev[l][1].record(stream)
-            runner.select()
-            if ev is not None:
-                ev[l][2].record(stream)
-            runner.assemble(co_d, kbar[l], vbar[l])
-            if ev is not None:
-                ev[l][3].record(stream)
+            if runner.indexed:
+                # top-k and the context index in one call (the final selection pass writes the index)
+                runner.select_assemble(co_d, kbar[l], vbar[l])
+                if ev is not None:
+                    ev[l][2].record(stream)
+                    ev[l][3].record(stream)
+            else:
+                runner.select()
+                if ev is not None:
+                    ev[l][2].record(stream)
+                runner.assemble(co_d, kbar[l], vbar[l])
+                if ev is not None:
+                    ev[l][3].record(stream)
             runner.attend(qq[l], kl[l], vl[l])
             if ev is not None:
                 ev[l][4].record(stream)
@@ -304,8 +311,10 @@ def main():
         "route_attn_us_per_query": round(ms_per_step * 1e3 / p.B, 1),
         "routing_GBps": round(routing_gbps, 1),
         "routing_frac_of_8TBps": round(routing_gbps / 8000, 4),
-        "stage_ms_per_step": ({"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
-                               "gather": round(stage[2], 4), "attention": round(stage[3], 4)} if args.rounds == 1 else
+        "stage_ms_per_step": (({"route_score": round(stage[0], 4), "topk_and_context_index": round(stage[1], 4),
+                                "attention": round(stage[3], 4)} if runner.indexed else
+                               {"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
+                                "gather": round(stage[2], 4), "attention": round(stage[3], 4)}) if args.rounds == 1 else
                               {"rounds_route_topk_append": round(stage[0], 4), "attention": round(stage[3], 4)}),
         "attention_GBps": round(attn_gbps, 1),
         "attention_frac_of_8TBps": round(attn_gbps / 8000, 4),
@@ -427,8 +436,8 @@ def train_main(args, torch):
             M.msa_route_loss(score, pos, tau, loss=loss[l], grad=grad)
             acc.zero_()
             M.msa_route_score_backward(qr[l], kr[l], ac, at, grad, dkr, dq_r=dqr)
-            M.msa_topk(score, k, ids=ids, vals=vals, ws=tk_ws)
-            M.msa_context_index(ids, co_d, N, max_doc, max_ctx, ctx_row=row, ctx_pos=cpos, ctx_len=clen)
+            M.msa_topk_context_index(score, k, co_d, N, max_doc, max_ctx, ids=ids, vals=vals, ctx_row=row, ctx_pos=cpos,
+                                     ctx_len=clen, ws=tk_ws)
             if ev is not None:
                 ev[l][1].record(stream)
             M.msa_sparse_attn_backward(qq[l], kbar[l], vbar[l], row, cpos, clen, kl[l], vl[l], p.qpo, dout[l], dkb,

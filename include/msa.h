@@ -286,6 +286,21 @@ int msa_context_index(const int32_t* ids, int B, int k, const int64_t* chunk_off
                       int32_t* ctx_len, void* stream);
 
 /*
+ * msa_topk_context_index - msa_topk followed by msa_context_index on its ids
+ * (Stage 2 selection and context assembly for a store in HBM), in one pass
+ * for k <= 64: the final selection pass, which holds each query's k
+ * documents, also writes their context entries.  Outputs are exactly those
+ * of the two calls (ids, vals, ctx_row, ctx_pos, ctx_len).  For k > 64 the
+ * two calls run one after the other.
+ *   arguments as for msa_topk and msa_context_index; ws: msa_topk_workspace()
+ * Errors: those of msa_topk and of msa_context_index.
+ */
+int msa_topk_context_index(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals,
+                           const int64_t* chunk_off, int max_doc_chunks, int64_t n_chunks, int max_ctx,
+                           int32_t* ctx_row, int32_t* ctx_pos, int32_t* ctx_len, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
  * msa_context_append - msa_context_index for one more round of Memory
  * Interleave: the documents ids[b, :] (rank order) are appended after the
  * ctx_len_in[b] entries already in the context, which are kept.

@@ -40,6 +40,7 @@ from ._binding import (  # noqa: F401
     msa_sparse_attn_indexed,
     msa_sparse_attn_workspace,
     msa_topk,
+    msa_topk_context_index,
     msa_tile_routing_keys,
     msa_topk_workspace,
     padded_chunks,

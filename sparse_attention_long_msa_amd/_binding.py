@@ -39,6 +39,7 @@ _SIGS = {
     "msa_gather_kv": (_I, [_I, _P, _I, _I, _P, _P, _L, _I, _P, _P, _L, _I, _I, _I, _I,
                            _P, _P, _P, _P, _P, _P, _P]),
     "msa_context_index": (_I, [_P, _I, _I, _P, _L, _I, _L, _I, _P, _P, _P, _P]),
+    "msa_topk_context_index": (_I, [_P, _I, _L, _I, _P, _P, _P, _I, _L, _I, _P, _P, _P, _P, _S, _P]),
     "msa_exclude_docs": (_I, [_P, _I, _L, _P, _I, _I, _P]),
     "msa_context_append": (_I, [_P, _I, _I, _P, _L, _I, _L, _I, _P, _P, _P, _P, _P]),
     "msa_sparse_attn_workspace": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
@@ -241,6 +242,28 @@ def msa_context_index(ids, chunk_off, n_chunks, max_doc_chunks, max_ctx, ctx_row
         _ptr(ids), B, k, _ptr(chunk_off), chunk_off.numel() - 1, max_doc_chunks, n_chunks, max_ctx, _ptr(ctx_row),
         _ptr(ctx_pos), _ptr(ctx_len), _stream(stream)))
     return ctx_row, ctx_pos, ctx_len
+
+
+def msa_topk_context_index(doc_score, k, chunk_off, n_chunks, max_doc_chunks, max_ctx, ids=None, vals=None,
+                           ctx_row=None, ctx_pos=None, ctx_len=None, ws=None, stream=None):
+    """msa_topk then msa_context_index on its ids, in one pass for k <= 64."""
+    B, n_docs = doc_score.shape
+    dev = doc_score.device
+    if ids is None:
+        ids = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty((B, k), dtype=torch.float32, device=dev)
+    if ctx_row is None:
+        ctx_row = torch.empty((B, max_ctx), dtype=torch.int32, device=dev)
+    if ctx_pos is None:
+        ctx_pos = torch.empty((B, max_ctx), dtype=torch.int32, device=dev)
+    if ctx_len is None:
+        ctx_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws, wsb = _ws(msa_topk_workspace(B, n_docs, k), dev, ws)
+    _check("msa_topk_context_index", lib.msa_topk_context_index(
+        _ptr(doc_score), B, n_docs, k, _ptr(ids), _ptr(vals), _ptr(chunk_off), max_doc_chunks, n_chunks, max_ctx,
+        _ptr(ctx_row), _ptr(ctx_pos), _ptr(ctx_len), _ptr(ws), wsb, _stream(stream)))
+    return ids, vals, ctx_row, ctx_pos, ctx_len
 
 
 def msa_exclude_docs(doc_score, ids_sets, stream=None):

@@ -88,6 +88,62 @@ constexpr int tw_per_wg(int waves, int pl) { return waves * 64 * pl; }
 // merge stage needs 64
 constexpr int tw_slots(int k, int pl) { return k * pl > 64 ? k * pl : 64; }
 
+// Optional context index of the final pass (msa_topk_context_index): the
+// selected documents' chunks, in rank order, as (store row, position in the
+// document) entries, as msa_context_index writes them.
+struct CtxOut {
+  const int64_t* chunk_off;   // NULL: no context index
+  int64_t n_docs;
+  int max_ctx;
+  int32_t* row;
+  int32_t* pos;
+  int32_t* len;
+};
+
+__device__ __forceinline__ int64_t shfl_up_i64(int64_t v, int s) {
+  const int lo = __shfl_up(int(uint32_t(uint64_t(v))), s), hi = __shfl_up(int(uint32_t(uint64_t(v) >> 32)), s);
+  return int64_t((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo));
+}
+
+// One wave, lane r < k holding the rank-r key: rank r's chunks start at the
+// exclusive prefix of the chunk counts; the entries are then written lane-
+// parallel, each finding its rank by a binary search over the starts.
+__device__ void context_index_wave(uint64_t key, int lane, int k, int b, const CtxOut& cx, int64_t* sdest,
+                                   int64_t* slo) {
+  const int32_t id = lane < k ? int32_t(uint32_t(key)) : -1;
+  int64_t lo = 0, n = 0;
+  if (id >= 0 && id < cx.n_docs) {
+    lo = cx.chunk_off[id];
+    n = cx.chunk_off[id + 1] - lo;
+  }
+  int64_t incl = n;
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) {
+    const int64_t o = shfl_up_i64(incl, sft);
+    if (lane >= sft) incl += o;
+  }
+  const int64_t dest = incl - n;
+  int64_t nc = n;
+  if (dest + nc > cx.max_ctx) nc = dest < cx.max_ctx ? cx.max_ctx - dest : 0;   // never past the context
+  if (lane == k - 1) cx.len[b] = int32_t(dest + nc);
+  sdest[lane] = dest;
+  slo[lane] = lo;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int64_t end = __shfl(int(dest + nc), k - 1);
+  const int64_t total = end < cx.max_ctx ? end : cx.max_ctx;
+  for (int64_t e = lane; e < total; e += 64) {
+    int r0 = 0, r1 = k - 1;   // the last rank whose start is <= e (empty ranks share the next start)
+    while (r0 < r1) {
+      const int mid = (r0 + r1 + 1) / 2;
+      if (sdest[mid] <= e) r0 = mid; else r1 = mid - 1;
+    }
+    const int64_t i = e - sdest[r0];
+    cx.pos[int64_t(b) * cx.max_ctx + e] = int32_t(i);
+    cx.row[int64_t(b) * cx.max_ctx + e] = int32_t(slo[r0] + i);
+  }
+}
+
 // Each wave selects the k best of up to 64 * TW_PER_LANE inputs.
 // Filter first: the k-th smallest of the 64 lane minima bounds the k-th
 // smallest key from above (those k lane minima are k distinct keys), so
@@ -101,7 +157,7 @@ template <bool FROM_SCORES, bool FINAL, int TW_PER_LANE, int W>
 __global__ __launch_bounds__(64 * W) void topk_wave_kernel(const float* __restrict__ scores,
                                                            const uint64_t* __restrict__ keys_in, int64_t n, int k,
                                                            uint64_t* __restrict__ keys_out, int32_t* __restrict__ ids,
-                                                           float* __restrict__ vals) {
+                                                           float* __restrict__ vals, CtxOut cx) {
   constexpr int TW_PER_WAVE = 64 * TW_PER_LANE;
   extern __shared__ uint64_t surv_lds[];   // [W][tw_slots(k, TW_PER_LANE)]
   const int slots = tw_slots(k, TW_PER_LANE);
@@ -172,6 +228,10 @@ __global__ __launch_bounds__(64 * W) void topk_wave_kernel(const float* __restri
         keys_out[(int64_t(b) * gridDim.x + blockIdx.x) * k + lane] = acc;
       }
     }
+    if constexpr (FINAL) {
+      __shared__ int64_t sdest[64], slo[64];
+      if (cx.chunk_off) context_index_wave(acc, lane, k, b, cx, sdest, slo);
+    }
   }
 }
 
@@ -202,9 +262,42 @@ extern "C" size_t msa_topk_workspace(int B, int64_t n_docs, int k) {
   return 2 * msa::align_up(size_t(B) * size_t(mx) * sizeof(uint64_t), 256);
 }
 
+namespace msa {
+static int topk_run(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
+                    size_t ws_bytes, void* stream, const CtxOut& cx);
+}
+
 extern "C" int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
                         size_t ws_bytes, void* stream) {
+  return msa::topk_run(doc_score, B, n_docs, k, ids, vals, ws, ws_bytes, stream,
+                       msa::CtxOut{nullptr, 0, 0, nullptr, nullptr, nullptr});
+}
+
+extern "C" int msa_topk_context_index(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids,
+                                      float* vals, const int64_t* chunk_off, int max_doc_chunks, int64_t n_chunks,
+                                      int max_ctx, int32_t* ctx_row, int32_t* ctx_pos, int32_t* ctx_len, void* ws,
+                                      size_t ws_bytes, void* stream) {
   using namespace msa;
+  MSA_REQUIRE(chunk_off && ctx_row && ctx_pos && ctx_len, MSA_ERR_INVALID_ARG,
+              "msa_topk_context_index: NULL pointer");
+  MSA_REQUIRE(n_chunks >= 1 && max_doc_chunks >= 1, MSA_ERR_INVALID_ARG, "msa_topk_context_index: non-positive size");
+  MSA_REQUIRE(n_chunks <= INT32_MAX, MSA_ERR_UNSUPPORTED, "msa_topk_context_index: n_chunks must be below 2^31");
+  MSA_REQUIRE(int64_t(max_ctx) >= int64_t(k) * max_doc_chunks, MSA_ERR_INVALID_ARG,
+              "msa_topk_context_index: max_ctx < k * max_doc_chunks");
+  if (k > 64) {   // the slice passes: the selection, then the index on its own
+    const int rc = topk_run(doc_score, B, n_docs, k, ids, vals, ws, ws_bytes, stream,
+                            CtxOut{nullptr, 0, 0, nullptr, nullptr, nullptr});
+    if (rc != MSA_OK) return rc;
+    return msa_context_index(ids, B, k, chunk_off, n_docs, max_doc_chunks, n_chunks, max_ctx, ctx_row, ctx_pos,
+                             ctx_len, stream);
+  }
+  return topk_run(doc_score, B, n_docs, k, ids, vals, ws, ws_bytes, stream,
+                  CtxOut{chunk_off, n_docs, max_ctx, ctx_row, ctx_pos, ctx_len});
+}
+
+namespace msa {
+static int topk_run(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
+                    size_t ws_bytes, void* stream, const CtxOut& cx) {
   MSA_REQUIRE(doc_score && ids && vals, MSA_ERR_INVALID_ARG, "msa_topk: NULL pointer");
   MSA_REQUIRE(B >= 1 && n_docs >= 1, MSA_ERR_INVALID_ARG, "msa_topk: non-positive size");
   MSA_REQUIRE(k >= 1 && k <= n_docs, MSA_ERR_INVALID_ARG, "msa_topk: k must be in [1, n_docs]");
@@ -232,7 +325,8 @@ extern "C" int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, in
 #define TW_LAUNCH(FS, FIN, PL, W)                                                                                   \
   MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_wave_kernel<FS, FIN, PL, W>),               \
                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));                         \
-  hipLaunchKernelGGL((topk_wave_kernel<FS, FIN, PL, W>), grid, block, lds, s, doc_score, kin, n, k, kout, ids, vals)
+  hipLaunchKernelGGL((topk_wave_kernel<FS, FIN, PL, W>), grid, block, lds, s, doc_score, kin, n, k, kout, ids, vals, \
+                     last ? cx : CtxOut{nullptr, 0, 0, nullptr, nullptr, nullptr})
       if (first && last && wide) {
         TW_LAUNCH(true, true, TW_PL_WIDE, TW_WAVES_WIDE);
       } else if (first && last) {
@@ -272,6 +366,8 @@ extern "C" int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, in
   }
   return MSA_OK;
 }
+
+}  // namespace msa
 
 namespace msa {
 

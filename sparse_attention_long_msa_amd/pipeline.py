@@ -87,6 +87,17 @@ class LayerRunner:
         B.msa_topk(self.doc_score, self.k, ids=self.ids, vals=self.vals, ws=self.tk_ws, stream=stream)
         return self.ids, self.vals
 
+    def select_assemble(self, chunk_off, k_bar, v_bar, stream=None):
+        """select() then assemble(); on the HBM (indexed) path one fused call."""
+        if not self.indexed:
+            self.select(stream)
+            self.assemble(chunk_off, k_bar, v_bar, stream)
+            return
+        B.msa_topk_context_index(self.doc_score, self.k, chunk_off, k_bar.shape[0], self.max_doc_chunks, self.max_ctx,
+                                 ids=self.ids, vals=self.vals, ctx_row=self.ctx_row, ctx_pos=self.ctx_pos,
+                                 ctx_len=self.ctx_len, ws=self.tk_ws, stream=stream)
+        self._store = (k_bar, v_bar)
+
     def assemble(self, chunk_off, k_bar, v_bar, stream=None):
         if self.indexed:
             B.msa_context_index(self.ids, chunk_off, k_bar.shape[0], self.max_doc_chunks, self.max_ctx,
@@ -125,11 +136,13 @@ class LayerRunner:
             if r == 0 and route_events is not None:
                 route_events[1].record(stream)
             B.msa_exclude_docs(self.doc_score, self.ids_rounds[:r], stream)
-            B.msa_topk(self.doc_score, self.k, ids=self.ids_rounds[r], vals=self.vals, ws=self.tk_ws, stream=stream)
             if r == 0:
-                B.msa_context_index(self.ids_rounds[0], chunk_off, k_bar.shape[0], self.max_doc_chunks, self.max_ctx,
-                                    ctx_row=self.ctx_row, ctx_pos=self.ctx_pos, ctx_len=self._lens[0], stream=stream)
+                B.msa_topk_context_index(self.doc_score, self.k, chunk_off, k_bar.shape[0], self.max_doc_chunks,
+                                         self.max_ctx, ids=self.ids_rounds[0], vals=self.vals, ctx_row=self.ctx_row,
+                                         ctx_pos=self.ctx_pos, ctx_len=self._lens[0], ws=self.tk_ws, stream=stream)
             else:
+                B.msa_topk(self.doc_score, self.k, ids=self.ids_rounds[r], vals=self.vals, ws=self.tk_ws,
+                           stream=stream)
                 B.msa_context_append(self.ids_rounds[r], chunk_off, k_bar.shape[0], self.max_doc_chunks, self.ctx_row,
                                      self.ctx_pos, self._lens[(r - 1) % 2], self._lens[r % 2], stream=stream)
         self.ctx_len = self._lens[(R - 1) % 2]

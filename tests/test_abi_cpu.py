@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.msa_abi_version() == 7
+    assert M.msa_abi_version() == 8
     assert M.lib.msa_status_string(0).decode() == "ok"
     assert "workspace" in M.lib.msa_status_string(3).decode()
 

@@ -181,6 +181,39 @@ def test_gather(bf16, mode):
         np.testing.assert_array_equal(cp[b, :n].cpu().numpy(), rp)
 
 
+@pytest.mark.parametrize("B,D,k,n_excl", [(1, 195312, 16, 0), (32, 10518, 16, 0), (2, 300, 64, 0), (3, 2000, 16, 1990),
+                                          (2, 20000, 40, 0), (2, 5000, 100, 0)])
+def test_topk_context_index_matches_the_two_calls(B, D, k, n_excl):
+    """msa_topk_context_index writes exactly what msa_topk and then
+    msa_context_index write: the final selection pass of the 4- and 16-wave
+    kinds, after a reducing pass, with excluded documents (trailing ids -1),
+    and the k > 64 fallback."""
+    r = np.random.default_rng(D + k)
+    lens = r.integers(1, 700, D)
+    lens[r.integers(0, D, D // 20)] = 0                       # empty documents
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    s = np.round(r.normal(size=(B, D)), 3).astype(np.float32)  # exact ties
+    s[:, np.flatnonzero(lens == 0)] = -np.inf
+    if n_excl:
+        s[:, r.choice(D, n_excl, replace=False)] = np.nan      # fewer than k documents left
+    mdc = int(np.diff(chunk_off).max())
+    max_ctx = k * mdc
+    sd = torch.from_numpy(s).to(dev())
+    ids, vals = M.msa_topk(sd, k)
+    row, pos, ln = M.msa_context_index(ids, co_d, n_chunks, mdc, max_ctx)
+    fill = torch.full((B, max_ctx), -7, dtype=torch.int32, device=dev())
+    row2, pos2 = fill.clone(), fill.clone()
+    row[:], pos[:] = -7, -7                                   # entries past ctx_len stay untouched in both
+    M.msa_context_index(ids, co_d, n_chunks, mdc, max_ctx, ctx_row=row, ctx_pos=pos, ctx_len=ln)
+    ids2, vals2, row2, pos2, ln2 = M.msa_topk_context_index(sd, k, co_d, n_chunks, mdc, max_ctx, ctx_row=row2,
+                                                            ctx_pos=pos2)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(vals.view(torch.int32), vals2.view(torch.int32))
+    assert torch.equal(ln, ln2) and torch.equal(row, row2) and torch.equal(pos, pos2)
+    if n_excl:
+        assert (ids2[:, D - n_excl:] == -1).all()
+
+
 @pytest.mark.parametrize("B,k", [(3, 5), (1, 50), (4, 1)])
 def test_context_index(B, k):
     lens = ragged_lengths(7, 50, 0, 500, n_empty=3)
