@@ -124,6 +124,25 @@ def test_route_score_document_table_paths():
         print(f"route_score table paths layout={layout}: normwise err {err:.3g}")
 
 
+@pytest.mark.parametrize("bf16,layout", [(True, 1), (False, 0)])
+def test_route_score_single_chunk_is_the_cosine(bf16, layout):
+    """A memory of one document of one chunk and a one-token query: the score
+    is the head mean of the per-head cosines (the textbook cosine when the
+    heads agree)."""
+    H, d = 8, 128
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(np.array([40]), 64)
+    assert n_chunks == 1
+    dt = "bf16" if bf16 else "f32"
+    store = O.round_to_store(O.l2_normalize(gen(51, 0, synth.T_KR, (1, H, d), bf16).astype(np.float64)), dt)
+    q = gen(52, 0, synth.T_QR, (1, 1, H, d), bf16)
+    st = tile_np(store) if layout == 1 else store
+    got = host(M.msa_route_score(to_dev(q, bf16), to_dev(st, bf16), cd, 1, layout=layout))
+    qd = q.astype(np.float64)[0, 0]
+    want = np.mean([qd[h] @ store[0, h].astype(np.float64) / np.linalg.norm(qd[h]) for h in range(H)])
+    assert got.shape == (1, 1)
+    assert abs(got[0, 0] - want) <= RTOL_SCORE[dt] * max(abs(want), 1e-3)
+
+
 def test_route_score_rescale_invariance():
     """Cosine is invariant to a positive rescale of the routing query."""
     H, d = 8, 128
@@ -141,7 +160,9 @@ def test_route_score_rescale_invariance():
                                    (3, 4096, 1), (1, 4097, 32), (1, 9000, 9000 // 40),
                                    # the 16-wave final pass at its capacity (k = 64: the largest LDS),
                                    # one past it, a second reducing pass, a reducing pass into it
-                                   (2, 16384, 64), (1, 16385, 64), (2, 1_000_000, 64), (1, 300_000, 48)])
+                                   (2, 16384, 64), (1, 16385, 64), (2, 1_000_000, 64), (1, 300_000, 48),
+                                   # degenerate: every document selected; a single document
+                                   (2, 64, 64), (3, 1, 1), (1, 256, 256)])
 def test_topk_exact(B, D, k):
     r = np.random.default_rng(B * 7 + D)
     s = np.round(r.normal(size=(B, D)), 3).astype(np.float32)       # many exact ties
