@@ -4,10 +4,12 @@
 //  chunk-mean pooled; Inference Pipeline: Global Memory Encoding caches the
 //  pooled K, V and K_r.  Paper note 核心方法 > 架构: chunk-wise mean pool.)
 //
-// One workgroup per pooled chunk.  The chunk's token rows are contiguous
-// (H*d elements each), so threads stream them with 16-byte loads; row
-// groups of the workgroup take interleaved tokens and are combined in a
-// fixed order, so the result is deterministic.
+// A chunk's token rows are contiguous (H*d elements each) and are streamed
+// with 16-byte loads.  The common shapes (a row of whole waves of 16-byte
+// vectors, e.g. H = 8, d = 128) take pool_wave_kernel: one wave per chunk,
+// 16 chunks per workgroup.  Other shapes take pool_kernel: one workgroup
+// per chunk, whose row groups take interleaved tokens and are combined in a
+// fixed order.  Both are deterministic.
 #include <algorithm>
 
 #include "common.h"
@@ -101,6 +103,145 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
   }
 }
 
+// Wave-per-chunk pooling, for token rows whose 16-byte vectors fill whole
+// waves (H*d*bytes/16 a multiple of 64) and heads that span a power-of-two
+// number of lanes.  A workgroup of four waves pools 16 consecutive chunks:
+// in the tiled layout those form one 16-chunk group, so each output line is
+// written by a single workgroup (on a single XCD), and the padding chunks of
+// the last group are written as zeros here.  A wave takes CPW chunks at a
+// time and streams their token rows together, so the loads of all CPW chunks
+// are in flight at once; a chunk's rows are summed in token order.  A head's
+// squared norm is reduced over the lanes that hold it, and every lane writes
+// its 16-byte piece with one store.
+constexpr int kPoolWaveThreads = 256;
+
+// With chunk == 1 the chunk CSR equals the token CSR, so chunk c is token c
+// and the kernel (ONE) reads no index.
+template <int DT, int NP, int CPW, bool ONE>
+__global__ __launch_bounds__(kPoolWaveThreads) void pool_wave_kernel(
+    const typename Elem<DT>::T* __restrict__ x, const int64_t* __restrict__ tok_off,
+    const int64_t* __restrict__ chunk_off, const int32_t* __restrict__ chunk_doc, int64_t n_chunks,
+    int64_t n_tok, int H, int d, int chunk, int normalize, int tiled, typename Elem<DT>::T* __restrict__ out) {
+  using T = typename Elem<DT>::T;
+  constexpr int VE = 16 / Elem<DT>::bytes;  // elements per 16-byte vector
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int E = H * d;
+  const int lph = d / VE;                   // lanes per head
+  // tiled output: the group's 16 rows are staged in LDS (row stride padded
+  // so that the column-wise reads below spread over all banks) and then
+  // written out as one contiguous block in the tiled order
+  extern __shared__ __align__(16) unsigned char stage[];
+  const int row_b = E * Elem<DT>::bytes + 128 / VE;
+  const int64_t n_out = tiled ? (n_chunks + 15) / 16 * 16 : n_chunks;
+  const int64_t n_groups = (n_out + 15) / 16;
+  for (int64_t g = blockIdx.x; g < n_groups; g += gridDim.x) {
+    for (int s0 = 0; s0 < 4; s0 += CPW) {
+      int64_t c[CPW], t0[CPW];
+      int cnt[CPW];
+      int max_cnt = 0;
+#pragma unroll
+      for (int s = 0; s < CPW; ++s) {
+        c[s] = g * 16 + wave * 4 + s0 + s;
+        t0[s] = 0;
+        cnt[s] = 0;
+        if (ONE) {
+          t0[s] = c[s];
+          cnt[s] = c[s] < n_chunks ? 1 : 0;
+        } else if (c[s] < n_chunks) {
+          const int32_t doc = chunk_doc[c[s]];
+          t0[s] = tok_off[doc] + (c[s] - chunk_off[doc]) * chunk;
+          const int64_t t1 = min(t0[s] + chunk, tok_off[doc + 1]);
+          cnt[s] = int(t1 - t0[s]);
+        }
+        max_cnt = max(max_cnt, cnt[s]);
+      }
+      float acc[CPW][NP * VE];
+#pragma unroll
+      for (int s = 0; s < CPW; ++s)
+#pragma unroll
+        for (int k = 0; k < NP * VE; ++k) acc[s][k] = 0.f;
+      for (int i = 0; i < max_cnt; ++i) {
+        uint4 w[CPW][NP];
+#pragma unroll
+        for (int s = 0; s < CPW; ++s) {
+          // a chunk with fewer rows re-reads its last one (added with weight 0)
+          int64_t t = t0[s] + min(i, max(cnt[s], 1) - 1);
+          t = min(max(t, int64_t(0)), n_tok - 1);
+#pragma unroll
+          for (int p = 0; p < NP; ++p) w[s][p] = load_global(x + t * E + int64_t(lane + 64 * p) * VE);
+        }
+#pragma unroll
+        for (int s = 0; s < CPW; ++s) {
+          if (i >= cnt[s]) continue;
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            const uint32_t ww[4] = {w[s][p].x, w[s][p].y, w[s][p].z, w[s][p].w};
+            if constexpr (DT == MSA_BF16) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                acc[s][p * VE + 2 * e] += __uint_as_float(ww[e] << 16);
+                acc[s][p * VE + 2 * e + 1] += __uint_as_float(ww[e] & 0xFFFF0000u);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[s][p * VE + e] += __uint_as_float(ww[e]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < CPW; ++s) {
+        if (c[s] >= n_out) continue;
+        const float inv_cnt = cnt[s] > 0 ? 1.f / float(cnt[s]) : 0.f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          float r[VE];
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) {
+            r[e] = acc[s][p * VE + e] * inv_cnt;
+            ss += r[e] * r[e];
+          }
+          if (normalize) {
+            for (int m = 1; m < lph; m <<= 1) ss += __shfl_xor(ss, m);
+            const float inv = 1.f / fmaxf(sqrtf(ss), 1e-8f);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) r[e] *= inv;
+          }
+          const int e0 = (lane + 64 * p) * VE;
+          uint4 v;
+          if constexpr (DT == MSA_BF16) {
+            v.x = uint32_t(f32_to_bf16(r[0])) | (uint32_t(f32_to_bf16(r[1])) << 16);
+            v.y = uint32_t(f32_to_bf16(r[2])) | (uint32_t(f32_to_bf16(r[3])) << 16);
+            v.z = uint32_t(f32_to_bf16(r[4])) | (uint32_t(f32_to_bf16(r[5])) << 16);
+            v.w = uint32_t(f32_to_bf16(r[6])) | (uint32_t(f32_to_bf16(r[7])) << 16);
+          } else {
+            v = make_uint4(__float_as_uint(r[0]), __float_as_uint(r[1]), __float_as_uint(r[2]),
+                           __float_as_uint(r[3]));
+          }
+          if (tiled)
+            *reinterpret_cast<uint4*>(stage + (wave * 4 + s0 + s) * row_b + e0 * Elem<DT>::bytes) = v;
+          else
+            *reinterpret_cast<uint4*>(out + c[s] * E + e0) = v;
+        }
+      }
+    }
+    if (tiled) {
+      __syncthreads();
+      T* gout = out + g * 16 * int64_t(E);
+      for (int u = threadIdx.x; u < 16 * E / VE; u += kPoolWaveThreads) {
+        // 16-byte unit u of the group block: head h, then e/32, (e%32)/8,
+        // chunk within the group, e%8
+        const int o = u * VE, h = o / (16 * d), rem = o - h * 16 * d;
+        const int c16 = (rem & 127) >> 3, e = (rem >> 9) * 32 + ((rem >> 7) & 3) * 8 + (rem & 7);
+        *reinterpret_cast<uint4*>(gout + o) =
+            *reinterpret_cast<const uint4*>(stage + c16 * row_b + (h * d + e) * Elem<DT>::bytes);
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // MSA_LAYOUT_ROWS -> MSA_LAYOUT_TILED; one thread per 8 consecutive elements
 // of one (chunk, head); chunks past n_chunks in the last group are zeroed.
 template <typename T>
@@ -164,13 +305,61 @@ extern "C" int msa_pool_encode(int dtype, const void* x, const int64_t* tok_off,
   MSA_REQUIRE(d % 2 == 0, MSA_ERR_INVALID_ARG, "msa_pool_encode: d must be even");
   MSA_REQUIRE(out_layout == MSA_LAYOUT_ROWS || (out_layout == MSA_LAYOUT_TILED && d % 32 == 0), MSA_ERR_INVALID_ARG,
               "msa_pool_encode: bad out_layout (tiled needs d % 32 == 0)");
+  MSA_REQUIRE(chunk != 1 || n_chunks == n_tok, MSA_ERR_INVALID_ARG,
+              "msa_pool_encode: with chunk == 1 every token is a chunk (n_chunks must equal n_tok)");
   const int E = H * d;
   const int VE = 16 / dtype_bytes(dtype);
   MSA_REQUIRE(E <= 4096 && E % 8 == 0, MSA_ERR_UNSUPPORTED, "msa_pool_encode: H*d must be <= 4096 and a multiple of 8");
   const int V = E / VE;
-  MSA_REQUIRE(V >= kPoolThreads || kPoolThreads % V == 0, MSA_ERR_UNSUPPORTED,
-              "msa_pool_encode: H*d*elem_bytes/16 must divide 256 or be a multiple of it");
   MSA_REQUIRE(uintptr_t(x) % 16 == 0, MSA_ERR_INVALID_ARG, "msa_pool_encode: x not 16-byte aligned");
+  const int lph = d / VE;
+  if (V % 64 == 0 && V / 64 <= 8 && d % VE == 0 && lph <= 64 && (lph & (lph - 1)) == 0 &&
+      uintptr_t(out) % 16 == 0) {
+    const int64_t n_groups = (n_chunks + 15) / 16;
+    const dim3 grid(unsigned(std::min<int64_t>(n_groups, int64_t(1) << 20)));
+    const int tiled = out_layout == MSA_LAYOUT_TILED;
+    const size_t lds = tiled ? 16 * size_t(E * dtype_bytes(dtype) + 128 / VE) : 0;
+#define MSA_POOL_WAVE_1(NP, CPW, ONE)                                                                         \
+  do {                                                                                                        \
+    if (lds > 65536) {                                                                                        \
+      MSA_HIP_CHECK(hipFuncSetAttribute(                                                                      \
+          dtype == MSA_BF16 ? reinterpret_cast<const void*>(&pool_wave_kernel<MSA_BF16, NP, CPW, ONE>)        \
+                            : reinterpret_cast<const void*>(&pool_wave_kernel<MSA_F32, NP, CPW, ONE>),        \
+          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));                                             \
+    }                                                                                                         \
+    if (dtype == MSA_BF16)                                                                                    \
+      hipLaunchKernelGGL((pool_wave_kernel<MSA_BF16, NP, CPW, ONE>), grid, dim3(kPoolWaveThreads), lds,       \
+                         as_stream(stream), static_cast<const uint16_t*>(x), tok_off, chunk_off, chunk_doc,   \
+                         n_chunks, n_tok, H, d, chunk, l2_normalize, tiled, static_cast<uint16_t*>(out));     \
+    else                                                                                                      \
+      hipLaunchKernelGGL((pool_wave_kernel<MSA_F32, NP, CPW, ONE>), grid, dim3(kPoolWaveThreads), lds,        \
+                         as_stream(stream), static_cast<const float*>(x), tok_off, chunk_off, chunk_doc,      \
+                         n_chunks, n_tok, H, d, chunk, l2_normalize, tiled, static_cast<float*>(out));        \
+  } while (0)
+#define MSA_POOL_WAVE(NP, CPW)              \
+  do {                                      \
+    if (chunk == 1)                         \
+      MSA_POOL_WAVE_1(NP, CPW, true);       \
+    else                                    \
+      MSA_POOL_WAVE_1(NP, CPW, false);      \
+  } while (0)
+    switch (V / 64) {
+      case 1: MSA_POOL_WAVE(1, 4); break;
+      case 2: MSA_POOL_WAVE(2, 4); break;
+      case 3: MSA_POOL_WAVE(3, 2); break;
+      case 4: MSA_POOL_WAVE(4, 2); break;
+      case 5: MSA_POOL_WAVE(5, 1); break;
+      case 6: MSA_POOL_WAVE(6, 1); break;
+      case 7: MSA_POOL_WAVE(7, 1); break;
+      default: MSA_POOL_WAVE(8, 1); break;
+    }
+#undef MSA_POOL_WAVE
+#undef MSA_POOL_WAVE_1
+    MSA_LAUNCH_CHECK();
+    return MSA_OK;
+  }
+  MSA_REQUIRE(V >= kPoolThreads || kPoolThreads % V == 0, MSA_ERR_UNSUPPORTED,
+              "msa_pool_encode: unsupported H*d (16-byte vectors per token row)");
   const int R = V < kPoolThreads ? kPoolThreads / V : 1;
   const size_t smem = (size_t(R) * E + E + H) * sizeof(float);
   MSA_REQUIRE(smem <= 160 * 1024, MSA_ERR_UNSUPPORTED, "msa_pool_encode: LDS budget exceeded");

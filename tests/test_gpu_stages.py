@@ -77,6 +77,29 @@ def test_pool_encode(bf16, normalize, chunk, layout):
         np.testing.assert_allclose(got, ref, rtol=2e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("H,d", [(2, 32), (4, 64), (12, 128), (8, 256), (1, 512)])
+def test_pool_encode_head_shapes(bf16, layout, H, d):
+    # rows of 1/2 to 8 waves of 16-byte vectors, heads of 4 to 128 vectors:
+    # both the wave-per-chunk kernel and the workgroup-per-chunk one
+    lens = ragged_lengths(3, 41, 0, 90, n_empty=2)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 5)
+    x = gen(12, 0, synth.T_KR, (int(lens.sum()), H, d), bf16)
+    out = M.msa_pool_encode(to_dev(x, bf16), to_dev_i64(tok_off), co_d, cd, 5, True, layout=layout)
+    ref = O.pool_encode(x, tok_off, 5, True, "bf16" if bf16 else "f32")
+    got = host(out)
+    if layout == 1:
+        assert np.all(untile_np(got, got.shape[0])[n_chunks:] == 0)
+        got = untile_np(got, n_chunks)
+    if bf16:
+        ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+        assert np.all(np.abs(got - ref) <= ulp + 1e-30)
+        assert np.mean(got == ref) > 0.99
+    else:
+        np.testing.assert_allclose(got, ref, rtol=2e-6, atol=1e-7)
+
+
 @pytest.mark.parametrize("bf16,layout", [(True, 1), (True, 0), (False, 0)])
 @pytest.mark.parametrize("B,T", [(1, 64), (1, 16), (1, 1), (2, 32), (32, 1), (1, 128), (3, 7), (1, 80)])
 def test_route_score(bf16, layout, B, T):
