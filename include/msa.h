@@ -130,9 +130,11 @@ int msa_tile_routing_keys(int dtype, const void* src, int64_t n_chunks, int H, i
  *   tok_off   [n_docs + 1] int64, chunk_off [n_docs + 1] int64 (chunk CSR of
  *             tok_off for this chunk size), chunk_doc [n_chunks] int32
  *   out       [n_chunks, H, d] dtype in out_layout (msa_layout; MSA_LAYOUT_TILED
- *             needs d % 32 == 0 and room for ceil(n_chunks/16)*16 chunks)
+ *             needs d % 32 == 0 and room for ceil(n_chunks/16)*16 chunks);
+ *             must not overlap x (workgroups write their chunks while others
+ *             still read tokens)
  * Errors: INVALID_ARG (NULL, non-positive sizes, d odd, bad layout, x not
- * 16-byte aligned), UNSUPPORTED (H*d > 4096 or H*d not a multiple of 8, or
+ * 16-byte aligned, out == x), UNSUPPORTED (H*d > 4096 or H*d not a multiple of 8, or
  * a token row of n = H*d*bytes/16 16-byte vectors where n neither divides
  * 256 nor is a multiple of 256 and is not covered by the wave-per-chunk
  * kernel: n a multiple of 64 with each head d*bytes/16 vectors, a power of

@@ -300,6 +300,7 @@ extern "C" int msa_pool_encode(int dtype, const void* x, const int64_t* tok_off,
   MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, "msa_pool_encode: bad dtype");
   MSA_REQUIRE(x && tok_off && chunk_off && chunk_doc && out, MSA_ERR_INVALID_ARG,
               "msa_pool_encode: NULL pointer");
+  MSA_REQUIRE(out != x, MSA_ERR_INVALID_ARG, "msa_pool_encode: out must not alias x");
   MSA_REQUIRE(n_docs >= 1 && n_tok >= 1 && n_chunks >= 1 && H >= 1 && d >= 2 && chunk >= 1,
               MSA_ERR_INVALID_ARG, "msa_pool_encode: non-positive size");
   MSA_REQUIRE(d % 2 == 0, MSA_ERR_INVALID_ARG, "msa_pool_encode: d must be even");

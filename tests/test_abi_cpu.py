@@ -52,6 +52,7 @@ def test_chunk_offsets_rejects_bad_offsets(bad):
 
 
 P = ctypes.c_void_p(16)   # a non-null dummy; validation fails before any dereference
+Q = ctypes.c_void_p(48)   # a second one, for outputs that must not alias an input
 
 
 def test_route_score_validation():
@@ -189,14 +190,15 @@ def test_sparse_attn_validation():
 
 def test_pool_and_docmap_validation():
     L = M.lib
-    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 128, 0, 1, 0, P, None) == 1     # chunk 0
-    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 127, 64, 1, 0, P, None) == 1    # odd d
-    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 64, 128, 64, 1, 0, P, None) == 2   # H*d > 4096
-    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 48, 64, 1, 1, P, None) == 1     # tiled needs d % 32
-    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 128, 1, 1, 0, P, None) == 1     # chunk 1: a chunk per token
-    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 3, 64, 64, 1, 0, P, None) == 2     # 24 vectors per row
-    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 16, 96, 64, 1, 0, P, None) == 2    # 12 vectors per head
-    assert L.msa_pool_encode(1, ctypes.c_void_p(8), P, P, P, 4, 100, 8, 8, 128, 64, 1, 0, P, None) == 1  # x align
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 128, 0, 1, 0, Q, None) == 1     # chunk 0
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 127, 64, 1, 0, Q, None) == 1    # odd d
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 64, 128, 64, 1, 0, Q, None) == 2   # H*d > 4096
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 48, 64, 1, 1, Q, None) == 1     # tiled needs d % 32
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 8, 128, 1, 1, 0, Q, None) == 1     # chunk 1: a chunk per token
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 100, 8, 128, 1, 1, 0, P, None) == 1   # out aliases x
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 3, 64, 64, 1, 0, Q, None) == 2     # 24 vectors per row
+    assert L.msa_pool_encode(1, P, P, P, P, 4, 100, 8, 16, 96, 64, 1, 0, Q, None) == 2    # 12 vectors per head
+    assert L.msa_pool_encode(1, ctypes.c_void_p(8), P, P, P, 4, 100, 8, 8, 128, 64, 1, 0, Q, None) == 1  # x align
     assert L.msa_tile_routing_keys(1, P, 10, 8, 48, ctypes.c_void_p(32), None) == 1
     assert L.msa_tile_routing_keys(1, P, 10, 8, 128, P, None) == 1                     # aliased
     assert L.msa_chunk_doc_map(None, 4, 8, P, None) == 1
