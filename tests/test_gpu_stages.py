@@ -79,10 +79,11 @@ def test_pool_encode(bf16, normalize, chunk, layout):
 
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("layout", [0, 1])
-@pytest.mark.parametrize("H,d", [(2, 32), (4, 64), (12, 128), (8, 256), (1, 512)])
+@pytest.mark.parametrize("H,d", [(2, 32), (4, 64), (12, 128), (8, 256), (1, 512), (20, 128), (28, 128)])
 def test_pool_encode_head_shapes(bf16, layout, H, d):
-    # rows of 1/2 to 8 waves of 16-byte vectors, heads of 4 to 128 vectors:
-    # both the wave-per-chunk kernel and the workgroup-per-chunk one
+    # rows of 1/8 to 14 waves of 16-byte vectors, heads of 4 to 128 vectors:
+    # every instantiation of the wave-per-chunk kernel (1 to 8 vectors per
+    # lane) and the workgroup-per-chunk kernel
     lens = ragged_lengths(3, 41, 0, 90, n_empty=2)
     tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 5)
     x = gen(12, 0, synth.T_KR, (int(lens.sum()), H, d), bf16)
