@@ -11,7 +11,7 @@ from tests.helpers import gen, host, ragged_lengths, to_dev, to_dev_i64, untile_
 
 pytestmark = pytest.mark.gpu
 
-M = pytest.importorskip("sparse_attention_long_msa_amd")
+import sparse_attention_long_msa_amd as M  # noqa: E402  (a missing library fails loudly)
 
 
 def _case(seed, n_docs, hidden, H, d, chunk, bf16):

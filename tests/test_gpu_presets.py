@@ -15,7 +15,7 @@ from tests.helpers import ATOL_ATTN, BAND, RTOL_SCORE, check_ids, check_scores
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-M = pytest.importorskip("sparse_attention_long_msa_amd")
+import sparse_attention_long_msa_amd as M  # noqa: E402  (a missing library fails loudly)
 from tests.preset_run import GpuLayer, HostLayer  # noqa: E402
 
 
