@@ -111,8 +111,9 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
 // the last group are written as zeros here.  A wave takes CPW chunks at a
 // time and streams their token rows together, so the loads of all CPW chunks
 // are in flight at once; a chunk's rows are summed in token order.  A head's
-// squared norm is reduced over the lanes that hold it, and every lane writes
-// its 16-byte piece with one store.
+// squared norm is reduced over the lanes that hold it.  In the row layout
+// every lane writes its 16-byte piece with one store; in the tiled layout the
+// 16 results go through LDS first (below).
 constexpr int kPoolWaveThreads = 256;
 
 // With chunk == 1 the chunk CSR equals the token CSR, so chunk c is token c
