@@ -156,6 +156,5 @@ class LayerRunner:
 
     def run(self, q_r, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc, stream=None):
         self.route(q_r, kr_hat, chunk_doc, stream)
-        self.select(stream)
-        self.assemble(chunk_off, k_bar, v_bar, stream)
+        self.select_assemble(chunk_off, k_bar, v_bar, stream)
         return self.attend(q, k_loc, v_loc, stream)

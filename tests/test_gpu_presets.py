@@ -92,15 +92,16 @@ def test_preset_1m_full_ranking():
     assert e <= ATOL_ATTN["bf16"]
 
 
-@pytest.mark.parametrize("name", ["cfg3", "cfg4", "cfg5"])
-def test_preset_full_size_sampled(name):
+@pytest.mark.parametrize("name,tier", [("cfg3", "hbm"), ("cfg4", "hbm"), ("cfg4", "host"), ("cfg5", "hbm")])
+def test_preset_full_size_sampled(name, tier):
     p = configs.PRESETS[name]()
     layer = 17 if name == "cfg4" else 5
     host = HostLayer(p, layer)
-    # the 100M preset reads K/V over the host link; the HBM-resident presets
-    # read the selected rows in place (the batched-decode bench path)
-    mode = M.MSA_SRC_HOST_MAPPED if name == "cfg4" else M.MSA_SRC_DEVICE
-    g = GpuLayer(p, layer, host, src_mode=mode, indexed=name != "cfg4").run()
+    # HBM tier: the selected rows are read in place, with top-k and the
+    # context index in one call (the path bench.py times); host tier: the
+    # selected rows are gathered over the host link
+    mode = M.MSA_SRC_HOST_MAPPED if tier == "host" else M.MSA_SRC_DEVICE
+    g = GpuLayer(p, layer, host, src_mode=mode, indexed=tier == "hbm").run()
     _log(f"{name}: GPU layer {layer} done (ctx_len {g['ctx_len'][:4].tolist()}...)")
     _check_sampled(p, host, g, n_random=120 if name == "cfg5" else 200)
     for b in ([0, 13, 31] if p.B > 1 else [0]):
