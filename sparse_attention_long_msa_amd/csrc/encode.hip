@@ -104,9 +104,10 @@ __device__ __forceinline__ int64_t store_index(int64_t c, int h, int e, int H, i
          e % 8;
 }
 
-// Workgroup = 128 pooled rows x one head (128 columns) of one of K, V, K_r;
-// wave w computes rows 32w..32w+31 (two 16-row tiles, so that each weight
-// fragment feeds two products).  A operand: the pooled rows' two bf16 parts
+// Workgroup = 256 pooled rows x one head (128 columns) of one of K, V, K_r;
+// wave w computes rows 64w..64w+63 (four 16-row tiles, so that each weight
+// fragment read from LDS feeds four products, and each staged slice serves
+// 256 rows).  A operand: the pooled rows' two bf16 parts
 // (hi + lo, written by the pooling kernel), read by each wave; B operand:
 // the 32-wide k-slice of the head's 128 weight rows (w_t [3*H*128, hidden],
 // one row per output feature) staged once per workgroup in LDS, the next
@@ -117,10 +118,12 @@ __device__ __forceinline__ int64_t store_index(int64_t c, int h, int e, int H, i
 // row tiles in order, so the workgroups sharing a row tile run together and
 // the tile is read once per XCD.
 constexpr int EN_D = 128;
-constexpr int EN_ROWS = 128;   // pooled rows per workgroup
+constexpr int EN_MW = 4;              // 16-row tiles per wave
+constexpr int EN_ROWS = 64 * EN_MW;   // pooled rows per workgroup (four waves)
 constexpr int EN_BS = 5;       // LDS stride of a weight row, in 16-byte pieces (4 + 1 pad)
 
-__global__ __launch_bounds__(EN_THREADS) void encode_gemm_kernel(
+// Two waves per SIMD: the 128 accumulators fit in 256 VGPRs without AGPRs.
+__global__ __launch_bounds__(EN_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void encode_gemm_kernel(
     const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl, int hidden, const uint16_t* __restrict__ w_t,
     int H, int64_t n_chunks, int kr_tiled, uint16_t* __restrict__ k_bar, uint16_t* __restrict__ v_bar,
     uint16_t* __restrict__ kr_hat) {
@@ -140,16 +143,16 @@ __global__ __launch_bounds__(EN_THREADS) void encode_gemm_kernel(
     cb = int(blockIdx.x / n_rt);
   }
   const int tensor = cb / H, h = cb % H;
-  int64_t arow[2];
+  int64_t arow[EN_MW];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)   // A-operand row of this lane
-    arow[m] = min(rt * EN_ROWS + 32 * wave + 16 * m + lc, n_chunks - 1) * hidden + 8 * g4;
+  for (int m = 0; m < EN_MW; ++m)   // A-operand row of this lane
+    arow[m] = min(rt * EN_ROWS + 16 * EN_MW * wave + 16 * m + lc, n_chunks - 1) * hidden + 8 * g4;
   // staging: thread tid copies pieces (row tid / 2, k-quarters 2 * (tid % 2) + {0, 1}) of the slice
   const int srow = tid / 2, sq = 2 * (tid % 2);
   const uint16_t* sp = w_t + (int64_t(cb) * EN_D + srow) * hidden + 8 * sq;
-  f32x4 acc[2][8];
+  f32x4 acc[EN_MW][8];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < EN_MW; ++m)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_k = hidden / 32;
@@ -162,9 +165,9 @@ __global__ __launch_bounds__(EN_THREADS) void encode_gemm_kernel(
     w0 = load_global(sp + kn);
     w1 = load_global(sp + kn + 8);
     const int k0 = ks * 32;
-    bf16x8 ahi[2], alo[2];
+    bf16x8 ahi[EN_MW], alo[EN_MW];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < EN_MW; ++m) {
       ahi[m] = __builtin_bit_cast(bf16x8, load_global(xh + arow[m] + k0));
       alo[m] = __builtin_bit_cast(bf16x8, load_global(xl + arow[m] + k0));
     }
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(EN_THREADS) void encode_gemm_kernel(
     for (int t = 0; t < 8; ++t) {
       const bf16x8 b = __builtin_bit_cast(bf16x8, bs[buf][(16 * t + lc) * EN_BS + g4]);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+      for (int m = 0; m < EN_MW; ++m) {
         acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[m], b, acc[m][t], 0, 0, 0);
         acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[m], b, acc[m][t], 0, 0, 0);
       }
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(EN_THREADS) void encode_gemm_kernel(
   uint16_t* out = tensor == 0 ? k_bar : (tensor == 1 ? v_bar : kr_hat);
   const bool tiled = tensor == 2 && kr_tiled;
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < EN_MW; ++m) {
     float scale[4] = {1.f, 1.f, 1.f, 1.f};
     if (tensor == 2) {   // routing key: L2-normalise each row of this head
 #pragma unroll
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(EN_THREADS) void encode_gemm_kernel(
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t c = rt * EN_ROWS + 32 * wave + 16 * m + 4 * g4 + i;
+      const int64_t c = rt * EN_ROWS + 16 * EN_MW * wave + 16 * m + 4 * g4 + i;
       if (c >= n_chunks) continue;
 #pragma unroll
       for (int t = 0; t < 8; ++t)
