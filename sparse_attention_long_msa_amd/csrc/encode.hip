@@ -26,7 +26,8 @@ namespace msa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int EN_THREADS = 256;
+constexpr int EN_GW = 8;                 // waves per GEMM workgroup
+constexpr int EN_THREADS = 64 * EN_GW;
 constexpr float EN_EPS = 1e-8f;
 
 // xbar[c, :] = mean of the hidden rows of chunk c (float32).  SPLIT (bf16
@@ -104,10 +105,10 @@ __device__ __forceinline__ int64_t store_index(int64_t c, int h, int e, int H, i
          e % 8;
 }
 
-// Workgroup = 256 pooled rows x one head (128 columns) of one of K, V, K_r;
-// wave w computes rows 64w..64w+63 (four 16-row tiles, so that each weight
-// fragment read from LDS feeds four products, and each staged slice serves
-// 256 rows).  A operand: the pooled rows' two bf16 parts
+// Workgroup = 512 pooled rows x one head (128 columns) of one of K, V, K_r,
+// in eight waves; wave w computes rows 64w..64w+63 (four 16-row tiles, so
+// that each weight fragment read from LDS feeds four products, and each
+// staged slice serves 512 rows).  A operand: the pooled rows' two bf16 parts
 // (hi + lo, written by the pooling kernel), read by each wave; B operand:
 // the 32-wide k-slice of the head's 128 weight rows (w_t [3*H*128, hidden],
 // one row per output feature) staged once per workgroup in LDS, the next
@@ -119,7 +120,7 @@ __device__ __forceinline__ int64_t store_index(int64_t c, int h, int e, int H, i
 // the tile is read once per XCD.
 constexpr int EN_D = 128;
 constexpr int EN_MW = 4;              // 16-row tiles per wave
-constexpr int EN_ROWS = 64 * EN_MW;   // pooled rows per workgroup (four waves)
+constexpr int EN_ROWS = 16 * EN_MW * EN_GW;   // pooled rows per workgroup
 constexpr int EN_BS = 5;       // LDS stride of a weight row, in 16-byte pieces (4 + 1 pad)
 
 // Two waves per SIMD: the 128 accumulators fit in 256 VGPRs without AGPRs.
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(EN_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
   for (int m = 0; m < EN_MW; ++m)   // A-operand row of this lane
     arow[m] = min(rt * EN_ROWS + 16 * EN_MW * wave + 16 * m + lc, n_chunks - 1) * hidden + 8 * g4;
   // staging: thread tid copies pieces (row tid / 2, k-quarters 2 * (tid % 2) + {0, 1}) of the slice
-  const int srow = tid / 2, sq = 2 * (tid % 2);
+  const int srow = tid / 4, sq = tid % 4;
   const uint16_t* sp = w_t + (int64_t(cb) * EN_D + srow) * hidden + 8 * sq;
   f32x4 acc[EN_MW][8];
 #pragma unroll
@@ -156,14 +157,12 @@ __global__ __launch_bounds__(EN_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_k = hidden / 32;
-  uint4 w0 = load_global(sp), w1 = load_global(sp + 8);
+  uint4 w0 = load_global(sp);
   for (int ks = 0; ks < n_k; ++ks) {
     const int buf = ks & 1;
     bs[buf][srow * EN_BS + sq] = w0;
-    bs[buf][srow * EN_BS + sq + 1] = w1;
     const int kn = min(ks + 1, n_k - 1) * 32;   // the next slice (the last one again at the end: never used)
     w0 = load_global(sp + kn);
-    w1 = load_global(sp + kn + 8);
     const int k0 = ks * 32;
     bf16x8 ahi[EN_MW], alo[EN_MW];
 #pragma unroll
