@@ -49,8 +49,9 @@ def _magnitudes(x, w, tok_off, chunk, H, d):
 
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("chunk", [64, 7])
-def test_encode_mfma(layout, chunk):
-    H, d, hidden = 2, 128, 320
+@pytest.mark.parametrize("hidden", [320, 288])   # whole 64-wide k-stages, and a trailing 32-wide one
+def test_encode_mfma(layout, chunk, hidden):
+    H, d = 2, 128
     tok_off, chunk_off, n_chunks, co_d, cd, x, w = _case(31, 40, hidden, H, d, chunk, True)
     kb, vb, kr = M.msa_encode(to_dev(x, True), to_dev(w, True), to_dev_i64(tok_off), co_d, cd, chunk, H, d,
                               kr_layout=layout)
