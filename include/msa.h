@@ -115,8 +115,8 @@ int msa_chunk_doc_map(const int64_t* chunk_off, int64_t n_docs, int64_t n_chunks
 int msa_tile_routing_keys(int dtype, const void* src, int64_t n_chunks, int H, int d, void* dst, void* stream);
 
 /*
- * msa_pool_encode - Stage 1 ("Global Memory Encoding", README Inference
- * Pipeline; "chunk-wise mean pool", paper note 核心方法 > 架构).
+ * msa_pool_encode - Stage 1 (global memory encoding, README Inference
+ * Pipeline; mean pooling per chunk, paper note 核心方法 > 架构).
  * For pooled chunk c = chunk j of document i and head h:
  *   out[c,h,:] = mean of x[t,h,:] over the tokens t of that chunk
  *                (tokens tok_off[i] + j*chunk ... min(+chunk, tok_off[i+1]) - 1;
@@ -145,7 +145,7 @@ int msa_pool_encode(int dtype, const void* x, const int64_t* tok_off, const int6
                     int d, int chunk, int l2_normalize, int out_layout, void* out, void* stream);
 
 /*
- * msa_encode - Stage 1 at corpus scale ("Global Memory Encoding", README
+ * msa_encode - Stage 1 at corpus scale (global memory encoding, README
  * Inference Pipeline; paper note 核心方法 > 架构: each document's K, V and
  * routing key K_r - the latter from an extra projector - chunk-wise mean
  * pooled).  From the hidden states x of the memory's tokens and the
@@ -206,7 +206,7 @@ int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, cons
 
 /*
  * msa_topk - Stage 2 selection (README, Overall Design > Architecture:
- * "selects Top-k documents"; paper note 核心方法 > 架构: top-k documents by
+ * the router keeps the k best documents; paper note 核心方法 > 架构: top-k documents by
  * cosine similarity).  For each query b the k documents with the largest
  * doc_score, ordered by (score descending, document id ascending); ties are
  * broken by the lower id, so the result is unique.
@@ -238,7 +238,7 @@ int msa_exclude_docs(float* doc_score, int B, int64_t n_docs, const int32_t* ids
 
 /*
  * msa_gather_kv - Stage 2 context assembly (README, Inference Pipeline:
- * "load only the selected K/V"; tiered storage with the content K/V in host
+ * only the selected documents' K/V are loaded; tiered storage with the content K/V in host
  * DRAM fetched when selected: README Inference Pipeline and paper note
  * Memory Parallel 推理).  For query b:
  *   the context is the chunks of documents ids[b,0], ids[b,1], ... (rank
@@ -326,14 +326,14 @@ int msa_context_append(const int32_t* ids, int B, int k, const int64_t* chunk_of
 /*
  * msa_sparse_attn - Stage 3 sparse attention (README, Overall Design >
  * Architecture: the selected compressed K/V concatenated with the query's
- * local K/V for autoregressive decoding; "Parallel (document-wise) RoPE"
- * and "Global RoPE (active context)"; paper note, Document-wise RoPE).
+ * local K/V for autoregressive decoding; its parallel (document-wise) RoPE
+ * and global RoPE items; paper note, Document-wise RoPE).
  * For query b, token t < T and query head hq (KV head g = hq / (Hq/Hkv)):
  *   keys: context entries e < ctx_len[b] at position ctx_pos[b,e] (each
  *         document restarts at 0), all visible; local tokens i < L_loc at
  *         position q_pos_offset + i, visible iff i <= L_loc - T + t (the T
  *         query tokens are the last T local tokens; causal).
- *   query position: q_pos_offset + L_loc - T + t ("offset by k": pass k).
+ *   query position: q_pos_offset + L_loc - T + t (the pages offset the query by k: pass k).
  *   RoPE: rotate-half, the pair (m, m + d/2) turns by pos * rope_base^(-2m/d)
  *         (angles reduced in float64), applied to q and every key on the fly.
  *         The (cos, sin) rows come from rope_table (msa_rope_table with the same

@@ -18,7 +18,7 @@ and section:
 
 Readings where the pages are silent (each also listed in the design notes):
 
-* R1  "token-wise max" runs over the query tokens and the document's pooled
+* R1  the token-wise max runs over the query tokens and the document's pooled
       chunks, giving one score per document; the head mean sits inside.
 * R2  pool first, then L2-normalise the pooled routing key.
 * R3  routing uses as many query heads as key heads (no GQA in routing).
@@ -30,7 +30,7 @@ Readings where the pages are silent (each also listed in the design notes):
       is an error.
 * R11 a pooled chunk sits at its chunk index inside its document (0, 1, ...).
 * R12 local token i sits at position q_pos_offset + i, q_pos_offset = k by
-      default ("offset by k").
+      default (the pages offset the query by k).
 * R13 the T query tokens are the last T of the L_loc local tokens; causal
       inside the local part; every retrieved entry is visible to every query
       token.
@@ -98,8 +98,9 @@ def chunk_offsets(tok_off: np.ndarray, chunk: int) -> np.ndarray:
 
 # ---------------------------------------------------------------------------
 # Stage 1: chunk-mean pooling and routing-key normalisation
-# [P1 架构; P2 Overall Design > Architecture ("chunk-mean pooled"); P2 Inference
-#  Pipeline, "Global Memory Encoding"; P3 MSA Layer 工作流程 step 1]
+# [P1 架构; P2 Overall Design > Architecture (K, V and K_r are mean-pooled per
+#  chunk); P2 Inference Pipeline, stage 1 (global memory encoding); P3 MSA Layer
+#  工作流程 step 1]
 # ---------------------------------------------------------------------------
 
 def pool(x: np.ndarray, tok_off: np.ndarray, chunk: int) -> np.ndarray:
@@ -143,8 +144,8 @@ def pool_encode(x: np.ndarray, tok_off: np.ndarray, chunk: int, normalize: bool,
 # ---------------------------------------------------------------------------
 # Stage 2: routing score, top-k, context assembly
 # [P1 架构 (cosine similarity, top-k documents); P2 Overall Design >
-#  Architecture ("cosine similarity (mean-pooled over heads, then token-wise
-#  max)"); P2 Inference Pipeline, "Online Routing & Context Assembly";
+#  Architecture (cosine similarity, averaged over heads, then a max over
+#  tokens); P2 Inference Pipeline, stage 2 (online routing and context assembly);
 #  P3 MSA Layer 工作流程 steps 2-4]
 # ---------------------------------------------------------------------------
 
@@ -218,8 +219,8 @@ def gather(ids_b: np.ndarray, chunk_off: np.ndarray, k_bar: np.ndarray, v_bar: n
 # ---------------------------------------------------------------------------
 # Stage 3: sparse attention with document-wise and global RoPE
 # [P1 Document-wise RoPE; P2 Overall Design > Architecture, "Parallel
-#  (document-wise) RoPE" and "Global RoPE (active context)"; P2 Inference
-#  Pipeline, "Sparse Generation"; P3 MSA Layer 工作流程 steps 4-5]
+#  (document-wise) RoPE and global RoPE items; P2 Inference Pipeline, stage 3
+#  (sparse generation); P3 MSA Layer 工作流程 steps 4-5]
 # ---------------------------------------------------------------------------
 
 def rope_angles(pos: np.ndarray, d: int, base: float) -> np.ndarray:
@@ -596,7 +597,7 @@ def gather_backward(ids: np.ndarray, chunk_off: np.ndarray, ctx_grads, n_chunks:
 
 # ---------------------------------------------------------------------------
 # Stage 1 from hidden states: projection, then the chunk-wise pool
-# [P2 Inference Pipeline, "Global Memory Encoding" (a forward over the corpus
+# [P2 Inference Pipeline, stage 1, global memory encoding (a forward over the corpus
 #  caches the chunk-pooled K, V, K_r); P1 架构 (each document's K/V/K_r, the
 #  routing key from an extra projector, chunk-wise mean pooled)]
 #

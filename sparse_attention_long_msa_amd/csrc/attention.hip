@@ -2,8 +2,8 @@
 // document-wise RoPE applied on the fly.
 // (MSA README, Overall Design > Architecture: the selected compressed K/V
 //  are concatenated with the query's local K/V for autoregressive decoding;
-//  "Parallel (document-wise) RoPE": every document restarts at position 0;
-//  "Global RoPE (active context)": the query starts at index k.  Paper note,
+//  under the parallel (document-wise) RoPE item every document restarts at
+//  position 0; under the global RoPE item the query starts at index k.  Paper note,
 //  Document-wise RoPE.)
 //
 // Keys of query b: context entries e < ctx_len[b] (position ctx_pos[b,e],

@@ -1,7 +1,7 @@
 // Stage 1 at corpus scale: projection of the document tokens' hidden states
 // to K, V and the routing key K_r, then the chunk-wise mean pool (and the
 // routing key's L2 normalisation), in one call.
-// (README, Overall Design > Inference Pipeline, "Global Memory Encoding":
+// (README, Overall Design > Inference Pipeline, stage 1, global memory encoding:
 //  a forward over the corpus caches the chunk-pooled (K, V, K_r); paper note
 //  核心方法 > 架构: each document's K/V/K_r, the routing key from an extra
 //  projector, chunk-wise mean pooled.)

@@ -1,8 +1,8 @@
 // Stage 2 context assembly: copy the selected documents' pooled K / V into a
 // contiguous per-query context, in rank order, with each entry's position
 // inside its document (document-wise RoPE restarts at 0 per document).
-// (MSA README, Inference Pipeline: "load only the selected K/V and
-//  concatenate with local context"; content K/V may live in host DRAM and be
+// (MSA README, Inference Pipeline: only the selected documents' K/V are
+//  loaded and joined to the local context; content K/V may live in host DRAM and be
 //  fetched when selected: README Inference Pipeline, paper note Memory
 //  Parallel 推理.)
 //

@@ -1,8 +1,8 @@
 // Stage 2 routing score: cosine of every pooled routing key against the
 // routing query, mean over heads, max over query tokens and over the
 // document's chunks -> one score per (query, document).
-// (MSA README, Overall Design > Architecture: "cosine similarity (mean-pooled
-//  over heads, then token-wise max)"; Inference Pipeline, Online Routing;
+// (MSA README, Overall Design > Architecture: cosine similarity averaged over
+//  heads, then a max over tokens; Inference Pipeline, Online Routing;
 //  paper note 核心方法 > 架构 and Memory Parallel 推理: the score matrix is tiled
 //  rather than materialised.)
 //

@@ -1,5 +1,5 @@
 // Stage 2 selection: the k best documents per query by (score desc, id asc).
-// (MSA README, Overall Design > Architecture: "selects Top-k documents";
+// (MSA README, Overall Design > Architecture: the router keeps the k best documents;
 //  paper note 核心方法 > 架构: top-k documents by cosine similarity.)
 //
 // A NaN score marks a document excluded from the selection (msa_exclude_docs):

@@ -34,7 +34,7 @@ class LayerRunner:
         self.max_doc_chunks = max_doc_chunks
         self.max_ctx = rounds * k * max_doc_chunks
         self.L_loc = local_len
-        # "offset by k": the number of documents in the context (rounds x k)
+        # the query offset is the number of documents in the context (rounds x k)
         self.q_pos_offset = rounds * k if q_pos_offset is None else q_pos_offset
         self.rope_base = rope_base
         self.sm_scale = 1.0 / math.sqrt(head_dim) if sm_scale is None else sm_scale

@@ -27,11 +27,17 @@ def _lib():
 def fill(out: torch.Tensor, seed: int, layer: int, tensor_id: int, start: int = 0, scale_pow2: int = 0,
          stream=None) -> torch.Tensor:
     """out.view(-1)[i] = generator value start + i of stream (layer, tensor_id)."""
+    return fill_stream(out, seed, stream_id(layer, tensor_id), start, scale_pow2, stream)
+
+
+def fill_stream(out: torch.Tensor, seed: int, stream_no: int, start: int = 0, scale_pow2: int = 0,
+                stream=None) -> torch.Tensor:
+    """out.view(-1)[i] = generator value start + i of the numbered stream."""
     assert out.is_cuda and out.is_contiguous()
     assert out.dtype in (torch.float32, torch.bfloat16)
     s = torch.cuda.current_stream().cuda_stream if stream is None else stream.cuda_stream
-    rc = _lib().msa_synth_fill(int(out.dtype == torch.bfloat16), seed, stream_id(layer, tensor_id), start,
-                               out.numel(), scale_pow2, out.data_ptr(), s)
+    rc = _lib().msa_synth_fill(int(out.dtype == torch.bfloat16), seed, stream_no, start, out.numel(), scale_pow2,
+                               out.data_ptr(), s)
     if rc != 0:
         raise RuntimeError(f"msa_synth_fill failed ({rc})")
     return out

@@ -11,6 +11,7 @@ import torch
 
 import oracle as O
 import sparse_attention_long_msa_amd as M
+from sparse_attention_long_msa_amd import _binding as MB
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -204,3 +205,65 @@ def test_pool_and_docmap_validation():
     assert L.msa_chunk_doc_map(None, 4, 8, P, None) == 1
     assert L.msa_chunk_doc_map(P, 0, 8, P, None) == 1
     assert M.lib.msa_last_error().decode() != ""
+
+
+# ---------------------------------------------------------------- binding-side operand checks
+# The Python binding rejects operands that a kernel could not read correctly
+# (host memory where device memory is required, pageable memory where the
+# host tier needs pinned memory, strided views, wrong dtypes or shapes) with
+# ValueError, before any pointer reaches the library.  On a machine without a
+# GPU every CPU tensor is such an operand, so these run here.
+
+def _cpu(shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_rejects_host_tensor_as_device_operand():
+    q_r = _cpu((1, 4, 8, 128))
+    kr = _cpu((32, 8, 128))
+    cd = torch.zeros(32, dtype=torch.int32)
+    with pytest.raises(ValueError, match="q_r: must be in device memory"):
+        M.msa_route_score(q_r, kr, cd, 4)
+    with pytest.raises(ValueError, match="doc_score: must be in device memory"):
+        M.msa_topk(torch.zeros((1, 10)), 4)
+    with pytest.raises(ValueError, match="chunk_off: must be in device memory"):
+        M.msa_chunk_doc_map(torch.zeros(5, dtype=torch.int64), 8)
+    with pytest.raises(ValueError, match="x: must be in device memory"):
+        M.msa_pool_encode(_cpu((100, 8, 128)), torch.zeros(5, dtype=torch.int64), torch.zeros(5, dtype=torch.int64),
+                          cd, 64, True)
+    with pytest.raises(ValueError, match="q: must be in device memory"):
+        M.msa_sparse_attn(_cpu((1, 4, 32, 128)), _cpu((1, 16, 8, 128)), _cpu((1, 16, 8, 128)),
+                          torch.zeros((1, 16), dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+                          _cpu((1, 8, 8, 128)), _cpu((1, 8, 8, 128)), 4)
+    with pytest.raises(ValueError, match="x: expected a torch tensor"):
+        M.msa_encode(np.zeros((64, 256), np.float32), None, None, None, None, 64, 8, 128)
+
+
+def test_binding_rejects_pageable_host_tier():
+    ids = _cpu((1, 4), torch.int32)
+    co = torch.zeros(11, dtype=torch.int64)
+    kb = _cpu((80, 8, 128))
+    for mode in (M.MSA_SRC_HOST_MAPPED, M.MSA_SRC_HOST_MEMCPY):
+        # the device operands are checked first; a device-only box would reach the
+        # host-tier check, which a pageable tensor fails the same way
+        with pytest.raises(ValueError, match="(ids: must be in device memory|k_bar: must be in pinned host memory)"):
+            M.msa_gather_kv(ids, co, kb, kb, 8, 32, src_mode=mode)
+    with pytest.raises(ValueError, match="k_bar: must be in pinned host memory"):
+        MB._pinned(kb, "k_bar")
+
+
+def test_binding_rejects_strided_wrong_dtype_and_shape():
+    t = torch.zeros((8, 16))
+    with pytest.raises(ValueError, match="contiguous"):
+        MB._layout(t.t(), "x", None, None)
+    with pytest.raises(ValueError, match="dtype torch.float32, expected torch.int32"):
+        MB._layout(t, "ids", torch.int32, None)
+    with pytest.raises(ValueError, match=r"shape \(8, 16\), expected \(8, 8\)"):
+        MB._layout(t, "out", torch.float32, (8, 8))
+    MB._layout(t, "out", torch.float32, (8, None))          # None matches any extent
+    with pytest.raises(ValueError, match="required"):
+        MB._dev(None, "q")
+    MB._dev(None, "ws", optional=True)
+    with pytest.raises(ValueError, match="chunk_off_h"):
+        MB._host_i64(np.zeros(4, np.int32), "chunk_off_h")
+    MB._host_i64(np.zeros(4, np.int64), "chunk_off_h", 4)
