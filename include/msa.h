@@ -374,6 +374,29 @@ int msa_sparse_attn_indexed(int dtype, const void* q, int B, int T, int Hq, int 
                             float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * msa_sparse_attn_indexed_noalloc - msa_sparse_attn_indexed for callers that
+ * cannot allocate memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, same kernels and the
+ * same result, bit for bit, as msa_sparse_attn_indexed, without ws/ws_bytes:
+ * the workspace is a device array inside the library, MSA_NOALLOC_SCRATCH_BYTES
+ * long, that each GPU the library runs on holds until the process ends.  The
+ * call allocates nothing.  The caller still owns the inputs and `out`.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or host threads) race and must be serialised by
+ * the caller.
+ * Errors: those of msa_sparse_attn_indexed; UNSUPPORTED when the shape's
+ * workspace (msa_sparse_attn_workspace) exceeds MSA_NOALLOC_SCRATCH_BYTES;
+ * HIP when the array's device address cannot be taken.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int msa_sparse_attn_indexed_noalloc(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
+                                    const void* k_bar, const void* v_bar, int64_t n_chunks, const int32_t* ctx_row,
+                                    const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx, const void* k_loc,
+                                    const void* v_loc, int L_loc, int q_pos_offset, float rope_base,
+                                    const float* rope_table, int rope_table_rows, float sm_scale, float* out,
+                                    void* stream);
+
+/*
  * msa_rope_table - the (cos, sin) rows msa_sparse_attn rotates with, built
  * once and reused by every layer and call with the same base and d.  Row p,
  * pair m holds (cos, sin)(p * rope_base^(-2m/d)) with the angle formed and

@@ -38,6 +38,8 @@ from ._binding import (  # noqa: F401
     msa_sparse_attn_backward,
     msa_sparse_attn_backward_workspace,
     msa_sparse_attn_indexed,
+    msa_sparse_attn_indexed_noalloc,
+    MSA_NOALLOC_SCRATCH_BYTES,
     msa_sparse_attn_workspace,
     msa_topk,
     msa_topk_context_index,

@@ -47,6 +47,8 @@ _SIGS = {
                              _F, _P, _I, _F, _P, _P, _S, _P]),
     "msa_sparse_attn_indexed": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _L, _P, _P, _P, _I, _P, _P, _I, _I,
                                      _F, _P, _I, _F, _P, _P, _S, _P]),
+    "msa_sparse_attn_indexed_noalloc": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _L, _P, _P, _P, _I, _P, _P, _I,
+                                             _I, _F, _P, _I, _F, _P, _P]),
     "msa_rope_table_rows": (_I, [_I, _I, _I]),
     "msa_rope_table": (_I, [_I, _I, _F, _P, _P]),
     "msa_route_argmax_workspace": (_S, [_I, _I, _I, _I, _I, _L, _L]),
@@ -464,6 +466,31 @@ def msa_sparse_attn_indexed(q, k_bar, v_bar, ctx_row, ctx_pos, ctx_len, k_loc, v
         _ptr(ctx_len), max_ctx, _ptr(k_loc), _ptr(v_loc), L_loc, q_pos_offset, float(rope_base), _ptr(rope_table),
         0 if rope_table is None else rope_table.shape[0], float(sm_scale), _ptr(out), _ptr(ws), wsb,
         _stream(stream)))
+    return out
+
+
+MSA_NOALLOC_SCRATCH_BYTES = 32 << 20   # include/msa.h
+
+
+def msa_sparse_attn_indexed_noalloc(q, k_bar, v_bar, ctx_row, ctx_pos, ctx_len, k_loc, v_loc, q_pos_offset,
+                                    rope_base=1e6, sm_scale=None, out=None, rope_table=None, stream=None):
+    """msa_sparse_attn_indexed with the library's own device scratch instead
+    of a workspace (for callers that cannot allocate; pass ``out`` and
+    ``rope_table`` to allocate nothing here either)."""
+    B, T, Hq, d, Hkv, L_loc, out = _attn_operands(q, k_loc, v_loc, rope_table, out)
+    _dev(k_bar, "k_bar", q.dtype, (None, Hkv, d))
+    n_chunks = k_bar.shape[0]
+    _dev(v_bar, "v_bar", q.dtype, (n_chunks, Hkv, d))
+    _dev(ctx_row, "ctx_row", _I32, (B, None))
+    max_ctx = ctx_row.shape[1]
+    _dev(ctx_pos, "ctx_pos", _I32, (B, max_ctx))
+    _dev(ctx_len, "ctx_len", _I32, (B,))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    _check("msa_sparse_attn_indexed_noalloc", lib.msa_sparse_attn_indexed_noalloc(
+        _dtype(q), _ptr(q), B, T, Hq, Hkv, d, _ptr(k_bar), _ptr(v_bar), n_chunks, _ptr(ctx_row), _ptr(ctx_pos),
+        _ptr(ctx_len), max_ctx, _ptr(k_loc), _ptr(v_loc), L_loc, q_pos_offset, float(rope_base), _ptr(rope_table),
+        0 if rope_table is None else rope_table.shape[0], float(sm_scale), _ptr(out), _stream(stream)))
     return out
 
 

@@ -20,6 +20,7 @@
 // LDS.  Splits are merged by a combine kernel.  RoPE angles come from a
 // cos/sin table computed in float64 per call.
 #include <algorithm>
+#include <mutex>
 
 #include "attn_common.h"
 
@@ -999,4 +1000,65 @@ extern "C" int msa_sparse_attn_indexed(int dtype, const void* q, int B, int T, i
   return sparse_attn("msa_sparse_attn_indexed", dtype, q, B, T, Hq, Hkv, d, k_bar, v_bar, ctx_row, n_chunks, ctx_pos,
                      ctx_len, max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows,
                      sm_scale, out, nullptr, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- no-alloc variant
+// msa_sparse_attn_indexed for callers that cannot allocate: its workspace
+// (the RoPE table when the caller passes none, the split partials O, m, l)
+// is one file-scope device array that each GPU the library runs on holds
+// until the process ends.  In host code the array's name is not a device
+// address: its address on each device comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address reaches a
+// kernel.  Nothing in the scratch must start at zero: every split writes each
+// of its rows' partials before the combine reads them.  Calls that overlap on
+// one GPU share the array and race.
+namespace msa {
+
+static __device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[NOALLOC_MAX_DEVICES];
+
+// The device address of `scratch` on the current device.
+static int scratch_address(const std::string& fn, void** ptr) {
+  int dev = -1;
+  MSA_HIP_CHECK(hipGetDevice(&dev));
+  MSA_REQUIRE(dev >= 0 && dev < NOALLOC_MAX_DEVICES, MSA_ERR_UNSUPPORTED, fn + ": device ordinal beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    MSA_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    MSA_REQUIRE(p, MSA_ERR_HIP, fn + ": hipGetSymbolAddress gave NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return MSA_OK;
+}
+
+}  // namespace msa
+
+extern "C" int msa_sparse_attn_indexed_noalloc(int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
+                                               const void* k_bar, const void* v_bar, int64_t n_chunks,
+                                               const int32_t* ctx_row, const int32_t* ctx_pos, const int32_t* ctx_len,
+                                               int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
+                                               int q_pos_offset, float rope_base, const float* rope_table,
+                                               int rope_table_rows, float sm_scale, float* out, void* stream) {
+  using namespace msa;
+  const std::string fn = "msa_sparse_attn_indexed_noalloc";
+  MSA_REQUIRE(ctx_row, MSA_ERR_INVALID_ARG, fn + ": NULL pointer");
+  MSA_REQUIRE(n_chunks >= 1 && n_chunks <= INT32_MAX, MSA_ERR_INVALID_ARG, fn + ": n_chunks must lie in [1, 2^31)");
+  MSA_REQUIRE(B >= 1 && T >= 1 && Hq >= 1 && Hkv >= 1 && d >= 2 && max_ctx >= 1 && L_loc >= 1 && q_pos_offset >= 0,
+              MSA_ERR_INVALID_ARG, fn + ": non-positive size");
+  const size_t need = msa_sparse_attn_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
+  MSA_REQUIRE(need <= MSA_NOALLOC_SCRATCH_BYTES, MSA_ERR_UNSUPPORTED,
+              fn + ": this shape needs " + std::to_string(need) + " bytes of workspace; the no-alloc entry point "
+                   "holds " + std::to_string(size_t(MSA_NOALLOC_SCRATCH_BYTES)) +
+                   " (use msa_sparse_attn_indexed with a caller workspace)");
+  void* ws = nullptr;
+  const int st = scratch_address(fn, &ws);
+  if (st != MSA_OK) return st;
+  return sparse_attn(fn, dtype, q, B, T, Hq, Hkv, d, k_bar, v_bar, ctx_row, n_chunks, ctx_pos, ctx_len, max_ctx,
+                     k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows, sm_scale, out, nullptr,
+                     ws, MSA_NOALLOC_SCRATCH_BYTES, stream);
 }
