@@ -205,6 +205,30 @@ int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, cons
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * msa_chunk_scores, msa_segment_max - msa_route_score in two launches (the
+ * same definition, README Overall Design > Architecture): the per-chunk
+ * scores, then a standalone segmented max by document.  For every chunk c
+ *   chunk_score[b,c] = max over tokens t < T of
+ *                      (1/H) * sum_h < q_r[b,t,h,:] / max(||q_r[b,t,h,:]||, 1e-8), kr_hat[c,h,:] >
+ * and then
+ *   doc_score[b,i] = max over c in [chunk_off[i], chunk_off[i+1]) of chunk_score[b,c]
+ * (-inf for an empty document).  Max is exact, so the composition equals
+ * msa_route_score bit for bit; msa_route_score fuses the second step into the
+ * scan and never writes the [B, n_chunks] scores.
+ *   msa_chunk_scores: arguments as msa_route_score without the document map;
+ *     chunk_score [B, n_chunks] float32 output; the workspace is
+ *     msa_route_score_workspace(dtype, B, T, H, d, n_chunks, n_chunks) bytes.
+ *     UNSUPPORTED also for n_chunks >= 2^31.
+ *   msa_segment_max: chunk_score [B, n_chunks] float32, chunk_off [n_docs+1]
+ *     int64 (device), doc_score [B, n_docs] float32 output.  Offsets outside
+ *     [0, n_chunks] are clamped.  INVALID_ARG for NULL or non-positive sizes.
+ */
+int msa_chunk_scores(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat, int kr_layout,
+                     int64_t n_chunks, float* chunk_score, void* ws, size_t ws_bytes, void* stream);
+int msa_segment_max(const float* chunk_score, int B, int64_t n_chunks, const int64_t* chunk_off, int64_t n_docs,
+                    float* doc_score, void* stream);
+
+/*
  * msa_topk - Stage 2 selection (README, Overall Design > Architecture:
  * the router keeps the k best documents; paper note 核心方法 > 架构: top-k documents by
  * cosine similarity).  For each query b the k documents with the largest

@@ -19,6 +19,8 @@ from ._binding import (  # noqa: F401
     msa_abi_version,
     msa_chunk_doc_map,
     msa_chunk_offsets,
+    msa_chunk_scores,
+    msa_segment_max,
     msa_context_append,
     msa_context_index,
     msa_encode,

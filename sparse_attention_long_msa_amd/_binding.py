@@ -34,6 +34,8 @@ _SIGS = {
     "msa_pool_encode": (_I, [_I, _P, _P, _P, _P, _L, _L, _L, _I, _I, _I, _I, _I, _P, _P]),
     "msa_route_score_workspace": (_S, [_I, _I, _I, _I, _I, _L, _L]),
     "msa_route_score": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P, _P, _S, _P]),
+    "msa_chunk_scores": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _L, _P, _P, _S, _P]),
+    "msa_segment_max": (_I, [_P, _I, _L, _P, _L, _P, _P]),
     "msa_topk_workspace": (_S, [_I, _L, _I]),
     "msa_topk": (_I, [_P, _I, _L, _I, _P, _P, _P, _S, _P]),
     "msa_gather_kv": (_I, [_I, _P, _I, _I, _P, _P, _L, _I, _P, _P, _L, _I, _I, _I, _I,
@@ -258,6 +260,39 @@ def msa_route_score(q_r, kr_hat, chunk_doc, n_docs, doc_score=None, ws=None, lay
     _check("msa_route_score", lib.msa_route_score(
         dt, _ptr(q_r), B, T, H, d, _ptr(kr_hat), layout, _ptr(chunk_doc), n_docs, n_chunks, _ptr(doc_score),
         _ptr(ws), wsb, _stream(stream)))
+    return doc_score
+
+
+def msa_chunk_scores(q_r, kr_hat, n_chunks, chunk_score=None, ws=None, layout=MSA_LAYOUT_ROWS, stream=None):
+    """Per-chunk routing scores [B, n_chunks]: the max over the query's tokens
+    of the head-mean cosine (msa_route_score before its document max)."""
+    _dev(q_r, "q_r", _FLOAT, (None, None, None, None))
+    B, T, H, d = q_r.shape
+    _dev(kr_hat, "kr_hat", q_r.dtype, (None, H, d))
+    if kr_hat.shape[0] < padded_chunks(n_chunks, layout):
+        raise ValueError("kr_hat holds fewer than n_chunks chunks")
+    if chunk_score is None:
+        chunk_score = torch.empty((B, n_chunks), dtype=torch.float32, device=q_r.device)
+    _dev(chunk_score, "chunk_score", _F32, (B, n_chunks))
+    _dev(ws, "ws", optional=True)
+    dt = _dtype(q_r)
+    ws, wsb = _ws(msa_route_score_workspace(dt, B, T, H, d, n_chunks, n_chunks), q_r.device, ws)
+    _check("msa_chunk_scores", lib.msa_chunk_scores(dt, _ptr(q_r), B, T, H, d, _ptr(kr_hat), layout, n_chunks,
+                                                    _ptr(chunk_score), _ptr(ws), wsb, _stream(stream)))
+    return chunk_score
+
+
+def msa_segment_max(chunk_score, chunk_off, doc_score=None, stream=None):
+    """doc_score[b, i] = max of chunk_score[b, chunk_off[i]:chunk_off[i+1]] (-inf if empty)."""
+    _dev(chunk_score, "chunk_score", _F32, (None, None))
+    B, n_chunks = chunk_score.shape
+    _dev(chunk_off, "chunk_off", _I64, (None,))
+    n_docs = chunk_off.numel() - 1
+    if doc_score is None:
+        doc_score = torch.empty((B, n_docs), dtype=torch.float32, device=chunk_score.device)
+    _dev(doc_score, "doc_score", _F32, (B, n_docs))
+    _check("msa_segment_max", lib.msa_segment_max(_ptr(chunk_score), B, n_chunks, _ptr(chunk_off), n_docs,
+                                                  _ptr(doc_score), _stream(stream)))
     return doc_score
 
 

@@ -50,6 +50,12 @@ __device__ __forceinline__ float dpp_row_max16(float v) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// The document owning chunk c; without a map every chunk is its own
+// "document", which gives the per-chunk scores of msa_chunk_scores.
+__device__ __forceinline__ int doc_of(const int32_t* __restrict__ chunk_doc, int64_t c) {
+  return chunk_doc ? chunk_doc[c] : int(c);
+}
+
 // Segmented max over lanes 0..31 (one chunk each) by document id, then one
 // emit(doc, max) per run head.  doc < 0 marks a lane with no chunk.
 template <class Emit>
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
   float* tab = reinterpret_cast<float*>(smem + size_t(NT) * H * RS_KK * 1024 + size_t(RS_WAVES) * RS_SCRATCH +
                                         size_t(H) * NT * 16 * 4);
   const int64_t c_last = (t_end * TILE < n_chunks ? t_end * TILE : n_chunks) - 1;
-  const int doc_lo = chunk_doc[t_begin * TILE], doc_hi = chunk_doc[c_last];
+  const int doc_lo = doc_of(chunk_doc, t_begin * TILE), doc_hi = doc_of(chunk_doc, c_last);
   const int col_end = col0 + 64 < J ? col0 + 64 : J;
   const int q_lo = col0 / T, q_hi = (col_end - 1) / T;
   const int nq = q_hi - q_lo + 1;
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
   // waves without a tile skip the loop but still reach the table's barrier
   if (tile < t_end) {
     for (;;) {
-      const int mydoc = (lane < TILE && tile * TILE + lane < n_chunks) ? chunk_doc[tile * TILE + lane] : -1;
+      const int mydoc = (lane < TILE && tile * TILE + lane < n_chunks) ? doc_of(chunk_doc, tile * TILE + lane) : -1;
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -377,7 +383,7 @@ __global__ void route_score_vec_kernel(const typename Elem<DT>::T* __restrict__ 
   if (p >= n_chunks * J) return;
   const int64_t c = p / J;
   const int j = int(p % J);
-  const int doc = chunk_doc[c];
+  const int doc = doc_of(chunk_doc, c);
   if (doc < 0 || doc >= n_docs) return;
   float s = 0.f;
   for (int h = 0; h < H; ++h) {
@@ -402,25 +408,29 @@ extern "C" size_t msa_route_score_workspace(int dtype, int B, int T, int H, int 
   return msa::align_up(size_t(B) * T * H * sizeof(float), 256);
 }
 
-extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
-                               int kr_layout, const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks,
-                               float* doc_score, void* ws, size_t ws_bytes, void* stream) {
+namespace msa {
+
+// Shared body of msa_route_score (chunk_doc given) and msa_chunk_scores
+// (chunk_doc NULL: every chunk is its own document, n_docs = n_chunks).
+static int route_score(const std::string& fn, int dtype, const void* q_r, int B, int T, int H, int d,
+                       const void* kr_hat, int kr_layout, const int32_t* chunk_doc, int64_t n_docs,
+                       int64_t n_chunks, float* doc_score, void* ws, size_t ws_bytes, void* stream) {
   using namespace msa;
-  MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, "msa_route_score: bad dtype");
-  MSA_REQUIRE(q_r && kr_hat && chunk_doc && doc_score, MSA_ERR_INVALID_ARG, "msa_route_score: NULL pointer");
+  MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
+  MSA_REQUIRE(q_r && kr_hat && doc_score, MSA_ERR_INVALID_ARG, fn + ": NULL pointer");
   MSA_REQUIRE(B >= 1 && T >= 1 && H >= 1 && d >= 1 && n_docs >= 1 && n_chunks >= 1, MSA_ERR_INVALID_ARG,
-              "msa_route_score: non-positive size");
-  MSA_REQUIRE(int64_t(B) * T < (int64_t(1) << 24), MSA_ERR_UNSUPPORTED, "msa_route_score: B*T too large");
-  MSA_REQUIRE(d <= 256 && d % 8 == 0, MSA_ERR_UNSUPPORTED, "msa_route_score: d must be a multiple of 8, <= 256");
+              fn + ": non-positive size");
+  MSA_REQUIRE(int64_t(B) * T < (int64_t(1) << 24), MSA_ERR_UNSUPPORTED, fn + ": B*T too large");
+  MSA_REQUIRE(d <= 256 && d % 8 == 0, MSA_ERR_UNSUPPORTED, fn + ": d must be a multiple of 8, <= 256");
   MSA_REQUIRE(kr_layout == MSA_LAYOUT_ROWS || kr_layout == MSA_LAYOUT_TILED, MSA_ERR_INVALID_ARG,
-              "msa_route_score: bad kr_layout");
+              fn + ": bad kr_layout");
   MSA_REQUIRE(kr_layout == MSA_LAYOUT_ROWS || use_mfma(dtype, H, d), MSA_ERR_UNSUPPORTED,
-              "msa_route_score: the tiled layout needs the MFMA path (bf16, H = 8, d = 128)");
+              fn + ": the tiled layout needs the MFMA path (bf16, H = 8, d = 128)");
   const size_t need = msa_route_score_workspace(dtype, B, T, H, d, n_docs, n_chunks);
-  MSA_REQUIRE(ws_bytes >= need, MSA_ERR_WORKSPACE, "msa_route_score: workspace too small");
-  MSA_REQUIRE(need == 0 || ws, MSA_ERR_INVALID_ARG, "msa_route_score: NULL workspace");
+  MSA_REQUIRE(ws_bytes >= need, MSA_ERR_WORKSPACE, fn + ": workspace too small");
+  MSA_REQUIRE(need == 0 || ws, MSA_ERR_INVALID_ARG, fn + ": NULL workspace");
   MSA_REQUIRE(uintptr_t(q_r) % 16 == 0 && uintptr_t(kr_hat) % 16 == 0, MSA_ERR_INVALID_ARG,
-              "msa_route_score: q_r and kr_hat must be 16-byte aligned");
+              fn + ": q_r and kr_hat must be 16-byte aligned");
   hipStream_t s = as_stream(stream);
   const int J = B * T;
   const int64_t nscore = int64_t(B) * n_docs;
@@ -501,6 +511,58 @@ extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, 
   else
     hipLaunchKernelGGL(route_score_vec_kernel<MSA_F32>, grid, block, 0, s, static_cast<const float*>(q_r), T, J,
                        H, d, static_cast<const float*>(kr_hat), chunk_doc, n_docs, n_chunks, winv, doc_score);
+  MSA_LAUNCH_CHECK();
+  return MSA_OK;
+}
+
+}  // namespace msa
+
+extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
+                               int kr_layout, const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks,
+                               float* doc_score, void* ws, size_t ws_bytes, void* stream) {
+  MSA_REQUIRE(chunk_doc, MSA_ERR_INVALID_ARG, "msa_route_score: NULL pointer");
+  return msa::route_score("msa_route_score", dtype, q_r, B, T, H, d, kr_hat, kr_layout, chunk_doc, n_docs, n_chunks,
+                          doc_score, ws, ws_bytes, stream);
+}
+
+extern "C" int msa_chunk_scores(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
+                                int kr_layout, int64_t n_chunks, float* chunk_score, void* ws, size_t ws_bytes,
+                                void* stream) {
+  MSA_REQUIRE(n_chunks < (int64_t(1) << 31), MSA_ERR_UNSUPPORTED, "msa_chunk_scores: n_chunks >= 2^31");
+  return msa::route_score("msa_chunk_scores", dtype, q_r, B, T, H, d, kr_hat, kr_layout, nullptr, n_chunks, n_chunks,
+                          chunk_score, ws, ws_bytes, stream);
+}
+
+namespace msa {
+
+// doc_score[b, i] = max of chunk_score[b, c] over the chunks c of document i
+// (chunk_off CSR); -inf for an empty document.  One thread per (query, document).
+__global__ void segment_max_kernel(const float* __restrict__ chunk_score, int B, int64_t n_chunks,
+                                   const int64_t* __restrict__ chunk_off, int64_t n_docs,
+                                   float* __restrict__ doc_score) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(B) * n_docs) return;
+  const int64_t b = i / n_docs, doc = i % n_docs;
+  int64_t lo = chunk_off[doc], hi = chunk_off[doc + 1];
+  lo = lo < 0 ? 0 : (lo > n_chunks ? n_chunks : lo);
+  hi = hi < lo ? lo : (hi > n_chunks ? n_chunks : hi);
+  const float* row = chunk_score + b * n_chunks;
+  float m = -INFINITY;
+  for (int64_t c = lo; c < hi; ++c) m = fmaxf(m, row[c]);
+  doc_score[i] = m;
+}
+
+}  // namespace msa
+
+extern "C" int msa_segment_max(const float* chunk_score, int B, int64_t n_chunks, const int64_t* chunk_off,
+                               int64_t n_docs, float* doc_score, void* stream) {
+  using namespace msa;
+  MSA_REQUIRE(chunk_score && chunk_off && doc_score, MSA_ERR_INVALID_ARG, "msa_segment_max: NULL pointer");
+  MSA_REQUIRE(B >= 1 && n_chunks >= 1 && n_docs >= 1, MSA_ERR_INVALID_ARG, "msa_segment_max: non-positive size");
+  MSA_REQUIRE(int64_t(B) * n_docs < (int64_t(1) << 40), MSA_ERR_UNSUPPORTED, "msa_segment_max: too many scores");
+  const int64_t n = int64_t(B) * n_docs;
+  hipLaunchKernelGGL(segment_max_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, as_stream(stream),
+                     chunk_score, B, n_chunks, chunk_off, n_docs, doc_score);
   MSA_LAUNCH_CHECK();
   return MSA_OK;
 }

@@ -267,3 +267,16 @@ def test_binding_rejects_strided_wrong_dtype_and_shape():
     with pytest.raises(ValueError, match="chunk_off_h"):
         MB._host_i64(np.zeros(4, np.int32), "chunk_off_h")
     MB._host_i64(np.zeros(4, np.int64), "chunk_off_h", 4)
+
+
+def test_unfused_routing_validation():
+    L = M.lib
+    #                     dt q  B  T  H  d   kr layout n_chunks score ws wsb stream
+    assert L.msa_chunk_scores(1, None, 1, 1, 8, 128, P, 0, 10, Q, None, 0, None) == 1
+    assert L.msa_chunk_scores(1, P, 1, 1, 8, 128, P, 0, 0, Q, None, 0, None) == 1
+    assert L.msa_chunk_scores(1, P, 1, 1, 8, 128, P, 0, 1 << 31, Q, None, 0, None) == 2
+    assert L.msa_chunk_scores(0, P, 1, 16, 8, 128, P, 0, 10, Q, P, 8, None) == 3      # float32 needs norms
+    #                    score B n_chunks chunk_off n_docs doc_score stream
+    assert L.msa_segment_max(None, 1, 10, P, 4, Q, None) == 1
+    assert L.msa_segment_max(P, 0, 10, P, 4, Q, None) == 1
+    assert L.msa_segment_max(P, 1, 10, None, 4, Q, None) == 1

@@ -126,6 +126,46 @@ def test_route_score(bf16, layout, B, T):
     assert np.argmax(got[0]) == nd
 
 
+@pytest.mark.parametrize("bf16,layout", [(True, 1), (True, 0), (False, 0)])
+@pytest.mark.parametrize("B,T", [(1, 64), (32, 1), (1, 128), (3, 7)])
+def test_route_score_unfused_equals_fused(bf16, layout, B, T):
+    """The unfused routing score: per-chunk scores (the max over the query's
+    tokens, compared with the oracle's chunk cosines) then the standalone
+    segmented max by document, which equals the fused msa_route_score bit for
+    bit (max is exact), empty documents included."""
+    H, d = 8, 128
+    lens = ragged_lengths(60 + T, 300, 1, 1500, n_empty=7)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    dt = "bf16" if bf16 else "f32"
+    store = O.round_to_store(O.l2_normalize(gen(61, 0, synth.T_KR, (n_chunks, H, d), bf16).astype(np.float64)), dt)
+    q = gen(62, 0, synth.T_QR, (B, T, H, d), bf16)
+    st = to_dev(tile_np(store) if layout == 1 else store, bf16)
+    qd = to_dev(q, bf16)
+    cs = M.msa_chunk_scores(qd, st, n_chunks, layout=layout)
+    ref_c = O.chunk_cosines(q, store).max(axis=1)                  # token max per chunk [B, N]
+    err = check_scores(host(cs), ref_c, RTOL_SCORE[dt], k=16)
+    fused = M.msa_route_score(qd, st, cd, len(lens), layout=layout)
+    seg = M.msa_segment_max(cs, co_d)
+    assert torch.equal(seg, fused)
+    print(f"unfused route score {dt} layout={layout} B={B} T={T}: chunk-score normwise err {err:.3g}")
+
+
+def test_segment_max_is_the_document_max():
+    rng = np.random.default_rng(7)
+    lens = rng.integers(0, 9, size=5000)
+    lens[:3] = 0
+    lens[-1] = 0
+    chunk_off = synth.offsets(lens)
+    n_chunks = int(chunk_off[-1])
+    x = rng.standard_normal((3, n_chunks)).astype(np.float32)
+    got = host(M.msa_segment_max(torch.from_numpy(x).to(dev()), to_dev_i64(chunk_off)))
+    want = np.full((3, len(lens)), -np.inf)
+    for i in range(len(lens)):
+        if lens[i]:
+            want[:, i] = x[:, chunk_off[i]:chunk_off[i + 1]].max(axis=1)
+    np.testing.assert_array_equal(got, want)
+
+
 def test_route_score_document_table_paths():
     """64 single-token queries over a memory mixing one-chunk documents (a
     workgroup's range holds more (document, query) pairs than its LDS table:
