@@ -1,13 +1,12 @@
 """Benchmark of the MSA routing + sparse-attention hot path on one MI355X.
 
 One step = one query through all routed layers: per layer, routing score over
-that layer's whole pooled routing-key store -> top-k -> context assembly
-(content K/V fetched from the host tier or HBM) -> sparse attention.  The
-default workload is the 100M-token memory (195,312 documents x 512 tokens,
-chunk 64 -> 1,562,496 pooled chunks per layer, 18 layers, 8 heads x 128,
-bf16; the routing-key store is 57.6 GB in HBM), query of 64 tokens, 32 query
-heads, 4,096 local tokens, k = 16.  Inputs are seeded synthetic data
-generated on the device before the timed region.
+that layer's whole pooled routing-key store -> top-k -> context assembly ->
+sparse attention.  The default workload is the 100M-token memory (195,312
+documents x 512 tokens, chunk 64 -> 1,562,496 pooled chunks per layer, 18
+layers, 8 heads x 128, bf16; the routing-key store is 57.6 GB in HBM), query
+of 64 tokens, 32 query heads, 4,096 local tokens, k = 16.  Inputs are seeded
+synthetic data generated on the device before the timed region.
 
 Timing: the K timed steps are measured by the wall clock between two device
 synchronisations; inside them only one pair of HIP events per step brackets a
@@ -16,8 +15,16 @@ breakdown comes from up to 3 further steps with events between all stages
 (each event record idles the device for a few microseconds, so these steps
 are not part of the timed region).
 
-Prints one JSON line.  --gpus above 1 is not supported (one GPU per process,
-no collectives in this build).
+The default run prints one JSON line: the 100M-token step with the content
+K/V in HBM (the line's value), then, in the same line,
+  ceiling      the streaming-read rate over the same bytes (msa_stream_read),
+  host_tier    the same step with the content K/V in pinned host memory,
+               fetched per layer by the zero-copy gather kernel (mapped) and
+               by hipMemcpyAsync per document (memcpy),
+  cpu_baseline the float64 oracle's routing on a bounded sample,
+  per_config   warm and cold lines of the four smaller presets with the
+               oracle's routing and attention times.
+--gpus above 1 is not supported (one GPU per process, no collectives).
 """
 from __future__ import annotations
 
@@ -37,11 +44,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="cfg4")
-    ap.add_argument("--kv-tier", choices=["host", "hbm"], default="host")
-    ap.add_argument("--gather", choices=["mapped", "memcpy"], default="mapped",
-                    help="host tier: how the selected K/V cross the host link")
     ap.add_argument("--hbm-assembly", choices=["index", "copy"], default="index",
-                    help="HBM tier: attention reads the selected rows in place (index) or from a gathered copy")
+                    help="attention reads the selected rows in place (index) or from a gathered copy")
+    ap.add_argument("--no-host-tier", action="store_true",
+                    help="skip the host-tier leg (content K/V in pinned host memory, fetched per layer)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-config lines of the smaller presets (after the 100M-token line)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--layers", type=int, default=None, help="override the routed-layer count (profiling only)")
     ap.add_argument("--rounds", type=int, default=1,
                     help="Memory Interleave rounds per layer (> 1: route, skip the fetched documents, select and "
@@ -80,256 +89,482 @@ def main():
     if args.encode:
         return encode_main(args, torch)
 
-    import synth
     from synth import configs
-    from synth import device as SD
-    import sparse_attention_long_msa_amd as M
 
     p = configs.PRESETS[args.config]()
-    layers = p.layers if args.layers is None else args.layers
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    bf = torch.bfloat16 if p.bf16 else torch.float32
-    esz = 2 if p.bf16 else 4
-    H, d, N, D = p.H, p.d, p.n_chunks, p.n_docs
-    log(f"{p.name}: {D} docs, {N} chunks/layer, {layers} layers, store {N * H * d * esz * layers / 1e9:.1f} GB")
+    pb = PresetBench(torch, p, args.layers, rounds=args.rounds)
+    pb.build_stores()
+    pb.build_content("hbm")
+    assembly = args.hbm_assembly if args.rounds == 1 else "index"
+    pb.make_runner("hbm", indexed=assembly == "index")
+    recall = pb.needle_recall()
+    res = pb.headline(args.steps, args.warmup)
+    res["config"]["gather"] = f"hbm-{assembly}"
+    res["needle_recall_layer0"] = recall
+    if not args.no_ceiling:
+        res["ceiling"] = pb.ceiling()
+    if p.name == "cfg4" and args.rounds == 1 and not args.no_host_tier:
+        res["host_tier"] = pb.host_tier(args.steps, args.warmup)
+    pb.release()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(p, pb.layers, args.cpu_sample_chunks)
+    if p.name == "cfg4" and args.rounds == 1 and not args.no_per_config:
+        res["per_config"] = {name: config_leg(torch, name, args) for name in ("cfg1", "cfg2", "cfg3", "cfg5")}
+    print(json.dumps(res), flush=True)
 
-    # ------------------------------------------------------------ document index
-    chunk_off = p.chunk_off
-    tok_off = p.tok_off
-    co_d = torch.from_numpy(chunk_off).to(dev)
-    cd = M.msa_chunk_doc_map(co_d, N)
 
-    # ------------------------------------------------------------ query-side inputs (per layer)
-    qr = [SD.fill(torch.empty((p.B, p.T, H, d), dtype=bf, device=dev), p.qseed, l, synth.T_QR) for l in range(layers)]
-    qq = [SD.fill(torch.empty((p.B, p.T, p.Hq, d), dtype=bf, device=dev), p.qseed, l, synth.T_Q) for l in range(layers)]
-    kl = [SD.fill(torch.empty((p.B, p.L_loc, H, d), dtype=bf, device=dev), p.qseed, l, synth.T_KLOC)
-          for l in range(layers)]
-    vl = [SD.fill(torch.empty((p.B, p.L_loc, H, d), dtype=bf, device=dev), p.qseed, l, synth.T_VLOC)
-          for l in range(layers)]
+class PresetBench:
+    """One workload preset on the device: its stores (built by the offline
+    stage before any timing), a LayerRunner and the whole-path step."""
 
-    # ------------------------------------------------------------ routing-key store (HBM)
-    # The offline stage (pooling) runs here, before the timed region.  The
-    # 100M-token preset is synthesised at pooled level (chunk = 1 pooling,
-    # which only normalises); the others pool raw per-token tensors.
-    t0 = time.time()
-    kr_layout = M.MSA_LAYOUT_TILED if p.bf16 else M.MSA_LAYOUT_ROWS
-    store = torch.empty((layers, M.padded_chunks(N, kr_layout), H, d), dtype=bf, device=dev)
-    if p.pooled_level:
-        rows_off, pool_chunk, n_rows, to_d = chunk_off, 1, N, co_d
-    else:
-        rows_off, pool_chunk, n_rows = tok_off, p.chunk, int(tok_off[-1])
-        to_d = torch.from_numpy(tok_off).to(dev)
-    raw = torch.empty((n_rows, H, d), dtype=bf, device=dev)
-    needles = synth.needle_docs(p.seed, D, p.n_needles)
-    encode_ms = []
-    for l in range(layers):
-        SD.fill(raw, p.seed, l, synth.T_KR)
-        for i, nd in enumerate(needles):
-            b = i if p.needle_per_query else 0
-            qh = qr[l][b].float().cpu().numpy()
-            lo, hi = int(rows_off[nd]), int(rows_off[nd + 1])
-            rows = synth.needle_rows(qh, p.seed, l, hi - lo, bf16=p.bf16, start=lo)
-            raw[lo:hi] = torch.from_numpy(rows).to(dev, bf)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        M.msa_pool_encode(raw, to_d, co_d, cd, pool_chunk, True, out=store[l], layout=kr_layout)
-        e1.record()
-        torch.cuda.synchronize()
-        encode_ms.append(e0.elapsed_time(e1))
-    torch.cuda.synchronize()
-    log(f"routing-key store ready in {time.time() - t0:.1f} s")
+    def __init__(self, torch, p, layers=None, rounds=1):
+        import synth
+        from synth import device as SD
+        import sparse_attention_long_msa_amd as M
+        self.torch, self.p, self.synth, self.SD, self.M = torch, p, synth, SD, M
+        self.layers = p.layers if layers is None else layers
+        self.rounds = rounds
+        self.dev = torch.device("cuda:0")
+        torch.cuda.set_device(self.dev)
+        self.bf = torch.bfloat16 if p.bf16 else torch.float32
+        self.esz = 2 if p.bf16 else 4
+        H, d, L = p.H, p.d, self.layers
+        self.co_d = torch.from_numpy(p.chunk_off).to(self.dev)
+        self.cd = M.msa_chunk_doc_map(self.co_d, p.n_chunks)
+        fill = lambda shape, tid, l, seed=p.qseed: SD.fill(torch.empty(shape, dtype=self.bf, device=self.dev),  # noqa
+                                                              seed, l, tid)
+        self.qr = [fill((p.B, p.T, H, d), synth.T_QR, l) for l in range(L)]
+        self.qq = [fill((p.B, p.T, p.Hq, d), synth.T_Q, l) for l in range(L)]
+        self.kl = [fill((p.B, p.L_loc, H, d), synth.T_KLOC, l) for l in range(L)]
+        self.vl = [fill((p.B, p.L_loc, H, d), synth.T_VLOC, l) for l in range(L)]
+        # routing queries of the later Memory Interleave rounds: seeded like round 0's, seed + round
+        self.qr_rounds = [[self.qr[l]] + [fill((p.B, p.T, H, d), synth.T_QR, l, p.qseed + r)
+                                          for r in range(1, rounds)] for l in range(L)]
+        self.kr_layout = M.MSA_LAYOUT_TILED if p.bf16 else M.MSA_LAYOUT_ROWS
+        if p.pooled_level:
+            self.rows_off, self.pool_chunk, self.n_rows, self.to_d = p.chunk_off, 1, p.n_chunks, self.co_d
+        else:
+            self.rows_off, self.pool_chunk, self.n_rows = p.tok_off, p.chunk, int(p.tok_off[-1])
+            self.to_d = torch.from_numpy(p.tok_off).to(self.dev)
+        self.needles = synth.needle_docs(p.seed, p.n_docs, p.n_needles)
+        self.kbar, self.vbar, self.store = [], [], None
+        self.encode_ms = []
 
-    # ------------------------------------------------------------ content K/V tier
-    t0 = time.time()
-    tier = args.kv_tier
-    if args.rounds > 1 and tier != "hbm":
-        log("Memory Interleave rounds read the content K/V in place: using the HBM tier")
-        tier = "hbm"
-    kbar, vbar = [], []
-    kv_scale = -3 if p.pooled_level else 0
+    def _raw(self):
+        if getattr(self, "raw", None) is None:
+            self.raw = self.torch.empty((self.n_rows, self.p.H, self.p.d), dtype=self.bf, device=self.dev)
+        return self.raw
 
-    def content(l, tid, out):
+    def build_stores(self):
+        """The offline stage: every layer's routing-key store (pooled, normalised,
+        in the MFMA-tiled layout), from seeded raw rows with planted needles."""
+        torch, p, M, synth = self.torch, self.p, self.M, self.synth
+        t0 = time.time()
+        log(f"{p.name}: {p.n_docs} docs, {p.n_chunks} chunks/layer, {self.layers} layers, routing-key store "
+            f"{p.n_chunks * p.H * p.d * self.esz * self.layers / 1e9:.1f} GB")
+        self.store = torch.empty((self.layers, M.padded_chunks(p.n_chunks, self.kr_layout), p.H, p.d), dtype=self.bf,
+                                 device=self.dev)
+        raw = self._raw()
+        for l in range(self.layers):
+            self.SD.fill(raw, p.seed, l, synth.T_KR)
+            for i, nd in enumerate(self.needles):
+                b = i if p.needle_per_query else 0
+                qh = self.qr[l][b].float().cpu().numpy()
+                lo, hi = int(self.rows_off[nd]), int(self.rows_off[nd + 1])
+                rows = synth.needle_rows(qh, p.seed, l, hi - lo, bf16=p.bf16, start=lo)
+                raw[lo:hi] = torch.from_numpy(rows).to(self.dev, self.bf)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            M.msa_pool_encode(raw, self.to_d, self.co_d, self.cd, self.pool_chunk, True, out=self.store[l],
+                              layout=self.kr_layout)
+            e1.record()
+            torch.cuda.synchronize()
+            self.encode_ms.append(e0.elapsed_time(e1))
+        log(f"routing-key store ready in {time.time() - t0:.1f} s")
+
+    def content(self, l, tid, out):
         """pooled K or V of layer l into out (device)"""
-        SD.fill(raw, p.seed, l, tid, scale_pow2=kv_scale)
-        return M.msa_pool_encode(raw, to_d, co_d, cd, pool_chunk, False, out=out)
+        raw = self._raw()
+        self.SD.fill(raw, self.p.seed, l, tid, scale_pow2=-3 if self.p.pooled_level else 0)
+        return self.M.msa_pool_encode(raw, self.to_d, self.co_d, self.cd, self.pool_chunk, False, out=out)
 
-    if tier == "host":
-        try:
-            tmp = torch.empty((N, H, d), dtype=bf, device=dev)
-            for l in range(layers):
-                for lst, tid in ((kbar, synth.T_K), (vbar, synth.T_V)):
-                    content(l, tid, tmp)
-                    h = torch.empty((N, H, d), dtype=bf, pin_memory=True)
-                    h.copy_(tmp)
-                    lst.append(h)
-                log(f"host tier layer {l} ready ({time.time() - t0:.1f} s)")
-            torch.cuda.synchronize()
-        except (RuntimeError, torch.OutOfMemoryError) as e:  # pinned host memory exhausted
-            log(f"pinned host tier unavailable ({str(e).splitlines()[0]}); falling back to the HBM tier")
-            kbar.clear()
-            vbar.clear()
-            torch.cuda.synchronize()
-            tier = "hbm"
-    if tier == "hbm":
-        for l in range(layers):
-            kbar.append(content(l, synth.T_K, torch.empty((N, H, d), dtype=bf, device=dev)))
-            vbar.append(content(l, synth.T_V, torch.empty((N, H, d), dtype=bf, device=dev)))
+    def build_content(self, tier):
+        torch, p = self.torch, self.p
+        t0 = time.time()
+        self.kbar, self.vbar = [], []
+        for l in range(self.layers):
+            for lst, tid in ((self.kbar, self.synth.T_K), (self.vbar, self.synth.T_V)):
+                lst.append(self.content(l, tid, torch.empty((p.n_chunks, p.H, p.d), dtype=self.bf, device=self.dev)))
         torch.cuda.synchronize()
-    del raw
-    log(f"content K/V tier '{tier}' ready in {time.time() - t0:.1f} s")
-    src_mode = M.MSA_SRC_DEVICE if tier == "hbm" else (
-        M.MSA_SRC_HOST_MAPPED if args.gather == "mapped" else M.MSA_SRC_HOST_MEMCPY)
+        self.raw = None
+        log(f"content K/V ({tier}) ready in {time.time() - t0:.1f} s")
 
-    runner = M.LayerRunner(batch=p.B, tokens=p.T, q_heads=p.Hq, kv_heads=H, head_dim=d, n_docs=D, n_chunks=N,
-                           k=p.k, max_doc_chunks=p.max_doc_chunks, local_len=p.L_loc, dtype=bf, device=dev,
-                           q_pos_offset=p.qpo if args.rounds == 1 else None, rope_base=p.rope_base,
-                           src_mode=src_mode, chunk_off_h=chunk_off, kr_layout=kr_layout,
-                           indexed=(tier == "hbm" and (args.hbm_assembly == "index" or args.rounds > 1)),
-                           rounds=args.rounds)
-    stream = torch.cuda.current_stream()
-    # routing queries of the later rounds: seeded like round 0's, seed + round
-    qr_rounds = [[qr[l]] + [SD.fill(torch.empty_like(qr[l]), p.qseed + r, l, synth.T_QR) for r in range(1, args.rounds)]
-                 for l in range(layers)]
+    def make_runner(self, tier, indexed, src_mode=None):
+        p, M = self.p, self.M
+        self.tier = tier
+        self.runner = M.LayerRunner(batch=p.B, tokens=p.T, q_heads=p.Hq, kv_heads=p.H, head_dim=p.d,
+                                    n_docs=p.n_docs, n_chunks=p.n_chunks, k=p.k, max_doc_chunks=p.max_doc_chunks,
+                                    local_len=p.L_loc, dtype=self.bf, device=self.dev,
+                                    q_pos_offset=p.qpo if self.rounds == 1 else None, rope_base=p.rope_base,
+                                    src_mode=M.MSA_SRC_DEVICE if src_mode is None else src_mode,
+                                    chunk_off_h=p.chunk_off, kr_layout=self.kr_layout, indexed=indexed,
+                                    rounds=self.rounds)
+        return self.runner
 
-    def step(ev=None, route_ev=None, route_layer=-1):
+    def step(self, ev=None, route_ev=None, route_layer=-1, kv=None, flush=None):
         """One pass of the whole path over all routed layers.  ev: per-stage
-        events of every layer (stage breakdown); route_ev: events around the
-        routing-score call of layer route_layer only (the timed steps)."""
-        for l in range(layers):
-            if args.rounds > 1:
-                if ev is not None:
-                    ev[l][0].record(stream)
-                runner.fetch_rounds(qr_rounds[l], store[l], cd, co_d, kbar[l], vbar[l],
+        events of every layer; route_ev: events around the routing-score call
+        of layer route_layer only (the timed steps); kv(l): the layer's
+        content stores (default: its own, in HBM); flush(): run before each
+        layer (cold-cache timing)."""
+        runner, stream = self.runner, self.torch.cuda.current_stream()
+
+        def rec(e):
+            if e is not None:
+                e.record(stream)
+        for l in range(self.layers):
+            kb, vb = (self.kbar[l], self.vbar[l]) if kv is None else kv(l)
+            if flush is not None:
+                flush()
+            e = ev[l] if ev is not None else [None] * 5
+            rec(e[0])
+            if self.rounds > 1:
+                runner.fetch_rounds(self.qr_rounds[l], self.store[l], self.cd, self.co_d, kb, vb,
                                     route_events=route_ev if l == route_layer else None)
-                if ev is not None:
-                    ev[l][3].record(stream)
-                runner.attend(qq[l], kl[l], vl[l])
-                if ev is not None:
-                    ev[l][4].record(stream)
+                rec(e[1])
+                rec(e[2])
+                rec(e[3])
+                runner.attend(self.qq[l], self.kl[l], self.vl[l])
+                rec(e[4])
                 continue
-            if ev is not None:
-                ev[l][0].record(stream)
             if l == route_layer:
-                route_ev[0].record(stream)
-            runner.route(qr[l], store[l], cd)
+                rec(route_ev[0])
+            runner.route(self.qr[l], self.store[l], self.cd)
             if l == route_layer:
-                route_ev[1].record(stream)
-            if ev is not None:
-                ev[l][1].record(stream)
+                rec(route_ev[1])
+            rec(e[1])
             if runner.indexed:
                 # top-k and the context index in one call (the final selection pass writes the index)
-                runner.select_assemble(co_d, kbar[l], vbar[l])
-                if ev is not None:
-                    ev[l][2].record(stream)
-                    ev[l][3].record(stream)
+                runner.select_assemble(self.co_d, kb, vb)
+                rec(e[2])
+                rec(e[3])
             else:
                 runner.select()
-                if ev is not None:
-                    ev[l][2].record(stream)
-                runner.assemble(co_d, kbar[l], vbar[l])
-                if ev is not None:
-                    ev[l][3].record(stream)
-            runner.attend(qq[l], kl[l], vl[l])
-            if ev is not None:
-                ev[l][4].record(stream)
+                rec(e[2])
+                runner.assemble(self.co_d, kb, vb)
+                rec(e[3])
+            runner.attend(self.qq[l], self.kl[l], self.vl[l])
+            rec(e[4])
 
-    # needle check on one pass (a property of the planted data, not timed)
-    step()
-    torch.cuda.synchronize()
-    ids_all = (runner.ids if args.rounds == 1 else runner.ids_rounds[0]).cpu().numpy()
-    recall = float(np.mean([int(nd) in set(ids_all[i if p.needle_per_query else 0].tolist())
-                            for i, nd in enumerate(needles)]))
+    def needle_recall(self):
+        """Planted-needle recall of layer 0 on one pass (a property of the data, not timed)."""
+        p = self.p
+        self.step()
+        self.torch.cuda.synchronize()
+        ids_all = (self.runner.ids if self.rounds == 1 else self.runner.ids_rounds[0]).cpu().numpy()
+        return float(np.mean([int(nd) in set(ids_all[i if p.needle_per_query else 0].tolist())
+                              for i, nd in enumerate(self.needles)]))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # timed steps: one pair of events per step, around one layer's routing-score
-    # call (a different layer each step), so that the step is not slowed by
-    # instrumentation; the whole-step time is the wall clock
-    route_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(args.steps):
-        step(route_ev=route_evs[s], route_layer=s % layers)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    route_ms = [e[0].elapsed_time(e[1]) for e in route_evs]
-    # stage breakdown: extra, untimed steps with events between all stages
-    n_stage = min(args.steps, 3)
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(layers)]
-           for _ in range(n_stage)]
-    for s in range(n_stage):
-        step(evs[s])
-    torch.cuda.synchronize()
-    stage = np.zeros(4)
-    for s in range(n_stage):
-        for l in range(layers):
-            e = evs[s][l]
-            if args.rounds > 1:   # rounds (route, skip, select, append) | attention
-                stage += [e[0].elapsed_time(e[3]), 0.0, 0.0, e[3].elapsed_time(e[4])]
+    def timed(self, steps, warmup, kv=None, route_events=True, graph=False):
+        """Wall-clock ms per step over `steps` timed steps after `warmup`, and
+        the event-timed routing-score launches (one per step).  With graph,
+        the step is captured once into a HIP graph (StepGraph) and the timed
+        steps are replays; the launch durations then come from as many eager
+        steps after the timed region."""
+        torch = self.torch
+        if graph:
+            g = self.M.StepGraph(lambda: self.step(kv=kv), warmup=1)
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            for _ in range(steps):
+                g.replay()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t_start
+            del g
+            route_ms = self.route_launches(steps, kv) if route_events else []
+            return wall * 1e3 / steps, route_ms
+        for _ in range(warmup):
+            self.step(kv=kv)
+        torch.cuda.synchronize()
+        route_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for s in range(steps):
+            if route_events:
+                self.step(route_ev=route_evs[s], route_layer=s % self.layers, kv=kv)
             else:
+                self.step(kv=kv)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        route_ms = [e[0].elapsed_time(e[1]) for e in route_evs] if route_events else []
+        return wall * 1e3 / steps, route_ms
+
+    def route_launches(self, n, kv=None):
+        """Event-timed routing-score calls: n eager steps, one layer's call each."""
+        torch = self.torch
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for s in range(n):
+            self.step(route_ev=evs[s], route_layer=s % self.layers, kv=kv)
+        torch.cuda.synchronize()
+        return [e[0].elapsed_time(e[1]) for e in evs]
+
+    def stages(self, n_steps, kv=None, flush=None):
+        """Per-stage ms per step: (route, top-k, assembly, attention), from
+        extra steps with events between all stages."""
+        torch = self.torch
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(self.layers)]
+               for _ in range(n_steps)]
+        for s in range(n_steps):
+            self.step(evs[s], kv=kv, flush=flush)
+        torch.cuda.synchronize()
+        stage = np.zeros(4)
+        for s in range(n_steps):
+            for l in range(self.layers):
+                e = evs[s][l]
                 stage += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
-    stage /= n_stage
-    ms_per_step = wall * 1e3 / args.steps
-    store_bytes = N * H * d * esz                      # per layer
-    step_bytes = store_bytes * layers * args.rounds   # every round scans the layer's store
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9   # GB/s over the whole step
-    routing_gbps = step_bytes / ((stage[0] + stage[1]) * 1e-3) / 1e9
-    # algorithmic bytes of one msa_route_score launch: the store, the chunk->doc map,
-    # the routing query and the score row (initial fill + result)
-    alg_bytes = store_bytes + N * 4 + p.B * p.T * H * d * esz + 2 * p.B * D * 4
-    route_avg_ms = float(np.mean(route_ms))
-    achieved = alg_bytes / (route_avg_ms * 1e-3) / 1e9
-    # attention: K/V of the context and the local part, read once per KV head, plus Q and O
-    ctx_len = runner.ctx_len.cpu().numpy().astype(np.int64)
-    attn_bytes = int((ctx_len + p.L_loc).sum()) * H * d * 2 * esz + p.B * p.T * p.Hq * d * (esz + 4)
-    attn_gbps = attn_bytes * layers / (stage[3] * 1e-3) / 1e9
-    raw_bytes = n_rows * H * d * esz
-    encode_gbps = (raw_bytes + store_bytes) / (float(np.median(encode_ms)) * 1e-3) / 1e9
+        return stage / n_steps
 
-    workload = (f"{p.name}: {int(p.lengths.sum())}-token memory, {D} docs, chunk {p.chunk}, {N} chunks/layer, "
-                f"{layers} routed layers, H={H}, d={d}; {p.B} quer{'y' if p.B == 1 else 'ies'} x T={p.T}, "
-                f"Hq={p.Hq}, L_loc={p.L_loc}, k={p.k}")
-    res = {
-        "metric": "routing-key (K_r) scan GB/s over the whole route+attn step",
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if p.bf16 else "f32",
-        "data": "synthetic (seeded counter-based generator; planted needles)",
-        "config": {"workload": workload,
-                   "global_batch": p.B, "seq_len": p.T, "parallelism": "single GPU",
-                   "kv_tier": tier, "gather": args.gather if tier == "host" else
-                   f"hbm-{args.hbm_assembly if args.rounds == 1 else 'index'}", "rounds": args.rounds},
-        "route_attn_us_per_query": round(ms_per_step * 1e3 / p.B, 1),
-        "routing_GBps": round(routing_gbps, 1),
-        "routing_frac_of_8TBps": round(routing_gbps / 8000, 4),
-        "stage_ms_per_step": (({"route_score": round(stage[0], 4), "topk_and_context_index": round(stage[1], 4),
-                                "attention": round(stage[3], 4)} if runner.indexed else
-                               {"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
-                                "gather": round(stage[2], 4), "attention": round(stage[3], 4)}) if args.rounds == 1 else
-                              {"rounds_route_topk_append": round(stage[0], 4), "attention": round(stage[3], 4)}),
-        "attention_GBps": round(attn_gbps, 1),
-        "attention_frac_of_8TBps": round(attn_gbps / 8000, 4),
-        "attention_bytes_per_layer": attn_bytes,
-        "encode_GBps": round(encode_gbps, 1),
+    def attn_bytes(self):
+        p = self.p
+        ctx_len = self.runner.ctx_len.cpu().numpy().astype(np.int64)
+        return int((ctx_len + p.L_loc).sum()) * p.H * p.d * 2 * self.esz + p.B * p.T * p.Hq * p.d * (self.esz + 4)
+
+    def headline(self, steps, warmup):
+        """The JSON line: whole-step throughput of the routing-key scan, the
+        stage breakdown and the roofline of the routing-score launch."""
+        p, layers = self.p, self.layers
+        ms_eager, _ = self.timed(steps, warmup, route_events=False)
+        ms_per_step, route_ms = self.timed(steps, warmup, graph=True)
+        stage = self.stages(min(steps, 3))
+        H, d, N, D = p.H, p.d, p.n_chunks, p.n_docs
+        store_bytes = N * H * d * self.esz                     # per layer
+        step_bytes = store_bytes * layers * self.rounds        # every round scans the layer's store
+        value = step_bytes / (ms_per_step * 1e-3) / 1e9
+        routing_gbps = step_bytes / ((stage[0] + stage[1]) * 1e-3) / 1e9
+        # algorithmic bytes of one msa_route_score launch: the store, the chunk->doc map,
+        # the routing query and the score row (initial fill + result)
+        alg_bytes = store_bytes + N * 4 + p.B * p.T * H * d * self.esz + 2 * p.B * D * 4
+        route_avg_ms = float(np.mean(route_ms))
+        achieved = alg_bytes / (route_avg_ms * 1e-3) / 1e9
+        attn_bytes = self.attn_bytes()
+        attn_gbps = attn_bytes * layers / (stage[3] * 1e-3) / 1e9
+        encode_gbps = (self.n_rows * H * d * self.esz + store_bytes) / (float(np.median(self.encode_ms)) * 1e-3) / 1e9
+        workload = (f"{p.name}: {int(p.lengths.sum())}-token memory, {D} docs, chunk {p.chunk}, {N} chunks/layer, "
+                    f"{layers} routed layers, H={H}, d={d}; {p.B} quer{'y' if p.B == 1 else 'ies'} x T={p.T}, "
+                    f"Hq={p.Hq}, L_loc={p.L_loc}, k={p.k}")
+        if self.rounds == 1:
+            stages = ({"route_score": round(stage[0], 4), "topk_and_context_index": round(stage[1], 4),
+                       "attention": round(stage[3], 4)} if self.runner.indexed else
+                      {"route_score": round(stage[0], 4), "topk": round(stage[1], 4), "gather": round(stage[2], 4),
+                       "attention": round(stage[3], 4)})
+        else:
+            stages = {"rounds_route_topk_append": round(stage[0] + stage[1] + stage[2], 4),
+                      "attention": round(stage[3], 4)}
+        self.route_avg_ms = route_avg_ms
+        return {
+            "metric": "routing-key (K_r) scan GB/s over the whole route+attn step",
+            "value": round(value, 1),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": steps,
+            "warmup": warmup,
+            "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16" if p.bf16 else "f32",
+            "data": "synthetic (seeded counter-based generator; planted needles)",
+            "config": {"workload": workload, "global_batch": p.B, "seq_len": p.T, "parallelism": "single GPU",
+                       "kv_tier": "hbm", "rounds": self.rounds, "step_launch": "hip-graph replay"},
+            "route_attn_us_per_query": round(ms_per_step * 1e3 / p.B, 1),
+            "ms_per_step_eager_launches": round(ms_eager, 4),
+            "routing_GBps": round(routing_gbps, 1),
+            "routing_frac_of_8TBps": round(routing_gbps / 8000, 4),
+            "stage_ms_per_step": stages,
+            "attention_GBps": round(attn_gbps, 1),
+            "attention_frac_of_8TBps": round(attn_gbps / 8000, 4),
+            "attention_bytes_per_layer": attn_bytes,
+            "encode_GBps": round(encode_gbps, 1),
+            "roofline": {"kernel": "msa_route_score (route_score_mfma_kernel + score fill)", "bound": "hbm",
+                         "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(achieved / 8000.0, 4), "traffic": counted_traffic(p.name),
+                         "avg_launch_ms": round(route_avg_ms, 4), "alg_bytes_per_launch": int(alg_bytes)},
+        }
+
+    def ceiling(self):
+        """The achievable streaming-read rate over the same bytes as one
+        routing launch: msa_stream_read over each layer's routing-key store
+        (each read cold: the previous layer's read evicted it), event-timed."""
+        torch, p = self.torch, self.p
+        sink = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        nbytes = p.n_chunks * p.H * p.d * self.esz
+        ms = []
+        for rep in range(2):
+            for l in range(self.layers):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                flat = self.store[l].view(-1)[: nbytes // self.esz]
+                e0.record()
+                self.M.msa_stream_read(flat, sink)
+                e1.record()
+                torch.cuda.synchronize()
+                if rep:
+                    ms.append(e0.elapsed_time(e1))
+        t = float(np.mean(ms))
+        gbps = nbytes / (t * 1e-3) / 1e9
+        route_gbps = nbytes / (self.route_avg_ms * 1e-3) / 1e9
+        return {"kernel": "msa_stream_read (1 KB-contiguous 16-byte non-temporal loads, no arithmetic)",
+                "bytes_per_read": nbytes, "avg_read_ms": round(t, 4), "ceiling_GBps": round(gbps, 1),
+                "ceiling_frac_of_8TBps": round(gbps / 8000, 4),
+                "route_store_GBps_over_ceiling": round(route_gbps / gbps, 4)}
+
+    def host_tier(self, steps, warmup):
+        """The pages' tier: content K/V in pinned host memory, the selected
+        documents fetched over the host link per layer.  The box pins only
+        part of the 115 GB, so as many layers as fit are pinned and the 18
+        layers cycle over them (the fetch cost does not depend on the values).
+        Timed for the zero-copy gather kernel (mapped) and for hipMemcpyAsync
+        per document on a side stream (memcpy)."""
+        torch, p, M = self.torch, self.p, self.M
+        t0 = time.time()
+        hk, hv = [], []
+        try:
+            for l in range(self.layers):
+                a = torch.empty((p.n_chunks, p.H, p.d), dtype=self.bf, pin_memory=True)
+                b = torch.empty((p.n_chunks, p.H, p.d), dtype=self.bf, pin_memory=True)
+                a.copy_(self.kbar[l])
+                b.copy_(self.vbar[l])
+                hk.append(a)
+                hv.append(b)
+        except (RuntimeError, torch.OutOfMemoryError) as e:   # pinned host memory exhausted
+            log(f"host tier: pinned {len(hk)} layers ({str(e).splitlines()[0]})")
+        torch.cuda.synchronize()
+        n_pin = len(hk)
+        if n_pin == 0:
+            return {"error": "no pinned host memory available"}
+        pinned_gb = 2 * n_pin * p.n_chunks * p.H * p.d * self.esz / 1e9
+        log(f"host tier: {n_pin} layers pinned ({pinned_gb:.1f} GB) in {time.time() - t0:.1f} s")
+        out = {"pinned_layers": n_pin, "pinned_GB": round(pinned_gb, 1), "layers_cycled": self.layers,
+               "note": f"layer l reads pinned layer l % {n_pin}"}
+        hbm_runner = self.runner
+        kv = lambda l: (hk[l % n_pin], hv[l % n_pin])   # noqa: E731
+        for mode, src in (("mapped", M.MSA_SRC_HOST_MAPPED), ("memcpy", M.MSA_SRC_HOST_MEMCPY)):
+            self.make_runner("host", indexed=False, src_mode=src)
+            ms, route_ms = self.timed(steps, warmup, kv=kv)
+            stage = self.stages(min(steps, 3), kv=kv)
+            out[mode] = {"route_attn_us_per_query": round(ms * 1e3 / p.B, 1), "ms_per_step": round(ms, 4),
+                         "fetch_ms_per_step": round(stage[2], 4),
+                         "stage_ms_per_step": {"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
+                                               "fetch": round(stage[2], 4), "attention": round(stage[3], 4)},
+                         "fetched_bytes_per_step": int(self.runner.ctx_len.sum().item()) * p.H * p.d * 2 * self.esz
+                         * self.layers}
+            log(f"host tier {mode}: {ms:.3f} ms per step, fetch {stage[2]:.3f} ms")
+        self.runner = hbm_runner
+        del hk, hv
+        if hasattr(torch._C, "_host_emptyCache"):
+            torch._C._host_emptyCache()    # hand the pinned pages back
+        return out
+
+    def cold(self, flush_buf):
+        """Per-stage ms per step with the caches flushed before every layer (a
+        1 GB buffer written), and the whole step as the sum of its stages."""
+        stage = self.stages(2, flush=lambda: flush_buf.fill_(1))
+        return stage
+
+    def release(self):
+        self.store = None
+        self.kbar, self.vbar = [], []
+        self.runner = None
+        self.raw = None
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def config_leg(torch, name, args):
+    """Per-config line for the smaller presets: warm and cold step times,
+    routing and attention GB/s, and the oracle's routing and attention time
+    on the machine's host cores (bounded samples)."""
+    from synth import configs
+    p = configs.PRESETS[name]()
+    pb = PresetBench(torch, p)
+    pb.build_stores()
+    pb.build_content("hbm")
+    pb.make_runner("hbm", indexed=True)
+    recall = pb.needle_recall()
+    steps, warmup = max(3, min(args.steps, 10)), max(1, min(args.warmup, 3))
+    ms_eager, _ = pb.timed(steps, warmup, route_events=False)
+    ms, _ = pb.timed(steps, warmup, route_events=False, graph=True)
+    warm = pb.stages(2)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=pb.dev)
+    cold = pb.cold(flush_buf)
+    del flush_buf
+    store_bytes = p.n_chunks * p.H * p.d * pb.esz * pb.layers
+    attn_bytes = pb.attn_bytes() * pb.layers
+
+    def gbps(b, ms_):
+        return round(b / (ms_ * 1e-3) / 1e9, 1)
+    out = {
+        "workload": f"{p.n_docs} docs, {int(p.lengths.sum())} tokens, {p.n_chunks} chunks/layer, {pb.layers} layers; "
+                    f"B={p.B} x T={p.T}, L_loc={p.L_loc}, k={p.k}, {'bf16' if p.bf16 else 'f32'}",
+        "ms_per_step": round(ms, 4), "us_per_query": round(ms * 1e3 / p.B, 1),
+        "ms_per_step_eager_launches": round(ms_eager, 4),
+        "routing_GBps": gbps(store_bytes, warm[0] + warm[1]),
+        "attention_GBps": gbps(attn_bytes, warm[3]),
+        "stage_ms_per_step": {"route_score": round(warm[0], 4), "topk_and_context_index": round(warm[1], 4),
+                              "attention": round(warm[3], 4)},
+        "cold": {"flush": "1 GB buffer written before every layer",
+                 "ms_per_step_sum_of_stages": round(float(cold.sum()), 4),
+                 "routing_GBps": gbps(store_bytes, cold[0] + cold[1]), "attention_GBps": gbps(attn_bytes, cold[3]),
+                 "stage_ms_per_step": {"route_score": round(cold[0], 4), "topk_and_context_index": round(cold[1], 4),
+                                       "attention": round(cold[3], 4)}},
         "needle_recall_layer0": recall,
-        "roofline": {"kernel": "msa_route_score (route_score_mfma_kernel + score fill)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-                     "frac": round(achieved / 8000.0, 4), "traffic": counted_traffic(p.name),
-                     "avg_launch_ms": round(route_avg_ms, 4), "alg_bytes_per_launch": int(alg_bytes)},
     }
-
+    ctx_len0 = int(pb.runner.ctx_len[0].item())
+    pb.release()
+    del pb
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(p, layers, args.cpu_sample_chunks)
-    print(json.dumps(res), flush=True)
+        out["oracle"] = oracle_leg(p, ctx_len0)
+    log(f"{name}: {ms:.3f} ms per step (warm), {float(cold.sum()):.3f} ms (cold)")
+    return out
+
+
+def oracle_leg(p, ctx_len0):
+    """The float64 oracle timed on the host cores: routing (score + top-k) of
+    two routed layers' queries against a bounded sample of the memory,
+    scaled to the whole memory, and the attention of query 0 over a context
+    of the GPU's length plus the local tokens."""
+    import oracle as O
+    import synth
+    cores = _oracle_threads()
+    base = cpu_baseline(p, 2, n_sample_chunks=min(p.n_chunks, 1 << 16), quiet=True)
+    route_ms = base["seconds"] * 1e3 / 2 * (p.n_chunks / base["sample_chunks"])
+    bf = p.bf16
+    H, d = p.H, p.d
+    kc = synth.tensor(p.seed, 0, synth.T_K, (max(ctx_len0, 1), H, d), bf16=bf, scale_pow2=-3)
+    vc = synth.tensor(p.seed, 0, synth.T_V, (max(ctx_len0, 1), H, d), bf16=bf, scale_pow2=-3)
+    pos = np.arange(max(ctx_len0, 1)) % max(p.max_doc_chunks, 1)
+    q = synth.tensor(p.qseed, 0, synth.T_Q, (1, p.T, p.Hq, d), bf16=bf)[0]
+    kl = synth.tensor(p.qseed, 0, synth.T_KLOC, (p.L_loc, H, d), bf16=bf)
+    vl = synth.tensor(p.qseed, 0, synth.T_VLOC, (p.L_loc, H, d), bf16=bf)
+    t0 = time.perf_counter()
+    O.attend_one(q, kc[:ctx_len0], vc[:ctx_len0], pos[:ctx_len0], kl, vl, p.qpo, p.rope_base, 1.0 / math.sqrt(d))
+    attn_ms = (time.perf_counter() - t0) * 1e3
+    return {"kind": "oracle", "cores": cores,
+            "route_ms_per_query_layer": round(route_ms / p.B, 4),
+            "attention_ms_per_query_layer": round(attn_ms, 4),
+            "route_sample": f"{base['sample_chunks']} of {p.n_chunks} chunks, 2 layers' queries, scaled to the whole "
+                            f"memory",
+            "attention_sample": f"query 0: {ctx_len0} context entries + {p.L_loc} local tokens, {p.T} tokens x "
+                                f"{p.Hq} heads"}
+
+
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
 
 
 def counted_traffic(preset_name):
@@ -596,7 +831,7 @@ def copy_calibration(torch):
     print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
-def cpu_baseline(p, layers, n_sample_chunks=None):
+def cpu_baseline(p, layers, n_sample_chunks=None, quiet=False):
     """The float64 oracle's routing (score + top-k) timed on a bounded sample
     of the same workload: every routed layer's query scored against the
     routing keys of layer 0's first documents.  The sample's keys come from
@@ -607,11 +842,7 @@ def cpu_baseline(p, layers, n_sample_chunks=None):
     import oracle as O
     import synth
     from synth import device as SD
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = _oracle_threads()
     if n_sample_chunks is None:
         n_sample_chunks = 1 << 20 if p.pooled_level else 1 << 18
     n_docs = int(np.searchsorted(p.chunk_off, n_sample_chunks, side="right") - 1)
@@ -660,9 +891,10 @@ def cpu_baseline(p, layers, n_sample_chunks=None):
         O.topk(s, p.k)
     dt = time.perf_counter() - t0
     gb = layers * n * p.H * p.d * (2 if p.bf16 else 4) / 1e9
-    log(f"cpu baseline: sample prepared in {t_prep:.1f} s, oracle routing {dt:.1f} s")
+    if not quiet:
+        log(f"cpu baseline ({p.name}): sample prepared in {t_prep:.1f} s, oracle routing {dt:.1f} s")
     return {"value": round(gb / dt, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 2),
+            "seconds": round(dt, 2), "sample_chunks": n,
             "sample": f"layer 0, first {n_docs} documents ({n} pooled chunks, "
                       f"{n * p.H * p.d * (2 if p.bf16 else 4) / 1e9:.2f} GB of routing keys) scored against each of the "
                       f"{layers} routed layers' {p.B} x {p.T}-token queries: routing score + top-k, float64"}

@@ -434,6 +434,18 @@ int msa_sparse_attn_indexed_noalloc(int dtype, const void* q, int B, int T, int 
 int msa_rope_table_rows(int max_ctx, int L_loc, int q_pos_offset);
 int msa_rope_table(int rows, int d, float rope_base, float* table, void* stream);
 
+/*
+ * msa_stream_read - measurement reference, not a step of the path: reads
+ * `bytes` of device memory at `buf` once, with the access pattern of the
+ * routing-key scan (each wave load instruction 1 KB contiguous, 16-byte
+ * non-temporal loads), computing nothing but an XOR of the data.  Its rate
+ * is the achievable streaming-read ceiling that the HBM-bound kernels are
+ * compared with next to the nominal 8 TB/s.  `sink` (one uint32, device) is
+ * written only if the XOR equals 0x9E3779B9.  bytes: a positive multiple of
+ * 16; buf 16-byte aligned.
+ */
+int msa_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 /* ------------------------------------------------------------------------
  * Training-time path (paper note 核心方法 > 训练: continued pre-training with
  * a generation loss and an auxiliary supervised contrastive routing loss;

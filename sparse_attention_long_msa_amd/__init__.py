@@ -47,6 +47,7 @@ from ._binding import (  # noqa: F401
     msa_topk_context_index,
     msa_tile_routing_keys,
     msa_topk_workspace,
+    msa_stream_read,
     padded_chunks,
 )
-from .pipeline import LayerRunner  # noqa: F401
+from .pipeline import LayerRunner, StepGraph  # noqa: F401

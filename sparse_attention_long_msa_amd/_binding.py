@@ -52,6 +52,7 @@ _SIGS = {
     "msa_sparse_attn_indexed_noalloc": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _L, _P, _P, _P, _I, _P, _P, _I,
                                              _I, _F, _P, _I, _F, _P, _P]),
     "msa_rope_table_rows": (_I, [_I, _I, _I]),
+    "msa_stream_read": (_I, [_P, _L, _P, _P]),
     "msa_rope_table": (_I, [_I, _I, _F, _P, _P]),
     "msa_route_argmax_workspace": (_S, [_I, _I, _I, _I, _I, _L, _L]),
     "msa_route_argmax": (_I, [_I, _P, _I, _I, _I, _I, _P, _P, _L, _L, _P, _P, _P, _P, _S, _P]),
@@ -527,6 +528,14 @@ def msa_sparse_attn_indexed_noalloc(q, k_bar, v_bar, ctx_row, ctx_pos, ctx_len, 
         _ptr(ctx_len), max_ctx, _ptr(k_loc), _ptr(v_loc), L_loc, q_pos_offset, float(rope_base), _ptr(rope_table),
         0 if rope_table is None else rope_table.shape[0], float(sm_scale), _ptr(out), _stream(stream)))
     return out
+
+
+def msa_stream_read(buf, sink, stream=None):
+    """Streaming-read reference: reads every byte of ``buf`` once."""
+    _dev(buf, "buf")
+    _dev(sink, "sink", (torch.int32, torch.uint32) if hasattr(torch, "uint32") else torch.int32, (1,))
+    _check("msa_stream_read", lib.msa_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                  _stream(stream)))
 
 
 # ---------------------------------------------------------------- training-time path

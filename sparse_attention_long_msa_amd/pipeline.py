@@ -158,3 +158,33 @@ class LayerRunner:
         self.route(q_r, kr_hat, chunk_doc, stream)
         self.select_assemble(chunk_off, k_bar, v_bar, stream)
         return self.attend(q, k_loc, v_loc, stream)
+
+
+class StepGraph:
+    """A sequence of library calls (typically every routed layer of one step)
+    captured once into a HIP graph and replayed.  Replay submits the whole
+    sequence at once, so the host no longer issues (and validates) each call:
+    for the smaller memories, where a layer's kernels take tens of
+    microseconds, host-side launch cost would otherwise set the step time.
+
+    ``fn`` must only enqueue work on the current stream with fixed buffers
+    (LayerRunner with preallocated outputs and workspaces does); calls that
+    synchronise with the host (msa_gather_kv in MSA_SRC_HOST_MEMCPY mode)
+    cannot be captured.  The library's kernels clear their own buffers with
+    fill kernels, never with memset nodes."""
+
+    def __init__(self, fn, warmup=1):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            fn()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graph.replay()

@@ -1,0 +1,75 @@
+"""The routed layers of one step captured into a HIP graph (StepGraph) and
+replayed: every replay gives the eager path's outputs bit for bit (scores,
+ids, context and attention), with eager work on the same buffers between
+replays; and the eager outputs match the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.helpers import ATOL_ATTN, RTOL_SCORE, check_ids, check_scores, dev, gen, host, ragged_lengths, tile_np, \
+    to_dev, to_dev_i64
+
+pytestmark = pytest.mark.gpu
+
+import sparse_attention_long_msa_amd as M  # noqa: E402  (a missing library fails loudly)
+
+
+@pytest.mark.parametrize("B,T,L_loc,k", [(1, 64, 512, 8), (8, 1, 1024, 4)])
+def test_step_graph_replays_equal_the_eager_step(B, T, L_loc, k):
+    H, d, Hq, layers = 8, 128, 32, 3
+    lens = ragged_lengths(90 + B, 700, 0, 900, n_empty=9)
+    tok_off = synth.offsets(lens)
+    chunk_off = O.chunk_offsets(tok_off, 64)
+    n_chunks, D = int(chunk_off[-1]), len(lens)
+    mdc = int(np.diff(chunk_off).max())
+    co_d = to_dev_i64(chunk_off)
+    cd = M.msa_chunk_doc_map(co_d, n_chunks)
+    L = []
+    for l in range(layers):
+        store = O.round_to_bf16(O.l2_normalize(gen(71, l, synth.T_KR, (n_chunks, H, d), True).astype(np.float64)))
+        x = dict(store=store,
+                 kb=gen(71, l, synth.T_K, (n_chunks, H, d), True, scale_pow2=-3),
+                 vb=gen(71, l, synth.T_V, (n_chunks, H, d), True, scale_pow2=-3),
+                 qr=gen(72, l, synth.T_QR, (B, T, H, d), True), q=gen(72, l, synth.T_Q, (B, T, Hq, d), True),
+                 kl=gen(72, l, synth.T_KLOC, (B, L_loc, H, d), True),
+                 vl=gen(72, l, synth.T_VLOC, (B, L_loc, H, d), True))
+        x["dev"] = [to_dev(tile_np(store), True)] + [to_dev(x[n], True) for n in ("kb", "vb", "qr", "q", "kl", "vl")]
+        x["run"] = M.LayerRunner(batch=B, tokens=T, q_heads=Hq, kv_heads=H, head_dim=d, n_docs=D, n_chunks=n_chunks,
+                                 k=k, max_doc_chunks=mdc, local_len=L_loc, dtype=torch.bfloat16, device=dev(),
+                                 kr_layout=M.MSA_LAYOUT_TILED, indexed=True)
+        L.append(x)
+
+    def step():
+        for x in L:
+            kr, kb, vb, qr, q, kl, vl = x["dev"]
+            x["run"].run(qr, kr, cd, co_d, kb, vb, q, kl, vl)
+
+    names = ("doc_score", "ids", "vals", "ctx_row", "ctx_pos", "ctx_len", "out")
+    step()
+    torch.cuda.synchronize()
+    eager = [{n: getattr(x["run"], n).clone() for n in names} for x in L]
+    g = M.StepGraph(step)
+    for rep in range(3):
+        for x in L:                                   # eager work on the same buffers between replays
+            for n in names:
+                getattr(x["run"], n).fill_(-3 if getattr(x["run"], n).dtype == torch.int32 else float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l, x in enumerate(L):
+            r = x["run"]
+            for n in ("doc_score", "ids", "vals", "ctx_len", "out"):
+                assert torch.equal(getattr(r, n), eager[l][n]), f"replay {rep}, layer {l}: {n}"
+            for b in range(B):                        # the context entries (rows past ctx_len are not written)
+                n_b = int(eager[l]["ctx_len"][b])
+                for n in ("ctx_row", "ctx_pos"):
+                    assert torch.equal(getattr(r, n)[b, :n_b], eager[l][n][b, :n_b]), f"replay {rep}, layer {l}: {n}"
+    # the eager outputs against the oracle
+    for l, x in enumerate(L):
+        ref = O.layer(x["qr"], x["store"], chunk_off, x["kb"], x["vb"], k, x["q"], x["kl"], x["vl"],
+                      ids_override=eager[l]["ids"].cpu().numpy())
+        check_scores(host(eager[l]["doc_score"]), ref["doc_score"], RTOL_SCORE["bf16"], k)
+        check_ids(eager[l]["ids"].cpu().numpy(), ref["doc_score"], k)
+        assert np.abs(host(eager[l]["out"]) - ref["out"]).max() <= ATOL_ATTN["bf16"]
