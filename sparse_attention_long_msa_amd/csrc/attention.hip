@@ -72,7 +72,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void attn_decode_kernel(
     const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
     const int32_t* __restrict__ ctx_row_in, int64_t ctx_rows, const float2* __restrict__ tab, int P, float scale_log2,
-    float* __restrict__ ws_o, float2* __restrict__ ws_ml, int n_splits, int n_hg) {
+    uint16_t* __restrict__ ws_o, float4* __restrict__ ws_ml, int n_splits, int n_hg) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int32_t* __restrict__ ctx_row = IDX ? ctx_row_in : nullptr;
   const int nw = blockDim.x / 64;
@@ -327,13 +327,8 @@ __global__ __launch_bounds__(DC_THREADS, 2) void attn_decode_kernel(
   // ---- partial result of this split: O^T[d = 16dt + 4*g4 + i][row lc]
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (!row_ok) return;
   const int64_t rowid = ((int64_t(split) * B + b) * T + t) * Hq + hq;
-  float* op = ws_o + rowid * AT_D;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-    *reinterpret_cast<float4*>(op + 16 * dt + 4 * g4) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-  if (g4 == 0) ws_ml[rowid] = make_float2(m_run, l_run);
+  store_partial(o, m_run, l_run, row_ok, g4, ws_o + rowid * AT_D, ws_ml + rowid);
 }
 
 // ---------------------------------------------------------------- prefill (many query rows)
@@ -365,7 +360,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
     const int32_t* __restrict__ ctx_row_in, int64_t ctx_rows, const float2* __restrict__ tab, int P, float scale_log2,
-    float* __restrict__ ws_o, float2* __restrict__ ws_ml, int n_splits, int n_rt, int n_rg, float* __restrict__ out,
+    uint16_t* __restrict__ ws_o, float4* __restrict__ ws_ml, int n_splits, int n_rt, int n_rg, float* __restrict__ out,
     float* __restrict__ lse) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int32_t* __restrict__ ctx_row = IDX ? ctx_row_in : nullptr;
@@ -598,8 +593,13 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     float l = l_run[i];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
+    if (n_splits > 1) {
+      const int64_t rowid = ((int64_t(split) * B + b) * T + trow[i]) * Hq + hqrow[i];
+      store_partial(o[i], m_run[i], l, rok[i], g4, ws_o + rowid * AT_D, ws_ml + rowid);
+      continue;
+    }
     if (!rok[i]) continue;
-    if (n_splits == 1) {
+    {
       // one split: the combine's result directly, with its arithmetic
       // (out = O / l, lse = m + log2 l; a row that saw no visible key gets 0, -inf)
       const int64_t row = (int64_t(b) * T + trow[i]) * Hq + hqrow[i];
@@ -610,20 +610,14 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
         *reinterpret_cast<float4*>(op + 16 * dt + 4 * g4) =
             make_float4(o[i][dt][0] * r, o[i][dt][1] * r, o[i][dt][2] * r, o[i][dt][3] * r);
       if (lse && g4 == 0) lse[row] = l > 0.f ? m_run[i] + __log2f(l) : -INFINITY;
-      continue;
     }
-    const int64_t rowid = ((int64_t(split) * B + b) * T + trow[i]) * Hq + hqrow[i];
-    float* op = ws_o + rowid * AT_D;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(op + 16 * dt + 4 * g4) = make_float4(o[i][dt][0], o[i][dt][1], o[i][dt][2], o[i][dt][3]);
-    if (g4 == 0) ws_ml[rowid] = make_float2(m_run[i], l);
   }
 }
 
 // out[b,t,hq,:] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, one pass with
-// a running maximum; eight splits' loads are issued together.
-__global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, int n_splits,
+// a running maximum; eight splits' loads are issued together.  O_s arrives
+// as float16 scaled by 2^-c_s (store_partial), so its weight is 2^(m_s + c_s - m).
+__global__ void attn_combine_kernel(const uint16_t* __restrict__ ws_o, const float4* __restrict__ ws_ml, int n_splits,
                                     int64_t rows, int d, float* __restrict__ out, float* __restrict__ lse) {
   // one thread per (row, 4 dims); d is a multiple of 4 on this path
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -635,13 +629,13 @@ __global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float2
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   constexpr int U = 8;
   for (int s0 = 0; s0 < n_splits; s0 += U) {
-    float2 ml[U];
-    float4 v[U];
+    float4 ml[U];
+    uint2 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int sp = min(s0 + u, n_splits - 1);
       ml[u] = ws_ml[sp * rows + row];
-      v[u] = *reinterpret_cast<const float4*>(ws_o + (sp * rows + row) * d + e);
+      v[u] = *reinterpret_cast<const uint2*>(ws_o + (sp * rows + row) * d + e);
       if (s0 + u >= n_splits) ml[u].x = -INFINITY;   // past the last split: weight 0
     }
     float mg = m;
@@ -656,12 +650,14 @@ __global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float2
     num.w *= a;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float w = __builtin_amdgcn_exp2f(ml[u].x - mg);   // 0 for a split that saw no visible key
+      const float w = __builtin_amdgcn_exp2f(ml[u].x - mg);           // 0 for a split that saw no visible key
+      const float wo = __builtin_amdgcn_exp2f(ml[u].x + ml[u].z - mg);
+      const float2 lo = unpack_f16x2(v[u].x), hi = unpack_f16x2(v[u].y);
       den += w * ml[u].y;
-      num.x += w * v[u].x;
-      num.y += w * v[u].y;
-      num.z += w * v[u].z;
-      num.w += w * v[u].w;
+      num.x += wo * lo.x;
+      num.y += wo * lo.y;
+      num.z += wo * hi.x;
+      num.w += wo * hi.y;
     }
     m = mg;
   }
@@ -810,8 +806,8 @@ static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int m
   if (max_ctx > AT_CIDX) s = std::max<int64_t>(s, (n_keys_max + AT_CIDX - 33) / (AT_CIDX - 32));
   p.n_splits = int(s);
   const int64_t rows = int64_t(B) * T * Hq;
-  p.o_bytes = align_up(size_t(p.n_splits) * rows * d * sizeof(float), 256);
-  p.ml_bytes = align_up(size_t(p.n_splits) * rows * sizeof(float2), 256);
+  p.o_bytes = align_up(size_t(p.n_splits) * rows * d * sizeof(uint16_t), 256);   // float16 partials
+  p.ml_bytes = align_up(size_t(p.n_splits) * rows * sizeof(float4), 256);
   return p;
 }
 
@@ -884,8 +880,8 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
     MSA_REQUIRE(uintptr_t(q) % 16 == 0 && uintptr_t(k_ctx) % 16 == 0 && uintptr_t(v_ctx) % 16 == 0 &&
                     uintptr_t(k_loc) % 16 == 0 && uintptr_t(v_loc) % 16 == 0,
                 MSA_ERR_INVALID_ARG, fn + ": tensors must be 16-byte aligned");
-    float* ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.tab_bytes);
-    float2* ws_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.tab_bytes + p.o_bytes);
+    uint16_t* ws_o = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.tab_bytes);
+    float4* ws_ml = reinterpret_cast<float4*>(static_cast<char*>(ws) + p.tab_bytes + p.o_bytes);
     const int G = Hq / Hkv;
     const float scale_log2_pf = sm_scale * 1.4426950408889634f;
     if (p.prefill) {

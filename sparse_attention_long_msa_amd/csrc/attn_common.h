@@ -91,6 +91,44 @@ __device__ __forceinline__ void rope_rotate(uint4 (&v)[4], const float2* __restr
   }
 }
 
+// A key split's partial result for one query row, as attn_combine_kernel
+// reads it: the unnormalised O scaled by 2^-c, with c the exponent of the
+// row's largest |O| (frexp), so every element lies in (-1, 1), stored in
+// float16; and (m, l, c) in float32.  Half the bytes of a float32 partial;
+// the power-of-two scale keeps any O in range, and the float16 rounding stays
+// within 2^-12 of the row's largest element.  Lane (lc, g4) holds
+// O^T[16*dt + 4*g4 + e][row lc]; the four lanes of a row (g4 = 0..3) must all
+// call it (the row maximum crosses them); row_ok selects the lanes that store.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const half2_t v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float2 unpack_f16x2(uint32_t u) {
+  const half2_t v = __builtin_bit_cast(half2_t, u);
+  return make_float2(static_cast<float>(v.x), static_cast<float>(v.y));
+}
+
+__device__ __forceinline__ void store_partial(const f32x4 (&o)[8], float m, float l, bool row_ok, int g4,
+                                              uint16_t* __restrict__ ws_oh_row, float4* __restrict__ ws_ml_row) {
+  float rmax = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rmax = fmaxf(rmax, fabsf(o[dt][e]));
+  rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+  rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+  int c = 0;
+  (void)frexpf(rmax, &c);
+  const float sc = ldexpf(1.f, -c);
+  if (!row_ok) return;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<uint2*>(ws_oh_row + 16 * dt + 4 * g4) =
+        make_uint2(pack_f16x2(o[dt][0] * sc, o[dt][1] * sc), pack_f16x2(o[dt][2] * sc, o[dt][3] * sc));
+  if (g4 == 0) *ws_ml_row = make_float4(m, l, float(c), 0.f);
+}
+
 struct KeySrc {
   int64_t row;   // row index into the [*, Hkv, d] tensor (already including b)
   int pos;
