@@ -615,7 +615,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
 }
 
 // out[b,t,hq,:] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, one pass with
-// a running maximum; eight splits' loads are issued together.  O_s arrives
+// a running maximum; sixteen splits' loads are issued together.  O_s arrives
 // as float16 scaled by 2^-c_s (store_partial), so its weight is 2^(m_s + c_s - m).
 __global__ void attn_combine_kernel(const uint16_t* __restrict__ ws_o, const float4* __restrict__ ws_ml, int n_splits,
                                     int64_t rows, int d, float* __restrict__ out, float* __restrict__ lse) {
@@ -627,7 +627,7 @@ __global__ void attn_combine_kernel(const uint16_t* __restrict__ ws_o, const flo
   const int e = int(i % dq) * 4;
   float m = -INFINITY, den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  constexpr int U = 8;
+  constexpr int U = 16;
   for (int s0 = 0; s0 < n_splits; s0 += U) {
     float4 ml[U];
     uint2 v[U];
