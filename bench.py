@@ -9,8 +9,10 @@ of 64 tokens, 32 query heads, 4,096 local tokens, k = 16.  Inputs are seeded
 synthetic data generated on the device before the timed region.
 
 Timing: the K timed steps are measured by the wall clock between two device
-synchronisations; inside them only one pair of HIP events per step brackets a
-routing-score launch (the roofline's launch duration).  The per-stage
+synchronisations, once with the library calls launched one by one (inside
+them only one pair of HIP events per step brackets a routing-score launch:
+the roofline's launch duration) and once replaying the step captured as a
+HIP graph; the line reports the faster of the two and both times.  The per-stage
 breakdown comes from up to 3 further steps with events between all stages
 (each event record idles the device for a few microseconds, so these steps
 are not part of the timed region).
@@ -51,6 +53,8 @@ def parse():
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the per-config lines of the smaller presets (after the 100M-token line)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (no HIP graph replay; for counter collection)")
     ap.add_argument("--layers", type=int, default=None, help="override the routed-layer count (profiling only)")
     ap.add_argument("--rounds", type=int, default=1,
                     help="Memory Interleave rounds per layer (> 1: route, skip the fetched documents, select and "
@@ -64,6 +68,9 @@ def parse():
     ap.add_argument("--encode", action="store_true",
                     help="time Stage 1 from hidden states instead (msa_encode over a 1M-token memory, one layer per "
                          "call, hidden 2560)")
+    ap.add_argument("--corpus", action="store_true",
+                    help="with --encode: Stage 1 over the whole 100M-token memory (195,312 documents x 512 tokens) "
+                         "for every routed layer, a block of 2,048 documents per call, into the full stores")
     ap.add_argument("--train", action="store_true",
                     help="time the training-time path instead (routing loss and attention backward per routed "
                          "layer; --config defaults to train64k)")
@@ -86,13 +93,15 @@ def main():
         return copy_calibration(torch)
     if args.train:
         return train_main(args, torch)
+    if args.encode and args.corpus:
+        return encode_corpus_main(args, torch)
     if args.encode:
         return encode_main(args, torch)
 
     from synth import configs
 
     p = configs.PRESETS[args.config]()
-    pb = PresetBench(torch, p, args.layers, rounds=args.rounds)
+    pb = PresetBench(torch, p, args.layers, rounds=args.rounds, graph=not args.no_graph)
     pb.build_stores()
     pb.build_content("hbm")
     assembly = args.hbm_assembly if args.rounds == 1 else "index"
@@ -117,13 +126,14 @@ class PresetBench:
     """One workload preset on the device: its stores (built by the offline
     stage before any timing), a LayerRunner and the whole-path step."""
 
-    def __init__(self, torch, p, layers=None, rounds=1):
+    def __init__(self, torch, p, layers=None, rounds=1, graph=True):
         import synth
         from synth import device as SD
         import sparse_attention_long_msa_amd as M
         self.torch, self.p, self.synth, self.SD, self.M = torch, p, synth, SD, M
         self.layers = p.layers if layers is None else layers
         self.rounds = rounds
+        self.graph = graph
         self.dev = torch.device("cuda:0")
         torch.cuda.set_device(self.dev)
         self.bf = torch.bfloat16 if p.bf16 else torch.float32
@@ -335,8 +345,10 @@ class PresetBench:
         """The JSON line: whole-step throughput of the routing-key scan, the
         stage breakdown and the roofline of the routing-score launch."""
         p, layers = self.p, self.layers
-        ms_eager, _ = self.timed(steps, warmup, route_events=False)
-        ms_per_step, route_ms = self.timed(steps, warmup, graph=True)
+        ms_eager, route_ms = self.timed(steps, warmup)
+        ms_graph = self.timed(steps, warmup, route_events=False, graph=True)[0] if self.graph else float("inf")
+        launch = "hip-graph replay" if ms_graph < ms_eager else "eager launches"
+        ms_per_step = min(ms_eager, ms_graph)
         stage = self.stages(min(steps, 3))
         H, d, N, D = p.H, p.d, p.n_chunks, p.n_docs
         store_bytes = N * H * d * self.esz                     # per layer
@@ -377,9 +389,10 @@ class PresetBench:
             "dtype": "bf16" if p.bf16 else "f32",
             "data": "synthetic (seeded counter-based generator; planted needles)",
             "config": {"workload": workload, "global_batch": p.B, "seq_len": p.T, "parallelism": "single GPU",
-                       "kv_tier": "hbm", "rounds": self.rounds, "step_launch": "hip-graph replay"},
+                       "kv_tier": "hbm", "rounds": self.rounds, "step_launch": launch},
             "route_attn_us_per_query": round(ms_per_step * 1e3 / p.B, 1),
             "ms_per_step_eager_launches": round(ms_eager, 4),
+            "ms_per_step_graph_replay": round(ms_graph, 4) if self.graph else None,
             "routing_GBps": round(routing_gbps, 1),
             "routing_frac_of_8TBps": round(routing_gbps / 8000, 4),
             "stage_ms_per_step": stages,
@@ -487,14 +500,15 @@ def config_leg(torch, name, args):
     on the machine's host cores (bounded samples)."""
     from synth import configs
     p = configs.PRESETS[name]()
-    pb = PresetBench(torch, p)
+    pb = PresetBench(torch, p, graph=not args.no_graph)
     pb.build_stores()
     pb.build_content("hbm")
     pb.make_runner("hbm", indexed=True)
     recall = pb.needle_recall()
     steps, warmup = max(3, min(args.steps, 10)), max(1, min(args.warmup, 3))
     ms_eager, _ = pb.timed(steps, warmup, route_events=False)
-    ms, _ = pb.timed(steps, warmup, route_events=False, graph=True)
+    ms_graph = pb.timed(steps, warmup, route_events=False, graph=True)[0] if pb.graph else float("inf")
+    ms = min(ms_eager, ms_graph)
     warm = pb.stages(2)
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=pb.dev)
     cold = pb.cold(flush_buf)
@@ -508,7 +522,9 @@ def config_leg(torch, name, args):
         "workload": f"{p.n_docs} docs, {int(p.lengths.sum())} tokens, {p.n_chunks} chunks/layer, {pb.layers} layers; "
                     f"B={p.B} x T={p.T}, L_loc={p.L_loc}, k={p.k}, {'bf16' if p.bf16 else 'f32'}",
         "ms_per_step": round(ms, 4), "us_per_query": round(ms * 1e3 / p.B, 1),
+        "step_launch": "hip-graph replay" if ms_graph < ms_eager else "eager launches",
         "ms_per_step_eager_launches": round(ms_eager, 4),
+        "ms_per_step_graph_replay": round(ms_graph, 4) if pb.graph else None,
         "routing_GBps": gbps(store_bytes, warm[0] + warm[1]),
         "attention_GBps": gbps(attn_bytes, warm[3]),
         "stage_ms_per_step": {"route_score": round(warm[0], 4), "topk_and_context_index": round(warm[1], 4),
@@ -817,6 +833,99 @@ def encode_main(args, torch):
     print(json.dumps(res), flush=True)
 
 
+def encode_corpus_main(args, torch):
+    """Stage 1 at corpus scale: the pooled stores of every routed layer of the
+    100M-token memory (195,312 documents x 512 tokens, chunk 64: K, V and the
+    normalised K_r, 1,562,496 chunks per layer, 173 GB in HBM) built from the
+    tokens' hidden states (width 2,560) with msa_encode, 2,048 documents (1M
+    tokens, 5.4 GB of hidden states) per call.  The hidden states of each
+    block are seeded synthetic values generated on the device just before
+    the call (not part of the encode time); the projection weights are
+    synthetic per layer."""
+    import synth
+    from synth import configs
+    from synth import device as SD
+    import sparse_attention_long_msa_amd as M
+
+    p = configs.cfg4()
+    layers = p.layers if args.layers is None else args.layers
+    hidden, H, d, chunk = 2560, p.H, p.d, p.chunk
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16
+    N = p.n_chunks
+    blk_docs = 2048
+    tok_per_doc = int(p.lengths[0])
+    assert (p.lengths == tok_per_doc).all()
+    kb = torch.empty((layers, N, H, d), dtype=bf, device=dev)
+    vb = torch.empty((layers, N, H, d), dtype=bf, device=dev)
+    kr = torch.empty((layers, M.padded_chunks(N, M.MSA_LAYOUT_TILED), H, d), dtype=bf, device=dev)
+    x = torch.empty((blk_docs * tok_per_doc, hidden), dtype=bf, device=dev)
+    w = torch.empty((3 * H * d, hidden), dtype=bf, device=dev)
+    cpb = blk_docs * tok_per_doc // chunk                     # chunks per full block
+    ws = torch.empty(M.lib.msa_encode_workspace(M.MSA_BF16, cpb, hidden, H, d), dtype=torch.uint8, device=dev)
+    # the document index of a full block and of the last, partial one
+    def index(n_docs):
+        to = synth.offsets(np.full(n_docs, tok_per_doc, dtype=np.int64))
+        co = synth.offsets(np.full(n_docs, tok_per_doc // chunk, dtype=np.int64))
+        to_d, co_d = torch.from_numpy(to).to(dev), torch.from_numpy(co).to(dev)
+        return to_d, co_d, M.msa_chunk_doc_map(co_d, int(co[-1]))
+    n_blocks = (p.n_docs + blk_docs - 1) // blk_docs
+    last_docs = p.n_docs - (n_blocks - 1) * blk_docs
+    idx = {blk_docs: index(blk_docs), last_docs: index(last_docs)}
+    log(f"encode corpus: {p.n_docs} docs, {N} chunks/layer, {layers} layers, {n_blocks} blocks per layer; stores "
+        f"{3 * layers * N * H * d * 2 / 1e9:.1f} GB")
+    ms_calls = []
+    t0 = time.perf_counter()
+    for l in range(layers):
+        SD.fill(w, p.seed, l, synth.T_V, scale_pow2=-6)
+        for bi in range(n_blocks):
+            nd = blk_docs if bi < n_blocks - 1 else last_docs
+            to_d, co_d, cd = idx[nd]
+            n_tok, nc = nd * tok_per_doc, nd * tok_per_doc // chunk
+            c0 = bi * cpb
+            xb = x[:n_tok]
+            SD.fill(xb, p.seed, l, synth.T_K, start=bi * blk_docs * tok_per_doc * hidden)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            M.msa_encode(xb, w, to_d, co_d, cd, chunk, H, d, kr_layout=M.MSA_LAYOUT_TILED, k_bar=kb[l, c0:c0 + nc],
+                         v_bar=vb[l, c0:c0 + nc], kr_hat=kr[l, c0:c0 + M.padded_chunks(nc, M.MSA_LAYOUT_TILED)],
+                         ws=ws)
+            e1.record()
+            ms_calls.append((e0, e1))
+        torch.cuda.synchronize()
+        log(f"encode corpus: layer {l} done ({time.perf_counter() - t0:.1f} s)")
+    wall = time.perf_counter() - t0
+    enc_ms = float(sum(a.elapsed_time(b) for a, b in ms_calls))
+    n_tok_total = int(p.lengths.sum())
+    x_bytes = n_tok_total * hidden * 2 * layers
+    res = {
+        "metric": "Stage-1 encode at corpus scale: hidden-state GB/s (pool + projection to K, V, K_r)",
+        "value": round(x_bytes / (enc_ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": 1,
+        "warmup": 0,
+        "ms_per_step": round(enc_ms, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; synthetic projection weights)",
+        "config": {"workload": f"encode corpus: {n_tok_total}-token memory ({p.n_docs} docs x {tok_per_doc}), "
+                               f"chunk {chunk}, {N} chunks/layer, {layers} routed layers, hidden {hidden}, H={H}, "
+                               f"d={d}; {n_blocks} calls of {blk_docs} docs per layer",
+                   "global_batch": 1, "seq_len": n_tok_total, "parallelism": "single GPU"},
+        "encode_s_all_layers": round(enc_ms * 1e-3, 3),
+        "wall_s_with_input_generation": round(wall, 2),
+        "tokens_per_s": round(n_tok_total * layers / (enc_ms * 1e-3), 1),
+        "calls": len(ms_calls),
+        "avg_call_ms": round(enc_ms / len(ms_calls), 4),
+        "stores_GB": round(3 * layers * N * H * d * 2 / 1e9, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration(torch):
     """A plain device copy of 1 GiB, three times: the reference that scales the
     HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the other kernels."""
@@ -894,7 +1003,7 @@ def cpu_baseline(p, layers, n_sample_chunks=None, quiet=False):
     if not quiet:
         log(f"cpu baseline ({p.name}): sample prepared in {t_prep:.1f} s, oracle routing {dt:.1f} s")
     return {"value": round(gb / dt, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 2), "sample_chunks": n,
+            "seconds": round(dt, 4), "sample_chunks": n,
             "sample": f"layer 0, first {n_docs} documents ({n} pooled chunks, "
                       f"{n * p.H * p.d * (2 if p.bf16 else 4) / 1e9:.2f} GB of routing keys) scored against each of the "
                       f"{layers} routed layers' {p.B} x {p.T}-token queries: routing score + top-k, float64"}

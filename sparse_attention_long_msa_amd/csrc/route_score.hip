@@ -358,42 +358,87 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
   }
 }
 
-// Vector path: float32 (or any head size) - one thread per (chunk, column),
-// per-head dot products in float32 scaled by the precomputed column norms.
+// Vector path: float32 (or any head size).  The query is first scaled per
+// (column, head) by 1 / (H * max(||q||, eps)) into float32 rows q' (one wave
+// per (column, head)), so a chunk's score for column j is the flat dot product
+// of q'[j] and the chunk's H*d elements.  A workgroup stages a block of CB
+// columns of q' in LDS and each wave takes one chunk at a time: lanes stride
+// over the chunk's elements (coalesced) with CB accumulators, a wave-wide sum
+// per column, then the token max inside each query and one atomic max per
+// (query, chunk) into its document.
 template <int DT>
-__global__ void qnorm_kernel(const typename Elem<DT>::T* __restrict__ q_r, int J, int H, int d,
-                             float* __restrict__ winv) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= J * H) return;
-  const typename Elem<DT>::T* p = q_r + int64_t(i) * d;
+__global__ void qscale_vec_kernel(const typename Elem<DT>::T* __restrict__ q_r, int J, int H, int d,
+                                  float* __restrict__ qs) {
+  // one wave per (column, head): lanes stride over the head's d elements
+  const int64_t i = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
+  const int lane = threadIdx.x % 64;
+  if (i >= int64_t(J) * H) return;               // uniform in the wave
+  const typename Elem<DT>::T* p = q_r + i * d;
   float ss = 0.f;
-  for (int e = 0; e < d; ++e) {
+  for (int e = lane; e < d; e += 64) {
     const float x = Elem<DT>::load(p, e);
     ss += x * x;
   }
-  winv[i] = 1.f / (float(H) * fmaxf(sqrtf(ss), 1e-8f));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float w = 1.f / (float(H) * fmaxf(sqrtf(ss), 1e-8f));
+  float* o = qs + i * d;
+  for (int e = lane; e < d; e += 64) o[e] = Elem<DT>::load(p, e) * w;
 }
 
-template <int DT>
-__global__ void route_score_vec_kernel(const typename Elem<DT>::T* __restrict__ q_r, int T, int J, int H, int d,
-                                       const typename Elem<DT>::T* __restrict__ kr,
-                                       const int32_t* __restrict__ chunk_doc, int64_t n_docs, int64_t n_chunks,
-                                       const float* __restrict__ winv, float* __restrict__ doc_score) {
-  const int64_t p = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (p >= n_chunks * J) return;
-  const int64_t c = p / J;
-  const int j = int(p % J);
-  const int doc = doc_of(chunk_doc, c);
-  if (doc < 0 || doc >= n_docs) return;
-  float s = 0.f;
-  for (int h = 0; h < H; ++h) {
-    const typename Elem<DT>::T* qp = q_r + (int64_t(j) * H + h) * d;
-    const typename Elem<DT>::T* kp = kr + (c * H + h) * d;
-    float dot = 0.f;
-    for (int e = 0; e < d; ++e) dot += Elem<DT>::load(qp, e) * Elem<DT>::load(kp, e);
-    s += winv[j * H + h] * dot;
+constexpr int RV_THREADS = 256;
+constexpr int RV_CB = 16;    // largest column block
+
+template <int DT, int CB>
+__global__ __launch_bounds__(RV_THREADS) void route_score_vec_kernel(
+    const float* __restrict__ qs, int T, int J, int E, const typename Elem<DT>::T* __restrict__ kr,
+    const int32_t* __restrict__ chunk_doc, int64_t n_docs, int64_t n_chunks, float* __restrict__ doc_score) {
+  extern __shared__ float qcol[];                  // [CB][E]
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int j0 = blockIdx.y * CB;
+  const int nc = min(CB, J - j0);
+  for (int i = threadIdx.x; i < CB * E; i += RV_THREADS) {
+    const int jj = i / E;
+    qcol[i] = jj < nc ? qs[int64_t(j0 + jj) * E + (i % E)] : 0.f;
   }
-  atomic_max_float(doc_score + int64_t(j / T) * n_docs + doc, s);
+  __syncthreads();
+  const int64_t stride = int64_t(gridDim.x) * (RV_THREADS / 64);
+  for (int64_t c = int64_t(blockIdx.x) * (RV_THREADS / 64) + wave; c < n_chunks; c += stride) {
+    const int doc = doc_of(chunk_doc, c);
+    if (doc < 0 || doc >= n_docs) continue;        // uniform in the wave
+    const typename Elem<DT>::T* kp = kr + c * E;
+    float acc[CB];
+#pragma unroll
+    for (int jj = 0; jj < CB; ++jj) acc[jj] = 0.f;
+    for (int e = lane; e < E; e += 64) {
+      const float kv = Elem<DT>::load(kp, e);
+#pragma unroll
+      for (int jj = 0; jj < CB; ++jj) acc[jj] += qcol[jj * E + e] * kv;
+    }
+#pragma unroll
+    for (int jj = 0; jj < CB; ++jj) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc[jj] += __shfl_xor(acc[jj], o);
+    }
+    // token max inside each query of the block, one atomic per (query, chunk)
+    if (lane == 0) {
+      int b = -1;
+      float v = -INFINITY;
+#pragma unroll
+      for (int jj = 0; jj < CB; ++jj) {
+        if (jj >= nc) break;
+        const int bj = (j0 + jj) / T;
+        if (bj != b) {
+          if (b >= 0) atomic_max_float(doc_score + int64_t(b) * n_docs + doc, v);
+          b = bj;
+          v = acc[jj];
+        } else {
+          v = fmaxf(v, acc[jj]);
+        }
+      }
+      if (b >= 0) atomic_max_float(doc_score + int64_t(b) * n_docs + doc, v);
+    }
+  }
 }
 
 static bool use_mfma(int dtype, int H, int d) { return dtype == MSA_BF16 && d == RS_D && H == RS_H; }
@@ -405,7 +450,8 @@ extern "C" size_t msa_route_score_workspace(int dtype, int B, int T, int H, int 
   (void)n_docs;
   (void)n_chunks;
   if (msa::use_mfma(dtype, H, d)) return 0;
-  return msa::align_up(size_t(B) * T * H * sizeof(float), 256);
+  return msa::align_up(size_t(B) * T * H * d * sizeof(float), 256);   // the scaled query rows q'
+
 }
 
 namespace msa {
@@ -493,24 +539,48 @@ static int route_score(const std::string& fn, int dtype, const void* q_r, int B,
     MSA_LAUNCH_CHECK();
     return MSA_OK;
   }
-  float* winv = static_cast<float*>(ws);
-  if (dtype == MSA_BF16) {
-    hipLaunchKernelGGL(qnorm_kernel<MSA_BF16>, dim3((J * H + 255) / 256), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(q_r), J, H, d, winv);
-  } else {
-    hipLaunchKernelGGL(qnorm_kernel<MSA_F32>, dim3((J * H + 255) / 256), dim3(256), 0, s,
-                       static_cast<const float*>(q_r), J, H, d, winv);
-  }
-  MSA_LAUNCH_CHECK();
-  const int64_t work = n_chunks * J;
-  const dim3 grid(unsigned((work + 255) / 256)), block(256);
+  float* qs = static_cast<float*>(ws);
+  const unsigned qblocks = unsigned((int64_t(J) * H + 3) / 4);   // four waves per block
   if (dtype == MSA_BF16)
-    hipLaunchKernelGGL(route_score_vec_kernel<MSA_BF16>, grid, block, 0, s, static_cast<const uint16_t*>(q_r), T,
-                       J, H, d, static_cast<const uint16_t*>(kr_hat), chunk_doc, n_docs, n_chunks, winv,
-                       doc_score);
+    hipLaunchKernelGGL(qscale_vec_kernel<MSA_BF16>, dim3(qblocks), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(q_r), J, H, d, qs);
   else
-    hipLaunchKernelGGL(route_score_vec_kernel<MSA_F32>, grid, block, 0, s, static_cast<const float*>(q_r), T, J,
-                       H, d, static_cast<const float*>(kr_hat), chunk_doc, n_docs, n_chunks, winv, doc_score);
+    hipLaunchKernelGGL(qscale_vec_kernel<MSA_F32>, dim3(qblocks), dim3(256), 0, s,
+                       static_cast<const float*>(q_r), J, H, d, qs);
+  MSA_LAUNCH_CHECK();
+  {
+    const int E = H * d;
+    int dev = 0, n_cu = 0;
+    MSA_HIP_CHECK(hipGetDevice(&dev));
+    MSA_HIP_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+    // column block: as many columns as fit 64 KB of LDS, at most 16
+    const int cb_fit = int(std::max<int64_t>(1, std::min<int64_t>(RV_CB, 65536 / (int64_t(E) * 4))));
+    const int CB = cb_fit >= 16 ? 16 : (cb_fit >= 8 ? 8 : (cb_fit >= 4 ? 4 : 1));
+    const int n_cb = (J + CB - 1) / CB;
+    const int64_t waves_per_wg = RV_THREADS / 64;
+    const int64_t gx = std::max<int64_t>(1, std::min<int64_t>((n_chunks + waves_per_wg - 1) / waves_per_wg,
+                                                                std::max<int64_t>(1, 4 * int64_t(n_cu) / n_cb)));
+    const size_t smem = size_t(CB) * E * sizeof(float);
+    MSA_REQUIRE(smem <= 65536 && n_cb <= 65535, MSA_ERR_UNSUPPORTED, fn + ": vector path shape");
+    const dim3 grid{unsigned(gx), unsigned(n_cb)}, block{unsigned(RV_THREADS)};
+#define RV_LAUNCH(DTV, TV, CBV)                                                                              \
+  hipLaunchKernelGGL((route_score_vec_kernel<DTV, CBV>), grid, block, smem, s, qs, T, J, E,                  \
+                     static_cast<const TV*>(kr_hat), chunk_doc, n_docs, n_chunks, doc_score)
+#define RV_DT(DTV, TV)                                      \
+    switch (CB) {                                           \
+      case 16: RV_LAUNCH(DTV, TV, 16); break;                \
+      case 8: RV_LAUNCH(DTV, TV, 8); break;                  \
+      case 4: RV_LAUNCH(DTV, TV, 4); break;                  \
+      default: RV_LAUNCH(DTV, TV, 1); break;                 \
+    }
+    if (dtype == MSA_BF16) {
+      RV_DT(MSA_BF16, uint16_t);
+    } else {
+      RV_DT(MSA_F32, float);
+    }
+#undef RV_DT
+#undef RV_LAUNCH
+  }
   MSA_LAUNCH_CHECK();
   return MSA_OK;
 }

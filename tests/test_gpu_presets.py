@@ -12,7 +12,7 @@ import torch
 import oracle as O
 import synth
 from synth import configs
-from tests.helpers import ATOL_ATTN, BAND, RTOL_SCORE, check_ids, check_scores
+from tests.helpers import ATOL_ATTN, RTOL_SCORE, check_ids, check_scores, untile_np
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -48,11 +48,32 @@ def test_preset_tiny_full():
     assert g["ids"][0, 0] == host.needles[0]          # the planted needle ranks first
 
 
-def _check_full(p, host, g, queries):
+def _check_store(p, host, gl, store):
+    """The GPU's pooled routing keys against the oracle's: equal, except a
+    small fraction one store-dtype ulp apart (the GPU rounds its float32
+    pooled and normalised value once, the oracle its float64 value)."""
+    g = gl.store[synth.T_KR].float().cpu().numpy()
+    g = untile_np(g, p.n_chunks) if p.bf16 else g[: p.n_chunks]
+    diff = g != store
+    frac = diff.mean()
+    if diff.any():
+        a, b = g[diff].astype(np.float64), store[diff].astype(np.float64)
+        _, e = np.frexp(np.maximum(np.abs(a), np.abs(b)))
+        ulp = np.ldexp(1.0, e - (8 if p.bf16 else 24))
+        assert (np.abs(a - b) <= ulp).all(), "a stored routing key differs by more than one ulp"
+    _log(f"{p.name} layer {host.l}: stored routing keys differing from the oracle's by one ulp: {diff.sum()} "
+         f"({frac:.2e})")
+    assert frac <= 1e-4
+
+
+def _check_full(p, host, g, queries, gl=None):
     """Scores of every document, ids against the full ranking, the selected
     values, and the attention of the given queries."""
     rtol = RTOL_SCORE[host.dt]
-    ref = host.all_doc_scores()
+    store = host.routing_store()
+    if gl is not None:
+        _check_store(p, host, gl, store)
+    ref = host.all_doc_scores(store)
     err = check_scores(g["doc_score"], ref, rtol, p.k)
     exact = check_ids(g["ids"], ref, p.k)
     n_exact = sum(check_ids(g["ids"][b:b + 1], ref[b:b + 1], p.k) for b in range(p.B))
@@ -75,9 +96,10 @@ def _check_full(p, host, g, queries):
 def test_preset_1m_full_ranking(layer):
     p = configs.cfg2()
     host = HostLayer(p, layer)
-    g = GpuLayer(p, layer, host).run()
+    gl = GpuLayer(p, layer, host)
+    g = gl.run()
     _log(f"cfg2: GPU layer {layer} done; oracle ranking of all {p.n_docs} documents")
-    _check_full(p, host, g, [0])
+    _check_full(p, host, g, [0], gl)
     _log(f"cfg2: needle recall {_needle_recall(p, host, g)}")
 
 
@@ -92,9 +114,10 @@ def test_preset_full_size_full_ranking(name, tier):
     # context index in one call (the path bench.py times); host tier: the
     # selected rows are gathered over the host link
     mode = M.MSA_SRC_HOST_MAPPED if tier == "host" else M.MSA_SRC_DEVICE
-    g = GpuLayer(p, layer, host, src_mode=mode, indexed=tier == "hbm").run()
+    gl = GpuLayer(p, layer, host, src_mode=mode, indexed=tier == "hbm")
+    g = gl.run()
     _log(f"{name}: GPU layer {layer} done (ctx_len {g['ctx_len'][:4].tolist()}...); oracle ranking of all "
          f"{p.n_docs} documents")
-    _check_full(p, host, g, list(range(p.B)))
+    _check_full(p, host, g, list(range(p.B)), gl if tier == "hbm" else None)
     _log(f"{name}: needle recall {_needle_recall(p, host, g)}")
     assert _needle_recall(p, host, g) >= 0.75

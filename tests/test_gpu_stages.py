@@ -166,6 +166,26 @@ def test_segment_max_is_the_document_max():
     np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("bf16,H,d,B,T", [(True, 4, 64, 2, 9), (False, 16, 256, 1, 20), (False, 2, 16, 5, 4),
+                                         (False, 8, 128, 40, 1)])
+def test_route_score_vector_path(bf16, H, d, B, T):
+    """The vector path (float32, or head shapes off the MFMA path): column
+    blocks of 16, 8 and 4 (by the LDS the scaled query rows take), ragged and
+    empty documents, several queries per block."""
+    lens = ragged_lengths(80 + d, 150, 0, 900, n_empty=6)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    dt = "bf16" if bf16 else "f32"
+    store = O.round_to_store(O.l2_normalize(gen(81, 0, synth.T_KR, (n_chunks, H, d), bf16).astype(np.float64)), dt)
+    q = gen(82, 0, synth.T_QR, (B, T, H, d), bf16)
+    got = host(M.msa_route_score(to_dev(q, bf16), to_dev(store, bf16), cd, len(lens)))
+    ref = O.route_scores(q, store, chunk_off)
+    err = check_scores(got, ref, RTOL_SCORE[dt], k=8)
+    cs = M.msa_chunk_scores(to_dev(q, bf16), to_dev(store, bf16), n_chunks)
+    fused = M.msa_route_score(to_dev(q, bf16), to_dev(store, bf16), cd, len(lens))
+    assert torch.equal(M.msa_segment_max(cs, co_d), fused)
+    print(f"route_score vector path {dt} H={H} d={d} B={B} T={T}: normwise err {err:.3g}")
+
+
 def test_route_score_document_table_paths():
     """64 single-token queries over a memory mixing one-chunk documents (a
     workgroup's range holds more (document, query) pairs than its LDS table:
