@@ -836,12 +836,15 @@ def encode_main(args, torch):
 def encode_corpus_main(args, torch):
     """Stage 1 at corpus scale: the pooled stores of every routed layer of the
     100M-token memory (195,312 documents x 512 tokens, chunk 64: K, V and the
-    normalised K_r, 1,562,496 chunks per layer, 173 GB in HBM) built from the
-    tokens' hidden states (width 2,560) with msa_encode, 2,048 documents (1M
-    tokens, 5.4 GB of hidden states) per call.  The hidden states of each
-    block are seeded synthetic values generated on the device just before
-    the call (not part of the encode time); the projection weights are
-    synthetic per layer."""
+    normalised K_r, 1,562,496 chunks per layer, 173 GB in HBM) from the
+    tokens' hidden states (width 2,560), 2,048 documents (1M tokens, 5.4 GB of
+    hidden states) per block, 96 blocks per layer.  The hidden states of four
+    blocks are generated once (seeded synthetic values) and the blocks cycle
+    over them: the encode cost does not depend on the values, and the inputs
+    of a 100M-token layer (512 GB) cannot be held at once.  Timed twice:
+    msa_encode per block on one stream (serial), and msa_encode_pool /
+    msa_encode_project on two streams with two workspaces, so that a block's
+    pooling (HBM-bound) overlaps the previous block's projection (MFMA)."""
     import synth
     from synth import configs
     from synth import device as SD
@@ -860,11 +863,15 @@ def encode_corpus_main(args, torch):
     kb = torch.empty((layers, N, H, d), dtype=bf, device=dev)
     vb = torch.empty((layers, N, H, d), dtype=bf, device=dev)
     kr = torch.empty((layers, M.padded_chunks(N, M.MSA_LAYOUT_TILED), H, d), dtype=bf, device=dev)
-    x = torch.empty((blk_docs * tok_per_doc, hidden), dtype=bf, device=dev)
-    w = torch.empty((3 * H * d, hidden), dtype=bf, device=dev)
+    NX = 4
+    xs = [SD.fill(torch.empty((blk_docs * tok_per_doc, hidden), dtype=bf, device=dev), p.seed, 0, synth.T_K,
+                  start=i * blk_docs * tok_per_doc * hidden) for i in range(NX)]
+    ws_ = [SD.fill(torch.empty((3 * H * d, hidden), dtype=bf, device=dev), p.seed, l, synth.T_V, scale_pow2=-6)
+           for l in range(layers)]
     cpb = blk_docs * tok_per_doc // chunk                     # chunks per full block
-    ws = torch.empty(M.lib.msa_encode_workspace(M.MSA_BF16, cpb, hidden, H, d), dtype=torch.uint8, device=dev)
-    # the document index of a full block and of the last, partial one
+    wsb = M.lib.msa_encode_workspace(M.MSA_BF16, cpb, hidden, H, d)
+    work = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(2)]
+
     def index(n_docs):
         to = synth.offsets(np.full(n_docs, tok_per_doc, dtype=np.int64))
         co = synth.offsets(np.full(n_docs, tok_per_doc // chunk, dtype=np.int64))
@@ -875,52 +882,80 @@ def encode_corpus_main(args, torch):
     idx = {blk_docs: index(blk_docs), last_docs: index(last_docs)}
     log(f"encode corpus: {p.n_docs} docs, {N} chunks/layer, {layers} layers, {n_blocks} blocks per layer; stores "
         f"{3 * layers * N * H * d * 2 / 1e9:.1f} GB")
-    ms_calls = []
-    t0 = time.perf_counter()
-    for l in range(layers):
-        SD.fill(w, p.seed, l, synth.T_V, scale_pow2=-6)
-        for bi in range(n_blocks):
-            nd = blk_docs if bi < n_blocks - 1 else last_docs
-            to_d, co_d, cd = idx[nd]
-            n_tok, nc = nd * tok_per_doc, nd * tok_per_doc // chunk
-            c0 = bi * cpb
-            xb = x[:n_tok]
-            SD.fill(xb, p.seed, l, synth.T_K, start=bi * blk_docs * tok_per_doc * hidden)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            M.msa_encode(xb, w, to_d, co_d, cd, chunk, H, d, kr_layout=M.MSA_LAYOUT_TILED, k_bar=kb[l, c0:c0 + nc],
-                         v_bar=vb[l, c0:c0 + nc], kr_hat=kr[l, c0:c0 + M.padded_chunks(nc, M.MSA_LAYOUT_TILED)],
-                         ws=ws)
-            e1.record()
-            ms_calls.append((e0, e1))
+
+    def block(bi):
+        nd = blk_docs if bi < n_blocks - 1 else last_docs
+        n_tok, nc = nd * tok_per_doc, nd * tok_per_doc // chunk
+        return idx[nd], n_tok, nc, bi * cpb
+
+    def outs(l, c0, nc):
+        return dict(k_bar=kb[l, c0:c0 + nc], v_bar=vb[l, c0:c0 + nc],
+                    kr_hat=kr[l, c0:c0 + M.padded_chunks(nc, M.MSA_LAYOUT_TILED)])
+
+    def serial():
+        for l in range(layers):
+            for bi in range(n_blocks):
+                (to_d, co_d, cd), n_tok, nc, c0 = block(bi)
+                M.msa_encode(xs[bi % NX][:n_tok], ws_[l], to_d, co_d, cd, chunk, H, d, kr_layout=M.MSA_LAYOUT_TILED,
+                             ws=work[0], **outs(l, c0, nc))
+
+    s_pool, s_proj = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def pipelined():
+        s_pool.wait_stream(torch.cuda.current_stream())
+        s_proj.wait_stream(torch.cuda.current_stream())
+        done = [None, None]                  # the projection that last read each workspace
+        i = 0
+        for l in range(layers):
+            for bi in range(n_blocks):
+                (to_d, co_d, cd), n_tok, nc, c0 = block(bi)
+                w = work[i % 2]
+                if done[i % 2] is not None:
+                    s_pool.wait_event(done[i % 2])
+                with torch.cuda.stream(s_pool):
+                    M.msa_encode_pool(xs[bi % NX][:n_tok], to_d, co_d, cd, chunk, H, d, ws=w)
+                    pooled = torch.cuda.Event()
+                    pooled.record(s_pool)
+                s_proj.wait_event(pooled)
+                with torch.cuda.stream(s_proj):
+                    M.msa_encode_project(ws_[l], nc, H, d, w, kr_layout=M.MSA_LAYOUT_TILED, **outs(l, c0, nc))
+                    done[i % 2] = torch.cuda.Event()
+                    done[i % 2].record(s_proj)
+                i += 1
+        torch.cuda.current_stream().wait_stream(s_proj)
+
+    res_t = {}
+    for name, fn in (("serial", serial), ("pipelined", pipelined)):
         torch.cuda.synchronize()
-        log(f"encode corpus: layer {l} done ({time.perf_counter() - t0:.1f} s)")
-    wall = time.perf_counter() - t0
-    enc_ms = float(sum(a.elapsed_time(b) for a, b in ms_calls))
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        res_t[name] = time.perf_counter() - t0
+        log(f"encode corpus {name}: {res_t[name]:.3f} s for {layers} layers")
     n_tok_total = int(p.lengths.sum())
     x_bytes = n_tok_total * hidden * 2 * layers
+    best = min(res_t, key=res_t.get)
+    t = res_t[best]
     res = {
         "metric": "Stage-1 encode at corpus scale: hidden-state GB/s (pool + projection to K, V, K_r)",
-        "value": round(x_bytes / (enc_ms * 1e-3) / 1e9, 1),
+        "value": round(x_bytes / t / 1e9, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": 1,
         "warmup": 0,
-        "ms_per_step": round(enc_ms, 2),
+        "ms_per_step": round(t * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded counter-based generator; synthetic projection weights)",
+        "data": "synthetic (seeded counter-based generator; four input blocks cycled; synthetic projection weights)",
         "config": {"workload": f"encode corpus: {n_tok_total}-token memory ({p.n_docs} docs x {tok_per_doc}), "
                                f"chunk {chunk}, {N} chunks/layer, {layers} routed layers, hidden {hidden}, H={H}, "
-                               f"d={d}; {n_blocks} calls of {blk_docs} docs per layer",
-                   "global_batch": 1, "seq_len": n_tok_total, "parallelism": "single GPU"},
-        "encode_s_all_layers": round(enc_ms * 1e-3, 3),
-        "wall_s_with_input_generation": round(wall, 2),
-        "tokens_per_s": round(n_tok_total * layers / (enc_ms * 1e-3), 1),
-        "calls": len(ms_calls),
-        "avg_call_ms": round(enc_ms / len(ms_calls), 4),
+                               f"d={d}; {n_blocks} blocks of {blk_docs} docs per layer",
+                   "global_batch": 1, "seq_len": n_tok_total, "parallelism": "single GPU", "launch": best},
+        "encode_s_all_layers": {k: round(v, 3) for k, v in res_t.items()},
+        "tokens_per_s": round(n_tok_total * layers / t, 1),
+        "ms_per_block": {k: round(v * 1e3 / (layers * n_blocks), 4) for k, v in res_t.items()},
         "stores_GB": round(3 * layers * N * H * d * 2 / 1e9, 1),
     }
     print(json.dumps(res), flush=True)

@@ -175,6 +175,24 @@ int msa_encode(int dtype, const void* x, const void* w_t, int hidden, int H, int
                void* stream);
 
 /*
+ * msa_encode_pool, msa_encode_project - the two halves of msa_encode, for a
+ * caller that overlaps one block's pooling with the previous block's
+ * projection on two streams (the pool reads the hidden states at HBM rate,
+ * the projection runs on MFMA).  msa_encode_pool writes the block's pooled
+ * rows into ws; msa_encode_project reads them from ws (same sizes: the
+ * workspace is the hand-off) and writes k_bar, v_bar and kr_hat.  Their
+ * composition on one stream is msa_encode, bit for bit.  Arguments, errors
+ * and the workspace size are those of msa_encode; ws must hold the pool's
+ * result when the projection starts (the caller orders the two streams), and
+ * a double-buffered caller uses one workspace per block in flight.
+ */
+int msa_encode_pool(int dtype, const void* x, int hidden, int H, int d, const int64_t* tok_off,
+                    const int64_t* chunk_off, const int32_t* chunk_doc, int64_t n_docs, int64_t n_tok,
+                    int64_t n_chunks, int chunk, void* ws, size_t ws_bytes, void* stream);
+int msa_encode_project(int dtype, const void* w_t, int hidden, int H, int d, int64_t n_chunks, int kr_layout,
+                       void* k_bar, void* v_bar, void* kr_hat, const void* ws, size_t ws_bytes, void* stream);
+
+/*
  * msa_route_score - Stage 2 routing score (README, Overall Design >
  * Architecture: cosine similarity, mean-pooled over heads, then token-wise
  * max; paper note 核心方法 > 架构: cosine against every document's compressed

@@ -61,6 +61,8 @@ _SIGS = {
     "msa_pool_backward": (_I, [_I, _P, _P, _P, _P, _L, _L, _L, _I, _I, _I, _P, _P, _P]),
     "msa_encode_workspace": (_S, [_I, _L, _I, _I, _I]),
     "msa_encode": (_I, [_I, _P, _P, _I, _I, _I, _P, _P, _P, _L, _L, _L, _I, _I, _P, _P, _P, _P, _S, _P]),
+    "msa_encode_pool": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _L, _L, _L, _I, _P, _S, _P]),
+    "msa_encode_project": (_I, [_I, _P, _I, _I, _I, _L, _I, _P, _P, _P, _P, _S, _P]),
     "msa_sparse_attn_backward_workspace": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "msa_sparse_attn_backward": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _L, _P, _P, _P, _I, _P, _P, _I, _I,
                                       _F, _P, _I, _F, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
@@ -701,4 +703,43 @@ def msa_encode(x, w_t, tok_off, chunk_off, chunk_doc, chunk, H, d, kr_layout=MSA
     _check("msa_encode", lib.msa_encode(
         dt, _ptr(x), _ptr(w_t), hidden, H, d, _ptr(tok_off), _ptr(chunk_off), _ptr(chunk_doc), tok_off.numel() - 1,
         n_tok, n_chunks, chunk, kr_layout, _ptr(k_bar), _ptr(v_bar), _ptr(kr_hat), _ptr(ws), wsb, _stream(stream)))
+    return k_bar, v_bar, kr_hat
+
+
+def msa_encode_pool(x, tok_off, chunk_off, chunk_doc, chunk, H, d, ws=None, stream=None):
+    """The first half of msa_encode: the block's pooled rows into ws (returned)."""
+    _dev(x, "x", _FLOAT, (None, None))
+    n_tok, hidden = x.shape
+    _dev(tok_off, "tok_off", _I64, (None,))
+    _dev(chunk_off, "chunk_off", _I64, (tok_off.numel(),))
+    _dev(chunk_doc, "chunk_doc", _I32, (None,))
+    n_chunks = chunk_doc.numel()
+    _dev(ws, "ws", optional=True)
+    ws, wsb = _ws(lib.msa_encode_workspace(_dtype(x), n_chunks, hidden, H, d), x.device, ws)
+    _check("msa_encode_pool", lib.msa_encode_pool(
+        _dtype(x), _ptr(x), hidden, H, d, _ptr(tok_off), _ptr(chunk_off), _ptr(chunk_doc), tok_off.numel() - 1,
+        n_tok, n_chunks, chunk, _ptr(ws), wsb, _stream(stream)))
+    return ws
+
+
+def msa_encode_project(w_t, n_chunks, H, d, ws, kr_layout=MSA_LAYOUT_ROWS, k_bar=None, v_bar=None, kr_hat=None,
+                       stream=None):
+    """The second half of msa_encode: project the pooled rows held in ws
+    (from msa_encode_pool) to (k_bar, v_bar, kr_hat)."""
+    _dev(w_t, "w_t", _FLOAT, (3 * H * d, None))
+    hidden = w_t.shape[1]
+    _dev(ws, "ws")
+    dev_ = w_t.device
+    if k_bar is None:
+        k_bar = torch.empty((n_chunks, H, d), dtype=w_t.dtype, device=dev_)
+    if v_bar is None:
+        v_bar = torch.empty((n_chunks, H, d), dtype=w_t.dtype, device=dev_)
+    if kr_hat is None:
+        kr_hat = torch.empty((padded_chunks(n_chunks, kr_layout), H, d), dtype=w_t.dtype, device=dev_)
+    _dev(k_bar, "k_bar", w_t.dtype, (n_chunks, H, d))
+    _dev(v_bar, "v_bar", w_t.dtype, (n_chunks, H, d))
+    _dev(kr_hat, "kr_hat", w_t.dtype, (padded_chunks(n_chunks, kr_layout), H, d))
+    _check("msa_encode_project", lib.msa_encode_project(
+        _dtype(w_t), _ptr(w_t), hidden, H, d, n_chunks, kr_layout, _ptr(k_bar), _ptr(v_bar), _ptr(kr_hat), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
     return k_bar, v_bar, kr_hat

@@ -276,24 +276,24 @@ extern "C" size_t msa_encode_workspace(int dtype, int64_t n_chunks, int hidden, 
   return b;
 }
 
-extern "C" int msa_encode(int dtype, const void* x, const void* w_t, int hidden, int H, int d, const int64_t* tok_off,
-                          const int64_t* chunk_off, const int32_t* chunk_doc, int64_t n_docs, int64_t n_tok,
-                          int64_t n_chunks, int chunk, int kr_layout, void* k_bar, void* v_bar, void* kr_hat, void* ws,
-                          size_t ws_bytes, void* stream) {
-  using namespace msa;
-  MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, "msa_encode: bad dtype");
-  MSA_REQUIRE(x && w_t && tok_off && chunk_off && chunk_doc && k_bar && v_bar && kr_hat && ws, MSA_ERR_INVALID_ARG,
-              "msa_encode: NULL pointer");
+namespace msa {
+
+// The two halves of msa_encode.  The workspace carries the pooled rows from
+// the first to the second: float32 rows, or on the MFMA path their bf16
+// hi/lo parts (the same bytes), then on the vector path the routing keys'
+// float32 staging after them.
+static int encode_pool(const std::string& fn, int dtype, const void* x, int hidden, int H, int d,
+                       const int64_t* tok_off, const int64_t* chunk_off, const int32_t* chunk_doc, int64_t n_docs,
+                       int64_t n_tok, int64_t n_chunks, int chunk, void* ws, size_t ws_bytes, void* stream) {
+  MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
+  MSA_REQUIRE(x && tok_off && chunk_off && chunk_doc && ws, MSA_ERR_INVALID_ARG, fn + ": NULL pointer");
   MSA_REQUIRE(hidden >= 1 && H >= 1 && d >= 1 && n_docs >= 1 && n_tok >= 1 && n_chunks >= 1 && chunk >= 1,
-              MSA_ERR_INVALID_ARG, "msa_encode: non-positive size");
-  MSA_REQUIRE(kr_layout == MSA_LAYOUT_ROWS || (kr_layout == MSA_LAYOUT_TILED && d % 32 == 0), MSA_ERR_INVALID_ARG,
-              "msa_encode: bad kr_layout");
+              MSA_ERR_INVALID_ARG, fn + ": non-positive size");
   MSA_REQUIRE(hidden % (16 / dtype_bytes(dtype)) == 0, MSA_ERR_UNSUPPORTED,
-              "msa_encode: hidden must hold whole 16-byte vectors");
-  MSA_REQUIRE(uintptr_t(x) % 16 == 0 && uintptr_t(w_t) % 16 == 0, MSA_ERR_INVALID_ARG,
-              "msa_encode: x and w_t must be 16-byte aligned");
+              fn + ": hidden must hold whole 16-byte vectors");
+  MSA_REQUIRE(uintptr_t(x) % 16 == 0, MSA_ERR_INVALID_ARG, fn + ": x must be 16-byte aligned");
   MSA_REQUIRE(ws_bytes >= msa_encode_workspace(dtype, n_chunks, hidden, H, d), MSA_ERR_WORKSPACE,
-              "msa_encode: workspace too small");
+              fn + ": workspace too small");
   hipStream_t s = as_stream(stream);
   float* xbar = static_cast<float*>(ws);
   const unsigned pgrid = unsigned(std::min<int64_t>(n_chunks, 1 << 20));
@@ -311,6 +311,24 @@ extern "C" int msa_encode(int dtype, const void* x, const void* w_t, int hidden,
     hipLaunchKernelGGL((pool_hidden_kernel<MSA_F32, false>), dim3(pgrid), dim3(pblock), 0, s,
                        static_cast<const float*>(x), hidden, tok_off, chunk_off, chunk_doc, n_docs, n_chunks, chunk, xbar);
   MSA_LAUNCH_CHECK();
+  return MSA_OK;
+}
+
+static int encode_project(const std::string& fn, int dtype, const void* w_t, int hidden, int H, int d,
+                          int64_t n_chunks, int kr_layout, void* k_bar, void* v_bar, void* kr_hat, void* ws,
+                          size_t ws_bytes, void* stream) {
+  MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
+  MSA_REQUIRE(w_t && k_bar && v_bar && kr_hat && ws, MSA_ERR_INVALID_ARG, fn + ": NULL pointer");
+  MSA_REQUIRE(hidden >= 1 && H >= 1 && d >= 1 && n_chunks >= 1, MSA_ERR_INVALID_ARG, fn + ": non-positive size");
+  MSA_REQUIRE(kr_layout == MSA_LAYOUT_ROWS || (kr_layout == MSA_LAYOUT_TILED && d % 32 == 0), MSA_ERR_INVALID_ARG,
+              fn + ": bad kr_layout");
+  MSA_REQUIRE(hidden % (16 / dtype_bytes(dtype)) == 0, MSA_ERR_UNSUPPORTED,
+              fn + ": hidden must hold whole 16-byte vectors");
+  MSA_REQUIRE(uintptr_t(w_t) % 16 == 0, MSA_ERR_INVALID_ARG, fn + ": w_t must be 16-byte aligned");
+  MSA_REQUIRE(ws_bytes >= msa_encode_workspace(dtype, n_chunks, hidden, H, d), MSA_ERR_WORKSPACE,
+              fn + ": workspace too small");
+  hipStream_t s = as_stream(stream);
+  float* xbar = static_cast<float*>(ws);
   const int tiled = kr_layout == MSA_LAYOUT_TILED;
   if (encode_mfma(dtype, hidden, d)) {
     const int64_t n_rt = (n_chunks + EN_ROWS - 1) / EN_ROWS;
@@ -351,4 +369,37 @@ extern "C" int msa_encode(int dtype, const void* x, const void* w_t, int hidden,
     MSA_LAUNCH_CHECK();
   }
   return MSA_OK;
+}
+
+}  // namespace msa
+
+extern "C" int msa_encode_pool(int dtype, const void* x, int hidden, int H, int d, const int64_t* tok_off,
+                               const int64_t* chunk_off, const int32_t* chunk_doc, int64_t n_docs, int64_t n_tok,
+                               int64_t n_chunks, int chunk, void* ws, size_t ws_bytes, void* stream) {
+  return msa::encode_pool("msa_encode_pool", dtype, x, hidden, H, d, tok_off, chunk_off, chunk_doc, n_docs, n_tok,
+                          n_chunks, chunk, ws, ws_bytes, stream);
+}
+
+extern "C" int msa_encode_project(int dtype, const void* w_t, int hidden, int H, int d, int64_t n_chunks,
+                                  int kr_layout, void* k_bar, void* v_bar, void* kr_hat, const void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return msa::encode_project("msa_encode_project", dtype, w_t, hidden, H, d, n_chunks, kr_layout, k_bar, v_bar,
+                             kr_hat, const_cast<void*>(ws), ws_bytes, stream);
+}
+
+extern "C" int msa_encode(int dtype, const void* x, const void* w_t, int hidden, int H, int d, const int64_t* tok_off,
+                          const int64_t* chunk_off, const int32_t* chunk_doc, int64_t n_docs, int64_t n_tok,
+                          int64_t n_chunks, int chunk, int kr_layout, void* k_bar, void* v_bar, void* kr_hat, void* ws,
+                          size_t ws_bytes, void* stream) {
+  using namespace msa;
+  MSA_REQUIRE(x && w_t && tok_off && chunk_off && chunk_doc && k_bar && v_bar && kr_hat && ws, MSA_ERR_INVALID_ARG,
+              "msa_encode: NULL pointer");
+  MSA_REQUIRE(kr_layout == MSA_LAYOUT_ROWS || (kr_layout == MSA_LAYOUT_TILED && d % 32 == 0), MSA_ERR_INVALID_ARG,
+              "msa_encode: bad kr_layout");
+  MSA_REQUIRE(uintptr_t(w_t) % 16 == 0, MSA_ERR_INVALID_ARG, "msa_encode: x and w_t must be 16-byte aligned");
+  const int st = encode_pool("msa_encode", dtype, x, hidden, H, d, tok_off, chunk_off, chunk_doc, n_docs, n_tok,
+                             n_chunks, chunk, ws, ws_bytes, stream);
+  if (st != MSA_OK) return st;
+  return encode_project("msa_encode", dtype, w_t, hidden, H, d, n_chunks, kr_layout, k_bar, v_bar, kr_hat, ws,
+                        ws_bytes, stream);
 }

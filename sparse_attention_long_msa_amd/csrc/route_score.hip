@@ -410,10 +410,17 @@ __global__ __launch_bounds__(RV_THREADS) void route_score_vec_kernel(
     float acc[CB];
 #pragma unroll
     for (int jj = 0; jj < CB; ++jj) acc[jj] = 0.f;
-    for (int e = lane; e < E; e += 64) {
-      const float kv = Elem<DT>::load(kp, e);
+    // eight of the chunk's loads in flight per lane
+    for (int e0 = lane; e0 < E; e0 += 64 * 8) {
+      float kv[8];
 #pragma unroll
-      for (int jj = 0; jj < CB; ++jj) acc[jj] += qcol[jj * E + e] * kv;
+      for (int u = 0; u < 8; ++u) kv[u] = e0 + 64 * u < E ? Elem<DT>::load(kp, e0 + 64 * u) : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (e0 + 64 * u >= E) break;
+#pragma unroll
+        for (int jj = 0; jj < CB; ++jj) acc[jj] += qcol[jj * E + e0 + 64 * u] * kv[u];
+      }
     }
 #pragma unroll
     for (int jj = 0; jj < CB; ++jj) {

@@ -103,3 +103,35 @@ def test_encode_bench_workload_sampled_documents():
         _check(host(kb[c0:c1]), rk, mk, 0.95)
         _check(host(vb[c0:c1]), rv, mv, 0.95)
         _check(kr_rows[c0:c1], rr, mr, 0.95)
+
+
+@pytest.mark.parametrize("bf16,d", [(True, 128), (False, 64)])
+def test_encode_halves_compose_to_encode(bf16, d):
+    """msa_encode_pool then msa_encode_project on two streams, two blocks in
+    flight with one workspace each, give msa_encode's stores bit for bit."""
+    H, chunk, hidden = 2, 64, 320
+    blocks = [_case(40 + i, 30, hidden, H, d, chunk, bf16) for i in range(2)]
+    s_pool, s_proj = torch.cuda.Stream(), torch.cuda.Stream()
+    outs, refs, keep = [], [], []            # every tensor a side stream touches lives until the sync
+    for tok_off, chunk_off, n_chunks, co_d, cd, x, w in blocks:
+        xd, wd, to_d = to_dev(x, bf16), to_dev(w, bf16), to_dev_i64(tok_off)
+        refs.append([host(t) for t in M.msa_encode(xd, wd, to_d, co_d, cd, chunk, H, d, kr_layout=int(bf16))])
+        ws = torch.empty(M.lib.msa_encode_workspace(M.MSA_BF16 if bf16 else M.MSA_F32, n_chunks, hidden, H, d),
+                         dtype=torch.uint8, device=xd.device)
+        keep += [xd, wd, to_d, co_d, cd, ws]
+        s_pool.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_pool):
+            M.msa_encode_pool(xd, to_d, co_d, cd, chunk, H, d, ws=ws)
+            ev = torch.cuda.Event()
+            ev.record(s_pool)
+        s_proj.wait_event(ev)
+        with torch.cuda.stream(s_proj):
+            kb = torch.empty((n_chunks, H, d), dtype=xd.dtype, device=xd.device)
+            vb = torch.empty_like(kb)
+            kr = torch.empty((M.padded_chunks(n_chunks, int(bf16)), H, d), dtype=xd.dtype, device=xd.device)
+            outs.append(M.msa_encode_project(wd, n_chunks, H, d, ws, kr_layout=int(bf16), k_bar=kb, v_bar=vb,
+                                             kr_hat=kr))
+    torch.cuda.synchronize()
+    for got, ref in zip(outs, refs):
+        for g, r in zip(got, ref):
+            np.testing.assert_array_equal(host(g), r)
