@@ -71,7 +71,7 @@ typedef enum {
                               a side stream                                             */
 } msa_src_mode;
 
-/* Version of this ABI (bumped on any signature change). */
+/* Version of this ABI (bumped on any signature or workspace-layout change, and on added calls). */
 int msa_abi_version(void);
 
 /* Static description of a status code. */
