@@ -666,9 +666,12 @@ __global__ void attn_combine_kernel(const uint16_t* __restrict__ ws_o, const flo
   if (lse && e == 0) lse[row] = den > 0.f ? m + __log2f(den) : -INFINITY;
 }
 
-// Vector path (float32 or any even d): one workgroup per (b, t, hq); the
-// logits of every visible key are formed in float32, then the softmax and
-// the value sum.
+// Vector path (float32 or any even d <= 256): one workgroup per (b, t, hq).
+// Logits: one wave per key, the lanes over the rotated pairs (m, m + d/2),
+// four keys' loads issued before any is used; a wave-wide sum per key.  The
+// softmax is taken over the logits in LDS; the value sum gives each wave a
+// quarter of the keys (lanes over d, coalesced) and adds the four partial
+// rows at the end.
 template <int DT>
 __global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
     const typename Elem<DT>::T* __restrict__ q, int B, int T, int Hq, int Hkv, int d,
@@ -678,10 +681,13 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
     int qpo, const int32_t* __restrict__ ctx_row, int64_t ctx_rows, const float2* __restrict__ tab, int P,
     float sm_scale, float* __restrict__ out, float* __restrict__ lse) {
   using E = Elem<DT>;
+  constexpr int NW = AT_VEC_THREADS / 64, KU = 4;
   extern __shared__ float vsm[];
   float* qr = vsm;               // [d]
   float* red = vsm + d;          // [AT_VEC_THREADS]
-  float* logit = red + AT_VEC_THREADS;
+  float* part = red + AT_VEC_THREADS;   // [NW][d]
+  float* logit = part + NW * d;  // [n_keys]
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int hq = blockIdx.x % Hq;
   const int t = (blockIdx.x / Hq) % T;
   const int b = blockIdx.x / (Hq * T);
@@ -699,34 +705,61 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
   __syncthreads();
   const int ctxl = min(max(ctx_len[b], 0), max_ctx);
   const int n_keys = ctxl + L_loc;
+  // the rotated query pairs this lane multiplies (d <= 256: at most two)
+  float qa[2], qb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = lane + 64 * i;
+    qa[i] = m < half ? qr[m] : 0.f;
+    qb[i] = m < half ? qr[m + half] : 0.f;
+  }
   float mx = -INFINITY;
-  for (int j = threadIdx.x; j < n_keys; j += AT_VEC_THREADS) {
-    const typename E::T* kp;
-    int pos;
-    bool vis = true;
-    if (j < ctxl) {
-      kp = k_ctx + (ctx_src_row(int64_t(b) * max_ctx + j, ctx_row, ctx_rows) * Hkv + g) * d;
-      pos = ctx_pos[int64_t(b) * max_ctx + j];
-      pos = pos < 0 ? 0 : (pos >= P ? P - 1 : pos);
-    } else {
-      const int li = j - ctxl;
-      kp = k_loc + ((int64_t(b) * L_loc + li) * Hkv + g) * d;
-      pos = qpo + li;
-      vis = li <= horizon;
-    }
-    float lg = -INFINITY;
-    if (vis) {
-      float dot = 0.f;
-      const float2* cs = tab + int64_t(pos) * half;
-      for (int m = 0; m < half; ++m) {
-        const float k1 = E::load(kp, m), k2 = E::load(kp, m + half);
-        const float2 c = cs[m];
-        dot += qr[m] * (k1 * c.x - k2 * c.y) + qr[m + half] * (k2 * c.x + k1 * c.y);
+  for (int j0 = wave * KU; j0 < n_keys; j0 += NW * KU) {
+    float k1[KU][2], k2[KU][2];
+    float2 cs[KU][2];
+    bool ok[KU];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int j = j0 + u;
+      const typename E::T* kp = k_loc;
+      int pos = 0;
+      ok[u] = false;
+      if (j < ctxl) {
+        kp = k_ctx + (ctx_src_row(int64_t(b) * max_ctx + j, ctx_row, ctx_rows) * Hkv + g) * d;
+        pos = ctx_pos[int64_t(b) * max_ctx + j];
+        pos = pos < 0 ? 0 : (pos >= P ? P - 1 : pos);
+        ok[u] = true;
+      } else if (j < n_keys) {
+        const int li = j - ctxl;
+        kp = k_loc + ((int64_t(b) * L_loc + li) * Hkv + g) * d;
+        pos = qpo + li;
+        ok[u] = li <= horizon;
       }
-      lg = dot * sm_scale;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int m = lane + 64 * i;
+        const bool in = ok[u] && m < half;
+        k1[u][i] = in ? E::load(kp, m) : 0.f;
+        k2[u][i] = in ? E::load(kp, m + half) : 0.f;
+        cs[u][i] = in ? tab[int64_t(pos) * half + m] : make_float2(0.f, 0.f);
+      }
     }
-    logit[j] = lg;
-    mx = fmaxf(mx, lg);
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dot += qa[i] * (k1[u][i] * cs[u][i].x - k2[u][i] * cs[u][i].y) +
+               qb[i] * (k2[u][i] * cs[u][i].x + k1[u][i] * cs[u][i].y);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+      const int j = j0 + u;
+      if (j < n_keys) {
+        const float lg = ok[u] ? dot * sm_scale : -INFINITY;
+        if (lane == 0) logit[j] = lg;
+        mx = fmaxf(mx, lg);
+      }
+    }
   }
   red[threadIdx.x] = mx;
   __syncthreads();
@@ -749,19 +782,45 @@ __global__ __launch_bounds__(AT_VEC_THREADS) void attn_vec_kernel(
     __syncthreads();
   }
   const float den = red[0];
+  // value sum: wave w takes keys w, w + NW, ...; lanes over d (at most four
+  // elements each), four keys' loads in flight
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = wave; j0 < n_keys; j0 += NW * KU) {
+    float pv[KU], vv[KU][4];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int j = j0 + NW * u;
+      const bool in = j < n_keys;
+      pv[u] = in ? logit[j] : 0.f;
+      const typename E::T* vp = v_loc;
+      if (in)
+        vp = j < ctxl ? v_ctx + (ctx_src_row(int64_t(b) * max_ctx + j, ctx_row, ctx_rows) * Hkv + g) * d
+                      : v_loc + ((int64_t(b) * L_loc + (j - ctxl)) * Hkv + g) * d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        vv[u][i] = (pv[u] != 0.f && e < d) ? E::load(vp, e) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += pv[u] * vv[u][i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    if (e < d) part[wave * d + e] = acc[i];
+  }
+  __syncthreads();
   float* op = out + ((int64_t(b) * T + t) * Hq + hq) * d;
   if (lse && threadIdx.x == 0)
     lse[(int64_t(b) * T + t) * Hq + hq] = den > 0.f ? (gmax + logf(den)) * 1.4426950408889634f : -INFINITY;
   for (int e = threadIdx.x; e < d; e += AT_VEC_THREADS) {
-    float acc = 0.f;
-    for (int j = 0; j < n_keys; ++j) {
-      const float p = logit[j];
-      if (p == 0.f) continue;
-      const typename E::T* vp = j < ctxl ? v_ctx + (ctx_src_row(int64_t(b) * max_ctx + j, ctx_row, ctx_rows) * Hkv + g) * d
-                                         : v_loc + ((int64_t(b) * L_loc + (j - ctxl)) * Hkv + g) * d;
-      acc += p * E::load(vp, e);
-    }
-    op[e] = acc / den;
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) a += part[w * d + e];
+    op[e] = a / den;
   }
 }
 
@@ -955,7 +1014,7 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
     MSA_LAUNCH_CHECK();
     return MSA_OK;
   }
-  const size_t smem = (size_t(d) + AT_VEC_THREADS + size_t(max_ctx) + L_loc) * sizeof(float);
+  const size_t smem = (size_t(d) * (1 + AT_VEC_THREADS / 64) + AT_VEC_THREADS + size_t(max_ctx) + L_loc) * sizeof(float);
   const dim3 grid(unsigned(int64_t(B) * T * Hq)), block(AT_VEC_THREADS);
   if (dtype == MSA_BF16)
     hipLaunchKernelGGL(attn_vec_kernel<MSA_BF16>, grid, block, smem, s, static_cast<const uint16_t*>(q), B, T, Hq, Hkv,

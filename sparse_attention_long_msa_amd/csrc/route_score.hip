@@ -397,9 +397,39 @@ __global__ __launch_bounds__(RV_THREADS) void route_score_vec_kernel(
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int j0 = blockIdx.y * CB;
   const int nc = min(CB, J - j0);
-  for (int i = threadIdx.x; i < CB * E; i += RV_THREADS) {
-    const int jj = i / E;
-    qcol[i] = jj < nc ? qs[int64_t(j0 + jj) * E + (i % E)] : 0.f;
+  // the block's columns are consecutive rows of q', so the block is one
+  // contiguous span; columns past J are zero.  Eight loads in flight per lane
+  // (a serial staging loop is one L2 round trip per element).
+  {
+    const float* src = qs + int64_t(j0) * E;
+    const int n_valid = nc * E, n_all = CB * E;
+    if ((E & 3) == 0) {
+      float4* dst4 = reinterpret_cast<float4*>(qcol);
+      const float4* src4 = reinterpret_cast<const float4*>(src);
+      for (int i0 = threadIdx.x; i0 < n_all / 4; i0 += RV_THREADS * 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * RV_THREADS;
+          v[u] = i < n_valid / 4 ? src4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u * RV_THREADS < n_all / 4) dst4[i0 + u * RV_THREADS] = v[u];
+      }
+    } else {
+      for (int i0 = threadIdx.x; i0 < n_all; i0 += RV_THREADS * 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * RV_THREADS;
+          v[u] = i < n_valid ? src[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u * RV_THREADS < n_all) qcol[i0 + u * RV_THREADS] = v[u];
+      }
+    }
   }
   __syncthreads();
   const int64_t stride = int64_t(gridDim.x) * (RV_THREADS / 64);

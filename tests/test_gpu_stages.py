@@ -481,6 +481,31 @@ def _attn_case(seed, B, T, Hq, Hkv, d, L_loc, ctx_lens, bf16, max_ctx):
     return q, kl, vl, kc, vc, cp, cl
 
 
+@pytest.mark.parametrize("bf16,Hq,Hkv,d,B,T,L_loc,ctx", [
+    (False, 4, 2, 2, 2, 3, 5, [0, 9]),              # smallest head, empty context
+    (True, 6, 2, 64, 3, 2, 40, [17, 0, 130]),       # off the MFMA path: d = 64, group of 3
+    (False, 8, 8, 96, 1, 16, 16, [700]),            # d = 96 (pairs not a multiple of 64)
+    (True, 4, 1, 256, 2, 1, 300, [2100, 5]),        # largest head, two pairs per lane
+    (False, 32, 8, 128, 1, 7, 7, [4000]),           # key count off the four-key step
+])
+def test_sparse_attention_vector_path(bf16, Hq, Hkv, d, B, T, L_loc, ctx):
+    """The vector attention path (float32, or head shapes off the MFMA path)
+    against the oracle, over head sizes from 2 to 256 and group sizes 1-4."""
+    max_ctx = max(max(ctx), 1)
+    qpo = 16
+    q, kl, vl, kc, vc, cp, cl = _attn_case(90 + d, B, T, Hq, Hkv, d, L_loc, ctx, bf16, max_ctx)
+    out = M.msa_sparse_attn(to_dev(q, bf16), to_dev(kc, bf16), to_dev(vc, bf16),
+                            torch.from_numpy(cp).to(dev()), torch.from_numpy(cl).to(dev()), to_dev(kl, bf16),
+                            to_dev(vl, bf16), qpo)
+    got = host(out)
+    sm = 1.0 / math.sqrt(d)
+    for b in range(B):
+        n = int(cl[b])
+        ref = O.attend_one(q[b], kc[b, :n], vc[b, :n], cp[b, :n], kl[b], vl[b], qpo, 1e6, sm)
+        e = np.abs(got[b] - ref).max()
+        assert e <= ATOL_ATTN["bf16" if bf16 else "f32"], f"b={b}: max-abs {e}"
+
+
 @pytest.mark.parametrize("bf16", [True, False])
 @pytest.mark.parametrize("B,T,L_loc,ctx", [(1, 16, 16, [32]), (1, 64, 4096, [128]), (32, 1, 8192, None),
                                            (2, 3, 50, [0, 77]), (1, 128, 300, [1000]), (4, 1, 1, [5, 0, 31, 64])])
