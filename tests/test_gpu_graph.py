@@ -73,3 +73,43 @@ def test_step_graph_replays_equal_the_eager_step(B, T, L_loc, k):
         check_scores(host(eager[l]["doc_score"]), ref["doc_score"], RTOL_SCORE["bf16"], k)
         check_ids(eager[l]["ids"].cpu().numpy(), ref["doc_score"], k)
         assert np.abs(host(eager[l]["out"]) - ref["out"]).max() <= ATOL_ATTN["bf16"]
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg5", "cfg4"])
+def test_step_graph_full_size(name):
+    """The bench's graph-replayed step at the full presets (two routed layers of
+    the 1M-token, batched-decode and 100M-token workloads, context read in
+    place): every replay equals the eager step bit for bit.  The eager step is
+    checked against the oracle by the preset parity tests."""
+    from synth import configs
+    from tests.preset_run import GpuLayer, HostLayer
+    p = getattr(configs, name)()
+    layers = [GpuLayer(p, l, HostLayer(p, l), indexed=True) for l in (0, 1)]
+
+    def step():
+        for gl in layers:
+            gl.runner.run(gl.qr, gl.store[synth.T_KR], gl.cd, gl.co_d, gl.kb, gl.vb, gl.q, gl.kl, gl.vl)
+
+    names = ("doc_score", "ids", "vals", "ctx_row", "ctx_pos", "ctx_len", "out")
+    step()
+    torch.cuda.synchronize()
+    eager = [{n: getattr(gl.runner, n).clone() for n in names} for gl in layers]
+    g = M.StepGraph(step)
+    for rep in range(2):
+        for gl in layers:
+            for n in names:
+                t = getattr(gl.runner, n)
+                t.fill_(-3 if t.dtype == torch.int32 else float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l, gl in enumerate(layers):
+            r = gl.runner
+            for n in ("doc_score", "ids", "vals", "ctx_len", "out"):
+                assert torch.equal(getattr(r, n), eager[l][n]), f"{name} replay {rep}, layer {l}: {n}"
+            for b in range(p.B):
+                n_b = int(eager[l]["ctx_len"][b])
+                for n in ("ctx_row", "ctx_pos"):
+                    assert torch.equal(getattr(r, n)[b, :n_b], eager[l][n][b, :n_b]), f"{name} replay {rep}: {n}"
+    del g, layers
+    torch.cuda.empty_cache()
