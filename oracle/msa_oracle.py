@@ -200,6 +200,31 @@ def topk(doc_score: np.ndarray, k: int):
     return ids, vals
 
 
+def topk_merge(vals: np.ndarray, ids: np.ndarray, id_offset: np.ndarray, k: int):
+    """Memory Parallel's global reduce of per-shard top-k lists ([P2] Overall
+    Design > Inference Pipeline: the routing keys are sharded over GPUs, each
+    scores its shard locally and a global reduce follows; [P1] Memory Parallel
+    推理).  vals [G, B, k_in] scores and ids [G, B, k_in]
+    shard-local document ids (-1 or a NaN score: an empty slot) of G shards
+    whose documents start at global id id_offset[g].  The result is the k best
+    valid entries per query by (score desc, global id asc) (R9), as
+    (ids int32 [B, k], vals float64 [B, k]); when fewer than k are valid the
+    trailing ids are -1 and their values NaN."""
+    vals = np.asarray(vals, dtype=np.float64)
+    ids = np.asarray(ids, dtype=np.int64)
+    G, B, k_in = vals.shape
+    out_ids = np.full((B, k), -1, dtype=np.int32)
+    out_vals = np.full((B, k), np.nan)
+    for b in range(B):
+        cand = [(vals[g, b, j], int(ids[g, b, j]) + int(id_offset[g]))
+                for g in range(G) for j in range(k_in) if ids[g, b, j] >= 0 and vals[g, b, j] == vals[g, b, j]]
+        cand.sort(key=lambda t: (-t[0], t[1]))
+        for r, (v, i) in enumerate(cand[:k]):
+            out_ids[b, r] = i
+            out_vals[b, r] = v
+    return out_ids, out_vals
+
+
 def gather(ids_b: np.ndarray, chunk_off: np.ndarray, k_bar: np.ndarray, v_bar: np.ndarray):
     """Context of one query: the selected documents' pooled K/V in rank order,
     each document's chunks in order (R17), with each entry's position inside

@@ -227,6 +227,57 @@ def test_topk_rejects_bad_k():
         O.topk(np.zeros((1, 4)), 0)
 
 
+
+# ---------------------------------------------------------------- Memory Parallel merge
+
+def _shard_bounds(r, D, G):
+    """G contiguous document ranges covering [0, D) (some may be empty)."""
+    cuts = np.sort(r.integers(0, D + 1, size=G - 1))
+    return np.concatenate([[0], cuts, [D]]).astype(np.int64)
+
+
+def test_topk_merge_of_shards_is_the_global_topk():
+    """Per-shard top-k lists merged by (score desc, global id asc) give the
+    top-k of the whole memory, ties included, whatever the shard boundaries;
+    a shard with fewer than k documents pads with -1 / NaN."""
+    r = rng(31)
+    for trial in range(40):
+        D = int(r.integers(1, 400))
+        k = int(r.integers(1, min(D, 64) + 1))
+        G = int(r.integers(1, 7))
+        B = 2
+        s = np.round(r.normal(size=(B, D)), 1)          # many exact ties, also across shards
+        s[0, r.integers(0, D, size=D // 4)] = -np.inf
+        bounds = _shard_bounds(r, D, G)
+        vals = np.full((G, B, k), np.nan)
+        ids = np.full((G, B, k), -1, dtype=np.int32)
+        for g in range(G):
+            lo, hi = int(bounds[g]), int(bounds[g + 1])
+            if hi == lo:
+                continue
+            kk = min(k, hi - lo)
+            gi, gv = O.topk(s[:, lo:hi], kk)
+            ids[g, :, :kk], vals[g, :, :kk] = gi, gv
+        mi, mv = O.topk_merge(vals, ids, bounds[:-1], k)
+        wi, wv = O.topk(s, k)
+        np.testing.assert_array_equal(mi, wi)
+        np.testing.assert_array_equal(mv, wv)
+
+
+def test_topk_merge_worked_cases():
+    # equal scores in two shards: the smaller global id ranks first
+    vals = np.array([[[0.5, 0.25]], [[0.5, 0.75]]])
+    ids = np.array([[[3, 1]], [[0, 2]]], dtype=np.int32)
+    mi, mv = O.topk_merge(vals, ids, np.array([0, 10]), 3)
+    assert mi[0].tolist() == [12, 3, 10]
+    assert mv[0].tolist() == [0.75, 0.5, 0.5]
+    # empty slots (id -1 or NaN score) never rank; too few entries pad with -1 / NaN
+    vals = np.array([[[1.0, np.nan]], [[2.0, 3.0]]])
+    ids = np.array([[[0, 5]], [[-1, 4]]], dtype=np.int32)
+    mi, mv = O.topk_merge(vals, ids, np.array([0, 100]), 3)
+    assert mi[0].tolist() == [104, 0, -1]
+    assert mv[0, :2].tolist() == [3.0, 1.0] and np.isnan(mv[0, 2])
+
 # ---------------------------------------------------------------- gather (P9)
 
 def test_gather_is_index_copy():
