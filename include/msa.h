@@ -266,6 +266,28 @@ int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids,
              size_t ws_bytes, void* stream);
 
 /*
+ * msa_topk_merge - Memory Parallel's global reduce (README, Overall Design >
+ * Inference Pipeline: the routing keys are sharded over GPUs, each scores its
+ * shard and a global reduce follows; paper note 核心方法 > Memory Parallel 推理).
+ * G shards each ran msa_route_score + msa_topk over a contiguous range of the
+ * documents with shard-local ids; for each query b the result is the k best of
+ * their entries by (score descending, global id ascending), which equals
+ * msa_topk over the whole memory when every shard kept at least min(k, its
+ * documents) entries.
+ *   vals      [G, B, k_in] float32 device, ids [G, B, k_in] int32 device:
+ *              shard g's lists; a slot with id < 0 or a NaN score is empty
+ *   id_offset [G] int64 device: the global id of shard g's first document
+ *              (global ids must stay below 2^31)
+ *   ids_out   [B, k] int32 output (global ids), vals_out [B, k] float32 output;
+ *              when fewer than k entries are valid the trailing ids are -1
+ *              (their vals NaN)
+ * Errors: INVALID_ARG (NULL, non-positive sizes, k > G * k_in),
+ * UNSUPPORTED (k > 64, G * k_in > 2^24).
+ */
+int msa_topk_merge(const float* vals, const int32_t* ids, const int64_t* id_offset, int G, int B, int k_in, int k,
+                   int32_t* ids_out, float* vals_out, void* stream);
+
+/*
  * msa_exclude_docs - Memory Interleave (paper note 核心方法 > Memory
  * Interleave; README, Key Contributions and Fig. 3: rounds of retrieval, each
  * adding documents to the context).  Marks the documents fetched in earlier

@@ -38,6 +38,7 @@ _SIGS = {
     "msa_segment_max": (_I, [_P, _I, _L, _P, _L, _P, _P]),
     "msa_topk_workspace": (_S, [_I, _L, _I]),
     "msa_topk": (_I, [_P, _I, _L, _I, _P, _P, _P, _S, _P]),
+    "msa_topk_merge": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "msa_gather_kv": (_I, [_I, _P, _I, _I, _P, _P, _L, _I, _P, _P, _L, _I, _I, _I, _I,
                            _P, _P, _P, _P, _P, _P, _P]),
     "msa_context_index": (_I, [_P, _I, _I, _P, _L, _I, _L, _I, _P, _P, _P, _P]),
@@ -318,6 +319,25 @@ def msa_topk(doc_score, k, ids=None, vals=None, ws=None, stream=None):
                                     _stream(stream)))
     return ids, vals
 
+
+
+def msa_topk_merge(vals, ids, id_offset, k, ids_out=None, vals_out=None, stream=None):
+    """Global top-k of G shards' top-k lists.  vals [G, B, k_in] float32 and
+    ids [G, B, k_in] int32 (shard-local ids, -1 for an empty slot), id_offset
+    [G] int64 (each shard's first global id), all on the device."""
+    _dev(vals, "vals", _F32, (None, None, None))
+    G, B, k_in = vals.shape
+    _dev(ids, "ids", _I32, (G, B, k_in))
+    _dev(id_offset, "id_offset", _I64, (G,))
+    if ids_out is None:
+        ids_out = torch.empty((B, k), dtype=torch.int32, device=vals.device)
+    if vals_out is None:
+        vals_out = torch.empty((B, k), dtype=torch.float32, device=vals.device)
+    _dev(ids_out, "ids_out", _I32, (B, k))
+    _dev(vals_out, "vals_out", _F32, (B, k))
+    _check("msa_topk_merge", lib.msa_topk_merge(_ptr(vals), _ptr(ids), _ptr(id_offset), G, B, k_in, k, _ptr(ids_out),
+                                                _ptr(vals_out), _stream(stream)))
+    return ids_out, vals_out
 
 def msa_gather_kv(ids, chunk_off, k_bar, v_bar, max_doc_chunks, max_ctx, src_mode=MSA_SRC_DEVICE,
                   chunk_off_h=None, k_ctx=None, v_ctx=None, ctx_pos=None, ctx_len=None, ids_h=None,

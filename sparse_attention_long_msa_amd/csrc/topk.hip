@@ -235,6 +235,40 @@ __global__ __launch_bounds__(64 * W) void topk_wave_kernel(const float* __restri
   }
 }
 
+// Memory Parallel's global reduce (README, Overall Design > Inference
+// Pipeline: sharded routing keys, local scoring, then a global reduce): the
+// per-shard top-k lists of G shards merged into the k best by (score desc,
+// global id asc).  One wave per query walks the G * k_in candidates 64 at a
+// time, keeping its 64 smallest keys sorted across the lanes (the first batch
+// is sorted, later batches are merged in when one of them beats the k-th key).
+// A slot with id < 0 or a NaN score is empty.
+__global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict__ vals,
+                                                        const int32_t* __restrict__ ids,
+                                                        const int64_t* __restrict__ id_offset, int G, int B,
+                                                        int k_in, int k, int32_t* __restrict__ ids_out,
+                                                        float* __restrict__ vals_out) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int64_t n = int64_t(G) * k_in;
+  constexpr uint64_t SENT = ~uint64_t(0);
+  uint64_t best = SENT;
+  for (int64_t i0 = 0; i0 < n; i0 += 64) {   // uniform in the wave
+    const int64_t i = i0 + lane;
+    uint64_t key = SENT;
+    if (i < n) {
+      const int g = int(i / k_in), j = int(i % k_in);
+      const int64_t e = (int64_t(g) * B + b) * k_in + j;
+      const int32_t id = ids[e];
+      const float v = vals[e];
+      if (id >= 0 && v == v) key = score_key(v, uint32_t(int64_t(id) + id_offset[g]));
+    }
+    best = i0 == 0 ? wave_sort64(key, lane) : wave_insert(best, key, lane, k);
+  }
+  if (lane < k) {
+    ids_out[int64_t(b) * k + lane] = int32_t(uint32_t(best));
+    vals_out[int64_t(b) * k + lane] = order_key_float(~uint32_t(best >> 32));
+  }
+}
+
 // Candidate counts of the wave passes: inputs > one workgroup's capacity are
 // reduced by non-final passes (every workgroup keeps k of its 2048 inputs;
 // idle waves of the last workgroup contribute sentinel keys).
@@ -392,6 +426,20 @@ extern "C" int msa_exclude_docs(float* doc_score, int B, int64_t n_docs, const i
   if (n == 0) return MSA_OK;
   hipLaunchKernelGGL(exclude_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, as_stream(stream), doc_score, B,
                      n_docs, ids, k, n);
+  MSA_LAUNCH_CHECK();
+  return MSA_OK;
+}
+
+extern "C" int msa_topk_merge(const float* vals, const int32_t* ids, const int64_t* id_offset, int G, int B, int k_in,
+                              int k, int32_t* ids_out, float* vals_out, void* stream) {
+  using namespace msa;
+  MSA_REQUIRE(vals && ids && id_offset && ids_out && vals_out, MSA_ERR_INVALID_ARG, "msa_topk_merge: NULL pointer");
+  MSA_REQUIRE(G >= 1 && B >= 1 && k_in >= 1 && k >= 1, MSA_ERR_INVALID_ARG, "msa_topk_merge: non-positive size");
+  MSA_REQUIRE(int64_t(G) * k_in >= k, MSA_ERR_INVALID_ARG, "msa_topk_merge: k > G * k_in");
+  MSA_REQUIRE(k <= 64, MSA_ERR_UNSUPPORTED, "msa_topk_merge: k > 64");
+  MSA_REQUIRE(int64_t(G) * k_in <= (int64_t(1) << 24), MSA_ERR_UNSUPPORTED, "msa_topk_merge: G * k_in > 2^24");
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(unsigned(B)), dim3(64), 0, as_stream(stream), vals, ids, id_offset, G, B,
+                     k_in, k, ids_out, vals_out);
   MSA_LAUNCH_CHECK();
   return MSA_OK;
 }

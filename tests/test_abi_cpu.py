@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.msa_abi_version() == 9
+    assert M.msa_abi_version() == 10
     assert M.lib.msa_status_string(0).decode() == "ok"
     assert "workspace" in M.lib.msa_status_string(3).decode()
 
@@ -80,6 +80,18 @@ def test_topk_validation():
     assert L.msa_topk(P, 1, 100000, 16, P, P, P, need - 1, None) == 3
     assert L.msa_topk_workspace(1, 4096, 16) == 0      # one slice: no workspace
 
+
+
+def test_topk_merge_validation():
+    L = M.lib
+    assert L.msa_topk_merge(P, P, P, 2, 1, 8, 0, P, P, None) == 1          # k < 1
+    assert L.msa_topk_merge(P, P, P, 2, 1, 8, 17, P, P, None) == 1         # k > G * k_in
+    assert L.msa_topk_merge(P, P, P, 0, 1, 8, 4, P, P, None) == 1          # no shard
+    assert L.msa_topk_merge(None, P, P, 2, 1, 8, 4, P, P, None) == 1       # NULL
+    assert L.msa_topk_merge(P, P, P, 4, 1, 32, 65, P, P, None) == 2        # k > 64
+    with pytest.raises(ValueError, match="vals: must be in device memory"):
+        M.msa_topk_merge(torch.zeros((2, 1, 4)), torch.zeros((2, 1, 4), dtype=torch.int32),
+                         torch.zeros(2, dtype=torch.int64), 4)
 
 def test_gather_rejects_small_context_and_bad_mode():
     L = M.lib
