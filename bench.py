@@ -20,6 +20,9 @@ are not part of the timed region).
 The default run prints one JSON line: the 100M-token step with the content
 K/V in HBM (the line's value), then, in the same line,
   ceiling      the streaming-read rate over the same bytes (msa_stream_read),
+  memory_parallel  the calls one GPU of a 2-, 4- or 8-GPU Memory Parallel
+               step makes (routing and top-k over its shard of the store) and
+               the global reduce of the shards' lists (msa_topk_merge),
   host_tier    the same step with the content K/V in pinned host memory,
                fetched per layer by the zero-copy gather kernel (mapped) and
                by hipMemcpyAsync per document (memcpy),
@@ -60,6 +63,8 @@ def parse():
                     help="Memory Interleave rounds per layer (> 1: route, skip the fetched documents, select and "
                          "append, rounds times, then attend; content K/V in HBM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-memory-parallel", action="store_true",
+                    help="skip the Memory Parallel leg (per-shard routing and top-k at 2, 4 and 8 shards, merge)")
     ap.add_argument("--cpu-sample-chunks", type=int, default=None,
                     help="routing-key chunks of the oracle's sample (default: 1048576 at pooled level, "
                          "262144 for token-level memories, whose sample the oracle also pools)")
@@ -112,6 +117,8 @@ def main():
     res["needle_recall_layer0"] = recall
     if not args.no_ceiling:
         res["ceiling"] = pb.ceiling()
+    if p.name == "cfg4" and args.rounds == 1 and not args.no_memory_parallel:
+        res["memory_parallel"] = pb.memory_parallel()
     if p.name == "cfg4" and args.rounds == 1 and not args.no_host_tier:
         res["host_tier"] = pb.host_tier(args.steps, args.warmup)
     pb.release()
@@ -431,6 +438,73 @@ class PresetBench:
                 "bytes_per_read": nbytes, "avg_read_ms": round(t, 4), "ceiling_GBps": round(gbps, 1),
                 "ceiling_frac_of_8TBps": round(gbps / 8000, 4),
                 "route_store_GBps_over_ceiling": round(route_gbps / gbps, 4)}
+
+    def memory_parallel(self, shard_counts=(2, 4, 8)):
+        """The pages' Memory Parallel as far as one GPU shows it: the store cut
+        into G contiguous document shards, and the calls one GPU of G makes per
+        layer at its real shape (routing score and top-k over its shard), then
+        the global reduce of the G lists (msa_topk_merge).  Event-timed over
+        the layers; the all-gather of the G * k keys between GPUs is not
+        measured here (one GPU).  Each leg is captured once and replayed as a
+        HIP graph."""
+        torch, p, M = self.torch, self.p, self.M
+        co = p.chunk_off
+        ok = np.flatnonzero(co[:-1] % 16 == 0)   # shards start on 16-chunk groups of the tiled store
+        k, B = p.k, p.B
+        out = {"note": "per-GPU calls of a G-GPU Memory Parallel step, timed on one GPU; the all-gather of "
+                       "G x k (score, id) keys per query between GPUs is not measured"}
+        for G in shard_counts:
+            cuts = [0] + [int(ok[np.searchsorted(ok, g * p.n_docs // G)]) for g in range(1, G)] + [p.n_docs]
+            lo, hi = cuts[0], cuts[1]
+            c0, c1 = int(co[lo]), int(co[hi])
+            nc, nd = c1 - c0, hi - lo
+            co_g = torch.from_numpy(co[lo:hi + 1] - c0).to(self.dev)
+            cd_g = M.msa_chunk_doc_map(co_g, nc)
+            score = torch.empty((B, nd), dtype=torch.float32, device=self.dev)
+            ids = torch.empty((B, k), dtype=torch.int32, device=self.dev)
+            vals = torch.empty((B, k), dtype=torch.float32, device=self.dev)
+            tk_ws = torch.empty(max(M.msa_topk_workspace(B, nd, k), 1), dtype=torch.uint8, device=self.dev)
+            lay = self.kr_layout
+            shards = [self.store[l][c0:c0 + M.padded_chunks(nc, lay)] for l in range(self.layers)]
+
+            def select():
+                for l in range(self.layers):
+                    M.msa_route_score(self.qr[l], shards[l], cd_g, nd, doc_score=score, layout=lay)
+                    M.msa_topk(score, k, ids=ids, vals=vals, ws=tk_ws)
+            # replayed as HIP graphs, so that the host's issue rate does not
+            # bound the small per-shard launches
+            g_sel = M.StepGraph(select)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g_sel.replay()
+            e0.record()
+            g_sel.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            sel_us = e0.elapsed_time(e1) * 1e3 / self.layers
+            gv = vals.unsqueeze(0).expand(G, B, k).contiguous()
+            gi = ids.unsqueeze(0).expand(G, B, k).contiguous()
+            off = torch.tensor(cuts[:-1], dtype=torch.int64, device=self.dev)
+            mi = torch.empty((B, k), dtype=torch.int32, device=self.dev)
+            mv = torch.empty((B, k), dtype=torch.float32, device=self.dev)
+
+            def merge():
+                for _ in range(self.layers):
+                    M.msa_topk_merge(gv, gi, off, k, ids_out=mi, vals_out=mv)
+            g_m = M.StepGraph(merge)
+            g_m.replay()
+            e0.record()
+            g_m.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            merge_us = e0.elapsed_time(e1) * 1e3 / self.layers
+            shard_bytes = nc * p.H * p.d * self.esz
+            out[f"G{G}"] = {"shard_docs": nd, "shard_chunks": nc, "shard_store_GB": round(shard_bytes / 1e9, 3),
+                            "route_and_topk_us_per_layer": round(sel_us, 2),
+                            "shard_routing_GBps": round(shard_bytes / (sel_us * 1e-6) / 1e9, 1),
+                            "merge_us_per_layer": round(merge_us, 2),
+                            "select_ms_per_step": round((sel_us + merge_us) * self.layers / 1e3, 4)}
+            del shards, g_sel, g_m
+        return out
 
     def host_tier(self, steps, warmup):
         """The pages' tier: content K/V in pinned host memory, the selected
