@@ -102,7 +102,8 @@ def test_pool_encode_head_shapes(bf16, layout, H, d):
 
 
 @pytest.mark.parametrize("bf16,layout", [(True, 1), (True, 0), (False, 0)])
-@pytest.mark.parametrize("B,T", [(1, 64), (1, 16), (1, 1), (2, 32), (32, 1), (1, 128), (3, 7), (1, 80)])
+@pytest.mark.parametrize("B,T", [(1, 64), (1, 16), (1, 1), (2, 32), (32, 1), (1, 128), (3, 7), (1, 80), (4, 64),
+                                 (100, 1)])
 def test_route_score(bf16, layout, B, T):
     H, d = 8, 128
     lens = ragged_lengths(3 + T, 180, 1, 1500, n_empty=5)
