@@ -17,15 +17,18 @@ breakdown comes from up to 3 further steps with events between all stages
 (each event record idles the device for a few microseconds, so these steps
 are not part of the timed region).
 
-The default run prints one JSON line: the 100M-token step with the content
-K/V in HBM (the line's value), then, in the same line,
+The default run prints one JSON line: the 100M-token step as the workload
+states it, with the content K/V in pinned host memory and the selected
+documents fetched per layer by the zero-copy gather kernel (the line's value;
+the box pins 8 of the 18 layers' K/V, which the layers cycle over), then, in
+the same line,
+  hbm_tier     the same step with the content K/V in HBM, read in place,
   ceiling      the streaming-read rate over the same bytes (msa_stream_read),
   memory_parallel  the calls one GPU of a 2-, 4- or 8-GPU Memory Parallel
                step makes (routing and top-k over its shard of the store) and
                the global reduce of the shards' lists (msa_topk_merge),
-  host_tier    the same step with the content K/V in pinned host memory,
-               fetched per layer by the zero-copy gather kernel (mapped) and
-               by hipMemcpyAsync per document (memcpy),
+  host_tier    the pinned layers, and the step with the fetch done by
+               hipMemcpyAsync per document (memcpy) instead,
   cpu_baseline the float64 oracle's routing on a bounded sample,
   per_config   warm and cold lines of the four smaller presets with the
                oracle's routing and attention times.
@@ -112,15 +115,37 @@ def main():
     assembly = args.hbm_assembly if args.rounds == 1 else "index"
     pb.make_runner("hbm", indexed=assembly == "index")
     recall = pb.needle_recall()
-    res = pb.headline(args.steps, args.warmup)
-    res["config"]["gather"] = f"hbm-{assembly}"
+    hbm = pb.headline(args.steps, args.warmup)
+    hbm["config"]["gather"] = f"hbm-{assembly}"
+    res = hbm
+    # the 100M-token workload keeps the content K/V in pinned host memory and
+    # fetches the selected documents per layer: that step leads the line, the
+    # same step with the content K/V in HBM follows it
+    pinned = pb.pin_host() if p.name == "cfg4" and args.rounds == 1 and not args.no_host_tier else None
+    if pinned is not None:
+        kv, desc = pinned
+        pb.make_runner("host", indexed=False, src_mode=pb.M.MSA_SRC_HOST_MAPPED)
+        res = pb.headline(args.steps, args.warmup, kv=kv,
+                          tier=f"host-mapped ({desc['pinned_layers']} of {pb.layers} layers' K/V pinned, cycled)")
+        res["config"]["gather"] = "host-mapped gather kernel"
+        res["hbm_tier"] = {k: hbm[k] for k in ("value", "ms_per_step", "route_attn_us_per_query",
+                                              "ms_per_step_eager_launches", "ms_per_step_graph_replay",
+                                              "stage_ms_per_step", "attention_GBps")}
+        res["hbm_tier"]["config"] = hbm["config"]
+        pb.make_runner("hbm", indexed=assembly == "index")
+        res["roofline"] = hbm["roofline"]
     res["needle_recall_layer0"] = recall
     if not args.no_ceiling:
         res["ceiling"] = pb.ceiling()
     if p.name == "cfg4" and args.rounds == 1 and not args.no_memory_parallel:
         res["memory_parallel"] = pb.memory_parallel()
-    if p.name == "cfg4" and args.rounds == 1 and not args.no_host_tier:
-        res["host_tier"] = pb.host_tier(args.steps, args.warmup)
+    if pinned is not None:
+        res["host_tier"] = pb.host_tier(args.steps, args.warmup, pinned, modes=("memcpy",))
+        res["host_tier"]["mapped"] = {"route_attn_us_per_query": res["route_attn_us_per_query"],
+                                      "ms_per_step": res["ms_per_step"],
+                                      "fetch_ms_per_step": res["stage_ms_per_step"].get("fetch"),
+                                      "note": "the line's own step"}
+        pb.unpin_host()
     pb.release()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, pb.layers, args.cpu_sample_chunks)
@@ -348,15 +373,17 @@ class PresetBench:
         ctx_len = self.runner.ctx_len.cpu().numpy().astype(np.int64)
         return int((ctx_len + p.L_loc).sum()) * p.H * p.d * 2 * self.esz + p.B * p.T * p.Hq * p.d * (self.esz + 4)
 
-    def headline(self, steps, warmup):
+    def headline(self, steps, warmup, kv=None, tier="hbm"):
         """The JSON line: whole-step throughput of the routing-key scan, the
-        stage breakdown and the roofline of the routing-score launch."""
+        stage breakdown and the roofline of the routing-score launch.  kv(l):
+        the layer's content stores when they are not the HBM ones (tier names
+        where they are)."""
         p, layers = self.p, self.layers
-        ms_eager, route_ms = self.timed(steps, warmup)
-        ms_graph = self.timed(steps, warmup, route_events=False, graph=True)[0] if self.graph else float("inf")
+        ms_eager, route_ms = self.timed(steps, warmup, kv=kv)
+        ms_graph = self.timed(steps, warmup, kv=kv, route_events=False, graph=True)[0] if self.graph else float("inf")
         launch = "hip-graph replay" if ms_graph < ms_eager else "eager launches"
         ms_per_step = min(ms_eager, ms_graph)
-        stage = self.stages(min(steps, 3))
+        stage = self.stages(min(steps, 3), kv=kv)
         H, d, N, D = p.H, p.d, p.n_chunks, p.n_docs
         store_bytes = N * H * d * self.esz                     # per layer
         step_bytes = store_bytes * layers * self.rounds        # every round scans the layer's store
@@ -376,8 +403,8 @@ class PresetBench:
         if self.rounds == 1:
             stages = ({"route_score": round(stage[0], 4), "topk_and_context_index": round(stage[1], 4),
                        "attention": round(stage[3], 4)} if self.runner.indexed else
-                      {"route_score": round(stage[0], 4), "topk": round(stage[1], 4), "gather": round(stage[2], 4),
-                       "attention": round(stage[3], 4)})
+                      {"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
+                       ("fetch" if kv is not None else "gather"): round(stage[2], 4), "attention": round(stage[3], 4)})
         else:
             stages = {"rounds_route_topk_append": round(stage[0] + stage[1] + stage[2], 4),
                       "attention": round(stage[3], 4)}
@@ -396,7 +423,7 @@ class PresetBench:
             "dtype": "bf16" if p.bf16 else "f32",
             "data": "synthetic (seeded counter-based generator; planted needles)",
             "config": {"workload": workload, "global_batch": p.B, "seq_len": p.T, "parallelism": "single GPU",
-                       "kv_tier": "hbm", "rounds": self.rounds, "step_launch": launch},
+                       "kv_tier": tier, "rounds": self.rounds, "step_launch": launch},
             "route_attn_us_per_query": round(ms_per_step * 1e3 / p.B, 1),
             "ms_per_step_eager_launches": round(ms_eager, 4),
             "ms_per_step_graph_replay": round(ms_graph, 4) if self.graph else None,
@@ -506,14 +533,12 @@ class PresetBench:
             del shards, g_sel, g_m
         return out
 
-    def host_tier(self, steps, warmup):
-        """The pages' tier: content K/V in pinned host memory, the selected
-        documents fetched over the host link per layer.  The box pins only
-        part of the 115 GB, so as many layers as fit are pinned and the 18
-        layers cycle over them (the fetch cost does not depend on the values).
-        Timed for the zero-copy gather kernel (mapped) and for hipMemcpyAsync
-        per document on a side stream (memcpy)."""
-        torch, p, M = self.torch, self.p, self.M
+    def pin_host(self):
+        """The pages' tier: content K/V in pinned host memory.  The box pins
+        only part of the 115 GB, so as many layers as fit are pinned and the
+        18 layers cycle over them (the fetch cost does not depend on the
+        values).  Returns kv(l) and a description, or None."""
+        torch, p = self.torch, self.p
         t0 = time.time()
         hk, hv = [], []
         try:
@@ -529,14 +554,30 @@ class PresetBench:
         torch.cuda.synchronize()
         n_pin = len(hk)
         if n_pin == 0:
-            return {"error": "no pinned host memory available"}
+            return None
         pinned_gb = 2 * n_pin * p.n_chunks * p.H * p.d * self.esz / 1e9
         log(f"host tier: {n_pin} layers pinned ({pinned_gb:.1f} GB) in {time.time() - t0:.1f} s")
-        out = {"pinned_layers": n_pin, "pinned_GB": round(pinned_gb, 1), "layers_cycled": self.layers,
-               "note": f"layer l reads pinned layer l % {n_pin}"}
+        self.pinned = (hk, hv)
+        desc = {"pinned_layers": n_pin, "pinned_GB": round(pinned_gb, 1), "layers_cycled": self.layers,
+                "note": f"layer l reads pinned layer l % {n_pin}"}
+        return (lambda l: (hk[l % n_pin], hv[l % n_pin])), desc
+
+    def unpin_host(self):
+        self.pinned = None
+        if hasattr(self.torch._C, "_host_emptyCache"):
+            self.torch._C._host_emptyCache()    # hand the pinned pages back
+
+    def host_tier(self, steps, warmup, pinned, modes=("mapped", "memcpy")):
+        """The step with the content K/V in pinned host memory (pin_host),
+        timed for the zero-copy gather kernel (mapped) and for hipMemcpyAsync
+        per document on a side stream (memcpy)."""
+        p, M = self.p, self.M
+        kv, desc = pinned
+        out = dict(desc)
         hbm_runner = self.runner
-        kv = lambda l: (hk[l % n_pin], hv[l % n_pin])   # noqa: E731
-        for mode, src in (("mapped", M.MSA_SRC_HOST_MAPPED), ("memcpy", M.MSA_SRC_HOST_MEMCPY)):
+        srcs = {"mapped": M.MSA_SRC_HOST_MAPPED, "memcpy": M.MSA_SRC_HOST_MEMCPY}
+        for mode in modes:
+            src = srcs[mode]
             self.make_runner("host", indexed=False, src_mode=src)
             ms, route_ms = self.timed(steps, warmup, kv=kv)
             stage = self.stages(min(steps, 3), kv=kv)
@@ -548,9 +589,6 @@ class PresetBench:
                          * self.layers}
             log(f"host tier {mode}: {ms:.3f} ms per step, fetch {stage[2]:.3f} ms")
         self.runner = hbm_runner
-        del hk, hv
-        if hasattr(torch._C, "_host_emptyCache"):
-            torch._C._host_emptyCache()    # hand the pinned pages back
         return out
 
     def cold(self, flush_buf):
