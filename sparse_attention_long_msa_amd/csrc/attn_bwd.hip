@@ -426,7 +426,8 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(
     int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ krot, const uint16_t* __restrict__ vg, int KM,
     const int32_t* __restrict__ ctx_len, int max_ctx, int L_loc, const uint16_t* __restrict__ qs16,
     const uint16_t* __restrict__ do16, const float* __restrict__ lse, const float* __restrict__ Dv, int n_rg,
-    int n_splits, float* __restrict__ ws_dq) {
+    int n_splits, float* __restrict__ ws_dq, const float2* __restrict__ tab, int P, int qpo, float scale,
+    float* __restrict__ dq_out) {
   __shared__ __attribute__((aligned(16))) unsigned char kt[2][BQ_KV_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char vt[2][BQ_KV_BYTES];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -533,6 +534,33 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(
     }
   }
   if (!rok) return;
+  if (dq_out) {
+    // one split: this is the whole sum, so the scale and the query's inverse
+    // rotation are applied here, with attn_bwd_dq_sum_kernel's arithmetic.
+    // Lane (lc, g4) holds dims 16*dt + 4*g4 + e: the pair (m, m + 64) of dt < 4
+    // sits in dt and dt + 4 of the same lane.
+    int pq = qpo + L_loc - T + t;
+    pq = pq < 0 ? 0 : (pq >= P ? P - 1 : pq);
+    const float2* tr = tab + int64_t(pq) * (AT_D / 2);
+    float* dp = dq_out + grow * AT_D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int m0 = 16 * dt + 4 * g4;
+      float lo4[4], hi4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 c = tr[m0 + e];
+        float a = dqT[dt][e], bb = dqT[dt + 4][e];
+        a *= scale;
+        bb *= scale;
+        lo4[e] = a * c.x + bb * c.y;
+        hi4[e] = bb * c.x - a * c.y;
+      }
+      *reinterpret_cast<float4*>(dp + m0) = make_float4(lo4[0], lo4[1], lo4[2], lo4[3]);
+      *reinterpret_cast<float4*>(dp + m0 + AT_D / 2) = make_float4(hi4[0], hi4[1], hi4[2], hi4[3]);
+    }
+    return;
+  }
   float* op = ws_dq + (int64_t(split) * B * T * Hq + grow) * AT_D;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
@@ -854,7 +882,8 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
                      ctx_len, max_ctx, L_loc, qs16, do16, lse, Dv, p.n_kb, p.rt_per, p.n_items, part_k, part_v);    \
   MSA_LAUNCH_CHECK();                                                                                              \
   hipLaunchKernelGGL((attn_bwd_dq_kernel<GV>), qgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, krot, vgat, KMK,     \
-                     ctx_len, max_ctx, L_loc, qs16, do16, lse, Dv, p.n_rg, p.n_splits, ws_dq)
+                     ctx_len, max_ctx, L_loc, qs16, do16, lse, Dv, p.n_rg, p.n_splits, ws_dq, tab, P, q_pos_offset, \
+                     sm_scale, p.n_splits == 1 ? dq : nullptr)
     switch (G) {
       case 1: BW_LAUNCH(1); break;
       case 2: BW_LAUNCH(2); break;
@@ -873,10 +902,12 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
                          max_ctx, tab, P, dk_loc, dv_loc, dk_bar, dv_bar);
       MSA_LAUNCH_CHECK();
     }
-    const int64_t n = rows * (d / 2);
-    hipLaunchKernelGGL(attn_bwd_dq_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, ws_dq, p.n_splits,
-                       rows, T, Hq, d, L_loc, q_pos_offset, tab, P, sm_scale, dq);
-    MSA_LAUNCH_CHECK();
+    if (p.n_splits > 1) {   // one split: the dQ kernel wrote dq itself
+      const int64_t n = rows * (d / 2);
+      hipLaunchKernelGGL(attn_bwd_dq_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, ws_dq, p.n_splits,
+                         rows, T, Hq, d, L_loc, q_pos_offset, tab, P, sm_scale, dq);
+      MSA_LAUNCH_CHECK();
+    }
     return MSA_OK;
   }
   const int n_keys_max = max_ctx + L_loc;
