@@ -361,7 +361,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
     const int32_t* __restrict__ ctx_row_in, int64_t ctx_rows, const float2* __restrict__ tab, int P, float scale_log2,
     uint16_t* __restrict__ ws_o, float4* __restrict__ ws_ml, int n_splits, int n_rt, int n_rg, float* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, BwdPrep prep) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int32_t* __restrict__ ctx_row = IDX ? ctx_row_in : nullptr;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -598,17 +598,40 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
       store_partial(o[i], m_run[i], l, rok[i], g4, ws_o + rowid * AT_D, ws_ml + rowid);
       continue;
     }
-    if (!rok[i]) continue;
+    if (!rok[i]) continue;   // uniform in each row's four lanes
     {
       // one split: the combine's result directly, with its arithmetic
       // (out = O / l, lse = m + log2 l; a row that saw no visible key gets 0, -inf)
       const int64_t row = (int64_t(b) * T + trow[i]) * Hq + hqrow[i];
       const float r = l > 0.f ? 1.f / l : 0.f;
-      float* op = out + row * AT_D;
+      if (prep.dout) {
+        // the backward's row preparation: lane (lc, g4) holds dims 16*dt + 4*g4 + e of
+        // the row, and its rotated query's dims 32*kk + 8*g4 .. + 7
+        const float* gp = prep.dout + row * AT_D;
+        float dacc = 0.f;
+        uint2 dpk[8];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<float4*>(op + 16 * dt + 4 * g4) =
-            make_float4(o[i][dt][0] * r, o[i][dt][1] * r, o[i][dt][2] * r, o[i][dt][3] * r);
+        for (int dt = 0; dt < 8; ++dt) {
+          const float4 g = *reinterpret_cast<const float4*>(gp + 16 * dt + 4 * g4);
+          const float o0 = o[i][dt][0] * r, o1 = o[i][dt][1] * r, o2 = o[i][dt][2] * r, o3 = o[i][dt][3] * r;
+          dacc += o0 * g.x + o1 * g.y + o2 * g.z + o3 * g.w;
+          dpk[dt] = make_uint2(pack_bf16x2(g.x, g.y), pack_bf16x2(g.z, g.w));
+        }
+        dacc += __shfl_xor(dacc, 16);
+        dacc += __shfl_xor(dacc, 32);
+        if (g4 == 0) prep.Dv[row] = dacc;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint2*>(prep.do16 + row * AT_D + 16 * dt + 4 * g4) = dpk[dt];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          *reinterpret_cast<uint4*>(prep.qs16 + row * AT_D + 32 * kk + 8 * g4) = __builtin_bit_cast(uint4, bq[i][kk]);
+      } else {
+        float* op = out + row * AT_D;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<float4*>(op + 16 * dt + 4 * g4) =
+              make_float4(o[i][dt][0] * r, o[i][dt][1] * r, o[i][dt][2] * r, o[i][dt][3] * r);
+      }
       if (lse && g4 == 0) lse[row] = l > 0.f ? m_run[i] + __log2f(l) : -INFINITY;
     }
   }
@@ -904,7 +927,9 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
                 const void* k_ctx, const void* v_ctx, const int32_t* ctx_row, int64_t ctx_rows, const int32_t* ctx_pos,
                 const int32_t* ctx_len, int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
                 int q_pos_offset, float rope_base, const float* rope_table, int rope_table_rows, float sm_scale,
-                float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                float* out, float* lse, void* ws, size_t ws_bytes, void* stream, const BwdPrep* prep,
+                bool* prep_done) {
+  if (prep_done) *prep_done = false;
   MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
   MSA_REQUIRE(q && k_ctx && v_ctx && ctx_pos && ctx_len && k_loc && v_loc && out && ws, MSA_ERR_INVALID_ARG,
               fn + ": NULL pointer");
@@ -944,6 +969,8 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
     const int G = Hq / Hkv;
     const float scale_log2_pf = sm_scale * 1.4426950408889634f;
     if (p.prefill) {
+      const bool fuse_prep = prep && p.n_splits == 1;
+      const BwdPrep pp = fuse_prep ? *prep : BwdPrep{};
       const dim3 pgrid(unsigned(int64_t(B) * Hkv * p.n_rg * p.n_splits)), pblock(PF_THREADS);
       const size_t psmem = 2 * size_t(PF_BUF) + AT_CIDX_BYTES;
 #define PF_LAUNCH2(GV, RV, IV)                                                                                      \
@@ -951,7 +978,7 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
                      Hq, Hkv, static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos,     \
                      ctx_len, max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc),     \
                      L_loc, q_pos_offset, ctx_row, ctx_rows, tab, p.P, scale_log2_pf, ws_o, ws_ml, p.n_splits,       \
-                     p.n_rt, p.n_rg, out, lse)
+                     p.n_rt, p.n_rg, out, lse, pp)
 #define PF_LAUNCH(GV, RV)       \
   if (ctx_row) {                \
     PF_LAUNCH2(GV, RV, true);   \
@@ -974,7 +1001,10 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
 #undef PF_LAUNCH
 #undef PF_LAUNCH2
       MSA_LAUNCH_CHECK();
-      if (p.n_splits == 1) return MSA_OK;   // the prefill wrote out (and lse) itself
+      if (p.n_splits == 1) {   // the prefill wrote out (or the backward's rows) and lse itself
+        if (prep_done) *prep_done = fuse_prep;
+        return MSA_OK;
+      }
       const int64_t rows = int64_t(B) * T * Hq;
       hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * (d / 4) + 255) / 256)), dim3(256), 0, s, ws_o,
                          ws_ml, p.n_splits, rows, d, out, lse);

@@ -847,9 +847,16 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
   uint16_t* krot = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(part_v) + p.part_bytes);
   uint16_t* vgat = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(krot) + p.key_bytes);
   // the forward (validates every shared argument) with the per-row log-sum-exp
+  // on the MFMA path the forward may also prepare the rows (D, bf16 dO and rotated query)
+  BwdPrep prep;
+  prep.dout = dout;
+  prep.Dv = Dv;
+  prep.qs16 = qs16;
+  prep.do16 = do16;
+  bool prep_done = false;
   const int rc = sparse_attn(fn, dtype, q, B, T, Hq, Hkv, d, k_bar, v_bar, ctx_row, n_chunks, ctx_pos, ctx_len,
                              max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows,
-                             sm_scale, out, lse, ws, p.fwd_bytes, stream);
+                             sm_scale, out, lse, ws, p.fwd_bytes, stream, p.mfma ? &prep : nullptr, &prep_done);
   if (rc != MSA_OK) return rc;
   hipStream_t s = as_stream(stream);
   // the forward built the RoPE rows at the start of its workspace when none were given
@@ -859,10 +866,12 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
   const int G = Hq / Hkv;
   const unsigned prep_grid = unsigned((rows + BW_WAVES - 1) / BW_WAVES);
   if (p.mfma) {
-    hipLaunchKernelGGL(bwd_prep128_kernel, dim3(unsigned((rows * 16 + BW_THREADS - 1) / BW_THREADS)),
-                       dim3(BW_THREADS), 0, s, static_cast<const uint16_t*>(q), T, Hq, L_loc, q_pos_offset, tab, P,
-                       sm_scale * BW_LOG2E, out, dout, rows, Dv, qs16, do16);
-    MSA_LAUNCH_CHECK();
+    if (!prep_done) {
+      hipLaunchKernelGGL(bwd_prep128_kernel, dim3(unsigned((rows * 16 + BW_THREADS - 1) / BW_THREADS)),
+                         dim3(BW_THREADS), 0, s, static_cast<const uint16_t*>(q), T, Hq, L_loc, q_pos_offset, tab, P,
+                         sm_scale * BW_LOG2E, out, dout, rows, Dv, qs16, do16);
+      MSA_LAUNCH_CHECK();
+    }
     const uint16_t* kb = static_cast<const uint16_t*>(k_bar);
     const uint16_t* vb = static_cast<const uint16_t*>(v_bar);
     const uint16_t* kl = static_cast<const uint16_t*>(k_loc);

@@ -204,13 +204,27 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // RoPE table rows the attention kernels need: max(qpo + L_loc, max_ctx, 32)
 inline int rope_rows(int max_ctx, int L_loc, int qpo) { return std::max(std::max(qpo + L_loc, max_ctx), 32); }
 
+// The backward's row preparation, done by the forward's epilogue when the
+// forward runs as one key split of the prefill kernel (the row's O is then in
+// registers): D = <dO, O>, dO rounded to bf16, and the rotated query times
+// sm_scale * log2(e) as the forward rounded it.  O itself is then not written.
+struct BwdPrep {
+  const float* dout = nullptr;
+  float* Dv = nullptr;
+  uint16_t* qs16 = nullptr;
+  uint16_t* do16 = nullptr;
+};
+
 // The forward of msa_sparse_attn / msa_sparse_attn_indexed (ctx_row NULL for
 // a gathered context); lse, when given, receives per query row the base-2
-// log-sum-exp of the logits scaled by sm_scale * log2(e).
+// log-sum-exp of the logits scaled by sm_scale * log2(e).  With prep, the
+// forward also does the backward's row preparation when its plan allows
+// (*prep_done tells).
 int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
                 const void* k_ctx, const void* v_ctx, const int32_t* ctx_row, int64_t ctx_rows, const int32_t* ctx_pos,
                 const int32_t* ctx_len, int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
                 int q_pos_offset, float rope_base, const float* rope_table, int rope_table_rows, float sm_scale,
-                float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+                float* out, float* lse, void* ws, size_t ws_bytes, void* stream, const BwdPrep* prep = nullptr,
+                bool* prep_done = nullptr);
 
 }  // namespace msa
