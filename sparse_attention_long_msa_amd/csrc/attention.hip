@@ -121,7 +121,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void attn_decode_kernel(
   // a step whose 32 keys are all local tokens addresses them affinely
   auto all_local = [&](int j0) { return j0 >= ctxl && j0 + 32 <= n_keys; };
 
-  const CtxCache cc = stage_ctx(reinterpret_cast<int2*>(smem + 2 * DC_TAB_BYTES + size_t(nw) * AT_V_BYTES), b, j_begin,
+  const CtxCache cc = stage_ctx(reinterpret_cast<int2*>(smem + 2 * DC_TAB_BYTES + size_t(nw) * AT_V_BYTES), AT_CIDX, b, j_begin,
                                 j_end, ctxl, max_ctx, ctx_pos, P, ctx_row, ctx_rows, tid, nthr);
   __syncthreads();
   // Addresses are formed under the (uniform) all-local test, the loads come
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
 
   // cooperative mapping of one 32-key step
   const int lk = tid / 16, lx = tid % 16;     // K: key, 4-dim block; V: key, 8-dim block
-  const CtxCache cc = stage_ctx(reinterpret_cast<int2*>(smem + 2 * size_t(PF_BUF)), b, j_begin, j_end, ctxl, max_ctx,
+  const CtxCache cc = stage_ctx(reinterpret_cast<int2*>(smem + 2 * size_t(PF_BUF)), PF_CIDX, b, j_begin, j_end, ctxl, max_ctx,
                                 ctx_pos, P, ctx_row, ctx_rows, tid, PF_THREADS);
   __syncthreads();
 
@@ -885,7 +885,8 @@ static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int m
   // context entries must fit the workgroup's LDS index cache
   int64_t s = (target + units - 1) / units;
   s = std::max<int64_t>(1, std::min<int64_t>(s, (n_keys_max + 63) / 64));
-  if (max_ctx > AT_CIDX) s = std::max<int64_t>(s, (n_keys_max + AT_CIDX - 33) / (AT_CIDX - 32));
+  const int cap = p.prefill ? PF_CIDX : AT_CIDX;
+  if (max_ctx > cap) s = std::max<int64_t>(s, (n_keys_max + cap - 33) / (cap - 32));
   p.n_splits = int(s);
   const int64_t rows = int64_t(B) * T * Hq;
   p.o_bytes = align_up(size_t(p.n_splits) * rows * d * sizeof(uint16_t), 256);   // float16 partials
@@ -972,8 +973,10 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
       const bool fuse_prep = prep && p.n_splits == 1;
       const BwdPrep pp = fuse_prep ? *prep : BwdPrep{};
       const dim3 pgrid(unsigned(int64_t(B) * Hkv * p.n_rg * p.n_splits)), pblock(PF_THREADS);
-      const size_t psmem = 2 * size_t(PF_BUF) + AT_CIDX_BYTES;
+      const size_t psmem = 2 * size_t(PF_BUF) + PF_CIDX_BYTES;
 #define PF_LAUNCH2(GV, RV, IV)                                                                                      \
+  MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefill_kernel<GV, RV, IV>),               \
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, int(psmem)));                       \
   hipLaunchKernelGGL((attn_prefill_kernel<GV, RV, IV>), pgrid, pblock, psmem, s, static_cast<const uint16_t*>(q), B, T,  \
                      Hq, Hkv, static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos,     \
                      ctx_len, max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc),     \

@@ -146,22 +146,28 @@ __device__ __forceinline__ int64_t ctx_src_row(int64_t e, const int32_t* __restr
 }
 
 // A workgroup's context entries [lo, lo + n) as (store row, clamped
-// position), staged in LDS once so that no step waits on an index load.
+// position), staged in LDS once so that no step waits on an index load.  The
+// decode kernel (two workgroups per CU) holds 1,024 entries; the prefill
+// kernel (one workgroup per CU) 4,096, so that a 4,096-entry context does
+// not force extra key splits.
 constexpr int AT_CIDX = 1024;
 constexpr int AT_CIDX_BYTES = AT_CIDX * 8;
+constexpr int PF_CIDX = 4096;
+constexpr int PF_CIDX_BYTES = PF_CIDX * 8;
 struct CtxCache {
   const int2* e;
-  int lo, n;
+  int lo, n, cap;
 };
 
-__device__ __forceinline__ CtxCache stage_ctx(int2* lds, int b, int j_begin, int j_end, int ctxl, int max_ctx,
-                                              const int32_t* __restrict__ ctx_pos, int P,
+__device__ __forceinline__ CtxCache stage_ctx(int2* lds, int cap, int b, int j_begin, int j_end, int ctxl,
+                                              int max_ctx, const int32_t* __restrict__ ctx_pos, int P,
                                               const int32_t* __restrict__ ctx_row, int64_t ctx_rows, int tid,
                                               int nthr) {
   CtxCache c;
   c.e = lds;
   c.lo = j_begin;
-  c.n = max(0, min(min(j_end, ctxl) - j_begin, AT_CIDX));
+  c.cap = cap;
+  c.n = max(0, min(min(j_end, ctxl) - j_begin, cap));
   for (int i = tid; i < c.n; i += nthr) {
     const int64_t e = int64_t(b) * max_ctx + j_begin + i;
     int p = ctx_pos[e];
@@ -185,7 +191,7 @@ __device__ __forceinline__ KeySrc key_src(int j, int b, int ctxl, int n_keys, in
   (void)ctx_rows;
   const int i = j - cc.lo;
   const bool in = i >= 0 && i < cc.n;
-  const int2 e = cc.e[min(max(i, 0), AT_CIDX - 1)];
+  const int2 e = cc.e[min(max(i, 0), cc.cap - 1)];
   const bool is_ctx = j < ctxl;
   const int li = min(max(j - ctxl, 0), L_loc - 1);
   const int64_t crow = ctx_row ? int64_t(in ? e.x : 0) : int64_t(b) * max_ctx + (in ? j : 0);
