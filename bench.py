@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the per-config lines of the smaller presets (after the 100M-token line)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    ap.add_argument("--overlap", action="store_true",
+                    help="on the host tier, run each layer's attention as its two calls, the local-window part on "
+                         "a side stream beside the fetch (measured slower than one call after the fetch)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP graph replay; for counter collection)")
     ap.add_argument("--layers", type=int, default=None, help="override the routed-layer count (profiling only)")
@@ -109,7 +112,8 @@ def main():
     from synth import configs
 
     p = configs.PRESETS[args.config]()
-    pb = PresetBench(torch, p, args.layers, rounds=args.rounds, graph=not args.no_graph)
+    pb = PresetBench(torch, p, args.layers, rounds=args.rounds, graph=not args.no_graph,
+                     overlap=args.overlap)
     pb.build_stores()
     pb.build_content("hbm")
     assembly = args.hbm_assembly if args.rounds == 1 else "index"
@@ -158,7 +162,7 @@ class PresetBench:
     """One workload preset on the device: its stores (built by the offline
     stage before any timing), a LayerRunner and the whole-path step."""
 
-    def __init__(self, torch, p, layers=None, rounds=1, graph=True):
+    def __init__(self, torch, p, layers=None, rounds=1, graph=True, overlap=False):
         import synth
         from synth import device as SD
         import sparse_attention_long_msa_amd as M
@@ -166,6 +170,7 @@ class PresetBench:
         self.layers = p.layers if layers is None else layers
         self.rounds = rounds
         self.graph = graph
+        self.overlap = overlap
         self.dev = torch.device("cuda:0")
         torch.cuda.set_device(self.dev)
         self.bf = torch.bfloat16 if p.bf16 else torch.float32
@@ -241,16 +246,19 @@ class PresetBench:
         self.raw = None
         log(f"content K/V ({tier}) ready in {time.time() - t0:.1f} s")
 
-    def make_runner(self, tier, indexed, src_mode=None):
+    def make_runner(self, tier, indexed, src_mode=None, overlap=None):
         p, M = self.p, self.M
         self.tier = tier
+        if overlap is None:
+            # only a fetched context leaves something to overlap
+            overlap = self.overlap and self.rounds == 1 and not indexed
         self.runner = M.LayerRunner(batch=p.B, tokens=p.T, q_heads=p.Hq, kv_heads=p.H, head_dim=p.d,
                                     n_docs=p.n_docs, n_chunks=p.n_chunks, k=p.k, max_doc_chunks=p.max_doc_chunks,
                                     local_len=p.L_loc, dtype=self.bf, device=self.dev,
                                     q_pos_offset=p.qpo if self.rounds == 1 else None, rope_base=p.rope_base,
                                     src_mode=M.MSA_SRC_DEVICE if src_mode is None else src_mode,
                                     chunk_off_h=p.chunk_off, kr_layout=self.kr_layout, indexed=indexed,
-                                    rounds=self.rounds)
+                                    rounds=self.rounds, overlap_local=overlap)
         return self.runner
 
     def step(self, ev=None, route_ev=None, route_layer=-1, kv=None, flush=None):
@@ -290,9 +298,14 @@ class PresetBench:
                 runner.select_assemble(self.co_d, kb, vb)
                 rec(e[2])
                 rec(e[3])
+                if runner.overlap_local:
+                    runner.start_local(self.qq[l], self.kl[l], self.vl[l])
             else:
                 runner.select()
                 rec(e[2])
+                if runner.overlap_local:
+                    # the local-window half of the attention, beside the fetch
+                    runner.start_local(self.qq[l], self.kl[l], self.vl[l])
                 runner.assemble(self.co_d, kb, vb)
                 rec(e[3])
             runner.attend(self.qq[l], self.kl[l], self.vl[l])
@@ -423,7 +436,10 @@ class PresetBench:
             "dtype": "bf16" if p.bf16 else "f32",
             "data": "synthetic (seeded counter-based generator; planted needles)",
             "config": {"workload": workload, "global_batch": p.B, "seq_len": p.T, "parallelism": "single GPU",
-                       "kv_tier": tier, "rounds": self.rounds, "step_launch": launch},
+                       "kv_tier": tier, "rounds": self.rounds, "step_launch": launch,
+                       "attention_calls": ("two: the local-window part on a side stream beside the fetch, the "
+                                           "context part and the merge after it")
+                       if self.runner.overlap_local else "one, after the context is assembled"},
             "route_attn_us_per_query": round(ms_per_step * 1e3 / p.B, 1),
             "ms_per_step_eager_launches": round(ms_eager, 4),
             "ms_per_step_graph_replay": round(ms_graph, 4) if self.graph else None,
@@ -612,7 +628,7 @@ def config_leg(torch, name, args):
     on the machine's host cores (bounded samples)."""
     from synth import configs
     p = configs.PRESETS[name]()
-    pb = PresetBench(torch, p, graph=not args.no_graph)
+    pb = PresetBench(torch, p, graph=not args.no_graph, overlap=args.overlap)
     pb.build_stores()
     pb.build_content("hbm")
     pb.make_runner("hbm", indexed=True)

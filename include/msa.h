@@ -71,6 +71,11 @@ typedef enum {
                               a side stream                                             */
 } msa_src_mode;
 
+typedef enum {
+  MSA_ATTN_PART_LOCAL = 1,   /* msa_sparse_attn_part: the local-window keys only          */
+  MSA_ATTN_PART_CONTEXT = 2  /* msa_sparse_attn_part: the context keys, then the merge    */
+} msa_attn_part;
+
 /* Version of this ABI (bumped on any signature or workspace-layout change, and on added calls). */
 int msa_abi_version(void);
 
@@ -436,6 +441,39 @@ int msa_sparse_attn_indexed(int dtype, const void* q, int B, int T, int Hq, int 
                             const int32_t* ctx_len, int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
                             int q_pos_offset, float rope_base, const float* rope_table, int rope_table_rows,
                             float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * msa_sparse_attn_part - msa_sparse_attn (or, with ctx_row, _indexed) in two
+ * calls, so that the local-window half of the attention can run while the
+ * selected documents' K/V are still being fetched (README, Overall Design >
+ * Inference Pipeline: content K/V stays in host memory and is fetched
+ * asynchronously once the top-k is known; the local tokens need no fetch).
+ *   part = MSA_ATTN_PART_LOCAL: the local keys only, as partial softmax sums
+ *     into ws.  Reads q, k_loc, v_loc and the RoPE rows; the context arguments
+ *     (k_ctx, v_ctx, ctx_row, ctx_pos, ctx_len) and out are not read and may be
+ *     NULL, so the call may run before or while the context is assembled.
+ *   part = MSA_ATTN_PART_CONTEXT: the context keys, then the merge of both
+ *     parts' partials into out.  ws must hold the local call's partials: the
+ *     same arguments, the same ws, and the local call complete (the caller
+ *     orders the two, e.g. with an event between two streams).
+ * The result is msa_sparse_attn's definition; the keys are split between
+ * partials differently, so it agrees with msa_sparse_attn to float rounding
+ * (the partials are float16), not bit for bit.
+ *   ctx_row NULL: k_ctx/v_ctx are a gathered context [B, max_ctx, Hkv, d]
+ *   (msa_gather_kv) and ctx_rows is ignored; otherwise they are the pooled
+ *   store [ctx_rows, Hkv, d] read in place (msa_context_index).
+ *   ws    msa_sparse_attn_part_workspace() bytes (not msa_sparse_attn_workspace)
+ * Errors: those of msa_sparse_attn; INVALID_ARG also for a bad part or, with
+ * ctx_row, ctx_rows outside [1, 2^31); UNSUPPORTED off the MFMA path (bf16,
+ * d = 128, Hq/Hkv in {1, 2, 4, 8, 16}).
+ */
+size_t msa_sparse_attn_part_workspace(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc,
+                                      int q_pos_offset);
+int msa_sparse_attn_part(int part, int dtype, const void* q, int B, int T, int Hq, int Hkv, int d, const void* k_ctx,
+                         const void* v_ctx, int64_t ctx_rows, const int32_t* ctx_row, const int32_t* ctx_pos,
+                         const int32_t* ctx_len, int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
+                         int q_pos_offset, float rope_base, const float* rope_table, int rope_table_rows,
+                         float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * msa_sparse_attn_indexed_noalloc - msa_sparse_attn_indexed for callers that

@@ -17,6 +17,7 @@ lib_path = os.path.join(_HERE, "libmsa.so")
 MSA_F32, MSA_BF16 = 0, 1
 MSA_SRC_DEVICE, MSA_SRC_HOST_MAPPED, MSA_SRC_HOST_MEMCPY = 0, 1, 2
 MSA_LAYOUT_ROWS, MSA_LAYOUT_TILED = 0, 1
+MSA_ATTN_PART_LOCAL, MSA_ATTN_PART_CONTEXT = 1, 2
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -52,6 +53,9 @@ _SIGS = {
                                      _F, _P, _I, _F, _P, _P, _S, _P]),
     "msa_sparse_attn_indexed_noalloc": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _L, _P, _P, _P, _I, _P, _P, _I,
                                              _I, _F, _P, _I, _F, _P, _P]),
+    "msa_sparse_attn_part_workspace": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "msa_sparse_attn_part": (_I, [_I, _I, _P, _I, _I, _I, _I, _I, _P, _P, _L, _P, _P, _P, _I, _P, _P, _I, _I,
+                                  _F, _P, _I, _F, _P, _P, _S, _P]),
     "msa_rope_table_rows": (_I, [_I, _I, _I]),
     "msa_stream_read": (_I, [_P, _L, _P, _P]),
     "msa_rope_table": (_I, [_I, _I, _F, _P, _P]),
@@ -521,6 +525,45 @@ def msa_sparse_attn_indexed(q, k_bar, v_bar, ctx_row, ctx_pos, ctx_len, k_loc, v
     ws, wsb = _ws(msa_sparse_attn_workspace(dt, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset), q.device, ws)
     _check("msa_sparse_attn_indexed", lib.msa_sparse_attn_indexed(
         dt, _ptr(q), B, T, Hq, Hkv, d, _ptr(k_bar), _ptr(v_bar), n_chunks, _ptr(ctx_row), _ptr(ctx_pos),
+        _ptr(ctx_len), max_ctx, _ptr(k_loc), _ptr(v_loc), L_loc, q_pos_offset, float(rope_base), _ptr(rope_table),
+        0 if rope_table is None else rope_table.shape[0], float(sm_scale), _ptr(out), _ptr(ws), wsb,
+        _stream(stream)))
+    return out
+
+
+def msa_sparse_attn_part_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset):
+    return lib.msa_sparse_attn_part_workspace(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset)
+
+
+def msa_sparse_attn_part(part, q, k_loc, v_loc, q_pos_offset, max_ctx, k_ctx=None, v_ctx=None, ctx_row=None,
+                         ctx_pos=None, ctx_len=None, rope_base=1e6, sm_scale=None, out=None, ws=None,
+                         rope_table=None, stream=None):
+    """One of the two calls of msa_sparse_attn_part: MSA_ATTN_PART_LOCAL (the
+    local keys' partials into ws; the context arguments are not needed) or
+    MSA_ATTN_PART_CONTEXT (the context keys and the merge into out, with the
+    local call's ws).  With ctx_row the context is read in place from the store
+    k_ctx/v_ctx [rows, Hkv, d]; without it k_ctx/v_ctx are a gathered context
+    [B, max_ctx, Hkv, d].  Both calls take the same max_ctx and ws."""
+    B, T, Hq, d, Hkv, L_loc, out = _attn_operands(q, k_loc, v_loc, rope_table, out)
+    ctx_rows = 0
+    if part == MSA_ATTN_PART_CONTEXT:
+        if ctx_row is None:
+            _dev(k_ctx, "k_ctx", q.dtype, (B, max_ctx, Hkv, d))
+            _dev(v_ctx, "v_ctx", q.dtype, (B, max_ctx, Hkv, d))
+        else:
+            _dev(k_ctx, "k_ctx", q.dtype, (None, Hkv, d))
+            ctx_rows = k_ctx.shape[0]
+            _dev(v_ctx, "v_ctx", q.dtype, (ctx_rows, Hkv, d))
+            _dev(ctx_row, "ctx_row", _I32, (B, max_ctx))
+        _dev(ctx_pos, "ctx_pos", _I32, (B, max_ctx))
+        _dev(ctx_len, "ctx_len", _I32, (B,))
+    _dev(ws, "ws", optional=True)
+    dt = _dtype(q)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    ws, wsb = _ws(msa_sparse_attn_part_workspace(dt, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset), q.device, ws)
+    _check("msa_sparse_attn_part", lib.msa_sparse_attn_part(
+        part, dt, _ptr(q), B, T, Hq, Hkv, d, _ptr(k_ctx), _ptr(v_ctx), ctx_rows, _ptr(ctx_row), _ptr(ctx_pos),
         _ptr(ctx_len), max_ctx, _ptr(k_loc), _ptr(v_loc), L_loc, q_pos_offset, float(rope_base), _ptr(rope_table),
         0 if rope_table is None else rope_table.shape[0], float(sm_scale), _ptr(out), _ptr(ws), wsb,
         _stream(stream)))

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void attn_decode_kernel(
     const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
     const int32_t* __restrict__ ctx_row_in, int64_t ctx_rows, const float2* __restrict__ tab, int P, float scale_log2,
-    uint16_t* __restrict__ ws_o, float4* __restrict__ ws_ml, int n_splits, int n_hg) {
+    uint16_t* __restrict__ ws_o, float4* __restrict__ ws_ml, int n_splits, int n_hg, int part, int split_base) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int32_t* __restrict__ ctx_row = IDX ? ctx_row_in : nullptr;
   const int nw = blockDim.x / 64;
@@ -111,8 +111,10 @@ __global__ __launch_bounds__(DC_THREADS, 2) void attn_decode_kernel(
     for (int kk = 0; kk < 4; ++kk) bq[kk] = __builtin_bit_cast(bf16x8, row_ok ? qv[kk] : make_uint4(0, 0, 0, 0));
   }
 
-  const int ctxl = min(max(ctx_len[b], 0), max_ctx);
-  const int n_keys = ctxl + L_loc;
+  // the keys of this launch: all, the local window only (the context is not
+  // read, not even its length) or the context only
+  const int ctxl = part == MSA_ATTN_PART_LOCAL ? 0 : min(max(ctx_len[b], 0), max_ctx);
+  const int n_keys = part == MSA_ATTN_PART_CONTEXT ? ctxl : ctxl + L_loc;
   // this query's keys split evenly over the n_splits workgroups (32-key steps)
   const int kps = ((n_keys + n_splits - 1) / n_splits + 31) / 32 * 32;
   const int j_begin = split * kps;
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void attn_decode_kernel(
   // ---- partial result of this split: O^T[d = 16dt + 4*g4 + i][row lc]
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  const int64_t rowid = ((int64_t(split) * B + b) * T + t) * Hq + hq;
+  const int64_t rowid = ((int64_t(split_base + split) * B + b) * T + t) * Hq + hq;
   store_partial(o, m_run, l_run, row_ok, g4, ws_o + rowid * AT_D, ws_ml + rowid);
 }
 
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
     const int32_t* __restrict__ ctx_row_in, int64_t ctx_rows, const float2* __restrict__ tab, int P, float scale_log2,
     uint16_t* __restrict__ ws_o, float4* __restrict__ ws_ml, int n_splits, int n_rt, int n_rg, float* __restrict__ out,
-    float* __restrict__ lse, BwdPrep prep) {
+    float* __restrict__ lse, int part, int split_base, BwdPrep prep) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int32_t* __restrict__ ctx_row = IDX ? ctx_row_in : nullptr;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -409,8 +411,10 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     if (rt < n_rt) hmin = min(hmin, L_loc - T + (rt * 16) / G);
   }
 
-  const int ctxl = min(max(ctx_len[b], 0), max_ctx);
-  const int n_keys = ctxl + L_loc;
+  // the keys of this launch: all, the local window only (the context is not
+  // read, not even its length) or the context only
+  const int ctxl = part == MSA_ATTN_PART_LOCAL ? 0 : min(max(ctx_len[b], 0), max_ctx);
+  const int n_keys = part == MSA_ATTN_PART_CONTEXT ? ctxl : ctxl + L_loc;
   // this query's keys split evenly over the n_splits workgroups (32-key steps)
   const int kps = ((n_keys + n_splits - 1) / n_splits + 31) / 32 * 32;
   const int j_begin = split * kps;
@@ -593,8 +597,8 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     float l = l_run[i];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if (n_splits > 1) {
-      const int64_t rowid = ((int64_t(split) * B + b) * T + trow[i]) * Hq + hqrow[i];
+    if (n_splits > 1 || part != 0) {
+      const int64_t rowid = ((int64_t(split_base + split) * B + b) * T + trow[i]) * Hq + hqrow[i];
       store_partial(o[i], m_run[i], l, rok[i], g4, ws_o + rowid * AT_D, ws_ml + rowid);
       continue;
     }
@@ -855,12 +859,13 @@ struct AttnPlan {
   int n_hg;         // KV-head groups of 8 (decode)
   int P;            // rows of the RoPE table
   int n_rt;         // 16-row tiles per (b, g)
-  int n_splits;
+  int n_splits;     // partials in the workspace
+  int n_sc, n_sl;   // msa_sparse_attn_part: context splits [0, n_sc), local splits [n_sc, n_splits)
   size_t tab_bytes, o_bytes, ml_bytes;
 };
 
 
-static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc, int qpo) {
+static AttnPlan attn_plan_splits(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc, int qpo) {
   AttnPlan p{};
   const int G = Hkv > 0 ? Hq / Hkv : 0;
   p.mfma = dtype == MSA_BF16 && d == AT_D && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
@@ -883,14 +888,35 @@ static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int m
   }
   // the kernels split each query's actual keys evenly over n_splits; a split's
   // context entries must fit the workgroup's LDS index cache
-  int64_t s = (target + units - 1) / units;
-  s = std::max<int64_t>(1, std::min<int64_t>(s, (n_keys_max + 63) / 64));
+  const int64_t want = (target + units - 1) / units;
   const int cap = p.prefill ? PF_CIDX : AT_CIDX;
+  int64_t s = std::max<int64_t>(1, std::min<int64_t>(want, (n_keys_max + 63) / 64));
   if (max_ctx > cap) s = std::max<int64_t>(s, (n_keys_max + cap - 33) / (cap - 32));
   p.n_splits = int(s);
+  // the two-call form: each part fills the chip on its own (the local part
+  // runs beside the context's fetch, the context part after it)
+  int64_t sc = std::max<int64_t>(1, std::min<int64_t>(want, (int64_t(max_ctx) + 63) / 64));
+  if (max_ctx > cap) sc = std::max<int64_t>(sc, (int64_t(max_ctx) + cap - 33) / (cap - 32));
+  const int64_t sl = std::max<int64_t>(1, std::min<int64_t>(want, (int64_t(L_loc) + 63) / 64));
+  p.n_sc = int(sc);
+  p.n_sl = int(sl);
+  return p;
+}
+
+// workspace byte counts for n partial splits
+static void plan_bytes(AttnPlan& p, int B, int T, int Hq, int d, int n) {
   const int64_t rows = int64_t(B) * T * Hq;
-  p.o_bytes = align_up(size_t(p.n_splits) * rows * d * sizeof(uint16_t), 256);   // float16 partials
-  p.ml_bytes = align_up(size_t(p.n_splits) * rows * sizeof(float4), 256);
+  p.o_bytes = p.mfma ? align_up(size_t(n) * rows * d * sizeof(uint16_t), 256) : 0;   // float16 partials
+  p.ml_bytes = p.mfma ? align_up(size_t(n) * rows * sizeof(float4), 256) : 0;
+}
+
+// part 0: msa_sparse_attn's plan; MSA_ATTN_PART_*: the two-call plan, whose
+// n_splits counts both parts' partials
+static AttnPlan attn_plan(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc, int qpo,
+                          int part) {
+  AttnPlan p = attn_plan_splits(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, qpo);
+  if (part != 0 && p.mfma) p.n_splits = p.n_sc + p.n_sl;
+  plan_bytes(p, B, T, Hq, d, p.n_splits);
   return p;
 }
 
@@ -916,7 +942,15 @@ extern "C" int msa_rope_table(int rows, int d, float rope_base, float* table, vo
 extern "C" size_t msa_sparse_attn_workspace(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx, int L_loc,
                                             int q_pos_offset) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 2 || max_ctx < 0 || L_loc < 1 || q_pos_offset < 0) return 0;
-  const msa::AttnPlan p = msa::attn_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
+  const msa::AttnPlan p = msa::attn_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset, 0);
+  return p.tab_bytes + p.o_bytes + p.ml_bytes;
+}
+
+extern "C" size_t msa_sparse_attn_part_workspace(int dtype, int B, int T, int Hq, int Hkv, int d, int max_ctx,
+                                                 int L_loc, int q_pos_offset) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 2 || max_ctx < 0 || L_loc < 1 || q_pos_offset < 0) return 0;
+  const msa::AttnPlan p =
+      msa::attn_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset, MSA_ATTN_PART_LOCAL);
   return p.tab_bytes + p.o_bytes + p.ml_bytes;
 }
 
@@ -929,11 +963,14 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
                 const int32_t* ctx_len, int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
                 int q_pos_offset, float rope_base, const float* rope_table, int rope_table_rows, float sm_scale,
                 float* out, float* lse, void* ws, size_t ws_bytes, void* stream, const BwdPrep* prep,
-                bool* prep_done) {
+                bool* prep_done, int part) {
   if (prep_done) *prep_done = false;
   MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
-  MSA_REQUIRE(q && k_ctx && v_ctx && ctx_pos && ctx_len && k_loc && v_loc && out && ws, MSA_ERR_INVALID_ARG,
-              fn + ": NULL pointer");
+  MSA_REQUIRE(part == 0 || part == MSA_ATTN_PART_LOCAL || part == MSA_ATTN_PART_CONTEXT, MSA_ERR_INVALID_ARG,
+              fn + ": bad part");
+  const bool local_part = part == MSA_ATTN_PART_LOCAL;   // reads neither the context nor its length
+  MSA_REQUIRE(q && k_loc && v_loc && ws && (local_part || (k_ctx && v_ctx && ctx_pos && ctx_len && out)),
+              MSA_ERR_INVALID_ARG, fn + ": NULL pointer");
   MSA_REQUIRE(B >= 1 && T >= 1 && Hq >= 1 && Hkv >= 1 && d >= 2 && max_ctx >= 1 && L_loc >= 1, MSA_ERR_INVALID_ARG,
               fn + ": non-positive size");
   MSA_REQUIRE(Hq % Hkv == 0, MSA_ERR_INVALID_ARG, fn + ": Hq % Hkv != 0");
@@ -943,7 +980,9 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
   MSA_REQUIRE(rope_base > 1.f, MSA_ERR_INVALID_ARG, fn + ": rope_base must exceed 1");
   MSA_REQUIRE(d <= 256, MSA_ERR_UNSUPPORTED, fn + ": d > 256");
   MSA_REQUIRE(int64_t(q_pos_offset) + L_loc < (int64_t(1) << 30), MSA_ERR_UNSUPPORTED, fn + ": positions too large");
-  const AttnPlan p = attn_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset);
+  const AttnPlan p = attn_plan(dtype, B, T, Hq, Hkv, d, max_ctx, L_loc, q_pos_offset, part);
+  MSA_REQUIRE(part == 0 || p.mfma, MSA_ERR_UNSUPPORTED,
+              fn + ": the two-call form needs the MFMA path (bf16, d = 128, Hq/Hkv in {1, 2, 4, 8, 16})");
   MSA_REQUIRE(ws_bytes >= p.tab_bytes + p.o_bytes + p.ml_bytes, MSA_ERR_WORKSPACE, fn + ": workspace too small");
   if (!p.mfma)
     MSA_REQUIRE(int64_t(max_ctx) + L_loc <= AT_VEC_MAX_KEYS, MSA_ERR_UNSUPPORTED,
@@ -967,12 +1006,23 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
                 MSA_ERR_INVALID_ARG, fn + ": tensors must be 16-byte aligned");
     uint16_t* ws_o = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.tab_bytes);
     float4* ws_ml = reinterpret_cast<float4*>(static_cast<char*>(ws) + p.tab_bytes + p.o_bytes);
+    if (local_part) {
+      // stand-ins for the context arguments, which the local part never
+      // dereferences: valid device addresses all the same
+      k_ctx = k_loc;
+      v_ctx = v_loc;
+      ctx_pos = ctx_len = reinterpret_cast<const int32_t*>(ws_ml);
+      ctx_row = nullptr;
+    }
+    // this launch's splits and the index of its first partial
+    const int n_launch = part == MSA_ATTN_PART_LOCAL ? p.n_sl : (part == MSA_ATTN_PART_CONTEXT ? p.n_sc : p.n_splits);
+    const int split_base = part == MSA_ATTN_PART_LOCAL ? p.n_sc : 0;
     const int G = Hq / Hkv;
     const float scale_log2_pf = sm_scale * 1.4426950408889634f;
     if (p.prefill) {
-      const bool fuse_prep = prep && p.n_splits == 1;
+      const bool fuse_prep = prep && part == 0 && p.n_splits == 1;
       const BwdPrep pp = fuse_prep ? *prep : BwdPrep{};
-      const dim3 pgrid(unsigned(int64_t(B) * Hkv * p.n_rg * p.n_splits)), pblock(PF_THREADS);
+      const dim3 pgrid(unsigned(int64_t(B) * Hkv * p.n_rg * n_launch)), pblock(PF_THREADS);
       const size_t psmem = 2 * size_t(PF_BUF) + PF_CIDX_BYTES;
 #define PF_LAUNCH2(GV, RV, IV)                                                                                      \
   MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefill_kernel<GV, RV, IV>),               \
@@ -980,8 +1030,8 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
   hipLaunchKernelGGL((attn_prefill_kernel<GV, RV, IV>), pgrid, pblock, psmem, s, static_cast<const uint16_t*>(q), B, T,  \
                      Hq, Hkv, static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos,     \
                      ctx_len, max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc),     \
-                     L_loc, q_pos_offset, ctx_row, ctx_rows, tab, p.P, scale_log2_pf, ws_o, ws_ml, p.n_splits,       \
-                     p.n_rt, p.n_rg, out, lse, pp)
+                     L_loc, q_pos_offset, ctx_row, ctx_rows, tab, p.P, scale_log2_pf, ws_o, ws_ml, n_launch,         \
+                     p.n_rt, p.n_rg, out, lse, part, split_base, pp)
 #define PF_LAUNCH(GV, RV)       \
   if (ctx_row) {                \
     PF_LAUNCH2(GV, RV, true);   \
@@ -1004,7 +1054,8 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
 #undef PF_LAUNCH
 #undef PF_LAUNCH2
       MSA_LAUNCH_CHECK();
-      if (p.n_splits == 1) {   // the prefill wrote out (or the backward's rows) and lse itself
+      if (local_part) return MSA_OK;   // the context part merges
+      if (part == 0 && p.n_splits == 1) {   // the prefill wrote out (or the backward's rows) and lse itself
         if (prep_done) *prep_done = fuse_prep;
         return MSA_OK;
       }
@@ -1015,7 +1066,7 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
       return MSA_OK;
     }
     const int nw = DC_WAVES;   // waves beyond Hkv only help stage the RoPE rows
-    const dim3 grid{unsigned(int64_t(B) * p.n_hg * p.n_splits)}, block{unsigned(DC_THREADS)};
+    const dim3 grid{unsigned(int64_t(B) * p.n_hg * n_launch)}, block{unsigned(DC_THREADS)};
     const size_t smem = 2 * size_t(DC_TAB_BYTES) + size_t(nw) * AT_V_BYTES + AT_CIDX_BYTES;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
 #define DC_LAUNCH2(GV, IV)                                                                                         \
@@ -1024,7 +1075,8 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
   hipLaunchKernelGGL((attn_decode_kernel<GV, IV>), grid, block, smem, s, static_cast<const uint16_t*>(q), B, T, Hq, Hkv, \
                      static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos, ctx_len,     \
                      max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc), L_loc,       \
-                     q_pos_offset, ctx_row, ctx_rows, tab, p.P, scale_log2, ws_o, ws_ml, p.n_splits, p.n_hg)
+                     q_pos_offset, ctx_row, ctx_rows, tab, p.P, scale_log2, ws_o, ws_ml, n_launch, p.n_hg, part,      \
+                     split_base)
 #define DC_LAUNCH(GV)        \
   if (ctx_row) {             \
     DC_LAUNCH2(GV, true);    \
@@ -1041,6 +1093,7 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
 #undef DC_LAUNCH
 #undef DC_LAUNCH2
     MSA_LAUNCH_CHECK();
+    if (local_part) return MSA_OK;
     const int64_t rows = int64_t(B) * T * Hq;
     hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned((rows * (d / 4) + 255) / 256)), dim3(256), 0, s, ws_o,
                        ws_ml, p.n_splits, rows, d, out, lse);
@@ -1088,6 +1141,22 @@ extern "C" int msa_sparse_attn_indexed(int dtype, const void* q, int B, int T, i
   return sparse_attn("msa_sparse_attn_indexed", dtype, q, B, T, Hq, Hkv, d, k_bar, v_bar, ctx_row, n_chunks, ctx_pos,
                      ctx_len, max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows,
                      sm_scale, out, nullptr, ws, ws_bytes, stream);
+}
+
+extern "C" int msa_sparse_attn_part(int part, int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
+                                    const void* k_ctx, const void* v_ctx, int64_t ctx_rows, const int32_t* ctx_row,
+                                    const int32_t* ctx_pos, const int32_t* ctx_len, int max_ctx, const void* k_loc,
+                                    const void* v_loc, int L_loc, int q_pos_offset, float rope_base,
+                                    const float* rope_table, int rope_table_rows, float sm_scale, float* out,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  using namespace msa;
+  const std::string fn = "msa_sparse_attn_part";
+  MSA_REQUIRE(part == MSA_ATTN_PART_LOCAL || part == MSA_ATTN_PART_CONTEXT, MSA_ERR_INVALID_ARG, fn + ": bad part");
+  MSA_REQUIRE(!ctx_row || (ctx_rows >= 1 && ctx_rows <= INT32_MAX), MSA_ERR_INVALID_ARG,
+              fn + ": ctx_rows must lie in [1, 2^31) with ctx_row");
+  return sparse_attn(fn, dtype, q, B, T, Hq, Hkv, d, k_ctx, v_ctx, ctx_row, ctx_row ? ctx_rows : 0, ctx_pos, ctx_len,
+                     max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows, sm_scale, out,
+                     nullptr, ws, ws_bytes, stream, nullptr, nullptr, part);
 }
 
 // ---------------------------------------------------------------- no-alloc variant

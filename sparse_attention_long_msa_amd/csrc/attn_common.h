@@ -225,12 +225,13 @@ struct BwdPrep {
 // a gathered context); lse, when given, receives per query row the base-2
 // log-sum-exp of the logits scaled by sm_scale * log2(e).  With prep, the
 // forward also does the backward's row preparation when its plan allows
-// (*prep_done tells).
+// (*prep_done tells).  part: 0 for the whole attention, MSA_ATTN_PART_LOCAL /
+// MSA_ATTN_PART_CONTEXT for the two calls of msa_sparse_attn_part.
 int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
                 const void* k_ctx, const void* v_ctx, const int32_t* ctx_row, int64_t ctx_rows, const int32_t* ctx_pos,
                 const int32_t* ctx_len, int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
                 int q_pos_offset, float rope_base, const float* rope_table, int rope_table_rows, float sm_scale,
                 float* out, float* lse, void* ws, size_t ws_bytes, void* stream, const BwdPrep* prep = nullptr,
-                bool* prep_done = nullptr);
+                bool* prep_done = nullptr, int part = 0);
 
 }  // namespace msa

@@ -9,6 +9,14 @@ outputs and workspaces so a loop over layers allocates nothing.
 With ``indexed=True`` (a device-resident K/V store) the context is not copied:
 assembly writes each context entry's store row and attention reads the rows in
 place; the result is bit-identical to the gathered path.
+
+With ``overlap_local=True`` the attention runs as its two parts
+(msa_sparse_attn_part): the local-window part on a side stream once the top-k
+is known, beside the context's fetch, which it does not need; the context
+part, with the merge, after both.  At the 100M-token preset's host tier this
+measured slower than one call after the fetch (the two streams' kernels slow
+each other, and the fork and join cost more than the overlap saves), so it is
+off by default; started earlier, beside the top-k, it was slower still.
 """
 from __future__ import annotations
 
@@ -23,11 +31,13 @@ class LayerRunner:
     def __init__(self, *, batch, tokens, q_heads, kv_heads, head_dim, n_docs, n_chunks, k, max_doc_chunks,
                  local_len, dtype, device, q_pos_offset=None, rope_base=1e6, sm_scale=None,
                  src_mode=B.MSA_SRC_DEVICE, chunk_off_h=None, kr_layout=B.MSA_LAYOUT_ROWS, indexed=False,
-                 rounds=1):
+                 rounds=1, overlap_local=False):
         if indexed and src_mode != B.MSA_SRC_DEVICE:
             raise ValueError("indexed assembly reads the K/V store in place: it must be in device memory")
         if rounds > 1 and not indexed:
             raise ValueError("Memory Interleave rounds grow an indexed context (K/V store in device memory)")
+        if rounds > 1 and overlap_local:
+            raise ValueError("Memory Interleave runs the attention in one call (overlap_local is for one round)")
         self.rounds = rounds
         self.B, self.T, self.Hq, self.Hkv, self.d = batch, tokens, q_heads, kv_heads, head_dim
         self.n_docs, self.n_chunks, self.k = n_docs, n_chunks, k
@@ -67,8 +77,12 @@ class LayerRunner:
 
         self.rs_ws = ws(B.msa_route_score_workspace(dt, batch, tokens, kv_heads, head_dim, n_docs, n_chunks))
         self.tk_ws = ws(B.msa_topk_workspace(batch, n_docs, k))
-        self.at_ws = ws(B.msa_sparse_attn_workspace(dt, batch, tokens, q_heads, kv_heads, head_dim, self.max_ctx,
-                                                    local_len, self.q_pos_offset))
+        self.overlap_local = overlap_local
+        at_ws = B.msa_sparse_attn_part_workspace if overlap_local else B.msa_sparse_attn_workspace
+        self.at_ws = ws(at_ws(dt, batch, tokens, q_heads, kv_heads, head_dim, self.max_ctx, local_len,
+                              self.q_pos_offset))
+        # default priority, like every other stream here
+        self.local_stream = torch.cuda.Stream(device=dev) if overlap_local else None
         # the RoPE (cos, sin) rows are the same for every layer: built once
         self.rope_table = B.msa_rope_table(B.msa_rope_table_rows(self.max_ctx, local_len, self.q_pos_offset),
                                            head_dim, rope_base, device=dev)
@@ -108,7 +122,33 @@ class LayerRunner:
                         chunk_off_h=self.chunk_off_h, k_ctx=self.k_ctx, v_ctx=self.v_ctx, ctx_pos=self.ctx_pos,
                         ctx_len=self.ctx_len, ids_h=self.ids_h, stream=stream, copy_stream=self.copy_stream)
 
+    def start_local(self, q, k_loc, v_loc, stream=None):
+        """overlap_local: the local-window part of the attention, on the side
+        stream, after the work already queued on `stream`.  q, k_loc and v_loc
+        must stay alive until attend() has been queued."""
+        cur = torch.cuda.current_stream() if stream is None else stream
+        self.local_stream.wait_stream(cur)
+        B.msa_sparse_attn_part(B.MSA_ATTN_PART_LOCAL, q, k_loc, v_loc, self.q_pos_offset, self.max_ctx,
+                               rope_base=self.rope_base, sm_scale=self.sm_scale, ws=self.at_ws,
+                               rope_table=self.rope_table, stream=self.local_stream)
+
     def attend(self, q, k_loc, v_loc, stream=None):
+        """The layer's attention into out; with overlap_local, its context part
+        and the merge, after start_local() has queued the local part."""
+        if self.overlap_local:
+            # the context part, after start_local's part: the two merge into out
+            cur = torch.cuda.current_stream() if stream is None else stream
+            cur.wait_stream(self.local_stream)
+            if self.indexed:
+                k_bar, v_bar = self._store
+                kw = dict(k_ctx=k_bar, v_ctx=v_bar, ctx_row=self.ctx_row)
+            else:
+                kw = dict(k_ctx=self.k_ctx, v_ctx=self.v_ctx)
+            B.msa_sparse_attn_part(B.MSA_ATTN_PART_CONTEXT, q, k_loc, v_loc, self.q_pos_offset, self.max_ctx,
+                                   ctx_pos=self.ctx_pos, ctx_len=self.ctx_len, rope_base=self.rope_base,
+                                   sm_scale=self.sm_scale, out=self.out, ws=self.at_ws, rope_table=self.rope_table,
+                                   stream=stream, **kw)
+            return self.out
         if self.indexed:
             k_bar, v_bar = self._store
             B.msa_sparse_attn_indexed(q, k_bar, v_bar, self.ctx_row, self.ctx_pos, self.ctx_len, k_loc, v_loc,
@@ -156,7 +196,16 @@ class LayerRunner:
 
     def run(self, q_r, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc, stream=None):
         self.route(q_r, kr_hat, chunk_doc, stream)
-        self.select_assemble(chunk_off, k_bar, v_bar, stream)
+        if not self.overlap_local:
+            self.select_assemble(chunk_off, k_bar, v_bar, stream)
+        elif self.indexed:
+            # the context index comes out of the top-k call itself: nothing to overlap
+            self.select_assemble(chunk_off, k_bar, v_bar, stream)
+            self.start_local(q, k_loc, v_loc, stream)
+        else:
+            self.select(stream)
+            self.start_local(q, k_loc, v_loc, stream)
+            self.assemble(chunk_off, k_bar, v_bar, stream)
         return self.attend(q, k_loc, v_loc, stream)
 
 

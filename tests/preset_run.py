@@ -175,7 +175,7 @@ class HostLayer:
 class GpuLayer:
     """Layer l of preset p built and run on the GPU through the C ABI."""
 
-    def __init__(self, p, l, host: HostLayer, src_mode=M.MSA_SRC_DEVICE, indexed=False):
+    def __init__(self, p, l, host: HostLayer, src_mode=M.MSA_SRC_DEVICE, indexed=False, overlap_local=False):
         self.p, self.l = p, l
         d0 = dev()
         bf = torch.bfloat16 if p.bf16 else torch.float32
@@ -216,7 +216,7 @@ class GpuLayer:
                                     local_len=p.L_loc, dtype=bf, device=d0, q_pos_offset=p.qpo,
                                     rope_base=p.rope_base, src_mode=src_mode, chunk_off_h=co,
                                     kr_layout=M.MSA_LAYOUT_TILED if p.bf16 else M.MSA_LAYOUT_ROWS,
-                                    indexed=indexed)
+                                    indexed=indexed, overlap_local=overlap_local)
 
     def run(self):
         r = self.runner

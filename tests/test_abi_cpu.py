@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.msa_abi_version() == 10
+    assert M.msa_abi_version() == 11
     assert M.lib.msa_status_string(0).decode() == "ok"
     assert "workspace" in M.lib.msa_status_string(3).decode()
 
@@ -174,6 +174,25 @@ def test_sparse_attn_indexed_validation():
     assert call(q=None) == 1
     assert call(wsb=16) == 3
     assert "msa_sparse_attn_indexed" in L.msa_last_error().decode()
+
+
+def test_sparse_attn_part_validation():
+    L = M.lib
+
+    def call(part=1, dtype=1, kc=None, cl=None, row=None, rows=0, wsb=1 << 30, d=128, out=None):
+        return L.msa_sparse_attn_part(part, dtype, P, 1, 4, 32, 8, d, kc, kc, rows, row, cl, cl, 16, P, P, 8, 4,
+                                      1e6, None, 0, 0.088, out, P, wsb, None)
+    assert call(part=0) == 1 and call(part=3) == 1
+    # the local part takes no context arguments: a NULL context passes validation
+    assert call(part=1, wsb=16) == 3
+    assert call(part=2) == 1                                  # the context part needs them
+    assert call(part=2, kc=P, cl=P, row=P, rows=0, out=P) == 1    # ctx_rows with ctx_row
+    assert call(part=2, kc=P, cl=P, wsb=16) == 1                  # ... and out
+    assert call(part=2, kc=P, cl=P, wsb=16, out=P) == 3
+    assert call(dtype=0) == 2                                 # float32: off the MFMA path
+    assert call(d=64) == 2
+    assert L.msa_sparse_attn_part_workspace(1, 1, 64, 32, 8, 128, 128, 4096, 16) > 0
+    assert "msa_sparse_attn_part" in L.msa_last_error().decode()
 
 
 def test_sparse_attn_validation():

@@ -16,8 +16,12 @@ pytestmark = pytest.mark.gpu
 import sparse_attention_long_msa_amd as M  # noqa: E402  (a missing library fails loudly)
 
 
-@pytest.mark.parametrize("B,T,L_loc,k", [(1, 64, 512, 8), (8, 1, 1024, 4)])
-def test_step_graph_replays_equal_the_eager_step(B, T, L_loc, k):
+@pytest.mark.parametrize("B,T,L_loc,k,overlap,indexed", [(1, 64, 512, 8, False, True), (8, 1, 1024, 4, False, True),
+                                                           (1, 64, 512, 8, True, True), (8, 1, 1024, 4, True, True),
+                                                           (1, 64, 512, 8, True, False)])
+def test_step_graph_replays_equal_the_eager_step(B, T, L_loc, k, overlap, indexed):
+    """overlap: the attention's local part on a side stream (two streams in
+    the captured graph); indexed: the context read in place, else gathered."""
     H, d, Hq, layers = 8, 128, 32, 3
     lens = ragged_lengths(90 + B, 700, 0, 900, n_empty=9)
     tok_off = synth.offsets(lens)
@@ -38,7 +42,7 @@ def test_step_graph_replays_equal_the_eager_step(B, T, L_loc, k):
         x["dev"] = [to_dev(tile_np(store), True)] + [to_dev(x[n], True) for n in ("kb", "vb", "qr", "q", "kl", "vl")]
         x["run"] = M.LayerRunner(batch=B, tokens=T, q_heads=Hq, kv_heads=H, head_dim=d, n_docs=D, n_chunks=n_chunks,
                                  k=k, max_doc_chunks=mdc, local_len=L_loc, dtype=torch.bfloat16, device=dev(),
-                                 kr_layout=M.MSA_LAYOUT_TILED, indexed=True)
+                                 kr_layout=M.MSA_LAYOUT_TILED, indexed=indexed, overlap_local=overlap)
         L.append(x)
 
     def step():
@@ -46,7 +50,7 @@ def test_step_graph_replays_equal_the_eager_step(B, T, L_loc, k):
             kr, kb, vb, qr, q, kl, vl = x["dev"]
             x["run"].run(qr, kr, cd, co_d, kb, vb, q, kl, vl)
 
-    names = ("doc_score", "ids", "vals", "ctx_row", "ctx_pos", "ctx_len", "out")
+    names = ("doc_score", "ids", "vals", "ctx_row" if indexed else "k_ctx", "ctx_pos", "ctx_len", "out")
     step()
     torch.cuda.synchronize()
     eager = [{n: getattr(x["run"], n).clone() for n in names} for x in L]
@@ -64,7 +68,7 @@ def test_step_graph_replays_equal_the_eager_step(B, T, L_loc, k):
                 assert torch.equal(getattr(r, n), eager[l][n]), f"replay {rep}, layer {l}: {n}"
             for b in range(B):                        # the context entries (rows past ctx_len are not written)
                 n_b = int(eager[l]["ctx_len"][b])
-                for n in ("ctx_row", "ctx_pos"):
+                for n in (names[3], "ctx_pos"):
                     assert torch.equal(getattr(r, n)[b, :n_b], eager[l][n][b, :n_b]), f"replay {rep}, layer {l}: {n}"
     # the eager outputs against the oracle
     for l, x in enumerate(L):
@@ -75,16 +79,18 @@ def test_step_graph_replays_equal_the_eager_step(B, T, L_loc, k):
         assert np.abs(host(eager[l]["out"]) - ref["out"]).max() <= ATOL_ATTN["bf16"]
 
 
-@pytest.mark.parametrize("name", ["cfg2", "cfg5", "cfg4"])
-def test_step_graph_full_size(name):
+@pytest.mark.parametrize("name,overlap", [("cfg2", True), ("cfg5", True), ("cfg4", True), ("cfg4", False)])
+def test_step_graph_full_size(name, overlap):
     """The bench's graph-replayed step at the full presets (two routed layers of
     the 1M-token, batched-decode and 100M-token workloads, context read in
-    place): every replay equals the eager step bit for bit.  The eager step is
-    checked against the oracle by the preset parity tests."""
+    place, the attention as its two calls with the local part on a side stream, and the
+    100M-token step with one attention call): every replay equals the eager
+    step bit for bit.  The eager step is checked against the oracle by the
+    preset parity tests."""
     from synth import configs
     from tests.preset_run import GpuLayer, HostLayer
     p = getattr(configs, name)()
-    layers = [GpuLayer(p, l, HostLayer(p, l), indexed=True) for l in (0, 1)]
+    layers = [GpuLayer(p, l, HostLayer(p, l), indexed=True, overlap_local=overlap) for l in (0, 1)]
 
     def step():
         for gl in layers:

@@ -534,6 +534,65 @@ def test_sparse_attention(bf16, B, T, L_loc, ctx):
     print(f"attention bf16={bf16} B={B} T={T}: max-abs {worst:.3g}")
 
 
+@pytest.mark.parametrize("B,T,L_loc,ctx,indexed", [
+    (1, 64, 4096, [128], False),          # the 100M-token preset's shape, gathered (host-tier) context
+    (1, 64, 4096, [128], True),           # the same, context read in place
+    (32, 1, 8192, None, True),            # batched decode (decode kernel)
+    (2, 3, 50, [0, 77], False),           # an empty context, ragged lengths
+    (4, 1, 1, [5, 0, 31, 64], False),     # one local token
+    (1, 128, 300, [1000], True),          # two row groups
+    (2, 64, 64, [5000, 4100], True),      # context over the LDS index cache: several context splits
+    (1, 16, 16, [0], False),              # no context at all: the context part only merges
+])
+def test_sparse_attention_two_calls(B, T, L_loc, ctx, indexed):
+    """msa_sparse_attn_part: the local call on a side stream (it reads no
+    context), the context call after it on the main stream; the oracle within
+    the attention tolerance, and msa_sparse_attn within the same bound."""
+    Hq, Hkv, d, qpo, n_rows = 32, 8, 128, 16, 6000
+    if ctx is None:
+        ctx = list(np.random.default_rng(2).integers(100, 2048, size=B))
+    max_ctx = max(max(ctx), 1)
+    seed = 110 + T
+    q = gen(seed, 0, synth.T_Q, (B, T, Hq, d), True)
+    kl = gen(seed, 0, synth.T_KLOC, (B, L_loc, Hkv, d), True)
+    vl = gen(seed, 0, synth.T_VLOC, (B, L_loc, Hkv, d), True)
+    kst = gen(seed, 0, synth.T_K, (n_rows, Hkv, d), True, scale_pow2=-3)
+    vst = gen(seed, 0, synth.T_V, (n_rows, Hkv, d), True, scale_pow2=-3)
+    r = np.random.default_rng(seed)
+    rows = r.integers(0, n_rows, size=(B, max_ctx)).astype(np.int32)
+    cp = r.integers(0, min(128, max_ctx), size=(B, max_ctx)).astype(np.int32)
+    cl = np.asarray(ctx, dtype=np.int32)
+    d_rows, d_cp, d_cl = (torch.from_numpy(a).to(dev()) for a in (rows, cp, cl))
+    kst_d, vst_d = to_dev(kst, True), to_dev(vst, True)
+    qd, kld, vld = to_dev(q, True), to_dev(kl, True), to_dev(vl, True)
+    kc_d, vc_d = kst_d[d_rows.long()].contiguous(), vst_d[d_rows.long()].contiguous()
+    ws = torch.empty(M.msa_sparse_attn_part_workspace(M.MSA_BF16, B, T, Hq, Hkv, d, max_ctx, L_loc, qpo),
+                     dtype=torch.uint8, device=dev())
+    side, main = torch.cuda.Stream(), torch.cuda.current_stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        M.msa_sparse_attn_part(M.MSA_ATTN_PART_LOCAL, qd, kld, vld, qpo, max_ctx, ws=ws, stream=side)
+    main.wait_stream(side)
+    if indexed:
+        out = M.msa_sparse_attn_part(M.MSA_ATTN_PART_CONTEXT, qd, kld, vld, qpo, max_ctx, k_ctx=kst_d, v_ctx=vst_d,
+                                     ctx_row=d_rows, ctx_pos=d_cp, ctx_len=d_cl, ws=ws)
+    else:
+        out = M.msa_sparse_attn_part(M.MSA_ATTN_PART_CONTEXT, qd, kld, vld, qpo, max_ctx, k_ctx=kc_d, v_ctx=vc_d,
+                                     ctx_pos=d_cp, ctx_len=d_cl, ws=ws)
+    whole = M.msa_sparse_attn(qd, kc_d, vc_d, d_cp, d_cl, kld, vld, qpo)
+    got = host(out)
+    assert np.isfinite(got).all()
+    e_whole = np.abs(got - host(whole)).max()
+    assert e_whole <= ATOL_ATTN["bf16"], f"against msa_sparse_attn: max-abs {e_whole}"
+    sm = 1.0 / math.sqrt(d)
+    for b in (range(B) if B <= 4 else [0, 13, 31]):
+        n = int(cl[b])
+        ref = O.attend_one(q[b], kst[rows[b, :n]], vst[rows[b, :n]], cp[b, :n], kl[b], vl[b], qpo, 1e6, sm)
+        e = np.abs(got[b] - ref).max()
+        assert e <= ATOL_ATTN["bf16"], f"b={b}: max-abs {e}"
+    print(f"two-call attention B={B} T={T} indexed={indexed}: against msa_sparse_attn {e_whole:.3g}")
+
+
 def test_rope_table_values_and_reuse():
     rows, d, base = M.msa_rope_table_rows(2048, 8192, 16), 128, 1e6
     tab = M.msa_rope_table(rows, d, base, device=dev()).cpu().numpy().astype(np.float64)
