@@ -356,16 +356,20 @@ struct PfRegs {
   uint4 v;            // V[t/16][8*(t%16) .. +7]
 };
 
-template <int G, int RTW, bool IDX>
+// PRE: the keys come already rotated and in key order, k_ctx/v_ctx being
+// [B, km, Hkv, d] with key j of query b at row b * km + j (context entries,
+// then the local tokens, zero past the query's keys): the prepared keys of the
+// backward, so that its forward recompute neither rotates nor looks keys up.
+template <int G, int RTW, bool IDX, bool PRE = false>
 __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int B, int T, int Hq, int Hkv, const uint16_t* __restrict__ k_ctx,
     const uint16_t* __restrict__ v_ctx, const int32_t* __restrict__ ctx_pos, const int32_t* __restrict__ ctx_len,
     int max_ctx, const uint16_t* __restrict__ k_loc, const uint16_t* __restrict__ v_loc, int L_loc, int qpo,
     const int32_t* __restrict__ ctx_row_in, int64_t ctx_rows, const float2* __restrict__ tab, int P, float scale_log2,
     uint16_t* __restrict__ ws_o, float4* __restrict__ ws_ml, int n_splits, int n_rt, int n_rg, float* __restrict__ out,
-    float* __restrict__ lse, int part, int split_base, BwdPrep prep) {
+    float* __restrict__ lse, int part, int split_base, int km, BwdPrep prep) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int32_t* __restrict__ ctx_row = IDX ? ctx_row_in : nullptr;
+  const int32_t* __restrict__ ctx_row = IDX && !PRE ? ctx_row_in : nullptr;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int lc = lane % 16, g4 = lane / 16;
 
@@ -422,8 +426,9 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
 
   // cooperative mapping of one 32-key step
   const int lk = tid / 16, lx = tid % 16;     // K: key, 4-dim block; V: key, 8-dim block
-  const CtxCache cc = stage_ctx(reinterpret_cast<int2*>(smem + 2 * size_t(PF_BUF)), PF_CIDX, b, j_begin, j_end, ctxl, max_ctx,
-                                ctx_pos, P, ctx_row, ctx_rows, tid, PF_THREADS);
+  // prepared keys need no index: the cache stays empty
+  const CtxCache cc = stage_ctx(reinterpret_cast<int2*>(smem + 2 * size_t(PF_BUF)), PF_CIDX, b, j_begin,
+                                PRE ? j_begin : j_end, ctxl, max_ctx, ctx_pos, P, ctx_row, ctx_rows, tid, PF_THREADS);
   __syncthreads();
 
   // a step whose 32 keys are all local tokens addresses them affinely
@@ -436,6 +441,16 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
   const int64_t loc_kv = (int64_t(b) * L_loc - ctxl + lk) * kv_stride + int64_t(g) * AT_D;
   const int64_t loc_tab = int64_t(qpo - ctxl + lk) * (AT_D / 2) + 4 * lx;
   auto load_step = [&](int j0) {
+    PfRegs R;
+    if constexpr (PRE) {
+      // row b * km + j (clamped into the query's rows; keys past n_keys are masked)
+      const int64_t off = (int64_t(b) * km + min(j0 + lk, km - 1)) * kv_stride + int64_t(g) * AT_D;
+      R.klo = load_global8(k_ctx + off + 4 * lx);
+      R.khi = load_global8(k_ctx + off + 4 * lx + 64);
+      R.cs0 = R.cs1 = make_float4(0.f, 0.f, 0.f, 0.f);
+      R.v = load_global(v_ctx + off + 8 * lx);
+      return R;
+    }
     const uint16_t* kp;
     const uint16_t* vp;
     const float2* tp;
@@ -451,7 +466,6 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
       vp = (ks.local ? v_loc : v_ctx) + off + 8 * lx;
       tp = tab + int64_t(ks.pos) * (AT_D / 2) + 4 * lx;
     }
-    PfRegs R;
     R.klo = load_global8(kp);
     R.khi = load_global8(kp + 64);
     R.cs0 = __builtin_bit_cast(float4, load_global(tp));
@@ -460,6 +474,13 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     return R;
   };
   auto store_step = [&](const PfRegs& R, unsigned char* buf) {
+    if constexpr (PRE) {   // already rotated: stored as loaded
+      unsigned char* krow = buf + lk * PF_KS;
+      *reinterpret_cast<uint2*>(krow + 8 * lx) = R.klo;
+      *reinterpret_cast<uint2*>(krow + 128 + 8 * lx) = R.khi;
+      *reinterpret_cast<uint4*>(buf + PF_K_BYTES + lk * AT_VS + 16 * lx) = R.v;
+      return;
+    }
     // rotate the 4 (m, m+64) pairs of this thread and store K_rot[key][d]
     const float c[4] = {R.cs0.x, R.cs0.z, R.cs1.x, R.cs1.z};
     const float sn[4] = {R.cs0.y, R.cs0.w, R.cs1.y, R.cs1.w};
@@ -963,7 +984,7 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
                 const int32_t* ctx_len, int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
                 int q_pos_offset, float rope_base, const float* rope_table, int rope_table_rows, float sm_scale,
                 float* out, float* lse, void* ws, size_t ws_bytes, void* stream, const BwdPrep* prep,
-                bool* prep_done, int part) {
+                bool* prep_done, int part, bool check_only) {
   if (prep_done) *prep_done = false;
   MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
   MSA_REQUIRE(part == 0 || part == MSA_ATTN_PART_LOCAL || part == MSA_ATTN_PART_CONTEXT, MSA_ERR_INVALID_ARG,
@@ -990,6 +1011,11 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
   MSA_REQUIRE(!rope_table || rope_table_rows >= p.P, MSA_ERR_INVALID_ARG,
               fn + ": rope_table has fewer rows than msa_rope_table_rows()");
   MSA_REQUIRE(uintptr_t(rope_table) % 16 == 0, MSA_ERR_INVALID_ARG, fn + ": rope_table must be 16-byte aligned");
+  if (p.mfma)
+    MSA_REQUIRE(uintptr_t(q) % 16 == 0 && uintptr_t(k_ctx) % 16 == 0 && uintptr_t(v_ctx) % 16 == 0 &&
+                    uintptr_t(k_loc) % 16 == 0 && uintptr_t(v_loc) % 16 == 0,
+                MSA_ERR_INVALID_ARG, fn + ": tensors must be 16-byte aligned");
+  if (check_only) return MSA_OK;
   hipStream_t s = as_stream(stream);
   const float2* tab = reinterpret_cast<const float2*>(rope_table);
   if (!tab) {
@@ -1001,9 +1027,6 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
     tab = wtab;
   }
   if (p.mfma) {
-    MSA_REQUIRE(uintptr_t(q) % 16 == 0 && uintptr_t(k_ctx) % 16 == 0 && uintptr_t(v_ctx) % 16 == 0 &&
-                    uintptr_t(k_loc) % 16 == 0 && uintptr_t(v_loc) % 16 == 0,
-                MSA_ERR_INVALID_ARG, fn + ": tensors must be 16-byte aligned");
     uint16_t* ws_o = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.tab_bytes);
     float4* ws_ml = reinterpret_cast<float4*>(static_cast<char*>(ws) + p.tab_bytes + p.o_bytes);
     if (local_part) {
@@ -1022,21 +1045,26 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
     if (p.prefill) {
       const bool fuse_prep = prep && part == 0 && p.n_splits == 1;
       const BwdPrep pp = fuse_prep ? *prep : BwdPrep{};
+      const bool pre = prep && prep->krot && prep->vg && part == 0;   // the backward's prepared keys
+      const uint16_t* kk_src = static_cast<const uint16_t*>(pre ? prep->krot : k_ctx);
+      const uint16_t* vv_src = static_cast<const uint16_t*>(pre ? prep->vg : v_ctx);
+      const int km = pre ? prep->km : 0;
       const dim3 pgrid(unsigned(int64_t(B) * Hkv * p.n_rg * n_launch)), pblock(PF_THREADS);
       const size_t psmem = 2 * size_t(PF_BUF) + PF_CIDX_BYTES;
-#define PF_LAUNCH2(GV, RV, IV)                                                                                      \
-  MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefill_kernel<GV, RV, IV>),               \
+#define PF_LAUNCH3(GV, RV, IV, PV)                                                                                  \
+  MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefill_kernel<GV, RV, IV, PV>),           \
                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(psmem)));                       \
-  hipLaunchKernelGGL((attn_prefill_kernel<GV, RV, IV>), pgrid, pblock, psmem, s, static_cast<const uint16_t*>(q), B, T,  \
-                     Hq, Hkv, static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), ctx_pos,     \
-                     ctx_len, max_ctx, static_cast<const uint16_t*>(k_loc), static_cast<const uint16_t*>(v_loc),     \
-                     L_loc, q_pos_offset, ctx_row, ctx_rows, tab, p.P, scale_log2_pf, ws_o, ws_ml, n_launch,         \
-                     p.n_rt, p.n_rg, out, lse, part, split_base, pp)
-#define PF_LAUNCH(GV, RV)       \
-  if (ctx_row) {                \
-    PF_LAUNCH2(GV, RV, true);   \
-  } else {                      \
-    PF_LAUNCH2(GV, RV, false);  \
+  hipLaunchKernelGGL((attn_prefill_kernel<GV, RV, IV, PV>), pgrid, pblock, psmem, s, static_cast<const uint16_t*>(q), B, \
+                     T, Hq, Hkv, kk_src, vv_src, ctx_pos, ctx_len, max_ctx, static_cast<const uint16_t*>(k_loc),     \
+                     static_cast<const uint16_t*>(v_loc), L_loc, q_pos_offset, ctx_row, ctx_rows, tab, p.P,          \
+                     scale_log2_pf, ws_o, ws_ml, n_launch, p.n_rt, p.n_rg, out, lse, part, split_base, km, pp)
+#define PF_LAUNCH(GV, RV)                 \
+  if (pre) {                              \
+    PF_LAUNCH3(GV, RV, false, true);      \
+  } else if (ctx_row) {                   \
+    PF_LAUNCH3(GV, RV, true, false);      \
+  } else {                                \
+    PF_LAUNCH3(GV, RV, false, false);     \
   }
       const int key = G * 4 + p.rtw;
       switch (key) {
@@ -1052,7 +1080,7 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
         default: PF_LAUNCH(16, 2); break;
       }
 #undef PF_LAUNCH
-#undef PF_LAUNCH2
+#undef PF_LAUNCH3
       MSA_LAUNCH_CHECK();
       if (local_part) return MSA_OK;   // the context part merges
       if (part == 0 && p.n_splits == 1) {   // the prefill wrote out (or the backward's rows) and lse itself

@@ -846,22 +846,49 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
   float* part_v = reinterpret_cast<float*>(reinterpret_cast<char*>(part_k) + p.part_bytes);
   uint16_t* krot = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(part_v) + p.part_bytes);
   uint16_t* vgat = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(krot) + p.key_bytes);
-  // the forward (validates every shared argument) with the per-row log-sum-exp
-  // on the MFMA path the forward may also prepare the rows (D, bf16 dO and rotated query)
+  // every argument the forward shares is checked before any launch
+  {
+    const int rc = sparse_attn(fn, dtype, q, B, T, Hq, Hkv, d, k_bar, v_bar, ctx_row, n_chunks, ctx_pos, ctx_len,
+                               max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows,
+                               sm_scale, out, lse, ws, p.fwd_bytes, stream, nullptr, nullptr, 0, true);
+    if (rc != MSA_OK) return rc;
+  }
+  hipStream_t s = as_stream(stream);
+  const int P = rope_rows(max_ctx, L_loc, q_pos_offset);
+  if (!rope_table) {
+    // the RoPE rows at the start of the forward's workspace, before the keys are prepared
+    const int rc = msa_rope_table(P, d, rope_base, static_cast<float*>(ws), stream);
+    if (rc != MSA_OK) return rc;
+    rope_table = static_cast<const float*>(ws);
+    rope_table_rows = P;
+  }
+  const float2* tab = reinterpret_cast<const float2*>(rope_table);
+  const int KMK = max_ctx + L_loc;   // keys per query in the prepared key buffers
+  if (p.mfma) {
+    // every key of every query rotated once, in key order: the forward below
+    // and both backward kernels read these
+    const int64_t n = int64_t(B) * KMK * Hkv * 8;
+    hipLaunchKernelGGL(bwd_keys_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, B, KMK, Hkv,
+                       static_cast<const uint16_t*>(k_bar), static_cast<const uint16_t*>(v_bar), n_chunks, ctx_row,
+                       ctx_pos, ctx_len, max_ctx, static_cast<const uint16_t*>(k_loc),
+                       static_cast<const uint16_t*>(v_loc), L_loc, q_pos_offset, tab, P, krot, vgat);
+    MSA_LAUNCH_CHECK();
+  }
+  // the forward with the per-row log-sum-exp; on the MFMA path it may also
+  // prepare the rows (D, bf16 dO and rotated query)
   BwdPrep prep;
   prep.dout = dout;
   prep.Dv = Dv;
   prep.qs16 = qs16;
   prep.do16 = do16;
+  prep.krot = krot;
+  prep.vg = vgat;
+  prep.km = KMK;
   bool prep_done = false;
   const int rc = sparse_attn(fn, dtype, q, B, T, Hq, Hkv, d, k_bar, v_bar, ctx_row, n_chunks, ctx_pos, ctx_len,
                              max_ctx, k_loc, v_loc, L_loc, q_pos_offset, rope_base, rope_table, rope_table_rows,
                              sm_scale, out, lse, ws, p.fwd_bytes, stream, p.mfma ? &prep : nullptr, &prep_done);
   if (rc != MSA_OK) return rc;
-  hipStream_t s = as_stream(stream);
-  // the forward built the RoPE rows at the start of its workspace when none were given
-  const float2* tab = reinterpret_cast<const float2*>(rope_table ? rope_table : static_cast<const float*>(ws));
-  const int P = rope_rows(max_ctx, L_loc, q_pos_offset);
   const int64_t rows = int64_t(B) * T * Hq;
   const int G = Hq / Hkv;
   const unsigned prep_grid = unsigned((rows + BW_WAVES - 1) / BW_WAVES);
@@ -872,20 +899,8 @@ extern "C" int msa_sparse_attn_backward(int dtype, const void* q, int B, int T, 
                          sm_scale * BW_LOG2E, out, dout, rows, Dv, qs16, do16);
       MSA_LAUNCH_CHECK();
     }
-    const uint16_t* kb = static_cast<const uint16_t*>(k_bar);
-    const uint16_t* vb = static_cast<const uint16_t*>(v_bar);
-    const uint16_t* kl = static_cast<const uint16_t*>(k_loc);
-    const uint16_t* vl = static_cast<const uint16_t*>(v_loc);
     const dim3 kgrid(unsigned(int64_t(B) * Hkv * p.n_items)),
         qgrid(unsigned(int64_t(B) * Hkv * p.n_rg * p.n_splits));
-
-    const int KMK = max_ctx + L_loc;   // keys per query in the prepared key buffers
-    {
-      const int64_t n = int64_t(B) * KMK * Hkv * 8;
-      hipLaunchKernelGGL(bwd_keys_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, B, KMK, Hkv, kb, vb,
-                         n_chunks, ctx_row, ctx_pos, ctx_len, max_ctx, kl, vl, L_loc, q_pos_offset, tab, P, krot, vgat);
-      MSA_LAUNCH_CHECK();
-    }
 #define BW_LAUNCH(GV)                                                                                              \
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<GV>), kgrid, dim3(BW_THREADS), 0, s, B, T, Hq, Hkv, krot, vgat, KMK,   \
                      ctx_len, max_ctx, L_loc, qs16, do16, lse, Dv, p.n_kb, p.rt_per, p.n_items, part_k, part_v);    \

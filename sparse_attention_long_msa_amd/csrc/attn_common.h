@@ -219,6 +219,12 @@ struct BwdPrep {
   float* Dv = nullptr;
   uint16_t* qs16 = nullptr;
   uint16_t* do16 = nullptr;
+  // the backward's prepared keys (rotated K and V in key order, [B, km, Hkv, d]),
+  // when already written: the prefill forward then reads them instead of
+  // rotating and looking up every key itself
+  const uint16_t* krot = nullptr;
+  const uint16_t* vg = nullptr;
+  int km = 0;
 };
 
 // The forward of msa_sparse_attn / msa_sparse_attn_indexed (ctx_row NULL for
@@ -226,12 +232,14 @@ struct BwdPrep {
 // log-sum-exp of the logits scaled by sm_scale * log2(e).  With prep, the
 // forward also does the backward's row preparation when its plan allows
 // (*prep_done tells).  part: 0 for the whole attention, MSA_ATTN_PART_LOCAL /
-// MSA_ATTN_PART_CONTEXT for the two calls of msa_sparse_attn_part.
+// MSA_ATTN_PART_CONTEXT for the two calls of msa_sparse_attn_part.  check_only:
+// validate the arguments (the status a call would return before launching) and
+// launch nothing.
 int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, int Hq, int Hkv, int d,
                 const void* k_ctx, const void* v_ctx, const int32_t* ctx_row, int64_t ctx_rows, const int32_t* ctx_pos,
                 const int32_t* ctx_len, int max_ctx, const void* k_loc, const void* v_loc, int L_loc,
                 int q_pos_offset, float rope_base, const float* rope_table, int rope_table_rows, float sm_scale,
                 float* out, float* lse, void* ws, size_t ws_bytes, void* stream, const BwdPrep* prep = nullptr,
-                bool* prep_done = nullptr, int part = 0);
+                bool* prep_done = nullptr, int part = 0, bool check_only = false);
 
 }  // namespace msa
