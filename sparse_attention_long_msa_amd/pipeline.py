@@ -83,6 +83,7 @@ class LayerRunner:
                               self.q_pos_offset))
         # default priority, like every other stream here
         self.local_stream = torch.cuda.Stream(device=dev) if overlap_local else None
+        self._local_queued = False
         # the RoPE (cos, sin) rows are the same for every layer: built once
         self.rope_table = B.msa_rope_table(B.msa_rope_table_rows(self.max_ctx, local_len, self.q_pos_offset),
                                            head_dim, rope_base, device=dev)
@@ -126,17 +127,23 @@ class LayerRunner:
         """overlap_local: the local-window part of the attention, on the side
         stream, after the work already queued on `stream`.  q, k_loc and v_loc
         must stay alive until attend() has been queued."""
+        if not self.overlap_local:
+            raise RuntimeError("start_local needs LayerRunner(overlap_local=True)")
         cur = torch.cuda.current_stream() if stream is None else stream
         self.local_stream.wait_stream(cur)
         B.msa_sparse_attn_part(B.MSA_ATTN_PART_LOCAL, q, k_loc, v_loc, self.q_pos_offset, self.max_ctx,
                                rope_base=self.rope_base, sm_scale=self.sm_scale, ws=self.at_ws,
                                rope_table=self.rope_table, stream=self.local_stream)
+        self._local_queued = True
 
     def attend(self, q, k_loc, v_loc, stream=None):
         """The layer's attention into out; with overlap_local, its context part
         and the merge, after start_local() has queued the local part."""
         if self.overlap_local:
             # the context part, after start_local's part: the two merge into out
+            if not self._local_queued:
+                raise RuntimeError("overlap_local: start_local() must queue the local part before attend()")
+            self._local_queued = False
             cur = torch.cuda.current_stream() if stream is None else stream
             cur.wait_stream(self.local_stream)
             if self.indexed:
