@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the per-config lines of the smaller presets (after the 100M-token line)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    ap.add_argument("--no-balance", action="store_true",
+                    help="keep the routing scan's chunk ranges equal over the XCDs (by default msa_route_balance "
+                         "sizes them per XCD from timed launches before the timed region)")
     ap.add_argument("--overlap", action="store_true",
                     help="on the host tier, run each layer's attention as its two calls, the local-window part on "
                          "a side stream beside the fetch (measured slower than one call after the fetch)")
@@ -118,6 +121,7 @@ def main():
     pb.build_content("hbm")
     assembly = args.hbm_assembly if args.rounds == 1 else "index"
     pb.make_runner("hbm", indexed=assembly == "index")
+    shares = pb.balance(not args.no_balance)
     recall = pb.needle_recall()
     hbm = pb.headline(args.steps, args.warmup)
     hbm["config"]["gather"] = f"hbm-{assembly}"
@@ -139,6 +143,7 @@ def main():
         pb.make_runner("hbm", indexed=assembly == "index")
         res["roofline"] = hbm["roofline"]
     res["needle_recall_layer0"] = recall
+    res["config"]["xcd_shares"] = shares
     if not args.no_ceiling:
         res["ceiling"] = pb.ceiling()
     if p.name == "cfg4" and args.rounds == 1 and not args.no_memory_parallel:
@@ -245,6 +250,15 @@ class PresetBench:
         torch.cuda.synchronize()
         self.raw = None
         log(f"content K/V ({tier}) ready in {time.time() - t0:.1f} s")
+
+    def balance(self, on=True):
+        """msa_route_balance on layer 0's store and query before any timing (the
+        shares hold for the device); off: equal ranges.  Returns the shares used."""
+        r = self.runner
+        shares = r.balance(self.qr[0], self.store[0], self.cd, rounds=4 if on else 0)
+        self.torch.cuda.synchronize()
+        log(f"routing scan split per XCD: {' '.join(f'{v:.4f}' for v in shares)}")
+        return [round(float(v), 4) for v in shares]
 
     def make_runner(self, tier, indexed, src_mode=None, overlap=None):
         p, M = self.p, self.M

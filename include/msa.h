@@ -19,7 +19,9 @@
  *    human-readable detail of the last failure on the calling thread.
  *  - Ownership: the caller owns every buffer.  The library allocates no
  *    device or host memory; scratch space comes from the caller through
- *    `ws` / `ws_bytes`, sized by the matching *_workspace query.
+ *    `ws` / `ws_bytes`, sized by the matching *_workspace query.  (The one
+ *    exception is msa_route_balance, a setup-time calibration that allocates
+ *    and frees a 4 KB timing buffer.)
  *  - Pointers are device pointers unless the name ends in `_h` (host).
  *    Device buffers must be 16-byte aligned.
  *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
@@ -31,8 +33,10 @@
  *  - dtype: MSA_F32 or MSA_BF16 (bfloat16 stored as its 16-bit pattern).
  *  - Device faults of an enqueued kernel surface as MSA_ERR_HIP from the
  *    launch check or at the caller's next synchronisation.
- *  - No mutable global state: calls on distinct streams may run from
- *    different threads.
+ *  - Calls on distinct streams may run from different threads.  The one
+ *    mutable global state is the per-device XCD split of the routing scan set
+ *    by msa_route_balance (guarded by a lock); it changes how later routing
+ *    launches divide their chunks, never their results.
  */
 #ifndef MSA_H_
 #define MSA_H_
@@ -226,6 +230,31 @@ size_t msa_route_score_workspace(int dtype, int B, int T, int H, int d, int64_t 
 int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat, int kr_layout,
                     const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks, float* doc_score,
                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * msa_route_balance - sizes msa_route_score's chunk ranges per XCD on the
+ * current device (not a step of the method: a calibration of how the scan is
+ * spread over MI355X's eight XCDs).  Workgroup b of the scan runs on XCD
+ * b % 8; when the XCDs stream at different rates, equal ranges leave the
+ * launch waiting for the slowest.  The call runs four untimed routing
+ * launches, then `rounds` rounds of three timed ones, on the caller's
+ * arguments (those of msa_route_score;
+ * doc_score receives the scores), and after each round moves every XCD's
+ * share by the ratio of the XCDs' mean workgroup end time to its own (each
+ * share kept within 0.75x..1.25x of 1/8).  Later msa_route_score and
+ * msa_chunk_scores calls on this device use the shares where the scan runs one
+ * column group with one workgroup per CU; elsewhere ranges stay equal.  Scores
+ * do not depend on the split (maxima are exact): only the launch time does.
+ *   rounds      0 clears the device's shares (equal ranges again); at most 64
+ *   shares_out  8 floats (host), may be NULL: the shares now in use (1/8 each
+ *               when the shape does not size ranges per XCD, and nothing is stored)
+ * Setup-time call: it allocates a small device buffer, synchronises the stream
+ * and must not be captured into a graph.  Errors: those of msa_route_score;
+ * INVALID_ARG also for rounds outside [0, 64].
+ */
+int msa_route_balance(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat, int kr_layout,
+                      const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks, float* doc_score, void* ws,
+                      size_t ws_bytes, int rounds, float* shares_out, void* stream);
 
 /*
  * msa_chunk_scores, msa_segment_max - msa_route_score in two launches (the

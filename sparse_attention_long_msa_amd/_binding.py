@@ -35,6 +35,7 @@ _SIGS = {
     "msa_pool_encode": (_I, [_I, _P, _P, _P, _P, _L, _L, _L, _I, _I, _I, _I, _I, _P, _P]),
     "msa_route_score_workspace": (_S, [_I, _I, _I, _I, _I, _L, _L]),
     "msa_route_score": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P, _P, _S, _P]),
+    "msa_route_balance": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P, _P, _S, _I, _P, _P]),
     "msa_chunk_scores": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _L, _P, _P, _S, _P]),
     "msa_segment_max": (_I, [_P, _I, _L, _P, _L, _P, _P]),
     "msa_topk_workspace": (_S, [_I, _L, _I]),
@@ -269,6 +270,34 @@ def msa_route_score(q_r, kr_hat, chunk_doc, n_docs, doc_score=None, ws=None, lay
         dt, _ptr(q_r), B, T, H, d, _ptr(kr_hat), layout, _ptr(chunk_doc), n_docs, n_chunks, _ptr(doc_score),
         _ptr(ws), wsb, _stream(stream)))
     return doc_score
+
+
+def msa_route_balance(q_r, kr_hat, chunk_doc, n_docs, rounds=3, doc_score=None, ws=None, layout=MSA_LAYOUT_ROWS,
+                      stream=None):
+    """Sizes msa_route_score's chunk ranges per XCD on the current device from
+    `rounds` rounds of timed launches on these arguments (a setup-time call: it
+    synchronises and must not be captured); rounds=0 clears them.  Returns the
+    8 XCD shares now in use."""
+    shares = np.zeros(8, dtype=np.float32)
+    if rounds == 0:
+        _check("msa_route_balance", lib.msa_route_balance(0, None, 0, 0, 0, 0, None, 0, None, 0, 0, None, None, 0, 0,
+                                                          shares.ctypes.data, None))
+        return shares
+    _dev(q_r, "q_r", _FLOAT, (None, None, None, None))
+    B, T, H, d = q_r.shape
+    _dev(kr_hat, "kr_hat", q_r.dtype)
+    _dev(chunk_doc, "chunk_doc", _I32, (None,))
+    n_chunks = chunk_doc.shape[0]
+    dt = _dtype(q_r)
+    if doc_score is None:
+        doc_score = torch.empty((B, n_docs), dtype=torch.float32, device=q_r.device)
+    _dev(doc_score, "doc_score", _F32, (B, n_docs))
+    _dev(ws, "ws", optional=True)
+    ws, wsb = _ws(msa_route_score_workspace(dt, B, T, H, d, n_docs, n_chunks), q_r.device, ws)
+    _check("msa_route_balance", lib.msa_route_balance(
+        dt, _ptr(q_r), B, T, H, d, _ptr(kr_hat), layout, _ptr(chunk_doc), n_docs, n_chunks, _ptr(doc_score),
+        _ptr(ws), wsb, int(rounds), shares.ctypes.data, _stream(stream)))
+    return shares
 
 
 def msa_chunk_scores(q_r, kr_hat, n_chunks, chunk_score=None, ws=None, layout=MSA_LAYOUT_ROWS, stream=None):

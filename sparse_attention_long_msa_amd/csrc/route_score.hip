@@ -18,6 +18,18 @@
 // workgroup's chunk range; documents inside the range are then stored once,
 // and only the range's two boundary documents take an exact ordered global
 // atomic max.
+//
+// Workgroup b runs on XCD b % 8.  The XCDs of one device need not stream at
+// the same rate (on the MI355X boxes measured, the odd ones took 4-5% longer
+// for the same bytes), so the chunk ranges may be sized per XCD: shares set
+// by msa_route_balance, which times this kernel per workgroup.  Any split of
+// the tiles into ranges gives the same scores; only the launch's length
+// depends on it.
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+#include <vector>
+
 #include "common.h"
 
 namespace msa {
@@ -83,11 +95,18 @@ __device__ __forceinline__ void lds_max_float(float* addr, float v) {
 // tile belongs to one query (T % 16 == 0), so the token max is taken in
 // registers before the document max.
 // D: head loads in flight per wave (the ring)
+// Chunk ranges sized per XCD: workgroup b (one column group) takes len[b % 8]
+// tiles, the ranges laid out in workgroup order; on = 0: equal ranges.
+struct XcdSplit {
+  int64_t len[8];
+  int on;
+};
+
 template <int NT, bool UNIFORM_B, bool TILED, int D>
 __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     const uint16_t* __restrict__ q_r, int T, int J, const uint16_t* __restrict__ kr,
     const int32_t* __restrict__ chunk_doc, int64_t n_docs, int64_t n_chunks, float* __restrict__ doc_score,
-    int n_groups, int n_ranges, int64_t tiles_per_range, int tab_cap) {
+    int n_groups, int n_ranges, int64_t tiles_per_range, int tab_cap, XcdSplit xs, uint64_t* __restrict__ wg_ts) {
   constexpr int H = RS_H;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint4* qfrag = reinterpret_cast<uint4*>(smem);  // [NT][H][KK][64 lanes] x 16 B
@@ -106,6 +125,8 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     range = (slot / n_groups) * 8 + xcd;
   }
   if (range >= n_ranges) return;
+  // per-workgroup start and end stamps (the 100 MHz real-time counter), for msa_route_balance
+  if (wg_ts && threadIdx.x == 0) wg_ts[2 * blockIdx.x] = __builtin_amdgcn_s_memrealtime();
   const int col0 = group * 64;
 
   const int g4 = lane / 16;       // lane group: k-slice of the operands, row block of the result
@@ -113,10 +134,25 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
   constexpr int MT = RS_MT;
   constexpr int TILE = 16 * MT;   // chunks per wave tile
   const int64_t tiles_total = (n_chunks + TILE - 1) / TILE;
-  const int64_t t_begin = int64_t(range) * tiles_per_range;
+  int64_t t_begin = int64_t(range) * tiles_per_range;
   int64_t t_end = t_begin + tiles_per_range;
+  if (xs.on) {   // one column group: range == blockIdx.x, on XCD range % 8
+    // selects over the unrolled XCDs (no dynamic index into the argument)
+    int64_t round = 0, before = 0, mine = 0;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      round += xs.len[x];
+      before += x < range % 8 ? xs.len[x] : 0;
+      mine = x == range % 8 ? xs.len[x] : mine;
+    }
+    t_begin = int64_t(range / 8) * round + before;
+    t_end = t_begin + mine;
+  }
   if (t_end > tiles_total) t_end = tiles_total;
-  if (t_begin >= t_end) return;             // a range past the last tile (whole workgroup)
+  if (t_begin >= t_end) {                   // a range past the last tile (whole workgroup)
+    if (wg_ts && threadIdx.x == 0) wg_ts[2 * blockIdx.x + 1] = wg_ts[2 * blockIdx.x];
+    return;
+  }
   const int64_t rowE = int64_t(H) * RS_D;  // elements per chunk
   int64_t tile = t_begin + wave;
 
@@ -356,6 +392,10 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
         atomic_max_float(dst, v);
     }
   }
+  if (wg_ts) {
+    __syncthreads();
+    if (threadIdx.x == 0) wg_ts[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+  }
 }
 
 // Vector path: float32 (or any head size).  The query is first scaled per
@@ -480,6 +520,31 @@ __global__ __launch_bounds__(RV_THREADS) void route_score_vec_kernel(
 
 static bool use_mfma(int dtype, int H, int d) { return dtype == MSA_BF16 && d == RS_D && H == RS_H; }
 
+// Per-device XCD shares of the chunk ranges (set by msa_route_balance; none: equal ranges).
+constexpr int RB_MAX_DEVICES = 64;
+static std::mutex g_balance_mu;
+static float g_shares[RB_MAX_DEVICES][8];
+static bool g_has_shares[RB_MAX_DEVICES];
+
+// The shares of device dev, if set.
+static bool device_shares(int dev, float (&sh)[8]) {
+  if (dev < 0 || dev >= RB_MAX_DEVICES) return false;
+  std::lock_guard<std::mutex> lock(g_balance_mu);
+  if (!g_has_shares[dev]) return false;
+  for (int x = 0; x < 8; ++x) sh[x] = g_shares[dev][x];
+  return true;
+}
+
+// Range lengths per XCD for shares sh (summing to 1): rounds = workgroups per
+// XCD; the ranges cover every tile (the last ones may fall short or be empty).
+static XcdSplit make_split(const float (&sh)[8], int64_t tiles_total, int64_t rounds) {
+  XcdSplit xs{};
+  xs.on = 1;
+  for (int x = 0; x < 8; ++x)
+    xs.len[x] = std::max<int64_t>(1, int64_t(std::ceil(double(tiles_total) * sh[x] / double(rounds))));
+  return xs;
+}
+
 }  // namespace msa
 
 extern "C" size_t msa_route_score_workspace(int dtype, int B, int T, int H, int d, int64_t n_docs,
@@ -495,9 +560,15 @@ namespace msa {
 
 // Shared body of msa_route_score (chunk_doc given) and msa_chunk_scores
 // (chunk_doc NULL: every chunk is its own document, n_docs = n_chunks).
+// shares (msa_route_balance): the XCD shares to use instead of the device's;
+// wg_ts: per-workgroup start and end stamps; *split_used: whether the ranges
+// were sized per XCD (one column group, one workgroup per CU).
 static int route_score(const std::string& fn, int dtype, const void* q_r, int B, int T, int H, int d,
                        const void* kr_hat, int kr_layout, const int32_t* chunk_doc, int64_t n_docs,
-                       int64_t n_chunks, float* doc_score, void* ws, size_t ws_bytes, void* stream) {
+                       int64_t n_chunks, float* doc_score, void* ws, size_t ws_bytes, void* stream,
+                       const float* shares = nullptr, uint64_t* wg_ts = nullptr, bool* split_used = nullptr,
+                       int* n_wg = nullptr) {
+  if (split_used) *split_used = false;
   using namespace msa;
   MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
   MSA_REQUIRE(q_r && kr_hat && doc_score, MSA_ERR_INVALID_ARG, fn + ": NULL pointer");
@@ -534,6 +605,19 @@ static int route_score(const std::string& fn, int dtype, const void* q_r, int B,
     int64_t n_ranges = std::min<int64_t>(n_cu, (tiles_total + RS_WAVES - 1) / RS_WAVES);
     if (n_groups > 1) n_ranges = (n_ranges + 7) / 8 * 8;
     const int64_t tiles_per_range = (tiles_total + n_ranges - 1) / n_ranges;
+    XcdSplit xs{};
+    if (n_groups == 1 && n_ranges == n_cu && n_cu % 8 == 0) {
+      float sh[8];
+      bool have = shares != nullptr;
+      if (have) {
+        for (int x = 0; x < 8; ++x) sh[x] = shares[x];
+      } else {
+        have = device_shares(dev, sh);
+      }
+      if (have) xs = make_split(sh, tiles_total, n_cu / 8);
+    }
+    if (split_used) *split_used = xs.on != 0;
+    if (n_wg) *n_wg = int(n_ranges * n_groups);
     const size_t smem_base =
         size_t(NT) * RS_H * RS_KK * 1024 + size_t(RS_WAVES) * RS_SCRATCH + size_t(RS_H) * NT * 16 * 4;
     int lds_max = 0;
@@ -547,7 +631,8 @@ static int route_score(const std::string& fn, int dtype, const void* q_r, int B,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)));           \
   hipLaunchKernelGGL((route_score_mfma_kernel<NTV, UNI, TIL, DV>), grid, block, smem, s,               \
                      static_cast<const uint16_t*>(q_r), T, J, static_cast<const uint16_t*>(kr_hat),     \
-                     chunk_doc, n_docs, n_chunks, doc_score, n_groups, int(n_ranges), tiles_per_range, tab_cap)
+                     chunk_doc, n_docs, n_chunks, doc_score, n_groups, int(n_ranges), tiles_per_range, tab_cap, \
+                     xs, wg_ts)
 // Tiled stores stream one 16-chunk group per wave, a head at a time: one head
 // in flight per wave reads each group strictly in order and measured best
 // with one column group; column groups sharing a range (their second read
@@ -671,5 +756,106 @@ extern "C" int msa_segment_max(const float* chunk_score, int B, int64_t n_chunks
   hipLaunchKernelGGL(segment_max_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, as_stream(stream),
                      chunk_score, B, n_chunks, chunk_off, n_docs, doc_score);
   MSA_LAUNCH_CHECK();
+  return MSA_OK;
+}
+
+// Calibration of the per-XCD range sizes: rounds of timed launches of the
+// routing kernel on the caller's store; after each, every XCD's share moves
+// by the ratio of the XCDs' mean workgroup duration to its own.
+extern "C" int msa_route_balance(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
+                                 int kr_layout, const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks,
+                                 float* doc_score, void* ws, size_t ws_bytes, int rounds, float* shares_out,
+                                 void* stream) {
+  using namespace msa;
+  const std::string fn = "msa_route_balance";
+  MSA_REQUIRE(rounds >= 0 && rounds <= 64, MSA_ERR_INVALID_ARG, fn + ": rounds must lie in [0, 64]");
+  int dev = 0;
+  MSA_HIP_CHECK(hipGetDevice(&dev));
+  MSA_REQUIRE(dev >= 0 && dev < RB_MAX_DEVICES, MSA_ERR_UNSUPPORTED, fn + ": device ordinal beyond 63");
+  float sh[8];
+  for (int x = 0; x < 8; ++x) sh[x] = 0.125f;
+  if (rounds == 0) {   // back to equal ranges
+    std::lock_guard<std::mutex> lock(g_balance_mu);
+    g_has_shares[dev] = false;
+    if (shares_out)
+      for (int x = 0; x < 8; ++x) shares_out[x] = sh[x];
+    return MSA_OK;
+  }
+  MSA_REQUIRE(chunk_doc, MSA_ERR_INVALID_ARG, fn + ": NULL pointer");
+  {
+    float cur[8];
+    if (device_shares(dev, cur))
+      for (int x = 0; x < 8; ++x) sh[x] = cur[x];
+  }
+  int n_cu = 0;
+  MSA_HIP_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  uint64_t* ts = nullptr;
+  MSA_HIP_CHECK(hipMalloc(reinterpret_cast<void**>(&ts), size_t(2) * std::max(n_cu, 1) * sizeof(uint64_t)));
+  std::vector<uint64_t> h(size_t(2) * std::max(n_cu, 1));
+  hipStream_t s = as_stream(stream);
+  int st = MSA_OK;
+  bool balanced = false;
+  // untimed launches first: the clocks of an idle device take a few launches to settle
+  for (int w = 0; w < 4 && st == MSA_OK; ++w)
+    st = route_score(fn, dtype, q_r, B, T, H, d, kr_hat, kr_layout, chunk_doc, n_docs, n_chunks, doc_score, ws,
+                     ws_bytes, stream, sh);
+  for (int r = 0; r < rounds && st == MSA_OK; ++r) {
+    double sum[8] = {0}, cnt[8] = {0};
+    for (int rep = 0; rep < 3 && st == MSA_OK; ++rep) {
+      bool used = false;
+      int n_wg = 0;
+      st = route_score(fn, dtype, q_r, B, T, H, d, kr_hat, kr_layout, chunk_doc, n_docs, n_chunks, doc_score, ws,
+                       ws_bytes, stream, sh, ts, &used, &n_wg);
+      if (st != MSA_OK) break;
+      if (!used || n_wg != n_cu) {   // this shape does not size ranges per XCD: nothing to balance
+        rounds = 0;
+        break;
+      }
+      if (hipStreamSynchronize(s) != hipSuccess ||
+          hipMemcpy(h.data(), ts, h.size() * sizeof(uint64_t), hipMemcpyDeviceToHost) != hipSuccess) {
+        st = MSA_ERR_HIP;
+        break;
+      }
+      uint64_t t0 = UINT64_MAX;
+      for (int b = 0; b < n_cu; ++b) t0 = std::min(t0, h[2 * b]);
+      for (int b = 0; b < n_cu; ++b) {
+        if (h[2 * b + 1] <= h[2 * b]) continue;   // an empty range
+        sum[b % 8] += double(h[2 * b + 1] - t0);
+        cnt[b % 8] += 1;
+      }
+    }
+    if (st != MSA_OK || rounds == 0) break;
+    double mean_end[8], all = 0;
+    int n_ok = 0;
+    for (int x = 0; x < 8; ++x) {
+      mean_end[x] = cnt[x] > 0 ? sum[x] / cnt[x] : 0;
+      if (cnt[x] > 0) {
+        all += mean_end[x];
+        ++n_ok;
+      }
+    }
+    if (n_ok < 8) break;
+    all /= 8;
+    double tot = 0;
+    for (int x = 0; x < 8; ++x) {
+      // the share moves by the XCD's rate relative to the others, within 0.75x..1.25x of equal
+      const double v = double(sh[x]) * all / mean_end[x];
+      sh[x] = float(std::min(1.25 / 8, std::max(0.75 / 8, v)));
+      tot += sh[x];
+    }
+    for (int x = 0; x < 8; ++x) sh[x] = float(sh[x] / tot);
+    balanced = true;
+  }
+  hipFree(ts);
+  if (st != MSA_OK) return st;
+  {
+    std::lock_guard<std::mutex> lock(g_balance_mu);
+    if (balanced) {
+      for (int x = 0; x < 8; ++x) g_shares[dev][x] = sh[x];
+      g_has_shares[dev] = true;
+    }
+  }
+  if (shares_out)
+    for (int x = 0; x < 8; ++x) shares_out[x] = balanced ? sh[x] : 0.125f;
   return MSA_OK;
 }

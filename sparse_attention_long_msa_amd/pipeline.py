@@ -93,6 +93,14 @@ class LayerRunner:
             self.ids_h = torch.empty((batch, k), dtype=i32, pin_memory=True)
             self.copy_stream = torch.cuda.Stream(device=dev)
 
+    def balance(self, q_r, kr_hat, chunk_doc, rounds=4):
+        """Setup-time: size the routing scan's chunk ranges per XCD for this
+        device from timed launches on this layer's arguments
+        (msa_route_balance; it synchronises, so never inside a captured step).
+        Scores are unchanged; returns the 8 XCD shares."""
+        return B.msa_route_balance(q_r, kr_hat, chunk_doc, self.n_docs, rounds=rounds, doc_score=self.doc_score,
+                                   ws=self.rs_ws, layout=self.kr_layout)
+
     def route(self, q_r, kr_hat, chunk_doc, stream=None):
         B.msa_route_score(q_r, kr_hat, chunk_doc, self.n_docs, doc_score=self.doc_score, ws=self.rs_ws,
                           layout=self.kr_layout, stream=stream)

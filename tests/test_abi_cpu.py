@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.msa_abi_version() == 11
+    assert M.msa_abi_version() == 12
     assert M.lib.msa_status_string(0).decode() == "ok"
     assert "workspace" in M.lib.msa_status_string(3).decode()
 
@@ -174,6 +174,15 @@ def test_sparse_attn_indexed_validation():
     assert call(q=None) == 1
     assert call(wsb=16) == 3
     assert "msa_sparse_attn_indexed" in L.msa_last_error().decode()
+
+
+def test_route_balance_validation():
+    L = M.lib
+    out = (ctypes.c_float * 8)()
+    # rounds out of range
+    assert L.msa_route_balance(1, P, 1, 64, 8, 128, P, 1, P, 4, 64, P, None, 0, -1, out, None) == 1
+    assert L.msa_route_balance(1, P, 1, 64, 8, 128, P, 1, P, 4, 64, P, None, 0, 65, out, None) == 1
+    assert "msa_route_balance" in L.msa_last_error().decode()
 
 
 def test_sparse_attn_part_validation():

@@ -127,6 +127,42 @@ def test_route_score(bf16, layout, B, T):
     assert np.argmax(got[0]) == nd
 
 
+@pytest.mark.parametrize("layout", [1, 0])
+def test_route_balance_keeps_the_scores(layout):
+    """msa_route_balance sizes the scan's chunk ranges per XCD: the shares stay
+    in their band and sum to one, and the scores after it equal, bit for bit,
+    those of equal ranges (one 64-token query and 32 single-token queries, a
+    store large enough for one workgroup per CU).  Clearing restores 1/8 each."""
+    from synth import device as SD
+    H, d = 8, 128
+    r = np.random.default_rng(40)
+    chunks = r.integers(1, 31, size=2600).astype(np.int64)
+    chunks[r.choice(2600, size=7, replace=False)] = 0                # empty documents
+    chunk_off = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int64)
+    n_chunks, D = int(chunk_off[-1]), len(chunks)
+    assert n_chunks > 256 * 8 * 16
+    co_d = to_dev_i64(chunk_off)
+    cd = M.msa_chunk_doc_map(co_d, n_chunks)
+    rows = torch.empty((n_chunks, H, d), dtype=torch.bfloat16, device=dev())
+    SD.fill(rows, 41, 0, synth.T_KR)
+    st = M.msa_tile_routing_keys(rows) if layout == 1 else rows
+    try:
+        for B, T in ((1, 64), (32, 1)):
+            q = SD.fill(torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev()), 42, 0, synth.T_QR)
+            M.msa_route_balance(None, None, None, 0, rounds=0)
+            ref = M.msa_route_score(q, st, cd, D, layout=layout).clone()
+            shares = M.msa_route_balance(q, st, cd, D, rounds=2, layout=layout)
+            assert abs(float(shares.sum()) - 1.0) < 1e-5
+            assert (shares >= 0.75 / 8 - 1e-6).all() and (shares <= 1.25 / 8 + 1e-6).all()
+            got = M.msa_route_score(q, st, cd, D, layout=layout)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), f"B={B} T={T}"
+            print(f"balance B={B} T={T} layout={layout}: shares {np.round(shares, 4).tolist()}")
+    finally:
+        cleared = M.msa_route_balance(None, None, None, 0, rounds=0)
+    assert np.allclose(cleared, 0.125)
+
+
 @pytest.mark.parametrize("bf16,layout", [(True, 1), (True, 0), (False, 0)])
 @pytest.mark.parametrize("B,T", [(1, 64), (32, 1), (1, 128), (3, 7)])
 def test_route_score_unfused_equals_fused(bf16, layout, B, T):
