@@ -242,12 +242,13 @@ int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, cons
  * doc_score receives the scores), and after each round moves every XCD's
  * share by the ratio of the XCDs' mean workgroup end time to its own (each
  * share kept within 0.75x..1.25x of 1/8).  Later msa_route_score and
- * msa_chunk_scores calls on this device use the shares where the scan runs one
- * column group with one workgroup per CU; elsewhere ranges stay equal.  Scores
+ * msa_chunk_scores calls on this device use the shares wherever the scan runs
+ * one chunk range per CU (the calibration itself needs one column group,
+ * B*T <= 64); elsewhere ranges stay equal.  Scores
  * do not depend on the split (maxima are exact): only the launch time does.
  *   rounds      0 clears the device's shares (equal ranges again); at most 64
- *   shares_out  8 floats (host), may be NULL: the shares now in use (1/8 each
- *               when the shape does not size ranges per XCD, and nothing is stored)
+ *   shares_out  8 floats (host), may be NULL: the shares in use after the call
+ *               (unchanged when the shape cannot be calibrated: then nothing is stored)
  * Setup-time call: it allocates a small device buffer, synchronises the stream
  * and must not be captured into a graph.  Errors: those of msa_route_score;
  * INVALID_ARG also for rounds outside [0, 64].

@@ -95,8 +95,9 @@ __device__ __forceinline__ void lds_max_float(float* addr, float v) {
 // tile belongs to one query (T % 16 == 0), so the token max is taken in
 // registers before the document max.
 // D: head loads in flight per wave (the ring)
-// Chunk ranges sized per XCD: workgroup b (one column group) takes len[b % 8]
-// tiles, the ranges laid out in workgroup order; on = 0: equal ranges.
+// Chunk ranges sized per XCD: range r (on XCD r % 8, with all its column
+// groups) takes len[r % 8] tiles, the ranges laid out in order; on = 0: equal
+// ranges.
 struct XcdSplit {
   int64_t len[8];
   int on;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
   const int64_t tiles_total = (n_chunks + TILE - 1) / TILE;
   int64_t t_begin = int64_t(range) * tiles_per_range;
   int64_t t_end = t_begin + tiles_per_range;
-  if (xs.on) {   // one column group: range == blockIdx.x, on XCD range % 8
+  if (xs.on) {   // range r and its column groups run on XCD r % 8
     // selects over the unrolled XCDs (no dynamic index into the argument)
     int64_t round = 0, before = 0, mine = 0;
 #pragma unroll
@@ -562,7 +563,7 @@ namespace msa {
 // (chunk_doc NULL: every chunk is its own document, n_docs = n_chunks).
 // shares (msa_route_balance): the XCD shares to use instead of the device's;
 // wg_ts: per-workgroup start and end stamps; *split_used: whether the ranges
-// were sized per XCD (one column group, one workgroup per CU).
+// were sized per XCD (one range per CU).
 static int route_score(const std::string& fn, int dtype, const void* q_r, int B, int T, int H, int d,
                        const void* kr_hat, int kr_layout, const int32_t* chunk_doc, int64_t n_docs,
                        int64_t n_chunks, float* doc_score, void* ws, size_t ws_bytes, void* stream,
@@ -606,7 +607,7 @@ static int route_score(const std::string& fn, int dtype, const void* q_r, int B,
     if (n_groups > 1) n_ranges = (n_ranges + 7) / 8 * 8;
     const int64_t tiles_per_range = (tiles_total + n_ranges - 1) / n_ranges;
     XcdSplit xs{};
-    if (n_groups == 1 && n_ranges == n_cu && n_cu % 8 == 0) {
+    if (n_ranges == n_cu && n_cu % 8 == 0) {
       float sh[8];
       bool have = shares != nullptr;
       if (have) {
@@ -855,7 +856,7 @@ extern "C" int msa_route_balance(int dtype, const void* q_r, int B, int T, int H
       g_has_shares[dev] = true;
     }
   }
-  if (shares_out)
-    for (int x = 0; x < 8; ++x) shares_out[x] = balanced ? sh[x] : 0.125f;
+  if (shares_out)   // the shares in use from now on (unchanged when nothing was calibrated)
+    for (int x = 0; x < 8; ++x) shares_out[x] = sh[x];
   return MSA_OK;
 }
