@@ -521,8 +521,10 @@ __global__ __launch_bounds__(RV_THREADS) void route_score_vec_kernel(
 
 static bool use_mfma(int dtype, int H, int d) { return dtype == MSA_BF16 && d == RS_D && H == RS_H; }
 
-// Per-device XCD shares of the chunk ranges (set by msa_route_balance; none: equal ranges).
+// Per-device XCD shares of the chunk ranges (set by msa_route_balance; none: equal ranges),
+// used where every range has at least RB_MIN_TILES tiles.
 constexpr int RB_MAX_DEVICES = 64;
+constexpr int64_t RB_MIN_TILES = 128;
 static std::mutex g_balance_mu;
 static float g_shares[RB_MAX_DEVICES][8];
 static bool g_has_shares[RB_MAX_DEVICES];
@@ -607,7 +609,8 @@ static int route_score(const std::string& fn, int dtype, const void* q_r, int B,
     if (n_groups > 1) n_ranges = (n_ranges + 7) / 8 * 8;
     const int64_t tiles_per_range = (tiles_total + n_ranges - 1) / n_ranges;
     XcdSplit xs{};
-    if (n_ranges == n_cu && n_cu % 8 == 0) {
+    // only long ranges: at ~40 tiles per range (a 10M-token store) the split measured no faster
+    if (n_ranges == n_cu && n_cu % 8 == 0 && tiles_total >= RB_MIN_TILES * n_ranges) {
       float sh[8];
       bool have = shares != nullptr;
       if (have) {
@@ -812,8 +815,10 @@ extern "C" int msa_route_balance(int dtype, const void* q_r, int B, int T, int H
         rounds = 0;
         break;
       }
-      if (hipStreamSynchronize(s) != hipSuccess ||
-          hipMemcpy(h.data(), ts, h.size() * sizeof(uint64_t), hipMemcpyDeviceToHost) != hipSuccess) {
+      hipError_t e = hipStreamSynchronize(s);
+      if (e == hipSuccess) e = hipMemcpy(h.data(), ts, h.size() * sizeof(uint64_t), hipMemcpyDeviceToHost);
+      if (e != hipSuccess) {
+        set_error(fn + ": " + hipGetErrorString(e));
         st = MSA_ERR_HIP;
         break;
       }

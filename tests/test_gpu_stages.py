@@ -131,16 +131,18 @@ def test_route_score(bf16, layout, B, T):
 def test_route_balance_keeps_the_scores(layout):
     """msa_route_balance sizes the scan's chunk ranges per XCD: the shares stay
     in their band and sum to one, and the scores after it equal, bit for bit,
-    those of equal ranges (one 64-token query and 32 single-token queries, a
-    store large enough for one workgroup per CU).  Clearing restores 1/8 each."""
+    those of equal ranges (one 64-token query, 32 single-token queries and two
+    column-grouped shapes, over a 1.1 GB store whose ranges are long enough for
+    the split).  Clearing restores 1/8 each."""
     from synth import device as SD
     H, d = 8, 128
     r = np.random.default_rng(40)
-    chunks = r.integers(1, 31, size=2600).astype(np.int64)
-    chunks[r.choice(2600, size=7, replace=False)] = 0                # empty documents
+    chunks = r.integers(1, 31, size=36000).astype(np.int64)
+    chunks[r.choice(36000, size=7, replace=False)] = 0               # empty documents
     chunk_off = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int64)
     n_chunks, D = int(chunk_off[-1]), len(chunks)
-    assert n_chunks > 256 * 8 * 16
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert n_chunks >= 128 * 16 * n_cu                                 # ranges of 128+ tiles
     co_d = to_dev_i64(chunk_off)
     cd = M.msa_chunk_doc_map(co_d, n_chunks)
     rows = torch.empty((n_chunks, H, d), dtype=torch.bfloat16, device=dev())
