@@ -268,6 +268,161 @@ __global__ __launch_bounds__(TR_THREADS) void route_argmax_mfma_kernel(
   }
 }
 
+// bf16, d = 128, the queries staged in LDS: workgroup = (group of 64 query
+// columns, four 16-chunk tiles), one tile per wave.  The column group's
+// operands of every head (H x 16 KB, in fragment order) and its 1/(H ||q||)
+// scales are staged once per workgroup, so each query fragment is read from
+// L2 once per four tiles instead of once per tile; the tile's rows stream
+// from global memory one head ahead.  Products, the per-head scaling and the
+// keys are those of route_argmax_mfma_kernel, so the maxima are identical.
+__device__ __forceinline__ void argmax_emit(const f32x4 (&tot)[AX_NT], int64_t c0, int col0, int T, int J,
+                                            const int (&rdoc)[4], int64_t n_docs, uint64_t* __restrict__ keys,
+                                            int lc, int g4) {
+  // merge rows of one document in a lane's four rows, then one atomic maximum per run
+  auto emit = [&](const uint64_t (&key)[4], int b) {
+    uint64_t run = key[0];
+    int run_doc = rdoc[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      if (rdoc[i] == run_doc) {
+        run = key[i] > run ? key[i] : run;
+      } else {
+        if (run_doc >= 0 && run_doc < n_docs)
+          atomicMax(reinterpret_cast<unsigned long long*>(keys + int64_t(b) * n_docs + run_doc), (unsigned long long)run);
+        run = key[i];
+        run_doc = rdoc[i];
+      }
+    }
+    if (run_doc >= 0 && run_doc < n_docs)
+      atomicMax(reinterpret_cast<unsigned long long*>(keys + int64_t(b) * n_docs + run_doc), (unsigned long long)run);
+  };
+  const int col_last = col0 + 16 * AX_NT - 1;
+  if (col_last < J && col0 / T == col_last / T) {   // all 64 columns are tokens of one query
+    uint64_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t c = c0 + 4 * g4 + i;
+      uint64_t kmax = 0;
+#pragma unroll
+      for (int n = 0; n < AX_NT; ++n) {
+        const int t = (col0 + 16 * n + lc) % T;
+        const uint64_t kn = rdoc[i] >= 0 ? cand_key(tot[n][i], uint32_t(c * T + t)) : 0;
+        kmax = kn > kmax ? kn : kmax;
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        const uint64_t o = shfl_xor_u64(kmax, m);
+        kmax = o > kmax ? o : kmax;
+      }
+      key[i] = kmax;
+    }
+    if (lc == 0) emit(key, col0 / T);
+    return;
+  }
+#pragma unroll
+  for (int n = 0; n < AX_NT; ++n) {
+    const int cbase = col0 + 16 * n;
+    if (cbase >= J) break;
+    const int col = cbase + lc;
+    const bool col_ok = col < J;
+    const int t = col % T, b = col / T;
+    uint64_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t c = c0 + 4 * g4 + i;
+      key[i] = (col_ok && rdoc[i] >= 0) ? cand_key(tot[n][i], uint32_t(c * T + t)) : 0;
+    }
+    const bool one_query = cbase / T == min(cbase + 15, J - 1) / T && cbase + 15 < J;
+    if (one_query) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+          const uint64_t o = shfl_xor_u64(key[i], m);
+          key[i] = o > key[i] ? o : key[i];
+        }
+      }
+    }
+    if (!col_ok || (one_query && lc != 0)) continue;
+    emit(key, b);
+  }
+}
+
+constexpr int AX_D = 128;
+constexpr int AX_KK = AX_D / 32;
+
+__global__ __launch_bounds__(TR_THREADS) void route_argmax_lds_kernel(
+    const uint16_t* __restrict__ q, int T, int J, int H, const uint16_t* __restrict__ kr,
+    const int32_t* __restrict__ chunk_doc, int64_t n_docs, int64_t n_chunks, const float* __restrict__ winv,
+    int n_cg, uint64_t* __restrict__ keys) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint4* qf = reinterpret_cast<uint4*>(smem);                                     // [H][KK][NT][64 lanes]
+  float* wl = reinterpret_cast<float*>(smem + size_t(H) * AX_KK * AX_NT * 1024);  // [H][NT][16]
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, lc = lane % 16, g4 = lane / 16;
+  const int cg = int(blockIdx.x % n_cg);
+  const int64_t tile = int64_t(blockIdx.x / n_cg) * TR_WAVES + wave;
+  const int col0 = cg * 16 * AX_NT;
+  // ---- stage the column group's query fragments and scales (every thread takes part)
+  const int n_pieces = H * AX_KK * AX_NT * 64;
+  for (int p = threadIdx.x; p < n_pieces; p += TR_THREADS) {
+    const int l = p % 64, f = p / 64;
+    const int n = f % AX_NT, kk = (f / AX_NT) % AX_KK, h = f / (AX_NT * AX_KK);
+    const int col = col0 + 16 * n + (l % 16);
+    qf[p] = col < J ? *reinterpret_cast<const uint4*>(q + (int64_t(col) * H + h) * AX_D + 32 * kk + 8 * (l / 16))
+                    : make_uint4(0, 0, 0, 0);
+  }
+  for (int p = threadIdx.x; p < H * AX_NT * 16; p += TR_THREADS) {
+    const int c16 = p % 16, n = (p / 16) % AX_NT, h = p / (16 * AX_NT);
+    const int col = col0 + 16 * n + c16;
+    wl[p] = col < J ? winv[int64_t(col) * H + h] : 0.f;
+  }
+  __syncthreads();
+  const int64_t c0 = tile * 16;
+  if (c0 >= n_chunks) return;   // after the barrier: this wave has no tile
+  const int64_t crow = c0 + lc;
+  const bool crow_ok = crow < n_chunks;
+  int rdoc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t c = c0 + 4 * g4 + i;
+    rdoc[i] = c < n_chunks ? chunk_doc[c] : -1;
+  }
+  f32x4 tot[AX_NT];
+#pragma unroll
+  for (int n = 0; n < AX_NT; ++n) tot[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load_a = [&](int h, uint4 (&a)[AX_KK]) {
+#pragma unroll
+    for (int kk = 0; kk < AX_KK; ++kk)
+      a[kk] = crow_ok ? *reinterpret_cast<const uint4*>(kr + (crow * H + h) * AX_D + 32 * kk + 8 * g4)
+                      : make_uint4(0, 0, 0, 0);
+  };
+  auto compute = [&](int h, const uint4 (&a)[AX_KK]) {
+    f32x4 acc[AX_NT];
+#pragma unroll
+    for (int n = 0; n < AX_NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < AX_KK; ++kk)
+#pragma unroll
+      for (int n = 0; n < AX_NT; ++n)
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_tr(a[kk]),
+                                                          as_bf16x8_tr(qf[((h * AX_KK + kk) * AX_NT + n) * 64 + lane]),
+                                                          acc[n], 0, 0, 0);
+#pragma unroll
+    for (int n = 0; n < AX_NT; ++n) tot[n] += wl[(h * AX_NT + n) * 16 + lc] * acc[n];
+  };
+  // heads in pairs, the next head's rows loading while one is computed; the
+  // request after the last head repeats it (in bounds, never used)
+  uint4 a0[AX_KK], a1[AX_KK];
+  load_a(0, a0);
+  for (int h = 0; h < H; h += 2) {
+    load_a(h + 1, a1);
+    compute(h, a0);
+    load_a(min(h + 2, H - 1), a0);
+    compute(h + 1, a1);
+  }
+  argmax_emit(tot, c0, col0, T, J, rdoc, n_docs, keys, lc, g4);
+}
+
 // float32 (or any head size) path: one thread per (chunk, column)
 template <int DT>
 __global__ void route_argmax_vec_kernel(const typename Elem<DT>::T* __restrict__ q, int T, int J, int H, int d,
@@ -632,7 +787,19 @@ extern "C" int msa_route_argmax(int dtype, const void* q_r, int B, int T, int H,
   if (argmax_mfma(dtype, d)) {
     const int64_t tiles = (n_chunks + 15) / 16;
     const int n_cg = (J + 16 * AX_NT - 1) / (16 * AX_NT);
-    if (d == 128 && H % 2 == 0)
+    int lds_max = 0, dev = 0;
+    MSA_HIP_CHECK(hipGetDevice(&dev));
+    MSA_HIP_CHECK(hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
+    const size_t lsmem = size_t(H) * AX_KK * AX_NT * 1024 + size_t(H) * AX_NT * 16 * sizeof(float);
+    const int64_t groups = (tiles + TR_WAVES - 1) / TR_WAVES;
+    if (d == AX_D && H % 2 == 0 && lsmem <= size_t(lds_max) && groups * n_cg < (int64_t(1) << 31)) {
+      // the column group's queries staged once per four tiles
+      MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&route_argmax_lds_kernel),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lsmem)));
+      hipLaunchKernelGGL(route_argmax_lds_kernel, dim3(unsigned(groups * n_cg)), dim3(TR_THREADS), lsmem, s,
+                         static_cast<const uint16_t*>(q_r), T, J, H, static_cast<const uint16_t*>(kr_hat), chunk_doc,
+                         n_docs, n_chunks, winv, n_cg, keys);
+    } else if (d == 128 && H % 2 == 0)
       hipLaunchKernelGGL(route_argmax_mfma_kernel<4>, dim3(grid_for(tiles * n_cg, TR_WAVES)), dim3(TR_THREADS), 0, s,
                          static_cast<const uint16_t*>(q_r), T, J, H, d, static_cast<const uint16_t*>(kr_hat),
                          chunk_doc, n_docs, n_chunks, winv, n_cg, keys);
