@@ -20,7 +20,8 @@ are not part of the timed region).
 The default run prints one JSON line: the 100M-token step as the workload
 states it, with the content K/V in pinned host memory and the selected
 documents fetched per layer by the zero-copy gather kernel (the line's value;
-the box pins 8 of the 18 layers' K/V, which the layers cycle over), then, in
+the host pins as many layers' K/V as it can, 8 of 18 with ~270 GB of RAM,
+which the layers cycle over), then, in
 the same line,
   hbm_tier     the same step with the content K/V in HBM, read in place,
   ceiling      the streaming-read rate over the same bytes (msa_stream_read),
@@ -98,7 +99,7 @@ def log(*a):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 "
+        print(json.dumps({"error": "this benchmark runs on one GPU only: --gpus must be 1 "
                                    "(no sharding and no collectives)"}))
         sys.exit(2)
     import torch
@@ -564,7 +565,7 @@ class PresetBench:
         return out
 
     def pin_host(self):
-        """The pages' tier: content K/V in pinned host memory.  The box pins
+        """The pages' tier: content K/V in pinned host memory.  A host pins
         only part of the 115 GB, so as many layers as fit are pinned and the
         18 layers cycle over them (the fetch cost does not depend on the
         values).  Returns kv(l) and a description, or None."""
@@ -639,7 +640,7 @@ class PresetBench:
 def config_leg(torch, name, args):
     """Per-config line for the smaller presets: warm and cold step times,
     routing and attention GB/s, and the oracle's routing and attention time
-    on the machine's host cores (bounded samples)."""
+    on the host's cores (bounded samples)."""
     from synth import configs
     p = configs.PRESETS[name]()
     pb = PresetBench(torch, p, graph=not args.no_graph, overlap=args.overlap)

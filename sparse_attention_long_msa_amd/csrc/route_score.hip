@@ -20,7 +20,7 @@
 // atomic max.
 //
 // Workgroup b runs on XCD b % 8.  The XCDs of one device need not stream at
-// the same rate (on the MI355X boxes measured, the odd ones took 4-5% longer
+// the same rate (on some MI355X devices the odd ones take 4-5% longer
 // for the same bytes), so the chunk ranges may be sized per XCD: shares set
 // by msa_route_balance, which times this kernel per workgroup.  Any split of
 // the tiles into ranges gives the same scores; only the launch's length

@@ -284,8 +284,8 @@ def test_binding_rejects_pageable_host_tier():
     co = torch.zeros(11, dtype=torch.int64)
     kb = _cpu((80, 8, 128))
     for mode in (M.MSA_SRC_HOST_MAPPED, M.MSA_SRC_HOST_MEMCPY):
-        # the device operands are checked first; a device-only box would reach the
-        # host-tier check, which a pageable tensor fails the same way
+        # the device operands are checked first; with device-resident ids the
+        # host-tier check comes next, which a pageable tensor fails the same way
         with pytest.raises(ValueError, match="(ids: must be in device memory|k_bar: must be in pinned host memory)"):
             M.msa_gather_kv(ids, co, kb, kb, 8, 32, src_mode=mode)
     with pytest.raises(ValueError, match="k_bar: must be in pinned host memory"):
