@@ -120,7 +120,13 @@ def test_preset_full_size_full_ranking(name, tier):
     # and tiny presets against the oracle.
     mode = M.MSA_SRC_HOST_MAPPED if tier == "host" else M.MSA_SRC_DEVICE
     gl = GpuLayer(p, layer, host, src_mode=mode, indexed=tier == "hbm", overlap_local=True)
-    g = gl.run()
+    try:
+        # the routing scan split per XCD as bench.py times it (where the store is long enough)
+        shares = gl.runner.balance(gl.qr, gl.store[synth.T_KR], gl.cd)
+        _log(f"{name}: XCD shares {np.round(shares, 4).tolist()}")
+        g = gl.run()
+    finally:
+        M.msa_route_balance(None, None, None, 0, rounds=0)
     _log(f"{name}: GPU layer {layer} done (ctx_len {g['ctx_len'][:4].tolist()}...); oracle ranking of all "
          f"{p.n_docs} documents")
     _check_full(p, host, g, list(range(p.B)), gl if tier == "hbm" else None)
