@@ -243,10 +243,10 @@ int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, cons
  * share by the ratio of the XCDs' mean workgroup end time to its own (each
  * share kept within 0.75x..1.25x of 1/8).  Later msa_route_score and
  * msa_chunk_scores calls on this device use the shares wherever the scan runs
- * one chunk range per CU and every range holds at least 128 tiles of 16
- * chunks (n_chunks >= 2048 x the CU count; shorter scans measured no faster);
- * the calibration itself also needs one column group (B*T <= 64).  Elsewhere
- * ranges stay equal.  Scores
+ * one workgroup per CU (a chunk range, or a range and its column groups of 64
+ * query columns) and every range holds at least 128 tiles of 16 chunks
+ * (shorter scans measured no faster); the calibration needs such a scan too.
+ * Elsewhere ranges stay equal.  Scores
  * do not depend on the split (maxima are exact): only the launch time does.
  *   rounds      0 clears the device's shares (equal ranges again); at most 64
  *   shares_out  8 floats (host), may be NULL: the shares in use after the call

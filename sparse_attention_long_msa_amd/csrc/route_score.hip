@@ -565,7 +565,7 @@ namespace msa {
 // (chunk_doc NULL: every chunk is its own document, n_docs = n_chunks).
 // shares (msa_route_balance): the XCD shares to use instead of the device's;
 // wg_ts: per-workgroup start and end stamps; *split_used: whether the ranges
-// were sized per XCD (one range per CU).
+// were sized per XCD (one workgroup per CU).
 static int route_score(const std::string& fn, int dtype, const void* q_r, int B, int T, int H, int d,
                        const void* kr_hat, int kr_layout, const int32_t* chunk_doc, int64_t n_docs,
                        int64_t n_chunks, float* doc_score, void* ws, size_t ws_bytes, void* stream,
@@ -606,11 +606,18 @@ static int route_score(const std::string& fn, int dtype, const void* q_r, int B,
     MSA_HIP_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
     const int64_t tiles_total = (n_chunks + 16 * RS_MT - 1) / (16 * RS_MT);
     int64_t n_ranges = std::min<int64_t>(n_cu, (tiles_total + RS_WAVES - 1) / RS_WAVES);
-    if (n_groups > 1) n_ranges = (n_ranges + 7) / 8 * 8;
+    if (n_groups > 1) {
+      n_ranges = (n_ranges + 7) / 8 * 8;
+      // column groups: one round of workgroups (ranges x groups = CUs) when every range still
+      // holds 64+ tiles.  Two rounds measured slower on a 10M-token store (T = 128: 76.8 vs
+      // 72.8 us; 200 columns: 170.8 vs 150.9 us) but faster on a 1M-token one (16.7 vs 21.4 us).
+      const int64_t one_round = std::max<int64_t>(8, (n_cu / n_groups) / 8 * 8);
+      if (one_round < n_ranges && tiles_total >= 64 * one_round) n_ranges = one_round;
+    }
     const int64_t tiles_per_range = (tiles_total + n_ranges - 1) / n_ranges;
     XcdSplit xs{};
     // only long ranges: at ~40 tiles per range (a 10M-token store) the split measured no faster
-    if (n_ranges == n_cu && n_cu % 8 == 0 && tiles_total >= RB_MIN_TILES * n_ranges) {
+    if (n_ranges * n_groups == n_cu && n_ranges % 8 == 0 && tiles_total >= RB_MIN_TILES * n_ranges) {
       float sh[8];
       bool have = shares != nullptr;
       if (have) {
@@ -618,7 +625,7 @@ static int route_score(const std::string& fn, int dtype, const void* q_r, int B,
       } else {
         have = device_shares(dev, sh);
       }
-      if (have) xs = make_split(sh, tiles_total, n_cu / 8);
+      if (have) xs = make_split(sh, tiles_total, n_ranges / 8);
     }
     if (split_used) *split_used = xs.on != 0;
     if (n_wg) *n_wg = int(n_ranges * n_groups);

@@ -148,13 +148,13 @@ def test_route_balance_keeps_the_scores(layout):
     rows = torch.empty((n_chunks, H, d), dtype=torch.bfloat16, device=dev())
     SD.fill(rows, 41, 0, synth.T_KR)
     st = M.msa_tile_routing_keys(rows) if layout == 1 else rows
-    shapes = ((1, 64), (32, 1), (1, 128), (2, 100))   # the last two: two column groups per range
+    shapes = ((1, 64), (32, 1), (1, 128), (2, 100), (3, 64))   # the last three: 2, 4 and 3 column groups
     qs = [SD.fill(torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev()), 42 + i, 0, synth.T_QR)
           for i, (B, T) in enumerate(shapes)]
     try:
         M.msa_route_balance(None, None, None, 0, rounds=0)
         refs = [M.msa_route_score(q, st, cd, D, layout=layout).clone() for q in qs]
-        for q, (B, T) in zip(qs[:2], shapes[:2]):
+        for q, (B, T) in zip(qs[:3], shapes[:3]):   # one and two column groups can be calibrated
             shares = M.msa_route_balance(q, st, cd, D, rounds=2, layout=layout)
             assert abs(float(shares.sum()) - 1.0) < 1e-5
             assert (shares >= 0.75 / 8 - 1e-6).all() and (shares <= 1.25 / 8 + 1e-6).all()
@@ -163,8 +163,8 @@ def test_route_balance_keeps_the_scores(layout):
                 got = M.msa_route_score(q2, st, cd, D, layout=layout)
                 torch.cuda.synchronize()
                 assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), f"B={B2} T={T2}"
-        # a shape that cannot be calibrated (two column groups): the shares stay
-        kept = M.msa_route_balance(qs[2], st, cd, D, rounds=1, layout=layout)
+        # three column groups do not divide the CUs into one round: no calibration, the shares stay
+        kept = M.msa_route_balance(qs[4], st, cd, D, rounds=1, layout=layout)
         assert np.array_equal(kept, shares)
     finally:
         cleared = M.msa_route_balance(None, None, None, 0, rounds=0)
