@@ -285,9 +285,11 @@ def msa_route_balance(q_r, kr_hat, chunk_doc, n_docs, rounds=3, doc_score=None, 
         return shares
     _dev(q_r, "q_r", _FLOAT, (None, None, None, None))
     B, T, H, d = q_r.shape
-    _dev(kr_hat, "kr_hat", q_r.dtype)
     _dev(chunk_doc, "chunk_doc", _I32, (None,))
-    n_chunks = chunk_doc.shape[0]
+    n_chunks = chunk_doc.numel()
+    _dev(kr_hat, "kr_hat", q_r.dtype, (None, H, d))
+    if kr_hat.shape[0] < padded_chunks(n_chunks, layout):
+        raise ValueError("kr_hat holds fewer chunks than chunk_doc names")
     dt = _dtype(q_r)
     if doc_score is None:
         doc_score = torch.empty((B, n_docs), dtype=torch.float32, device=q_r.device)

@@ -264,6 +264,11 @@ def test_binding_rejects_host_tensor_as_device_operand():
     cd = torch.zeros(32, dtype=torch.int32)
     with pytest.raises(ValueError, match="q_r: must be in device memory"):
         M.msa_route_score(q_r, kr, cd, 4)
+    with pytest.raises(ValueError, match="q_r: must be in device memory"):
+        M.msa_route_balance(q_r, kr, cd, 4)
+    with pytest.raises(ValueError, match="q: must be in device memory"):
+        M.msa_sparse_attn_part(M.MSA_ATTN_PART_LOCAL, _cpu((1, 4, 32, 128)), _cpu((1, 8, 8, 128)),
+                               _cpu((1, 8, 8, 128)), 4, 16)
     with pytest.raises(ValueError, match="doc_score: must be in device memory"):
         M.msa_topk(torch.zeros((1, 10)), 4)
     with pytest.raises(ValueError, match="chunk_off: must be in device memory"):
