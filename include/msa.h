@@ -203,9 +203,10 @@ int msa_encode_project(int dtype, const void* w_t, int hidden, int H, int d, int
 
 /*
  * msa_route_score - Stage 2 routing score (README, Overall Design >
- * Architecture: cosine similarity, mean-pooled over heads, then token-wise
- * max; paper note 核心方法 > 架构: cosine against every document's compressed
- * routing key).  For query b and document i:
+ * Architecture: each chunk's cosine with the routing query is averaged across
+ * heads, and the largest value over the query's tokens is kept; paper note
+ * 核心方法 > 架构: every document's compressed routing key is compared by
+ * cosine).  For query b and document i:
  *   doc_score[b,i] = max over tokens t < T and chunks c of document i of
  *                    (1/H) * sum_h < q_r[b,t,h,:] / max(||q_r[b,t,h,:]||, 1e-8), kr_hat[c,h,:] >
  * kr_hat must already be L2-normalised (msa_pool_encode with l2_normalize),
@@ -426,9 +427,9 @@ int msa_context_append(const int32_t* ids, int B, int k, const int64_t* chunk_of
 
 /*
  * msa_sparse_attn - Stage 3 sparse attention (README, Overall Design >
- * Architecture: the selected compressed K/V concatenated with the query's
- * local K/V for autoregressive decoding; its parallel (document-wise) RoPE
- * and global RoPE items; paper note, Document-wise RoPE).
+ * Architecture: the chosen documents' pooled K/V placed ahead of the query's
+ * own recent K/V, attended over at each decoding step; its parallel
+ * (document-wise) RoPE and global RoPE items; paper note, Document-wise RoPE).
  * For query b, token t < T and query head hq (KV head g = hq / (Hq/Hkv)):
  *   keys: context entries e < ctx_len[b] at position ctx_pos[b,e] (each
  *         document restarts at 0), all visible; local tokens i < L_loc at

@@ -1,7 +1,8 @@
 // Stage 3 sparse attention over [retrieved pooled K/V ; local K/V] with
 // document-wise RoPE applied on the fly.
-// (MSA README, Overall Design > Architecture: the selected compressed K/V
-//  are concatenated with the query's local K/V for autoregressive decoding;
+// (MSA README, Overall Design > Architecture: the chosen documents' pooled
+//  K/V are placed ahead of the query's own recent K/V, and each generated
+//  token attends over both;
 //  under the parallel (document-wise) RoPE item every document restarts at
 //  position 0; under the global RoPE item the query starts at index k.  Paper note,
 //  Document-wise RoPE.)
