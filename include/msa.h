@@ -479,8 +479,9 @@ int msa_sparse_attn_indexed(int dtype, const void* q, int B, int T, int Hq, int 
  * msa_sparse_attn_part - msa_sparse_attn (or, with ctx_row, _indexed) in two
  * calls, so that the local-window half of the attention can run while the
  * selected documents' K/V are still being fetched (README, Overall Design >
- * Inference Pipeline: content K/V stays in host memory and is fetched
- * asynchronously once the top-k is known; the local tokens need no fetch).
+ * Inference Pipeline: the pooled content K/V live in host memory and are brought
+ * over in the background once the top-k is known; the local tokens need no
+ * fetch).
  *   part = MSA_ATTN_PART_LOCAL: the local keys only, as partial softmax sums
  *     into ws.  Reads q, k_loc, v_loc and the RoPE rows; the context arguments
  *     (k_ctx, v_ctx, ctx_row, ctx_pos, ctx_len) and out are not read and may be
