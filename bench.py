@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="on the host tier, run each layer's attention as its two calls, the local-window part on "
                          "a side stream beside the fetch (measured slower than one call after the fetch)")
+    ap.add_argument("--no-fill-in-topk", action="store_true",
+                    help="fill the score buffer with -inf in a launch of its own before every routing call (by "
+                         "default each layer's top-k leaves it at -inf for the next layer's routing call)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP graph replay; for counter collection)")
     ap.add_argument("--layers", type=int, default=None, help="override the routed-layer count (profiling only)")
@@ -117,7 +120,7 @@ def main():
 
     p = configs.PRESETS[args.config]()
     pb = PresetBench(torch, p, args.layers, rounds=args.rounds, graph=not args.no_graph,
-                     overlap=args.overlap)
+                     overlap=args.overlap, fill_in_topk=not args.no_fill_in_topk)
     pb.build_stores()
     pb.build_content("hbm")
     assembly = args.hbm_assembly if args.rounds == 1 else "index"
@@ -168,7 +171,7 @@ class PresetBench:
     """One workload preset on the device: its stores (built by the offline
     stage before any timing), a LayerRunner and the whole-path step."""
 
-    def __init__(self, torch, p, layers=None, rounds=1, graph=True, overlap=False):
+    def __init__(self, torch, p, layers=None, rounds=1, graph=True, overlap=False, fill_in_topk=True):
         import synth
         from synth import device as SD
         import sparse_attention_long_msa_amd as M
@@ -177,6 +180,7 @@ class PresetBench:
         self.rounds = rounds
         self.graph = graph
         self.overlap = overlap
+        self.fill_in_topk = fill_in_topk and rounds == 1
         self.dev = torch.device("cuda:0")
         torch.cuda.set_device(self.dev)
         self.bf = torch.bfloat16 if p.bf16 else torch.float32
@@ -273,7 +277,7 @@ class PresetBench:
                                     q_pos_offset=p.qpo if self.rounds == 1 else None, rope_base=p.rope_base,
                                     src_mode=M.MSA_SRC_DEVICE if src_mode is None else src_mode,
                                     chunk_off_h=p.chunk_off, kr_layout=self.kr_layout, indexed=indexed,
-                                    rounds=self.rounds, overlap_local=overlap)
+                                    rounds=self.rounds, overlap_local=overlap, fill_in_topk=self.fill_in_topk)
         return self.runner
 
     def step(self, ev=None, route_ev=None, route_layer=-1, kv=None, flush=None):
@@ -417,9 +421,11 @@ class PresetBench:
         step_bytes = store_bytes * layers * self.rounds        # every round scans the layer's store
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
         routing_gbps = step_bytes / ((stage[0] + stage[1]) * 1e-3) / 1e9
-        # algorithmic bytes of one msa_route_score launch: the store, the chunk->doc map,
-        # the routing query and the score row (initial fill + result)
-        alg_bytes = store_bytes + N * 4 + p.B * p.T * H * d * self.esz + 2 * p.B * D * 4
+        # algorithmic bytes of one msa_route_score call: the store, the chunk->doc map,
+        # the routing query and the score row (the result, and the -inf fill when the
+        # call launches it itself)
+        fills = 1 if self.runner.fill_in_topk else 2
+        alg_bytes = store_bytes + N * 4 + p.B * p.T * H * d * self.esz + fills * p.B * D * 4
         route_avg_ms = float(np.mean(route_ms))
         achieved = alg_bytes / (route_avg_ms * 1e-3) / 1e9
         attn_bytes = self.attn_bytes()
@@ -452,6 +458,8 @@ class PresetBench:
             "data": "synthetic (seeded counter-based generator; planted needles)",
             "config": {"workload": workload, "global_batch": p.B, "seq_len": p.T, "parallelism": "single GPU",
                        "kv_tier": tier, "rounds": self.rounds, "step_launch": launch,
+                       "score_fill": ("in the previous layer's top-k (MSA_TOPK_RESET_SCORES)"
+                                      if self.runner.fill_in_topk else "a launch before each routing call"),
                        "attention_calls": ("two: the local-window part on a side stream beside the fetch, the "
                                            "context part and the merge after it")
                        if self.runner.overlap_local else "one, after the context is assembled"},
@@ -465,7 +473,8 @@ class PresetBench:
             "attention_frac_of_8TBps": round(attn_gbps / 8000, 4),
             "attention_bytes_per_layer": attn_bytes,
             "encode_GBps": round(encode_gbps, 1),
-            "roofline": {"kernel": "msa_route_score (route_score_mfma_kernel + score fill)", "bound": "hbm",
+            "roofline": {"kernel": "msa_route_score (route_score_mfma_kernel" +
+                                   (")" if self.runner.fill_in_topk else " + score fill)"), "bound": "hbm",
                          "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
                          "frac": round(achieved / 8000.0, 4), "traffic": counted_traffic(p.name),
                          "avg_launch_ms": round(route_avg_ms, 4), "alg_bytes_per_launch": int(alg_bytes)},
@@ -643,7 +652,7 @@ def config_leg(torch, name, args):
     on the host's cores (bounded samples)."""
     from synth import configs
     p = configs.PRESETS[name]()
-    pb = PresetBench(torch, p, graph=not args.no_graph, overlap=args.overlap)
+    pb = PresetBench(torch, p, graph=not args.no_graph, overlap=args.overlap, fill_in_topk=not args.no_fill_in_topk)
     pb.build_stores()
     pb.build_content("hbm")
     pb.make_runner("hbm", indexed=True)

@@ -80,6 +80,16 @@ typedef enum {
   MSA_ATTN_PART_CONTEXT = 2  /* msa_sparse_attn_part: the context keys, then the merge    */
 } msa_attn_part;
 
+typedef enum {
+  MSA_ROUTE_PREFILLED = 1    /* msa_route_score: doc_score already holds -inf everywhere (left so
+                                by msa_topk with MSA_TOPK_RESET_SCORES); the call skips its fill */
+} msa_route_flags;
+
+typedef enum {
+  MSA_TOPK_RESET_SCORES = 1  /* msa_topk, msa_topk_context_index: write -inf over doc_score as it
+                                is read, ready for the next layer's MSA_ROUTE_PREFILLED call     */
+} msa_topk_flags;
+
 /* Version of this ABI (bumped on any signature or workspace-layout change, and on added calls). */
 int msa_abi_version(void);
 
@@ -226,11 +236,17 @@ int msa_encode_project(int dtype, const void* w_t, int hidden, int H, int d, int
  *   ws         msa_route_score_workspace() bytes (may be 0 -> ws may be NULL)
  * Errors: INVALID_ARG (NULL, non-positive sizes, bad layout), WORKSPACE,
  * UNSUPPORTED (d > 256 or d % 8 != 0; MSA_LAYOUT_TILED outside the MFMA path).
+ *   flags      0, or MSA_ROUTE_PREFILLED: the call does not fill doc_score
+ *              with -inf first (a separate launch); the caller guarantees
+ *              that every entry already holds -inf, as a previous msa_topk
+ *              with MSA_TOPK_RESET_SCORES on the same buffer leaves it.  Any
+ *              other content is max-combined into the result (wrong scores,
+ *              no error).
  */
 size_t msa_route_score_workspace(int dtype, int B, int T, int H, int d, int64_t n_docs, int64_t n_chunks);
 int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat, int kr_layout,
                     const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks, float* doc_score,
-                    void* ws, size_t ws_bytes, void* stream);
+                    void* ws, size_t ws_bytes, int flags, void* stream);
 
 /*
  * msa_route_balance - sizes msa_route_score's chunk ranges per XCD on the
@@ -296,12 +312,17 @@ int msa_segment_max(const float* chunk_score, int B, int64_t n_chunks, const int
  *              when fewer than k documents are left, the trailing ids are -1
  *              (their vals NaN)
  *   ws        msa_topk_workspace() bytes
- * Errors: INVALID_ARG (NULL, B < 1, k < 1, k > n_docs), UNSUPPORTED (k > 256),
- * WORKSPACE.
+ *   flags     0, or MSA_TOPK_RESET_SCORES: the first selection pass writes
+ *              -inf over each score once it has read it, so doc_score leaves
+ *              the call ready for msa_route_score with MSA_ROUTE_PREFILLED
+ *              (the fill moves into a pass that reads the buffer anyway);
+ *              doc_score then no longer holds the scores
+ * Errors: INVALID_ARG (NULL, B < 1, k < 1, k > n_docs, unknown flags),
+ * UNSUPPORTED (k > 256), WORKSPACE.
  */
 size_t msa_topk_workspace(int B, int64_t n_docs, int k);
-int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
-             size_t ws_bytes, void* stream);
+int msa_topk(float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
+             size_t ws_bytes, int flags, void* stream);
 
 /*
  * msa_topk_merge - Memory Parallel's global reduce (README, Overall Design >
@@ -400,13 +421,14 @@ int msa_context_index(const int32_t* ids, int B, int k, const int64_t* chunk_off
  * documents, also writes their context entries.  Outputs are exactly those
  * of the two calls (ids, vals, ctx_row, ctx_pos, ctx_len).  For k > 64 the
  * two calls run one after the other.
- *   arguments as for msa_topk and msa_context_index; ws: msa_topk_workspace()
+ *   arguments as for msa_topk and msa_context_index; ws: msa_topk_workspace();
+ *   flags as for msa_topk
  * Errors: those of msa_topk and of msa_context_index.
  */
-int msa_topk_context_index(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals,
+int msa_topk_context_index(float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals,
                            const int64_t* chunk_off, int max_doc_chunks, int64_t n_chunks, int max_ctx,
                            int32_t* ctx_row, int32_t* ctx_pos, int32_t* ctx_len, void* ws, size_t ws_bytes,
-                           void* stream);
+                           int flags, void* stream);
 
 /*
  * msa_context_append - msa_context_index for one more round of Memory

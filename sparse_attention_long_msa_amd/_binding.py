@@ -18,6 +18,8 @@ MSA_F32, MSA_BF16 = 0, 1
 MSA_SRC_DEVICE, MSA_SRC_HOST_MAPPED, MSA_SRC_HOST_MEMCPY = 0, 1, 2
 MSA_LAYOUT_ROWS, MSA_LAYOUT_TILED = 0, 1
 MSA_ATTN_PART_LOCAL, MSA_ATTN_PART_CONTEXT = 1, 2
+MSA_ROUTE_PREFILLED = 1
+MSA_TOPK_RESET_SCORES = 1
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -34,17 +36,17 @@ _SIGS = {
     "msa_tile_routing_keys": (_I, [_I, _P, _L, _I, _I, _P, _P]),
     "msa_pool_encode": (_I, [_I, _P, _P, _P, _P, _L, _L, _L, _I, _I, _I, _I, _I, _P, _P]),
     "msa_route_score_workspace": (_S, [_I, _I, _I, _I, _I, _L, _L]),
-    "msa_route_score": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P, _P, _S, _P]),
+    "msa_route_score": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P, _P, _S, _I, _P]),
     "msa_route_balance": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P, _P, _S, _I, _P, _P]),
     "msa_chunk_scores": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _L, _P, _P, _S, _P]),
     "msa_segment_max": (_I, [_P, _I, _L, _P, _L, _P, _P]),
     "msa_topk_workspace": (_S, [_I, _L, _I]),
-    "msa_topk": (_I, [_P, _I, _L, _I, _P, _P, _P, _S, _P]),
+    "msa_topk": (_I, [_P, _I, _L, _I, _P, _P, _P, _S, _I, _P]),
     "msa_topk_merge": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "msa_gather_kv": (_I, [_I, _P, _I, _I, _P, _P, _L, _I, _P, _P, _L, _I, _I, _I, _I,
                            _P, _P, _P, _P, _P, _P, _P]),
     "msa_context_index": (_I, [_P, _I, _I, _P, _L, _I, _L, _I, _P, _P, _P, _P]),
-    "msa_topk_context_index": (_I, [_P, _I, _L, _I, _P, _P, _P, _I, _L, _I, _P, _P, _P, _P, _S, _P]),
+    "msa_topk_context_index": (_I, [_P, _I, _L, _I, _P, _P, _P, _I, _L, _I, _P, _P, _P, _P, _S, _I, _P]),
     "msa_exclude_docs": (_I, [_P, _I, _L, _P, _I, _I, _P]),
     "msa_context_append": (_I, [_P, _I, _I, _P, _L, _I, _L, _I, _P, _P, _P, _P, _P]),
     "msa_sparse_attn_workspace": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
@@ -252,7 +254,12 @@ def msa_route_score_workspace(dtype, B, T, H, d, n_docs, n_chunks):
     return lib.msa_route_score_workspace(dtype, B, T, H, d, n_docs, n_chunks)
 
 
-def msa_route_score(q_r, kr_hat, chunk_doc, n_docs, doc_score=None, ws=None, layout=MSA_LAYOUT_ROWS, stream=None):
+def msa_route_score(q_r, kr_hat, chunk_doc, n_docs, doc_score=None, ws=None, layout=MSA_LAYOUT_ROWS, stream=None,
+                    prefilled=False):
+    """prefilled: doc_score already holds -inf everywhere (msa_topk with
+    reset=True left it so); the call then skips its fill."""
+    if prefilled and doc_score is None:
+        raise ValueError("prefilled needs the doc_score buffer that holds -inf")
     _dev(q_r, "q_r", _FLOAT, (None, None, None, None))
     B, T, H, d = q_r.shape
     _dev(chunk_doc, "chunk_doc", _I32, (None,))
@@ -268,7 +275,7 @@ def msa_route_score(q_r, kr_hat, chunk_doc, n_docs, doc_score=None, ws=None, lay
     ws, wsb = _ws(msa_route_score_workspace(dt, B, T, H, d, n_docs, n_chunks), q_r.device, ws)
     _check("msa_route_score", lib.msa_route_score(
         dt, _ptr(q_r), B, T, H, d, _ptr(kr_hat), layout, _ptr(chunk_doc), n_docs, n_chunks, _ptr(doc_score),
-        _ptr(ws), wsb, _stream(stream)))
+        _ptr(ws), wsb, MSA_ROUTE_PREFILLED if prefilled else 0, _stream(stream)))
     return doc_score
 
 
@@ -339,7 +346,9 @@ def msa_topk_workspace(B, n_docs, k):
     return lib.msa_topk_workspace(B, n_docs, k)
 
 
-def msa_topk(doc_score, k, ids=None, vals=None, ws=None, stream=None):
+def msa_topk(doc_score, k, ids=None, vals=None, ws=None, stream=None, reset=False):
+    """reset: write -inf over doc_score as it is read (it then no longer
+    holds the scores), ready for msa_route_score(prefilled=True)."""
     _dev(doc_score, "doc_score", _F32, (None, None))
     B, n_docs = doc_score.shape
     if ids is None:
@@ -351,7 +360,7 @@ def msa_topk(doc_score, k, ids=None, vals=None, ws=None, stream=None):
     _dev(ws, "ws", optional=True)
     ws, wsb = _ws(msa_topk_workspace(B, n_docs, k), doc_score.device, ws)
     _check("msa_topk", lib.msa_topk(_ptr(doc_score), B, n_docs, k, _ptr(ids), _ptr(vals), _ptr(ws), wsb,
-                                    _stream(stream)))
+                                    MSA_TOPK_RESET_SCORES if reset else 0, _stream(stream)))
     return ids, vals
 
 
@@ -440,8 +449,9 @@ def msa_context_index(ids, chunk_off, n_chunks, max_doc_chunks, max_ctx, ctx_row
 
 
 def msa_topk_context_index(doc_score, k, chunk_off, n_chunks, max_doc_chunks, max_ctx, ids=None, vals=None,
-                           ctx_row=None, ctx_pos=None, ctx_len=None, ws=None, stream=None):
-    """msa_topk then msa_context_index on its ids, in one pass for k <= 64."""
+                           ctx_row=None, ctx_pos=None, ctx_len=None, ws=None, stream=None, reset=False):
+    """msa_topk then msa_context_index on its ids, in one pass for k <= 64;
+    reset as for msa_topk."""
     _dev(doc_score, "doc_score", _F32, (None, None))
     _dev(chunk_off, "chunk_off", _I64, (doc_score.shape[1] + 1,))
     B, n_docs = doc_score.shape
@@ -457,7 +467,8 @@ def msa_topk_context_index(doc_score, k, chunk_off, n_chunks, max_doc_chunks, ma
     ws, wsb = _ws(msa_topk_workspace(B, n_docs, k), dev, ws)
     _check("msa_topk_context_index", lib.msa_topk_context_index(
         _ptr(doc_score), B, n_docs, k, _ptr(ids), _ptr(vals), _ptr(chunk_off), max_doc_chunks, n_chunks, max_ctx,
-        _ptr(ctx_row), _ptr(ctx_pos), _ptr(ctx_len), _ptr(ws), wsb, _stream(stream)))
+        _ptr(ctx_row), _ptr(ctx_pos), _ptr(ctx_len), _ptr(ws), wsb, MSA_TOPK_RESET_SCORES if reset else 0,
+        _stream(stream)))
     return ids, vals, ctx_row, ctx_pos, ctx_len
 
 

@@ -565,12 +565,13 @@ namespace msa {
 // (chunk_doc NULL: every chunk is its own document, n_docs = n_chunks).
 // shares (msa_route_balance): the XCD shares to use instead of the device's;
 // wg_ts: per-workgroup start and end stamps; *split_used: whether the ranges
-// were sized per XCD (one workgroup per CU).
+// were sized per XCD (one workgroup per CU); prefilled: doc_score already
+// holds -inf (MSA_ROUTE_PREFILLED), so the fill is not launched.
 static int route_score(const std::string& fn, int dtype, const void* q_r, int B, int T, int H, int d,
                        const void* kr_hat, int kr_layout, const int32_t* chunk_doc, int64_t n_docs,
                        int64_t n_chunks, float* doc_score, void* ws, size_t ws_bytes, void* stream,
                        const float* shares = nullptr, uint64_t* wg_ts = nullptr, bool* split_used = nullptr,
-                       int* n_wg = nullptr) {
+                       int* n_wg = nullptr, bool prefilled = false) {
   if (split_used) *split_used = false;
   using namespace msa;
   MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
@@ -591,7 +592,7 @@ static int route_score(const std::string& fn, int dtype, const void* q_r, int B,
   hipStream_t s = as_stream(stream);
   const int J = B * T;
   const int64_t nscore = int64_t(B) * n_docs;
-  {
+  if (!prefilled) {
     const int64_t blocks = std::min<int64_t>((nscore + 255) / 256, 65536);
     hipLaunchKernelGGL(fill_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, doc_score, nscore, -INFINITY);
     MSA_LAUNCH_CHECK();
@@ -722,10 +723,12 @@ static int route_score(const std::string& fn, int dtype, const void* q_r, int B,
 
 extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
                                int kr_layout, const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks,
-                               float* doc_score, void* ws, size_t ws_bytes, void* stream) {
+                               float* doc_score, void* ws, size_t ws_bytes, int flags, void* stream) {
   MSA_REQUIRE(chunk_doc, MSA_ERR_INVALID_ARG, "msa_route_score: NULL pointer");
+  MSA_REQUIRE((flags & ~MSA_ROUTE_PREFILLED) == 0, MSA_ERR_INVALID_ARG, "msa_route_score: unknown flags");
   return msa::route_score("msa_route_score", dtype, q_r, B, T, H, d, kr_hat, kr_layout, chunk_doc, n_docs, n_chunks,
-                          doc_score, ws, ws_bytes, stream);
+                          doc_score, ws, ws_bytes, stream, nullptr, nullptr, nullptr, nullptr,
+                          (flags & MSA_ROUTE_PREFILLED) != 0);
 }
 
 extern "C" int msa_chunk_scores(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,

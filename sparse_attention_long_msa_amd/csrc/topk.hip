@@ -26,11 +26,16 @@ constexpr int TK_MAXK = 256;
 // in:  scores [B][n] (FROM_SCORES) or keys [B][n]
 // out: keys [B][n_slices][k] (sorted ascending inside a slice), or, when
 //      FINAL, ids/vals [B][k]
+//
+// reset (FROM_SCORES passes only): once its scores are read, each workgroup
+// writes -inf over them, leaving the buffer ready for a routing call that
+// max-accumulates (msa_route_score with MSA_ROUTE_PREFILLED).
 template <bool FROM_SCORES, bool FINAL>
-__global__ __launch_bounds__(TK_THREADS) void topk_pass_kernel(const float* __restrict__ scores,
+__global__ __launch_bounds__(TK_THREADS) void topk_pass_kernel(float* __restrict__ scores,
                                                                const uint64_t* __restrict__ keys_in, int64_t n,
                                                                int k, uint64_t* __restrict__ keys_out,
-                                                               int32_t* __restrict__ ids, float* __restrict__ vals) {
+                                                               int32_t* __restrict__ ids, float* __restrict__ vals,
+                                                               int reset) {
   __shared__ uint64_t sk[TK_SLICE];
   const int b = blockIdx.y;
   const int64_t slice = blockIdx.x;
@@ -49,6 +54,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_pass_kernel(const float* __re
     sk[i] = key;
   }
   __syncthreads();
+  if (FROM_SCORES && reset) {   // the slice is read (its keys are in LDS)
+    for (int i = threadIdx.x; i < TK_SLICE; i += TK_THREADS)
+      if (base + i < n) scores[int64_t(b) * n + base + i] = -INFINITY;
+  }
   for (int size = 2; size <= TK_SLICE; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = threadIdx.x; i < TK_SLICE / 2; i += TK_THREADS) {
@@ -154,10 +163,10 @@ __device__ void context_index_wave(uint64_t key, int lane, int k, int b, const C
 // not FINAL, they go to keys_out[b][workgroup][k]; FINAL (one workgroup per
 // query), they are written as ids/vals.
 template <bool FROM_SCORES, bool FINAL, int TW_PER_LANE, int W>
-__global__ __launch_bounds__(64 * W) void topk_wave_kernel(const float* __restrict__ scores,
+__global__ __launch_bounds__(64 * W) void topk_wave_kernel(float* __restrict__ scores,
                                                            const uint64_t* __restrict__ keys_in, int64_t n, int k,
                                                            uint64_t* __restrict__ keys_out, int32_t* __restrict__ ids,
-                                                           float* __restrict__ vals, CtxOut cx) {
+                                                           float* __restrict__ vals, CtxOut cx, int reset) {
   constexpr int TW_PER_WAVE = 64 * TW_PER_LANE;
   extern __shared__ uint64_t surv_lds[];   // [W][tw_slots(k, TW_PER_LANE)]
   const int slots = tw_slots(k, TW_PER_LANE);
@@ -208,6 +217,13 @@ __global__ __launch_bounds__(64 * W) void topk_wave_kernel(const float* __restri
   // the list of wave w + half, log2(W) rounds
   static_assert((W & (W - 1)) == 0, "a power-of-two number of waves");
   __syncthreads();
+  if (FROM_SCORES && reset) {   // every score of this wave is read (its keys are sorted)
+#pragma unroll
+    for (int i = 0; i < TW_PER_LANE; ++i) {
+      const int64_t g = base + int64_t(i) * 64 + lane;
+      if (g < n) scores[int64_t(b) * n + g] = -INFINITY;
+    }
+  }
   sw[lane] = best;
   __syncthreads();
 #pragma unroll
@@ -297,20 +313,20 @@ extern "C" size_t msa_topk_workspace(int B, int64_t n_docs, int k) {
 }
 
 namespace msa {
-static int topk_run(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
-                    size_t ws_bytes, void* stream, const CtxOut& cx);
+static int topk_run(float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
+                    size_t ws_bytes, void* stream, const CtxOut& cx, int flags);
 }
 
-extern "C" int msa_topk(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
-                        size_t ws_bytes, void* stream) {
+extern "C" int msa_topk(float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
+                        size_t ws_bytes, int flags, void* stream) {
   return msa::topk_run(doc_score, B, n_docs, k, ids, vals, ws, ws_bytes, stream,
-                       msa::CtxOut{nullptr, 0, 0, nullptr, nullptr, nullptr});
+                       msa::CtxOut{nullptr, 0, 0, nullptr, nullptr, nullptr}, flags);
 }
 
-extern "C" int msa_topk_context_index(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids,
+extern "C" int msa_topk_context_index(float* doc_score, int B, int64_t n_docs, int k, int32_t* ids,
                                       float* vals, const int64_t* chunk_off, int max_doc_chunks, int64_t n_chunks,
                                       int max_ctx, int32_t* ctx_row, int32_t* ctx_pos, int32_t* ctx_len, void* ws,
-                                      size_t ws_bytes, void* stream) {
+                                      size_t ws_bytes, int flags, void* stream) {
   using namespace msa;
   MSA_REQUIRE(chunk_off && ctx_row && ctx_pos && ctx_len, MSA_ERR_INVALID_ARG,
               "msa_topk_context_index: NULL pointer");
@@ -320,19 +336,21 @@ extern "C" int msa_topk_context_index(const float* doc_score, int B, int64_t n_d
               "msa_topk_context_index: max_ctx < k * max_doc_chunks");
   if (k > 64) {   // the slice passes: the selection, then the index on its own
     const int rc = topk_run(doc_score, B, n_docs, k, ids, vals, ws, ws_bytes, stream,
-                            CtxOut{nullptr, 0, 0, nullptr, nullptr, nullptr});
+                            CtxOut{nullptr, 0, 0, nullptr, nullptr, nullptr}, flags);
     if (rc != MSA_OK) return rc;
     return msa_context_index(ids, B, k, chunk_off, n_docs, max_doc_chunks, n_chunks, max_ctx, ctx_row, ctx_pos,
                              ctx_len, stream);
   }
   return topk_run(doc_score, B, n_docs, k, ids, vals, ws, ws_bytes, stream,
-                  CtxOut{chunk_off, n_docs, max_ctx, ctx_row, ctx_pos, ctx_len});
+                  CtxOut{chunk_off, n_docs, max_ctx, ctx_row, ctx_pos, ctx_len}, flags);
 }
 
 namespace msa {
-static int topk_run(const float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
-                    size_t ws_bytes, void* stream, const CtxOut& cx) {
+static int topk_run(float* doc_score, int B, int64_t n_docs, int k, int32_t* ids, float* vals, void* ws,
+                    size_t ws_bytes, void* stream, const CtxOut& cx, int flags) {
   MSA_REQUIRE(doc_score && ids && vals, MSA_ERR_INVALID_ARG, "msa_topk: NULL pointer");
+  MSA_REQUIRE((flags & ~MSA_TOPK_RESET_SCORES) == 0, MSA_ERR_INVALID_ARG, "msa_topk: unknown flags");
+  const int reset = (flags & MSA_TOPK_RESET_SCORES) ? 1 : 0;
   MSA_REQUIRE(B >= 1 && n_docs >= 1, MSA_ERR_INVALID_ARG, "msa_topk: non-positive size");
   MSA_REQUIRE(k >= 1 && k <= n_docs, MSA_ERR_INVALID_ARG, "msa_topk: k must be in [1, n_docs]");
   MSA_REQUIRE(k <= TK_MAXK, MSA_ERR_UNSUPPORTED, "msa_topk: k > 256");
@@ -360,7 +378,7 @@ static int topk_run(const float* doc_score, int B, int64_t n_docs, int k, int32_
   MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_wave_kernel<FS, FIN, PL, W>),               \
                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));                         \
   hipLaunchKernelGGL((topk_wave_kernel<FS, FIN, PL, W>), grid, block, lds, s, doc_score, kin, n, k, kout, ids, vals, \
-                     last ? cx : CtxOut{nullptr, 0, 0, nullptr, nullptr, nullptr})
+                     last ? cx : CtxOut{nullptr, 0, 0, nullptr, nullptr, nullptr}, first ? reset : 0)
       if (first && last && wide) {
         TW_LAUNCH(true, true, TW_PL_WIDE, TW_WAVES_WIDE);
       } else if (first && last) {
@@ -389,13 +407,17 @@ static int topk_run(const float* doc_score, int B, int64_t n_docs, int k, int32_
     const uint64_t* kin = first ? nullptr : buf[(p - 1) % 2];
     uint64_t* kout = last ? nullptr : buf[p % 2];
     if (first && last)
-      hipLaunchKernelGGL((topk_pass_kernel<true, true>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+      hipLaunchKernelGGL((topk_pass_kernel<true, true>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals,
+                         first ? reset : 0);
     else if (first)
-      hipLaunchKernelGGL((topk_pass_kernel<true, false>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+      hipLaunchKernelGGL((topk_pass_kernel<true, false>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals,
+                         first ? reset : 0);
     else if (last)
-      hipLaunchKernelGGL((topk_pass_kernel<false, true>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+      hipLaunchKernelGGL((topk_pass_kernel<false, true>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals,
+                         first ? reset : 0);
     else
-      hipLaunchKernelGGL((topk_pass_kernel<false, false>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals);
+      hipLaunchKernelGGL((topk_pass_kernel<false, false>), grid, block, 0, s, doc_score, kin, n, k, kout, ids, vals,
+                         first ? reset : 0);
     MSA_LAUNCH_CHECK();
   }
   return MSA_OK;

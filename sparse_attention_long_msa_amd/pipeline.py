@@ -17,6 +17,15 @@ part, with the merge, after both.  At the 100M-token preset's host tier this
 measured slower than one call after the fetch (the two streams' kernels slow
 each other, and the fork and join cost more than the overlap saves), so it is
 off by default; started earlier, beside the top-k, it was slower still.
+
+With ``fill_in_topk=True`` the routing score's -inf fill (a launch of its own
+per layer) moves into the top-k: its first pass writes -inf over the scores
+once it has read them (MSA_TOPK_RESET_SCORES), and the next route() skips the
+fill (MSA_ROUTE_PREFILLED).  ``doc_score`` then holds -inf after select(), not
+the scores.  The runner tracks whether the buffer was left so; a route() that
+follows anything else fills as usual.  A captured step (StepGraph) must start
+where the last call on the runner was a select (as after any run()), and every
+replay leaves it so.
 """
 from __future__ import annotations
 
@@ -31,7 +40,7 @@ class LayerRunner:
     def __init__(self, *, batch, tokens, q_heads, kv_heads, head_dim, n_docs, n_chunks, k, max_doc_chunks,
                  local_len, dtype, device, q_pos_offset=None, rope_base=1e6, sm_scale=None,
                  src_mode=B.MSA_SRC_DEVICE, chunk_off_h=None, kr_layout=B.MSA_LAYOUT_ROWS, indexed=False,
-                 rounds=1, overlap_local=False):
+                 rounds=1, overlap_local=False, fill_in_topk=False):
         if indexed and src_mode != B.MSA_SRC_DEVICE:
             raise ValueError("indexed assembly reads the K/V store in place: it must be in device memory")
         if rounds > 1 and not indexed:
@@ -39,6 +48,8 @@ class LayerRunner:
         if rounds > 1 and overlap_local:
             raise ValueError("Memory Interleave runs the attention in one call (overlap_local is for one round)")
         self.rounds = rounds
+        self.fill_in_topk = fill_in_topk
+        self._prefilled = False   # doc_score holds -inf, left so by the last select()
         self.B, self.T, self.Hq, self.Hkv, self.d = batch, tokens, q_heads, kv_heads, head_dim
         self.n_docs, self.n_chunks, self.k = n_docs, n_chunks, k
         self.max_doc_chunks = max_doc_chunks
@@ -98,16 +109,20 @@ class LayerRunner:
         device from timed launches on this layer's arguments
         (msa_route_balance; it synchronises, so never inside a captured step).
         Scores are unchanged; returns the 8 XCD shares."""
+        self._prefilled = False   # the calibration writes scores into doc_score
         return B.msa_route_balance(q_r, kr_hat, chunk_doc, self.n_docs, rounds=rounds, doc_score=self.doc_score,
                                    ws=self.rs_ws, layout=self.kr_layout)
 
     def route(self, q_r, kr_hat, chunk_doc, stream=None):
+        prefilled, self._prefilled = self._prefilled, False
         B.msa_route_score(q_r, kr_hat, chunk_doc, self.n_docs, doc_score=self.doc_score, ws=self.rs_ws,
-                          layout=self.kr_layout, stream=stream)
+                          layout=self.kr_layout, stream=stream, prefilled=prefilled)
         return self.doc_score
 
     def select(self, stream=None):
-        B.msa_topk(self.doc_score, self.k, ids=self.ids, vals=self.vals, ws=self.tk_ws, stream=stream)
+        B.msa_topk(self.doc_score, self.k, ids=self.ids, vals=self.vals, ws=self.tk_ws, stream=stream,
+                   reset=self.fill_in_topk)
+        self._prefilled = self.fill_in_topk
         return self.ids, self.vals
 
     def select_assemble(self, chunk_off, k_bar, v_bar, stream=None):
@@ -118,7 +133,8 @@ class LayerRunner:
             return
         B.msa_topk_context_index(self.doc_score, self.k, chunk_off, k_bar.shape[0], self.max_doc_chunks, self.max_ctx,
                                  ids=self.ids, vals=self.vals, ctx_row=self.ctx_row, ctx_pos=self.ctx_pos,
-                                 ctx_len=self.ctx_len, ws=self.tk_ws, stream=stream)
+                                 ctx_len=self.ctx_len, ws=self.tk_ws, stream=stream, reset=self.fill_in_topk)
+        self._prefilled = self.fill_in_topk
         self._store = (k_bar, v_bar)
 
     def assemble(self, chunk_off, k_bar, v_bar, stream=None):
@@ -202,6 +218,7 @@ class LayerRunner:
                                      self.ctx_pos, self._lens[(r - 1) % 2], self._lens[r % 2], stream=stream)
         self.ctx_len = self._lens[(R - 1) % 2]
         self._store = (k_bar, v_bar)
+        self._prefilled = False   # the rounds keep their scores (no reset)
 
     def interleave(self, q_r_rounds, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc, stream=None):
         """Memory Interleave: fetch_rounds, then attention over every fetched

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.msa_abi_version() == 12
+    assert M.msa_abi_version() == 13
     assert M.lib.msa_status_string(0).decode() == "ok"
     assert "workspace" in M.lib.msa_status_string(3).decode()
 
@@ -58,27 +58,30 @@ Q = ctypes.c_void_p(48)   # a second one, for outputs that must not alias an inp
 
 def test_route_score_validation():
     L = M.lib
-    assert L.msa_route_score(1, None, 1, 1, 8, 128, P, 0, P, 4, 4, P, None, 0, None) == 1
-    assert L.msa_route_score(1, P, 0, 1, 8, 128, P, 0, P, 4, 4, P, None, 0, None) == 1
-    assert L.msa_route_score(7, P, 1, 1, 8, 128, P, 0, P, 4, 4, P, None, 0, None) == 1
-    assert L.msa_route_score(1, P, 1, 1, 8, 260, P, 0, P, 4, 4, P, None, 0, None) == 2
-    assert L.msa_route_score(1, P, 1, 1, 8, 128, P, 5, P, 4, 4, P, None, 0, None) == 1     # bad layout
-    assert L.msa_route_score(1, P, 1, 1, 4, 128, P, 1, P, 4, 4, P, P, 1 << 20, None) == 2  # tiled off the MFMA path
+    assert L.msa_route_score(1, None, 1, 1, 8, 128, P, 0, P, 4, 4, P, None, 0, 0, None) == 1
+    assert L.msa_route_score(1, P, 0, 1, 8, 128, P, 0, P, 4, 4, P, None, 0, 0, None) == 1
+    assert L.msa_route_score(7, P, 1, 1, 8, 128, P, 0, P, 4, 4, P, None, 0, 0, None) == 1
+    assert L.msa_route_score(1, P, 1, 1, 8, 260, P, 0, P, 4, 4, P, None, 0, 0, None) == 2
+    assert L.msa_route_score(1, P, 1, 1, 8, 128, P, 5, P, 4, 4, P, None, 0, 0, None) == 1     # bad layout
+    assert L.msa_route_score(1, P, 1, 1, 4, 128, P, 1, P, 4, 4, P, P, 1 << 20, 0, None) == 2  # tiled off the MFMA path
     # float32 needs a workspace for the column norms
     need = L.msa_route_score_workspace(0, 1, 16, 8, 128, 4, 4)
     assert need >= 16 * 8 * 4
-    assert L.msa_route_score(0, P, 1, 16, 8, 128, P, 0, P, 4, 4, P, P, need - 1, None) == 3
+    assert L.msa_route_score(0, P, 1, 16, 8, 128, P, 0, P, 4, 4, P, P, need - 1, 0, None) == 3
+    assert L.msa_route_score(1, P, 1, 1, 8, 128, P, 0, P, 4, 4, P, None, 0, 2, None) == 1   # unknown flag
 
 
 def test_topk_validation():
     L = M.lib
-    assert L.msa_topk(P, 1, 10, 0, P, P, P, 1 << 20, None) == 1
-    assert L.msa_topk(P, 1, 10, 11, P, P, P, 1 << 20, None) == 1
-    assert L.msa_topk(P, 1, 1000, 300, P, P, P, 1 << 30, None) == 2
+    assert L.msa_topk(P, 1, 10, 0, P, P, P, 1 << 20, 0, None) == 1
+    assert L.msa_topk(P, 1, 10, 11, P, P, P, 1 << 20, 0, None) == 1
+    assert L.msa_topk(P, 1, 1000, 300, P, P, P, 1 << 30, 0, None) == 2
     need = L.msa_topk_workspace(1, 100000, 16)
     assert need > 0
-    assert L.msa_topk(P, 1, 100000, 16, P, P, P, need - 1, None) == 3
+    assert L.msa_topk(P, 1, 100000, 16, P, P, P, need - 1, 0, None) == 3
     assert L.msa_topk_workspace(1, 4096, 16) == 0      # one slice: no workspace
+    assert L.msa_topk(P, 1, 10, 4, P, P, P, 1 << 20, 2, None) == 1     # unknown flag
+    assert L.msa_topk_context_index(P, 1, 10, 4, P, P, P, 8, 40, 32, P, P, P, P, 1 << 20, 2, None) == 1
 
 
 

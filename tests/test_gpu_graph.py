@@ -119,3 +119,69 @@ def test_step_graph_full_size(name, overlap):
                     assert torch.equal(getattr(r, n)[b, :n_b], eager[l][n][b, :n_b]), f"{name} replay {rep}: {n}"
     del g, layers
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("indexed", [True, False])
+def test_fill_in_topk_step_equals_the_filling_step(indexed):
+    """LayerRunner(fill_in_topk=True): one runner over three layers, as the
+    benchmark drives it, the score fill moved into the previous layer's top-k.
+    Eager steps and graph replays give the selection, context and attention
+    of a runner that fills before every routing call, bit for bit."""
+    B, T, L_loc, k, H, d, Hq, layers = 1, 64, 512, 8, 8, 128, 32, 3
+    lens = ragged_lengths(95, 700, 0, 900, n_empty=9)
+    tok_off = synth.offsets(lens)
+    chunk_off = O.chunk_offsets(tok_off, 64)
+    n_chunks, D = int(chunk_off[-1]), len(lens)
+    mdc = int(np.diff(chunk_off).max())
+    co_d = to_dev_i64(chunk_off)
+    cd = M.msa_chunk_doc_map(co_d, n_chunks)
+    L = []
+    for l in range(layers):
+        store = O.round_to_bf16(O.l2_normalize(gen(75, l, synth.T_KR, (n_chunks, H, d), True).astype(np.float64)))
+        L.append([to_dev(tile_np(store), True)] +
+                 [to_dev(gen(75, l, t, (n_chunks, H, d), True, scale_pow2=-3), True) for t in (synth.T_K, synth.T_V)] +
+                 [to_dev(gen(76, l, t, shp, True), True) for t, shp in ((synth.T_QR, (B, T, H, d)),
+                                                                        (synth.T_Q, (B, T, Hq, d)),
+                                                                        (synth.T_KLOC, (B, L_loc, H, d)),
+                                                                        (synth.T_VLOC, (B, L_loc, H, d)))])
+
+    def runner(fused):
+        return M.LayerRunner(batch=B, tokens=T, q_heads=Hq, kv_heads=H, head_dim=d, n_docs=D, n_chunks=n_chunks,
+                             k=k, max_doc_chunks=mdc, local_len=L_loc, dtype=torch.bfloat16, device=dev(),
+                             kr_layout=M.MSA_LAYOUT_TILED, indexed=indexed, fill_in_topk=fused)
+
+    names = ("ids", "vals", "ctx_len", "out")
+    plain, fused = runner(False), runner(True)
+
+    def step(r, keep=None):
+        for l, (kr, kb, vb, qr, q, kl, vl) in enumerate(L):
+            r.run(qr, kr, cd, co_d, kb, vb, q, kl, vl)
+            if keep is not None:
+                keep.append({n: getattr(r, n).clone() for n in names})
+
+    want = []
+    step(plain, want)
+    for rep in range(2):                                  # eager steps
+        got = []
+        step(fused, got)
+        torch.cuda.synchronize()
+        for l in range(layers):
+            for n in names:
+                assert torch.equal(got[l][n], want[l][n]), f"eager step {rep}, layer {l}: {n}"
+        assert bool((fused.doc_score == float("-inf")).all())
+    g = M.StepGraph(lambda: step(fused))
+    for rep in range(3):                                  # replays: the last layer's outputs
+        fused.out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(fused, n), want[-1][n]), f"replay {rep}: {n}"
+        step(fused)                                       # eager work on the same runner between replays
+        torch.cuda.synchronize()
+    # a route() that does not follow a select fills the buffer itself
+    kr, kb, vb, qr, q, kl, vl = L[0]
+    fused.route(qr, kr, cd)
+    fused.route(qr, kr, cd)
+    ref = plain.route(qr, kr, cd)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.doc_score.view(torch.int32), ref.view(torch.int32))

@@ -364,6 +364,66 @@ def test_topk_context_index_matches_the_two_calls(B, D, k, n_excl):
         assert (ids2[:, D - n_excl:] == -1).all()
 
 
+@pytest.mark.parametrize("B,D,k", [(1, 195312, 16), (32, 10518, 16), (2, 3000, 64), (3, 1, 1), (2, 20000, 100),
+                                    (1, 4096, 200)])
+def test_topk_reset_leaves_minus_inf(B, D, k):
+    """MSA_TOPK_RESET_SCORES: the selection and the context index are those of
+    the call without it, and every score reads -inf afterwards (a reducing
+    pass of either kind, a single pass, the k > 64 slice passes, NaN-excluded
+    documents)."""
+    r = np.random.default_rng(D * 3 + k)
+    lens = r.integers(1, 600, D)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    s = np.round(r.normal(size=(B, D)), 3).astype(np.float32)
+    s[:, r.integers(0, D, size=max(1, D // 50))] = np.nan
+    s[:, 0] = 5.0
+    sd = torch.from_numpy(s).to(dev())
+    ids, vals = M.msa_topk(sd, k)
+    work = sd.clone()
+    ids2, vals2 = M.msa_topk(work, k, reset=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(vals.view(torch.int32), vals2.view(torch.int32))
+    assert bool((work == float("-inf")).all())
+    mdc = int(np.diff(chunk_off).max())
+    max_ctx = k * mdc
+    row, pos, ln = M.msa_context_index(ids, co_d, n_chunks, mdc, max_ctx)
+    work = sd.clone()
+    ids3, vals3, row3, pos3, ln3 = M.msa_topk_context_index(work, k, co_d, n_chunks, mdc, max_ctx, reset=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids3) and torch.equal(vals.view(torch.int32), vals3.view(torch.int32))
+    assert torch.equal(ln, ln3)
+    for b in range(B):
+        n = int(ln[b])
+        assert torch.equal(row[b, :n], row3[b, :n]) and torch.equal(pos[b, :n], pos3[b, :n])
+    assert bool((work == float("-inf")).all())
+
+
+@pytest.mark.parametrize("bf16,layout,B,T", [(True, 1, 1, 64), (True, 0, 3, 16), (True, 1, 32, 1), (False, 0, 2, 5)])
+def test_route_prefilled_after_reset(bf16, layout, B, T):
+    """Route -> top-k with reset -> route with MSA_ROUTE_PREFILLED on the same
+    buffer, three layers in a row: every layer's scores, ids and values equal
+    those of the filling call bit for bit, and the buffer ends at -inf."""
+    H, d = 8, 128
+    lens = ragged_lengths(13, 700, 0, 900, n_empty=11)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    D, k = len(lens), 16
+    buf = torch.full((B, D), float("-inf"), dtype=torch.float32, device=dev())
+    for l in range(3):
+        st = O.round_to_store(O.l2_normalize(gen(31, l, synth.T_KR, (n_chunks, H, d), bf16).astype(np.float64)),
+                              "bf16" if bf16 else "f32")
+        st_d = to_dev(tile_np(st) if layout == 1 else st, bf16)
+        q = to_dev(gen(32, l, synth.T_QR, (B, T, H, d), bf16), bf16)
+        ref = M.msa_route_score(q, st_d, cd, D, layout=layout)
+        ids, vals = M.msa_topk(ref, k)
+        M.msa_route_score(q, st_d, cd, D, doc_score=buf, layout=layout, prefilled=True)
+        torch.cuda.synchronize()
+        assert torch.equal(buf.view(torch.int32), ref.view(torch.int32)), f"layer {l}"
+        ids2, vals2 = M.msa_topk(buf, k, reset=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids2) and torch.equal(vals.view(torch.int32), vals2.view(torch.int32))
+        assert bool((buf == float("-inf")).all())
+
+
 @pytest.mark.parametrize("B,k", [(3, 5), (1, 50), (4, 1)])
 def test_context_index(B, k):
     lens = ragged_lengths(7, 50, 0, 500, n_empty=3)
