@@ -343,6 +343,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void attn_decode_kernel(
 // while the current step is computed (two LDS buffers).
 
 constexpr int PF_WAVES = 8;
+constexpr int PF_BOTH = 3;   // part value of a one-launch split of both parts (split_base = context splits)
 constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_KS = 272;                         // bytes per key row of K_rot in LDS (256 + pad)
 constexpr int PF_K_BYTES = 32 * PF_KS;
@@ -418,11 +419,21 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
 
   // the keys of this launch: all, the local window only (the context is not
   // read, not even its length) or the context only
-  const int ctxl = part == MSA_ATTN_PART_LOCAL ? 0 : min(max(ctx_len[b], 0), max_ctx);
-  const int n_keys = part == MSA_ATTN_PART_CONTEXT ? ctxl : ctxl + L_loc;
-  // this query's keys split evenly over the n_splits workgroups (32-key steps)
-  const int kps = ((n_keys + n_splits - 1) / n_splits + 31) / 32 * 32;
-  const int j_begin = split * kps;
+  // PF_BOTH (one launch, both parts): the first split_base splits take the
+  // context keys and the others the local keys, each set split evenly, so the
+  // local splits start loading without waiting for the context's length
+  int kpart = part, ksplit = split, kn = n_splits;
+  if (part == PF_BOTH) {
+    const bool c = split < split_base;
+    kpart = c ? MSA_ATTN_PART_CONTEXT : MSA_ATTN_PART_LOCAL;
+    ksplit = c ? split : split - split_base;
+    kn = c ? split_base : n_splits - split_base;
+  }
+  const int ctxl = kpart == MSA_ATTN_PART_LOCAL ? 0 : min(max(ctx_len[b], 0), max_ctx);
+  const int n_keys = kpart == MSA_ATTN_PART_CONTEXT ? ctxl : ctxl + L_loc;
+  // this query's keys split evenly over the kn workgroups (32-key steps)
+  const int kps = ((n_keys + kn - 1) / kn + 31) / 32 * 32;
+  const int j_begin = ksplit * kps;
   const int j_end = min(n_keys, j_begin + kps);
 
   // cooperative mapping of one 32-key step
@@ -620,7 +631,8 @@ __global__ __launch_bounds__(PF_THREADS) void attn_prefill_kernel(
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (n_splits > 1 || part != 0) {
-      const int64_t rowid = ((int64_t(split_base + split) * B + b) * T + trow[i]) * Hq + hqrow[i];
+      const int pidx = part == PF_BOTH ? split : split_base + split;   // this workgroup's partial
+      const int64_t rowid = ((int64_t(pidx) * B + b) * T + trow[i]) * Hq + hqrow[i];
       store_partial(o[i], m_run[i], l, rok[i], g4, ws_o + rowid * AT_D, ws_ml + rowid);
       continue;
     }
@@ -883,6 +895,8 @@ struct AttnPlan {
   int n_rt;         // 16-row tiles per (b, g)
   int n_splits;     // partials in the workspace
   int n_sc, n_sl;   // msa_sparse_attn_part: context splits [0, n_sc), local splits [n_sc, n_splits)
+  int n_bc;         // one call, prefill: > 0 when the first n_bc of its splits take the context keys
+                    // and the others the local keys (PF_BOTH)
   size_t tab_bytes, o_bytes, ml_bytes;
 };
 
@@ -915,6 +929,11 @@ static AttnPlan attn_plan_splits(int dtype, int B, int T, int Hq, int Hkv, int d
   int64_t s = std::max<int64_t>(1, std::min<int64_t>(want, (n_keys_max + 63) / 64));
   if (max_ctx > cap) s = std::max<int64_t>(s, (n_keys_max + cap - 33) / (cap - 32));
   p.n_splits = int(s);
+  // A context no longer than one split's share of the keys (the 100M and 1M
+  // presets: 128 context rows beside 4,096 local tokens) gets a split of its
+  // own and the local keys the others, so that the local splits need not wait
+  // for the context's length before loading.
+  if (p.prefill && s >= 3 && int64_t(max_ctx) <= (n_keys_max + s - 1) / s) p.n_bc = 1;
   // the two-call form: each part fills the chip on its own (the local part
   // runs beside the context's fetch, the context part after it)
   int64_t sc = std::max<int64_t>(1, std::min<int64_t>(want, (int64_t(max_ctx) + 63) / 64));
@@ -1040,7 +1059,7 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
     }
     // this launch's splits and the index of its first partial
     const int n_launch = part == MSA_ATTN_PART_LOCAL ? p.n_sl : (part == MSA_ATTN_PART_CONTEXT ? p.n_sc : p.n_splits);
-    const int split_base = part == MSA_ATTN_PART_LOCAL ? p.n_sc : 0;
+    int split_base = part == MSA_ATTN_PART_LOCAL ? p.n_sc : 0;
     const int G = Hq / Hkv;
     const float scale_log2_pf = sm_scale * 1.4426950408889634f;
     if (p.prefill) {
@@ -1050,6 +1069,10 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
       const uint16_t* kk_src = static_cast<const uint16_t*>(pre ? prep->krot : k_ctx);
       const uint16_t* vv_src = static_cast<const uint16_t*>(pre ? prep->vg : v_ctx);
       const int km = pre ? prep->km : 0;
+      // one call over both parts in separate splits (the prepared keys keep one order)
+      const bool both = part == 0 && p.n_bc > 0 && !pre;
+      const int kpart = both ? PF_BOTH : part;
+      if (both) split_base = p.n_bc;
       const dim3 pgrid(unsigned(int64_t(B) * Hkv * p.n_rg * n_launch)), pblock(PF_THREADS);
       const size_t psmem = 2 * size_t(PF_BUF) + PF_CIDX_BYTES;
 #define PF_LAUNCH3(GV, RV, IV, PV)                                                                                  \
@@ -1058,7 +1081,7 @@ int sparse_attn(const std::string& fn, int dtype, const void* q, int B, int T, i
   hipLaunchKernelGGL((attn_prefill_kernel<GV, RV, IV, PV>), pgrid, pblock, psmem, s, static_cast<const uint16_t*>(q), B, \
                      T, Hq, Hkv, kk_src, vv_src, ctx_pos, ctx_len, max_ctx, static_cast<const uint16_t*>(k_loc),     \
                      static_cast<const uint16_t*>(v_loc), L_loc, q_pos_offset, ctx_row, ctx_rows, tab, p.P,          \
-                     scale_log2_pf, ws_o, ws_ml, n_launch, p.n_rt, p.n_rg, out, lse, part, split_base, km, pp)
+                     scale_log2_pf, ws_o, ws_ml, n_launch, p.n_rt, p.n_rg, out, lse, kpart, split_base, km, pp)
 #define PF_LAUNCH(GV, RV)                 \
   if (pre) {                              \
     PF_LAUNCH3(GV, RV, false, true);      \

@@ -697,6 +697,54 @@ def test_sparse_attention_two_calls(B, T, L_loc, ctx, indexed):
     print(f"two-call attention B={B} T={T} indexed={indexed}: against msa_sparse_attn {e_whole:.3g}")
 
 
+@pytest.mark.parametrize("Hq,B,T,L_loc,ctx", [
+    (32, 1, 64, 4096, [128]),        # the 100M- and 1M-token presets' shape
+    (32, 2, 64, 4096, [128, 0]),     # an empty context: its split sees no key
+    (32, 3, 32, 2048, [100, 37, 1]),  # contexts shorter than max_ctx
+    (16, 1, 16, 512, [40]),          # group of 2
+    (64, 2, 64, 1024, [64, 20]),     # group of 8
+])
+def test_sparse_attention_context_split(Hq, B, T, L_loc, ctx):
+    """Shapes whose context is no longer than one split's share of the keys:
+    the one-call attention gives the context a split of its own and the local
+    keys the others.  Against the oracle within the attention tolerance, the
+    in-place and gathered contexts bit for bit, and the two-call form within
+    the same tolerance."""
+    Hkv, d, qpo, n_rows = 8, 128, 16, 4000
+    max_ctx = max(ctx)
+    seed = 130 + T + Hq
+    q = gen(seed, 0, synth.T_Q, (B, T, Hq, d), True)
+    kl = gen(seed, 0, synth.T_KLOC, (B, L_loc, Hkv, d), True)
+    vl = gen(seed, 0, synth.T_VLOC, (B, L_loc, Hkv, d), True)
+    kst = gen(seed, 0, synth.T_K, (n_rows, Hkv, d), True, scale_pow2=-3)
+    vst = gen(seed, 0, synth.T_V, (n_rows, Hkv, d), True, scale_pow2=-3)
+    r = np.random.default_rng(seed)
+    rows = r.integers(0, n_rows, size=(B, max_ctx)).astype(np.int32)
+    cp = r.integers(0, min(128, max_ctx), size=(B, max_ctx)).astype(np.int32)
+    cl = np.asarray(ctx, dtype=np.int32)
+    d_rows, d_cp, d_cl = (torch.from_numpy(a).to(dev()) for a in (rows, cp, cl))
+    kst_d, vst_d = to_dev(kst, True), to_dev(vst, True)
+    qd, kld, vld = to_dev(q, True), to_dev(kl, True), to_dev(vl, True)
+    got = M.msa_sparse_attn_indexed(qd, kst_d, vst_d, d_rows, d_cp, d_cl, kld, vld, qpo)
+    kc_d, vc_d = kst_d[d_rows.long()].contiguous(), vst_d[d_rows.long()].contiguous()
+    gathered = M.msa_sparse_attn(qd, kc_d, vc_d, d_cp, d_cl, kld, vld, qpo)
+    assert torch.equal(got, gathered)
+    ws = torch.empty(M.msa_sparse_attn_part_workspace(M.MSA_BF16, B, T, Hq, Hkv, d, max_ctx, L_loc, qpo),
+                     dtype=torch.uint8, device=dev())
+    M.msa_sparse_attn_part(M.MSA_ATTN_PART_LOCAL, qd, kld, vld, qpo, max_ctx, ws=ws)
+    two = M.msa_sparse_attn_part(M.MSA_ATTN_PART_CONTEXT, qd, kld, vld, qpo, max_ctx, k_ctx=kc_d, v_ctx=vc_d,
+                                 ctx_pos=d_cp, ctx_len=d_cl, ws=ws)
+    g = host(got)
+    assert np.isfinite(g).all()
+    assert np.abs(g - host(two)).max() <= ATOL_ATTN["bf16"]
+    sm = 1.0 / math.sqrt(d)
+    for b in range(B):
+        n = int(cl[b])
+        ref = O.attend_one(q[b], kst[rows[b, :n]], vst[rows[b, :n]], cp[b, :n], kl[b], vl[b], qpo, 1e6, sm)
+        e = np.abs(g[b] - ref).max()
+        assert e <= ATOL_ATTN["bf16"], f"b={b}: max-abs {e}"
+
+
 def test_rope_table_values_and_reuse():
     rows, d, base = M.msa_rope_table_rows(2048, 8192, 16), 128, 1e6
     tab = M.msa_rope_table(rows, d, base, device=dev()).cpu().numpy().astype(np.float64)
