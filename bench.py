@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--no-fill-in-topk", action="store_true",
                     help="fill the score buffer with -inf in a launch of its own before every routing call (by "
                          "default each layer's top-k leaves it at -inf for the next layer's routing call)")
+    ap.add_argument("--no-fetch-in-route", action="store_true",
+                    help="on the host tier, fetch each layer's documents in a launch of their own after its top-k "
+                         "(by default the fetch runs in the next layer's routing scan, msa_route_score_fetch)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP graph replay; for counter collection)")
     ap.add_argument("--layers", type=int, default=None, help="override the routed-layer count (profiling only)")
@@ -120,7 +123,8 @@ def main():
 
     p = configs.PRESETS[args.config]()
     pb = PresetBench(torch, p, args.layers, rounds=args.rounds, graph=not args.no_graph,
-                     overlap=args.overlap, fill_in_topk=not args.no_fill_in_topk)
+                     overlap=args.overlap, fill_in_topk=not args.no_fill_in_topk,
+                     fetch_in_route=not args.no_fetch_in_route)
     pb.build_stores()
     pb.build_content("hbm")
     assembly = args.hbm_assembly if args.rounds == 1 else "index"
@@ -137,9 +141,12 @@ def main():
     if pinned is not None:
         kv, desc = pinned
         pb.make_runner("host", indexed=False, src_mode=pb.M.MSA_SRC_HOST_MAPPED)
+        host_pipelined = pb.pipelined
         res = pb.headline(args.steps, args.warmup, kv=kv,
                           tier=f"host-mapped ({desc['pinned_layers']} of {pb.layers} layers' K/V pinned, cycled)")
-        res["config"]["gather"] = "host-mapped gather kernel"
+        res["config"]["gather"] = ("host-mapped: each layer's documents fetched in the next layer's routing scan "
+                                   "(msa_route_score_fetch), the last layer's by the gather kernel"
+                                   if host_pipelined else "host-mapped gather kernel")
         res["hbm_tier"] = {k: hbm[k] for k in ("value", "ms_per_step", "route_attn_us_per_query",
                                               "ms_per_step_eager_launches", "ms_per_step_graph_replay",
                                               "stage_ms_per_step", "attention_GBps")}
@@ -156,7 +163,8 @@ def main():
         res["host_tier"] = pb.host_tier(args.steps, args.warmup, pinned, modes=("memcpy",))
         res["host_tier"]["mapped"] = {"route_attn_us_per_query": res["route_attn_us_per_query"],
                                       "ms_per_step": res["ms_per_step"],
-                                      "fetch_ms_per_step": res["stage_ms_per_step"].get("fetch"),
+                                      "fetch_ms_per_step": res["stage_ms_per_step"].get(
+                                          "fetch_last_layer" if host_pipelined else "fetch"),
                                       "note": "the line's own step"}
         pb.unpin_host()
     pb.release()
@@ -171,7 +179,8 @@ class PresetBench:
     """One workload preset on the device: its stores (built by the offline
     stage before any timing), a LayerRunner and the whole-path step."""
 
-    def __init__(self, torch, p, layers=None, rounds=1, graph=True, overlap=False, fill_in_topk=True):
+    def __init__(self, torch, p, layers=None, rounds=1, graph=True, overlap=False, fill_in_topk=True,
+                 fetch_in_route=True):
         import synth
         from synth import device as SD
         import sparse_attention_long_msa_amd as M
@@ -181,6 +190,8 @@ class PresetBench:
         self.graph = graph
         self.overlap = overlap
         self.fill_in_topk = fill_in_topk and rounds == 1
+        self.fetch_in_route = fetch_in_route and rounds == 1
+        self.pipelined = False   # the current runner's step fetches layer l in layer l + 1's routing scan
         self.dev = torch.device("cuda:0")
         torch.cuda.set_device(self.dev)
         self.bf = torch.bfloat16 if p.bf16 else torch.float32
@@ -278,57 +289,88 @@ class PresetBench:
                                     src_mode=M.MSA_SRC_DEVICE if src_mode is None else src_mode,
                                     chunk_off_h=p.chunk_off, kr_layout=self.kr_layout, indexed=indexed,
                                     rounds=self.rounds, overlap_local=overlap, fill_in_topk=self.fill_in_topk)
+        # a fetched context from mapped host memory: each layer's fetch runs in the next layer's routing scan
+        self.pipelined = (self.fetch_in_route and not indexed and not overlap
+                          and src_mode == M.MSA_SRC_HOST_MAPPED)
         return self.runner
 
-    def step(self, ev=None, route_ev=None, route_layer=-1, kv=None, flush=None):
-        """One pass of the whole path over all routed layers.  ev: per-stage
-        events of every layer; route_ev: events around the routing-score call
-        of layer route_layer only (the timed steps); kv(l): the layer's
-        content stores (default: its own, in HBM); flush(): run before each
-        layer (cold-cache timing)."""
+    def step(self, mark=None, route_ev=None, route_layer=-1, kv=None, flush=None):
+        """One pass of the whole path over all routed layers.  mark(stage):
+        called after each call of the step, stage 0 routing, 1 top-k (and the
+        context index), 2 context assembly, 3 attention, and mark(None) where
+        a stretch that belongs to no stage ends (stage timing); route_ev:
+        events around the routing-score call of layer route_layer only (the
+        timed steps); kv(l): the layer's content stores (default: its own, in
+        HBM); flush(): run before each layer (cold-cache timing)."""
         runner, stream = self.runner, self.torch.cuda.current_stream()
 
-        def rec(e):
-            if e is not None:
-                e.record(stream)
+        def done(stage):
+            if mark is not None:
+                mark(stage)
+
+        def route(l, fn):
+            if l == route_layer:
+                route_ev[0].record(stream)
+            fn()
+            if l == route_layer:
+                route_ev[1].record(stream)
+            done(0)
+
+        def kv_of(l):
+            return (self.kbar[l], self.vbar[l]) if kv is None else kv(l)
+        if self.pipelined:
+            # layer l's context is fetched in layer l + 1's routing scan (LayerRunner.run_layers' order)
+            for l in range(-1, self.layers):
+                if flush is not None:
+                    flush()
+                    done(None)
+                if l + 1 < self.layers:
+                    nl = l + 1
+                    if l < 0:
+                        route(nl, lambda: runner.route(self.qr[nl], self.store[nl], self.cd))
+                    else:
+                        kb, vb = kv_of(l)
+                        route(nl, lambda: runner.route_fetch(self.qr[nl], self.store[nl], self.cd, self.co_d, kb, vb))
+                else:
+                    kb, vb = kv_of(l)
+                    runner.assemble(self.co_d, kb, vb)
+                    done(2)
+                if l >= 0:
+                    runner.attend(self.qq[l], self.kl[l], self.vl[l])
+                    done(3)
+                if l + 1 < self.layers:
+                    runner.select()
+                    done(1)
+            return
         for l in range(self.layers):
-            kb, vb = (self.kbar[l], self.vbar[l]) if kv is None else kv(l)
+            kb, vb = kv_of(l)
             if flush is not None:
                 flush()
-            e = ev[l] if ev is not None else [None] * 5
-            rec(e[0])
+                done(None)
             if self.rounds > 1:
                 runner.fetch_rounds(self.qr_rounds[l], self.store[l], self.cd, self.co_d, kb, vb,
                                     route_events=route_ev if l == route_layer else None)
-                rec(e[1])
-                rec(e[2])
-                rec(e[3])
+                done(0)
                 runner.attend(self.qq[l], self.kl[l], self.vl[l])
-                rec(e[4])
+                done(3)
                 continue
-            if l == route_layer:
-                rec(route_ev[0])
-            runner.route(self.qr[l], self.store[l], self.cd)
-            if l == route_layer:
-                rec(route_ev[1])
-            rec(e[1])
+            route(l, lambda: runner.route(self.qr[l], self.store[l], self.cd))
             if runner.indexed:
                 # top-k and the context index in one call (the final selection pass writes the index)
                 runner.select_assemble(self.co_d, kb, vb)
-                rec(e[2])
-                rec(e[3])
+                done(1)
                 if runner.overlap_local:
                     runner.start_local(self.qq[l], self.kl[l], self.vl[l])
             else:
                 runner.select()
-                rec(e[2])
+                done(1)
                 if runner.overlap_local:
                     # the local-window half of the attention, beside the fetch
                     runner.start_local(self.qq[l], self.kl[l], self.vl[l])
                 runner.assemble(self.co_d, kb, vb)
-                rec(e[3])
+                done(2)
             runner.attend(self.qq[l], self.kl[l], self.vl[l])
-            rec(e[4])
+            done(3)
 
     def needle_recall(self):
         """Planted-needle recall of layer 0 on one pass (a property of the data, not timed)."""
@@ -386,18 +428,26 @@ class PresetBench:
 
     def stages(self, n_steps, kv=None, flush=None):
         """Per-stage ms per step: (route, top-k, assembly, attention), from
-        extra steps with events between all stages."""
+        extra steps with one event after every call (each stage is the time
+        from the previous event)."""
         torch = self.torch
-        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(self.layers)]
-               for _ in range(n_steps)]
+        stream = torch.cuda.current_stream()
+        spans, last = [], [None]
+
+        def mark(stage):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            if stage is not None and last[0] is not None:
+                spans.append((stage, last[0], e))
+            last[0] = e
         for s in range(n_steps):
-            self.step(evs[s], kv=kv, flush=flush)
+            last[0] = None
+            mark(None)
+            self.step(mark, kv=kv, flush=flush)
         torch.cuda.synchronize()
         stage = np.zeros(4)
-        for s in range(n_steps):
-            for l in range(self.layers):
-                e = evs[s][l]
-                stage += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
+        for st, a, b in spans:
+            stage[st] += a.elapsed_time(b)
         return stage / n_steps
 
     def attn_bytes(self):
@@ -435,10 +485,17 @@ class PresetBench:
                     f"{layers} routed layers, H={H}, d={d}; {p.B} quer{'y' if p.B == 1 else 'ies'} x T={p.T}, "
                     f"Hq={p.Hq}, L_loc={p.L_loc}, k={p.k}")
         if self.rounds == 1:
-            stages = ({"route_score": round(stage[0], 4), "topk_and_context_index": round(stage[1], 4),
-                       "attention": round(stage[3], 4)} if self.runner.indexed else
-                      {"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
-                       ("fetch" if kv is not None else "gather"): round(stage[2], 4), "attention": round(stage[3], 4)})
+            if self.runner.indexed:
+                stages = {"route_score": round(stage[0], 4), "topk_and_context_index": round(stage[1], 4),
+                          "attention": round(stage[3], 4)}
+            elif self.pipelined:
+                # the fetch of layers 0 .. L-2 runs inside the next layer's routing call
+                stages = {"route_score_and_previous_fetch": round(stage[0], 4), "topk": round(stage[1], 4),
+                          "fetch_last_layer": round(stage[2], 4), "attention": round(stage[3], 4)}
+            else:
+                stages = {"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
+                          ("fetch" if kv is not None else "gather"): round(stage[2], 4),
+                          "attention": round(stage[3], 4)}
         else:
             stages = {"rounds_route_topk_append": round(stage[0] + stage[1] + stage[2], 4),
                       "attention": round(stage[3], 4)}

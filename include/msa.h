@@ -249,6 +249,38 @@ int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, cons
                     void* ws, size_t ws_bytes, int flags, void* stream);
 
 /*
+ * msa_route_score_fetch - msa_route_score of one layer, with the context
+ * assembly of another layer done inside the same launch (README, Overall
+ * Design > Inference Pipeline: the content K/V stays in host memory and the
+ * selected documents are fetched asynchronously; here the fetch of layer l's
+ * selection hides behind layer l+1's routing scan).  The scan's workgroups
+ * that finish their chunk ranges first copy the selected documents, one
+ * (query, rank) at a time, while the others still stream: the host link and
+ * the HBM scan overlap.  Results are exactly those of msa_route_score
+ * followed by msa_gather_kv in MSA_SRC_DEVICE / MSA_SRC_HOST_MAPPED mode.
+ *   routing arguments and flags as msa_route_score
+ *   f_ids       [f_B, f_k] int32: the other layer's selection (msa_topk)
+ *   f_chunk_off [f_n_docs + 1] int64 (device) of that layer's documents
+ *   f_k_bar, f_v_bar [n, f_Hkv, f_d] dtype: its content store, in device
+ *               memory or in pinned host memory the GPU can map
+ *   f_max_ctx, f_k_ctx, f_v_ctx [f_B, f_max_ctx, f_Hkv, f_d], f_ctx_pos
+ *               [f_B, f_max_ctx], f_ctx_len [f_B]: as msa_gather_kv's outputs
+ *   ws          msa_route_score_fetch_workspace() bytes: the routing
+ *               workspace, then 256 bytes for the fetch's counter (no
+ *               initial contents needed; the launch clears it)
+ * The fetch's outputs must not be read by anything running beside the call.
+ * Off the MFMA path the two calls run one after the other.
+ * Errors: those of msa_route_score and msa_gather_kv; WORKSPACE.
+ */
+size_t msa_route_score_fetch_workspace(int dtype, int B, int T, int H, int d, int64_t n_docs, int64_t n_chunks);
+int msa_route_score_fetch(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat, int kr_layout,
+                          const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks, float* doc_score, void* ws,
+                          size_t ws_bytes, int flags, const int32_t* f_ids, int f_B, int f_k,
+                          const int64_t* f_chunk_off, int64_t f_n_docs, int f_max_doc_chunks, const void* f_k_bar,
+                          const void* f_v_bar, int f_Hkv, int f_d, int f_max_ctx, void* f_k_ctx, void* f_v_ctx,
+                          int32_t* f_ctx_pos, int32_t* f_ctx_len, void* stream);
+
+/*
  * msa_route_balance - sizes msa_route_score's chunk ranges per XCD on the
  * current device (not a step of the method: a calibration of how the scan is
  * spread over MI355X's eight XCDs).  Workgroup b of the scan runs on XCD

@@ -37,6 +37,9 @@ _SIGS = {
     "msa_pool_encode": (_I, [_I, _P, _P, _P, _P, _L, _L, _L, _I, _I, _I, _I, _I, _P, _P]),
     "msa_route_score_workspace": (_S, [_I, _I, _I, _I, _I, _L, _L]),
     "msa_route_score": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P, _P, _S, _I, _P]),
+    "msa_route_score_fetch_workspace": (_S, [_I, _I, _I, _I, _I, _L, _L]),
+    "msa_route_score_fetch": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P, _P, _S, _I,
+                                   _P, _I, _I, _P, _L, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
     "msa_route_balance": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P, _P, _S, _I, _P, _P]),
     "msa_chunk_scores": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, _L, _P, _P, _S, _P]),
     "msa_segment_max": (_I, [_P, _I, _L, _P, _L, _P, _P]),
@@ -276,6 +279,50 @@ def msa_route_score(q_r, kr_hat, chunk_doc, n_docs, doc_score=None, ws=None, lay
     _check("msa_route_score", lib.msa_route_score(
         dt, _ptr(q_r), B, T, H, d, _ptr(kr_hat), layout, _ptr(chunk_doc), n_docs, n_chunks, _ptr(doc_score),
         _ptr(ws), wsb, MSA_ROUTE_PREFILLED if prefilled else 0, _stream(stream)))
+    return doc_score
+
+
+def msa_route_score_fetch(q_r, kr_hat, chunk_doc, n_docs, f_ids, f_chunk_off, f_k_bar, f_v_bar, f_max_doc_chunks,
+                          k_ctx, v_ctx, ctx_pos, ctx_len, doc_score=None, ws=None, layout=MSA_LAYOUT_ROWS,
+                          stream=None, prefilled=False):
+    """msa_route_score of this layer, and in the scan's tail the fetch that
+    msa_gather_kv makes of another layer's selection f_ids [B', k] from its
+    content store f_k_bar / f_v_bar [n, Hkv, d] (device or pinned host memory)
+    into k_ctx / v_ctx [B', max_ctx, Hkv, d], ctx_pos, ctx_len."""
+    if prefilled and doc_score is None:
+        raise ValueError("prefilled needs the doc_score buffer that holds -inf")
+    _dev(q_r, "q_r", _FLOAT, (None, None, None, None))
+    B, T, H, d = q_r.shape
+    _dev(chunk_doc, "chunk_doc", _I32, (None,))
+    n_chunks = chunk_doc.numel()
+    _dev(kr_hat, "kr_hat", q_r.dtype, (None, H, d))
+    if kr_hat.shape[0] < padded_chunks(n_chunks, layout):
+        raise ValueError("kr_hat holds fewer chunks than chunk_doc names")
+    dt = _dtype(q_r)
+    if doc_score is None:
+        doc_score = torch.empty((B, n_docs), dtype=torch.float32, device=q_r.device)
+    _dev(doc_score, "doc_score", _F32, (B, n_docs))
+    _dev(f_ids, "f_ids", _I32, (None, None))
+    fB, fk = f_ids.shape
+    _dev(f_chunk_off, "f_chunk_off", _I64, (None,))
+    if not isinstance(f_k_bar, torch.Tensor) or f_k_bar.dim() != 3:
+        _fail("f_k_bar", "expected a [n_chunks, Hkv, d] tensor")
+    n_src, Hkv, fd = f_k_bar.shape
+    src = _dev if f_k_bar.is_cuda else _pinned
+    src(f_k_bar, "f_k_bar", q_r.dtype, (n_src, Hkv, fd))
+    src(f_v_bar, "f_v_bar", q_r.dtype, (n_src, Hkv, fd))
+    _dev(k_ctx, "k_ctx", q_r.dtype, (fB, None, Hkv, fd))
+    max_ctx = k_ctx.shape[1]
+    _dev(v_ctx, "v_ctx", q_r.dtype, (fB, max_ctx, Hkv, fd))
+    _dev(ctx_pos, "ctx_pos", _I32, (fB, max_ctx))
+    _dev(ctx_len, "ctx_len", _I32, (fB,))
+    _dev(ws, "ws", optional=True)
+    ws, wsb = _ws(lib.msa_route_score_fetch_workspace(dt, B, T, H, d, n_docs, n_chunks), q_r.device, ws)
+    _check("msa_route_score_fetch", lib.msa_route_score_fetch(
+        dt, _ptr(q_r), B, T, H, d, _ptr(kr_hat), layout, _ptr(chunk_doc), n_docs, n_chunks, _ptr(doc_score),
+        _ptr(ws), wsb, MSA_ROUTE_PREFILLED if prefilled else 0, _ptr(f_ids), fB, fk, _ptr(f_chunk_off),
+        f_chunk_off.numel() - 1, f_max_doc_chunks, _ptr(f_k_bar), _ptr(f_v_bar), Hkv, fd, max_ctx, _ptr(k_ctx),
+        _ptr(v_ctx), _ptr(ctx_pos), _ptr(ctx_len), _stream(stream)))
     return doc_score
 
 

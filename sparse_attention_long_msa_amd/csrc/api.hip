@@ -29,7 +29,7 @@ __global__ void chunk_doc_kernel(const int64_t* __restrict__ chunk_off, int64_t 
 
 extern "C" {
 
-int msa_abi_version(void) { return 13; }
+int msa_abi_version(void) { return 14; }
 
 const char* msa_status_string(int status) {
   switch (status) {

@@ -103,6 +103,11 @@ template <> struct Elem<MSA_BF16> {
 };
 
 inline int dtype_bytes(int dt) { return dt == MSA_F32 ? 4 : 2; }
+
+// msa_gather_kv's copy from any GPU-readable source (gather.hip)
+int gather_copy(const int32_t* ids, int B, int k, const int64_t* chunk_off, int64_t n_docs, const void* k_bar,
+                const void* v_bar, int64_t row_vec, int max_ctx, void* k_ctx, void* v_ctx, int32_t* ctx_pos,
+                int32_t* ctx_len, hipStream_t s);
 inline bool dtype_ok(int dt) { return dt == MSA_F32 || dt == MSA_BF16; }
 
 }  // namespace msa

@@ -101,6 +101,18 @@ __global__ __launch_bounds__(GK_THREADS) void gather_kernel(const int32_t* __res
   }
 }
 
+// the device-side copy (any GPU-readable source): shared with msa_route_score_fetch's fallback
+int gather_copy(const int32_t* ids, int B, int k, const int64_t* chunk_off, int64_t n_docs, const void* k_bar,
+                const void* v_bar, int64_t row_vec, int max_ctx, void* k_ctx, void* v_ctx, int32_t* ctx_pos,
+                int32_t* ctx_len, hipStream_t s) {
+  const dim3 grid{unsigned(k), unsigned(B)}, block{GK_THREADS};
+  hipLaunchKernelGGL(gather_kernel<GK_COPY>, grid, block, 0, s, ids, k, chunk_off, n_docs,
+                     static_cast<const uint4*>(k_bar), static_cast<const uint4*>(v_bar), row_vec, max_ctx,
+                     static_cast<uint4*>(k_ctx), static_cast<uint4*>(v_ctx), ctx_pos, ctx_len, nullptr, nullptr);
+  MSA_LAUNCH_CHECK();
+  return MSA_OK;
+}
+
 struct CopyEvent {
   hipEvent_t ev = nullptr;
   ~CopyEvent() {
@@ -135,13 +147,8 @@ extern "C" int msa_gather_kv(int dtype, const int32_t* ids, int B, int k, const 
   const int64_t row_vec = row_bytes / 16;
   hipStream_t s = as_stream(stream);
   const dim3 grid{unsigned(k), unsigned(B)}, block{GK_THREADS};
-  if (src_mode != MSA_SRC_HOST_MEMCPY) {
-    hipLaunchKernelGGL(gather_kernel<GK_COPY>, grid, block, 0, s, ids, k, chunk_off, n_docs,
-                       static_cast<const uint4*>(k_bar), static_cast<const uint4*>(v_bar), row_vec, max_ctx,
-                       static_cast<uint4*>(k_ctx), static_cast<uint4*>(v_ctx), ctx_pos, ctx_len, nullptr, nullptr);
-    MSA_LAUNCH_CHECK();
-    return MSA_OK;
-  }
+  if (src_mode != MSA_SRC_HOST_MEMCPY)
+    return gather_copy(ids, B, k, chunk_off, n_docs, k_bar, v_bar, row_vec, max_ctx, k_ctx, v_ctx, ctx_pos, ctx_len, s);
   // host copies: the selection must be known on the host
   MSA_REQUIRE(chunk_off_h && ids_h, MSA_ERR_INVALID_ARG, "msa_gather_kv: host mode needs chunk_off_h and ids_h");
   hipStream_t cs = copy_stream ? as_stream(copy_stream) : s;

@@ -91,6 +91,91 @@ __device__ __forceinline__ void lds_max_float(float* addr, float v) {
     atomicMin(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
 }
 
+// A fetch done in the launch's tail (msa_route_score_fetch): the workgroups
+// that finish their chunk ranges first copy the documents another layer
+// selected (its pooled K / V rows, in device memory or mapped pinned host
+// memory) into that layer's context, one (query, rank) at a time, taken from
+// a counter.  The copy is the one msa_gather_kv makes: rank r of query b lands
+// at the sum of the chunk counts of ranks < r, never past max_ctx.
+struct TailFetch {
+  unsigned* counter;          // NULL: no fetch
+  const int32_t* ids;         // [B, k]
+  int B, k;
+  const int64_t* chunk_off;   // [n_docs + 1]
+  int64_t n_docs;
+  const uint4* k_bar;         // pooled rows of row_vec 16-byte vectors
+  const uint4* v_bar;
+  int64_t row_vec;
+  int max_ctx;
+  uint4* k_ctx;               // [B, max_ctx] rows
+  uint4* v_ctx;
+  int32_t* ctx_pos;           // [B, max_ctx]
+  int32_t* ctx_len;           // [B]
+};
+
+// The whole workgroup takes (query, rank) items until the counter passes the
+// last one.  lds: 16 bytes of LDS no longer in use.  Every item is a plain
+// copy of the same bytes to the same place, so an item taken twice (a counter
+// that workgroup 0 clears late, at its start) changes nothing.
+__device__ void tail_fetch(const TailFetch& tf, unsigned* lds) {
+  if (!tf.counter) return;
+  const unsigned n_items = unsigned(tf.B) * unsigned(tf.k);
+  for (;;) {
+    __syncthreads();   // the LDS words are free
+    if (threadIdx.x == 0) lds[0] = atomicAdd(tf.counter, 1u);
+    __syncthreads();
+    const unsigned item = lds[0];
+    if (item >= n_items) return;
+    const int b = int(item / unsigned(tf.k)), r = int(item % unsigned(tf.k));
+    const int32_t* ids_b = tf.ids + int64_t(b) * tf.k;
+    if (threadIdx.x < 64) {   // dest: the chunk counts of ranks < r (at most max_ctx in all)
+      int mine = 0;
+      for (int q = threadIdx.x; q < r; q += 64) {
+        const int32_t doc = ids_b[q];
+        if (doc >= 0 && doc < tf.n_docs) mine += int(tf.chunk_off[doc + 1] - tf.chunk_off[doc]);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o);
+      if (threadIdx.x == 0) lds[1] = unsigned(mine);
+    }
+    __syncthreads();
+    const int64_t dest = int64_t(lds[1]);
+    const int32_t doc = ids_b[r];
+    int64_t lo = 0, n = 0;
+    if (doc >= 0 && doc < tf.n_docs) {
+      lo = tf.chunk_off[doc];
+      n = tf.chunk_off[doc + 1] - lo;
+    }
+    if (dest + n > tf.max_ctx) n = dest < tf.max_ctx ? tf.max_ctx - dest : 0;   // never past the context
+    if (r == tf.k - 1 && threadIdx.x == 0) tf.ctx_len[b] = int32_t(dest + n);
+    for (int64_t i = threadIdx.x; i < n; i += RS_THREADS) tf.ctx_pos[int64_t(b) * tf.max_ctx + dest + i] = int32_t(i);
+    const int64_t total = n * tf.row_vec;
+    const uint4* ks = tf.k_bar + lo * tf.row_vec;
+    const uint4* vs = tf.v_bar + lo * tf.row_vec;
+    uint4* kd = tf.k_ctx + (int64_t(b) * tf.max_ctx + dest) * tf.row_vec;
+    uint4* vd = tf.v_ctx + (int64_t(b) * tf.max_ctx + dest) * tf.row_vec;
+    constexpr int U = 4;   // four 16-byte loads of K and of V in flight per thread
+    int64_t i = threadIdx.x;
+    for (; i + (U - 1) * RS_THREADS < total; i += U * RS_THREADS) {
+      uint4 a[U], c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        a[u] = ks[i + u * RS_THREADS];
+        c[u] = vs[i + u * RS_THREADS];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kd[i + u * RS_THREADS] = a[u];
+        vd[i + u * RS_THREADS] = c[u];
+      }
+    }
+    for (; i < total; i += RS_THREADS) {
+      kd[i] = ks[i];
+      vd[i] = vs[i];
+    }
+  }
+}
+
 // NT: 16-column tiles per column group (<= 4); UNIFORM_B: every 16-column
 // tile belongs to one query (T % 16 == 0), so the token max is taken in
 // registers before the document max.
@@ -107,7 +192,8 @@ template <int NT, bool UNIFORM_B, bool TILED, int D>
 __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     const uint16_t* __restrict__ q_r, int T, int J, const uint16_t* __restrict__ kr,
     const int32_t* __restrict__ chunk_doc, int64_t n_docs, int64_t n_chunks, float* __restrict__ doc_score,
-    int n_groups, int n_ranges, int64_t tiles_per_range, int tab_cap, XcdSplit xs, uint64_t* __restrict__ wg_ts) {
+    int n_groups, int n_ranges, int64_t tiles_per_range, int tab_cap, XcdSplit xs, uint64_t* __restrict__ wg_ts,
+    TailFetch tf) {
   constexpr int H = RS_H;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint4* qfrag = reinterpret_cast<uint4*>(smem);  // [NT][H][KK][64 lanes] x 16 B
@@ -125,7 +211,11 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     group = slot % n_groups;
     range = (slot / n_groups) * 8 + xcd;
   }
-  if (range >= n_ranges) return;
+  if (tf.counter && blockIdx.x == 0 && threadIdx.x == 0) atomicExch(tf.counter, 0u);   // the tail fetch's counter
+  if (range >= n_ranges) {
+    tail_fetch(tf, reinterpret_cast<unsigned*>(smem));
+    return;
+  }
   // per-workgroup start and end stamps (the 100 MHz real-time counter), for msa_route_balance
   if (wg_ts && threadIdx.x == 0) wg_ts[2 * blockIdx.x] = __builtin_amdgcn_s_memrealtime();
   const int col0 = group * 64;
@@ -152,6 +242,7 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
   if (t_end > tiles_total) t_end = tiles_total;
   if (t_begin >= t_end) {                   // a range past the last tile (whole workgroup)
     if (wg_ts && threadIdx.x == 0) wg_ts[2 * blockIdx.x + 1] = wg_ts[2 * blockIdx.x];
+    tail_fetch(tf, reinterpret_cast<unsigned*>(smem));
     return;
   }
   const int64_t rowE = int64_t(H) * RS_D;  // elements per chunk
@@ -397,6 +488,7 @@ __global__ __launch_bounds__(RS_THREADS) void route_score_mfma_kernel(
     __syncthreads();
     if (threadIdx.x == 0) wg_ts[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
   }
+  tail_fetch(tf, reinterpret_cast<unsigned*>(smem));   // the query fragments are no longer read
 }
 
 // Vector path: float32 (or any head size).  The query is first scaled per
@@ -571,7 +663,7 @@ static int route_score(const std::string& fn, int dtype, const void* q_r, int B,
                        const void* kr_hat, int kr_layout, const int32_t* chunk_doc, int64_t n_docs,
                        int64_t n_chunks, float* doc_score, void* ws, size_t ws_bytes, void* stream,
                        const float* shares = nullptr, uint64_t* wg_ts = nullptr, bool* split_used = nullptr,
-                       int* n_wg = nullptr, bool prefilled = false) {
+                       int* n_wg = nullptr, bool prefilled = false, const TailFetch* fetch = nullptr) {
   if (split_used) *split_used = false;
   using namespace msa;
   MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
@@ -638,13 +730,14 @@ static int route_score(const std::string& fn, int dtype, const void* q_r, int B,
     const int tab_cap = int(std::min<int64_t>(8192, std::max<int64_t>(0, (int64_t(lds_max) - int64_t(smem_base)) / 4)));
     const size_t smem = smem_base + size_t(tab_cap) * 4;
     const dim3 grid(unsigned(n_ranges * n_groups)), block(RS_THREADS);
+    const TailFetch tfv = fetch ? *fetch : TailFetch{};
 #define RS_LAUNCH3(NTV, UNI, TIL, DV)                                                                    \
   MSA_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&route_score_mfma_kernel<NTV, UNI, TIL, DV>), \
                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)));           \
   hipLaunchKernelGGL((route_score_mfma_kernel<NTV, UNI, TIL, DV>), grid, block, smem, s,               \
                      static_cast<const uint16_t*>(q_r), T, J, static_cast<const uint16_t*>(kr_hat),     \
                      chunk_doc, n_docs, n_chunks, doc_score, n_groups, int(n_ranges), tiles_per_range, tab_cap, \
-                     xs, wg_ts)
+                     xs, wg_ts, tfv)
 // Tiled stores stream one 16-chunk group per wave, a head at a time: one head
 // in flight per wave reads each group strictly in order and measured best
 // with one column group; column groups sharing a range (their second read
@@ -729,6 +822,66 @@ extern "C" int msa_route_score(int dtype, const void* q_r, int B, int T, int H, 
   return msa::route_score("msa_route_score", dtype, q_r, B, T, H, d, kr_hat, kr_layout, chunk_doc, n_docs, n_chunks,
                           doc_score, ws, ws_bytes, stream, nullptr, nullptr, nullptr, nullptr,
                           (flags & MSA_ROUTE_PREFILLED) != 0);
+}
+
+extern "C" size_t msa_route_score_fetch_workspace(int dtype, int B, int T, int H, int d, int64_t n_docs,
+                                                  int64_t n_chunks) {
+  return msa::align_up(msa_route_score_workspace(dtype, B, T, H, d, n_docs, n_chunks), 256) + 256;
+}
+
+extern "C" int msa_route_score_fetch(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,
+                                     int kr_layout, const int32_t* chunk_doc, int64_t n_docs, int64_t n_chunks,
+                                     float* doc_score, void* ws, size_t ws_bytes, int flags, const int32_t* f_ids,
+                                     int f_B, int f_k, const int64_t* f_chunk_off, int64_t f_n_docs,
+                                     int f_max_doc_chunks, const void* f_k_bar, const void* f_v_bar, int f_Hkv,
+                                     int f_d, int f_max_ctx, void* f_k_ctx, void* f_v_ctx, int32_t* f_ctx_pos,
+                                     int32_t* f_ctx_len, void* stream) {
+  using namespace msa;
+  const std::string fn = "msa_route_score_fetch";
+  MSA_REQUIRE(chunk_doc, MSA_ERR_INVALID_ARG, fn + ": NULL pointer");
+  MSA_REQUIRE((flags & ~MSA_ROUTE_PREFILLED) == 0, MSA_ERR_INVALID_ARG, fn + ": unknown flags");
+  MSA_REQUIRE(dtype_ok(dtype), MSA_ERR_INVALID_ARG, fn + ": bad dtype");
+  MSA_REQUIRE(f_ids && f_chunk_off && f_k_bar && f_v_bar && f_k_ctx && f_v_ctx && f_ctx_pos && f_ctx_len,
+              MSA_ERR_INVALID_ARG, fn + ": NULL fetch pointer");
+  MSA_REQUIRE(f_B >= 1 && f_k >= 1 && f_n_docs >= 1 && f_max_doc_chunks >= 1 && f_Hkv >= 1 && f_d >= 1,
+              MSA_ERR_INVALID_ARG, fn + ": non-positive fetch size");
+  MSA_REQUIRE(f_k <= f_n_docs, MSA_ERR_INVALID_ARG, fn + ": f_k > f_n_docs");
+  MSA_REQUIRE(int64_t(f_max_ctx) >= int64_t(f_k) * f_max_doc_chunks, MSA_ERR_INVALID_ARG,
+              fn + ": f_max_ctx < f_k * f_max_doc_chunks");
+  MSA_REQUIRE(f_B <= 65535 && f_k <= 65535, MSA_ERR_UNSUPPORTED, fn + ": f_B or f_k too large");
+  const int64_t row_bytes = int64_t(f_Hkv) * f_d * dtype_bytes(dtype);
+  MSA_REQUIRE(row_bytes % 16 == 0, MSA_ERR_UNSUPPORTED, fn + ": f_Hkv*f_d*elem_bytes must be a multiple of 16");
+  MSA_REQUIRE(uintptr_t(f_k_bar) % 16 == 0 && uintptr_t(f_v_bar) % 16 == 0 && uintptr_t(f_k_ctx) % 16 == 0 &&
+                  uintptr_t(f_v_ctx) % 16 == 0,
+              MSA_ERR_INVALID_ARG, fn + ": fetch K/V buffers must be 16-byte aligned");
+  const size_t rws = msa_route_score_workspace(dtype, B, T, H, d, n_docs, n_chunks);
+  MSA_REQUIRE(ws_bytes >= align_up(rws, 256) + 256, MSA_ERR_WORKSPACE, fn + ": workspace too small");
+  MSA_REQUIRE(ws, MSA_ERR_INVALID_ARG, fn + ": NULL workspace");
+  const bool prefilled = (flags & MSA_ROUTE_PREFILLED) != 0;
+  if (!use_mfma(dtype, H, d)) {   // the vector scan has no tail to spare: the two calls in order
+    const int rc = route_score(fn, dtype, q_r, B, T, H, d, kr_hat, kr_layout, chunk_doc, n_docs, n_chunks, doc_score,
+                               ws, rws, stream, nullptr, nullptr, nullptr, nullptr, prefilled);
+    if (rc != MSA_OK) return rc;
+    return gather_copy(f_ids, f_B, f_k, f_chunk_off, f_n_docs, f_k_bar, f_v_bar, row_bytes / 16, f_max_ctx, f_k_ctx,
+                       f_v_ctx, f_ctx_pos, f_ctx_len, as_stream(stream));
+  }
+  TailFetch tf{};
+  tf.counter = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + align_up(rws, 256));
+  tf.ids = f_ids;
+  tf.B = f_B;
+  tf.k = f_k;
+  tf.chunk_off = f_chunk_off;
+  tf.n_docs = f_n_docs;
+  tf.k_bar = static_cast<const uint4*>(f_k_bar);
+  tf.v_bar = static_cast<const uint4*>(f_v_bar);
+  tf.row_vec = row_bytes / 16;
+  tf.max_ctx = f_max_ctx;
+  tf.k_ctx = static_cast<uint4*>(f_k_ctx);
+  tf.v_ctx = static_cast<uint4*>(f_v_ctx);
+  tf.ctx_pos = f_ctx_pos;
+  tf.ctx_len = f_ctx_len;
+  return route_score(fn, dtype, q_r, B, T, H, d, kr_hat, kr_layout, chunk_doc, n_docs, n_chunks, doc_score, ws, rws,
+                     stream, nullptr, nullptr, nullptr, nullptr, prefilled, &tf);
 }
 
 extern "C" int msa_chunk_scores(int dtype, const void* q_r, int B, int T, int H, int d, const void* kr_hat,

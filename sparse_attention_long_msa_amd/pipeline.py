@@ -87,6 +87,9 @@ class LayerRunner:
             return torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
 
         self.rs_ws = ws(B.msa_route_score_workspace(dt, batch, tokens, kv_heads, head_dim, n_docs, n_chunks))
+        # route_fetch's workspace: the routing one and the fetch's counter
+        self.rf_ws = None if indexed else ws(B.lib.msa_route_score_fetch_workspace(dt, batch, tokens, kv_heads,
+                                                                                   head_dim, n_docs, n_chunks))
         self.tk_ws = ws(B.msa_topk_workspace(batch, n_docs, k))
         self.overlap_local = overlap_local
         at_ws = B.msa_sparse_attn_part_workspace if overlap_local else B.msa_sparse_attn_workspace
@@ -118,6 +121,50 @@ class LayerRunner:
         B.msa_route_score(q_r, kr_hat, chunk_doc, self.n_docs, doc_score=self.doc_score, ws=self.rs_ws,
                           layout=self.kr_layout, stream=stream, prefilled=prefilled)
         return self.doc_score
+
+    def route_fetch(self, q_r, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, stream=None):
+        """route() of this layer and, in its scan's tail, assemble() of the
+        last select(): that layer's documents copied from its content store
+        k_bar / v_bar (device or pinned host memory) into the context, hidden
+        behind this layer's routing (msa_route_score_fetch)."""
+        if self.indexed or self.src_mode == B.MSA_SRC_HOST_MEMCPY:
+            raise RuntimeError("route_fetch copies the context: a gathered runner over device or mapped memory")
+        prefilled, self._prefilled = self._prefilled, False
+        B.msa_route_score_fetch(q_r, kr_hat, chunk_doc, self.n_docs, self.ids, chunk_off, k_bar, v_bar,
+                                self.max_doc_chunks, self.k_ctx, self.v_ctx, self.ctx_pos, self.ctx_len,
+                                doc_score=self.doc_score, ws=self.rf_ws, layout=self.kr_layout, stream=stream,
+                                prefilled=prefilled)
+        return self.doc_score
+
+    def run_layers(self, layers, stream=None, after_layer=None):
+        """Every routed layer of one step with each layer's context fetch
+        hidden behind the next layer's routing scan: route and select layer 0;
+        then for each layer l, route_fetch(l + 1) (plain assemble() for the
+        last layer), attend(l), select(l + 1).  layers: per-layer tuples
+        (q_r, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc);
+        after_layer(l): called once layer l's output is queued in self.out.
+        The results are those of run() layer by layer."""
+        if self.overlap_local:
+            raise RuntimeError("run_layers runs the attention in one call (overlap_local is for run())")
+        L = len(layers)
+        if L == 0:
+            return self.out
+        q_r, kr_hat, chunk_doc = layers[0][:3]
+        self.route(q_r, kr_hat, chunk_doc, stream)
+        self.select(stream)
+        for l in range(L):
+            _, _, _, chunk_off, k_bar, v_bar, q, k_loc, v_loc = layers[l]
+            if l + 1 < L:
+                nq_r, nkr, ncd = layers[l + 1][:3]
+                self.route_fetch(nq_r, nkr, ncd, chunk_off, k_bar, v_bar, stream)
+            else:
+                self.assemble(chunk_off, k_bar, v_bar, stream)
+            self.attend(q, k_loc, v_loc, stream)
+            if after_layer is not None:
+                after_layer(l)
+            if l + 1 < L:
+                self.select(stream)
+        return self.out
 
     def select(self, stream=None):
         B.msa_topk(self.doc_score, self.k, ids=self.ids, vals=self.vals, ws=self.tk_ws, stream=stream,

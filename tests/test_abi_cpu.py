@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.msa_abi_version() == 13
+    assert M.msa_abi_version() == 14
     assert M.lib.msa_status_string(0).decode() == "ok"
     assert "workspace" in M.lib.msa_status_string(3).decode()
 
@@ -69,6 +69,32 @@ def test_route_score_validation():
     assert need >= 16 * 8 * 4
     assert L.msa_route_score(0, P, 1, 16, 8, 128, P, 0, P, 4, 4, P, P, need - 1, 0, None) == 3
     assert L.msa_route_score(1, P, 1, 1, 8, 128, P, 0, P, 4, 4, P, None, 0, 2, None) == 1   # unknown flag
+
+
+def test_route_score_fetch_validation():
+    L = M.lib
+    ws = L.msa_route_score_fetch_workspace(1, 1, 64, 8, 128, 4, 4)
+    assert ws >= 256
+    base = [1, P, 1, 64, 8, 128, P, 1, P, 4, 4, P, P, ws, 0]
+    fetch = [P, 1, 4, P, 4, 8, P, P, 8, 128, 32, P, P, P, P, None]
+    bad = list(fetch)
+    bad[0] = None                                                 # NULL selection
+    assert L.msa_route_score_fetch(*base, *bad) == 1
+    bad = list(fetch)
+    bad[2] = 5                                                    # f_k > f_n_docs
+    assert L.msa_route_score_fetch(*base, *bad) == 1
+    bad = list(fetch)
+    bad[10] = 31                                                  # f_max_ctx < f_k * f_max_doc_chunks
+    assert L.msa_route_score_fetch(*base, *bad) == 1
+    bad = list(fetch)
+    bad[8], bad[9] = 1, 2                                         # a row of 4 bytes
+    assert L.msa_route_score_fetch(*base, *bad) == 2
+    small = list(base)
+    small[13] = ws - 1
+    assert L.msa_route_score_fetch(*small, *fetch) == 3
+    flags = list(base)
+    flags[14] = 4
+    assert L.msa_route_score_fetch(*flags, *fetch) == 1
 
 
 def test_topk_validation():

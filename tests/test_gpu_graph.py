@@ -185,3 +185,57 @@ def test_fill_in_topk_step_equals_the_filling_step(indexed):
     ref = plain.route(qr, kr, cd)
     torch.cuda.synchronize()
     assert torch.equal(fused.doc_score.view(torch.int32), ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("host_src", [True, False])
+def test_run_layers_equals_run(host_src):
+    """LayerRunner.run_layers (each layer's context fetched in the next
+    layer's routing scan, msa_route_score_fetch) gives every layer the
+    selection, context and attention output of run() layer by layer, bit for
+    bit; eager and replayed as a HIP graph, from pinned host or device memory."""
+    B, T, L_loc, k, H, d, Hq, layers = 1, 64, 512, 8, 8, 128, 32, 4
+    lens = ragged_lengths(97, 700, 0, 900, n_empty=9)
+    tok_off = synth.offsets(lens)
+    chunk_off = O.chunk_offsets(tok_off, 64)
+    n_chunks, D = int(chunk_off[-1]), len(lens)
+    mdc = int(np.diff(chunk_off).max())
+    co_d = to_dev_i64(chunk_off)
+    cd = M.msa_chunk_doc_map(co_d, n_chunks)
+    L = []
+    for l in range(layers):
+        store = O.round_to_bf16(O.l2_normalize(gen(77, l, synth.T_KR, (n_chunks, H, d), True).astype(np.float64)))
+        kb, vb = (to_dev(gen(77, l, t, (n_chunks, H, d), True, scale_pow2=-3), True) for t in (synth.T_K, synth.T_V))
+        if host_src:
+            kb, vb = kb.cpu().pin_memory(), vb.cpu().pin_memory()
+        qr, q, kl, vl = (to_dev(gen(78, l, t, shp, True), True) for t, shp in ((synth.T_QR, (B, T, H, d)),
+                                                                             (synth.T_Q, (B, T, Hq, d)),
+                                                                             (synth.T_KLOC, (B, L_loc, H, d)),
+                                                                             (synth.T_VLOC, (B, L_loc, H, d))))
+        L.append((qr, to_dev(tile_np(store), True), cd, co_d, kb, vb, q, kl, vl))
+    src = M.MSA_SRC_HOST_MAPPED if host_src else M.MSA_SRC_DEVICE
+
+    def runner(fill):
+        return M.LayerRunner(batch=B, tokens=T, q_heads=Hq, kv_heads=H, head_dim=d, n_docs=D, n_chunks=n_chunks,
+                             k=k, max_doc_chunks=mdc, local_len=L_loc, dtype=torch.bfloat16, device=dev(),
+                             kr_layout=M.MSA_LAYOUT_TILED, src_mode=src, fill_in_topk=fill)
+
+    names = ("ids", "vals", "ctx_len", "out")
+    plain = runner(False)
+    want = []
+    for x in L:
+        plain.run(*x)
+        want.append({n: getattr(plain, n).clone() for n in names})
+    piped = runner(True)
+    got = []
+    piped.run_layers(L, after_layer=lambda l: got.append({n: getattr(piped, n).clone() for n in names}))
+    torch.cuda.synchronize()
+    for l in range(layers):
+        for n in names:
+            assert torch.equal(got[l][n], want[l][n]), f"layer {l}: {n}"
+    g = M.StepGraph(lambda: piped.run_layers(L))
+    for rep in range(3):
+        piped.out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(piped, n), want[-1][n]), f"replay {rep}: {n}"

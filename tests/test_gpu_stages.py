@@ -424,6 +424,53 @@ def test_route_prefilled_after_reset(bf16, layout, B, T):
         assert bool((buf == float("-inf")).all())
 
 
+@pytest.mark.parametrize("bf16,layout,B,T,host_src", [(True, 1, 1, 64, True), (True, 0, 3, 16, False),
+                                                      (True, 1, 32, 1, True), (False, 0, 2, 5, False)])
+def test_route_score_fetch_equals_the_two_calls(bf16, layout, B, T, host_src):
+    """msa_route_score_fetch: the scores of msa_route_score and the context of
+    msa_gather_kv, bit for bit, from device memory or pinned host memory; two
+    calls in a row on one workspace (the second finds the first's counter),
+    the second with a prefilled score buffer and a smaller selection."""
+    H, d, Hkv = 8, 128, 8
+    lens = ragged_lengths(17, 900, 0, 900, n_empty=13)
+    tok_off, chunk_off, n_chunks, co_d, cd = _doc_index(lens, 64)
+    D = len(lens)
+    mdc = int(np.diff(chunk_off).max())
+    st = O.round_to_store(O.l2_normalize(gen(33, 0, synth.T_KR, (n_chunks, H, d), bf16).astype(np.float64)),
+                          "bf16" if bf16 else "f32")
+    st_d = to_dev(tile_np(st) if layout == 1 else st, bf16)
+    q = to_dev(gen(34, 0, synth.T_QR, (B, T, H, d), bf16), bf16)
+    kb = to_dev(gen(35, 0, synth.T_K, (n_chunks, Hkv, d), bf16), bf16)
+    vb = to_dev(gen(35, 0, synth.T_V, (n_chunks, Hkv, d), bf16), bf16)
+    if host_src:
+        kb, vb = kb.cpu().pin_memory(), vb.cpu().pin_memory()
+    ws = torch.empty(M.lib.msa_route_score_fetch_workspace(int(bf16), B, T, H, d, D, n_chunks), dtype=torch.uint8,
+                     device=dev())
+    buf = torch.empty((B, D), dtype=torch.float32, device=dev())
+    r = np.random.default_rng(B + T)
+    for call, (fB, k) in enumerate(((3, 16), (2, 5))):
+        ids = np.stack([r.choice(D, size=k, replace=False) for _ in range(fB)]).astype(np.int32)
+        ids[0, -1] = -1                                   # a rank left empty (fewer documents than k)
+        ids_d = torch.from_numpy(ids).to(dev())
+        max_ctx = k * mdc
+        want = M.msa_gather_kv(ids_d, co_d, kb, vb, mdc, max_ctx,
+                               src_mode=M.MSA_SRC_HOST_MAPPED if host_src else M.MSA_SRC_DEVICE, device=dev())
+        ref = M.msa_route_score(q, st_d, cd, D, layout=layout)
+        out = [torch.full_like(want[0], 7), torch.full_like(want[1], 7), torch.full_like(want[2], -5),
+               torch.full_like(want[3], -5)]
+        if call == 1:
+            buf.fill_(float("-inf"))
+        M.msa_route_score_fetch(q, st_d, cd, D, ids_d, co_d, kb, vb, mdc, *out, doc_score=buf, ws=ws, layout=layout,
+                                prefilled=call == 1)
+        torch.cuda.synchronize()
+        assert torch.equal(buf.view(torch.int32), ref.view(torch.int32)), f"call {call}: scores"
+        assert torch.equal(out[3], want[3]), f"call {call}: ctx_len"
+        for b in range(fB):
+            n = int(want[3][b])
+            for i in range(3):
+                assert torch.equal(out[i][b, :n], want[i][b, :n]), f"call {call}, query {b}: output {i}"
+
+
 @pytest.mark.parametrize("B,k", [(3, 5), (1, 50), (4, 1)])
 def test_context_index(B, k):
     lens = ragged_lengths(7, 50, 0, 500, n_empty=3)
