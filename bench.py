@@ -69,9 +69,6 @@ def parse():
     ap.add_argument("--no-fill-in-topk", action="store_true",
                     help="fill the score buffer with -inf in a launch of its own before every routing call (by "
                          "default each layer's top-k leaves it at -inf for the next layer's routing call)")
-    ap.add_argument("--no-fetch-in-route", action="store_true",
-                    help="on the host tier, fetch each layer's documents in a launch of their own after its top-k "
-                         "(by default the fetch runs in the next layer's routing scan, msa_route_score_fetch)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP graph replay; for counter collection)")
     ap.add_argument("--layers", type=int, default=None, help="override the routed-layer count (profiling only)")
@@ -123,8 +120,7 @@ def main():
 
     p = configs.PRESETS[args.config]()
     pb = PresetBench(torch, p, args.layers, rounds=args.rounds, graph=not args.no_graph,
-                     overlap=args.overlap, fill_in_topk=not args.no_fill_in_topk,
-                     fetch_in_route=not args.no_fetch_in_route)
+                     overlap=args.overlap, fill_in_topk=not args.no_fill_in_topk)
     pb.build_stores()
     pb.build_content("hbm")
     assembly = args.hbm_assembly if args.rounds == 1 else "index"
@@ -141,12 +137,9 @@ def main():
     if pinned is not None:
         kv, desc = pinned
         pb.make_runner("host", indexed=False, src_mode=pb.M.MSA_SRC_HOST_MAPPED)
-        host_pipelined = pb.pipelined
         res = pb.headline(args.steps, args.warmup, kv=kv,
                           tier=f"host-mapped ({desc['pinned_layers']} of {pb.layers} layers' K/V pinned, cycled)")
-        res["config"]["gather"] = ("host-mapped: each layer's documents fetched in the next layer's routing scan "
-                                   "(msa_route_score_fetch), the last layer's by the gather kernel"
-                                   if host_pipelined else "host-mapped gather kernel")
+        res["config"]["gather"] = "host-mapped gather kernel"
         res["hbm_tier"] = {k: hbm[k] for k in ("value", "ms_per_step", "route_attn_us_per_query",
                                               "ms_per_step_eager_launches", "ms_per_step_graph_replay",
                                               "stage_ms_per_step", "attention_GBps")}
@@ -160,11 +153,10 @@ def main():
     if p.name == "cfg4" and args.rounds == 1 and not args.no_memory_parallel:
         res["memory_parallel"] = pb.memory_parallel()
     if pinned is not None:
-        res["host_tier"] = pb.host_tier(args.steps, args.warmup, pinned, modes=("memcpy",))
+        res["host_tier"] = pb.host_tier(args.steps, args.warmup, pinned, modes=("memcpy", "fetch_in_next_route"))
         res["host_tier"]["mapped"] = {"route_attn_us_per_query": res["route_attn_us_per_query"],
                                       "ms_per_step": res["ms_per_step"],
-                                      "fetch_ms_per_step": res["stage_ms_per_step"].get(
-                                          "fetch_last_layer" if host_pipelined else "fetch"),
+                                      "fetch_ms_per_step": res["stage_ms_per_step"].get("fetch"),
                                       "note": "the line's own step"}
         pb.unpin_host()
     pb.release()
@@ -180,7 +172,7 @@ class PresetBench:
     stage before any timing), a LayerRunner and the whole-path step."""
 
     def __init__(self, torch, p, layers=None, rounds=1, graph=True, overlap=False, fill_in_topk=True,
-                 fetch_in_route=True):
+                 fetch_in_route=False):
         import synth
         from synth import device as SD
         import sparse_attention_long_msa_amd as M
@@ -666,25 +658,40 @@ class PresetBench:
 
     def host_tier(self, steps, warmup, pinned, modes=("mapped", "memcpy")):
         """The step with the content K/V in pinned host memory (pin_host),
-        timed for the zero-copy gather kernel (mapped) and for hipMemcpyAsync
-        per document on a side stream (memcpy)."""
+        timed for the zero-copy gather kernel (mapped), for hipMemcpyAsync per
+        document on a side stream (memcpy), and with each layer's fetch done in
+        the next layer's routing scan (fetch_in_next_route,
+        msa_route_score_fetch)."""
         p, M = self.p, self.M
         kv, desc = pinned
         out = dict(desc)
         hbm_runner = self.runner
-        srcs = {"mapped": M.MSA_SRC_HOST_MAPPED, "memcpy": M.MSA_SRC_HOST_MEMCPY}
+        srcs = {"mapped": M.MSA_SRC_HOST_MAPPED, "memcpy": M.MSA_SRC_HOST_MEMCPY,
+                "fetch_in_next_route": M.MSA_SRC_HOST_MAPPED}
         for mode in modes:
             src = srcs[mode]
+            self.fetch_in_route = mode == "fetch_in_next_route"
             self.make_runner("host", indexed=False, src_mode=src)
             ms, route_ms = self.timed(steps, warmup, kv=kv)
+            if self.pipelined and self.graph:
+                ms = min(ms, self.timed(steps, warmup, kv=kv, route_events=False, graph=True)[0])
             stage = self.stages(min(steps, 3), kv=kv)
+            fetch_key = "fetch_last_layer" if self.pipelined else "fetch"
             out[mode] = {"route_attn_us_per_query": round(ms * 1e3 / p.B, 1), "ms_per_step": round(ms, 4),
                          "fetch_ms_per_step": round(stage[2], 4),
-                         "stage_ms_per_step": {"route_score": round(stage[0], 4), "topk": round(stage[1], 4),
-                                               "fetch": round(stage[2], 4), "attention": round(stage[3], 4)},
+                         "stage_ms_per_step": {("route_score_and_previous_fetch" if self.pipelined else "route_score"):
+                                               round(stage[0], 4), "topk": round(stage[1], 4),
+                                               fetch_key: round(stage[2], 4), "attention": round(stage[3], 4)},
                          "fetched_bytes_per_step": int(self.runner.ctx_len.sum().item()) * p.H * p.d * 2 * self.esz
                          * self.layers}
+            if self.pipelined:
+                out[mode]["note"] = ("each layer's fetch runs in the next layer's routing launch; this order holds "
+                                     "only when that routing call does not depend on the fetched layer's output, "
+                                     "as between independent queries served together (the synthetic layers here "
+                                     "are independent); one query's next-layer routing needs this layer's output")
             log(f"host tier {mode}: {ms:.3f} ms per step, fetch {stage[2]:.3f} ms")
+        self.fetch_in_route = False
+        self.pipelined = False
         self.runner = hbm_runner
         return out
 

@@ -249,18 +249,21 @@ int msa_route_score(int dtype, const void* q_r, int B, int T, int H, int d, cons
                     void* ws, size_t ws_bytes, int flags, void* stream);
 
 /*
- * msa_route_score_fetch - msa_route_score of one layer, with the context
- * assembly of another layer done inside the same launch (README, Overall
- * Design > Inference Pipeline: the content K/V stays in host memory and the
- * selected documents are fetched asynchronously; here the fetch of layer l's
- * selection hides behind layer l+1's routing scan).  The scan's workgroups
- * that finish their chunk ranges first copy the selected documents, one
- * (query, rank) at a time, while the others still stream: the host link and
- * the HBM scan overlap.  Results are exactly those of msa_route_score
- * followed by msa_gather_kv in MSA_SRC_DEVICE / MSA_SRC_HOST_MAPPED mode.
+ * msa_route_score_fetch - msa_route_score of one routing call, with the
+ * context assembly of a selection it does not depend on done inside the same
+ * launch (README, Overall Design > Inference Pipeline: the content K/V stays
+ * in host memory and the selected documents are fetched asynchronously).
+ * The scan's workgroups that finish their chunk ranges first copy the
+ * selected documents, one (query, rank) at a time, while the others still
+ * stream: the host link and the HBM scan overlap.  The order suits
+ * independent queries served together (one query's fetch inside another's
+ * routing); one query's next-layer routing needs this layer's attention
+ * output, so its own layers cannot use it.  Results are exactly those of
+ * msa_route_score followed by msa_gather_kv in MSA_SRC_DEVICE /
+ * MSA_SRC_HOST_MAPPED mode.
  *   routing arguments and flags as msa_route_score
- *   f_ids       [f_B, f_k] int32: the other layer's selection (msa_topk)
- *   f_chunk_off [f_n_docs + 1] int64 (device) of that layer's documents
+ *   f_ids       [f_B, f_k] int32: the selection to fetch (msa_topk)
+ *   f_chunk_off [f_n_docs + 1] int64 (device) of its documents
  *   f_k_bar, f_v_bar [n, f_Hkv, f_d] dtype: its content store, in device
  *               memory or in pinned host memory the GPU can map
  *   f_max_ctx, f_k_ctx, f_v_ctx [f_B, f_max_ctx, f_Hkv, f_d], f_ctx_pos

@@ -137,13 +137,16 @@ class LayerRunner:
         return self.doc_score
 
     def run_layers(self, layers, stream=None, after_layer=None):
-        """Every routed layer of one step with each layer's context fetch
-        hidden behind the next layer's routing scan: route and select layer 0;
-        then for each layer l, route_fetch(l + 1) (plain assemble() for the
-        last layer), attend(l), select(l + 1).  layers: per-layer tuples
-        (q_r, kr_hat, chunk_doc, chunk_off, k_bar, v_bar, q, k_loc, v_loc);
-        after_layer(l): called once layer l's output is queued in self.out.
-        The results are those of run() layer by layer."""
+        """A sequence of independent routed layers with each one's context
+        fetch hidden behind the next one's routing scan: route and select
+        layer 0; then for each layer l, route_fetch(l + 1) (plain assemble()
+        for the last layer), attend(l), select(l + 1).  The order is open only
+        when a layer's routing query does not depend on the previous layer's
+        output: independent queries served together, not the layers of one
+        query.  layers: per-layer tuples (q_r, kr_hat, chunk_doc, chunk_off,
+        k_bar, v_bar, q, k_loc, v_loc); after_layer(l): called once layer l's
+        output is queued in self.out.  The results are those of run() layer
+        by layer."""
         if self.overlap_local:
             raise RuntimeError("run_layers runs the attention in one call (overlap_local is for run())")
         L = len(layers)
