@@ -136,10 +136,12 @@ def main():
     pinned = pb.pin_host() if p.name == "cfg4" and args.rounds == 1 and not args.no_host_tier else None
     if pinned is not None:
         kv, desc = pinned
-        pb.make_runner("host", indexed=False, src_mode=pb.M.MSA_SRC_HOST_MAPPED)
+        # the selected rows are read in place from pinned host memory by the attention kernel
+        pb.make_runner("host", indexed=True, src_mode=pb.M.MSA_SRC_HOST_MAPPED)
         res = pb.headline(args.steps, args.warmup, kv=kv,
                           tier=f"host-mapped ({desc['pinned_layers']} of {pb.layers} layers' K/V pinned, cycled)")
-        res["config"]["gather"] = "host-mapped gather kernel"
+        res["config"]["gather"] = ("host-mapped, read in place: the top-k writes the selected rows' index and "
+                                   "the attention kernel reads those rows over the host link")
         res["hbm_tier"] = {k: hbm[k] for k in ("value", "ms_per_step", "route_attn_us_per_query",
                                               "ms_per_step_eager_launches", "ms_per_step_graph_replay",
                                               "stage_ms_per_step", "attention_GBps")}
@@ -153,11 +155,10 @@ def main():
     if p.name == "cfg4" and args.rounds == 1 and not args.no_memory_parallel:
         res["memory_parallel"] = pb.memory_parallel()
     if pinned is not None:
-        res["host_tier"] = pb.host_tier(args.steps, args.warmup, pinned, modes=("memcpy", "fetch_in_next_route"))
-        res["host_tier"]["mapped"] = {"route_attn_us_per_query": res["route_attn_us_per_query"],
-                                      "ms_per_step": res["ms_per_step"],
-                                      "fetch_ms_per_step": res["stage_ms_per_step"].get("fetch"),
-                                      "note": "the line's own step"}
+        res["host_tier"] = pb.host_tier(args.steps, args.warmup, pinned,
+                                        modes=("mapped", "memcpy", "fetch_in_next_route"))
+        res["host_tier"]["in_place"] = {"route_attn_us_per_query": res["route_attn_us_per_query"],
+                                        "ms_per_step": res["ms_per_step"], "note": "the line's own step"}
         pb.unpin_host()
     pb.release()
     if not args.no_cpu_baseline:

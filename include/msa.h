@@ -518,8 +518,13 @@ int msa_sparse_attn(int dtype, const void* q, int B, int T, int Hq, int Hkv, int
 /*
  * msa_sparse_attn_indexed - msa_sparse_attn over a context given by
  * msa_context_index: context entry e of query b is row ctx_row[b,e] of the
- * pooled store k_bar/v_bar [n_chunks, Hkv, d] (device memory, dtype), read in
- * place.  Every other argument, the result and the workspace
+ * pooled store k_bar/v_bar [n_chunks, Hkv, d] dtype, read in place.  The
+ * store may be in device memory or in pinned host memory mapped for the
+ * device (README, Overall Design > Inference Pipeline: the content K/V stays
+ * in host memory and only the selected documents are loaded): the kernel
+ * then reads the selected rows over the host link, and those reads overlap
+ * the local-window keys' work of the same launch, so no copy of the context
+ * is made.  Every other argument, the result and the workspace
  * (msa_sparse_attn_workspace) are those of msa_sparse_attn; the two give
  * bit-identical outputs for the same context.  Rows outside [0, n_chunks) are
  * clamped into the store (they are a caller error, never an out-of-bounds read).

@@ -136,6 +136,15 @@ def _dev(t, name, dtype=None, shape=None, optional=False):
     _layout(t, name, dtype, shape)
 
 
+def _store(t, name, dtype=None, shape=None):
+    """A K/V store that attention reads in place: device memory, or pinned
+    host memory, which the kernel then reads over the host link."""
+    if isinstance(t, torch.Tensor) and not t.is_cuda:
+        _pinned(t, name, dtype, shape)
+    else:
+        _dev(t, name, dtype, shape)
+
+
 def _pinned(t, name, dtype=None, shape=None):
     """A host-tier operand that a kernel or an async copy reads: a contiguous
     tensor in pinned (page-locked) host memory."""
@@ -600,9 +609,9 @@ def msa_sparse_attn(q, k_ctx, v_ctx, ctx_pos, ctx_len, k_loc, v_loc, q_pos_offse
 def msa_sparse_attn_indexed(q, k_bar, v_bar, ctx_row, ctx_pos, ctx_len, k_loc, v_loc, q_pos_offset, rope_base=1e6,
                             sm_scale=None, out=None, ws=None, rope_table=None, stream=None):
     B, T, Hq, d, Hkv, L_loc, out = _attn_operands(q, k_loc, v_loc, rope_table, out)
-    _dev(k_bar, "k_bar", q.dtype, (None, Hkv, d))
+    _store(k_bar, "k_bar", q.dtype, (None, Hkv, d))
     n_chunks = k_bar.shape[0]
-    _dev(v_bar, "v_bar", q.dtype, (n_chunks, Hkv, d))
+    _store(v_bar, "v_bar", q.dtype, (n_chunks, Hkv, d))
     _dev(ctx_row, "ctx_row", _I32, (B, None))
     max_ctx = ctx_row.shape[1]
     _dev(ctx_pos, "ctx_pos", _I32, (B, max_ctx))
@@ -640,9 +649,9 @@ def msa_sparse_attn_part(part, q, k_loc, v_loc, q_pos_offset, max_ctx, k_ctx=Non
             _dev(k_ctx, "k_ctx", q.dtype, (B, max_ctx, Hkv, d))
             _dev(v_ctx, "v_ctx", q.dtype, (B, max_ctx, Hkv, d))
         else:
-            _dev(k_ctx, "k_ctx", q.dtype, (None, Hkv, d))
+            _store(k_ctx, "k_ctx", q.dtype, (None, Hkv, d))
             ctx_rows = k_ctx.shape[0]
-            _dev(v_ctx, "v_ctx", q.dtype, (ctx_rows, Hkv, d))
+            _store(v_ctx, "v_ctx", q.dtype, (ctx_rows, Hkv, d))
             _dev(ctx_row, "ctx_row", _I32, (B, max_ctx))
         _dev(ctx_pos, "ctx_pos", _I32, (B, max_ctx))
         _dev(ctx_len, "ctx_len", _I32, (B,))
@@ -668,9 +677,9 @@ def msa_sparse_attn_indexed_noalloc(q, k_bar, v_bar, ctx_row, ctx_pos, ctx_len, 
     of a workspace (for callers that cannot allocate; pass ``out`` and
     ``rope_table`` to allocate nothing here either)."""
     B, T, Hq, d, Hkv, L_loc, out = _attn_operands(q, k_loc, v_loc, rope_table, out)
-    _dev(k_bar, "k_bar", q.dtype, (None, Hkv, d))
+    _store(k_bar, "k_bar", q.dtype, (None, Hkv, d))
     n_chunks = k_bar.shape[0]
-    _dev(v_bar, "v_bar", q.dtype, (n_chunks, Hkv, d))
+    _store(v_bar, "v_bar", q.dtype, (n_chunks, Hkv, d))
     _dev(ctx_row, "ctx_row", _I32, (B, None))
     max_ctx = ctx_row.shape[1]
     _dev(ctx_pos, "ctx_pos", _I32, (B, max_ctx))

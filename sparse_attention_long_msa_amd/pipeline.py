@@ -6,9 +6,11 @@ Assembly, then Sparse Generation; routing happens in every upper-half layer,
 each with its own routing-key store).  ``LayerRunner`` owns the per-layer
 outputs and workspaces so a loop over layers allocates nothing.
 
-With ``indexed=True`` (a device-resident K/V store) the context is not copied:
-assembly writes each context entry's store row and attention reads the rows in
-place; the result is bit-identical to the gathered path.
+With ``indexed=True`` the context is not copied: assembly writes each context
+entry's store row and attention reads the rows in place, from device memory or
+(src_mode MSA_SRC_HOST_MAPPED) from pinned host memory over the host link,
+where the reads overlap the local-window keys' work in the same kernel; the
+result is bit-identical to the gathered path.
 
 With ``overlap_local=True`` the attention runs as its two parts
 (msa_sparse_attn_part): the local-window part on a side stream once the top-k
@@ -41,8 +43,8 @@ class LayerRunner:
                  local_len, dtype, device, q_pos_offset=None, rope_base=1e6, sm_scale=None,
                  src_mode=B.MSA_SRC_DEVICE, chunk_off_h=None, kr_layout=B.MSA_LAYOUT_ROWS, indexed=False,
                  rounds=1, overlap_local=False, fill_in_topk=False):
-        if indexed and src_mode != B.MSA_SRC_DEVICE:
-            raise ValueError("indexed assembly reads the K/V store in place: it must be in device memory")
+        if indexed and src_mode == B.MSA_SRC_HOST_MEMCPY:
+            raise ValueError("indexed assembly reads the K/V store in place (device or mapped pinned host memory)")
         if rounds > 1 and not indexed:
             raise ValueError("Memory Interleave rounds grow an indexed context (K/V store in device memory)")
         if rounds > 1 and overlap_local:

@@ -239,3 +239,57 @@ def test_run_layers_equals_run(host_src):
         torch.cuda.synchronize()
         for n in names:
             assert torch.equal(getattr(piped, n), want[-1][n]), f"replay {rep}: {n}"
+
+
+def test_indexed_runner_over_a_host_store():
+    """LayerRunner(indexed=True, src_mode=MSA_SRC_HOST_MAPPED): the top-k
+    writes the selected rows' index and the attention reads them from pinned
+    host memory; every layer equals the runner over the same stores in device
+    memory bit for bit, eager and graph-replayed."""
+    B, T, L_loc, k, H, d, Hq, layers = 1, 64, 4096, 16, 8, 128, 32, 3
+    lens = ragged_lengths(99, 900, 0, 900, n_empty=9)
+    tok_off = synth.offsets(lens)
+    chunk_off = O.chunk_offsets(tok_off, 64)
+    n_chunks, D = int(chunk_off[-1]), len(lens)
+    mdc = int(np.diff(chunk_off).max())
+    co_d = to_dev_i64(chunk_off)
+    cd = M.msa_chunk_doc_map(co_d, n_chunks)
+    dev_layers, host_layers = [], []
+    for l in range(layers):
+        store = O.round_to_bf16(O.l2_normalize(gen(79, l, synth.T_KR, (n_chunks, H, d), True).astype(np.float64)))
+        kb, vb = (to_dev(gen(79, l, t, (n_chunks, H, d), True, scale_pow2=-3), True) for t in (synth.T_K, synth.T_V))
+        qr, q, kl, vl = (to_dev(gen(80, l, t, shp, True), True) for t, shp in ((synth.T_QR, (B, T, H, d)),
+                                                                             (synth.T_Q, (B, T, Hq, d)),
+                                                                             (synth.T_KLOC, (B, L_loc, H, d)),
+                                                                             (synth.T_VLOC, (B, L_loc, H, d))))
+        kr = to_dev(tile_np(store), True)
+        dev_layers.append((qr, kr, cd, co_d, kb, vb, q, kl, vl))
+        host_layers.append((qr, kr, cd, co_d, kb.cpu().pin_memory(), vb.cpu().pin_memory(), q, kl, vl))
+
+    def runner(src):
+        return M.LayerRunner(batch=B, tokens=T, q_heads=Hq, kv_heads=H, head_dim=d, n_docs=D, n_chunks=n_chunks,
+                             k=k, max_doc_chunks=mdc, local_len=L_loc, dtype=torch.bfloat16, device=dev(),
+                             kr_layout=M.MSA_LAYOUT_TILED, indexed=True, src_mode=src, fill_in_topk=True)
+
+    names = ("ids", "vals", "ctx_len", "out")
+    on_dev, on_host = runner(M.MSA_SRC_DEVICE), runner(M.MSA_SRC_HOST_MAPPED)
+    want = []
+    for x in dev_layers:
+        on_dev.run(*x)
+        want.append({n: getattr(on_dev, n).clone() for n in names})
+    for l, x in enumerate(host_layers):
+        on_host.run(*x)
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(on_host, n), want[l][n]), f"layer {l}: {n}"
+
+    def step():
+        for x in host_layers:
+            on_host.run(*x)
+    g = M.StepGraph(step)
+    for rep in range(2):
+        on_host.out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(on_host, n), want[-1][n]), f"replay {rep}: {n}"

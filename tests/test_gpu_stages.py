@@ -530,6 +530,33 @@ def test_sparse_attention_indexed(bf16, B, T, L_loc, ctx):
         assert e <= ATOL_ATTN["bf16" if bf16 else "f32"], f"b={b}: max-abs {e}"
 
 
+@pytest.mark.parametrize("B,T,L_loc,ctx", [(1, 64, 4096, [128]), (32, 1, 2048, None), (2, 64, 300, [0, 700]),
+                                           (1, 128, 200, [1000])])
+def test_sparse_attention_indexed_host_store(B, T, L_loc, ctx):
+    """The indexed attention reading its context rows from a store in pinned
+    host memory (over the host link) equals the same call on the store in
+    device memory bit for bit: the prefill (with the context's own split at
+    the 100M shape) and decode kernels, empty and long contexts."""
+    Hq, Hkv, d, qpo, n_rows = 32, 8, 128, 16, 3000
+    if ctx is None:
+        ctx = list(np.random.default_rng(3).integers(100, 1500, size=B))
+    max_ctx = max(max(ctx), 1)
+    seed = 150 + T
+    q, kl, vl = (to_dev(gen(seed, 0, t, shp, True), True) for t, shp in ((synth.T_Q, (B, T, Hq, d)),
+                                                                       (synth.T_KLOC, (B, L_loc, Hkv, d)),
+                                                                       (synth.T_VLOC, (B, L_loc, Hkv, d))))
+    kst = to_dev(gen(seed, 0, synth.T_K, (n_rows, Hkv, d), True, scale_pow2=-3), True)
+    vst = to_dev(gen(seed, 0, synth.T_V, (n_rows, Hkv, d), True, scale_pow2=-3), True)
+    r = np.random.default_rng(seed)
+    rows = torch.from_numpy(r.integers(0, n_rows, size=(B, max_ctx)).astype(np.int32)).to(dev())
+    cp = torch.from_numpy(r.integers(0, min(128, max_ctx), size=(B, max_ctx)).astype(np.int32)).to(dev())
+    cl = torch.from_numpy(np.asarray(ctx, dtype=np.int32)).to(dev())
+    want = M.msa_sparse_attn_indexed(q, kst, vst, rows, cp, cl, kl, vl, qpo)
+    got = M.msa_sparse_attn_indexed(q, kst.cpu().pin_memory(), vst.cpu().pin_memory(), rows, cp, cl, kl, vl, qpo)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+
+
 @pytest.mark.parametrize("B,D,k,n_sets", [(3, 5000, 16, 2), (2, 300, 64, 4), (1, 40, 16, 2), (2, 2000, 100, 3),
                                           (4, 20000, 32, 1)])
 def test_exclude_then_topk(B, D, k, n_sets):
