@@ -103,9 +103,10 @@ def test_preset_1m_full_ranking(layer):
     _log(f"cfg2: needle recall {_needle_recall(p, host, g)}")
 
 
-# cfg3 and cfg5 share their memory, the two cfg4 cases their layer: adjacent,
+# cfg3 and cfg5 share their memory, the cfg4 cases their layer: adjacent,
 # so the oracle's pooled store is built once per pair
-@pytest.mark.parametrize("name,tier", [("cfg3", "hbm"), ("cfg5", "hbm"), ("cfg4", "hbm"), ("cfg4", "host")])
+@pytest.mark.parametrize("name,tier", [("cfg3", "hbm"), ("cfg5", "hbm"), ("cfg4", "hbm"), ("cfg4", "host"),
+                                       ("cfg4", "host-in-place")])
 def test_preset_full_size_full_ranking(name, tier):
     p = configs.PRESETS[name]()
     layer = 17 if name == "cfg4" else 5
@@ -118,8 +119,10 @@ def test_preset_full_size_full_ranking(name, tier):
     # bench's default one-call attention is checked at these sizes by the
     # graph-replay tests against this eager path's ids, and by the 1M-token
     # and tiny presets against the oracle.
-    mode = M.MSA_SRC_HOST_MAPPED if tier == "host" else M.MSA_SRC_DEVICE
-    gl = GpuLayer(p, layer, host, src_mode=mode, indexed=tier == "hbm", overlap_local=True)
+    # host-in-place: the store in pinned host memory read in place by the one-call attention (the
+    # path bench.py times as host_tier.in_place)
+    mode = M.MSA_SRC_DEVICE if tier == "hbm" else M.MSA_SRC_HOST_MAPPED
+    gl = GpuLayer(p, layer, host, src_mode=mode, indexed=tier != "host", overlap_local=tier != "host-in-place")
     try:
         # the routing scan split per XCD as bench.py times it (where the store is long enough)
         shares = gl.runner.balance(gl.qr, gl.store[synth.T_KR], gl.cd)
