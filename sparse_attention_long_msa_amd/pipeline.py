@@ -52,6 +52,7 @@ class LayerRunner:
         self.rounds = rounds
         self.fill_in_topk = fill_in_topk
         self._prefilled = False   # doc_score holds -inf, left so by the last select()
+        self._selected = False    # ids hold a selection (route_fetch copies it)
         self.B, self.T, self.Hq, self.Hkv, self.d = batch, tokens, q_heads, kv_heads, head_dim
         self.n_docs, self.n_chunks, self.k = n_docs, n_chunks, k
         self.max_doc_chunks = max_doc_chunks
@@ -131,6 +132,8 @@ class LayerRunner:
         behind this layer's routing (msa_route_score_fetch)."""
         if self.indexed or self.src_mode == B.MSA_SRC_HOST_MEMCPY:
             raise RuntimeError("route_fetch copies the context: a gathered runner over device or mapped memory")
+        if not self._selected:
+            raise RuntimeError("route_fetch copies the last select()'s documents: select() first")
         prefilled, self._prefilled = self._prefilled, False
         B.msa_route_score_fetch(q_r, kr_hat, chunk_doc, self.n_docs, self.ids, chunk_off, k_bar, v_bar,
                                 self.max_doc_chunks, self.k_ctx, self.v_ctx, self.ctx_pos, self.ctx_len,
@@ -175,6 +178,7 @@ class LayerRunner:
         B.msa_topk(self.doc_score, self.k, ids=self.ids, vals=self.vals, ws=self.tk_ws, stream=stream,
                    reset=self.fill_in_topk)
         self._prefilled = self.fill_in_topk
+        self._selected = True
         return self.ids, self.vals
 
     def select_assemble(self, chunk_off, k_bar, v_bar, stream=None):
@@ -187,6 +191,7 @@ class LayerRunner:
                                  ids=self.ids, vals=self.vals, ctx_row=self.ctx_row, ctx_pos=self.ctx_pos,
                                  ctx_len=self.ctx_len, ws=self.tk_ws, stream=stream, reset=self.fill_in_topk)
         self._prefilled = self.fill_in_topk
+        self._selected = True
         self._store = (k_bar, v_bar)
 
     def assemble(self, chunk_off, k_bar, v_bar, stream=None):
